@@ -1,0 +1,240 @@
+"""Python binding of the MSA HIP library (libmsa.so).
+
+Argument marshalling only: every step of the hot path runs in the HIP
+kernels behind the C ABI of ``include/msa.h``.  PyTorch supplies device
+memory and the current stream.  There is no fallback: if the library is
+missing or cannot be loaded, every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+import re
+
+import torch
+
+__all__ = [
+    "MSAError", "Dims", "OP_INDEX_SELECT", "OP_BUILD_LISTS", "OP_ATTEND", "load_library",
+    "make_dims", "workspace_size", "index_select", "build_block_query_lists", "attend",
+    "msa_forward", "exported_symbols", "LIB_PATH", "HEADER_PATH",
+]
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libmsa.so")
+HEADER_PATH = os.path.join(os.path.dirname(_PKG), "include", "msa.h")
+
+OP_INDEX_SELECT, OP_BUILD_LISTS, OP_ATTEND = 0, 1, 2
+BLOCK = 128
+
+
+class MSAError(RuntimeError):
+    def __init__(self, status: int, where: str, detail: str = ""):
+        self.status = status
+        super().__init__(f"{where}: status {status} ({_status_string(status)}) {detail}".strip())
+
+
+class Dims(ctypes.Structure):
+    _fields_ = [
+        ("batch", ctypes.c_int32), ("num_q_heads", ctypes.c_int32),
+        ("num_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+        ("index_dim", ctypes.c_int32), ("block_size", ctypes.c_int32),
+        ("top_k", ctypes.c_int32), ("softmax_scale", ctypes.c_float),
+        ("total_q", ctypes.c_int64), ("total_k", ctypes.c_int64),
+        ("max_q_len", ctypes.c_int32), ("max_k_len", ctypes.c_int32),
+        ("q_chunk", ctypes.c_int32), ("reserved", ctypes.c_int32),
+    ]
+
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH):
+    """Load libmsa.so once; raises OSError/RuntimeError if it is not built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"MSA HIP library not built: {path} (run __graft_entry__.build())")
+    lib = ctypes.CDLL(path)
+    P, I32, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
+    DP = ctypes.POINTER(Dims)
+    lib.msa_abi_version.restype = I32
+    lib.msa_status_string.restype = ctypes.c_char_p
+    lib.msa_status_string.argtypes = [I32]
+    lib.msa_last_error.restype = ctypes.c_char_p
+    lib.msa_workspace_size.restype = I32
+    lib.msa_workspace_size.argtypes = [DP, I32, ctypes.POINTER(SZ)]
+    lib.msa_index_select.restype = I32
+    lib.msa_index_select.argtypes = [DP, P, P, P, P, P, P, P, SZ, P]
+    lib.msa_build_block_query_lists.restype = I32
+    lib.msa_build_block_query_lists.argtypes = [DP, P, P, P, P, P, P, SZ, P]
+    lib.msa_attend.restype = I32
+    lib.msa_attend.argtypes = [DP, P, P, P, P, P, P, P, P, P, P, P, SZ, P]
+    _lib = lib
+    return lib
+
+
+def _status_string(s: int) -> str:
+    try:
+        return load_library().msa_status_string(int(s)).decode()
+    except Exception:  # pragma: no cover - only while reporting another error
+        return "?"
+
+
+def _check(status: int, where: str):
+    if status != 0:
+        raise MSAError(status, where, load_library().msa_last_error().decode())
+
+
+def exported_symbols(header: str = HEADER_PATH) -> list:
+    """Function names declared in include/msa.h."""
+    txt = open(header).read()
+    return sorted(set(re.findall(r"\b(msa_[a-z_]+)\s*\(", txt)))
+
+
+def make_dims(*, batch, num_q_heads, num_kv_heads, head_dim, index_dim, top_k, total_q, total_k,
+              max_q_len, max_k_len, softmax_scale=0.0, q_chunk=0, block_size=BLOCK) -> Dims:
+    return Dims(int(batch), int(num_q_heads), int(num_kv_heads), int(head_dim), int(index_dim),
+                int(block_size), int(top_k), float(softmax_scale), int(total_q), int(total_k),
+                int(max_q_len), int(max_k_len), int(q_chunk), 0)
+
+
+def workspace_size(dims: Dims, op: int) -> int:
+    n = ctypes.c_size_t(0)
+    _check(load_library().msa_workspace_size(ctypes.byref(dims), int(op), ctypes.byref(n)),
+           "msa_workspace_size")
+    return int(n.value)
+
+
+def _ptr(t, name, dtype=None, device=True):
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if device and not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _shape(t, shape, name):
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+
+
+def _stream(stream):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _workspace(dims, op, workspace, device):
+    need = workspace_size(dims, op)
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=device)
+    return workspace
+
+
+def nb_max(dims: Dims) -> int:
+    return (dims.max_k_len + BLOCK - 1) // BLOCK
+
+
+def index_select(dims, q_idx, k_idx, cu_seqlens_q, cu_seqlens_k, sel, sel_score=None,
+                 workspace=None, stream=None):
+    G, T = dims.num_kv_heads, dims.total_q
+    _shape(q_idx, (T, G, dims.index_dim), "q_idx")
+    _shape(k_idx, (dims.total_k, dims.index_dim), "k_idx")
+    _shape(sel, (T, G, dims.top_k), "sel")
+    if sel_score is not None:
+        _shape(sel_score, (T, G, dims.top_k), "sel_score")
+    ws = _workspace(dims, OP_INDEX_SELECT, workspace, q_idx.device)
+    st = load_library().msa_index_select(
+        ctypes.byref(dims), _ptr(q_idx, "q_idx", torch.bfloat16), _ptr(k_idx, "k_idx", torch.bfloat16),
+        _ptr(cu_seqlens_q, "cu_seqlens_q", torch.int32), _ptr(cu_seqlens_k, "cu_seqlens_k", torch.int32),
+        _ptr(sel, "sel", torch.int32), _ptr(sel_score, "sel_score", torch.float32),
+        _ptr(ws, "workspace"), ctypes.c_size_t(ws.numel() * ws.element_size()), _stream(stream))
+    _check(st, "msa_index_select")
+    return sel
+
+
+def build_block_query_lists(dims, sel, cu_seqlens_q, cu_seqlens_k, block_offsets, block_entries,
+                            workspace=None, stream=None):
+    U = dims.batch * dims.num_kv_heads * nb_max(dims)
+    _shape(block_offsets, (U + 1,), "block_offsets")
+    if block_entries.numel() < dims.total_q * dims.num_kv_heads * dims.top_k:
+        raise ValueError("block_entries too small")
+    ws = _workspace(dims, OP_BUILD_LISTS, workspace, sel.device)
+    st = load_library().msa_build_block_query_lists(
+        ctypes.byref(dims), _ptr(sel, "sel", torch.int32),
+        _ptr(cu_seqlens_q, "cu_seqlens_q", torch.int32), _ptr(cu_seqlens_k, "cu_seqlens_k", torch.int32),
+        _ptr(block_offsets, "block_offsets", torch.int32), _ptr(block_entries, "block_entries", torch.int32),
+        _ptr(ws, "workspace"), ctypes.c_size_t(ws.numel() * ws.element_size()), _stream(stream))
+    _check(st, "msa_build_block_query_lists")
+    return block_offsets, block_entries
+
+
+def attend(dims, q, k, v, cu_seqlens_q, cu_seqlens_k, sel, block_offsets, block_entries, out,
+           lse=None, workspace=None, stream=None):
+    T, Hq, D, G = dims.total_q, dims.num_q_heads, dims.head_dim, dims.num_kv_heads
+    _shape(q, (T, Hq, D), "q")
+    _shape(k, (dims.total_k, G, D), "k")
+    _shape(v, (dims.total_k, G, D), "v")
+    _shape(out, (T, Hq, D), "out")
+    if lse is not None:
+        _shape(lse, (T, Hq), "lse")
+    ws = _workspace(dims, OP_ATTEND, workspace, q.device)
+    st = load_library().msa_attend(
+        ctypes.byref(dims), _ptr(q, "q", torch.bfloat16), _ptr(k, "k", torch.bfloat16),
+        _ptr(v, "v", torch.bfloat16), _ptr(cu_seqlens_q, "cu_seqlens_q", torch.int32),
+        _ptr(cu_seqlens_k, "cu_seqlens_k", torch.int32), _ptr(sel, "sel", torch.int32),
+        _ptr(block_offsets, "block_offsets", torch.int32), _ptr(block_entries, "block_entries", torch.int32),
+        _ptr(out, "out", torch.bfloat16), _ptr(lse, "lse", torch.float32), _ptr(ws, "workspace"),
+        ctypes.c_size_t(ws.numel() * ws.element_size()), _stream(stream))
+    _check(st, "msa_attend")
+    return out
+
+
+class Buffers:
+    """Output and workspace buffers of one MSA forward for fixed dims."""
+
+    def __init__(self, dims: Dims, device, want_scores=False, want_lse=True):
+        T, G, k = dims.total_q, dims.num_kv_heads, dims.top_k
+        dev = torch.device(device)
+        self.sel = torch.empty((T, G, k), dtype=torch.int32, device=dev)
+        self.sel_score = torch.empty((T, G, k), dtype=torch.float32, device=dev) if want_scores else None
+        U = dims.batch * G * nb_max(dims)
+        self.offsets = torch.empty((U + 1,), dtype=torch.int32, device=dev)
+        self.entries = torch.empty((max(1, T * G * k),), dtype=torch.int32, device=dev)
+        self.out = torch.empty((T, dims.num_q_heads, dims.head_dim), dtype=torch.bfloat16, device=dev)
+        self.lse = torch.empty((T, dims.num_q_heads), dtype=torch.float32, device=dev) if want_lse else None
+        need = max(workspace_size(dims, op) for op in (OP_INDEX_SELECT, OP_BUILD_LISTS, OP_ATTEND))
+        self.workspace = torch.empty((need,), dtype=torch.uint8, device=dev)
+
+
+def msa_forward(dims: Dims, q, k, v, q_idx, k_idx, cu_seqlens_q, cu_seqlens_k, bufs: Buffers = None,
+                stream=None) -> Buffers:
+    """The whole hot path: index_select -> build_block_query_lists -> attend.
+
+    One workspace serves the three calls (they run in order on one stream).
+    """
+    bufs = bufs or Buffers(dims, q.device)
+    index_select(dims, q_idx, k_idx, cu_seqlens_q, cu_seqlens_k, bufs.sel, bufs.sel_score,
+                 bufs.workspace, stream)
+    build_block_query_lists(dims, bufs.sel, cu_seqlens_q, cu_seqlens_k, bufs.offsets, bufs.entries,
+                            bufs.workspace, stream)
+    attend(dims, q, k, v, cu_seqlens_q, cu_seqlens_k, bufs.sel, bufs.offsets, bufs.entries,
+           bufs.out, bufs.lse, bufs.workspace, stream)
+    return bufs
+
+
+def dims_for(workload_like, q_chunk=0, softmax_scale=0.0) -> Dims:
+    """Dims of a problem described by per-sequence lengths and head sizes."""
+    w = workload_like
+    return make_dims(batch=len(w.seq_k_lens), num_q_heads=w.num_q_heads,
+                     num_kv_heads=w.num_kv_heads, head_dim=w.head_dim, index_dim=w.index_dim,
+                     top_k=w.top_k, total_q=sum(w.seq_q_lens), total_k=sum(w.seq_k_lens),
+                     max_q_len=max(w.seq_q_lens), max_k_len=max(w.seq_k_lens),
+                     softmax_scale=softmax_scale, q_chunk=q_chunk)

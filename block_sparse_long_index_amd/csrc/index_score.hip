@@ -1,0 +1,288 @@
+// Index Branch, step 1+2: token scores q_idx . k_idx on bf16 MFMA, max-pooled
+// per 128-token KV block.
+//
+// The Index Branch scores every visible key token with one index-query head
+// per GQA group against one shared index-key head, then max-pools the token
+// scores to block level (MSA guide, ai-tool-zukan.com/minimax-msa-guide,
+// sections "Index BranchとMain Branchの役割分担" and "2段階構造の中身").
+//
+// Only earlier blocks (beta < beta(p)) are scored: the query's own block is
+// always selected whatever its score, so its score is never needed for the
+// choice.  Output layout: S[beta * ld + row], row = (query - r0) * G + g, so a
+// workgroup's scores for one key block are one contiguous run (coalesced).
+//
+// Prefill kernel: a workgroup owns the rows (query, group) of a run of
+// queries in one sequence and streams the shared index keys block by block
+// through LDS; every wave keeps its rows' index queries in registers as the
+// MFMA B operand and computes S^T = K * Q^T so that each lane owns one row
+// and the block max is a register reduction plus one cross-half exchange.
+//
+// Decode kernel: few rows per sequence and long contexts, so the key range
+// is split over workgroups and the four waves split each block's 128 keys.
+#include "msa_common.h"
+
+namespace msa {
+
+// Copy one 128 x DI bf16 index-key block between global memory, registers and
+// a padded LDS tile (row stride DI + 8 elements keeps 16-byte reads of 32
+// consecutive rows on distinct banks).
+template <int DI, int NT>
+struct KTileStage {
+  static constexpr int kChunks = kBlock * DI / 8;              // 16-byte chunks per block
+  static constexpr int kPer = (kChunks + NT - 1) / NT;
+  static constexpr int kLd = DI + 8;
+  uint4 r[kPer];
+
+  __device__ inline void load(const uint16_t* __restrict__ src, int tid) {
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      int c = tid + i * NT;
+      if (kChunks % NT == 0 || c < kChunks) {
+        int row = c / (DI / 8), col = c % (DI / 8);
+        r[i] = *reinterpret_cast<const uint4*>(src + (size_t)row * DI + col * 8);
+      }
+    }
+  }
+  __device__ inline void store(uint16_t* lds, int tid) const {
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      int c = tid + i * NT;
+      if (kChunks % NT == 0 || c < kChunks) {
+        int row = c / (DI / 8), col = c % (DI / 8);
+        *reinterpret_cast<uint4*>(lds + row * kLd + col * 8) = r[i];
+      }
+    }
+  }
+};
+
+// ---------------------------------------------------------------------------
+// Prefill: RT row tiles of 32 rows per wave, NW waves per workgroup.
+// grid.x = query tiles per sequence, grid.y = sequence.
+// ---------------------------------------------------------------------------
+template <int DI, int RT, int NW>
+__global__ __launch_bounds__(NW * 64) void index_score_prefill_kernel(
+    const uint16_t* __restrict__ q_idx, const uint16_t* __restrict__ k_idx,
+    const int32_t* __restrict__ cu_q, const int32_t* __restrict__ cu_k, int G, int qt,
+    int r0, int r1, float* __restrict__ S, long long ld) {
+  constexpr int NT = NW * 64;
+  constexpr int KS = DI / 16;          // MFMA k-steps over the index dim
+  constexpr int LD = DI + 8;
+  __shared__ __attribute__((aligned(16))) uint16_t lds[2][kBlock * LD];
+
+  const int b = blockIdx.y;
+  const int qoff = cu_q[b], lq = cu_q[b + 1] - qoff;
+  const int koff = cu_k[b], lk = cu_k[b + 1] - koff;
+  int qa = qoff + (int)blockIdx.x * qt;
+  int qz = min(qoff + lq, qa + qt);
+  qa = max(qa, r0);
+  qz = min(qz, r1);
+  if (qa >= qz) return;
+  const int p_last = lk - lq + (qz - 1 - qoff);
+  const int beta_hi = p_last / kBlock;   // blocks 0 .. beta_hi-1 are non-local for the last row
+  if (beta_hi <= 0) return;
+  const int nrows = (qz - qa) * G;
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  const int lane = tid & 63;
+  const int col = lane & 31;
+  const int half = lane >> 5;
+
+  // index queries of this wave's rows, as MFMA B operands (k = 16ks + 8half + e)
+  bf16x8 qf[RT][KS];
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) {
+    int n = (wave * RT + rt) * 32 + col;
+    const uint16_t* src = q_idx + ((size_t)qa * G + n) * DI;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      uint4 v = make_uint4(0, 0, 0, 0);
+      if (n < nrows) v = *reinterpret_cast<const uint4*>(src + ks * 16 + half * 8);
+      qf[rt][ks] = as_bf16x8(v);
+    }
+  }
+
+  const uint16_t* kbase = k_idx + (size_t)koff * DI;
+  KTileStage<DI, NT> stage;
+  stage.load(kbase, tid);
+  stage.store(lds[0], tid);
+  __syncthreads();
+
+  const size_t srow = (size_t)(qa - r0) * G;
+  for (int beta = 0; beta < beta_hi; ++beta) {
+    // prefetch the next block (the last iteration re-reads its own block; unused)
+    const int nxt = min(beta + 1, beta_hi - 1);
+    stage.load(kbase + (size_t)nxt * kBlock * DI, tid);
+    const uint16_t* kt_lds = lds[beta & 1];
+
+    float rmax[RT];
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) rmax[rt] = -INFINITY;
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt) {
+      bf16x8 a[KS];
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+        a[ks] = as_bf16x8(*reinterpret_cast<const uint4*>(kt_lds + (kt * 32 + col) * LD + ks * 16 + half * 8));
+      f32x16 acc[RT];
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt) acc[rt] = f32x16{};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) acc[rt] = mfma32(a[ks], qf[rt][ks], acc[rt]);
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) rmax[rt] = fmaxf(rmax[rt], acc[rt][i]);
+    }
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+      rmax[rt] = fmaxf(rmax[rt], shfl_xor_f(rmax[rt], 32));
+      int n = (wave * RT + rt) * 32 + col;
+      if ((rt & 1) == half && n < nrows) S[(size_t)beta * ld + srow + n] = rmax[rt];
+    }
+    stage.store(lds[(beta + 1) & 1], tid);
+    __syncthreads();
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Decode: at most 32 rows per sequence; grid.x = key-block segment, grid.y = sequence.
+// Wave w computes keys 32w .. 32w+31 of every block in the segment.
+// ---------------------------------------------------------------------------
+template <int DI, int SEG>
+__global__ __launch_bounds__(256) void index_score_decode_kernel(
+    const uint16_t* __restrict__ q_idx, const uint16_t* __restrict__ k_idx,
+    const int32_t* __restrict__ cu_q, const int32_t* __restrict__ cu_k, int G, int r0, int r1,
+    float* __restrict__ S, long long ld) {
+  constexpr int NT = 256;
+  constexpr int KS = DI / 16;
+  constexpr int LD = DI + 8;
+  __shared__ __attribute__((aligned(16))) uint16_t lds[2][kBlock * LD];
+  __shared__ float red[2][4][32];
+
+  const int b = blockIdx.y;
+  const int qoff = cu_q[b], lq = cu_q[b + 1] - qoff;
+  const int koff = cu_k[b], lk = cu_k[b + 1] - koff;
+  int qa = max(qoff, r0), qz = min(qoff + lq, r1);
+  if (qa >= qz) return;
+  const int p_last = lk - lq + (qz - 1 - qoff);
+  const int beta_hi = p_last / kBlock;
+  const int b0 = (int)blockIdx.x * SEG;
+  const int b1 = min(beta_hi, b0 + SEG);
+  if (b0 >= b1) return;
+  const int nrows = min((qz - qa) * G, 32);
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  const int lane = tid & 63;
+  const int col = lane & 31;
+  const int half = lane >> 5;
+
+  bf16x8 qf[KS];
+  {
+    const uint16_t* src = q_idx + ((size_t)qa * G + col) * DI;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      uint4 v = make_uint4(0, 0, 0, 0);
+      if (col < nrows) v = *reinterpret_cast<const uint4*>(src + ks * 16 + half * 8);
+      qf[ks] = as_bf16x8(v);
+    }
+  }
+
+  const uint16_t* kbase = k_idx + (size_t)koff * DI;
+  KTileStage<DI, NT> stage;
+  stage.load(kbase + (size_t)b0 * kBlock * DI, tid);
+  stage.store(lds[0], tid);
+  __syncthreads();
+
+  const size_t srow = (size_t)(qa - r0) * G;
+  for (int beta = b0; beta < b1; ++beta) {
+    const int it = beta - b0;
+    stage.load(kbase + (size_t)min(beta + 1, b1 - 1) * kBlock * DI, tid);
+    // finish the previous block's reduction (its partial maxima are complete)
+    if (it > 0 && wave == 0 && lane < nrows) {
+      const float* rr = &red[(it - 1) & 1][0][0];
+      float m = fmaxf(fmaxf(rr[lane], rr[32 + lane]), fmaxf(rr[64 + lane], rr[96 + lane]));
+      S[(size_t)(beta - 1) * ld + srow + lane] = m;
+    }
+    const uint16_t* kt_lds = lds[it & 1];
+    f32x16 acc = f32x16{};
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      bf16x8 a = as_bf16x8(*reinterpret_cast<const uint4*>(kt_lds + (wave * 32 + col) * LD + ks * 16 + half * 8));
+      acc = mfma32(a, qf[ks], acc);
+    }
+    float m = acc[0];
+#pragma unroll
+    for (int i = 1; i < 16; ++i) m = fmaxf(m, acc[i]);
+    m = fmaxf(m, shfl_xor_f(m, 32));
+    if (half == 0) red[it & 1][wave][col] = m;
+    stage.store(lds[(it + 1) & 1], tid);
+    __syncthreads();
+  }
+  if (wave == 0 && lane < nrows) {
+    const int it = b1 - 1 - b0;
+    const float* rr = &red[it & 1][0][0];
+    float m = fmaxf(fmaxf(rr[lane], rr[32 + lane]), fmaxf(rr[64 + lane], rr[96 + lane]));
+    S[(size_t)(b1 - 1) * ld + srow + lane] = m;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// launchers
+// ---------------------------------------------------------------------------
+constexpr int kPrefillRT = 2;
+constexpr int kPrefillNW = 8;
+constexpr int kPrefillRows = kPrefillRT * kPrefillNW * 32;   // rows per workgroup
+constexpr int kDecodeSeg = 8;
+
+int prefill_rows_per_wg() { return kPrefillRows; }
+
+template <int DI>
+static hipError_t launch_prefill_di(const void* q_idx, const void* k_idx, const int32_t* cu_q,
+                                    const int32_t* cu_k, int batch, int G, int max_q_len, int r0,
+                                    int r1, float* S, long long ld, hipStream_t st) {
+  int qt = kPrefillRows / G;
+  if (qt < 1) return hipErrorInvalidValue;
+  dim3 grid((max_q_len + qt - 1) / qt, batch);
+  hipLaunchKernelGGL((index_score_prefill_kernel<DI, kPrefillRT, kPrefillNW>), grid,
+                     dim3(kPrefillNW * 64), 0, st, (const uint16_t*)q_idx, (const uint16_t*)k_idx,
+                     cu_q, cu_k, G, qt, r0, r1, S, ld);
+  return hipGetLastError();
+}
+
+hipError_t launch_index_score_prefill(const void* q_idx, const void* k_idx, const int32_t* cu_q,
+                                      const int32_t* cu_k, int batch, int G, int DI, int max_q_len,
+                                      int r0, int r1, float* S, long long ld, hipStream_t st) {
+  switch (DI) {
+    case 32: return launch_prefill_di<32>(q_idx, k_idx, cu_q, cu_k, batch, G, max_q_len, r0, r1, S, ld, st);
+    case 64: return launch_prefill_di<64>(q_idx, k_idx, cu_q, cu_k, batch, G, max_q_len, r0, r1, S, ld, st);
+    case 128: return launch_prefill_di<128>(q_idx, k_idx, cu_q, cu_k, batch, G, max_q_len, r0, r1, S, ld, st);
+  }
+  return hipErrorInvalidValue;
+}
+
+template <int DI>
+static hipError_t launch_decode_di(const void* q_idx, const void* k_idx, const int32_t* cu_q,
+                                   const int32_t* cu_k, int batch, int G, int nb_max, int r0, int r1,
+                                   float* S, long long ld, hipStream_t st) {
+  dim3 grid((nb_max + kDecodeSeg - 1) / kDecodeSeg, batch);
+  hipLaunchKernelGGL((index_score_decode_kernel<DI, kDecodeSeg>), grid, dim3(256), 0, st,
+                     (const uint16_t*)q_idx, (const uint16_t*)k_idx, cu_q, cu_k, G, r0, r1, S, ld);
+  return hipGetLastError();
+}
+
+hipError_t launch_index_score_decode(const void* q_idx, const void* k_idx, const int32_t* cu_q,
+                                     const int32_t* cu_k, int batch, int G, int DI, int nb_max,
+                                     int r0, int r1, float* S, long long ld, hipStream_t st) {
+  switch (DI) {
+    case 32: return launch_decode_di<32>(q_idx, k_idx, cu_q, cu_k, batch, G, nb_max, r0, r1, S, ld, st);
+    case 64: return launch_decode_di<64>(q_idx, k_idx, cu_q, cu_k, batch, G, nb_max, r0, r1, S, ld, st);
+    case 128: return launch_decode_di<128>(q_idx, k_idx, cu_q, cu_k, batch, G, nb_max, r0, r1, S, ld, st);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace msa

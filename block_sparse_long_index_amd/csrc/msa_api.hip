@@ -1,0 +1,266 @@
+// Host side of the C ABI declared in include/msa.h: argument validation,
+// workspace layout, query-chunk loops and kernel launches.  No device memory
+// is allocated here and nothing synchronises the stream.
+#include <math.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <string>
+
+#include "msa.h"
+#include "msa_common.h"
+
+namespace msa {
+hipError_t launch_index_score_prefill(const void*, const void*, const int32_t*, const int32_t*, int,
+                                      int, int, int, int, int, float*, long long, hipStream_t);
+hipError_t launch_index_score_decode(const void*, const void*, const int32_t*, const int32_t*, int,
+                                     int, int, int, int, int, float*, long long, hipStream_t);
+hipError_t launch_topk_select(const float*, long long, int, int, const int32_t*, const int32_t*, int,
+                              int, int, bool, int32_t*, float*, hipStream_t);
+size_t lists_workspace_bytes(int batch, int G, int nqt_max, int nb_max);
+int list_tile_rows();
+hipError_t launch_build_lists(const int32_t*, const int32_t*, const int32_t*, int, int, int, int,
+                              int, int32_t*, int32_t*, void*, hipStream_t);
+hipError_t launch_attend_blocks(int, int, const void*, const void*, const void*, const int32_t*,
+                                const int32_t*, int, int, int, int, int, const int32_t*,
+                                const int32_t*, int, int, float, float*, float2*, hipStream_t);
+hipError_t launch_merge(int, const float*, const float2*, const int32_t*, int, int, int, int, int,
+                        void*, float*, hipStream_t);
+}  // namespace msa
+
+namespace {
+
+thread_local std::string g_last_error;
+
+constexpr size_t kDefaultChunkBytes = (size_t)32 << 30;   // workspace cap when q_chunk == 0
+constexpr int kMaxNbLds = 12288;                          // per-sequence blocks the LDS lists hold
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+msa_status_t fail(msa_status_t s, const char* msg) {
+  g_last_error = msg;
+  return s;
+}
+
+struct Derived {
+  int G, Hq, D, DI, hpg, top_k;
+  int nb_max, nqt_max;
+  bool decode_path;
+  float scale;
+  long long total_q;
+};
+
+msa_status_t check_dims(const msa_dims_t* d, Derived* out) {
+  if (!d) return fail(MSA_ERR_NULL_ARG, "dims is NULL");
+  if (d->batch < 1) return fail(MSA_ERR_BAD_DIMS, "batch must be >= 1");
+  if (d->num_q_heads < 1 || d->num_kv_heads < 1) return fail(MSA_ERR_BAD_DIMS, "head counts must be >= 1");
+  if (d->num_q_heads % d->num_kv_heads) return fail(MSA_ERR_BAD_DIMS, "num_q_heads % num_kv_heads != 0");
+  int hpg = d->num_q_heads / d->num_kv_heads;
+  if (hpg > 32 || (hpg & (hpg - 1))) return fail(MSA_ERR_UNSUPPORTED, "heads per group must be a power of two <= 32");
+  if (d->head_dim != 64 && d->head_dim != 128) return fail(MSA_ERR_UNSUPPORTED, "head_dim must be 64 or 128");
+  if (d->index_dim != 32 && d->index_dim != 64 && d->index_dim != 128)
+    return fail(MSA_ERR_UNSUPPORTED, "index_dim must be 32, 64 or 128");
+  if (d->block_size != MSA_BLOCK_SIZE) return fail(MSA_ERR_UNSUPPORTED, "block_size must be 128");
+  if (d->top_k < 1 || d->top_k > MSA_MAX_TOP_K) return fail(MSA_ERR_BAD_DIMS, "top_k must be in 1..32");
+  if (!(d->softmax_scale >= 0.f) || isinf(d->softmax_scale)) return fail(MSA_ERR_BAD_DIMS, "softmax_scale must be finite and >= 0");
+  if (d->total_q < 0 || d->total_k < 0) return fail(MSA_ERR_BAD_DIMS, "negative totals");
+  if (d->total_q >= ((long long)1 << 26)) return fail(MSA_ERR_UNSUPPORTED, "total_q must be < 2^26");
+  if (d->total_k >= ((long long)1 << 31)) return fail(MSA_ERR_UNSUPPORTED, "total_k must be < 2^31");
+  if (d->total_q > d->total_k) return fail(MSA_ERR_BAD_DIMS, "total_q > total_k (each sequence needs Lq <= Lk)");
+  if (d->max_q_len < 0 || d->max_k_len < 0 || d->max_q_len > d->max_k_len)
+    return fail(MSA_ERR_BAD_DIMS, "need 0 <= max_q_len <= max_k_len");
+  if (d->max_q_len > d->total_q || d->max_k_len > d->total_k)
+    return fail(MSA_ERR_BAD_DIMS, "max lengths exceed totals");
+  if (d->q_chunk < 0) return fail(MSA_ERR_BAD_DIMS, "q_chunk must be >= 0");
+  if (d->reserved != 0) return fail(MSA_ERR_BAD_DIMS, "reserved must be 0");
+  out->G = d->num_kv_heads;
+  out->Hq = d->num_q_heads;
+  out->D = d->head_dim;
+  out->DI = d->index_dim;
+  out->hpg = hpg;
+  out->top_k = d->top_k;
+  out->nb_max = (d->max_k_len + MSA_BLOCK_SIZE - 1) / MSA_BLOCK_SIZE;
+  out->nqt_max = (d->max_q_len + msa::list_tile_rows() - 1) / msa::list_tile_rows();
+  if (out->nb_max + msa::list_tile_rows() * d->top_k > kMaxNbLds + 4096)
+    return fail(MSA_ERR_UNSUPPORTED, "max_k_len too long for the on-chip list builder");
+  if ((long long)d->batch * out->G * out->nb_max >= ((long long)1 << 30))
+    return fail(MSA_ERR_UNSUPPORTED, "batch * num_kv_heads * blocks too large");
+  out->decode_path = (long long)d->max_q_len * out->G <= 32;
+  out->scale = d->softmax_scale > 0.f ? d->softmax_scale : 1.f / sqrtf((float)d->head_dim);
+  out->total_q = d->total_q;
+  return MSA_OK;
+}
+
+long long round_chunk(long long rows, long long total) {
+  if (rows >= total) return total;
+  if (rows >= 128) rows -= rows % 128;
+  return rows < 1 ? 1 : rows;
+}
+
+// rows per pass of msa_index_select and the bytes of its score buffer
+long long select_chunk(const msa_dims_t* d, const Derived& x) {
+  long long per_row = (long long)x.G * x.nb_max * 4;
+  long long rows = d->q_chunk > 0 ? d->q_chunk : (long long)(kDefaultChunkBytes / (per_row ? per_row : 1));
+  return round_chunk(rows, x.total_q);
+}
+
+long long attend_chunk(const msa_dims_t* d, const Derived& x) {
+  long long per_row = (long long)x.Hq * x.top_k * ((long long)x.D * 4 + 8);
+  long long rows = d->q_chunk > 0 ? d->q_chunk : (long long)(kDefaultChunkBytes / per_row);
+  // partial rows are indexed with int32
+  long long cap = (((long long)1 << 31) - 1) / ((long long)x.Hq * x.top_k);
+  if (rows > cap) rows = cap;
+  return round_chunk(rows, x.total_q);
+}
+
+size_t ws_select(const msa_dims_t* d, const Derived& x) {
+  long long c = select_chunk(d, x);
+  return align256((size_t)c * x.G * x.nb_max * 4) + 256;
+}
+size_t ws_lists(const msa_dims_t* d, const Derived& x) {
+  return msa::lists_workspace_bytes(d->batch, x.G, x.nqt_max, x.nb_max) + 256;
+}
+size_t ws_attend(const msa_dims_t* d, const Derived& x) {
+  long long c = attend_chunk(d, x);
+  size_t rows = (size_t)c * x.Hq * x.top_k;
+  return align256(rows * x.D * 4) + align256(rows * 8) + 256;
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+msa_status_t hip_fail(hipError_t e) {
+  g_last_error = std::string("HIP: ") + hipGetErrorString(e);
+  return MSA_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t msa_abi_version(void) { return MSA_ABI_VERSION; }
+
+const char* msa_last_error(void) { return g_last_error.c_str(); }
+
+const char* msa_status_string(msa_status_t s) {
+  switch (s) {
+    case MSA_OK: return "MSA_OK";
+    case MSA_ERR_NULL_ARG: return "MSA_ERR_NULL_ARG: a required pointer is NULL";
+    case MSA_ERR_BAD_DIMS: return "MSA_ERR_BAD_DIMS: inconsistent or out-of-range sizes";
+    case MSA_ERR_UNSUPPORTED: return "MSA_ERR_UNSUPPORTED: size not implemented by this build";
+    case MSA_ERR_ALIGNMENT: return "MSA_ERR_ALIGNMENT: tensor pointer not 16-byte aligned";
+    case MSA_ERR_WORKSPACE_TOO_SMALL: return "MSA_ERR_WORKSPACE_TOO_SMALL: workspace below msa_workspace_size()";
+    case MSA_ERR_HIP: return "MSA_ERR_HIP: a HIP call failed";
+  }
+  return "MSA_ERR_UNKNOWN";
+}
+
+msa_status_t msa_workspace_size(const msa_dims_t* dims, msa_op_t op, size_t* bytes) {
+  Derived x;
+  msa_status_t s = check_dims(dims, &x);
+  if (s != MSA_OK) return s;
+  if (!bytes) return fail(MSA_ERR_NULL_ARG, "bytes is NULL");
+  switch (op) {
+    case MSA_OP_INDEX_SELECT: *bytes = ws_select(dims, x); return MSA_OK;
+    case MSA_OP_BUILD_LISTS: *bytes = ws_lists(dims, x); return MSA_OK;
+    case MSA_OP_ATTEND: *bytes = ws_attend(dims, x); return MSA_OK;
+  }
+  return fail(MSA_ERR_BAD_DIMS, "unknown op");
+}
+
+msa_status_t msa_index_select(const msa_dims_t* dims, const void* q_idx, const void* k_idx,
+                              const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                              int32_t* sel, float* sel_score, void* workspace,
+                              size_t workspace_bytes, void* stream) {
+  Derived x;
+  msa_status_t s = check_dims(dims, &x);
+  if (s != MSA_OK) return s;
+  if (x.total_q == 0) return MSA_OK;   // no queries: nothing to select
+  if (!q_idx || !k_idx || !cu_seqlens_q || !cu_seqlens_k || !sel || !workspace)
+    return fail(MSA_ERR_NULL_ARG, "a required pointer is NULL");
+  if (!aligned16(q_idx) || !aligned16(k_idx) || !aligned16(sel) || !aligned16(workspace) ||
+      (sel_score && !aligned16(sel_score)))
+    return fail(MSA_ERR_ALIGNMENT, "tensor pointers must be 16-byte aligned");
+  if (workspace_bytes < ws_select(dims, x))
+    return fail(MSA_ERR_WORKSPACE_TOO_SMALL, "index_select workspace too small");
+  hipStream_t st = (hipStream_t)stream;
+  float* S = (float*)(((uintptr_t)workspace + 255) & ~(uintptr_t)255);
+  const long long chunk = select_chunk(dims, x);
+  const bool wide = x.decode_path || chunk * x.G <= 16384;
+  for (long long r0 = 0; r0 < x.total_q; r0 += chunk) {
+    const int a = (int)r0, z = (int)std::min<long long>(x.total_q, r0 + chunk);
+    const long long ld = (long long)(z - a) * x.G;
+    hipError_t e;
+    if (x.decode_path)
+      e = msa::launch_index_score_decode(q_idx, k_idx, cu_seqlens_q, cu_seqlens_k, dims->batch, x.G,
+                                         x.DI, x.nb_max, a, z, S, ld, st);
+    else
+      e = msa::launch_index_score_prefill(q_idx, k_idx, cu_seqlens_q, cu_seqlens_k, dims->batch,
+                                          x.G, x.DI, dims->max_q_len, a, z, S, ld, st);
+    if (e != hipSuccess) return hip_fail(e);
+    e = msa::launch_topk_select(S, ld, a, z, cu_seqlens_q, cu_seqlens_k, dims->batch, x.G, x.top_k,
+                                wide, sel, sel_score, st);
+    if (e != hipSuccess) return hip_fail(e);
+  }
+  return MSA_OK;
+}
+
+msa_status_t msa_build_block_query_lists(const msa_dims_t* dims, const int32_t* sel,
+                                         const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                                         int32_t* block_offsets, int32_t* block_entries,
+                                         void* workspace, size_t workspace_bytes, void* stream) {
+  Derived x;
+  msa_status_t s = check_dims(dims, &x);
+  if (s != MSA_OK) return s;
+  // with no queries the offsets are still written (all zero); sel/entries are not touched
+  if (!cu_seqlens_q || !cu_seqlens_k || !block_offsets || !workspace ||
+      (x.total_q > 0 && (!sel || !block_entries)))
+    return fail(MSA_ERR_NULL_ARG, "a required pointer is NULL");
+  if (!aligned16(sel) || !aligned16(block_offsets) || !aligned16(block_entries) || !aligned16(workspace))
+    return fail(MSA_ERR_ALIGNMENT, "tensor pointers must be 16-byte aligned");
+  if (workspace_bytes < ws_lists(dims, x))
+    return fail(MSA_ERR_WORKSPACE_TOO_SMALL, "build_lists workspace too small");
+  void* ws = (void*)(((uintptr_t)workspace + 255) & ~(uintptr_t)255);
+  hipError_t e = msa::launch_build_lists(sel, cu_seqlens_q, cu_seqlens_k, dims->batch, x.G, x.top_k,
+                                         x.nqt_max, x.nb_max, block_offsets, block_entries, ws,
+                                         (hipStream_t)stream);
+  return e == hipSuccess ? MSA_OK : hip_fail(e);
+}
+
+msa_status_t msa_attend(const msa_dims_t* dims, const void* q, const void* k, const void* v,
+                        const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                        const int32_t* sel, const int32_t* block_offsets,
+                        const int32_t* block_entries, void* out, float* lse, void* workspace,
+                        size_t workspace_bytes, void* stream) {
+  Derived x;
+  msa_status_t s = check_dims(dims, &x);
+  if (s != MSA_OK) return s;
+  if (x.total_q == 0) return MSA_OK;   // no queries: no output
+  if (!q || !k || !v || !cu_seqlens_q || !cu_seqlens_k || !sel || !block_offsets || !block_entries ||
+      !out || !workspace)
+    return fail(MSA_ERR_NULL_ARG, "a required pointer is NULL");
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(sel) || !aligned16(out) ||
+      !aligned16(workspace) || !aligned16(block_offsets) || !aligned16(block_entries) ||
+      (lse && !aligned16(lse)))
+    return fail(MSA_ERR_ALIGNMENT, "tensor pointers must be 16-byte aligned");
+  if (workspace_bytes < ws_attend(dims, x))
+    return fail(MSA_ERR_WORKSPACE_TOO_SMALL, "attend workspace too small");
+  hipStream_t st = (hipStream_t)stream;
+  const long long chunk = attend_chunk(dims, x);
+  char* base = (char*)(((uintptr_t)workspace + 255) & ~(uintptr_t)255);
+  float* part_acc = (float*)base;
+  float2* part_ml = (float2*)(base + align256((size_t)chunk * x.Hq * x.top_k * x.D * 4));
+  const float scale_log2 = x.scale * 1.44269504088896340736f;
+  for (long long r0 = 0; r0 < x.total_q; r0 += chunk) {
+    const int a = (int)r0, z = (int)std::min<long long>(x.total_q, r0 + chunk);
+    hipError_t e = msa::launch_attend_blocks(x.D, x.hpg, q, k, v, cu_seqlens_q, cu_seqlens_k,
+                                             dims->batch, x.G, x.Hq, x.top_k, x.nb_max,
+                                             block_offsets, block_entries, a, z, scale_log2,
+                                             part_acc, part_ml, st);
+    if (e != hipSuccess) return hip_fail(e);
+    e = msa::launch_merge(x.D, part_acc, part_ml, sel, a, z, x.Hq, x.G, x.top_k, out, lse, st);
+    if (e != hipSuccess) return hip_fail(e);
+  }
+  return MSA_OK;
+}
+
+}  // extern "C"

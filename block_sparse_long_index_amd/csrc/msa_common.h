@@ -1,0 +1,82 @@
+// Internal helpers shared by the MSA kernels (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace msa {
+
+constexpr int kBlock = 128;          // KV block size B_k
+constexpr int kWave = 64;            // CDNA wavefront width
+constexpr int kEntrySlotBits = 5;    // list entries pack row * 32 + slot
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// Row geometry of one query row: its sequence, position and key offset.
+struct RowPos {
+  int b;       // sequence
+  int p;       // position within the sequence (queries are the last Lq of Lk)
+  int koff;    // first key row of the sequence
+  int lk;      // keys of the sequence
+  int qoff;    // first query row of the sequence
+};
+
+// Sequence that owns global query row r (binary search over cu_seqlens_q).
+__device__ inline RowPos locate_row(int r, const int32_t* __restrict__ cu_q,
+                                    const int32_t* __restrict__ cu_k, int batch) {
+  int lo = 0, hi = batch - 1;
+  while (lo < hi) {
+    int mid = (lo + hi + 1) >> 1;
+    if (cu_q[mid] <= r) lo = mid; else hi = mid - 1;
+  }
+  RowPos rp;
+  rp.b = lo;
+  rp.qoff = cu_q[lo];
+  int lq = cu_q[lo + 1] - rp.qoff;
+  rp.koff = cu_k[lo];
+  rp.lk = cu_k[lo + 1] - rp.koff;
+  rp.p = rp.lk - lq + (r - rp.qoff);
+  return rp;
+}
+
+// 32x32x16 bf16 MFMA, fp32 accumulate.  Output layout: lane l holds column
+// (l & 31) and, in register i, row 8*(i/4) + 4*(l/32) + (i%4).  The 16-wide
+// contraction is split over lane halves: half h supplies elements 8h..8h+7.
+__device__ inline f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ inline bf16x8 as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8, v); }
+__device__ inline uint4 as_u4(bf16x8 v) { return __builtin_bit_cast(uint4, v); }
+
+// fp32 -> bf16 bits, round to nearest even (NaN stays NaN).
+__device__ inline uint16_t f32_to_bf16_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+__device__ inline float bf16_bits_to_f32(uint16_t h) { return __uint_as_float(((uint32_t)h) << 16); }
+
+// Pack two floats as two bf16 (RNE) in one dword: lo in bits 0..15.
+__device__ inline uint32_t pack_bf16x2(float lo, float hi) {
+  return (uint32_t)f32_to_bf16_bits(lo) | ((uint32_t)f32_to_bf16_bits(hi) << 16);
+}
+
+// Order-preserving map of fp32 to uint32 (larger float -> larger key).
+__device__ inline uint32_t float_order_key(float f) {
+  uint32_t u = __float_as_uint(f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ inline float float_from_order_key(uint32_t k) {
+  uint32_t u = (k & 0x80000000u) ? (k & 0x7fffffffu) : ~k;
+  return __uint_as_float(u);
+}
+
+__device__ inline float shfl_xor_f(float v, int mask) { return __shfl_xor(v, mask, kWave); }
+
+}  // namespace msa

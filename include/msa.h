@@ -1,0 +1,180 @@
+/*
+ * msa.h -- C ABI of the MSA (MiniMax Sparse Attention) hot path on AMD MI355X (gfx950).
+ *
+ * MSA is two-branch block-sparse attention layered on GQA (MSA guide,
+ * ai-tool-zukan.com/minimax-msa-guide, section "MiniMax MSAとは何か").  The three
+ * compute entry points follow the decomposition the same page gives in its
+ * pseudocode figure (section "Index BranchとMain Branchの役割分担"):
+ *
+ *   msa_index_select()            score -> top_k(k) -> ensure_local_block
+ *   msa_build_block_query_lists() regroup the selection KV-block-outer
+ *                                 (tnkblog.net MiniMax M3 MSA post, section "MSA の実装")
+ *   msa_attend()                  exact softmax attention over the selected blocks
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ * - Tensors are dense, row-major, and live in device memory unless stated.
+ *   Every tensor pointer must be 16-byte aligned.
+ * - Sequences are packed ("varlen"): sequence b owns query rows
+ *   cu_seqlens_q[b] .. cu_seqlens_q[b+1]-1 and key rows cu_seqlens_k[b] ..
+ *   cu_seqlens_k[b+1]-1.  Its Lq_b queries are the LAST Lq_b of its Lk_b
+ *   positions: query i sits at position Lk_b - Lq_b + i (prefill: Lq = Lk;
+ *   decode: Lq = 1 at position Lk - 1).  Requires 0 <= Lq_b <= Lk_b.
+ *   cu_seqlens_* are int32 device arrays of batch + 1 entries.
+ * - KV block beta of a sequence is its positions [128*beta, 128*beta + 127];
+ *   blocks start at position 0 of every sequence.
+ * - Query head h belongs to GQA group h / (num_q_heads / num_kv_heads); there
+ *   is one index-query head per group and one shared index-key head.
+ * - Ownership: the caller allocates every buffer, workspace included; the
+ *   library never allocates, frees or keeps device memory.  All work is
+ *   enqueued on `stream` (a hipStream_t; NULL = the default stream) with no
+ *   host synchronisation; buffers must stay alive until the stream has passed
+ *   the call.  Outputs are bitwise deterministic for identical inputs.
+ * - Errors: every argument is validated on the host before anything is
+ *   launched; a call that returns an error has enqueued nothing.  A failed
+ *   HIP launch returns MSA_ERR_HIP (msa_last_error() gives HIP's message).
+ *   Device data that breaks the stated layout (e.g. a hand-written `sel`
+ *   with out-of-range ids, or cu_seqlens not matching the dims) gives
+ *   undefined results; kernels bound every address they derive from such
+ *   data, so it cannot make them read or write outside the buffers.
+ */
+#ifndef MSA_H_
+#define MSA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MSA_ABI_VERSION 1
+#define MSA_BLOCK_SIZE 128  /* B_k, MSA guide table in section "ブロック単位選択の数値設計" */
+#define MSA_MAX_TOP_K 32
+
+typedef enum msa_status {
+  MSA_OK = 0,
+  MSA_ERR_NULL_ARG = 1,            /* a required pointer is NULL */
+  MSA_ERR_BAD_DIMS = 2,            /* inconsistent or out-of-range sizes */
+  MSA_ERR_UNSUPPORTED = 3,         /* valid MSA, but not a size this build implements */
+  MSA_ERR_ALIGNMENT = 4,           /* a tensor pointer is not 16-byte aligned */
+  MSA_ERR_WORKSPACE_TOO_SMALL = 5, /* workspace_bytes below msa_workspace_size() */
+  MSA_ERR_HIP = 6                  /* a HIP runtime call or launch failed */
+} msa_status_t;
+
+typedef enum msa_op {
+  MSA_OP_INDEX_SELECT = 0,
+  MSA_OP_BUILD_LISTS = 1,
+  MSA_OP_ATTEND = 2
+} msa_op_t;
+
+/* Problem sizes; passed by pointer to every call.  All fields are host values. */
+typedef struct msa_dims {
+  int32_t batch;          /* number of packed sequences, >= 1 */
+  int32_t num_q_heads;    /* Hq; Hq / Hkv must be a power of two <= 32 */
+  int32_t num_kv_heads;   /* Hkv = G = number of GQA groups = number of index-query heads */
+  int32_t head_dim;       /* d in {64, 128} */
+  int32_t index_dim;      /* d_idx in {32, 64, 128} */
+  int32_t block_size;     /* must be 128 */
+  int32_t top_k;          /* blocks per (query, group) INCLUDING the forced local block, 1..32 */
+  float softmax_scale;    /* 0 -> 1/sqrt(head_dim); else finite and > 0 */
+  int64_t total_q;        /* sum of Lq_b; < 2^26 (list entries pack row * 32 + slot) */
+  int64_t total_k;        /* sum of Lk_b */
+  int32_t max_q_len;      /* max_b Lq_b (host-known upper bound; sizes launch grids) */
+  int32_t max_k_len;      /* max_b Lk_b (host-known upper bound; sizes launch grids) */
+  int32_t q_chunk;        /* query rows processed per internal pass; 0 -> library default.
+                             Bounds the workspace; results do not depend on it. */
+  int32_t reserved;       /* must be 0 */
+} msa_dims_t;
+
+/* Bytes of workspace the call `op` needs for `dims` (same dims as the call).
+ * Returns MSA_ERR_* on invalid dims, else MSA_OK and *bytes. */
+msa_status_t msa_workspace_size(const msa_dims_t* dims, msa_op_t op, size_t* bytes);
+
+/*
+ * Index Branch: per (query, group), the selected KV blocks.
+ *
+ * Computes, for every query row r at position p of its sequence and every
+ * group g (MSA guide, section "2段階構造の中身"; roles of the two index
+ * projections in section "Index BranchとMain Branchの役割分担"):
+ *   s[j]      = q_idx[r, g, :] . k_idx[j, :] for the visible keys j <= p,
+ *               accumulated in fp32 from bf16 inputs;
+ *   S[beta]   = max of s over the tokens of block beta (max-pooling);
+ *   sel[r, g] = { beta(p) } plus the top_k - 1 earlier blocks beta < beta(p)
+ *               with the largest S (ties: lower beta first); when fewer than
+ *               top_k - 1 earlier blocks exist, all of them.  The query's own
+ *               block is always in (section "クエリを含むローカルブロックの強制取り込み")
+ *               and counts toward top_k, so top_k = 16 keeps the fixed budget of
+ *               16 * 128 = 2,048 tokens (table in section "ブロック単位選択の数値設計").
+ *   The selection is shared by all query heads of the group and made
+ *   independently per group (section "GQAグループ単位の選択共有とは").
+ *
+ * q_idx     bf16  [total_q, num_kv_heads, index_dim]
+ * k_idx     bf16  [total_k, index_dim]
+ * sel       int32 [total_q, num_kv_heads, top_k]  out: ascending block ids, -1 padded
+ * sel_score fp32  [total_q, num_kv_heads, top_k]  out, optional (NULL): S of each
+ *           selected block, +inf for the local block, NaN for padding
+ * workspace >= msa_workspace_size(dims, MSA_OP_INDEX_SELECT) bytes
+ */
+msa_status_t msa_index_select(const msa_dims_t* dims, const void* q_idx, const void* k_idx,
+                              const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                              int32_t* sel, float* sel_score, void* workspace,
+                              size_t workspace_bytes, void* stream);
+
+/*
+ * KV-block-outer regrouping: for every (sequence b, group g, block beta) the
+ * queries whose selection holds beta (tnkblog.net MiniMax M3 MSA post,
+ * section "MSA の実装": KV block as the outer loop, gathering the queries that
+ * hit it; the same order in the wiki repost of the CSDN article, section
+ * "MiniMax Sparse Attention（MSA）", item 3).
+ *
+ * Bucket u = (b * num_kv_heads + g) * nb_max + beta, nb_max = ceil(max_k_len / 128).
+ * block_offsets int32 [batch * num_kv_heads * nb_max + 1]  out: CSR offsets
+ * block_entries int32 [total_q * num_kv_heads * top_k]     out: for bucket u,
+ *               entries block_offsets[u] .. block_offsets[u+1]-1 hold
+ *               row * 32 + slot with sel[row, g, slot] == beta, rows ascending.
+ *               Entries past block_offsets[U] are left untouched.
+ * sel           as produced by msa_index_select (any valid selection works).
+ * workspace >= msa_workspace_size(dims, MSA_OP_BUILD_LISTS) bytes
+ */
+msa_status_t msa_build_block_query_lists(const msa_dims_t* dims, const int32_t* sel,
+                                         const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                                         int32_t* block_offsets, int32_t* block_entries,
+                                         void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Main Branch: exact softmax attention of every query head over the visible
+ * keys of its group's selected blocks (MSA guide, sections "MiniMax MSAとは何か"
+ * and "2段階構造の中身"): out[r, h] = sum_j softmax_j(scale * q[r,h] . k[j,g]) v[j,g]
+ * over J = { j <= p : beta(j) in sel[r, g] }.  Run KV-block-outer: each block's
+ * K/V is staged on chip once per pass and serves every gathered query; the
+ * per-(query, head, block) softmax partials are merged by log-sum-exp.
+ *
+ * q        bf16 [total_q, num_q_heads, head_dim]
+ * k, v     bf16 [total_k, num_kv_heads, head_dim]
+ * sel, block_offsets, block_entries: as from the two calls above (same dims)
+ * out      bf16 [total_q, num_q_heads, head_dim]  out
+ * lse      fp32 [total_q, num_q_heads]  out, optional (NULL): natural-log
+ *          log-sum-exp of the scaled logits over J
+ * workspace >= msa_workspace_size(dims, MSA_OP_ATTEND) bytes
+ */
+msa_status_t msa_attend(const msa_dims_t* dims, const void* q, const void* k, const void* v,
+                        const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                        const int32_t* sel, const int32_t* block_offsets,
+                        const int32_t* block_entries, void* out, float* lse, void* workspace,
+                        size_t workspace_bytes, void* stream);
+
+/* Static description of a status code. */
+const char* msa_status_string(msa_status_t status);
+
+/* Message of the last MSA_ERR_HIP (or validation detail) on the calling thread. */
+const char* msa_last_error(void);
+
+/* MSA_ABI_VERSION of the loaded library. */
+int32_t msa_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MSA_H_ */

@@ -1,0 +1,132 @@
+"""Host-side checks of the C ABI (no GPU needed, nothing is launched).
+
+The library must load, export every function include/msa.h declares, and
+reject bad arguments on the host before any launch.  Pointers passed here
+are fake; every call below fails validation, so none reaches the device.
+"""
+import ctypes
+
+import pytest
+
+import block_sparse_long_index_amd as msa
+
+lib = None
+
+
+def setup_module(_):
+    global lib
+    lib = msa.load_library()
+
+
+def _dims(**kw):
+    base = dict(batch=1, num_q_heads=64, num_kv_heads=8, head_dim=128, index_dim=128, top_k=16,
+                total_q=32768, total_k=32768, max_q_len=32768, max_k_len=32768)
+    base.update(kw)
+    return msa.make_dims(**base)
+
+
+def test_exports_every_declared_symbol():
+    names = msa.exported_symbols()
+    assert set(names) >= {"msa_index_select", "msa_build_block_query_lists", "msa_attend",
+                          "msa_workspace_size", "msa_status_string", "msa_abi_version",
+                          "msa_last_error"}
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_abi_version_and_struct_layout():
+    assert lib.msa_abi_version() == 1
+    assert ctypes.sizeof(msa.Dims) == 64
+
+
+def test_status_strings():
+    for s in range(7):
+        assert lib.msa_status_string(s).decode().startswith("MSA_")
+
+
+def test_workspace_sizes_scale_with_chunk():
+    d = _dims()
+    full = msa.workspace_size(d, msa.OP_INDEX_SELECT)
+    assert full >= 32768 * 8 * 256 * 4
+    d2 = _dims(q_chunk=1024)
+    assert msa.workspace_size(d2, msa.OP_INDEX_SELECT) < full
+    a_full = msa.workspace_size(_dims(), msa.OP_ATTEND)
+    a_small = msa.workspace_size(_dims(q_chunk=256), msa.OP_ATTEND)
+    assert a_small < a_full
+    assert a_small >= 256 * 64 * 16 * (128 * 4 + 8)
+    assert msa.workspace_size(d, msa.OP_BUILD_LISTS) >= 256 * 8 * 256 * 4
+
+
+def test_1m_context_default_workspace_is_bounded():
+    d = _dims(total_q=1 << 20, total_k=1 << 20, max_q_len=1 << 20, max_k_len=1 << 20)
+    for op in (msa.OP_INDEX_SELECT, msa.OP_ATTEND):
+        assert msa.workspace_size(d, op) <= (33 << 30)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(batch=0), 2), (dict(num_q_heads=60), 2), (dict(num_q_heads=48, num_kv_heads=8), 3),
+    (dict(head_dim=96), 3), (dict(index_dim=48), 3), (dict(block_size=64), 3),
+    (dict(top_k=0), 2), (dict(top_k=33), 2), (dict(softmax_scale=-1.0), 2),
+    (dict(total_q=40000), 2), (dict(max_q_len=40000), 2), (dict(q_chunk=-1), 2),
+    (dict(total_q=1 << 26, total_k=1 << 27, max_q_len=1, max_k_len=1), 3),
+    (dict(total_k=1 << 22, max_k_len=1 << 22), 3),
+])
+def test_bad_dims_rejected(kw, status):
+    d = _dims(**kw)
+    n = ctypes.c_size_t(0)
+    assert lib.msa_workspace_size(ctypes.byref(d), 0, ctypes.byref(n)) == status
+
+
+def test_reserved_must_be_zero():
+    d = _dims()
+    d.reserved = 1
+    n = ctypes.c_size_t(0)
+    assert lib.msa_workspace_size(ctypes.byref(d), 0, ctypes.byref(n)) == 2
+
+
+def test_null_and_alignment_and_workspace_checks_launch_nothing():
+    d = _dims()
+    P = ctypes.c_void_p
+    ok = P(0x10000)
+    odd = P(0x10004)
+    big = ctypes.c_size_t(1 << 40)
+    sel = lib.msa_index_select
+    assert sel(ctypes.byref(d), None, ok, ok, ok, ok, None, ok, big, None) == 1
+    assert sel(ctypes.byref(d), odd, ok, ok, ok, ok, None, ok, big, None) == 4
+    assert sel(ctypes.byref(d), ok, ok, ok, ok, ok, None, ok, ctypes.c_size_t(16), None) == 5
+    assert "small" in lib.msa_last_error().decode()
+    bl = lib.msa_build_block_query_lists
+    assert bl(ctypes.byref(d), ok, ok, ok, None, ok, ok, big, None) == 1
+    assert bl(ctypes.byref(d), ok, ok, ok, ok, odd, ok, big, None) == 4
+    assert bl(ctypes.byref(d), ok, ok, ok, ok, ok, ok, ctypes.c_size_t(0), None) == 5
+    at = lib.msa_attend
+    assert at(ctypes.byref(d), ok, ok, ok, ok, ok, ok, ok, ok, None, None, ok, big, None) == 1
+    assert at(ctypes.byref(d), ok, ok, ok, ok, ok, ok, ok, ok, ok, odd, ok, big, None) == 4
+    assert at(ctypes.byref(d), ok, ok, ok, ok, ok, ok, ok, ok, ok, None, ok, ctypes.c_size_t(1), None) == 5
+    assert sel(None, ok, ok, ok, ok, ok, None, ok, big, None) == 1
+
+
+def test_python_binding_rejects_cpu_tensors():
+    import torch
+    d = msa.make_dims(batch=1, num_q_heads=4, num_kv_heads=1, head_dim=64, index_dim=32, top_k=4,
+                      total_q=256, total_k=256, max_q_len=256, max_k_len=256)
+    q_idx = torch.zeros((256, 1, 32), dtype=torch.bfloat16)
+    k_idx = torch.zeros((256, 32), dtype=torch.bfloat16)
+    cu = torch.tensor([0, 256], dtype=torch.int32)
+    sel = torch.zeros((256, 1, 4), dtype=torch.int32)
+    ws = torch.zeros(msa.workspace_size(d, msa.OP_INDEX_SELECT), dtype=torch.uint8)
+    with pytest.raises(ValueError):
+        msa.index_select(d, q_idx, k_idx, cu, cu, sel, workspace=ws, stream=object())
+
+
+def test_product_path_does_not_import_oracle():
+    import ast
+    import glob
+    import os
+    pkg = os.path.dirname(msa.__file__)
+    for f in glob.glob(os.path.join(pkg, "**", "*.py"), recursive=True):
+        tree = ast.parse(open(f).read())
+        for node in ast.walk(tree):
+            if isinstance(node, (ast.Import, ast.ImportFrom)):
+                mods = [a.name for a in node.names] if isinstance(node, ast.Import) else [node.module or ""]
+                assert not any(m.split(".")[0] == "oracle" for m in mods), f

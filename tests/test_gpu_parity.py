@@ -1,0 +1,183 @@
+"""GPU parity of the MSA hot path against the CPU oracle (small and ragged cases).
+
+Every call goes through the C ABI (libmsa.so) via the Python binding.  Sizes
+are small enough for the oracle to check every row while spanning several
+tiles, ragged tails, Lq < Lk, single-query sequences and the degenerate
+selections (top_k = 1; top_k covering every block).
+"""
+import numpy as np
+import pytest
+import torch
+
+from msa_inputs import custom, generate, workload
+from oracle import msa_oracle as O
+
+pytestmark = pytest.mark.gpu
+
+from gpu_helpers import check_out, check_selection, log, problem_from, run_gpu  # noqa: E402
+
+
+def _full_check(w, q_chunk=0, tag=""):
+    log(f"[{tag or w.name}] lens k={w.seq_k_lens} q={w.seq_q_lens} Hq={w.num_q_heads} G={w.num_kv_heads} "
+        f"d={w.head_dim} di={w.index_dim} k={w.top_k} chunk={q_chunk}")
+    t = generate(w, "cpu")
+    dims, bufs, _ = run_gpu(w, t, q_chunk=q_chunk)
+    P = problem_from(t, w)
+    rows = list(range(w.total_q))
+    ref = P.run(rows, want_scores=True)
+    sel = bufs.sel.cpu().numpy()
+    bad, ties = check_selection(P, rows, sel, bufs.sel_score.cpu().numpy(), ref, w.index_dim)
+    log(f"[{tag or w.name}] selection mismatches {len(bad)} near-ties {ties}")
+    assert not bad, bad[:5]
+    check_out(bufs.out.float().cpu().numpy(), ref["out"], bufs.lse.cpu().numpy(), ref["lse"],
+              tag or w.name)
+    # Main Branch on the oracle's own selection (same rows)
+    return t, dims, bufs, P, ref
+
+
+def test_tiny_full():
+    _full_check(workload("tiny"))
+
+
+def test_ragged_batch_prefill():
+    w = custom([1500, 900, 130, 128, 3000, 257], [1500, 300, 130, 1, 2000, 200], num_q_heads=8,
+               num_kv_heads=2, head_dim=64, index_dim=64, top_k=5, seed=21, qkv_std=1.0)
+    _full_check(w)
+
+
+def test_gqa8_d128_prefill():
+    w = custom([2200], [2200], num_q_heads=64, num_kv_heads=8, head_dim=128, index_dim=128,
+               top_k=16, seed=22, qkv_std=1.0)
+    _full_check(w)
+
+
+def test_decode_path_small():
+    w = custom([5000, 20000, 128, 300, 129], [1, 1, 1, 1, 1], num_q_heads=16, num_kv_heads=8,
+               head_dim=128, index_dim=128, top_k=16, seed=23, qkv_std=1.0)
+    _full_check(w)
+
+
+def test_multi_token_decode_path():
+    # 4 new tokens x 8 groups = 32 rows: still the split-scan index path
+    w = custom([9000, 4100], [4, 3], num_q_heads=32, num_kv_heads=8, head_dim=64, index_dim=32,
+               top_k=6, seed=24, qkv_std=1.0)
+    _full_check(w)
+
+
+def test_top_k_one_is_block_local():
+    w = custom([1000, 333], [1000, 333], num_q_heads=4, num_kv_heads=2, head_dim=64, index_dim=32,
+               top_k=1, seed=25, qkv_std=1.0)
+    _full_check(w)
+
+
+def test_top_k_covering_everything_is_dense():
+    w = custom([700, 1100], [700, 1100], num_q_heads=8, num_kv_heads=1, head_dim=128, index_dim=64,
+               top_k=9, seed=26, qkv_std=1.0)
+    _full_check(w)
+
+
+def test_top_k_32_and_hpg_32():
+    w = custom([6000], [6000], num_q_heads=32, num_kv_heads=1, head_dim=64, index_dim=32,
+               top_k=32, seed=27, qkv_std=1.0)
+    _full_check(w)
+
+
+def test_hpg_1():
+    w = custom([2000], [2000], num_q_heads=4, num_kv_heads=4, head_dim=64, index_dim=32,
+               top_k=3, seed=28, qkv_std=1.0)
+    _full_check(w)
+
+
+def test_chunking_is_bitwise_invisible():
+    w = custom([3000, 1000], [3000, 1000], num_q_heads=8, num_kv_heads=2, head_dim=128,
+               index_dim=64, top_k=4, seed=29, qkv_std=1.0)
+    t = generate(w, "cpu")
+    _, a, _ = run_gpu(w, t, q_chunk=0)
+    _, b, _ = run_gpu(w, t, q_chunk=333)
+    _, c, _ = run_gpu(w, t, q_chunk=1)
+    for x in (b, c):
+        assert torch.equal(a.sel, x.sel)
+        assert torch.equal(a.offsets, x.offsets)
+        assert torch.equal(a.out, x.out)
+        assert torch.equal(a.lse, x.lse)
+
+
+def test_deterministic_and_workspace_poison_proof():
+    w = custom([2500], [2500], num_q_heads=16, num_kv_heads=2, head_dim=128, index_dim=128,
+               top_k=8, seed=30, qkv_std=1.0)
+    t = generate(w, "cpu")
+    _, a, _ = run_gpu(w, t)
+    _, b, _ = run_gpu(w, t, workspace_fill=0xFF)   # all-NaN float workspace
+    _, c, _ = run_gpu(w, t, workspace_fill=0x00)
+    for x in (b, c):
+        assert torch.equal(a.sel, x.sel) and torch.equal(a.sel_score.nan_to_num(), x.sel_score.nan_to_num())
+        assert torch.equal(a.entries[: int(a.offsets[-1])], x.entries[: int(x.offsets[-1])])
+        assert torch.equal(a.out, x.out) and torch.equal(a.lse, x.lse)
+
+
+def test_lists_are_exact_inverse():
+    w = custom([1500, 900, 4000], [1500, 300, 4000], num_q_heads=8, num_kv_heads=2, head_dim=64,
+               index_dim=32, top_k=6, seed=31, qkv_std=1.0)
+    t = generate(w, "cpu")
+    dims, bufs, _ = run_gpu(w, t)
+    P = problem_from(t, w)
+    sel = bufs.sel.cpu().numpy()
+    off, ent = O.build_block_query_lists(sel, P.seq, P.batch, P.G, P.nb_max)
+    n = int(off[-1])
+    assert np.array_equal(bufs.offsets.cpu().numpy().astype(np.int64), off)
+    assert np.array_equal(bufs.entries[:n].cpu().numpy().astype(np.int64), ent)
+
+
+def test_attend_on_oracle_selection():
+    """Main Branch checked on the oracle's own selection (lists built on GPU)."""
+    import block_sparse_long_index_amd as msa
+    w = custom([3000, 700], [3000, 700], num_q_heads=16, num_kv_heads=4, head_dim=128,
+               index_dim=64, top_k=7, seed=32, qkv_std=1.0)
+    t = generate(w, "cpu")
+    P = problem_from(t, w)
+    ref = P.run()
+    dev = torch.device("cuda:0")
+    g = {k: v.to(dev) for k, v in t.items()}
+    dims = msa.dims_for(w)
+    bufs = msa.Buffers(dims, dev)
+    bufs.sel.copy_(torch.from_numpy(ref["sel"].astype(np.int32)))
+    msa.build_block_query_lists(dims, bufs.sel, g["cu_seqlens_q"], g["cu_seqlens_k"], bufs.offsets,
+                                bufs.entries, bufs.workspace)
+    msa.attend(dims, g["q"], g["k"], g["v"], g["cu_seqlens_q"], g["cu_seqlens_k"], bufs.sel,
+               bufs.offsets, bufs.entries, bufs.out, bufs.lse, bufs.workspace)
+    torch.cuda.synchronize()
+    check_out(bufs.out.float().cpu().numpy(), ref["out"], bufs.lse.cpu().numpy(), ref["lse"],
+              "oracle-selection")
+
+
+def test_decode_equals_prefill_last_row():
+    L = 3333
+    wp = custom([L], [L], num_q_heads=16, num_kv_heads=8, head_dim=128, index_dim=128, top_k=16,
+                seed=33, qkv_std=1.0)
+    t = generate(wp, "cpu")
+    _, pre, _ = run_gpu(wp, t)
+    td = dict(t)
+    td["q"] = t["q"][L - 1:L].clone()
+    td["q_idx"] = t["q_idx"][L - 1:L].clone()
+    td["cu_seqlens_q"] = torch.tensor([0, 1], dtype=torch.int32)
+    wd = custom([L], [1], 16, 8, 128, 128, 16, 33)
+    _, dec, _ = run_gpu(wd, td)
+    assert torch.equal(dec.sel[0], pre.sel[L - 1])
+    d = (dec.out[0].float() - pre.out[L - 1].float()).abs().max().item()
+    assert d <= 1e-2, d
+
+
+def test_empty_query_set():
+    import block_sparse_long_index_amd as msa
+    dims = msa.make_dims(batch=1, num_q_heads=4, num_kv_heads=1, head_dim=64, index_dim=32, top_k=4,
+                         total_q=0, total_k=256, max_q_len=0, max_k_len=256)
+    dev = torch.device("cuda:0")
+    q = torch.zeros((0, 4, 64), dtype=torch.bfloat16, device=dev)
+    kv = torch.zeros((256, 1, 64), dtype=torch.bfloat16, device=dev)
+    qi = torch.zeros((0, 1, 32), dtype=torch.bfloat16, device=dev)
+    ki = torch.zeros((256, 32), dtype=torch.bfloat16, device=dev)
+    cuq = torch.tensor([0, 0], dtype=torch.int32, device=dev)
+    cuk = torch.tensor([0, 256], dtype=torch.int32, device=dev)
+    bufs = msa.msa_forward(dims, q, kv, kv, qi, ki, cuq, cuk)
+    torch.cuda.synchronize()
+    assert int(bufs.offsets[-1]) == 0
