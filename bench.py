@@ -1,0 +1,433 @@
+#!/usr/bin/env python3
+"""MSA hot-path benchmark on one MI355X.
+
+One step = the whole hot path on one batch of synthetic input already in HBM:
+msa_index_select -> msa_build_block_query_lists -> msa_attend, through the C
+ABI on one stream.  Prints ONE JSON line on stdout; progress goes to stderr.
+
+    python bench.py [--steps K] [--warmup W] [--workload p128k|p1m|p32k|decode|tiny]
+
+The default workload is the 128K-token single-layer prefill (64 query heads /
+8 KV heads, head dim 128, index dim 128, top-k 16 incl. the local block).
+After the timed region the oracle runs on a bounded random sample of query
+rows on the host cores: its rate is the cpu_baseline, and the same rows gate
+parity (selection bit-exact except near-ties; output within tolerance).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "MSA prefill tokens/s + Main-Branch MFMA % at 128K/1M; decode HBM GB/s"
+PEAK_BF16_FLOPS = 2.5e15      # MI355X dense bf16 MFMA
+PEAK_HBM_BYTES = 8.0e12       # MI355X HBM3E
+BLOCK = 128
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+# ---------------------------------------------------------------------------
+# algorithmic work model (what the method must touch, not what a kernel does)
+# ---------------------------------------------------------------------------
+def work_model(w) -> dict:
+    """FLOPs and bytes per step implied by the method for workload w."""
+    G, Hq, d, di, k = w.num_kv_heads, w.num_q_heads, w.head_dim, w.index_dim, w.top_k
+    hpg = Hq // G
+    idx_flops = main_flops = 0.0
+    sel_total = 0.0            # sum over (row, group) of |Sel|
+    scored_keys = 0.0          # sum over rows of 128 * beta(p)  (non-local keys)
+    kv_blocks = 0.0            # (sequence, group, block) items read once
+    dec_kidx_tokens = 0.0
+    for lq, lk in zip(w.seq_q_lens, w.seq_k_lens):
+        if lq == 0:
+            continue
+        p = np.arange(lk - lq, lk, dtype=np.int64)
+        beta = p // BLOCK
+        nsel = np.minimum(k, beta + 1)
+        J = BLOCK * (nsel - 1) + (p % BLOCK) + 1
+        idx_flops += float(G * 2 * di * BLOCK * beta.sum())
+        main_flops += float(Hq * 4 * d * J.sum())
+        sel_total += float(G * nsel.sum())
+        scored_keys += float(BLOCK * beta.sum())
+        kv_blocks += float(G * min((lk + BLOCK - 1) // BLOCK, int(nsel.sum())))
+        dec_kidx_tokens += float(BLOCK * beta.max())
+    T = w.total_q
+    q_gather = sel_total * hpg * d * 2
+    part_write = sel_total * hpg * (d * 4 + 8)
+    kv_once = kv_blocks * BLOCK * d * 2 * 2
+    attend_bytes = q_gather + part_write + kv_once
+    merge_bytes = sel_total * hpg * (d * 4 + 8) + T * Hq * (d * 2 + 4)
+    topk_bytes = scored_keys * G * 4 / BLOCK + T * G * k * 4
+    # decode: index keys of every sequence's earlier blocks, read once for all groups,
+    # plus the selected K/V blocks, Q, index queries and O
+    decode_bytes = (dec_kidx_tokens * di * 2 + sel_total * BLOCK * d * 2 * 2
+                    + T * (Hq * d * 2 * 2 + G * di * 2))
+    return dict(index_flops=idx_flops, main_flops=main_flops, sel_total=sel_total,
+                attend_bytes=attend_bytes, merge_bytes=merge_bytes, topk_bytes=topk_bytes,
+                decode_bytes=decode_bytes, kv_once_bytes=kv_once)
+
+
+# ---------------------------------------------------------------------------
+# oracle on sampled rows (host cores)
+# ---------------------------------------------------------------------------
+class _RowSubset:
+    """Rows of a larger array, addressable by their global row index."""
+
+    def __init__(self, rows, data):
+        self.index = {int(r): i for i, r in enumerate(rows)}
+        self.data = data
+        self.shape = (None,) + tuple(data.shape[1:])
+
+    def __getitem__(self, r):
+        return self.data[self.index[int(r)]]
+
+
+class _LazyDevRows:
+    """Row-sliceable view of a device tensor; copies only what is indexed."""
+
+    def __init__(self, t, lo=0, hi=None):
+        self.t, self.lo = t, lo
+        self.hi = t.shape[0] if hi is None else hi
+        self.shape = (self.hi - self.lo,) + tuple(t.shape[1:])
+
+    def __getitem__(self, idx):
+        import torch
+        if isinstance(idx, slice):
+            a, b, _ = idx.indices(self.hi - self.lo)
+            return _LazyDevRows(self.t, self.lo + a, self.lo + b)
+        rows, rest = (idx[0], idx[1:]) if isinstance(idx, tuple) else (idx, ())
+        if isinstance(rows, (int, np.integer)):
+            x = self.t[self.lo + int(rows)]
+            x = x[int(rest[0])] if rest else x
+        else:
+            r = torch.as_tensor(np.asarray(rows, dtype=np.int64) + self.lo, device=self.t.device)
+            x = self.t.index_select(0, r)
+            x = x[:, int(rest[0])] if rest else x
+        return x.double().cpu().numpy()
+
+
+_W = {}   # per-worker cache: attached shared arrays and the oracle problem
+
+
+def _oracle_task(job):
+    """Worker: oracle rows on inputs held in shared memory."""
+    from multiprocessing import resource_tracker, shared_memory
+
+    from threadpoolctl import threadpool_limits
+
+    from oracle import msa_oracle as O
+    spec, rows = job
+    if _W.get("id") != spec["id"]:
+        arrs = {}
+        shms = []
+        for name, (shm_name, shape, dtype) in spec["arrays"].items():
+            shm = shared_memory.SharedMemory(name=shm_name)
+            try:
+                resource_tracker.unregister(shm._name, "shared_memory")
+            except Exception:
+                pass
+            shms.append(shm)
+            arrs[name] = np.ndarray(shape, dtype=dtype, buffer=shm.buf)
+        q = _RowSubset(spec["rows"], arrs["q"])
+        qi = _RowSubset(spec["rows"], arrs["q_idx"])
+        _W.clear()
+        _W.update(id=spec["id"], shms=shms,
+                  P=O.Problem(q, arrs["k"], arrs["v"], qi, arrs["k_idx"], arrs["cu_q"], arrs["cu_k"],
+                              spec["top_k"]))
+    P = _W["P"]
+    out = []
+    with threadpool_limits(limits=1):
+        for r in rows:
+            out.append((int(r), P.row(int(r), want_scores=True)))
+    return out
+
+
+class OraclePool:
+    """Worker processes forked before the GPU is touched; inputs reach them
+    through shared memory, so no worker inherits GPU state."""
+
+    def __init__(self, workers):
+        import multiprocessing as mp
+        self.workers = workers
+        self.pool = mp.get_context("fork").Pool(workers) if workers > 1 else None
+        self.shms = []
+
+    def share(self, arrays):
+        from multiprocessing import shared_memory
+        spec = {}
+        for name, a in arrays.items():
+            a = np.ascontiguousarray(a)
+            shm = shared_memory.SharedMemory(create=True, size=max(1, a.nbytes))
+            np.ndarray(a.shape, dtype=a.dtype, buffer=shm.buf)[...] = a
+            self.shms.append(shm)
+            spec[name] = (shm.name, a.shape, a.dtype.str)
+        return spec
+
+    def run(self, spec, rows):
+        jobs = [(spec, rows[i::self.workers * 4]) for i in range(self.workers * 4)]
+        jobs = [j for j in jobs if len(j[1])]
+        t0 = time.perf_counter()
+        parts = self.pool.map(_oracle_task, jobs) if self.pool else [_oracle_task(j) for j in jobs]
+        dt = time.perf_counter() - t0
+        return {r: x for part in parts for r, x in part}, dt
+
+    def close(self):
+        if self.pool:
+            self.pool.close()
+            self.pool.join()
+        for shm in self.shms:
+            try:
+                shm.close()
+                shm.unlink()
+            except Exception:
+                pass
+        self.shms = []
+
+
+def parity_on_rows(P, rows, ref, sel_gpu, out_gpu, lse_gpu, top_k):
+    from oracle import msa_oracle as O
+    bad = ties = 0
+    dmax = dsum = 0.0
+    n = 0
+    ref_abs_max = 0.0
+    l2d = l2r = 0.0
+    lse_max = 0.0
+    for i, r in enumerate(rows):
+        x = ref[r]
+        beta_p = int(P.pos[r]) // BLOCK
+        for g in range(P.G):
+            tie = O.near_tie(x["S"][g], beta_p, top_k)
+            ties += int(tie)
+            if not np.array_equal(sel_gpu[i, g], x["sel"][g]):
+                if not (tie and O.valid_selection(x["S"][g], beta_p, top_k, sel_gpu[i, g])):
+                    bad += 1
+        dd = np.abs(out_gpu[i] - x["out"])
+        dmax = max(dmax, float(dd.max()))
+        dsum += float(dd.sum())
+        n += dd.size
+        ref_abs_max = max(ref_abs_max, float(np.abs(x["out"]).max()))
+        l2d += float((dd ** 2).sum())
+        l2r += float((x["out"] ** 2).sum())
+        lse_max = max(lse_max, float(np.abs(lse_gpu[i] - x["lse"]).max()))
+    mean = dsum / max(n, 1)
+    rel2 = math.sqrt(l2d / max(l2r, 1e-300))
+    relmax = dmax / max(ref_abs_max, 1e-300)
+    ok = bad == 0 and dmax <= 2e-2 and mean <= 2e-3 and rel2 <= 1e-2 and relmax <= 2e-2 and lse_max <= 2e-3
+    return dict(ok=bool(ok), rows=len(rows), selection_mismatches=bad, near_ties=ties,
+                max_abs=dmax, mean_abs=mean, rel_l2=rel2, rel_max=relmax, lse_max_abs=lse_max)
+
+
+# ---------------------------------------------------------------------------
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="p128k")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="target host time of the oracle sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--q-chunk", type=int, default=0)
+    ap.add_argument("--json-out", default="")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); this build has no "
+              f"multi-GPU path. Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    from msa_inputs import workload as _wl
+    w = _wl(args.workload)
+    cores = min(16, len(os.sched_getaffinity(0)))
+    host_bytes = w.total_k * w.num_kv_heads * w.head_dim * 4 * 2 + w.total_k * w.index_dim * 4
+    pooled = (not args.no_cpu_baseline) and host_bytes <= (16 << 30) and cores > 1
+    pool = OraclePool(cores) if pooled else None   # forked before any GPU call
+
+    import torch
+
+    import block_sparse_long_index_amd as msa
+    from msa_inputs import generate
+
+    dev = torch.device("cuda:0")
+    log(f"[bench] workload {w.name}: {w.note}; generating inputs on {dev}")
+    t0 = time.perf_counter()
+    t = generate(w, dev)
+    torch.cuda.synchronize()
+    log(f"[bench] inputs ready in {time.perf_counter() - t0:.1f}s")
+    dims = msa.dims_for(w, q_chunk=args.q_chunk)
+    bufs = msa.Buffers(dims, dev, want_scores=False, want_lse=True)
+    log(f"[bench] workspace {bufs.workspace.numel() / 2**30:.2f} GiB")
+
+    def step():
+        msa.msa_forward(dims, t["q"], t["k"], t["v"], t["q_idx"], t["k_idx"], t["cu_seqlens_q"],
+                        t["cu_seqlens_k"], bufs)
+
+    for i in range(args.warmup):
+        step()
+        torch.cuda.synchronize()
+        log(f"[bench] warmup {i + 1}/{args.warmup} done")
+
+    msa.profile_collect()             # drop anything recorded before
+    msa.profile_enable(True)
+    torch.cuda.synchronize()
+    ts = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    te = time.perf_counter()
+    msa.profile_enable(False)
+    prof = msa.profile_collect()
+    ms_per_step = (te - ts) * 1e3 / args.steps
+    log(f"[bench] timed {args.steps} steps: {ms_per_step:.3f} ms/step")
+
+    wm = work_model(w)
+    stage = {}
+    for name, (ms, n) in prof.items():
+        if n:
+            stage[name] = dict(ms_per_step=ms / args.steps, launches_per_step=n / args.steps,
+                               ms_per_launch=ms / n)
+    per_step = {k_: v["ms_per_step"] for k_, v in stage.items()}
+    log("[bench] stages (ms/step): " + ", ".join(f"{k_} {v:.3f}" for k_, v in per_step.items()))
+
+    def roof(name):
+        s = stage.get(name)
+        if not s:
+            return None
+        sec = s["ms_per_step"] / 1e3
+        if name in ("index_score_prefill",):
+            a = wm["index_flops"] / sec
+            return dict(bound="mfma", achieved=a / 1e12, peak=PEAK_BF16_FLOPS / 1e12, unit="TFLOP/s",
+                        frac=a / PEAK_BF16_FLOPS, traffic=None)
+        bytes_ = {"attend_blocks": wm["attend_bytes"], "merge_partials": wm["merge_bytes"],
+                  "topk_select": wm["topk_bytes"],
+                  "index_score_decode": wm["decode_bytes"] - wm["sel_total"] * BLOCK * w.head_dim * 4}
+        if name in bytes_:
+            a = bytes_[name] / sec
+            return dict(bound="hbm", achieved=a / 1e9, peak=PEAK_HBM_BYTES / 1e9, unit="GB/s",
+                        frac=a / PEAK_HBM_BYTES, traffic=None)
+        return None
+
+    dominant = max(per_step, key=per_step.get) if per_step else None
+    kernels = {k_: dict(stage[k_], roofline=roof(k_)) for k_ in stage}
+    t_main = (per_step.get("attend_blocks", 0.0) + per_step.get("merge_partials", 0.0)) / 1e3
+    main_mfma_frac = wm["main_flops"] / (t_main * PEAK_BF16_FLOPS) if t_main > 0 else None
+    decode = w.name == "decode"
+    value = w.total_q / (ms_per_step / 1e3)
+    extra = {}
+    if decode:
+        gbs = wm["decode_bytes"] / (ms_per_step / 1e3) / 1e9
+        extra["decode_hbm_GBps"] = gbs
+        extra["decode_hbm_frac"] = gbs * 1e9 / PEAK_HBM_BYTES
+
+    # ---- oracle sample: parity gate + cpu baseline --------------------------------
+    cpu = None
+    parity = None
+    if not args.no_cpu_baseline:
+        from oracle import msa_oracle as O
+        rng = np.random.Generator(np.random.PCG64(12345))
+        cuq = t["cu_seqlens_q"].cpu().numpy()
+        cuk = t["cu_seqlens_k"].cpu().numpy()
+        if pooled:
+            kk = t["k"].float().cpu().numpy()
+            vv = t["v"].float().cpu().numpy()
+            kidx = t["k_idx"].float().cpu().numpy()
+        else:
+            kk, vv = _LazyDevRows(t["k"]), _LazyDevRows(t["v"])
+            kidx = t["k_idx"].float().cpu().numpy()
+
+        def host_rows(rows):
+            ridx = torch.as_tensor(rows, device=dev, dtype=torch.long)
+            return (t["q"].index_select(0, ridx).float().cpu().numpy(),
+                    t["q_idx"].index_select(0, ridx).float().cpu().numpy())
+
+        # per-row cost on one core, then a sample sized to the time target
+        pilot = sorted(set(int(x) for x in rng.integers(0, w.total_q, size=min(6, w.total_q))))
+        qh, qih = host_rows(pilot)
+        Pp = O.Problem(_RowSubset(pilot, qh), kk, vv, _RowSubset(pilot, qih), kidx, cuq, cuk, w.top_k)
+        tp0 = time.perf_counter()
+        for r in pilot:
+            Pp.row(r)
+        per_row = (time.perf_counter() - tp0) / len(pilot)
+        used = cores if pooled else 1
+        n_rows = int(max(16, min(w.total_q, args.cpu_seconds * used / max(per_row, 1e-6))))
+        rows = sorted(set(int(x) for x in rng.integers(0, w.total_q, size=n_rows)))
+        log(f"[bench] oracle: {per_row * 1e3:.1f} ms/row on one core; sampling {len(rows)} rows "
+            f"on {used} worker(s)")
+        qh, qih = host_rows(rows)
+        P = O.Problem(_RowSubset(rows, qh), kk, vv, _RowSubset(rows, qih), kidx, cuq, cuk, w.top_k)
+        if pooled:
+            spec = dict(id=1, rows=rows, top_k=w.top_k,
+                        arrays=pool.share(dict(q=qh, q_idx=qih, k=kk, v=vv, k_idx=kidx,
+                                               cu_q=cuq, cu_k=cuk)))
+            ref, dt = pool.run(spec, rows)
+            pool.close()
+        else:
+            t1 = time.perf_counter()
+            ref = {r: P.row(r, want_scores=True) for r in rows}
+            dt = time.perf_counter() - t1
+        log(f"[bench] oracle sample done in {dt:.1f}s")
+        ridx = torch.as_tensor(rows, device=dev, dtype=torch.long)
+        sel_g = bufs.sel.index_select(0, ridx).cpu().numpy()
+        out_g = bufs.out.index_select(0, ridx).float().cpu().numpy()
+        lse_g = bufs.lse.index_select(0, ridx).cpu().numpy()
+        parity = parity_on_rows(P, rows, ref, sel_g, out_g, lse_g, w.top_k)
+        log(f"[bench] parity on sampled rows: {parity}")
+        cpu = dict(value=len(rows) / dt, unit="tokens/s", cores=used, kind="oracle",
+                   sample=f"{len(rows)} uniformly random query rows of {w.name}, each through the "
+                          f"full Index and Main Branch in fp64 numpy; {used} worker process(es), "
+                          f"1 BLAS thread each; {dt:.1f} s")
+    elif pool:
+        pool.close()
+
+    line = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "tokens/s" if not decode else "tokens/s (new tokens)",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "seq_k_lens": (w.seq_k_lens if len(w.seq_k_lens) <= 4 else
+                                                       f"{len(w.seq_k_lens)} seqs, total {w.total_k}"),
+                   "total_q": w.total_q, "num_q_heads": w.num_q_heads,
+                   "num_kv_heads": w.num_kv_heads, "head_dim": w.head_dim,
+                   "index_dim": w.index_dim, "block": BLOCK, "top_k": w.top_k,
+                   "q_chunk": args.q_chunk, "parallelism": "single GPU"},
+        "roofline": roof(dominant) if dominant else None,
+        "dominant_kernel": dominant,
+        "main_branch_mfma_frac": main_mfma_frac,
+        "cpu_baseline": cpu,
+        "parity": parity,
+        "kernels": kernels,
+        "work": {k_: v for k_, v in wm.items()},
+        **extra,
+    }
+    s = json.dumps(line)
+    print(s, flush=True)
+    if args.json_out:
+        with open(args.json_out, "w") as f:
+            f.write(s + "\n")
+    if parity is not None and not parity["ok"]:
+        log("[bench] PARITY FAILED on sampled rows")
+        sys.exit(1)
+
+
+if __name__ == "__main__":
+    main()

@@ -71,6 +71,12 @@ def load_library(path: str = LIB_PATH):
     lib.msa_build_block_query_lists.argtypes = [DP, P, P, P, P, P, P, SZ, P]
     lib.msa_attend.restype = I32
     lib.msa_attend.argtypes = [DP, P, P, P, P, P, P, P, P, P, P, P, SZ, P]
+    lib.msa_profile_enable.restype = I32
+    lib.msa_profile_enable.argtypes = [I32]
+    lib.msa_profile_collect.restype = I32
+    lib.msa_profile_collect.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.POINTER(I32)]
+    lib.msa_profile_kernel_name.restype = ctypes.c_char_p
+    lib.msa_profile_kernel_name.argtypes = [I32]
     _lib = lib
     return lib
 
@@ -228,6 +234,25 @@ def msa_forward(dims: Dims, q, k, v, q_idx, k_idx, cu_seqlens_q, cu_seqlens_k, b
     attend(dims, q, k, v, cu_seqlens_q, cu_seqlens_k, bufs.sel, bufs.offsets, bufs.entries,
            bufs.out, bufs.lse, bufs.workspace, stream)
     return bufs
+
+
+PROFILE_KERNELS = 6
+
+
+def profile_enable(on: bool = True):
+    """Bracket every kernel stage with hipEvents on its launch stream."""
+    _check(load_library().msa_profile_enable(1 if on else 0), "msa_profile_enable")
+
+
+def profile_collect() -> dict:
+    """{stage name: (total ms, launches)} of the stages recorded since the last
+    collect; waits for the recorded events."""
+    lib = load_library()
+    ms = (ctypes.c_float * PROFILE_KERNELS)()
+    n = (ctypes.c_int32 * PROFILE_KERNELS)()
+    _check(lib.msa_profile_collect(ms, n), "msa_profile_collect")
+    return {lib.msa_profile_kernel_name(i).decode(): (float(ms[i]), int(n[i]))
+            for i in range(PROFILE_KERNELS)}
 
 
 def dims_for(workload_like, q_chunk=0, softmax_scale=0.0) -> Dims:

@@ -5,7 +5,10 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <atomic>
+#include <mutex>
 #include <string>
+#include <vector>
 
 #include "msa.h"
 #include "msa_common.h"
@@ -128,6 +131,49 @@ size_t ws_attend(const msa_dims_t* d, const Derived& x) {
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
+// --- opt-in per-launch timing: each launcher call is bracketed by two hipEvents
+// recorded on the launch stream; msa_profile_collect() waits for them.
+enum KernelId { K_INDEX_PREFILL, K_INDEX_DECODE, K_TOPK, K_LISTS, K_ATTEND, K_MERGE };
+const char* const kKernelNames[MSA_PROFILE_KERNELS] = {
+    "index_score_prefill", "index_score_decode", "topk_select",
+    "build_lists", "attend_blocks", "merge_partials"};
+
+std::atomic<bool> g_prof_on{false};
+std::mutex g_prof_mu;
+struct ProfRec { int kid; hipEvent_t a, b; };
+std::vector<ProfRec> g_prof_pending;
+std::vector<hipEvent_t> g_event_pool;
+
+hipEvent_t pool_get() {
+  if (!g_event_pool.empty()) {
+    hipEvent_t e = g_event_pool.back();
+    g_event_pool.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+
+struct ProfScope {
+  int kid;
+  hipStream_t st;
+  hipEvent_t a = nullptr, b = nullptr;
+  ProfScope(int k, hipStream_t s) : kid(k), st(s) {
+    if (!g_prof_on.load(std::memory_order_relaxed)) return;
+    std::lock_guard<std::mutex> lk(g_prof_mu);
+    a = pool_get();
+    b = pool_get();
+    if (a && b) (void)hipEventRecord(a, st);
+  }
+  ~ProfScope() {
+    if (!a || !b) return;
+    (void)hipEventRecord(b, st);
+    std::lock_guard<std::mutex> lk(g_prof_mu);
+    g_prof_pending.push_back({kid, a, b});
+  }
+};
+
 msa_status_t hip_fail(hipError_t e) {
   g_last_error = std::string("HIP: ") + hipGetErrorString(e);
   return MSA_ERR_HIP;
@@ -190,13 +236,17 @@ msa_status_t msa_index_select(const msa_dims_t* dims, const void* q_idx, const v
     const int a = (int)r0, z = (int)std::min<long long>(x.total_q, r0 + chunk);
     const long long ld = (long long)(z - a) * x.G;
     hipError_t e;
-    if (x.decode_path)
+    if (x.decode_path) {
+      ProfScope ps(K_INDEX_DECODE, st);
       e = msa::launch_index_score_decode(q_idx, k_idx, cu_seqlens_q, cu_seqlens_k, dims->batch, x.G,
                                          x.DI, x.nb_max, a, z, S, ld, st);
-    else
+    } else {
+      ProfScope ps(K_INDEX_PREFILL, st);
       e = msa::launch_index_score_prefill(q_idx, k_idx, cu_seqlens_q, cu_seqlens_k, dims->batch,
                                           x.G, x.DI, dims->max_q_len, a, z, S, ld, st);
+    }
     if (e != hipSuccess) return hip_fail(e);
+    ProfScope ps(K_TOPK, st);
     e = msa::launch_topk_select(S, ld, a, z, cu_seqlens_q, cu_seqlens_k, dims->batch, x.G, x.top_k,
                                 wide, sel, sel_score, st);
     if (e != hipSuccess) return hip_fail(e);
@@ -220,6 +270,7 @@ msa_status_t msa_build_block_query_lists(const msa_dims_t* dims, const int32_t* 
   if (workspace_bytes < ws_lists(dims, x))
     return fail(MSA_ERR_WORKSPACE_TOO_SMALL, "build_lists workspace too small");
   void* ws = (void*)(((uintptr_t)workspace + 255) & ~(uintptr_t)255);
+  ProfScope ps(K_LISTS, (hipStream_t)stream);
   hipError_t e = msa::launch_build_lists(sel, cu_seqlens_q, cu_seqlens_k, dims->batch, x.G, x.top_k,
                                          x.nqt_max, x.nb_max, block_offsets, block_entries, ws,
                                          (hipStream_t)stream);
@@ -252,15 +303,60 @@ msa_status_t msa_attend(const msa_dims_t* dims, const void* q, const void* k, co
   const float scale_log2 = x.scale * 1.44269504088896340736f;
   for (long long r0 = 0; r0 < x.total_q; r0 += chunk) {
     const int a = (int)r0, z = (int)std::min<long long>(x.total_q, r0 + chunk);
-    hipError_t e = msa::launch_attend_blocks(x.D, x.hpg, q, k, v, cu_seqlens_q, cu_seqlens_k,
+    hipError_t e;
+    {
+      ProfScope ps(K_ATTEND, st);
+      e = msa::launch_attend_blocks(x.D, x.hpg, q, k, v, cu_seqlens_q, cu_seqlens_k,
                                              dims->batch, x.G, x.Hq, x.top_k, x.nb_max,
                                              block_offsets, block_entries, a, z, scale_log2,
                                              part_acc, part_ml, st);
+    }
     if (e != hipSuccess) return hip_fail(e);
+    ProfScope ps(K_MERGE, st);
     e = msa::launch_merge(x.D, part_acc, part_ml, sel, a, z, x.Hq, x.G, x.top_k, out, lse, st);
     if (e != hipSuccess) return hip_fail(e);
   }
   return MSA_OK;
+}
+
+msa_status_t msa_profile_enable(int32_t enable) {
+  g_prof_on.store(enable != 0);
+  return MSA_OK;
+}
+
+msa_status_t msa_profile_collect(float* total_ms, int32_t* launches) {
+  if (!total_ms || !launches) return fail(MSA_ERR_NULL_ARG, "profile output is NULL");
+  for (int i = 0; i < MSA_PROFILE_KERNELS; ++i) {
+    total_ms[i] = 0.f;
+    launches[i] = 0;
+  }
+  std::vector<ProfRec> recs;
+  {
+    std::lock_guard<std::mutex> lk(g_prof_mu);
+    recs.swap(g_prof_pending);
+  }
+  msa_status_t st = MSA_OK;
+  for (const ProfRec& r : recs) {
+    float ms = 0.f;
+    hipError_t e = hipEventSynchronize(r.b);
+    if (e == hipSuccess) e = hipEventElapsedTime(&ms, r.a, r.b);
+    if (e != hipSuccess) {
+      st = hip_fail(e);
+    } else {
+      total_ms[r.kid] += ms;
+      launches[r.kid] += 1;
+    }
+  }
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  for (const ProfRec& r : recs) {
+    g_event_pool.push_back(r.a);
+    g_event_pool.push_back(r.b);
+  }
+  return st;
+}
+
+const char* msa_profile_kernel_name(int32_t id) {
+  return (id >= 0 && id < MSA_PROFILE_KERNELS) ? kKernelNames[id] : "";
 }
 
 }  // extern "C"

@@ -30,6 +30,8 @@
  *   enqueued on `stream` (a hipStream_t; NULL = the default stream) with no
  *   host synchronisation; buffers must stay alive until the stream has passed
  *   the call.  Outputs are bitwise deterministic for identical inputs.
+ * - No queries (total_q == 0): msa_index_select and msa_attend enqueue
+ *   nothing; msa_build_block_query_lists still writes all-zero offsets.
  * - Errors: every argument is validated on the host before anything is
  *   launched; a call that returns an error has enqueued nothing.  A failed
  *   HIP launch returns MSA_ERR_HIP (msa_last_error() gives HIP's message).
@@ -172,6 +174,22 @@ const char* msa_last_error(void);
 
 /* MSA_ABI_VERSION of the loaded library. */
 int32_t msa_abi_version(void);
+
+/*
+ * Per-kernel timing, a measuring aid (not part of the pages' method).  While
+ * enabled, every kernel stage a call launches is bracketed by two hipEvents
+ * recorded on the call's stream.  Stage ids: 0 index_score_prefill,
+ * 1 index_score_decode, 2 topk_select, 3 build_lists (all list kernels),
+ * 4 attend_blocks, 5 merge_partials.  msa_profile_collect() waits for every
+ * recorded event (it blocks the host), writes the summed milliseconds and the
+ * launch count per stage into caller arrays of MSA_PROFILE_KERNELS entries,
+ * and forgets the records.  Events are host-side HIP objects kept in a pool
+ * for the life of the process; no device memory is allocated.
+ */
+#define MSA_PROFILE_KERNELS 6
+msa_status_t msa_profile_enable(int32_t enable);
+msa_status_t msa_profile_collect(float* total_ms, int32_t* launches);
+const char* msa_profile_kernel_name(int32_t id);
 
 #ifdef __cplusplus
 }

@@ -116,3 +116,13 @@ def check_out(gpu_out, ref_out, gpu_lse=None, ref_lse=None, what=""):
         dl = float(np.abs(gpu_lse - ref_lse).max())
         log(f"{what}: max|d lse| {dl:.3e}")
         assert dl <= LSE_ABS
+
+
+def run_gpu_inputs(w, t, q_chunk=0, want_scores=True):
+    """Forward on inputs already on the GPU (full-size workloads)."""
+    dims = msa.dims_for(w, q_chunk=q_chunk)
+    bufs = msa.Buffers(dims, t["q"].device, want_scores=want_scores)
+    msa.msa_forward(dims, t["q"], t["k"], t["v"], t["q_idx"], t["k_idx"], t["cu_seqlens_q"],
+                    t["cu_seqlens_k"], bufs)
+    torch.cuda.synchronize()
+    return dims, bufs
