@@ -18,6 +18,8 @@
 //     m = max, P = 2^(z - m), l = sum P  (z in log2 units: scale * log2(e))
 //     O = P * V                          (P cast to bf16, fp32 accumulate)
 // and writes the unnormalised partial (m, l, O) of every (query, head, slot).
+// Partials are laid out [query][group][slot][head-in-group][d], so the
+// heads of one (query, slot) form one contiguous run of HPG * D floats.
 //
 // merge_partials_kernel: per (query, head) the log-sum-exp merge of its
 // partials -- M = max m_s, L = sum l_s 2^(m_s - M),
@@ -27,17 +29,74 @@
 
 namespace msa {
 
+// One 32-row tile's queries: the Q fragments (MFMA B operand, lane <-> query
+// row), the destination partial row (-1 for padding) and the query position.
 template <int D, int HPG>
-__global__ __launch_bounds__(256) void attend_blocks_kernel(
+struct TileQ {
+  static constexpr int KS = D / 16;
+  bf16x8 qf[KS];
+  int drow;   // (((r - r0) * G + g) * top_k + slot) * HPG + head-in-group; spare row if padding
+  int p;      // query position (for the causal mask)
+  bool ok;
+
+  // `ent` is the tile's list entry for this lane's query (-1: none).  Every
+  // load is issued unconditionally (padding lanes read row 0 and zero it),
+  // so the compiler can count outstanding memory operations exactly.
+  __device__ inline void load(const uint16_t* __restrict__ q, int ent, int r0, int r1, int top_k,
+                              int Hq, int G, int g, int hl, int half, int pshift, int spare_row) {
+    const int r = ent >> kEntrySlotBits, slot = ent & ((1 << kEntrySlotBits) - 1);
+    ok = ent >= 0 && r >= r0 && r < r1 && slot < top_k;
+    drow = ok ? ((((r - r0) * G + g) * top_k + slot) * HPG + hl) : spare_row;
+    p = ok ? r + pshift : 0x7fffffff;
+    const uint16_t* qs = q + ((size_t)(ok ? r : 0) * Hq + g * HPG + hl) * D + half * 8;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      uint4 x = *reinterpret_cast<const uint4*>(qs + ks * 16);
+      x = ok ? x : make_uint4(0, 0, 0, 0);
+      qf[ks] = as_bf16x8(x);
+    }
+  }
+};
+
+// list entry of position e of this item's range [.., e1), or -1 past its end
+// (the load is clamped into the range so it is always issued)
+__device__ inline int tile_entry(const int32_t* __restrict__ entries, int e, int e1) {
+  const int v = entries[min(e, e1 - 1)];
+  return e < e1 ? v : -1;
+}
+
+// First index in [lo, hi) of a sorted int array whose value is >= key, found
+// by one wave with 64-way splitting (a few dependent loads instead of log2 n).
+__device__ inline int wave_lower_bound(const int32_t* __restrict__ a, int lo, int hi, int key,
+                                       int lane) {
+  while (hi - lo > 64) {
+    const int span = hi - lo;
+    const int pos = lo + (int)(((long long)span * lane) >> 6);
+    const bool below = a[pos] < key;
+    const unsigned long long m = __ballot(below);
+    const int nb = __popcll(m);             // samples below the key (a prefix of the lanes)
+    const int nlo = nb == 0 ? lo : lo + (int)(((long long)span * (nb - 1)) >> 6) + 1;
+    const int nhi = nb == 64 ? hi : lo + (int)(((long long)span * nb) >> 6);
+    lo = nlo;
+    hi = max(nhi, nlo);
+  }
+  const int pos = lo + lane;
+  const bool below = pos < hi && a[pos] < key;
+  return lo + __popcll(__ballot(below));
+}
+
+template <int D, int HPG>
+__global__ __launch_bounds__(256, 2) void attend_blocks_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const int32_t* __restrict__ cu_q, const int32_t* __restrict__ cu_k, int batch, int G, int Hq,
     int top_k, int nb_max, const int32_t* __restrict__ offsets, const int32_t* __restrict__ entries,
-    int r0, int r1, float scale_log2, float* __restrict__ part_acc, float2* __restrict__ part_ml) {
+    int r0, int r1, int total_q, float scale_log2, float* __restrict__ part_acc,
+    float2* __restrict__ part_ml, int spare_row) {
   constexpr int QPT = 32 / HPG;   // queries per 32-row tile
   constexpr int KS = D / 16;      // k-steps of Q.K over the head dim
-  constexpr int DT = D / 32;      // 32-wide output column tiles
+  constexpr int DT = D / 32;      // 32-row tiles of the transposed output
   constexpr int LDK = D + 8;
-  constexpr int LDV = kBlock + 8;
+  constexpr int LDV = kBlock + 4;   // 66-dword rows: 8-byte reads of 16 rows hit distinct banks
   __shared__ __attribute__((aligned(16))) uint16_t Ks[kBlock * LDK];
   __shared__ __attribute__((aligned(16))) uint16_t Vt[D * LDV];
   __shared__ int range[2];
@@ -51,151 +110,180 @@ __global__ __launch_bounds__(256) void attend_blocks_kernel(
   if (beta * kBlock >= lk) return;
   const size_t u = (size_t)bg * nb_max + beta;
   const int tid = threadIdx.x;
-  if (tid == 0) {
-    int lo = offsets[u], hi = offsets[u + 1];
-    const int keys[2] = {r0 << kEntrySlotBits, r1 << kEntrySlotBits};
-    int a = lo;
-    for (int w = 0; w < 2; ++w) {
-      int l2 = a, h2 = hi;
-      while (l2 < h2) {
-        int mid = (l2 + h2) >> 1;
-        if (entries[mid] < keys[w]) l2 = mid + 1; else h2 = mid;
-      }
-      range[w] = l2;
-      a = l2;
+  if (tid < 64) {
+    // this pass's rows [r0, r1) are a contiguous run of the ascending list
+    const int lo = offsets[u], hi = offsets[u + 1];
+    const int a = (r0 == 0) ? lo : wave_lower_bound(entries, lo, hi, r0 << kEntrySlotBits, tid);
+    const int z = (r1 >= total_q) ? hi : wave_lower_bound(entries, a, hi, r1 << kEntrySlotBits, tid);
+    if (tid == 0) {
+      range[0] = a;
+      range[1] = z;
     }
   }
   __syncthreads();
   const int e0 = range[0], e1 = range[1];
   if (e0 >= e1) return;
 
-  // stage the block: K as [key][d], V as [d][key]; keys past the sequence are zero
-  const int kb = beta * kBlock;
-  for (int c = tid; c < kBlock * D / 8; c += 256) {
-    int key = c / (D / 8), dc = c % (D / 8);
-    uint4 kv = make_uint4(0, 0, 0, 0), vv = make_uint4(0, 0, 0, 0);
-    if (kb + key < lk) {
-      size_t src = ((size_t)(koff + kb + key) * G + g) * D + dc * 8;
-      kv = *reinterpret_cast<const uint4*>(k + src);
-      vv = *reinterpret_cast<const uint4*>(v + src);
-    }
-    *reinterpret_cast<uint4*>(Ks + key * LDK + dc * 8) = kv;
-    const uint16_t* ve = reinterpret_cast<const uint16_t*>(&vv);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) Vt[(dc * 8 + i) * LDV + key] = ve[i];
-  }
-  __syncthreads();
-
   const int wave = tid >> 6, lane = tid & 63, col = lane & 31, half = lane >> 5;
   const int qi = col / HPG, hl = col % HPG;
   const int ntiles = (e1 - e0 + QPT - 1) / QPT;
   const int pshift = lk - lq - qoff;   // position of global row r is r + pshift
 
-  for (int t = wave; t < ntiles; t += 4) {
-    const int e = e0 + t * QPT + qi;
-    const bool valid = e < e1;
-    const int ent = valid ? entries[e] : 0;
-    const int r = ent >> kEntrySlotBits, slot = ent & ((1 << kEntrySlotBits) - 1);
-    const bool ok = valid && r >= r0 && r < r1 && slot < top_k;
-    const int p = ok ? r + pshift : 0x7fffffff;
+  // Software pipeline over this wave's tiles t = wave, wave + 4, ...: list
+  // entries two tiles ahead and Q one tile ahead, ping-ponging two tile
+  // buffers; every load is issued before the current tile's stores (stores
+  // share the memory counter on this GPU, so a load issued after them could
+  // not be waited for on its own).
+  TileQ<D, HPG> A, B;
+  A.load(q, tile_entry(entries, e0 + wave * QPT + qi, e1), r0, r1, top_k, Hq, G, g, hl, half,
+         pshift, spare_row);
+  int ent_next = tile_entry(entries, e0 + (wave + 4) * QPT + qi, e1);
 
-    bf16x8 qf[KS];
-    {
-      const uint16_t* qs = q + ((size_t)(ok ? r : 0) * Hq + g * HPG + hl) * D + half * 8;
+  // stage the block: K as [key][d], V as [d][key]; keys past the sequence are zero.
+  // K: consecutive threads take consecutive 16-byte chunks of a key row.
+  // V: consecutive threads take consecutive keys, so the transposed 2-byte LDS
+  //    writes of a wave land on consecutive addresses.
+  const int kb = beta * kBlock;
+  for (int c = tid; c < kBlock * D / 8; c += 256) {
+    const int key = c / (D / 8), dc = c % (D / 8);
+    uint4 kv = make_uint4(0, 0, 0, 0);
+    if (kb + key < lk) kv = *reinterpret_cast<const uint4*>(k + ((size_t)(koff + kb + key) * G + g) * D + dc * 8);
+    *reinterpret_cast<uint4*>(Ks + key * LDK + dc * 8) = kv;
+  }
+  for (int c = tid; c < kBlock * D / 8; c += 256) {
+    const int key = c % kBlock, dc = c / kBlock;
+    uint4 vv = make_uint4(0, 0, 0, 0);
+    if (kb + key < lk) vv = *reinterpret_cast<const uint4*>(v + ((size_t)(koff + kb + key) * G + g) * D + dc * 8);
+    const uint32_t vw[4] = {vv.x, vv.y, vv.z, vv.w};
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        uint4 x = make_uint4(0, 0, 0, 0);
-        if (ok) x = *reinterpret_cast<const uint4*>(qs + ks * 16);
-        qf[ks] = as_bf16x8(x);
-      }
-    }
+    for (int i = 0; i < 8; ++i)
+      Vt[(dc * 8 + i) * LDV + key] = (uint16_t)(vw[i >> 1] >> (16 * (i & 1)));
+  }
+  __syncthreads();
 
+
+  auto tile = [&](const TileQ<D, HPG>& T) __attribute__((always_inline)) {
+    // The block's K/V fragments do not change across tiles; an opaque zero
+    // offset keeps their LDS reads inside the loop instead of letting the
+    // compiler hoist all of them into (spilled) registers.
+    int lo = 0;
+    asm volatile("" : "+v"(lo));
+    const uint16_t* Kl = Ks + lo;
+    const uint16_t* Vl = Vt + lo;
+    // S^T = K * Q^T: lane <-> query row, registers <-> keys
     f32x16 sacc[4];
 #pragma unroll
     for (int kt = 0; kt < 4; ++kt) {
       sacc[kt] = f32x16{};
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        bf16x8 a = as_bf16x8(*reinterpret_cast<const uint4*>(Ks + (kt * 32 + col) * LDK + ks * 16 + half * 8));
-        sacc[kt] = mfma32(a, qf[ks], sacc[kt]);
+        bf16x8 a = as_bf16x8(*reinterpret_cast<const uint4*>(Kl + (kt * 32 + col) * LDK + ks * 16 + half * 8));
+        sacc[kt] = mfma32(a, T.qf[ks], sacc[kt]);
       }
     }
+    const int drow = T.drow, p = T.p;
 
-    // softmax over this block's keys for the lane's query row
+    // softmax over this block's keys for the lane's query row, in log2 units:
+    // m = c * max(s), P = 2^(c*s - m) with c = scale * log2(e) > 0
     const bool partial = kb + kBlock - 1 > p;   // some keys lie after the query
-    float m = -INFINITY;
+    if (partial) {
+      // key kb + kt*32 + 8(i/4) + 4half + i%4 is after the query when its
+      // constant part exceeds p - kb - 4half
+      const int pr = p - kb - 4 * half;
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+          if (kt * 32 + 8 * (i >> 2) + (i & 3) > pr) sacc[kt][i] = -INFINITY;
+    }
+    float mr = sacc[0][0];
 #pragma unroll
     for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        float z = sacc[kt][i] * scale_log2;
-        if (partial) {
-          int key = kb + kt * 32 + 8 * (i >> 2) + 4 * half + (i & 3);
-          if (key > p) z = -INFINITY;
-        }
-        sacc[kt][i] = z;
-        m = fmaxf(m, z);
-      }
-    m = fmaxf(m, shfl_xor_f(m, 32));
-    const float msafe = (m == -INFINITY) ? 0.f : m;
+      for (int i = 0; i < 16; ++i) mr = fmaxf(mr, sacc[kt][i]);
+    mr = fmaxf(mr, shfl_xor_f(mr, 32));
+    const float m = mr * scale_log2;
+    const float nm = (mr == -INFINITY) ? 0.f : -m;
     float l = 0.f;
-#pragma unroll
-    for (int kt = 0; kt < 4; ++kt)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        float x = exp2f(sacc[kt][i] - msafe);
-        sacc[kt][i] = x;
-        l += x;
-      }
-    l += shfl_xor_f(l, 32);
-
-    f32x16 oacc[DT];
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt) oacc[dt] = f32x16{};
+    uint4 pk[8];   // P as bf16, MFMA B operand of O^T = V^T * P^T (k-step 2kt + s2)
 #pragma unroll
     for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
       for (int s2 = 0; s2 < 2; ++s2) {
-        uint4 pk;
-        pk.x = pack_bf16x2(sacc[kt][8 * s2 + 0], sacc[kt][8 * s2 + 1]);
-        pk.y = pack_bf16x2(sacc[kt][8 * s2 + 2], sacc[kt][8 * s2 + 3]);
-        pk.z = pack_bf16x2(sacc[kt][8 * s2 + 4], sacc[kt][8 * s2 + 5]);
-        pk.w = pack_bf16x2(sacc[kt][8 * s2 + 6], sacc[kt][8 * s2 + 7]);
-        const bf16x8 pa = as_bf16x8(pk);
+        float x[8];
 #pragma unroll
-        for (int dt = 0; dt < DT; ++dt) {
-          const uint16_t* vr = Vt + (dt * 32 + col) * LDV + kt * 32 + 16 * s2 + 4 * half;
-          uint2 lo = *reinterpret_cast<const uint2*>(vr);
-          uint2 hi = *reinterpret_cast<const uint2*>(vr + 8);
-          const bf16x8 vb = as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y));
-          oacc[dt] = mfma32(pa, vb, oacc[dt]);
+        for (int e = 0; e < 8; ++e) {
+          x[e] = __builtin_amdgcn_exp2f(fmaf(sacc[kt][8 * s2 + e], scale_log2, nm));
+          l += x[e];
         }
+        pk[2 * kt + s2] = make_uint4(pack2_bf16(x[0], x[1]), pack2_bf16(x[2], x[3]),
+                                     pack2_bf16(x[4], x[5]), pack2_bf16(x[6], x[7]));
       }
+    l += shfl_xor_f(l, 32);
 
-    // destination partial row of the lane's query row; -1 if none
-    const int drow = ok ? (((r - r0) * Hq + g * HPG + hl) * top_k + slot) : -1;
-    if (half == 0 && ok) part_ml[drow] = make_float2(m, l);
+    // O^T = V^T * P^T: lane <-> query row, register i <-> d = 32dt + 8(i/4) + 4half + i%4
+    f32x16 oacc[DT];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int mrow = 8 * (i >> 2) + 4 * half + (i & 3);
-      const int dm = __shfl(drow, mrow, kWave);
-      if (dm >= 0) {
-        float* dst = part_acc + (size_t)dm * D + col;
+    for (int dt = 0; dt < DT; ++dt) oacc[dt] = f32x16{};
 #pragma unroll
-        for (int dt = 0; dt < DT; ++dt) dst[dt * 32] = oacc[dt][i];
+    for (int ks = 0; ks < 8; ++ks) {
+      const bf16x8 pb = as_bf16x8(pk[ks]);
+      const int kt = ks >> 1, s2 = ks & 1;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        const uint16_t* vr = Vl + (dt * 32 + col) * LDV + kt * 32 + 16 * s2 + 4 * half;
+        uint2 lo = *reinterpret_cast<const uint2*>(vr);
+        uint2 hi = *reinterpret_cast<const uint2*>(vr + 8);
+        const bf16x8 va = as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y));
+        oacc[dt] = mfma32(va, pb, oacc[dt]);
       }
+    }
+
+    // write the partial (m, l, O) of the lane's row: 16-byte stores of 4 consecutive d
+    // (padding lanes write the spare row; stores are unconditional for the
+    // same exact-counting reason as the loads; both lane halves hold the
+    // row's m and l and write the same value)
+    {
+      part_ml[drow] = make_float2(m, l);
+      float* dst = part_acc + (size_t)drow * D + 4 * half;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          *reinterpret_cast<float4*>(dst + dt * 32 + 8 * j) =
+              make_float4(oacc[dt][4 * j], oacc[dt][4 * j + 1], oacc[dt][4 * j + 2], oacc[dt][4 * j + 3]);
+    }
+  };
+
+  for (int t = wave; t < ntiles; t += 8) {
+    {
+      const int ea = tile_entry(entries, e0 + (t + 8) * QPT + qi, e1);
+      B.load(q, ent_next, r0, r1, top_k, Hq, G, g, hl, half, pshift, spare_row);
+      ent_next = ea;
+      tile(A);
+    }
+    if (t + 4 >= ntiles) break;
+    {
+      const int ea = tile_entry(entries, e0 + (t + 12) * QPT + qi, e1);
+      A.load(q, ent_next, r0, r1, top_k, Hq, G, g, hl, half, pshift, spare_row);
+      ent_next = ea;
+      tile(B);
     }
   }
 }
 
-// one wave per (query row, head)
-template <int D>
-__global__ __launch_bounds__(256) void merge_partials_kernel(
+// One wave per (query row, head); KMAX >= top_k, so every slot load is issued
+// up front.  Eight waves per workgroup take eight consecutive heads, so a
+// workgroup reads whole (row, group) partial runs contiguously.
+constexpr int kMergeWaves = 8;
+template <int D, int KMAX>
+__global__ __launch_bounds__(kMergeWaves * 64) void merge_partials_kernel(
     const float* __restrict__ part_acc, const float2* __restrict__ part_ml,
     const int32_t* __restrict__ sel, int r0, int r1, int Hq, int G, int top_k,
     uint16_t* __restrict__ out, float* __restrict__ lse) {
   constexpr int PER = D / 64;
-  const long long w = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const long long w = (long long)blockIdx.x * kMergeWaves + wv;
   const long long n = (long long)(r1 - r0) * Hq;
   if (w >= n) return;
   const int lane = threadIdx.x & 63;
@@ -204,33 +292,53 @@ __global__ __launch_bounds__(256) void merge_partials_kernel(
   const int g = h / (Hq / G);
   const int32_t* srow = sel + ((size_t)r * G + g) * top_k;
   int ns = 0;
-  for (int s = 0; s < top_k; ++s) ns += srow[s] >= 0 ? 1 : 0;
-  const size_t base = ((size_t)rr * Hq + h) * top_k;
+#pragma unroll
+  for (int s = 0; s < KMAX; ++s)
+    if (s < top_k) ns += srow[s] >= 0 ? 1 : 0;
+  // partial rows of (row, group, slot) hold the group's heads contiguously
+  const int hpg = Hq / G;
+  const size_t base = ((size_t)rr * G + g) * top_k * hpg + (h - g * hpg);
+  float2 ml[KMAX];
+  float a[KMAX][PER];
+#pragma unroll
+  for (int s = 0; s < KMAX; ++s) {
+    ml[s] = make_float2(-INFINITY, 0.f);
+#pragma unroll
+    for (int j = 0; j < PER; ++j) a[s][j] = 0.f;
+    if (s < ns) {
+      ml[s] = part_ml[base + (size_t)s * hpg];
+      const float* src = part_acc + (base + (size_t)s * hpg) * D + lane * PER;
+      if constexpr (PER == 2) {
+        float2 x = *reinterpret_cast<const float2*>(src);
+        a[s][0] = x.x;
+        a[s][1] = x.y;
+      } else {
+        a[s][0] = src[0];
+      }
+    }
+  }
   float M = -INFINITY;
-  for (int s = 0; s < ns; ++s) M = fmaxf(M, part_ml[base + s].x);
+#pragma unroll
+  for (int s = 0; s < KMAX; ++s) M = fmaxf(M, ml[s].x);
   float L = 0.f;
   float acc[PER];
 #pragma unroll
   for (int j = 0; j < PER; ++j) acc[j] = 0.f;
-  for (int s = 0; s < ns; ++s) {
-    const float2 ml = part_ml[base + s];
-    const float wgt = exp2f(ml.x - M);
-    L += ml.y * wgt;
-    const float* src = part_acc + (base + s) * D + lane * PER;
-    if constexpr (PER == 2) {
-      float2 x = *reinterpret_cast<const float2*>(src);
-      acc[0] += wgt * x.x;
-      acc[1] += wgt * x.y;
-    } else {
-      acc[0] += wgt * src[0];
+#pragma unroll
+  for (int s = 0; s < KMAX; ++s) {
+    if (s < ns) {
+      const float wgt = exp2f(ml[s].x - M);
+      L += ml[s].y * wgt;
+#pragma unroll
+      for (int j = 0; j < PER; ++j) acc[j] += wgt * a[s][j];
     }
   }
   const float inv = 1.f / L;
   uint16_t* o = out + ((size_t)r * Hq + h) * D + lane * PER;
   if constexpr (PER == 2) {
-    *reinterpret_cast<uint32_t*>(o) = pack_bf16x2(acc[0] * inv, acc[1] * inv);
+    *reinterpret_cast<uint32_t*>(o) = pack2_bf16(acc[0] * inv, acc[1] * inv);
   } else {
-    o[0] = f32_to_bf16_bits(acc[0] * inv);
+    o[0] = __builtin_bit_cast(uint16_t, (__bf16)(acc[0] * inv));
   }
   if (lse && lane == 0) lse[(size_t)r * Hq + h] = (M + log2f(L)) * 0.69314718055994530942f;
 }
@@ -240,20 +348,23 @@ template <int D, int HPG>
 static void launch_attend_t(const void* q, const void* k, const void* v, const int32_t* cu_q,
                             const int32_t* cu_k, int batch, int G, int Hq, int top_k, int nb_max,
                             const int32_t* offsets, const int32_t* entries, int r0, int r1,
-                            float scale_log2, float* part_acc, float2* part_ml, hipStream_t st) {
+                            int total_q, float scale_log2, float* part_acc, float2* part_ml,
+                            hipStream_t st) {
   dim3 grid((unsigned)((size_t)nb_max * batch * G));
   hipLaunchKernelGGL((attend_blocks_kernel<D, HPG>), grid, dim3(256), 0, st, (const uint16_t*)q,
                      (const uint16_t*)k, (const uint16_t*)v, cu_q, cu_k, batch, G, Hq, top_k,
-                     nb_max, offsets, entries, r0, r1, scale_log2, part_acc, part_ml);
+                     nb_max, offsets, entries, r0, r1, total_q, scale_log2, part_acc, part_ml,
+                     (r1 - r0) * Hq * top_k);
 }
 
 template <int D>
 static hipError_t launch_attend_d(int hpg, const void* q, const void* k, const void* v,
                                   const int32_t* cu_q, const int32_t* cu_k, int batch, int G, int Hq,
                                   int top_k, int nb_max, const int32_t* offsets,
-                                  const int32_t* entries, int r0, int r1, float scale_log2,
-                                  float* part_acc, float2* part_ml, hipStream_t st) {
-#define MSA_ATT(H) launch_attend_t<D, H>(q, k, v, cu_q, cu_k, batch, G, Hq, top_k, nb_max, offsets, entries, r0, r1, scale_log2, part_acc, part_ml, st)
+                                  const int32_t* entries, int r0, int r1, int total_q,
+                                  float scale_log2, float* part_acc, float2* part_ml,
+                                  hipStream_t st) {
+#define MSA_ATT(H) launch_attend_t<D, H>(q, k, v, cu_q, cu_k, batch, G, Hq, top_k, nb_max, offsets, entries, r0, r1, total_q, scale_log2, part_acc, part_ml, st)
   switch (hpg) {
     case 1: MSA_ATT(1); break;
     case 2: MSA_ATT(2); break;
@@ -270,28 +381,46 @@ static hipError_t launch_attend_d(int hpg, const void* q, const void* k, const v
 hipError_t launch_attend_blocks(int D, int hpg, const void* q, const void* k, const void* v,
                                 const int32_t* cu_q, const int32_t* cu_k, int batch, int G, int Hq,
                                 int top_k, int nb_max, const int32_t* offsets,
-                                const int32_t* entries, int r0, int r1, float scale_log2,
-                                float* part_acc, float2* part_ml, hipStream_t st) {
+                                const int32_t* entries, int r0, int r1, int total_q,
+                                float scale_log2, float* part_acc, float2* part_ml, hipStream_t st) {
   if (D == 64)
     return launch_attend_d<64>(hpg, q, k, v, cu_q, cu_k, batch, G, Hq, top_k, nb_max, offsets,
-                               entries, r0, r1, scale_log2, part_acc, part_ml, st);
+                               entries, r0, r1, total_q, scale_log2, part_acc, part_ml, st);
   if (D == 128)
     return launch_attend_d<128>(hpg, q, k, v, cu_q, cu_k, batch, G, Hq, top_k, nb_max, offsets,
-                                entries, r0, r1, scale_log2, part_acc, part_ml, st);
+                                entries, r0, r1, total_q, scale_log2, part_acc, part_ml, st);
   return hipErrorInvalidValue;
+}
+
+template <int D, int KMAX>
+static void launch_merge_t(dim3 grid, const float* part_acc, const float2* part_ml, const int32_t* sel,
+                           int r0, int r1, int Hq, int G, int top_k, void* out, float* lse,
+                           hipStream_t st) {
+  hipLaunchKernelGGL((merge_partials_kernel<D, KMAX>), grid, dim3(kMergeWaves * 64), 0, st, part_acc, part_ml, sel,
+                     r0, r1, Hq, G, top_k, (uint16_t*)out, lse);
+}
+
+template <int D>
+static void launch_merge_d(dim3 grid, const float* part_acc, const float2* part_ml, const int32_t* sel,
+                           int r0, int r1, int Hq, int G, int top_k, void* out, float* lse,
+                           hipStream_t st) {
+#define MSA_MRG(K) launch_merge_t<D, K>(grid, part_acc, part_ml, sel, r0, r1, Hq, G, top_k, out, lse, st)
+  if (top_k <= 4) MSA_MRG(4);
+  else if (top_k <= 8) MSA_MRG(8);
+  else if (top_k <= 16) MSA_MRG(16);
+  else MSA_MRG(32);
+#undef MSA_MRG
 }
 
 hipError_t launch_merge(int D, const float* part_acc, const float2* part_ml, const int32_t* sel,
                         int r0, int r1, int Hq, int G, int top_k, void* out, float* lse,
                         hipStream_t st) {
   long long n = (long long)(r1 - r0) * Hq;
-  dim3 grid((unsigned)((n + 3) / 4));
+  dim3 grid((unsigned)((n + kMergeWaves - 1) / kMergeWaves));
   if (D == 64)
-    hipLaunchKernelGGL(merge_partials_kernel<64>, grid, dim3(256), 0, st, part_acc, part_ml, sel, r0,
-                       r1, Hq, G, top_k, (uint16_t*)out, lse);
+    launch_merge_d<64>(grid, part_acc, part_ml, sel, r0, r1, Hq, G, top_k, out, lse, st);
   else if (D == 128)
-    hipLaunchKernelGGL(merge_partials_kernel<128>, grid, dim3(256), 0, st, part_acc, part_ml, sel, r0,
-                       r1, Hq, G, top_k, (uint16_t*)out, lse);
+    launch_merge_d<128>(grid, part_acc, part_ml, sel, r0, r1, Hq, G, top_k, out, lse, st);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();

@@ -26,7 +26,7 @@ hipError_t launch_build_lists(const int32_t*, const int32_t*, const int32_t*, in
                               int, int32_t*, int32_t*, void*, hipStream_t);
 hipError_t launch_attend_blocks(int, int, const void*, const void*, const void*, const int32_t*,
                                 const int32_t*, int, int, int, int, int, const int32_t*,
-                                const int32_t*, int, int, float, float*, float2*, hipStream_t);
+                                const int32_t*, int, int, int, float, float*, float2*, hipStream_t);
 hipError_t launch_merge(int, const float*, const float2*, const int32_t*, int, int, int, int, int,
                         void*, float*, hipStream_t);
 }  // namespace msa
@@ -35,7 +35,7 @@ namespace {
 
 thread_local std::string g_last_error;
 
-constexpr size_t kDefaultChunkBytes = (size_t)32 << 30;   // workspace cap when q_chunk == 0
+constexpr size_t kDefaultChunkBytes = (size_t)48 << 30;   // workspace cap when q_chunk == 0
 constexpr int kMaxNbLds = 12288;                          // per-sequence blocks the LDS lists hold
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -94,17 +94,23 @@ msa_status_t check_dims(const msa_dims_t* d, Derived* out) {
   return MSA_OK;
 }
 
-long long round_chunk(long long rows, long long total) {
+// Rows per pass: an explicit q_chunk is used as given; a byte cap is turned
+// into equal passes (rounded up to 128 rows) so no pass is a small tail.
+long long round_chunk(long long rows, long long total, bool exact) {
   if (rows >= total) return total;
-  if (rows >= 128) rows -= rows % 128;
-  return rows < 1 ? 1 : rows;
+  if (rows < 1) rows = 1;
+  if (exact) return rows;
+  long long passes = (total + rows - 1) / rows;
+  long long even = (total + passes - 1) / passes;
+  long long r128 = (even + 127) / 128 * 128;
+  return r128 <= rows ? r128 : even;
 }
 
 // rows per pass of msa_index_select and the bytes of its score buffer
 long long select_chunk(const msa_dims_t* d, const Derived& x) {
   long long per_row = (long long)x.G * x.nb_max * 4;
   long long rows = d->q_chunk > 0 ? d->q_chunk : (long long)(kDefaultChunkBytes / (per_row ? per_row : 1));
-  return round_chunk(rows, x.total_q);
+  return round_chunk(rows, x.total_q, d->q_chunk > 0);
 }
 
 long long attend_chunk(const msa_dims_t* d, const Derived& x) {
@@ -113,7 +119,7 @@ long long attend_chunk(const msa_dims_t* d, const Derived& x) {
   // partial rows are indexed with int32
   long long cap = (((long long)1 << 31) - 1) / ((long long)x.Hq * x.top_k);
   if (rows > cap) rows = cap;
-  return round_chunk(rows, x.total_q);
+  return round_chunk(rows, x.total_q, d->q_chunk > 0 && d->q_chunk <= cap);
 }
 
 size_t ws_select(const msa_dims_t* d, const Derived& x) {
@@ -123,9 +129,12 @@ size_t ws_select(const msa_dims_t* d, const Derived& x) {
 size_t ws_lists(const msa_dims_t* d, const Derived& x) {
   return msa::lists_workspace_bytes(d->batch, x.G, x.nqt_max, x.nb_max) + 256;
 }
+// partial rows of one pass plus one spare row that padding lanes write to
+size_t attend_rows(const msa_dims_t* d, const Derived& x) {
+  return (size_t)attend_chunk(d, x) * x.Hq * x.top_k + 1;
+}
 size_t ws_attend(const msa_dims_t* d, const Derived& x) {
-  long long c = attend_chunk(d, x);
-  size_t rows = (size_t)c * x.Hq * x.top_k;
+  size_t rows = attend_rows(d, x);
   return align256(rows * x.D * 4) + align256(rows * 8) + 256;
 }
 
@@ -299,7 +308,7 @@ msa_status_t msa_attend(const msa_dims_t* dims, const void* q, const void* k, co
   const long long chunk = attend_chunk(dims, x);
   char* base = (char*)(((uintptr_t)workspace + 255) & ~(uintptr_t)255);
   float* part_acc = (float*)base;
-  float2* part_ml = (float2*)(base + align256((size_t)chunk * x.Hq * x.top_k * x.D * 4));
+  float2* part_ml = (float2*)(base + align256(attend_rows(dims, x) * x.D * 4));
   const float scale_log2 = x.scale * 1.44269504088896340736f;
   for (long long r0 = 0; r0 < x.total_q; r0 += chunk) {
     const int a = (int)r0, z = (int)std::min<long long>(x.total_q, r0 + chunk);
@@ -308,7 +317,8 @@ msa_status_t msa_attend(const msa_dims_t* dims, const void* q, const void* k, co
       ProfScope ps(K_ATTEND, st);
       e = msa::launch_attend_blocks(x.D, x.hpg, q, k, v, cu_seqlens_q, cu_seqlens_k,
                                              dims->batch, x.G, x.Hq, x.top_k, x.nb_max,
-                                             block_offsets, block_entries, a, z, scale_log2,
+                                             block_offsets, block_entries, a, z,
+                                             (int)x.total_q, scale_log2,
                                              part_acc, part_ml, st);
     }
     if (e != hipSuccess) return hip_fail(e);

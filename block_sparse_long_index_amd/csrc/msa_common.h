@@ -67,6 +67,14 @@ __device__ inline uint32_t pack_bf16x2(float lo, float hi) {
   return (uint32_t)f32_to_bf16_bits(lo) | ((uint32_t)f32_to_bf16_bits(hi) << 16);
 }
 
+// Same packing through the compiler's float -> __bf16 conversion, which on
+// gfx950 is one v_cvt_pk_bf16_f32 per pair (round to nearest even).
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+__device__ inline uint32_t pack2_bf16(float lo, float hi) {
+  bf16x2_t v = {(__bf16)lo, (__bf16)hi};
+  return __builtin_bit_cast(uint32_t, v);
+}
+
 // Order-preserving map of fp32 to uint32 (larger float -> larger key).
 __device__ inline uint32_t float_order_key(float f) {
   uint32_t u = __float_as_uint(f);
