@@ -85,25 +85,26 @@ __device__ inline int wave_lower_bound(const int32_t* __restrict__ a, int lo, in
   return lo + __popcll(__ballot(below));
 }
 
+// One (block, sequence, group) item: stage its K/V block, then attend every
+// gathered query of this pass.  Called by the whole workgroup; every exit is
+// workgroup-uniform.
 template <int D, int HPG>
-__global__ __launch_bounds__(256, 2) void attend_blocks_kernel(
-    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
-    const int32_t* __restrict__ cu_q, const int32_t* __restrict__ cu_k, int batch, int G, int Hq,
-    int top_k, int nb_max, const int32_t* __restrict__ offsets, const int32_t* __restrict__ entries,
-    int r0, int r1, int total_q, float scale_log2, float* __restrict__ part_acc,
-    float2* __restrict__ part_ml, int spare_row) {
+__device__ __forceinline__ void attend_item(
+    long long item, const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+    const uint16_t* __restrict__ v, const int32_t* __restrict__ cu_q,
+    const int32_t* __restrict__ cu_k, int batch, int G, int Hq, int top_k, int nb_max,
+    const int32_t* __restrict__ offsets, const int32_t* __restrict__ entries, int r0, int r1,
+    int total_q, float scale_log2, float* __restrict__ part_acc, float2* __restrict__ part_ml,
+    int spare_row, uint16_t* Ks, uint16_t* Vt, int* range) {
   constexpr int QPT = 32 / HPG;   // queries per 32-row tile
   constexpr int KS = D / 16;      // k-steps of Q.K over the head dim
   constexpr int DT = D / 32;      // 32-row tiles of the transposed output
   constexpr int LDK = D + 8;
   constexpr int LDV = kBlock + 4;   // 66-dword rows: 8-byte reads of 16 rows hit distinct banks
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[kBlock * LDK];
-  __shared__ __attribute__((aligned(16))) uint16_t Vt[D * LDV];
-  __shared__ int range[2];
 
   const int BG = batch * G;
-  const int beta = blockIdx.x / BG;
-  const int bg = blockIdx.x % BG;
+  const int beta = (int)(item / BG);
+  const int bg = (int)(item % BG);
   const int b = bg / G, g = bg % G;
   const int koff = cu_k[b], lk = cu_k[b + 1] - koff;
   const int qoff = cu_q[b], lq = cu_q[b + 1] - qoff;
@@ -272,6 +273,54 @@ __global__ __launch_bounds__(256, 2) void attend_blocks_kernel(
   }
 }
 
+// Items in block-major order (blocks that most queries select start first).
+// items_per_wg == 1: one item per workgroup.  items_per_wg in 2..64 (sparse
+// selections, e.g. decode): the workgroup finds which of its items have any
+// query with one coalesced load and processes only those.
+template <int D, int HPG>
+__global__ __launch_bounds__(256, 2) void attend_blocks_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+    const int32_t* __restrict__ cu_q, const int32_t* __restrict__ cu_k, int batch, int G, int Hq,
+    int top_k, int nb_max, const int32_t* __restrict__ offsets, const int32_t* __restrict__ entries,
+    int r0, int r1, int total_q, float scale_log2, float* __restrict__ part_acc,
+    float2* __restrict__ part_ml, int spare_row, int items_per_wg) {
+  constexpr int LDK = D + 8;
+  constexpr int LDV = kBlock + 4;
+  __shared__ __attribute__((aligned(16))) uint16_t Ks[kBlock * LDK];
+  __shared__ __attribute__((aligned(16))) uint16_t Vt[D * LDV];
+  __shared__ int range[2];
+  __shared__ unsigned long long todo;
+  const long long BG = (long long)batch * G;
+  const long long n_items = (long long)nb_max * BG;
+  const long long first = (long long)blockIdx.x * items_per_wg;
+  if (items_per_wg == 1) {
+    attend_item<D, HPG>(first, q, k, v, cu_q, cu_k, batch, G, Hq, top_k, nb_max, offsets, entries,
+                        r0, r1, total_q, scale_log2, part_acc, part_ml, spare_row, Ks, Vt, range);
+    return;
+  }
+  const int tid = threadIdx.x;
+  if (tid < 64) {
+    const long long it = first + tid;
+    bool busy = false;
+    if (tid < items_per_wg && it < n_items) {
+      const long long u = (it % BG) * nb_max + it / BG;
+      busy = offsets[u + 1] > offsets[u];
+    }
+    const unsigned long long m = __ballot(busy);
+    if (tid == 0) todo = m;
+  }
+  __syncthreads();
+  unsigned long long m = todo;
+  while (m) {
+    const int i = __ffsll((long long)m) - 1;
+    m &= m - 1;
+    attend_item<D, HPG>(first + i, q, k, v, cu_q, cu_k, batch, G, Hq, top_k, nb_max, offsets,
+                        entries, r0, r1, total_q, scale_log2, part_acc, part_ml, spare_row, Ks, Vt,
+                        range);
+    __syncthreads();   // LDS and range are reused by the next item
+  }
+}
+
 // One wave per (query row, head); KMAX >= top_k, so every slot load is issued
 // up front.  Eight waves per workgroup take eight consecutive heads, so a
 // workgroup reads whole (row, group) partial runs contiguously.
@@ -350,11 +399,15 @@ static void launch_attend_t(const void* q, const void* k, const void* v, const i
                             const int32_t* offsets, const int32_t* entries, int r0, int r1,
                             int total_q, float scale_log2, float* part_acc, float2* part_ml,
                             hipStream_t st) {
-  dim3 grid((unsigned)((size_t)nb_max * batch * G));
+  // sparse selections (few queries per item on average): scan items in runs of 64
+  const long long n_items = (long long)nb_max * batch * G;
+  const double per_item = (double)(r1 - r0) * G * top_k / (double)n_items;
+  const int ipw = per_item >= 4.0 ? 1 : 64;
+  dim3 grid((unsigned)((n_items + ipw - 1) / ipw));
   hipLaunchKernelGGL((attend_blocks_kernel<D, HPG>), grid, dim3(256), 0, st, (const uint16_t*)q,
                      (const uint16_t*)k, (const uint16_t*)v, cu_q, cu_k, batch, G, Hq, top_k,
                      nb_max, offsets, entries, r0, r1, total_q, scale_log2, part_acc, part_ml,
-                     (r1 - r0) * Hq * top_k);
+                     (r1 - r0) * Hq * top_k, ipw);
 }
 
 template <int D>
