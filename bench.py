@@ -306,7 +306,7 @@ def main():
         if not s:
             return None
         sec = s["ms_per_step"] / 1e3
-        if name in ("index_score_prefill",):
+        if name in ("index_select_prefill",):
             a = wm["index_flops"] / sec
             return dict(bound="mfma", achieved=a / 1e12, peak=PEAK_BF16_FLOPS / 1e12, unit="TFLOP/s",
                         frac=a / PEAK_BF16_FLOPS, traffic=None)

@@ -8,18 +8,21 @@
 //
 // Only earlier blocks (beta < beta(p)) are scored: the query's own block is
 // always selected whatever its score, so its score is never needed for the
-// choice.  Output layout: S[beta * ld + row], row = (query - r0) * G + g, so a
-// workgroup's scores for one key block are one contiguous run (coalesced).
+// choice.
 //
 // Prefill kernel: a workgroup owns the rows (query, group) of a run of
 // queries in one sequence and streams the shared index keys block by block
 // through LDS; every wave keeps its rows' index queries in registers as the
 // MFMA B operand and computes S^T = K * Q^T so that each lane owns one row
 // and the block max is a register reduction plus one cross-half exchange.
+// The top-k selection is fused (see the kernel).
 //
 // Decode kernel: few rows per sequence and long contexts, so the key range
 // is split over workgroups and the four waves split each block's 128 keys.
+// It writes block scores S[beta * ld + row], row = (query - r0) * G + g, for
+// the separate wide top-k kernel.
 #include "msa_common.h"
+#include "topk_common.h"
 
 namespace msa {
 
@@ -56,14 +59,19 @@ struct KTileStage {
 };
 
 // ---------------------------------------------------------------------------
-// Prefill: RT row tiles of 32 rows per wave, NW waves per workgroup.
-// grid.x = query tiles per sequence, grid.y = sequence.
+// Prefill: scoring fused with the selection.  RT (1 or 2) row tiles of 32 rows
+// per wave, NW waves per workgroup; grid.x = query tiles (latest first),
+// grid.y = sequence.  After each key block a lane holds the block score of
+// one row (lanes 32 * rt .. 32 * rt + 31 own row tile rt) and inserts it into
+// that row's running top-(k-1) list (KCAP keys in registers); at the end the
+// lane writes the row's selection.  No block-score buffer is needed.
 // ---------------------------------------------------------------------------
-template <int DI, int RT, int NW>
-__global__ __launch_bounds__(NW * 64) void index_score_prefill_kernel(
+template <int DI, int RT, int NW, int KCAP>
+__global__ __launch_bounds__(NW * 64) void index_select_prefill_kernel(
     const uint16_t* __restrict__ q_idx, const uint16_t* __restrict__ k_idx,
-    const int32_t* __restrict__ cu_q, const int32_t* __restrict__ cu_k, int G, int qt,
-    int r0, int r1, float* __restrict__ S, long long ld) {
+    const int32_t* __restrict__ cu_q, const int32_t* __restrict__ cu_k, int G, int qt, int top_k,
+    int32_t* __restrict__ sel, float* __restrict__ sel_score) {
+  static_assert(RT == 1 || RT == 2, "a lane owns at most one row");
   constexpr int NT = NW * 64;
   constexpr int KS = DI / 16;          // MFMA k-steps over the index dim
   constexpr int LD = DI + 8;
@@ -72,14 +80,13 @@ __global__ __launch_bounds__(NW * 64) void index_score_prefill_kernel(
   const int b = blockIdx.y;
   const int qoff = cu_q[b], lq = cu_q[b + 1] - qoff;
   const int koff = cu_k[b], lk = cu_k[b + 1] - koff;
-  int qa = qoff + (int)blockIdx.x * qt;
-  int qz = min(qoff + lq, qa + qt);
-  qa = max(qa, r0);
-  qz = min(qz, r1);
+  // later query tiles score more blocks (causal triangle): dispatch them first
+  const int tile = (int)(gridDim.x - 1 - blockIdx.x);
+  const int qa = qoff + tile * qt;
+  const int qz = min(qoff + lq, qa + qt);
   if (qa >= qz) return;
   const int p_last = lk - lq + (qz - 1 - qoff);
-  const int beta_hi = p_last / kBlock;   // blocks 0 .. beta_hi-1 are non-local for the last row
-  if (beta_hi <= 0) return;
+  const int beta_hi = p_last / kBlock;   // blocks 0 .. beta_hi-1 are earlier blocks for the last row
   const int nrows = (qz - qa) * G;
 
   const int tid = threadIdx.x;
@@ -88,62 +95,74 @@ __global__ __launch_bounds__(NW * 64) void index_score_prefill_kernel(
   const int col = lane & 31;
   const int half = lane >> 5;
 
-  // index queries of this wave's rows, as MFMA B operands (k = 16ks + 8half + e)
-  bf16x8 qf[RT][KS];
+  // the row this lane selects for
+  const bool owner = half < RT;
+  const int n_own = (wave * RT + (owner ? half : 0)) * 32 + col;
+  const bool own_valid = owner && n_own < nrows;
+  const int q_own = qa + n_own / G, g_own = n_own % G;
+  const int beta_own = own_valid ? (lk - lq + (q_own - qoff)) / kBlock : 0;
+  uint64_t list[KCAP];
 #pragma unroll
-  for (int rt = 0; rt < RT; ++rt) {
-    int n = (wave * RT + rt) * 32 + col;
-    const uint16_t* src = q_idx + ((size_t)qa * G + n) * DI;
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      uint4 v = make_uint4(0, 0, 0, 0);
-      if (n < nrows) v = *reinterpret_cast<const uint4*>(src + ks * 16 + half * 8);
-      qf[rt][ks] = as_bf16x8(v);
-    }
-  }
+  for (int i = 0; i < KCAP; ++i) list[i] = 0;
 
-  const uint16_t* kbase = k_idx + (size_t)koff * DI;
-  KTileStage<DI, NT> stage;
-  stage.load(kbase, tid);
-  stage.store(lds[0], tid);
-  __syncthreads();
-
-  const size_t srow = (size_t)(qa - r0) * G;
-  for (int beta = 0; beta < beta_hi; ++beta) {
-    // prefetch the next block (the last iteration re-reads its own block; unused)
-    const int nxt = min(beta + 1, beta_hi - 1);
-    stage.load(kbase + (size_t)nxt * kBlock * DI, tid);
-    const uint16_t* kt_lds = lds[beta & 1];
-
-    float rmax[RT];
-#pragma unroll
-    for (int rt = 0; rt < RT; ++rt) rmax[rt] = -INFINITY;
-#pragma unroll
-    for (int kt = 0; kt < 4; ++kt) {
-      bf16x8 a[KS];
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks)
-        a[ks] = as_bf16x8(*reinterpret_cast<const uint4*>(kt_lds + (kt * 32 + col) * LD + ks * 16 + half * 8));
-      f32x16 acc[RT];
-#pragma unroll
-      for (int rt = 0; rt < RT; ++rt) acc[rt] = f32x16{};
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks)
-#pragma unroll
-        for (int rt = 0; rt < RT; ++rt) acc[rt] = mfma32(a[ks], qf[rt][ks], acc[rt]);
-#pragma unroll
-      for (int rt = 0; rt < RT; ++rt)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) rmax[rt] = fmaxf(rmax[rt], acc[rt][i]);
-    }
+  if (beta_hi > 0) {
+    // index queries of this wave's rows, as MFMA B operands (k = 16ks + 8half + e)
+    bf16x8 qf[RT][KS];
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) {
-      rmax[rt] = fmaxf(rmax[rt], shfl_xor_f(rmax[rt], 32));
-      int n = (wave * RT + rt) * 32 + col;
-      if ((rt & 1) == half && n < nrows) S[(size_t)beta * ld + srow + n] = rmax[rt];
+      const int n = (wave * RT + rt) * 32 + col;
+      const uint16_t* src = q_idx + ((size_t)qa * G + min(n, nrows - 1)) * DI;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        uint4 v = *reinterpret_cast<const uint4*>(src + ks * 16 + half * 8);
+        qf[rt][ks] = as_bf16x8(n < nrows ? v : make_uint4(0, 0, 0, 0));
+      }
     }
-    stage.store(lds[(beta + 1) & 1], tid);
+
+    const uint16_t* kbase = k_idx + (size_t)koff * DI;
+    KTileStage<DI, NT> stage;
+    stage.load(kbase, tid);
+    stage.store(lds[0], tid);
     __syncthreads();
+
+    for (int beta = 0; beta < beta_hi; ++beta) {
+      // prefetch the next block (the last iteration re-reads its own block; unused)
+      const int nxt = min(beta + 1, beta_hi - 1);
+      stage.load(kbase + (size_t)nxt * kBlock * DI, tid);
+      const uint16_t* kt_lds = lds[beta & 1];
+
+      float rmax[RT];
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt) rmax[rt] = -INFINITY;
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt) {
+        bf16x8 a[KS];
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+          a[ks] = as_bf16x8(*reinterpret_cast<const uint4*>(kt_lds + (kt * 32 + col) * LD + ks * 16 + half * 8));
+        f32x16 acc[RT];
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) acc[rt] = f32x16{};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+          for (int rt = 0; rt < RT; ++rt) acc[rt] = mfma32(a[ks], qf[rt][ks], acc[rt]);
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) rmax[rt] = fmaxf(rmax[rt], acc[rt][i]);
+      }
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt) rmax[rt] = fmaxf(rmax[rt], shfl_xor_f(rmax[rt], 32));
+      const float mine = (RT == 1 || half == 0) ? rmax[0] : rmax[RT - 1];
+      if (beta < beta_own && mine == mine) list_insert(list, make_key(mine, beta));
+      stage.store(lds[(beta + 1) & 1], tid);
+      __syncthreads();
+    }
+  }
+  if (own_valid) {
+    const size_t o = ((size_t)q_own * G + g_own) * top_k;
+    write_selection(list, top_k - 1, beta_own, top_k, sel + o, sel_score ? sel_score + o : nullptr);
   }
 }
 
@@ -240,26 +259,41 @@ constexpr int kDecodeSeg = 8;
 
 int prefill_rows_per_wg() { return kPrefillRows; }
 
-template <int DI>
-static hipError_t launch_prefill_di(const void* q_idx, const void* k_idx, const int32_t* cu_q,
-                                    const int32_t* cu_k, int batch, int G, int max_q_len, int r0,
-                                    int r1, float* S, long long ld, hipStream_t st) {
-  int qt = kPrefillRows / G;
+template <int DI, int KCAP>
+static hipError_t launch_prefill_t(const void* q_idx, const void* k_idx, const int32_t* cu_q,
+                                   const int32_t* cu_k, int batch, int G, int max_q_len, int top_k,
+                                   int32_t* sel, float* sel_score, hipStream_t st) {
+  const int qt = kPrefillRows / G;
   if (qt < 1) return hipErrorInvalidValue;
   dim3 grid((max_q_len + qt - 1) / qt, batch);
-  hipLaunchKernelGGL((index_score_prefill_kernel<DI, kPrefillRT, kPrefillNW>), grid,
+  hipLaunchKernelGGL((index_select_prefill_kernel<DI, kPrefillRT, kPrefillNW, KCAP>), grid,
                      dim3(kPrefillNW * 64), 0, st, (const uint16_t*)q_idx, (const uint16_t*)k_idx,
-                     cu_q, cu_k, G, qt, r0, r1, S, ld);
+                     cu_q, cu_k, G, qt, top_k, sel, sel_score);
   return hipGetLastError();
 }
 
-hipError_t launch_index_score_prefill(const void* q_idx, const void* k_idx, const int32_t* cu_q,
-                                      const int32_t* cu_k, int batch, int G, int DI, int max_q_len,
-                                      int r0, int r1, float* S, long long ld, hipStream_t st) {
+template <int DI>
+static hipError_t launch_prefill_di(const void* q_idx, const void* k_idx, const int32_t* cu_q,
+                                    const int32_t* cu_k, int batch, int G, int max_q_len, int top_k,
+                                    int32_t* sel, float* sel_score, hipStream_t st) {
+  const int km = top_k - 1;
+#define MSA_PF(K) launch_prefill_t<DI, K>(q_idx, k_idx, cu_q, cu_k, batch, G, max_q_len, top_k, sel, sel_score, st)
+  if (km <= 1) return MSA_PF(1);
+  if (km <= 2) return MSA_PF(2);
+  if (km <= 4) return MSA_PF(4);
+  if (km <= 8) return MSA_PF(8);
+  if (km <= 16) return MSA_PF(16);
+  return MSA_PF(32);
+#undef MSA_PF
+}
+
+hipError_t launch_index_select_prefill(const void* q_idx, const void* k_idx, const int32_t* cu_q,
+                                       const int32_t* cu_k, int batch, int G, int DI, int max_q_len,
+                                       int top_k, int32_t* sel, float* sel_score, hipStream_t st) {
   switch (DI) {
-    case 32: return launch_prefill_di<32>(q_idx, k_idx, cu_q, cu_k, batch, G, max_q_len, r0, r1, S, ld, st);
-    case 64: return launch_prefill_di<64>(q_idx, k_idx, cu_q, cu_k, batch, G, max_q_len, r0, r1, S, ld, st);
-    case 128: return launch_prefill_di<128>(q_idx, k_idx, cu_q, cu_k, batch, G, max_q_len, r0, r1, S, ld, st);
+    case 32: return launch_prefill_di<32>(q_idx, k_idx, cu_q, cu_k, batch, G, max_q_len, top_k, sel, sel_score, st);
+    case 64: return launch_prefill_di<64>(q_idx, k_idx, cu_q, cu_k, batch, G, max_q_len, top_k, sel, sel_score, st);
+    case 128: return launch_prefill_di<128>(q_idx, k_idx, cu_q, cu_k, batch, G, max_q_len, top_k, sel, sel_score, st);
   }
   return hipErrorInvalidValue;
 }

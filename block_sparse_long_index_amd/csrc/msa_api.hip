@@ -14,8 +14,8 @@
 #include "msa_common.h"
 
 namespace msa {
-hipError_t launch_index_score_prefill(const void*, const void*, const int32_t*, const int32_t*, int,
-                                      int, int, int, int, int, float*, long long, hipStream_t);
+hipError_t launch_index_select_prefill(const void*, const void*, const int32_t*, const int32_t*, int,
+                                       int, int, int, int, int32_t*, float*, hipStream_t);
 hipError_t launch_index_score_decode(const void*, const void*, const int32_t*, const int32_t*, int,
                                      int, int, int, int, int, float*, long long, hipStream_t);
 hipError_t launch_topk_select(const float*, long long, int, int, const int32_t*, const int32_t*, int,
@@ -122,7 +122,10 @@ long long attend_chunk(const msa_dims_t* d, const Derived& x) {
   return round_chunk(rows, x.total_q, d->q_chunk > 0 && d->q_chunk <= cap);
 }
 
+// the prefill path selects inside its scoring kernel and needs no workspace;
+// the decode path keeps a block-score buffer for its wide top-k
 size_t ws_select(const msa_dims_t* d, const Derived& x) {
+  if (!x.decode_path) return 256;
   long long c = select_chunk(d, x);
   return align256((size_t)c * x.G * x.nb_max * 4) + 256;
 }
@@ -144,7 +147,7 @@ bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 // recorded on the launch stream; msa_profile_collect() waits for them.
 enum KernelId { K_INDEX_PREFILL, K_INDEX_DECODE, K_TOPK, K_LISTS, K_ATTEND, K_MERGE };
 const char* const kKernelNames[MSA_PROFILE_KERNELS] = {
-    "index_score_prefill", "index_score_decode", "topk_select",
+    "index_select_prefill", "index_score_decode", "topk_select",
     "build_lists", "attend_blocks", "merge_partials"};
 
 std::atomic<bool> g_prof_on{false};
@@ -238,26 +241,28 @@ msa_status_t msa_index_select(const msa_dims_t* dims, const void* q_idx, const v
   if (workspace_bytes < ws_select(dims, x))
     return fail(MSA_ERR_WORKSPACE_TOO_SMALL, "index_select workspace too small");
   hipStream_t st = (hipStream_t)stream;
+  if (!x.decode_path) {
+    ProfScope ps(K_INDEX_PREFILL, st);
+    hipError_t e = msa::launch_index_select_prefill(q_idx, k_idx, cu_seqlens_q, cu_seqlens_k,
+                                                    dims->batch, x.G, x.DI, dims->max_q_len,
+                                                    x.top_k, sel, sel_score, st);
+    return e == hipSuccess ? MSA_OK : hip_fail(e);
+  }
   float* S = (float*)(((uintptr_t)workspace + 255) & ~(uintptr_t)255);
   const long long chunk = select_chunk(dims, x);
-  const bool wide = x.decode_path || chunk * x.G <= 16384;
   for (long long r0 = 0; r0 < x.total_q; r0 += chunk) {
     const int a = (int)r0, z = (int)std::min<long long>(x.total_q, r0 + chunk);
     const long long ld = (long long)(z - a) * x.G;
     hipError_t e;
-    if (x.decode_path) {
+    {
       ProfScope ps(K_INDEX_DECODE, st);
       e = msa::launch_index_score_decode(q_idx, k_idx, cu_seqlens_q, cu_seqlens_k, dims->batch, x.G,
                                          x.DI, x.nb_max, a, z, S, ld, st);
-    } else {
-      ProfScope ps(K_INDEX_PREFILL, st);
-      e = msa::launch_index_score_prefill(q_idx, k_idx, cu_seqlens_q, cu_seqlens_k, dims->batch,
-                                          x.G, x.DI, dims->max_q_len, a, z, S, ld, st);
     }
     if (e != hipSuccess) return hip_fail(e);
     ProfScope ps(K_TOPK, st);
     e = msa::launch_topk_select(S, ld, a, z, cu_seqlens_q, cu_seqlens_k, dims->batch, x.G, x.top_k,
-                                wide, sel, sel_score, st);
+                                true, sel, sel_score, st);
     if (e != hipSuccess) return hip_fail(e);
   }
   return MSA_OK;

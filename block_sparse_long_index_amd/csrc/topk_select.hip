@@ -10,64 +10,16 @@
 // output is ascending, -1 padded; one selection per group, shared by the
 // group's heads (section "GQAグループ単位の選択共有とは").
 //
-// Each (score, block) pair is one 64-bit key: order-preserving float bits in
-// the high word, bitwise-not of the block id in the low word, so "better"
-// is one unsigned compare and ties resolve to the lower id.  Each lane keeps
-// a descending list of the KCAP best keys of its candidate stream in
-// registers (KCAP = next power of two >= top_k - 1).  With W lanes per row
-// the lanes split the row's blocks and merge their lists in top_k - 1
-// max-reduction rounds.
+// This kernel selects from a materialised block-score buffer (the decode
+// path); the prefill path fuses the same selection into its scoring kernel.
+// Each lane keeps a descending list of the KCAP best (score, block) keys of
+// its candidate stream in registers (KCAP = next power of two >= top_k - 1).
+// With W lanes per row the lanes split the row's blocks and merge their lists
+// in top_k - 1 max-reduction rounds.
 #include "msa_common.h"
+#include "topk_common.h"
 
 namespace msa {
-
-__device__ inline uint64_t make_key(float s, int beta) {
-  return ((uint64_t)float_order_key(s) << 32) | (uint64_t)(~(uint32_t)beta);
-}
-__device__ inline int key_block(uint64_t k) { return (int)(~(uint32_t)k); }
-__device__ inline float key_score(uint64_t k) { return float_from_order_key((uint32_t)(k >> 32)); }
-
-__device__ inline uint64_t shfl_xor_u64(uint64_t v, int mask) {
-  uint32_t lo = __shfl_xor((uint32_t)v, mask, kWave);
-  uint32_t hi = __shfl_xor((uint32_t)(v >> 32), mask, kWave);
-  return ((uint64_t)hi << 32) | lo;
-}
-
-// Insert `key` into a descending list of N keys (0 = empty), dropping the smallest.
-template <int N>
-__device__ inline void list_insert(uint64_t (&list)[N], uint64_t key) {
-  if (key > list[N - 1]) {
-#pragma unroll
-    for (int i = N - 1; i >= 0; --i) {
-      uint64_t prev = (i > 0) ? list[i - 1] : ~0ull;
-      bool gt_i = key > list[i];
-      bool gt_prev = key > prev;
-      list[i] = gt_i ? (gt_prev ? prev : key) : list[i];
-    }
-  }
-}
-
-// Ascending sort of N values (bitonic network, static indices).
-template <int N>
-__device__ inline void sort_ascending(uint64_t (&a)[N]) {
-#pragma unroll
-  for (int k = 2; k <= N; k <<= 1) {
-#pragma unroll
-    for (int j = k >> 1; j > 0; j >>= 1) {
-#pragma unroll
-      for (int i = 0; i < N; ++i) {
-        int l = i ^ j;
-        if (l > i) {
-          bool up = (i & k) == 0;
-          uint64_t x = a[i], y = a[l];
-          bool sw = up ? (x > y) : (x < y);
-          a[i] = sw ? y : x;
-          a[l] = sw ? x : y;
-        }
-      }
-    }
-  }
-}
 
 // grid.x covers the chunk's rows (chunk row = (query - r0) * G + g), 256 / W rows per workgroup.
 template <int KCAP, int W>
@@ -137,40 +89,8 @@ __global__ __launch_bounds__(256) void topk_select_kernel(
   }
   if (!active || w != 0) return;
 
-  // keep the km best, then order them by block id: (id << 32 | score key), empty -> max
-  uint64_t byid[KCAP];
-  int cnt = 0;
-#pragma unroll
-  for (int i = 0; i < KCAP; ++i) {
-    bool real = (i < km) && res[i] != 0;
-    cnt += real ? 1 : 0;
-    byid[i] = real ? (((uint64_t)(uint32_t)key_block(res[i]) << 32) | (res[i] >> 32)) : ~0ull;
-  }
-  sort_ascending(byid);
-
-  int32_t* so = sel + ((size_t)r * G + g) * top_k;
-  float* sc = sel_score ? sel_score + ((size_t)r * G + g) * top_k : nullptr;
-#pragma unroll
-  for (int j = 0; j < KCAP + 1; ++j) {
-    if (j < top_k) {
-      int id;
-      float s;
-      if (j < cnt) {
-        uint64_t v = (j < KCAP) ? byid[j < KCAP ? j : 0] : 0;
-        id = (int)(v >> 32);
-        s = float_from_order_key((uint32_t)v);
-      } else if (j == cnt) {
-        id = beta_p;
-        s = INFINITY;
-      } else {
-        id = -1;
-        s = __uint_as_float(0x7fc00000u);
-      }
-      so[j] = id;
-      if (sc) sc[j] = s;
-    }
-  }
-  // top_k beyond KCAP + 1 cannot occur (KCAP >= top_k - 1)
+  write_selection(res, km, beta_p, top_k, sel + ((size_t)r * G + g) * top_k,
+                  sel_score ? sel_score + ((size_t)r * G + g) * top_k : nullptr);
 }
 
 template <int KCAP>

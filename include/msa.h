@@ -178,7 +178,7 @@ int32_t msa_abi_version(void);
 /*
  * Per-kernel timing, a measuring aid (not part of the pages' method).  While
  * enabled, every kernel stage a call launches is bracketed by two hipEvents
- * recorded on the call's stream.  Stage ids: 0 index_score_prefill,
+ * recorded on the call's stream.  Stage ids: 0 index_select_prefill (scores + top-k),
  * 1 index_score_decode, 2 topk_select, 3 build_lists (all list kernels),
  * 4 attend_blocks, 5 merge_partials.  msa_profile_collect() waits for every
  * recorded event (it blocks the host), writes the summed milliseconds and the

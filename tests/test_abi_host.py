@@ -46,10 +46,14 @@ def test_status_strings():
 
 def test_workspace_sizes_scale_with_chunk():
     d = _dims()
-    full = msa.workspace_size(d, msa.OP_INDEX_SELECT)
-    assert full >= 32768 * 8 * 256 * 4
-    d2 = _dims(q_chunk=1024)
-    assert msa.workspace_size(d2, msa.OP_INDEX_SELECT) < full
+    # prefill selects inside its scoring kernel: no block-score buffer
+    assert msa.workspace_size(d, msa.OP_INDEX_SELECT) <= 4096
+    # decode (<= 32 rows per sequence) keeps a block-score buffer per pass
+    dec = _dims(batch=32, total_q=32, total_k=32 * 65536, max_q_len=1, max_k_len=65536)
+    full = msa.workspace_size(dec, msa.OP_INDEX_SELECT)
+    assert full >= 32 * 8 * 512 * 4
+    dec2 = _dims(batch=32, total_q=32, total_k=32 * 65536, max_q_len=1, max_k_len=65536, q_chunk=8)
+    assert msa.workspace_size(dec2, msa.OP_INDEX_SELECT) < full
     a_full = msa.workspace_size(_dims(), msa.OP_ATTEND)
     a_small = msa.workspace_size(_dims(q_chunk=256), msa.OP_ATTEND)
     assert a_small < a_full
