@@ -241,6 +241,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--q-chunk", type=int, default=0)
     ap.add_argument("--json-out", default="")
+    ap.add_argument("--graph", choices=["auto", "on", "off"], default="auto",
+                    help="replay the step as a captured HIP graph (auto: on for decode, whose "
+                         "kernels are short enough for launch gaps to matter)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -279,17 +282,44 @@ def main():
         torch.cuda.synchronize()
         log(f"[bench] warmup {i + 1}/{args.warmup} done")
 
-    msa.profile_collect()             # drop anything recorded before
-    msa.profile_enable(True)
-    torch.cuda.synchronize()
-    ts = time.perf_counter()
-    for _ in range(args.steps):
-        step()
-    torch.cuda.synchronize()
-    te = time.perf_counter()
-    msa.profile_enable(False)
-    prof = msa.profile_collect()
-    ms_per_step = (te - ts) * 1e3 / args.steps
+    use_graph = args.graph == "on" or (args.graph == "auto" and w.name == "decode")
+    run = step
+    if use_graph:
+        # capture the three calls once (no allocation, no memset, no host sync inside)
+        cs = torch.cuda.Stream()
+        cs.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(cs):
+            step()
+        torch.cuda.current_stream().wait_stream(cs)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=cs):
+            step()
+        torch.cuda.synchronize()
+        run = graph.replay
+        log("[bench] step captured as a graph")
+
+    def timed(fn, n, profile):
+        if profile:
+            msa.profile_collect()             # drop anything recorded before
+            msa.profile_enable(True)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(n):
+            fn()
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        prof = None
+        if profile:
+            msa.profile_enable(False)
+            prof = msa.profile_collect()
+        return (t1 - t0) * 1e3 / n, prof
+
+    # timed region: exactly `steps` steps; stage times from library HIP events on the
+    # launch stream (an eager pass of the same length when the timed steps are graph replays)
+    ms_per_step, prof = timed(run, args.steps, profile=not use_graph)
+    if use_graph:
+        _, prof = timed(step, args.steps, profile=True)
     log(f"[bench] timed {args.steps} steps: {ms_per_step:.3f} ms/step")
 
     wm = work_model(w)
@@ -404,6 +434,7 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
+        "graph": use_graph,
         "config": {"workload": w.name, "seq_k_lens": (w.seq_k_lens if len(w.seq_k_lens) <= 4 else
                                                        f"{len(w.seq_k_lens)} seqs, total {w.total_k}"),
                    "total_q": w.total_q, "num_q_heads": w.num_q_heads,

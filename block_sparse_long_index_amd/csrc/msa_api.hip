@@ -27,6 +27,9 @@ hipError_t launch_build_lists(const int32_t*, const int32_t*, const int32_t*, in
 hipError_t launch_attend_blocks(int, int, const void*, const void*, const void*, const int32_t*,
                                 const int32_t*, int, int, int, int, int, const int32_t*,
                                 const int32_t*, int, int, int, float, float*, float2*, hipStream_t);
+hipError_t launch_attend_decode(int, int, const void*, const void*, const void*, const int32_t*,
+                                const int32_t*, int, int, int, int, const int32_t*, int, int, float,
+                                float*, float2*, hipStream_t);
 hipError_t launch_merge(int, const float*, const float2*, const int32_t*, int, int, int, int, int,
                         void*, float*, hipStream_t);
 }  // namespace msa
@@ -320,11 +323,17 @@ msa_status_t msa_attend(const msa_dims_t* dims, const void* q, const void* k, co
     hipError_t e;
     {
       ProfScope ps(K_ATTEND, st);
-      e = msa::launch_attend_blocks(x.D, x.hpg, q, k, v, cu_seqlens_q, cu_seqlens_k,
-                                             dims->batch, x.G, x.Hq, x.top_k, x.nb_max,
-                                             block_offsets, block_entries, a, z,
-                                             (int)x.total_q, scale_log2,
-                                             part_acc, part_ml, st);
+      if (dims->max_q_len == 1)
+        // one query per sequence: each selected block is hit by that query only;
+        // one wave per (query, slot) reads it once, straight from the selection
+        e = msa::launch_attend_decode(x.D, x.hpg, q, k, v, cu_seqlens_q, cu_seqlens_k, dims->batch,
+                                      x.G, x.Hq, x.top_k, sel, a, z, scale_log2, part_acc, part_ml,
+                                      st);
+      else
+        e = msa::launch_attend_blocks(x.D, x.hpg, q, k, v, cu_seqlens_q, cu_seqlens_k,
+                                      dims->batch, x.G, x.Hq, x.top_k, x.nb_max, block_offsets,
+                                      block_entries, a, z, (int)x.total_q, scale_log2, part_acc,
+                                      part_ml, st);
     }
     if (e != hipSuccess) return hip_fail(e);
     ProfScope ps(K_MERGE, st);

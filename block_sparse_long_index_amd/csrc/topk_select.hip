@@ -48,17 +48,20 @@ __global__ __launch_bounds__(256) void topk_select_kernel(
 
   if (active && km > 0) {
     const float* col = S + crow;
-    int beta = w;
-    // two candidates per step to overlap the loads
-    for (; beta + W < beta_p; beta += 2 * W) {
-      float s0 = col[(size_t)beta * ld];
-      float s1 = col[(size_t)(beta + W) * ld];
-      if (s0 == s0) list_insert(list, make_key(s0, beta));
-      if (s1 == s1) list_insert(list, make_key(s1, beta + W));
-    }
-    if (beta < beta_p) {
-      float s0 = col[(size_t)beta * ld];
-      if (s0 == s0) list_insert(list, make_key(s0, beta));
+    // eight candidates per step: their loads are all in flight before the inserts
+    constexpr int kBatch = 8;
+    for (int base = w; base < beta_p; base += kBatch * W) {
+      float sc[kBatch];
+#pragma unroll
+      for (int i = 0; i < kBatch; ++i) {
+        const int beta = base + i * W;
+        sc[i] = col[(size_t)min(beta, beta_p - 1) * ld];
+      }
+#pragma unroll
+      for (int i = 0; i < kBatch; ++i) {
+        const int beta = base + i * W;
+        if (beta < beta_p && sc[i] == sc[i]) list_insert(list, make_key(sc[i], beta));
+      }
     }
   }
 
