@@ -241,6 +241,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--q-chunk", type=int, default=0)
     ap.add_argument("--json-out", default="")
+    ap.add_argument("--copy-gib", type=float, default=0.0,
+                    help="before the workload, run three device copies of this many GiB (fp32): a "
+                         "kernel of known traffic for scaling the FETCH_SIZE/WRITE_SIZE counters")
     ap.add_argument("--graph", choices=["auto", "on", "off"], default="auto",
                     help="replay the step as a captured HIP graph (auto: on for decode, whose "
                          "kernels are short enough for launch gaps to matter)")
@@ -264,6 +267,16 @@ def main():
     from msa_inputs import generate
 
     dev = torch.device("cuda:0")
+    if args.copy_gib > 0:
+        n = int(args.copy_gib * 2**30) // 4
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"[bench] copied {args.copy_gib} GiB three times (counter calibration)")
+        del src, dst
+        torch.cuda.empty_cache()
     log(f"[bench] workload {w.name}: {w.note}; generating inputs on {dev}")
     t0 = time.perf_counter()
     t = generate(w, dev)
@@ -331,22 +344,40 @@ def main():
     per_step = {k_: v["ms_per_step"] for k_, v in stage.items()}
     log("[bench] stages (ms/step): " + ", ".join(f"{k_} {v:.3f}" for k_, v in per_step.items()))
 
-    def roof(name):
-        s = stage.get(name)
-        if not s:
+    def traffic_record(name):
+        """Measured HBM bytes per launch (FETCH_SIZE/WRITE_SIZE scaled by a copy of known
+        size, profiles/<kernel>_<workload>_traffic.json) if the kernel source is unchanged."""
+        import hashlib
+        path = os.path.join(ROOT, "profiles", f"{name}_{w.name}_traffic.json")
+        if not os.path.exists(path):
             return None
-        sec = s["ms_per_step"] / 1e3
+        rec = json.load(open(path))
+        src = open(os.path.join(ROOT, rec["source"]), "rb").read()
+        if hashlib.sha256(src).hexdigest() != rec["source_sha256"] or args.q_chunk:
+            return None
+        return rec["per_dispatch"]["total_bytes"] / 1e9
+
+    def roof(name):
+        """Roofline of one stage: algorithmic work per launch / average launch time."""
+        s_ = stage.get(name)
+        if not s_:
+            return None
+        n_launch = s_["launches_per_step"]
+        sec = s_["ms_per_launch"] / 1e3
         if name in ("index_select_prefill",):
-            a = wm["index_flops"] / sec
+            a = wm["index_flops"] / n_launch / sec
             return dict(bound="mfma", achieved=a / 1e12, peak=PEAK_BF16_FLOPS / 1e12, unit="TFLOP/s",
                         frac=a / PEAK_BF16_FLOPS, traffic=None)
         bytes_ = {"attend_blocks": wm["attend_bytes"], "merge_partials": wm["merge_bytes"],
                   "topk_select": wm["topk_bytes"],
                   "index_score_decode": wm["decode_bytes"] - wm["sel_total"] * BLOCK * w.head_dim * 4}
         if name in bytes_:
-            a = bytes_[name] / sec
+            per_launch = bytes_[name] / n_launch
+            a = per_launch / sec
             return dict(bound="hbm", achieved=a / 1e9, peak=PEAK_HBM_BYTES / 1e9, unit="GB/s",
-                        frac=a / PEAK_HBM_BYTES, traffic=None)
+                        frac=a / PEAK_HBM_BYTES, traffic=traffic_record(name),
+                        traffic_unit="GB per launch (HBM, counters scaled by a copy of known size)",
+                        algorithmic_per_launch=per_launch / 1e9)
         return None
 
     dominant = max(per_step, key=per_step.get) if per_step else None

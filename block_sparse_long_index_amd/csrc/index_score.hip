@@ -66,16 +66,60 @@ struct KTileStage {
 // that row's running top-(k-1) list (KCAP keys in registers); at the end the
 // lane writes the row's selection.  No block-score buffer is needed.
 // ---------------------------------------------------------------------------
+// Index-key blocks reach LDS by direct global->LDS 16-byte loads: one wave
+// instruction fills 1 KiB (lane L -> bytes 16L..16L+15), i.e. 64 / CPR whole
+// rows of CPR = DI / 8 chunks.  Rows are not padded; instead chunk c of row m
+// is stored at chunk position c ^ (m % CPR) (the swizzle is applied by
+// choosing each lane's source address), so the MFMA A-fragment reads of
+// eight consecutive rows at one logical chunk hit distinct banks.
+template <int DI, int NW>
+struct KRing {
+  static constexpr int CPR = DI / 8;                  // 16-byte chunks per key row
+  static constexpr int ROWS_PER_INSTR = 64 / CPR;
+  static constexpr int INSTR = kBlock / ROWS_PER_INSTR;   // 1 KiB pieces per block
+  static constexpr int PER_WAVE = INSTR / NW;          // loads per wave per block
+  static_assert(INSTR % NW == 0, "block must split evenly over the waves");
+
+  // issue this wave's loads of key block `blk` (rows of `kbase`) into `buf`
+  __device__ static inline void load(const uint16_t* __restrict__ kbase, int blk, uint16_t* buf,
+                                     int wave, int lane) {
+#pragma unroll
+    for (int i = 0; i < PER_WAVE; ++i) {
+      const int piece = wave * PER_WAVE + i;
+      const int m = piece * ROWS_PER_INSTR + lane / CPR;
+      const int lc = (lane % CPR) ^ (m % CPR);
+      const uint16_t* src = kbase + ((size_t)blk * kBlock + m) * DI + lc * 8;
+      __builtin_amdgcn_global_load_lds(src, buf + piece * 512, 16, 0, 0);
+    }
+  }
+  // A fragment: row m, logical chunk lc
+  __device__ static inline bf16x8 frag(const uint16_t* buf, int m, int lc) {
+    return as_bf16x8(*reinterpret_cast<const uint4*>(buf + m * DI + ((lc ^ (m % CPR)) * 8)));
+  }
+};
+
+// vmcnt(n) with the other counters left alone (gfx9 s_waitcnt encoding)
+template <int N>
+__device__ inline void wait_vmcnt() {
+  static_assert(N >= 0 && N < 16, "small counts only");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | N);
+}
+
 template <int DI, int RT, int NW, int KCAP>
 __global__ __launch_bounds__(NW * 64) void index_select_prefill_kernel(
     const uint16_t* __restrict__ q_idx, const uint16_t* __restrict__ k_idx,
     const int32_t* __restrict__ cu_q, const int32_t* __restrict__ cu_k, int G, int qt, int top_k,
     int32_t* __restrict__ sel, float* __restrict__ sel_score) {
   static_assert(RT == 1 || RT == 2, "a lane owns at most one row");
-  constexpr int NT = NW * 64;
+  using Ring = KRing<DI, NW>;
   constexpr int KS = DI / 16;          // MFMA k-steps over the index dim
-  constexpr int LD = DI + 8;
-  __shared__ __attribute__((aligned(16))) uint16_t lds[2][kBlock * LD];
+  // three key-block buffers: block beta is scored while beta+1 and beta+2 load.
+  // Separate arrays named statically in each step let the compiler see that
+  // the direct loads into one buffer cannot alias reads of another, so it
+  // does not drain the younger loads before reading.
+  __shared__ __attribute__((aligned(1024))) uint16_t ring0[kBlock * DI];
+  __shared__ __attribute__((aligned(1024))) uint16_t ring1[kBlock * DI];
+  __shared__ __attribute__((aligned(1024))) uint16_t ring2[kBlock * DI];
 
   const int b = blockIdx.y;
   const int qoff = cu_q[b], lq = cu_q[b + 1] - qoff;
@@ -90,7 +134,7 @@ __global__ __launch_bounds__(NW * 64) void index_select_prefill_kernel(
   const int nrows = (qz - qa) * G;
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
   const int col = lane & 31;
   const int half = lane >> 5;
@@ -120,16 +164,21 @@ __global__ __launch_bounds__(NW * 64) void index_select_prefill_kernel(
     }
 
     const uint16_t* kbase = k_idx + (size_t)koff * DI;
-    KTileStage<DI, NT> stage;
-    stage.load(kbase, tid);
-    stage.store(lds[0], tid);
-    __syncthreads();
+    Ring::load(kbase, 0, ring0, wave, lane);
+    if (beta_hi > 1) Ring::load(kbase, 1, ring1, wave, lane);
 
-    for (int beta = 0; beta < beta_hi; ++beta) {
-      // prefetch the next block (the last iteration re-reads its own block; unused)
-      const int nxt = min(beta + 1, beta_hi - 1);
-      stage.load(kbase + (size_t)nxt * kBlock * DI, tid);
-      const uint16_t* kt_lds = lds[beta & 1];
+    // score block beta from `rbuf`; first start loading block beta+2 into `lbuf`
+    auto step = [&](int beta, const uint16_t* rbuf, uint16_t* lbuf) __attribute__((always_inline)) {
+      // this wave's pieces of block beta have landed (only block beta+1 may be
+      // younger); the barrier makes every wave's pieces visible and retires
+      // the buffer read in the previous step (a plain __syncthreads would also
+      // drain the younger block's loads)
+      if (beta + 1 < beta_hi) wait_vmcnt<Ring::PER_WAVE>(); else wait_vmcnt<0>();
+      __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0): this wave's LDS reads are done
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+      if (beta + 2 < beta_hi) Ring::load(kbase, beta + 2, lbuf, wave, lane);
 
       float rmax[RT];
 #pragma unroll
@@ -138,8 +187,7 @@ __global__ __launch_bounds__(NW * 64) void index_select_prefill_kernel(
       for (int kt = 0; kt < 4; ++kt) {
         bf16x8 a[KS];
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks)
-          a[ks] = as_bf16x8(*reinterpret_cast<const uint4*>(kt_lds + (kt * 32 + col) * LD + ks * 16 + half * 8));
+        for (int ks = 0; ks < KS; ++ks) a[ks] = Ring::frag(rbuf, kt * 32 + col, 2 * ks + half);
         f32x16 acc[RT];
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt) acc[rt] = f32x16{};
@@ -156,8 +204,12 @@ __global__ __launch_bounds__(NW * 64) void index_select_prefill_kernel(
       for (int rt = 0; rt < RT; ++rt) rmax[rt] = fmaxf(rmax[rt], shfl_xor_f(rmax[rt], 32));
       const float mine = (RT == 1 || half == 0) ? rmax[0] : rmax[RT - 1];
       if (beta < beta_own && mine == mine) list_insert(list, make_key(mine, beta));
-      stage.store(lds[(beta + 1) & 1], tid);
-      __syncthreads();
+    };
+
+    for (int beta = 0; beta < beta_hi; beta += 3) {
+      step(beta, ring0, ring2);
+      if (beta + 1 < beta_hi) step(beta + 1, ring1, ring0);
+      if (beta + 2 < beta_hi) step(beta + 2, ring2, ring1);
     }
   }
   if (own_valid) {

@@ -82,6 +82,20 @@ def test_top_k_32_and_hpg_32():
     _full_check(w)
 
 
+def test_three_groups_non_power_of_two():
+    # G = 3: a prefill tile holds 170 queries x 3 groups = 510 of its 512 rows
+    w = custom([1900, 700], [1900, 700], num_q_heads=12, num_kv_heads=3, head_dim=64,
+               index_dim=64, top_k=5, seed=34, qkv_std=1.0)
+    _full_check(w)
+
+
+def test_six_groups_hpg_16_offset_queries():
+    # Lq < Lk with an offset that is not a multiple of the tile: tiles span blocks
+    w = custom([2500, 1333], [1111, 1333], num_q_heads=96, num_kv_heads=6, head_dim=128,
+               index_dim=32, top_k=7, seed=35, qkv_std=1.0)
+    _full_check(w)
+
+
 def test_hpg_1():
     w = custom([2000], [2000], num_q_heads=4, num_kv_heads=4, head_dim=64, index_dim=32,
                top_k=3, seed=28, qkv_std=1.0)
