@@ -6,6 +6,7 @@ msa_index_select -> msa_build_block_query_lists -> msa_attend, through the C
 ABI on one stream.  Prints ONE JSON line on stdout; progress goes to stderr.
 
     python bench.py [--steps K] [--warmup W] [--workload p128k|p1m|p32k|decode|tiny]
+                    [--index bf16|fp8]
 
 The default workload is the 128K-token single-layer prefill (64 query heads /
 8 KV heads, head dim 128, index dim 128, top-k 16 incl. the local block).
@@ -30,6 +31,8 @@ if ROOT not in sys.path:
 
 METRIC = "MSA prefill tokens/s + Main-Branch MFMA % at 128K/1M; decode HBM GB/s"
 PEAK_BF16_FLOPS = 2.5e15      # MI355X dense bf16 MFMA
+PEAK_FP8_FLOPS = 5.0e15       # MI355X dense fp8 MFMA
+FP8_DOT_REL = 2.0 ** -10      # fp8 matrix-core dot product error bound, relative to sum |q_c k_c|
 PEAK_HBM_BYTES = 8.0e12       # MI355X HBM3E
 BLOCK = 128
 
@@ -74,9 +77,19 @@ def work_model(w) -> dict:
     # plus the selected K/V blocks, Q, index queries and O
     decode_bytes = (dec_kidx_tokens * di * 2 + sel_total * BLOCK * d * 2 * 2
                     + T * (Hq * d * 2 * 2 + G * di * 2))
+    # fp8 index branch: quantisation reads the bf16 projections and writes codes + exponents;
+    # the decode scan then reads one byte per index-key element
+    nblk = sum((lk + BLOCK - 1) // BLOCK for lk in w.seq_k_lens)
+    quant_bytes = (T * G * di + w.total_k * di) * 3 + T * G + nblk
+    if w.name == "decode":      # a decode step quantises only its new index queries
+        quant_bytes = T * G * di * 3 + T * G
+    decode_fp8_bytes = (dec_kidx_tokens * di + sel_total * BLOCK * d * 2 * 2
+                        + T * (Hq * d * 2 * 2 + G * (di + 1)))
+    index_decode_fp8_bytes = dec_kidx_tokens * di + T * G * (di + 1)
     return dict(index_flops=idx_flops, main_flops=main_flops, sel_total=sel_total,
                 attend_bytes=attend_bytes, merge_bytes=merge_bytes, topk_bytes=topk_bytes,
-                decode_bytes=decode_bytes, kv_once_bytes=kv_once)
+                decode_bytes=decode_bytes, kv_once_bytes=kv_once, quant_bytes=quant_bytes,
+                decode_fp8_bytes=decode_fp8_bytes, index_decode_fp8_bytes=index_decode_fp8_bytes)
 
 
 # ---------------------------------------------------------------------------
@@ -196,9 +209,32 @@ class OraclePool:
         self.shms = []
 
 
-def parity_on_rows(P, rows, ref, sel_gpu, out_gpu, lse_gpu, top_k):
+def _fp8_top_set_valid(P, r, g, S, sel):
+    """fp8 index branch: a selection that differs from the oracle's is valid if
+    every chosen block could still outrank every unchosen one after each block
+    score moves by the matrix cores' error bound (FP8_DOT_REL * sum |q_c k_c|,
+    maximised over the block's tokens)."""
+    from oracle import msa_oracle as O
+    b, p, ko = int(P.seq[r]), int(P.pos[r]), int(P.koff[r])
+    lk = int(P.cu_k[b + 1] - P.cu_k[b])
+    qa = np.abs(np.asarray(P.q_idx[r], dtype=np.float64))[g:g + 1]
+    ka = np.abs(np.asarray(P.k_idx[ko:ko + lk][: p + 1], dtype=np.float64))
+    B = FP8_DOT_REL * O.block_max_pool(qa @ ka.T, p, P.block)[0]
+    beta_p = p // P.block
+    mine = [int(x) for x in sel if x >= 0]
+    if beta_p not in mine or len(set(mine)) != len(mine) or max(mine) > beta_p:
+        return False
+    chosen = [x for x in mine if x != beta_p]
+    others = [z for z in range(beta_p) if z not in chosen]
+    if len(mine) != min(P.top_k, beta_p + 1) or not chosen:
+        return len(mine) == min(P.top_k, beta_p + 1)
+    return min(S[x] + B[x] for x in chosen) >= max((S[z] - B[z] for z in others), default=-np.inf)
+
+
+def parity_on_rows(P, rows, ref, sel_gpu, out_gpu, lse_gpu, top_k, fp8=False):
     from oracle import msa_oracle as O
     bad = ties = 0
+    fp8_differ = 0
     dmax = dsum = 0.0
     n = 0
     ref_abs_max = 0.0
@@ -207,26 +243,39 @@ def parity_on_rows(P, rows, ref, sel_gpu, out_gpu, lse_gpu, top_k):
     for i, r in enumerate(rows):
         x = ref[r]
         beta_p = int(P.pos[r]) // BLOCK
+        ref_out, ref_lse = x["out"], x["lse"]
+        differs = False
         for g in range(P.G):
             tie = O.near_tie(x["S"][g], beta_p, top_k)
             ties += int(tie)
             if not np.array_equal(sel_gpu[i, g], x["sel"][g]):
-                if not (tie and O.valid_selection(x["S"][g], beta_p, top_k, sel_gpu[i, g])):
+                differs = True
+                if fp8:
+                    fp8_differ += 1
+                    if not _fp8_top_set_valid(P, r, g, x["S"][g], sel_gpu[i, g]):
+                        bad += 1
+                elif not (tie and O.valid_selection(x["S"][g], beta_p, top_k, sel_gpu[i, g])):
                     bad += 1
-        dd = np.abs(out_gpu[i] - x["out"])
+        if differs:
+            # Main Branch checked on the selection the GPU made
+            ref_out, ref_lse = P.attend_with_selection(r, sel_gpu[i])
+        dd = np.abs(out_gpu[i] - ref_out)
         dmax = max(dmax, float(dd.max()))
         dsum += float(dd.sum())
         n += dd.size
-        ref_abs_max = max(ref_abs_max, float(np.abs(x["out"]).max()))
+        ref_abs_max = max(ref_abs_max, float(np.abs(ref_out).max()))
         l2d += float((dd ** 2).sum())
-        l2r += float((x["out"] ** 2).sum())
-        lse_max = max(lse_max, float(np.abs(lse_gpu[i] - x["lse"]).max()))
+        l2r += float((ref_out ** 2).sum())
+        lse_max = max(lse_max, float(np.abs(lse_gpu[i] - ref_lse).max()))
     mean = dsum / max(n, 1)
     rel2 = math.sqrt(l2d / max(l2r, 1e-300))
     relmax = dmax / max(ref_abs_max, 1e-300)
     ok = bad == 0 and dmax <= 2e-2 and mean <= 2e-3 and rel2 <= 1e-2 and relmax <= 2e-2 and lse_max <= 2e-3
-    return dict(ok=bool(ok), rows=len(rows), selection_mismatches=bad, near_ties=ties,
-                max_abs=dmax, mean_abs=mean, rel_l2=rel2, rel_max=relmax, lse_max_abs=lse_max)
+    res = dict(ok=bool(ok), rows=len(rows), selection_mismatches=bad, near_ties=ties,
+               max_abs=dmax, mean_abs=mean, rel_l2=rel2, rel_max=relmax, lse_max_abs=lse_max)
+    if fp8:
+        res["fp8_selections_differing_within_bound"] = fp8_differ
+    return res
 
 
 # ---------------------------------------------------------------------------
@@ -244,6 +293,9 @@ def main():
     ap.add_argument("--copy-gib", type=float, default=0.0,
                     help="before the workload, run three device copies of this many GiB (fp32): a "
                          "kernel of known traffic for scaling the FETCH_SIZE/WRITE_SIZE counters")
+    ap.add_argument("--index", choices=["bf16", "fp8"], default="bf16",
+                    help="Index Branch precision: bf16 projections, or quantised in the step to "
+                         "FP8 E4M3 with power-of-two scales and scored on the fp8 matrix cores")
     ap.add_argument("--graph", choices=["auto", "on", "off"], default="auto",
                     help="replay the step as a captured HIP graph (auto: on for decode, whose "
                          "kernels are short enough for launch gaps to matter)")
@@ -284,11 +336,19 @@ def main():
     log(f"[bench] inputs ready in {time.perf_counter() - t0:.1f}s")
     dims = msa.dims_for(w, q_chunk=args.q_chunk)
     bufs = msa.Buffers(dims, dev, want_scores=False, want_lse=True)
-    log(f"[bench] workspace {bufs.workspace.numel() / 2**30:.2f} GiB")
+    fp8 = msa.Fp8Index(dims, dev) if args.index == "fp8" else None
+    log(f"[bench] workspace {bufs.workspace.numel() / 2**30:.2f} GiB; index branch {args.index}")
+    # fp8 decode: the index-key cache is stored quantised (quantised once, outside the step);
+    # each step quantises only its new index queries.  Prefill quantises both in the step.
+    step_k_idx = t["k_idx"]
+    if fp8 is not None and w.name == "decode":
+        msa.index_quantize_fp8(dims, None, t["k_idx"], t["cu_seqlens_k"], fp8)
+        torch.cuda.synchronize()
+        step_k_idx = None
 
     def step():
-        msa.msa_forward(dims, t["q"], t["k"], t["v"], t["q_idx"], t["k_idx"], t["cu_seqlens_q"],
-                        t["cu_seqlens_k"], bufs)
+        msa.msa_forward(dims, t["q"], t["k"], t["v"], t["q_idx"], step_k_idx, t["cu_seqlens_q"],
+                        t["cu_seqlens_k"], bufs, fp8=fp8)
 
     for i in range(args.warmup):
         step()
@@ -364,13 +424,17 @@ def main():
             return None
         n_launch = s_["launches_per_step"]
         sec = s_["ms_per_launch"] / 1e3
-        if name in ("index_select_prefill",):
+        if name in ("index_select_prefill", "index_select_prefill_fp8"):
+            peak = PEAK_FP8_FLOPS if name.endswith("fp8") else PEAK_BF16_FLOPS
             a = wm["index_flops"] / n_launch / sec
-            return dict(bound="mfma", achieved=a / 1e12, peak=PEAK_BF16_FLOPS / 1e12, unit="TFLOP/s",
-                        frac=a / PEAK_BF16_FLOPS, traffic=None)
+            return dict(bound="mfma", achieved=a / 1e12, peak=peak / 1e12, unit="TFLOP/s",
+                        frac=a / peak, traffic=traffic_record(name),
+                        dtype="fp8 e4m3" if name.endswith("fp8") else "bf16")
         bytes_ = {"attend_blocks": wm["attend_bytes"], "merge_partials": wm["merge_bytes"],
                   "topk_select": wm["topk_bytes"],
-                  "index_score_decode": wm["decode_bytes"] - wm["sel_total"] * BLOCK * w.head_dim * 4}
+                  "index_score_decode": wm["decode_bytes"] - wm["sel_total"] * BLOCK * w.head_dim * 4,
+                  "index_score_decode_fp8": wm["index_decode_fp8_bytes"],
+                  "quantize_index_fp8": wm["quant_bytes"]}
         if name in bytes_:
             per_launch = bytes_[name] / n_launch
             a = per_launch / sec
@@ -388,7 +452,7 @@ def main():
     value = w.total_q / (ms_per_step / 1e3)
     extra = {}
     if decode:
-        gbs = wm["decode_bytes"] / (ms_per_step / 1e3) / 1e9
+        gbs = wm["decode_fp8_bytes" if fp8 is not None else "decode_bytes"] / (ms_per_step / 1e3) / 1e9
         extra["decode_hbm_GBps"] = gbs
         extra["decode_hbm_frac"] = gbs * 1e9 / PEAK_HBM_BYTES
 
@@ -408,10 +472,20 @@ def main():
             kk, vv = _LazyDevRows(t["k"]), _LazyDevRows(t["v"])
             kidx = t["k_idx"].float().cpu().numpy()
 
+        if fp8 is not None:
+            # the oracle scores the dequantised codes it computes itself from the bf16 inputs
+            from oracle import fp8_index as F
+            nbk = int((np.diff(cuk).max() + BLOCK - 1) // BLOCK)
+            kc, ke = F.quantize_k_idx(kidx, cuk, nbk)
+            kidx = F.dequantize_k_idx(kc, ke, cuk)
+            del kc
+
         def host_rows(rows):
             ridx = torch.as_tensor(rows, device=dev, dtype=torch.long)
-            return (t["q"].index_select(0, ridx).float().cpu().numpy(),
-                    t["q_idx"].index_select(0, ridx).float().cpu().numpy())
+            qi = t["q_idx"].index_select(0, ridx).float().cpu().numpy()
+            if fp8 is not None:
+                qi = F.dequantize_q_idx(*F.quantize_q_idx(qi))
+            return t["q"].index_select(0, ridx).float().cpu().numpy(), qi
 
         # per-row cost on one core, then a sample sized to the time target
         pilot = sorted(set(int(x) for x in rng.integers(0, w.total_q, size=min(6, w.total_q))))
@@ -443,12 +517,13 @@ def main():
         sel_g = bufs.sel.index_select(0, ridx).cpu().numpy()
         out_g = bufs.out.index_select(0, ridx).float().cpu().numpy()
         lse_g = bufs.lse.index_select(0, ridx).cpu().numpy()
-        parity = parity_on_rows(P, rows, ref, sel_g, out_g, lse_g, w.top_k)
+        parity = parity_on_rows(P, rows, ref, sel_g, out_g, lse_g, w.top_k, fp8=fp8 is not None)
         log(f"[bench] parity on sampled rows: {parity}")
         cpu = dict(value=len(rows) / dt, unit="tokens/s", cores=used, kind="oracle",
                    sample=f"{len(rows)} uniformly random query rows of {w.name}, each through the "
-                          f"full Index and Main Branch in fp64 numpy; {used} worker process(es), "
-                          f"1 BLAS thread each; {dt:.1f} s")
+                          f"full Index and Main Branch in fp64 numpy"
+                          f"{' (on the dequantised fp8 index projections)' if fp8 is not None else ''}; "
+                          f"{used} worker process(es), 1 BLAS thread each; {dt:.1f} s")
     elif pool:
         pool.close()
 
@@ -463,7 +538,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": "bf16" if fp8 is None else "bf16 (Main Branch), fp8 e4m3 (Index Branch)",
         "data": "synthetic",
         "graph": use_graph,
         "config": {"workload": w.name, "seq_k_lens": (w.seq_k_lens if len(w.seq_k_lens) <= 4 else
@@ -471,7 +546,8 @@ def main():
                    "total_q": w.total_q, "num_q_heads": w.num_q_heads,
                    "num_kv_heads": w.num_kv_heads, "head_dim": w.head_dim,
                    "index_dim": w.index_dim, "block": BLOCK, "top_k": w.top_k,
-                   "q_chunk": args.q_chunk, "parallelism": "single GPU"},
+                   "q_chunk": args.q_chunk, "index_branch": args.index,
+                   "parallelism": "single GPU"},
         "roofline": roof(dominant) if dominant else None,
         "dominant_kernel": dominant,
         "main_branch_mfma_frac": main_mfma_frac,

@@ -17,7 +17,8 @@ import torch
 __all__ = [
     "MSAError", "Dims", "OP_INDEX_SELECT", "OP_BUILD_LISTS", "OP_ATTEND", "load_library",
     "make_dims", "workspace_size", "index_select", "build_block_query_lists", "attend",
-    "msa_forward", "exported_symbols", "LIB_PATH", "HEADER_PATH",
+    "msa_forward", "exported_symbols", "LIB_PATH", "HEADER_PATH", "index_quantize_fp8",
+    "index_select_fp8", "Fp8Index",
 ]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -67,6 +68,10 @@ def load_library(path: str = LIB_PATH):
     lib.msa_workspace_size.argtypes = [DP, I32, ctypes.POINTER(SZ)]
     lib.msa_index_select.restype = I32
     lib.msa_index_select.argtypes = [DP, P, P, P, P, P, P, P, SZ, P]
+    lib.msa_index_quantize_fp8.restype = I32
+    lib.msa_index_quantize_fp8.argtypes = [DP, P, P, P, P, P, P, P, P]
+    lib.msa_index_select_fp8.restype = I32
+    lib.msa_index_select_fp8.argtypes = [DP, P, P, P, P, P, P, P, P, P, SZ, P]
     lib.msa_build_block_query_lists.restype = I32
     lib.msa_build_block_query_lists.argtypes = [DP, P, P, P, P, P, P, SZ, P]
     lib.msa_attend.restype = I32
@@ -96,7 +101,7 @@ def _check(status: int, where: str):
 def exported_symbols(header: str = HEADER_PATH) -> list:
     """Function names declared in include/msa.h."""
     txt = open(header).read()
-    return sorted(set(re.findall(r"\b(msa_[a-z_]+)\s*\(", txt)))
+    return sorted(set(re.findall(r"\b(msa_[a-z0-9_]+)\s*\(", txt)))
 
 
 def make_dims(*, batch, num_q_heads, num_kv_heads, head_dim, index_dim, top_k, total_q, total_k,
@@ -166,6 +171,63 @@ def index_select(dims, q_idx, k_idx, cu_seqlens_q, cu_seqlens_k, sel, sel_score=
     return sel
 
 
+class Fp8Index:
+    """E4M3 codes and E8M0 exponents of the index projections for fixed dims."""
+
+    def __init__(self, dims: Dims, device):
+        T, G, DI = dims.total_q, dims.num_kv_heads, dims.index_dim
+        dev = torch.device(device)
+        self.q_idx8 = torch.empty((T, G, DI), dtype=torch.uint8, device=dev)
+        self.q_exp = torch.empty((T, G), dtype=torch.uint8, device=dev)
+        self.k_idx8 = torch.empty((dims.total_k, DI), dtype=torch.uint8, device=dev)
+        self.k_exp = torch.empty((dims.batch, nb_max(dims)), dtype=torch.uint8, device=dev)
+
+
+def index_quantize_fp8(dims, q_idx, k_idx, cu_seqlens_k, fp8: Fp8Index, stream=None):
+    """bf16 index projections -> E4M3 codes with power-of-two scales (into `fp8`).
+
+    Either q_idx or k_idx may be None: that side is left as it is in `fp8`.
+    """
+    G, T, DI = dims.num_kv_heads, dims.total_q, dims.index_dim
+    if q_idx is not None:
+        _shape(q_idx, (T, G, DI), "q_idx")
+    if k_idx is not None:
+        _shape(k_idx, (dims.total_k, DI), "k_idx")
+    _shape(fp8.q_idx8, (T, G, DI), "q_idx8")
+    _shape(fp8.q_exp, (T, G), "q_exp")
+    _shape(fp8.k_idx8, (dims.total_k, DI), "k_idx8")
+    _shape(fp8.k_exp, (dims.batch, nb_max(dims)), "k_exp")
+    st = load_library().msa_index_quantize_fp8(
+        ctypes.byref(dims), _ptr(q_idx, "q_idx", torch.bfloat16), _ptr(k_idx, "k_idx", torch.bfloat16),
+        _ptr(cu_seqlens_k, "cu_seqlens_k", torch.int32), _ptr(fp8.q_idx8, "q_idx8", torch.uint8),
+        _ptr(fp8.q_exp, "q_exp", torch.uint8), _ptr(fp8.k_idx8, "k_idx8", torch.uint8),
+        _ptr(fp8.k_exp, "k_exp", torch.uint8), _stream(stream))
+    _check(st, "msa_index_quantize_fp8")
+    return fp8
+
+
+def index_select_fp8(dims, fp8: Fp8Index, cu_seqlens_q, cu_seqlens_k, sel, sel_score=None,
+                     workspace=None, stream=None):
+    """Index Branch on the quantised projections (see msa_index_select_fp8)."""
+    G, T = dims.num_kv_heads, dims.total_q
+    _shape(fp8.q_idx8, (T, G, dims.index_dim), "q_idx8")
+    _shape(fp8.k_idx8, (dims.total_k, dims.index_dim), "k_idx8")
+    _shape(fp8.q_exp, (T, G), "q_exp")
+    _shape(fp8.k_exp, (dims.batch, nb_max(dims)), "k_exp")
+    _shape(sel, (T, G, dims.top_k), "sel")
+    if sel_score is not None:
+        _shape(sel_score, (T, G, dims.top_k), "sel_score")
+    ws = _workspace(dims, OP_INDEX_SELECT, workspace, sel.device)
+    st = load_library().msa_index_select_fp8(
+        ctypes.byref(dims), _ptr(fp8.q_idx8, "q_idx8", torch.uint8), _ptr(fp8.q_exp, "q_exp", torch.uint8),
+        _ptr(fp8.k_idx8, "k_idx8", torch.uint8), _ptr(fp8.k_exp, "k_exp", torch.uint8),
+        _ptr(cu_seqlens_q, "cu_seqlens_q", torch.int32), _ptr(cu_seqlens_k, "cu_seqlens_k", torch.int32),
+        _ptr(sel, "sel", torch.int32), _ptr(sel_score, "sel_score", torch.float32),
+        _ptr(ws, "workspace"), ctypes.c_size_t(ws.numel() * ws.element_size()), _stream(stream))
+    _check(st, "msa_index_select_fp8")
+    return sel
+
+
 def build_block_query_lists(dims, sel, cu_seqlens_q, cu_seqlens_k, block_offsets, block_entries,
                             workspace=None, stream=None):
     U = dims.batch * dims.num_kv_heads * nb_max(dims)
@@ -221,14 +283,22 @@ class Buffers:
 
 
 def msa_forward(dims: Dims, q, k, v, q_idx, k_idx, cu_seqlens_q, cu_seqlens_k, bufs: Buffers = None,
-                stream=None) -> Buffers:
+                stream=None, fp8: Fp8Index = None) -> Buffers:
     """The whole hot path: index_select -> build_block_query_lists -> attend.
 
     One workspace serves the three calls (they run in order on one stream).
+    With `fp8` given, the Index Branch quantises q_idx and k_idx into it and
+    selects on the codes (index_quantize_fp8 -> index_select_fp8); k_idx=None
+    keeps the key codes already in `fp8` (a quantised index-key cache).
     """
     bufs = bufs or Buffers(dims, q.device)
-    index_select(dims, q_idx, k_idx, cu_seqlens_q, cu_seqlens_k, bufs.sel, bufs.sel_score,
-                 bufs.workspace, stream)
+    if fp8 is None:
+        index_select(dims, q_idx, k_idx, cu_seqlens_q, cu_seqlens_k, bufs.sel, bufs.sel_score,
+                     bufs.workspace, stream)
+    else:
+        index_quantize_fp8(dims, q_idx, k_idx, cu_seqlens_k, fp8, stream)
+        index_select_fp8(dims, fp8, cu_seqlens_q, cu_seqlens_k, bufs.sel, bufs.sel_score,
+                         bufs.workspace, stream)
     build_block_query_lists(dims, bufs.sel, cu_seqlens_q, cu_seqlens_k, bufs.offsets, bufs.entries,
                             bufs.workspace, stream)
     attend(dims, q, k, v, cu_seqlens_q, cu_seqlens_k, bufs.sel, bufs.offsets, bufs.entries,
@@ -236,7 +306,7 @@ def msa_forward(dims: Dims, q, k, v, q_idx, k_idx, cu_seqlens_q, cu_seqlens_k, b
     return bufs
 
 
-PROFILE_KERNELS = 6
+PROFILE_KERNELS = 9
 
 
 def profile_enable(on: bool = True):

@@ -1,0 +1,550 @@
+// Quantised Index Branch: 8-bit index queries and keys.
+//
+// The pages state that the production model runs the sparse-attention indexer
+// (and Main Branch) with 8-bit queries and 8-bit keys, moving to 4-bit keys
+// (MSA guide, ai-tool-zukan.com/minimax-msa-guide, discussion of the model
+// card's quantisation notes).  The format and scaling are not given; this
+// file implements OCP FP8 E4M3 codes with power-of-two (E8M0) scales, one per
+// (query row, group) of q_idx and one per (sequence, 128-token block) of
+// k_idx.  The selection rule is the one of the bf16 path (token scores,
+// block max-pool, forced local block, top_k - 1 others; sections
+// "2段階構造の中身" and "クエリを含むローカルブロックの強制取り込み"), evaluated on
+// the dequantised values.
+//
+// Because a key block's scale 2^ek is one positive factor for all its keys,
+// max_j (2^eq q8 . 2^ek k8_j) = 2^(eq + ek) max_j (q8 . k8_j): the kernels
+// contract raw codes on the fp8 MFMA and apply the two exponents once per
+// (row, block), exactly (ldexp).
+#include "msa_common.h"
+#include "topk_common.h"
+
+namespace msa {
+
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+
+// 32x32x64 MFMA on OCP E4M3 operands (A and B format code 0), fp32
+// accumulate, no block scaling.  Same output layout as mfma32; each lane half
+// supplies 32 of the 64 contraction bytes of its row / column, with the same
+// assignment in A and B.
+__device__ inline f32x16 mfma32_fp8(i32x8 a, i32x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+}
+
+__device__ inline i32x8 as_i32x8(uint4 lo, uint4 hi) {
+  i32x8 r;
+  r[0] = (int)lo.x; r[1] = (int)lo.y; r[2] = (int)lo.z; r[3] = (int)lo.w;
+  r[4] = (int)hi.x; r[5] = (int)hi.y; r[6] = (int)hi.z; r[7] = (int)hi.w;
+  return r;
+}
+
+// Smallest e with amax * 2^-e <= 448 (the largest E4M3 value), clamped to
+// [-127, 127]; 0 for amax == 0.  amax = f * 2^E with f in [0.5, 1):
+// f * 2^9 <= 448 exactly when f <= 0.875.
+__device__ inline int fp8_scale_exponent(float amax) {
+  if (amax == 0.f) return 0;
+  int E;
+  const float f = frexpf(amax, &E);
+  const int e = f <= 0.875f ? E - 9 : E - 8;
+  return min(127, max(-127, e));
+}
+
+// Eight bf16 values -> eight E4M3 codes of x * 2^-e (exact scaling, then one
+// round-to-nearest-even conversion), little-endian in two dwords.
+__device__ inline uint2 quantize8(const float (&x)[8], int e) {
+  float y[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) y[i] = fminf(448.f, fmaxf(-448.f, ldexpf(x[i], -e)));
+  int w0 = __builtin_amdgcn_cvt_pk_fp8_f32(y[0], y[1], 0, false);
+  w0 = __builtin_amdgcn_cvt_pk_fp8_f32(y[2], y[3], w0, true);
+  int w1 = __builtin_amdgcn_cvt_pk_fp8_f32(y[4], y[5], 0, false);
+  w1 = __builtin_amdgcn_cvt_pk_fp8_f32(y[6], y[7], w1, true);
+  return make_uint2((uint32_t)w0, (uint32_t)w1);
+}
+
+__device__ inline void unpack8_bf16(uint4 v, float (&x)[8]) {
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    x[2 * i] = __uint_as_float(w[i] << 16);
+    x[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Quantisation.  q rows: DI / 8 lanes per (query, group) row, each converting
+// 8 elements; the row maximum is a shuffle reduction inside the row's lanes.
+// ---------------------------------------------------------------------------
+template <int DI>
+__global__ __launch_bounds__(256) void quantize_q_kernel(const uint16_t* __restrict__ q,
+                                                         long long rows,
+                                                         uint8_t* __restrict__ q8,
+                                                         uint8_t* __restrict__ qe) {
+  constexpr int LPR = DI / 8;
+  const long long t = (long long)blockIdx.x * 256 + threadIdx.x;
+  const long long row = t / LPR;
+  const int c = (int)(t % LPR);
+  const bool ok = row < rows;
+  uint4 v = make_uint4(0, 0, 0, 0);
+  if (ok) v = *reinterpret_cast<const uint4*>(q + row * DI + c * 8);
+  float x[8];
+  unpack8_bf16(v, x);
+  float a = 0.f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) a = fmaxf(a, fabsf(x[i]));
+#pragma unroll
+  for (int off = LPR / 2; off >= 1; off >>= 1) a = fmaxf(a, shfl_xor_f(a, off));
+  const int e = fp8_scale_exponent(a);
+  const uint2 w = quantize8(x, e);
+  if (ok) {
+    *reinterpret_cast<uint2*>(q8 + row * DI + c * 8) = w;
+    if (c == 0) qe[row] = (uint8_t)(e + 127);
+  }
+}
+
+// k blocks: one workgroup per (block beta, sequence b); block maximum over the
+// block's keys that belong to the sequence; blocks past its end get 127.
+template <int DI>
+__global__ __launch_bounds__(256) void quantize_k_kernel(const uint16_t* __restrict__ k,
+                                                         const int32_t* __restrict__ cu_k,
+                                                         int nb_max, uint8_t* __restrict__ k8,
+                                                         uint8_t* __restrict__ ke) {
+  constexpr int LPR = DI / 8;                      // 16-byte bf16 chunks per key row
+  constexpr int PER = kBlock * LPR / 256;          // chunks per thread
+  __shared__ float red[4];
+  const int beta = blockIdx.x, b = blockIdx.y;
+  const int koff = cu_k[b], lk = cu_k[b + 1] - koff;
+  const int n = min(kBlock, lk - beta * kBlock);   // keys of this block in the sequence
+  const int tid = threadIdx.x;
+  if (n <= 0) {
+    if (tid == 0) ke[(size_t)b * nb_max + beta] = 127;
+    return;
+  }
+  const uint16_t* src = k + ((size_t)koff + (size_t)beta * kBlock) * DI;
+  float x[PER][8];
+  float a = 0.f;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int c = tid + i * 256, row = c / LPR, col = c % LPR;
+    uint4 v = make_uint4(0, 0, 0, 0);
+    if (row < n) v = *reinterpret_cast<const uint4*>(src + (size_t)row * DI + col * 8);
+    unpack8_bf16(v, x[i]);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) a = fmaxf(a, fabsf(x[i][j]));
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) a = fmaxf(a, shfl_xor_f(a, off));
+  if ((tid & 63) == 0) red[tid >> 6] = a;
+  __syncthreads();
+  a = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  const int e = fp8_scale_exponent(a);
+  uint8_t* dst = k8 + ((size_t)koff + (size_t)beta * kBlock) * DI;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int c = tid + i * 256, row = c / LPR, col = c % LPR;
+    const uint2 w = quantize8(x[i], e);
+    if (row < n) *reinterpret_cast<uint2*>(dst + (size_t)row * DI + col * 8) = w;
+  }
+  if (tid == 0) ke[(size_t)b * nb_max + beta] = (uint8_t)(e + 127);
+}
+
+// ---------------------------------------------------------------------------
+// Prefill scoring + selection on E4M3 codes.  Same organisation as the bf16
+// prefill kernel: a workgroup owns RT * NW * 32 (query, group) rows of one
+// sequence, waves hold their rows' index queries as MFMA B operands, key
+// blocks stream through a three-buffer LDS ring filled by direct
+// global->LDS loads, and every lane keeps its row's running top-(k-1) list.
+// ---------------------------------------------------------------------------
+// Ring of 128 x DI-byte key blocks.  One wave instruction fills 1 KiB (lane L
+// -> bytes 16L..16L+15): 64 / CPR whole rows of CPR = DI / 16 chunks.  Chunk c
+// of row m is stored at chunk position c ^ (m % CPR) (chosen through the
+// source address), so fragment reads of consecutive rows spread over banks.
+template <int DI, int NW>
+struct KRing8 {
+  static constexpr int CPR = DI / 16;
+  static constexpr int ROWS_PER_INSTR = 64 / CPR;
+  static constexpr int INSTR = kBlock / ROWS_PER_INSTR;          // 1 KiB pieces per block
+  static constexpr int PER_WAVE = INSTR >= NW ? INSTR / NW : 1;  // loads per loading wave
+  static constexpr int LOADERS = INSTR >= NW ? NW : INSTR;       // waves that load
+  static_assert(INSTR < NW || INSTR % NW == 0, "block must split evenly over the waves");
+
+  __device__ static inline void load(const uint8_t* __restrict__ kbase, int blk, uint8_t* buf,
+                                     int wave, int lane) {
+    if (wave >= LOADERS) return;
+#pragma unroll
+    for (int i = 0; i < PER_WAVE; ++i) {
+      const int piece = wave * PER_WAVE + i;
+      const int m = piece * ROWS_PER_INSTR + lane / CPR;
+      const int lc = (lane % CPR) ^ (m % CPR);
+      const uint8_t* src = kbase + ((size_t)blk * kBlock + m) * DI + lc * 16;
+      __builtin_amdgcn_global_load_lds(src, buf + piece * 1024, 16, 0, 0);
+    }
+  }
+  __device__ static inline uint4 chunk(const uint8_t* buf, int m, int lc) {
+    return *reinterpret_cast<const uint4*>(buf + m * DI + ((lc ^ (m % CPR)) * 16));
+  }
+  // A fragment of k-step ks for lane half h: logical chunks 4ks + 2h, +1
+  // (DI = 32: chunk h and 16 zero bytes)
+  __device__ static inline i32x8 frag(const uint8_t* buf, int m, int ks, int h) {
+    if constexpr (DI == 32) {
+      return as_i32x8(chunk(buf, m, h), make_uint4(0, 0, 0, 0));
+    } else {
+      return as_i32x8(chunk(buf, m, 4 * ks + 2 * h), chunk(buf, m, 4 * ks + 2 * h + 1));
+    }
+  }
+};
+
+constexpr int kFp8ExpLds = 16384;   // key blocks per sequence whose exponents fit on chip
+
+template <int DI, int RT, int NW, int KCAP>
+__global__ __launch_bounds__(NW * 64) void index_select_prefill_fp8_kernel(
+    const uint8_t* __restrict__ q8, const uint8_t* __restrict__ qe, const uint8_t* __restrict__ k8,
+    const uint8_t* __restrict__ ke, const int32_t* __restrict__ cu_q,
+    const int32_t* __restrict__ cu_k, int G, int nb_max, int qt, int top_k,
+    int32_t* __restrict__ sel, float* __restrict__ sel_score) {
+  static_assert(RT == 1 || RT == 2, "a lane owns at most one row");
+  using Ring = KRing8<DI, NW>;
+  constexpr int KS = DI >= 64 ? DI / 64 : 1;   // MFMA k-steps over the index dim
+  __shared__ __attribute__((aligned(1024))) uint8_t ring0[kBlock * DI];
+  __shared__ __attribute__((aligned(1024))) uint8_t ring1[kBlock * DI];
+  __shared__ __attribute__((aligned(1024))) uint8_t ring2[kBlock * DI];
+  __shared__ uint8_t kexp[kFp8ExpLds];
+
+  const int b = blockIdx.y;
+  const int qoff = cu_q[b], lq = cu_q[b + 1] - qoff;
+  const int koff = cu_k[b], lk = cu_k[b + 1] - koff;
+  const int tile = (int)(gridDim.x - 1 - blockIdx.x);   // latest query tiles first
+  const int qa = qoff + tile * qt;
+  const int qz = min(qoff + lq, qa + qt);
+  if (qa >= qz) return;
+  const int p_last = lk - lq + (qz - 1 - qoff);
+  const int beta_hi = min(p_last / kBlock, kFp8ExpLds);
+  const int nrows = (qz - qa) * G;
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  const int col = lane & 31;
+  const int half = lane >> 5;
+
+  const bool owner = half < RT;
+  const int n_own = (wave * RT + (owner ? half : 0)) * 32 + col;
+  const bool own_valid = owner && n_own < nrows;
+  const int q_own = qa + n_own / G, g_own = n_own % G;
+  const int beta_own = own_valid ? (lk - lq + (q_own - qoff)) / kBlock : 0;
+  const int eq_own = own_valid ? (int)qe[(size_t)q_own * G + g_own] - 127 : 0;
+  uint64_t list[KCAP];
+#pragma unroll
+  for (int i = 0; i < KCAP; ++i) list[i] = 0;
+
+  if (beta_hi > 0) {
+    // the sequence's key-block exponents, staged once
+    for (int i = tid; i < beta_hi; i += NW * 64) kexp[i] = ke[(size_t)b * nb_max + i];
+
+    i32x8 qf[RT][KS];
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+      const int n = (wave * RT + rt) * 32 + col;
+      const uint8_t* src = q8 + ((size_t)qa * G + min(n, nrows - 1)) * DI;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        uint4 lo, hi = make_uint4(0, 0, 0, 0);
+        if constexpr (DI == 32) {
+          lo = *reinterpret_cast<const uint4*>(src + half * 16);
+        } else {
+          lo = *reinterpret_cast<const uint4*>(src + ks * 64 + half * 32);
+          hi = *reinterpret_cast<const uint4*>(src + ks * 64 + half * 32 + 16);
+        }
+        if (n >= nrows) lo = hi = make_uint4(0, 0, 0, 0);
+        qf[rt][ks] = as_i32x8(lo, hi);
+      }
+    }
+    __syncthreads();   // exponents visible; every earlier load has landed
+
+    const uint8_t* kbase = k8 + (size_t)koff * DI;
+    Ring::load(kbase, 0, ring0, wave, lane);
+    if (beta_hi > 1) Ring::load(kbase, 1, ring1, wave, lane);
+
+    auto step = [&](int beta, const uint8_t* rbuf, uint8_t* lbuf) __attribute__((always_inline)) {
+      // this wave's pieces of block beta have landed (only beta+1 may be
+      // younger); the barrier publishes every wave's pieces and retires the
+      // reads of the buffer about to be refilled
+      if (beta + 1 < beta_hi) wait_vmcnt<Ring::PER_WAVE>(); else wait_vmcnt<0>();
+      __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0)
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+      if (beta + 2 < beta_hi) Ring::load(kbase, beta + 2, lbuf, wave, lane);
+
+      float rmax[RT];
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt) rmax[rt] = -INFINITY;
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt) {
+        i32x8 a[KS];
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) a[ks] = Ring::frag(rbuf, kt * 32 + col, ks, half);
+        f32x16 acc[RT];
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) acc[rt] = f32x16{};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+          for (int rt = 0; rt < RT; ++rt) acc[rt] = mfma32_fp8(a[ks], qf[rt][ks], acc[rt]);
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) rmax[rt] = fmaxf(rmax[rt], acc[rt][i]);
+      }
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt) rmax[rt] = fmaxf(rmax[rt], shfl_xor_f(rmax[rt], 32));
+      const float mine = (RT == 1 || half == 0) ? rmax[0] : rmax[RT - 1];
+      const float score = ldexpf(mine, eq_own + (int)kexp[beta] - 127);
+      if (beta < beta_own && score == score) list_insert(list, make_key(score, beta));
+    };
+
+    for (int beta = 0; beta < beta_hi; beta += 3) {
+      step(beta, ring0, ring2);
+      if (beta + 1 < beta_hi) step(beta + 1, ring1, ring0);
+      if (beta + 2 < beta_hi) step(beta + 2, ring2, ring1);
+    }
+  }
+  if (own_valid) {
+    const size_t o = ((size_t)q_own * G + g_own) * top_k;
+    write_selection(list, top_k - 1, beta_own, top_k, sel + o, sel_score ? sel_score + o : nullptr);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Decode scoring on E4M3 codes: at most 32 rows per sequence; grid.x = key-block
+// segment, grid.y = sequence; wave w computes keys 32w .. 32w+31 of each block.
+// Writes S[beta * ld + row] = 2^(eq + ek) * max_j (q8 . k8_j) for the wide top-k.
+// ---------------------------------------------------------------------------
+// One 128 x DI-byte key block through registers into a padded LDS tile
+// (row stride DI + 16 bytes).
+template <int DI, int NT>
+struct KTileStage8 {
+  static constexpr int kCpr = DI / 16;
+  static constexpr int kChunks = kBlock * kCpr;
+  static constexpr int kPer = (kChunks + NT - 1) / NT;
+  static constexpr int kLd = DI + 16;
+  uint4 r[kPer];
+
+  __device__ inline void load(const uint8_t* __restrict__ src, int tid) {
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const int c = tid + i * NT;
+      if (kChunks % NT == 0 || c < kChunks)
+        r[i] = *reinterpret_cast<const uint4*>(src + (size_t)(c / kCpr) * DI + (c % kCpr) * 16);
+    }
+  }
+  __device__ inline void store(uint8_t* lds, int tid) const {
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const int c = tid + i * NT;
+      if (kChunks % NT == 0 || c < kChunks)
+        *reinterpret_cast<uint4*>(lds + (c / kCpr) * kLd + (c % kCpr) * 16) = r[i];
+    }
+  }
+};
+
+template <int DI, int SEG>
+__global__ __launch_bounds__(256) void index_score_decode_fp8_kernel(
+    const uint8_t* __restrict__ q8, const uint8_t* __restrict__ qe, const uint8_t* __restrict__ k8,
+    const uint8_t* __restrict__ ke, const int32_t* __restrict__ cu_q,
+    const int32_t* __restrict__ cu_k, int G, int nb_max, int r0, int r1, float* __restrict__ S,
+    long long ld) {
+  constexpr int NT = 256;
+  constexpr int KS = DI >= 64 ? DI / 64 : 1;
+  constexpr int LD = KTileStage8<DI, NT>::kLd;
+  __shared__ __attribute__((aligned(16))) uint8_t lds[2][kBlock * LD];
+  __shared__ float red[2][4][32];
+
+  const int b = blockIdx.y;
+  const int qoff = cu_q[b], lq = cu_q[b + 1] - qoff;
+  const int koff = cu_k[b], lk = cu_k[b + 1] - koff;
+  const int qa = max(qoff, r0), qz = min(qoff + lq, r1);
+  if (qa >= qz) return;
+  const int p_last = lk - lq + (qz - 1 - qoff);
+  const int beta_hi = p_last / kBlock;
+  const int b0 = (int)blockIdx.x * SEG;
+  const int b1 = min(beta_hi, b0 + SEG);
+  if (b0 >= b1) return;
+  const int nrows = min((qz - qa) * G, 32);
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  const int lane = tid & 63;
+  const int col = lane & 31;
+  const int half = lane >> 5;
+
+  i32x8 qf[KS];
+  {
+    const uint8_t* src = q8 + ((size_t)qa * G + col) * DI;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      uint4 lo = make_uint4(0, 0, 0, 0), hi = make_uint4(0, 0, 0, 0);
+      if (col < nrows) {
+        if constexpr (DI == 32) {
+          lo = *reinterpret_cast<const uint4*>(src + half * 16);
+        } else {
+          lo = *reinterpret_cast<const uint4*>(src + ks * 64 + half * 32);
+          hi = *reinterpret_cast<const uint4*>(src + ks * 64 + half * 32 + 16);
+        }
+      }
+      qf[ks] = as_i32x8(lo, hi);
+    }
+  }
+  const int eq_lane = lane < nrows ? (int)qe[(size_t)qa * G + lane] - 127 : 0;
+
+  const uint8_t* kbase = k8 + (size_t)koff * DI;
+  KTileStage8<DI, NT> stage;
+  stage.load(kbase + (size_t)b0 * kBlock * DI, tid);
+  stage.store(lds[0], tid);
+  __syncthreads();
+
+  const size_t srow = (size_t)(qa - r0) * G;
+  for (int beta = b0; beta < b1; ++beta) {
+    const int it = beta - b0;
+    stage.load(kbase + (size_t)min(beta + 1, b1 - 1) * kBlock * DI, tid);
+    // finish the previous block's reduction (its partial maxima are complete)
+    if (it > 0 && wave == 0 && lane < nrows) {
+      const float* rr = &red[(it - 1) & 1][0][0];
+      const float m = fmaxf(fmaxf(rr[lane], rr[32 + lane]), fmaxf(rr[64 + lane], rr[96 + lane]));
+      const int ek = (int)ke[(size_t)b * nb_max + beta - 1] - 127;
+      S[(size_t)(beta - 1) * ld + srow + lane] = ldexpf(m, eq_lane + ek);
+    }
+    const uint8_t* kt_lds = lds[it & 1];
+    const uint8_t* arow = kt_lds + (wave * 32 + col) * LD;
+    f32x16 acc = f32x16{};
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      i32x8 a;
+      if constexpr (DI == 32) {
+        a = as_i32x8(*reinterpret_cast<const uint4*>(arow + half * 16), make_uint4(0, 0, 0, 0));
+      } else {
+        a = as_i32x8(*reinterpret_cast<const uint4*>(arow + ks * 64 + half * 32),
+                     *reinterpret_cast<const uint4*>(arow + ks * 64 + half * 32 + 16));
+      }
+      acc = mfma32_fp8(a, qf[ks], acc);
+    }
+    float m = acc[0];
+#pragma unroll
+    for (int i = 1; i < 16; ++i) m = fmaxf(m, acc[i]);
+    m = fmaxf(m, shfl_xor_f(m, 32));
+    if (half == 0) red[it & 1][wave][col] = m;
+    stage.store(lds[(it + 1) & 1], tid);
+    __syncthreads();
+  }
+  if (wave == 0 && lane < nrows) {
+    const int it = b1 - 1 - b0;
+    const float* rr = &red[it & 1][0][0];
+    const float m = fmaxf(fmaxf(rr[lane], rr[32 + lane]), fmaxf(rr[64 + lane], rr[96 + lane]));
+    const int ek = (int)ke[(size_t)b * nb_max + b1 - 1] - 127;
+    S[(size_t)(b1 - 1) * ld + srow + lane] = ldexpf(m, eq_lane + ek);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// launchers
+// ---------------------------------------------------------------------------
+constexpr int kFp8RT = 2;
+constexpr int kFp8NW = 8;
+constexpr int kFp8Rows = kFp8RT * kFp8NW * 32;
+constexpr int kFp8DecodeSeg = 8;
+
+int fp8_max_blocks_per_sequence() { return kFp8ExpLds; }
+
+template <int DI>
+static hipError_t launch_quantize_di(const void* q, const void* k, const int32_t* cu_k, int batch,
+                                     int nb_max, long long q_rows, void* q8, uint8_t* qe, void* k8,
+                                     uint8_t* ke, hipStream_t st) {
+  if (q_rows > 0) {
+    const long long threads = q_rows * (DI / 8);
+    hipLaunchKernelGGL((quantize_q_kernel<DI>), dim3((unsigned)((threads + 255) / 256)), dim3(256),
+                       0, st, (const uint16_t*)q, q_rows, (uint8_t*)q8, qe);
+  }
+  if (nb_max > 0)
+    hipLaunchKernelGGL((quantize_k_kernel<DI>), dim3(nb_max, batch), dim3(256), 0, st,
+                       (const uint16_t*)k, cu_k, nb_max, (uint8_t*)k8, ke);
+  return hipGetLastError();
+}
+
+hipError_t launch_quantize_index_fp8(int DI, const void* q, const void* k, const int32_t* cu_k,
+                                     int batch, int nb_max, long long q_rows, void* q8, uint8_t* qe,
+                                     void* k8, uint8_t* ke, hipStream_t st) {
+  switch (DI) {
+    case 32: return launch_quantize_di<32>(q, k, cu_k, batch, nb_max, q_rows, q8, qe, k8, ke, st);
+    case 64: return launch_quantize_di<64>(q, k, cu_k, batch, nb_max, q_rows, q8, qe, k8, ke, st);
+    case 128: return launch_quantize_di<128>(q, k, cu_k, batch, nb_max, q_rows, q8, qe, k8, ke, st);
+  }
+  return hipErrorInvalidValue;
+}
+
+template <int DI, int KCAP>
+static hipError_t launch_prefill8_t(const void* q8, const uint8_t* qe, const void* k8,
+                                    const uint8_t* ke, const int32_t* cu_q, const int32_t* cu_k,
+                                    int batch, int G, int nb_max, int max_q_len, int top_k,
+                                    int32_t* sel, float* sel_score, hipStream_t st) {
+  const int qt = kFp8Rows / G;
+  if (qt < 1) return hipErrorInvalidValue;
+  dim3 grid((max_q_len + qt - 1) / qt, batch);
+  hipLaunchKernelGGL((index_select_prefill_fp8_kernel<DI, kFp8RT, kFp8NW, KCAP>), grid,
+                     dim3(kFp8NW * 64), 0, st, (const uint8_t*)q8, qe, (const uint8_t*)k8, ke, cu_q,
+                     cu_k, G, nb_max, qt, top_k, sel, sel_score);
+  return hipGetLastError();
+}
+
+template <int DI>
+static hipError_t launch_prefill8_di(const void* q8, const uint8_t* qe, const void* k8,
+                                     const uint8_t* ke, const int32_t* cu_q, const int32_t* cu_k,
+                                     int batch, int G, int nb_max, int max_q_len, int top_k,
+                                     int32_t* sel, float* sel_score, hipStream_t st) {
+  const int km = top_k - 1;
+#define MSA_PF8(K) launch_prefill8_t<DI, K>(q8, qe, k8, ke, cu_q, cu_k, batch, G, nb_max, max_q_len, top_k, sel, sel_score, st)
+  if (km <= 1) return MSA_PF8(1);
+  if (km <= 2) return MSA_PF8(2);
+  if (km <= 4) return MSA_PF8(4);
+  if (km <= 8) return MSA_PF8(8);
+  if (km <= 16) return MSA_PF8(16);
+  return MSA_PF8(32);
+#undef MSA_PF8
+}
+
+hipError_t launch_index_select_prefill_fp8(const void* q8, const uint8_t* qe, const void* k8,
+                                           const uint8_t* ke, const int32_t* cu_q,
+                                           const int32_t* cu_k, int batch, int G, int DI,
+                                           int nb_max, int max_q_len, int top_k, int32_t* sel,
+                                           float* sel_score, hipStream_t st) {
+  switch (DI) {
+    case 32: return launch_prefill8_di<32>(q8, qe, k8, ke, cu_q, cu_k, batch, G, nb_max, max_q_len, top_k, sel, sel_score, st);
+    case 64: return launch_prefill8_di<64>(q8, qe, k8, ke, cu_q, cu_k, batch, G, nb_max, max_q_len, top_k, sel, sel_score, st);
+    case 128: return launch_prefill8_di<128>(q8, qe, k8, ke, cu_q, cu_k, batch, G, nb_max, max_q_len, top_k, sel, sel_score, st);
+  }
+  return hipErrorInvalidValue;
+}
+
+template <int DI>
+static hipError_t launch_decode8_di(const void* q8, const uint8_t* qe, const void* k8,
+                                    const uint8_t* ke, const int32_t* cu_q, const int32_t* cu_k,
+                                    int batch, int G, int nb_max, int r0, int r1, float* S,
+                                    long long ld, hipStream_t st) {
+  dim3 grid((nb_max + kFp8DecodeSeg - 1) / kFp8DecodeSeg, batch);
+  hipLaunchKernelGGL((index_score_decode_fp8_kernel<DI, kFp8DecodeSeg>), grid, dim3(256), 0, st,
+                     (const uint8_t*)q8, qe, (const uint8_t*)k8, ke, cu_q, cu_k, G, nb_max, r0, r1,
+                     S, ld);
+  return hipGetLastError();
+}
+
+hipError_t launch_index_score_decode_fp8(const void* q8, const uint8_t* qe, const void* k8,
+                                         const uint8_t* ke, const int32_t* cu_q,
+                                         const int32_t* cu_k, int batch, int G, int DI, int nb_max,
+                                         int r0, int r1, float* S, long long ld, hipStream_t st) {
+  switch (DI) {
+    case 32: return launch_decode8_di<32>(q8, qe, k8, ke, cu_q, cu_k, batch, G, nb_max, r0, r1, S, ld, st);
+    case 64: return launch_decode8_di<64>(q8, qe, k8, ke, cu_q, cu_k, batch, G, nb_max, r0, r1, S, ld, st);
+    case 128: return launch_decode8_di<128>(q8, qe, k8, ke, cu_q, cu_k, batch, G, nb_max, r0, r1, S, ld, st);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace msa

@@ -98,13 +98,6 @@ struct KRing {
   }
 };
 
-// vmcnt(n) with the other counters left alone (gfx9 s_waitcnt encoding)
-template <int N>
-__device__ inline void wait_vmcnt() {
-  static_assert(N >= 0 && N < 16, "small counts only");
-  __builtin_amdgcn_s_waitcnt(0x0F70 | N);
-}
-
 template <int DI, int RT, int NW, int KCAP>
 __global__ __launch_bounds__(NW * 64) void index_select_prefill_kernel(
     const uint16_t* __restrict__ q_idx, const uint16_t* __restrict__ k_idx,

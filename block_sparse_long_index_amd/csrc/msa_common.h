@@ -87,4 +87,11 @@ __device__ inline float float_from_order_key(uint32_t k) {
 
 __device__ inline float shfl_xor_f(float v, int mask) { return __shfl_xor(v, mask, kWave); }
 
+// vmcnt(n) with the other counters left alone (gfx9 s_waitcnt encoding)
+template <int N>
+__device__ inline void wait_vmcnt() {
+  static_assert(N >= 0 && N < 16, "small counts only");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | N);
+}
+
 }  // namespace msa

@@ -166,6 +166,56 @@ msa_status_t msa_attend(const msa_dims_t* dims, const void* q, const void* k, co
                         const int32_t* block_entries, void* out, float* lse, void* workspace,
                         size_t workspace_bytes, void* stream);
 
+/*
+ * Quantised Index Branch (optional; the bf16 calls above are the reference
+ * path).  The pages note that the production model runs the sparse
+ * attention's indexer with 8-bit queries and 8-bit keys (MSA guide, remarks on
+ * the model card's quantisation: indexer and Main Branch "Q8KV8", moving to
+ * 4-bit keys).  Format and scaling are this library's reading:
+ *   - codes are OCP FP8 E4M3 (bias 7, largest finite 448, no infinities);
+ *   - scales are powers of two stored as E8M0 bytes (value = 2^(byte - 127));
+ *   - one scale per (query row, group) of q_idx, one per (sequence, 128-token
+ *     KV block) of k_idx;
+ *   - a row's or block's exponent e is the smallest integer with
+ *     max|x| * 2^-e <= 448, clamped to [-127, 127] (0 for an all-zero row or
+ *     block); code = round-to-nearest-even E4M3 of x * 2^-e.
+ * Non-finite index inputs give unspecified codes.
+ *
+ * msa_index_quantize_fp8: bf16 index projections -> codes + exponents.
+ *   Either side may be left out by passing NULL as its input (its outputs
+ *   are then not touched): a decode step quantises its new index queries
+ *   against an index-key cache quantised once when it was written.
+ *   q_idx   bf16 [total_q, num_kv_heads, index_dim]   or NULL
+ *   k_idx   bf16 [total_k, index_dim]                 or NULL
+ *   q_idx8  uint8 E4M3 [total_q, num_kv_heads, index_dim]  out
+ *   q_exp   uint8 E8M0 [total_q, num_kv_heads]              out (no alignment needed)
+ *   k_idx8  uint8 E4M3 [total_k, index_dim]                 out
+ *   k_exp   uint8 E8M0 [batch, nb_max], nb_max = ceil(max_k_len / 128)   out;
+ *           k_exp[b, beta] scales keys cu_k[b] + 128 beta .. of sequence b;
+ *           blocks past a sequence's end get 127.
+ *   No workspace.  With total_q == 0 only the keys are quantised.  Keys are
+ *   quantised per whole block, so a key cache quantised this way is
+ *   re-quantised block by block as blocks fill (the selection never scores a
+ *   query's own, still filling, block).
+ *
+ * msa_index_select_fp8: msa_index_select on the dequantised values
+ *   q = decode(q_idx8) * 2^(q_exp - 127), k = decode(k_idx8) * 2^(k_exp - 127).
+ *   Token dot products of the codes accumulate in fp32 on the fp8 matrix
+ *   cores; since a block's scale is common to its keys, the block score is
+ *   2^(eq + ek) * max_j (q8 . k8_j), applied exactly.  Selection rule, tie
+ *   rule, outputs and workspace (msa_workspace_size with MSA_OP_INDEX_SELECT)
+ *   are those of msa_index_select; sel_score holds the dequantised block
+ *   scores.  Requires ceil(max_k_len / 128) <= 16384 (MSA_ERR_UNSUPPORTED).
+ */
+msa_status_t msa_index_quantize_fp8(const msa_dims_t* dims, const void* q_idx, const void* k_idx,
+                                    const int32_t* cu_seqlens_k, void* q_idx8, uint8_t* q_exp,
+                                    void* k_idx8, uint8_t* k_exp, void* stream);
+msa_status_t msa_index_select_fp8(const msa_dims_t* dims, const void* q_idx8, const uint8_t* q_exp,
+                                  const void* k_idx8, const uint8_t* k_exp,
+                                  const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                                  int32_t* sel, float* sel_score, void* workspace,
+                                  size_t workspace_bytes, void* stream);
+
 /* Static description of a status code. */
 const char* msa_status_string(msa_status_t status);
 
@@ -180,13 +230,14 @@ int32_t msa_abi_version(void);
  * enabled, every kernel stage a call launches is bracketed by two hipEvents
  * recorded on the call's stream.  Stage ids: 0 index_select_prefill (scores + top-k),
  * 1 index_score_decode, 2 topk_select, 3 build_lists (all list kernels),
- * 4 attend_blocks, 5 merge_partials.  msa_profile_collect() waits for every
+ * 4 attend_blocks, 5 merge_partials, 6 quantize_index_fp8,
+ * 7 index_select_prefill_fp8, 8 index_score_decode_fp8.  msa_profile_collect() waits for every
  * recorded event (it blocks the host), writes the summed milliseconds and the
  * launch count per stage into caller arrays of MSA_PROFILE_KERNELS entries,
  * and forgets the records.  Events are host-side HIP objects kept in a pool
  * for the life of the process; no device memory is allocated.
  */
-#define MSA_PROFILE_KERNELS 6
+#define MSA_PROFILE_KERNELS 9
 msa_status_t msa_profile_enable(int32_t enable);
 msa_status_t msa_profile_collect(float* total_ms, int32_t* launches);
 const char* msa_profile_kernel_name(int32_t id);

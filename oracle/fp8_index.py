@@ -176,7 +176,7 @@ def dequantize_k_idx(codes, ex, cu_seqlens_k, block=BLOCK):
     out = np.empty(vals.shape, dtype=np.float64)
     ex = np.asarray(ex, dtype=np.int64)
     for b in range(len(cu_k) - 1):
-        for j in range(int(cu_k[b]), int(cu_k[b + 1])):
-            beta = (j - int(cu_k[b])) // block
-            out[j] = np.ldexp(vals[j], int(ex[b, beta]) - E8M0_BIAS)
+        lo, hi = int(cu_k[b]), int(cu_k[b + 1])
+        beta = np.arange(hi - lo) // block                 # block of each key of sequence b
+        out[lo:hi] = np.ldexp(vals[lo:hi], (ex[b, beta] - E8M0_BIAS)[:, None])
     return out

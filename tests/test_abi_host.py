@@ -134,3 +134,33 @@ def test_product_path_does_not_import_oracle():
             if isinstance(node, (ast.Import, ast.ImportFrom)):
                 mods = [a.name for a in node.names] if isinstance(node, ast.Import) else [node.module or ""]
                 assert not any(m.split(".")[0] == "oracle" for m in mods), f
+
+
+def test_fp8_entry_points_validate_on_host():
+    d = _dims()
+    P = ctypes.c_void_p
+    ok = P(0x10000)
+    odd = P(0x10004)
+    big = ctypes.c_size_t(1 << 40)
+    qz = lib.msa_index_quantize_fp8
+    # a side with an input needs its outputs
+    assert qz(ctypes.byref(d), ok, None, None, None, ok, None, None, None) == 1
+    assert qz(ctypes.byref(d), None, ok, ok, None, None, ok, None, None) == 1
+    assert qz(ctypes.byref(d), None, ok, None, None, None, ok, ok, None) == 1
+    assert qz(ctypes.byref(d), ok, ok, ok, odd, ok, ok, ok, None) == 4
+    assert qz(ctypes.byref(d), None, ok, ok, None, None, odd, ok, None) == 4
+    # exponent arrays are bytes: no alignment asked of them (fails later on NULL k_exp)
+    assert qz(ctypes.byref(d), ok, ok, ok, ok, odd, ok, None, None) == 1
+    s8 = lib.msa_index_select_fp8
+    assert s8(ctypes.byref(d), ok, None, ok, ok, ok, ok, ok, None, ok, big, None) == 1
+    assert s8(ctypes.byref(d), ok, ok, odd, ok, ok, ok, ok, None, ok, big, None) == 4
+    assert s8(ctypes.byref(d), ok, ok, ok, ok, ok, ok, ok, None, ok, ctypes.c_size_t(8), None) == 5
+    # more key blocks per sequence than the kernels hold on chip
+    long = _dims(total_q=1, total_k=16385 * 128, max_q_len=1, max_k_len=16385 * 128)
+    assert s8(ctypes.byref(long), ok, ok, ok, ok, ok, ok, ok, None, ok, big, None) == 3
+    # no queries and no keys: nothing to do, success without touching pointers
+    empty = _dims(total_q=0, total_k=0, max_q_len=0, max_k_len=0)
+    assert qz(ctypes.byref(empty), None, None, None, None, None, None, None, None) == 0
+    # no inputs at all: nothing to quantise
+    assert qz(ctypes.byref(d), None, None, None, None, None, None, None, None) == 0
+    assert s8(ctypes.byref(empty), None, None, None, None, None, None, None, None, None, big, None) == 0
