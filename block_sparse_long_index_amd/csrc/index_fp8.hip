@@ -156,11 +156,14 @@ __global__ __launch_bounds__(256) void quantize_k_kernel(const uint16_t* __restr
 // ---------------------------------------------------------------------------
 // Ring of 128 x DI-byte key blocks.  One wave instruction fills 1 KiB (lane L
 // -> bytes 16L..16L+15): 64 / CPR whole rows of CPR = DI / 16 chunks.  Chunk c
-// of row m is stored at chunk position c ^ (m % CPR) (chosen through the
-// source address), so fragment reads of consecutive rows spread over banks.
+// of row m is stored at chunk position c ^ swz(m) (chosen through the source
+// address).  The 64 four-byte banks span 256 bytes, i.e. R = 16 / CPR rows, and
+// a fragment read serves 16 consecutive rows at a time; swz(m) = (m / R) % CPR
+// gives those 16 rows 16 different 16-byte bank groups.
 template <int DI, int NW>
 struct KRing8 {
   static constexpr int CPR = DI / 16;
+  static constexpr int R = 16 / CPR;                              // rows per 256-byte bank line
   static constexpr int ROWS_PER_INSTR = 64 / CPR;
   static constexpr int INSTR = kBlock / ROWS_PER_INSTR;          // 1 KiB pieces per block
   static constexpr int PER_WAVE = INSTR >= NW ? INSTR / NW : 1;  // loads per loading wave
@@ -174,13 +177,14 @@ struct KRing8 {
     for (int i = 0; i < PER_WAVE; ++i) {
       const int piece = wave * PER_WAVE + i;
       const int m = piece * ROWS_PER_INSTR + lane / CPR;
-      const int lc = (lane % CPR) ^ (m % CPR);
+      const int lc = (lane % CPR) ^ swz(m);
       const uint8_t* src = kbase + ((size_t)blk * kBlock + m) * DI + lc * 16;
       __builtin_amdgcn_global_load_lds(src, buf + piece * 1024, 16, 0, 0);
     }
   }
+  __device__ static inline int swz(int m) { return (m / R) % CPR; }
   __device__ static inline uint4 chunk(const uint8_t* buf, int m, int lc) {
-    return *reinterpret_cast<const uint4*>(buf + m * DI + ((lc ^ (m % CPR)) * 16));
+    return *reinterpret_cast<const uint4*>(buf + m * DI + ((lc ^ swz(m)) * 16));
   }
   // A fragment of k-step ks for lane half h: logical chunks 4ks + 2h, +1
   // (DI = 32: chunk h and 16 zero bytes)
@@ -196,7 +200,7 @@ struct KRing8 {
 constexpr int kFp8ExpLds = 16384;   // key blocks per sequence whose exponents fit on chip
 
 template <int DI, int RT, int NW, int KCAP>
-__global__ __launch_bounds__(NW * 64) void index_select_prefill_fp8_kernel(
+__global__ __launch_bounds__(NW * 64, 2) void index_select_prefill_fp8_kernel(
     const uint8_t* __restrict__ q8, const uint8_t* __restrict__ qe, const uint8_t* __restrict__ k8,
     const uint8_t* __restrict__ ke, const int32_t* __restrict__ cu_q,
     const int32_t* __restrict__ cu_k, int G, int nb_max, int qt, int top_k,
@@ -232,9 +236,8 @@ __global__ __launch_bounds__(NW * 64) void index_select_prefill_fp8_kernel(
   const int q_own = qa + n_own / G, g_own = n_own % G;
   const int beta_own = own_valid ? (lk - lq + (q_own - qoff)) / kBlock : 0;
   const int eq_own = own_valid ? (int)qe[(size_t)q_own * G + g_own] - 127 : 0;
-  uint64_t list[KCAP];
-#pragma unroll
-  for (int i = 0; i < KCAP; ++i) list[i] = 0;
+  OrderedTopList<KCAP> list;
+  list.clear();
 
   if (beta_hi > 0) {
     // the sequence's key-block exponents, staged once
@@ -261,6 +264,8 @@ __global__ __launch_bounds__(NW * 64) void index_select_prefill_fp8_kernel(
     __syncthreads();   // exponents visible; every earlier load has landed
 
     const uint8_t* kbase = k8 + (size_t)koff * DI;
+    uint32_t pending = 0;   // previous block's score key, inserted during the next block's MFMAs
+    int pending_beta = 0;
     Ring::load(kbase, 0, ring0, wave, lane);
     if (beta_hi > 1) Ring::load(kbase, 1, ring1, wave, lane);
 
@@ -275,31 +280,43 @@ __global__ __launch_bounds__(NW * 64) void index_select_prefill_fp8_kernel(
       asm volatile("" ::: "memory");
       if (beta + 2 < beta_hi) Ring::load(kbase, beta + 2, lbuf, wave, lane);
 
+      // software pipeline: the MFMAs of key tile kt+1 are issued before the
+      // row maxima of tile kt are taken, and the previous block's top-k
+      // insert runs while tile 0's MFMAs execute
       float rmax[RT];
 #pragma unroll
       for (int rt = 0; rt < RT; ++rt) rmax[rt] = -INFINITY;
+      f32x16 acc[2][RT];
 #pragma unroll
       for (int kt = 0; kt < 4; ++kt) {
         i32x8 a[KS];
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) a[ks] = Ring::frag(rbuf, kt * 32 + col, ks, half);
-        f32x16 acc[RT];
 #pragma unroll
-        for (int rt = 0; rt < RT; ++rt) acc[rt] = f32x16{};
+        for (int rt = 0; rt < RT; ++rt) acc[kt & 1][rt] = f32x16{};
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
-          for (int rt = 0; rt < RT; ++rt) acc[rt] = mfma32_fp8(a[ks], qf[rt][ks], acc[rt]);
+          for (int rt = 0; rt < RT; ++rt)
+            acc[kt & 1][rt] = mfma32_fp8(a[ks], qf[rt][ks], acc[kt & 1][rt]);
+        if (kt == 0) {
+          list.insert(pending, pending_beta);
+        } else {
 #pragma unroll
-        for (int rt = 0; rt < RT; ++rt)
+          for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
-          for (int i = 0; i < 16; ++i) rmax[rt] = fmaxf(rmax[rt], acc[rt][i]);
+            for (int i = 0; i < 16; ++i) rmax[rt] = fmaxf(rmax[rt], acc[(kt - 1) & 1][rt][i]);
+        }
       }
 #pragma unroll
-      for (int rt = 0; rt < RT; ++rt) rmax[rt] = fmaxf(rmax[rt], shfl_xor_f(rmax[rt], 32));
-      const float mine = (RT == 1 || half == 0) ? rmax[0] : rmax[RT - 1];
+      for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) rmax[rt] = fmaxf(rmax[rt], acc[1][rt][i]);
+      const float mine = row_tile_max<RT>(rmax, half);
       const float score = ldexpf(mine, eq_own + (int)kexp[beta] - 127);
-      if (beta < beta_own && score == score) list_insert(list, make_key(score, beta));
+      // key 0 is never inserted
+      pending = (beta < beta_own && score == score) ? float_order_key(score) : 0u;
+      pending_beta = beta;
     };
 
     for (int beta = 0; beta < beta_hi; beta += 3) {
@@ -307,10 +324,13 @@ __global__ __launch_bounds__(NW * 64) void index_select_prefill_fp8_kernel(
       if (beta + 1 < beta_hi) step(beta + 1, ring1, ring0);
       if (beta + 2 < beta_hi) step(beta + 2, ring2, ring1);
     }
+    list.insert(pending, pending_beta);
   }
   if (own_valid) {
     const size_t o = ((size_t)q_own * G + g_own) * top_k;
-    write_selection(list, top_k - 1, beta_own, top_k, sel + o, sel_score ? sel_score + o : nullptr);
+    uint64_t keys[KCAP];
+    list.to_keys(keys);
+    write_selection(keys, top_k - 1, beta_own, top_k, sel + o, sel_score ? sel_score + o : nullptr);
   }
 }
 
@@ -447,8 +467,11 @@ __global__ __launch_bounds__(256) void index_score_decode_fp8_kernel(
 // ---------------------------------------------------------------------------
 // launchers
 // ---------------------------------------------------------------------------
+// Four waves per workgroup: with 64 KiB of LDS two workgroups share a CU, and
+// since they are not barrier-locked to each other one's top-k/epilogue VALU
+// work overlaps the other's MFMAs (8 waves per workgroup leave one per CU).
 constexpr int kFp8RT = 2;
-constexpr int kFp8NW = 8;
+constexpr int kFp8NW = 4;
 constexpr int kFp8Rows = kFp8RT * kFp8NW * 32;
 constexpr int kFp8DecodeSeg = 8;
 

@@ -69,12 +69,15 @@ struct KTileStage {
 // Index-key blocks reach LDS by direct global->LDS 16-byte loads: one wave
 // instruction fills 1 KiB (lane L -> bytes 16L..16L+15), i.e. 64 / CPR whole
 // rows of CPR = DI / 8 chunks.  Rows are not padded; instead chunk c of row m
-// is stored at chunk position c ^ (m % CPR) (the swizzle is applied by
-// choosing each lane's source address), so the MFMA A-fragment reads of
-// eight consecutive rows at one logical chunk hit distinct banks.
+// is stored at chunk position c ^ swz(m) (the swizzle is applied by choosing
+// each lane's source address).  The 64 four-byte banks span 256 bytes, i.e.
+// R = 16 / CPR rows (1 for DI = 128), and an A-fragment read serves 16
+// consecutive rows at one logical chunk at a time: swz(m) = (m / R) % CPR
+// gives those rows 16 different 16-byte bank groups.
 template <int DI, int NW>
 struct KRing {
   static constexpr int CPR = DI / 8;                  // 16-byte chunks per key row
+  static constexpr int R = 16 / CPR;                  // rows per 256-byte bank line
   static constexpr int ROWS_PER_INSTR = 64 / CPR;
   static constexpr int INSTR = kBlock / ROWS_PER_INSTR;   // 1 KiB pieces per block
   static constexpr int PER_WAVE = INSTR / NW;          // loads per wave per block
@@ -87,14 +90,15 @@ struct KRing {
     for (int i = 0; i < PER_WAVE; ++i) {
       const int piece = wave * PER_WAVE + i;
       const int m = piece * ROWS_PER_INSTR + lane / CPR;
-      const int lc = (lane % CPR) ^ (m % CPR);
+      const int lc = (lane % CPR) ^ swz(m);
       const uint16_t* src = kbase + ((size_t)blk * kBlock + m) * DI + lc * 8;
       __builtin_amdgcn_global_load_lds(src, buf + piece * 512, 16, 0, 0);
     }
   }
+  __device__ static inline int swz(int m) { return (m / R) % CPR; }
   // A fragment: row m, logical chunk lc
   __device__ static inline bf16x8 frag(const uint16_t* buf, int m, int lc) {
-    return as_bf16x8(*reinterpret_cast<const uint4*>(buf + m * DI + ((lc ^ (m % CPR)) * 8)));
+    return as_bf16x8(*reinterpret_cast<const uint4*>(buf + m * DI + ((lc ^ swz(m)) * 8)));
   }
 };
 
@@ -193,9 +197,7 @@ __global__ __launch_bounds__(NW * 64) void index_select_prefill_kernel(
 #pragma unroll
           for (int i = 0; i < 16; ++i) rmax[rt] = fmaxf(rmax[rt], acc[rt][i]);
       }
-#pragma unroll
-      for (int rt = 0; rt < RT; ++rt) rmax[rt] = fmaxf(rmax[rt], shfl_xor_f(rmax[rt], 32));
-      const float mine = (RT == 1 || half == 0) ? rmax[0] : rmax[RT - 1];
+      const float mine = row_tile_max<RT>(rmax, half);
       if (beta < beta_own && mine == mine) list_insert(list, make_key(mine, beta));
     };
 

@@ -87,6 +87,24 @@ __device__ inline float float_from_order_key(uint32_t k) {
 
 __device__ inline float shfl_xor_f(float v, int mask) { return __shfl_xor(v, mask, kWave); }
 
+// Block maxima of a lane's own row from per-lane partial maxima over the keys
+// of its lane half (S^T layout: lane l and lane l ^ 32 hold the same query
+// column, each for half of the keys).  RT == 2: half h owns row tile h, so
+// one v_permlane32_swap hands each half the other half's partial of the tile
+// it owns (lanes 0-31 receive rmax[0] of lanes 32-63, lanes 32-63 receive
+// rmax[1] of lanes 0-31).  RT == 1: both halves own row tile 0.
+template <int RT>
+__device__ inline float row_tile_max(const float (&rmax)[RT], int half) {
+  if constexpr (RT == 2) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(rmax[0]),
+                                                    __float_as_uint(rmax[1]), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  } else {
+    (void)half;
+    return fmaxf(rmax[0], shfl_xor_f(rmax[0], 32));
+  }
+}
+
 // vmcnt(n) with the other counters left alone (gfx9 s_waitcnt encoding)
 template <int N>
 __device__ inline void wait_vmcnt() {

@@ -36,6 +36,48 @@ __device__ inline void list_insert(uint64_t (&list)[N], uint64_t key) {
   }
 }
 
+// Running top list of one row whose candidate blocks arrive in increasing id
+// order (the prefill kernels scan blocks 0, 1, 2, ...).  Then every listed id
+// is smaller than a newcomer's, so under "equal scores: lower id first" a
+// newcomer outranks an entry exactly when its score is strictly larger: the
+// list keeps 32-bit order keys of the scores (descending, 0 = empty) beside
+// the ids, and an insert is one 32-bit median per slot for the keys plus a
+// compare and two selects per slot for the ids.
+template <int N>
+struct OrderedTopList {
+  uint32_t key[N];
+  int32_t id[N];
+
+  __device__ inline void clear() {
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      key[i] = 0;
+      id[i] = 0;
+    }
+  }
+  // k = float_order_key(score) of block beta (> every listed id); k == 0 is a no-op
+  __device__ inline void insert(uint32_t k, int beta) {
+    if (k > key[N - 1]) {
+      bool gt[N];
+#pragma unroll
+      for (int i = 0; i < N; ++i) gt[i] = k > key[i];
+#pragma unroll
+      for (int i = N - 1; i >= 1; --i) {
+        id[i] = gt[i - 1] ? id[i - 1] : (gt[i] ? beta : id[i]);
+        key[i] = max(key[i], min(key[i - 1], k));   // median, as key[i-1] >= key[i]
+      }
+      id[0] = gt[0] ? beta : id[0];
+      key[0] = max(key[0], k);
+    }
+  }
+  // the same list as 64-bit keys (order key << 32 | ~id; 0 = empty)
+  __device__ inline void to_keys(uint64_t (&out)[N]) const {
+#pragma unroll
+    for (int i = 0; i < N; ++i)
+      out[i] = key[i] ? (((uint64_t)key[i] << 32) | (uint64_t)(~(uint32_t)id[i])) : 0ull;
+  }
+};
+
 // Ascending sort of N values (bitonic network, static indices).
 template <int N>
 __device__ inline void sort_ascending(uint64_t (&a)[N]) {
