@@ -142,9 +142,8 @@ __global__ __launch_bounds__(NW * 64) void index_select_prefill_kernel(
   const bool own_valid = owner && n_own < nrows;
   const int q_own = qa + n_own / G, g_own = n_own % G;
   const int beta_own = own_valid ? (lk - lq + (q_own - qoff)) / kBlock : 0;
-  uint64_t list[KCAP];
-#pragma unroll
-  for (int i = 0; i < KCAP; ++i) list[i] = 0;
+  OrderedTopList<KCAP> list;
+  list.clear();
 
   if (beta_hi > 0) {
     // index queries of this wave's rows, as MFMA B operands (k = 16ks + 8half + e)
@@ -161,6 +160,8 @@ __global__ __launch_bounds__(NW * 64) void index_select_prefill_kernel(
     }
 
     const uint16_t* kbase = k_idx + (size_t)koff * DI;
+    uint32_t pending = 0;   // previous block's score key, inserted during the next block's MFMAs
+    int pending_beta = 0;
     Ring::load(kbase, 0, ring0, wave, lane);
     if (beta_hi > 1) Ring::load(kbase, 1, ring1, wave, lane);
 
@@ -177,6 +178,9 @@ __global__ __launch_bounds__(NW * 64) void index_select_prefill_kernel(
       asm volatile("" ::: "memory");
       if (beta + 2 < beta_hi) Ring::load(kbase, beta + 2, lbuf, wave, lane);
 
+      // the previous block's top-k insert runs while this block's first
+      // fragments load
+      list.insert(pending, pending_beta);
       float rmax[RT];
 #pragma unroll
       for (int rt = 0; rt < RT; ++rt) rmax[rt] = -INFINITY;
@@ -198,7 +202,9 @@ __global__ __launch_bounds__(NW * 64) void index_select_prefill_kernel(
           for (int i = 0; i < 16; ++i) rmax[rt] = fmaxf(rmax[rt], acc[rt][i]);
       }
       const float mine = row_tile_max<RT>(rmax, half);
-      if (beta < beta_own && mine == mine) list_insert(list, make_key(mine, beta));
+      // key 0 is never inserted
+      pending = (beta < beta_own && mine == mine) ? float_order_key(mine) : 0u;
+      pending_beta = beta;
     };
 
     for (int beta = 0; beta < beta_hi; beta += 3) {
@@ -206,10 +212,13 @@ __global__ __launch_bounds__(NW * 64) void index_select_prefill_kernel(
       if (beta + 1 < beta_hi) step(beta + 1, ring1, ring0);
       if (beta + 2 < beta_hi) step(beta + 2, ring2, ring1);
     }
+    list.insert(pending, pending_beta);
   }
   if (own_valid) {
     const size_t o = ((size_t)q_own * G + g_own) * top_k;
-    write_selection(list, top_k - 1, beta_own, top_k, sel + o, sel_score ? sel_score + o : nullptr);
+    uint64_t keys[KCAP];
+    list.to_keys(keys);
+    write_selection(keys, top_k - 1, beta_own, top_k, sel + o, sel_score ? sel_score + o : nullptr);
   }
 }
 
