@@ -2,14 +2,15 @@
 //
 // The pages state that the production model runs the sparse-attention indexer
 // (and Main Branch) with 8-bit queries and 8-bit keys, moving to 4-bit keys
-// (MSA guide, ai-tool-zukan.com/minimax-msa-guide, discussion of the model
-// card's quantisation notes).  The format and scaling are not given; this
+// (dot-ai.myuuu.co.jp article on MiniMax M3.1 Flash, section
+// "MiniMax M3.1 Flashとは？428BのMoEモデルがウェイト公開", on the model card's
+// quantisation notes).  The format and scaling are not given; this
 // file implements OCP FP8 E4M3 codes with power-of-two (E8M0) scales, one per
 // (query row, group) of q_idx and one per (sequence, 128-token block) of
 // k_idx.  The selection rule is the one of the bf16 path (token scores,
-// block max-pool, forced local block, top_k - 1 others; sections
-// "2段階構造の中身" and "クエリを含むローカルブロックの強制取り込み"), evaluated on
-// the dequantised values.
+// block max-pool, forced local block, top_k - 1 others; MSA guide,
+// ai-tool-zukan.com/minimax-msa-guide, sections "2段階構造の中身" and
+// "クエリを含むローカルブロックの強制取り込み"), evaluated on the dequantised values.
 //
 // Because a key block's scale 2^ek is one positive factor for all its keys,
 // max_j (2^eq q8 . 2^ek k8_j) = 2^(eq + ek) max_j (q8 . k8_j): the kernels

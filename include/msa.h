@@ -169,9 +169,10 @@ msa_status_t msa_attend(const msa_dims_t* dims, const void* q, const void* k, co
 /*
  * Quantised Index Branch (optional; the bf16 calls above are the reference
  * path).  The pages note that the production model runs the sparse
- * attention's indexer with 8-bit queries and 8-bit keys (MSA guide, remarks on
- * the model card's quantisation: indexer and Main Branch "Q8KV8", moving to
- * 4-bit keys).  Format and scaling are this library's reading:
+ * attention's indexer with 8-bit queries and 8-bit keys (dot-ai.myuuu.co.jp
+ * article on MiniMax M3.1 Flash, section "MiniMax M3.1 Flashとは？428Bの
+ * MoEモデルがウェイト公開", on the model card's quantisation notes: indexer
+ * and Main Branch "Q8KV8", moving to 4-bit keys).  Format and scaling are this library's reading:
  *   - codes are OCP FP8 E4M3 (bias 7, largest finite 448, no infinities);
  *   - scales are powers of two stored as E8M0 bytes (value = 2^(byte - 127));
  *   - one scale per (query row, group) of q_idx, one per (sequence, 128-token

@@ -4,8 +4,9 @@ TEST INFRASTRUCTURE ONLY.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
 benchmark's ``cpu_baseline`` leg may import or call this module.  It shares no
 code, tables or helpers with the HIP library, and imports nothing from it.
 
-Source: the MSA guide (ai-tool-zukan.com/minimax-msa-guide), section on the
-model's release notes ("M3からの変更点" discussion of quantisation): the sparse
+Source: the dot-ai.myuuu.co.jp article on MiniMax M3.1 Flash, section
+"MiniMax M3.1 Flashとは？428BのMoEモデルがウェイト公開" (its discussion of the
+changes from M3 and of the model card's quantisation notes): the sparse
 attention's indexer and Main Branch run with 8-bit queries and 8-bit keys
 ("Q8KV8"), moving to 4-bit keys.  The pages fix neither the 8-bit format nor
 the scaling, so this module takes the following readings:
