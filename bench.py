@@ -231,6 +231,39 @@ def _fp8_top_set_valid(P, r, g, S, sel):
     return min(S[x] + B[x] for x in chosen) >= max((S[z] - B[z] for z in others), default=-np.inf)
 
 
+def projection_parity(proj, t, w, D, dev, n_rows=64):
+    """Index projections on sampled rows against the oracle's: each bf16 output
+    equals the rounding of the exact sum, or (where the fp32-accumulated sum
+    may cross a rounding boundary) lies within the accumulation bound plus one
+    unit in the last place of it."""
+    import torch
+    from oracle import projections as PR
+    rng = np.random.Generator(np.random.PCG64(4321))
+    rows = np.unique(rng.integers(0, w.total_q, n_rows))
+    ridx = torch.as_tensor(rows, device=dev, dtype=torch.long)
+    x = proj["x"].index_select(0, ridx).double().cpu().numpy()
+    wq, wk = proj["w_q"].double().cpu().numpy(), proj["w_k"].double().cpu().numpy()
+    cuq = t["cu_seqlens_q"].cpu().numpy()
+    cuk = t["cu_seqlens_k"].cpu().numpy()
+    b = np.searchsorted(cuq, rows, side="right") - 1
+    krows = cuk[b] + (cuk[b + 1] - cuk[b]) - (cuq[b + 1] - cuq[b]) + (rows - cuq[b])
+    got_q = t["q_idx"].index_select(0, ridx).double().cpu().numpy().reshape(len(rows), -1)
+    got_k = t["k_idx"].index_select(0, torch.as_tensor(krows, device=dev)).double().cpu().numpy()
+    bad = n_diff = 0
+    for got, W in ((got_q, wq), (got_k, wk)):
+        y, sa = x @ W.T, np.abs(x) @ np.abs(W).T
+        r = PR.bf16_round(y)
+        _, e = np.frexp(np.abs(y))
+        ulp = np.ldexp(1.0, np.maximum(e, -125) - 8)
+        eps = D * 2.0 ** -24 * sa + 1e-300
+        diff = got != r
+        ok = ((ulp / 2 - np.abs(y - r)) <= eps) & (np.abs(got - y) <= eps + ulp)
+        n_diff += int(diff.sum())
+        bad += int((diff & ~ok).sum())
+    return dict(ok=bad == 0, rows=int(len(rows)), outputs_differing_from_rounding=n_diff,
+                outputs_outside_bound=bad)
+
+
 def parity_on_rows(P, rows, ref, sel_gpu, out_gpu, lse_gpu, top_k, fp8=False):
     from oracle import msa_oracle as O
     bad = ties = 0
@@ -296,6 +329,10 @@ def main():
     ap.add_argument("--index", choices=["bf16", "fp8"], default="bf16",
                     help="Index Branch precision: bf16 projections, or quantised in the step to "
                          "FP8 E4M3 with power-of-two scales and scored on the fp8 matrix cores")
+    ap.add_argument("--project-dim", type=int, default=0,
+                    help="also run the index projections in the step: q_idx and the new tokens' "
+                         "k_idx from a layer input of this width (0: off; the index projections "
+                         "are then checked element-wise on the sampled rows instead of the whole path)")
     ap.add_argument("--graph", choices=["auto", "on", "off"], default="auto",
                     help="replay the step as a captured HIP graph (auto: on for decode, whose "
                          "kernels are short enough for launch gaps to matter)")
@@ -310,7 +347,8 @@ def main():
     w = _wl(args.workload)
     cores = min(16, len(os.sched_getaffinity(0)))
     host_bytes = w.total_k * w.num_kv_heads * w.head_dim * 4 * 2 + w.total_k * w.index_dim * 4
-    pooled = (not args.no_cpu_baseline) and host_bytes <= (16 << 30) and cores > 1
+    pooled = (not args.no_cpu_baseline) and not args.project_dim and host_bytes <= (16 << 30) \
+        and cores > 1
     pool = OraclePool(cores) if pooled else None   # forked before any GPU call
 
     import torch
@@ -346,7 +384,18 @@ def main():
         torch.cuda.synchronize()
         step_k_idx = None
 
+    proj = None
+    if args.project_dim:
+        from msa_inputs import generate_projection
+        proj = generate_projection(w, args.project_dim, dev)
+        torch.cuda.synchronize()
+        log(f"[bench] index projections from a width-{args.project_dim} layer input")
+
     def step():
+        if proj is not None:
+            # q_idx and the new tokens' index keys come from the layer input
+            msa.index_project(dims, proj["x"], proj["w_q"], proj["w_k"], t["cu_seqlens_q"],
+                              t["cu_seqlens_k"], t["q_idx"], t["k_idx"])
         msa.msa_forward(dims, t["q"], t["k"], t["v"], t["q_idx"], step_k_idx, t["cu_seqlens_q"],
                         t["cu_seqlens_k"], bufs, fp8=fp8)
 
@@ -396,6 +445,8 @@ def main():
     log(f"[bench] timed {args.steps} steps: {ms_per_step:.3f} ms/step")
 
     wm = work_model(w)
+    wm["project_flops"] = (2.0 * w.total_q * args.project_dim * (w.num_kv_heads + 1) * w.index_dim
+                           if args.project_dim else 0.0)
     stage = {}
     for name, (ms, n) in prof.items():
         if n:
@@ -424,6 +475,10 @@ def main():
             return None
         n_launch = s_["launches_per_step"]
         sec = s_["ms_per_launch"] / 1e3
+        if name == "index_project":
+            a = wm["project_flops"] / n_launch / sec
+            return dict(bound="mfma", achieved=a / 1e12, peak=PEAK_BF16_FLOPS / 1e12, unit="TFLOP/s",
+                        frac=a / PEAK_BF16_FLOPS, traffic=traffic_record(name), dtype="bf16")
         if name in ("index_select_prefill", "index_select_prefill_fp8"):
             peak = PEAK_FP8_FLOPS if name.endswith("fp8") else PEAK_BF16_FLOPS
             a = wm["index_flops"] / n_launch / sec
@@ -459,7 +514,10 @@ def main():
     # ---- oracle sample: parity gate + cpu baseline --------------------------------
     cpu = None
     parity = None
-    if not args.no_cpu_baseline:
+    if proj is not None:
+        parity = projection_parity(proj, t, w, args.project_dim, dev)
+        log(f"[bench] projection parity on sampled rows: {parity}")
+    elif not args.no_cpu_baseline:
         from oracle import msa_oracle as O
         rng = np.random.Generator(np.random.PCG64(12345))
         cuq = t["cu_seqlens_q"].cpu().numpy()
@@ -547,6 +605,7 @@ def main():
                    "num_kv_heads": w.num_kv_heads, "head_dim": w.head_dim,
                    "index_dim": w.index_dim, "block": BLOCK, "top_k": w.top_k,
                    "q_chunk": args.q_chunk, "index_branch": args.index,
+                   "index_projection_dim": args.project_dim or None,
                    "parallelism": "single GPU"},
         "roofline": roof(dominant) if dominant else None,
         "dominant_kernel": dominant,

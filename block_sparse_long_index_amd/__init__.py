@@ -18,7 +18,7 @@ __all__ = [
     "MSAError", "Dims", "OP_INDEX_SELECT", "OP_BUILD_LISTS", "OP_ATTEND", "load_library",
     "make_dims", "workspace_size", "index_select", "build_block_query_lists", "attend",
     "msa_forward", "exported_symbols", "LIB_PATH", "HEADER_PATH", "index_quantize_fp8",
-    "index_select_fp8", "Fp8Index",
+    "index_select_fp8", "Fp8Index", "index_project",
 ]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -68,6 +68,8 @@ def load_library(path: str = LIB_PATH):
     lib.msa_workspace_size.argtypes = [DP, I32, ctypes.POINTER(SZ)]
     lib.msa_index_select.restype = I32
     lib.msa_index_select.argtypes = [DP, P, P, P, P, P, P, P, SZ, P]
+    lib.msa_index_project.restype = I32
+    lib.msa_index_project.argtypes = [DP, I32, P, P, P, P, P, P, P, P]
     lib.msa_index_quantize_fp8.restype = I32
     lib.msa_index_quantize_fp8.argtypes = [DP, P, P, P, P, P, P, P, P]
     lib.msa_index_select_fp8.restype = I32
@@ -169,6 +171,24 @@ def index_select(dims, q_idx, k_idx, cu_seqlens_q, cu_seqlens_k, sel, sel_score=
         _ptr(ws, "workspace"), ctypes.c_size_t(ws.numel() * ws.element_size()), _stream(stream))
     _check(st, "msa_index_select")
     return sel
+
+
+def index_project(dims, x, w_q, w_k, cu_seqlens_q, cu_seqlens_k, q_idx, k_idx, stream=None):
+    """q_idx = x W_q^T, and the new tokens' rows of k_idx = x W_k^T (bf16)."""
+    G, T, DI = dims.num_kv_heads, dims.total_q, dims.index_dim
+    D = int(x.shape[1]) if x.dim() == 2 else -1
+    _shape(x, (T, D), "x")
+    _shape(w_q, (G * DI, D), "w_q")
+    _shape(w_k, (DI, D), "w_k")
+    _shape(q_idx, (T, G, DI), "q_idx")
+    _shape(k_idx, (dims.total_k, DI), "k_idx")
+    st = load_library().msa_index_project(
+        ctypes.byref(dims), D, _ptr(x, "x", torch.bfloat16), _ptr(w_q, "w_q", torch.bfloat16),
+        _ptr(w_k, "w_k", torch.bfloat16), _ptr(cu_seqlens_q, "cu_seqlens_q", torch.int32),
+        _ptr(cu_seqlens_k, "cu_seqlens_k", torch.int32), _ptr(q_idx, "q_idx", torch.bfloat16),
+        _ptr(k_idx, "k_idx", torch.bfloat16), _stream(stream))
+    _check(st, "msa_index_project")
+    return q_idx, k_idx
 
 
 class Fp8Index:
@@ -306,7 +326,7 @@ def msa_forward(dims: Dims, q, k, v, q_idx, k_idx, cu_seqlens_q, cu_seqlens_k, b
     return bufs
 
 
-PROFILE_KERNELS = 9
+PROFILE_KERNELS = 10
 
 
 def profile_enable(on: bool = True):

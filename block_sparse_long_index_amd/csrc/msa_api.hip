@@ -33,6 +33,8 @@ hipError_t launch_attend_decode(int, int, const void*, const void*, const void*,
 hipError_t launch_merge(int, const float*, const float2*, const int32_t*, int, int, int, int, int,
                         void*, float*, hipStream_t);
 int fp8_max_blocks_per_sequence();
+hipError_t launch_index_project(const void*, const void*, const void*, int, int, int, int,
+                                const int32_t*, const int32_t*, int, void*, void*, hipStream_t);
 hipError_t launch_quantize_index_fp8(int, const void*, const void*, const int32_t*, int, int,
                                      long long, void*, uint8_t*, void*, uint8_t*, hipStream_t);
 hipError_t launch_index_select_prefill_fp8(const void*, const uint8_t*, const void*, const uint8_t*,
@@ -158,11 +160,12 @@ bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 // --- opt-in per-launch timing: each launcher call is bracketed by two hipEvents
 // recorded on the launch stream; msa_profile_collect() waits for them.
 enum KernelId { K_INDEX_PREFILL, K_INDEX_DECODE, K_TOPK, K_LISTS, K_ATTEND, K_MERGE,
-                K_QUANT_FP8, K_INDEX_PREFILL_FP8, K_INDEX_DECODE_FP8 };
+                K_QUANT_FP8, K_INDEX_PREFILL_FP8, K_INDEX_DECODE_FP8, K_PROJECT };
 const char* const kKernelNames[MSA_PROFILE_KERNELS] = {
     "index_select_prefill", "index_score_decode", "topk_select",
     "build_lists", "attend_blocks", "merge_partials",
-    "quantize_index_fp8", "index_select_prefill_fp8", "index_score_decode_fp8"};
+    "quantize_index_fp8", "index_select_prefill_fp8", "index_score_decode_fp8",
+    "index_project"};
 
 std::atomic<bool> g_prof_on{false};
 std::mutex g_prof_mu;
@@ -280,6 +283,27 @@ msa_status_t msa_index_select(const msa_dims_t* dims, const void* q_idx, const v
     if (e != hipSuccess) return hip_fail(e);
   }
   return MSA_OK;
+}
+
+msa_status_t msa_index_project(const msa_dims_t* dims, int32_t model_dim, const void* x,
+                               const void* w_q, const void* w_k, const int32_t* cu_seqlens_q,
+                               const int32_t* cu_seqlens_k, void* q_idx, void* k_idx,
+                               void* stream) {
+  Derived x_;
+  msa_status_t s = check_dims(dims, &x_);
+  if (s != MSA_OK) return s;
+  if (model_dim < 64 || model_dim % 64 || model_dim > 65536)
+    return fail(MSA_ERR_UNSUPPORTED, "model_dim must be a multiple of 64 in 64..65536");
+  if (x_.total_q == 0) return MSA_OK;   // no new tokens
+  if (!x || !w_q || !w_k || !cu_seqlens_q || !cu_seqlens_k || !q_idx || !k_idx)
+    return fail(MSA_ERR_NULL_ARG, "a required pointer is NULL");
+  if (!aligned16(x) || !aligned16(w_q) || !aligned16(w_k) || !aligned16(q_idx) || !aligned16(k_idx))
+    return fail(MSA_ERR_ALIGNMENT, "tensor pointers must be 16-byte aligned");
+  hipStream_t st = (hipStream_t)stream;
+  ProfScope ps(K_PROJECT, st);
+  hipError_t e = msa::launch_index_project(x, w_q, w_k, model_dim, x_.G, x_.DI, (int)x_.total_q,
+                                           cu_seqlens_q, cu_seqlens_k, dims->batch, q_idx, k_idx, st);
+  return e == hipSuccess ? MSA_OK : hip_fail(e);
 }
 
 msa_status_t msa_index_quantize_fp8(const msa_dims_t* dims, const void* q_idx, const void* k_idx,

@@ -167,6 +167,33 @@ msa_status_t msa_attend(const msa_dims_t* dims, const void* q, const void* k, co
                         size_t workspace_bytes, void* stream);
 
 /*
+ * Index projections: the two projection matrices the Index Branch adds to a
+ * GQA layer (MSA guide, section "Index BranchとMain Branchの役割分担": one
+ * index-query head per group, one shared index-key head), applied to the
+ * layer input of the new tokens:
+ *   q_idx[r, g, :] = x[r, :] . W_q[g * index_dim + c, :]  (c = 0 .. index_dim-1)
+ *   k_idx[row(r), :] = x[r, :] . W_k[c, :]
+ * accumulated in fp32 and rounded to bf16 (nearest even).  x has one row per
+ * query row r; row(r) is the key row of that token in its sequence
+ * (cu_seqlens_k[b] + Lk_b - Lq_b + i for the i-th query of sequence b), so a
+ * prefill (Lq = Lk) writes every key row and a decode step writes each
+ * sequence's new keys after its cached ones; other key rows are untouched.
+ * No bias.  The pages give no layer width: model_dim is a parameter.
+ *
+ * model_dim D: multiple of 64, 64 .. 65536 (else MSA_ERR_UNSUPPORTED)
+ * x      bf16 [total_q, D]
+ * w_q    bf16 [num_kv_heads * index_dim, D]   (out_features x in_features)
+ * w_k    bf16 [index_dim, D]
+ * q_idx  bf16 [total_q, num_kv_heads, index_dim]  out
+ * k_idx  bf16 [total_k, index_dim]                out (the new tokens' rows)
+ * No workspace.  total_q == 0 enqueues nothing.
+ */
+msa_status_t msa_index_project(const msa_dims_t* dims, int32_t model_dim, const void* x,
+                               const void* w_q, const void* w_k, const int32_t* cu_seqlens_q,
+                               const int32_t* cu_seqlens_k, void* q_idx, void* k_idx,
+                               void* stream);
+
+/*
  * Quantised Index Branch (optional; the bf16 calls above are the reference
  * path).  The pages note that the production model runs the sparse
  * attention's indexer with 8-bit queries and 8-bit keys (dot-ai.myuuu.co.jp
@@ -232,13 +259,13 @@ int32_t msa_abi_version(void);
  * recorded on the call's stream.  Stage ids: 0 index_select_prefill (scores + top-k),
  * 1 index_score_decode, 2 topk_select, 3 build_lists (all list kernels),
  * 4 attend_blocks, 5 merge_partials, 6 quantize_index_fp8,
- * 7 index_select_prefill_fp8, 8 index_score_decode_fp8.  msa_profile_collect() waits for every
+ * 7 index_select_prefill_fp8, 8 index_score_decode_fp8, 9 index_project.  msa_profile_collect() waits for every
  * recorded event (it blocks the host), writes the summed milliseconds and the
  * launch count per stage into caller arrays of MSA_PROFILE_KERNELS entries,
  * and forgets the records.  Events are host-side HIP objects kept in a pool
  * for the life of the process; no device memory is allocated.
  */
-#define MSA_PROFILE_KERNELS 9
+#define MSA_PROFILE_KERNELS 10
 msa_status_t msa_profile_enable(int32_t enable);
 msa_status_t msa_profile_collect(float* total_ms, int32_t* launches);
 const char* msa_profile_kernel_name(int32_t id);

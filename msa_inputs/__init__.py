@@ -206,3 +206,27 @@ def sample_rows(w: Workload, n_random: int, seed: int = 7) -> list:
     if tq > 0 and n_random > 0:
         rows.update(int(x) for x in rng.integers(0, tq, size=n_random))
     return sorted(rows)
+
+
+def generate_projection(w: Workload, model_dim: int, device="cpu", seed_offset: int = 100) -> dict:
+    """Layer input and index-projection weights for workload ``w``.
+
+    x: bf16 [total_q, model_dim] ~ N(0, 1) (one row per new token, query-row
+    order); w_q: bf16 [num_kv_heads * index_dim, model_dim] and w_k: bf16
+    [index_dim, model_dim] ~ N(0, 1/model_dim), so projected values are of
+    order one.  Drawn with their own generator (seed + seed_offset) in fixed
+    row chunks, so they do not disturb the other inputs of the workload.
+    """
+    device = torch.device(device)
+    gen = torch.Generator(device=device)
+    gen.manual_seed(int(w.seed) + int(seed_offset))
+    G, di, D = w.num_kv_heads, w.index_dim, int(model_dim)
+    bf = torch.bfloat16
+    sw = float(D) ** -0.5
+    w_q = _randn(gen, (G * di, D), device, sw).to(bf)
+    w_k = _randn(gen, (di, D), device, sw).to(bf)
+    x = torch.empty((w.total_q, D), dtype=bf, device=device)
+    for r0 in range(0, w.total_q, _ROW_CHUNK):
+        r1 = min(w.total_q, r0 + _ROW_CHUNK)
+        x[r0:r1] = _randn(gen, (r1 - r0, D), device).to(bf)
+    return dict(x=x.contiguous(), w_q=w_q.contiguous(), w_k=w_k.contiguous())

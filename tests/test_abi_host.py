@@ -164,3 +164,17 @@ def test_fp8_entry_points_validate_on_host():
     # no inputs at all: nothing to quantise
     assert qz(ctypes.byref(d), None, None, None, None, None, None, None, None) == 0
     assert s8(ctypes.byref(empty), None, None, None, None, None, None, None, None, None, big, None) == 0
+
+
+def test_projection_entry_point_validates_on_host():
+    d = _dims()
+    P = ctypes.c_void_p
+    ok = P(0x10000)
+    odd = P(0x10004)
+    pj = lib.msa_index_project
+    assert pj(ctypes.byref(d), 96, ok, ok, ok, ok, ok, ok, ok, None) == 3      # not a multiple of 64
+    assert pj(ctypes.byref(d), 0, ok, ok, ok, ok, ok, ok, ok, None) == 3
+    assert pj(ctypes.byref(d), 8192, None, ok, ok, ok, ok, ok, ok, None) == 1
+    assert pj(ctypes.byref(d), 8192, ok, ok, odd, ok, ok, ok, ok, None) == 4
+    empty = _dims(total_q=0, max_q_len=0)
+    assert pj(ctypes.byref(empty), 8192, None, None, None, None, None, None, None, None) == 0
