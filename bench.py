@@ -333,11 +333,17 @@ def main():
                     help="also run the index projections in the step: q_idx and the new tokens' "
                          "k_idx from a layer input of this width (0: off; the index projections "
                          "are then checked element-wise on the sampled rows instead of the whole path)")
+    ap.add_argument("--kl", action="store_true",
+                    help="also compute the Index Branch's KL-alignment target in the step "
+                         "(Main-Branch block masses + index log-probabilities + KL per query and group)")
     ap.add_argument("--graph", choices=["auto", "on", "off"], default="auto",
                     help="replay the step as a captured HIP graph (auto: on for decode, whose "
                          "kernels are short enough for launch gaps to matter)")
     args = ap.parse_args()
 
+    if args.kl and args.index != "bf16":
+        print("--kl uses the bf16 index branch", file=sys.stderr)
+        sys.exit(2)
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); this build has no "
               f"multi-GPU path. Run with --gpus 1.", file=sys.stderr)
@@ -373,7 +379,11 @@ def main():
     torch.cuda.synchronize()
     log(f"[bench] inputs ready in {time.perf_counter() - t0:.1f}s")
     dims = msa.dims_for(w, q_chunk=args.q_chunk)
-    bufs = msa.Buffers(dims, dev, want_scores=False, want_lse=True)
+    bufs = msa.Buffers(dims, dev, want_scores=args.kl, want_lse=True)
+    kl_out = None
+    if args.kl:
+        kl_out = dict(mass=torch.empty((w.total_q, w.num_kv_heads, w.top_k), dtype=torch.float32, device=dev),
+                      kl=torch.empty((w.total_q, w.num_kv_heads), dtype=torch.float32, device=dev))
     fp8 = msa.Fp8Index(dims, dev) if args.index == "fp8" else None
     log(f"[bench] workspace {bufs.workspace.numel() / 2**30:.2f} GiB; index branch {args.index}")
     # fp8 decode: the index-key cache is stored quantised (quantised once, outside the step);
@@ -396,8 +406,20 @@ def main():
             # q_idx and the new tokens' index keys come from the layer input
             msa.index_project(dims, proj["x"], proj["w_q"], proj["w_k"], t["cu_seqlens_q"],
                               t["cu_seqlens_k"], t["q_idx"], t["k_idx"])
-        msa.msa_forward(dims, t["q"], t["k"], t["v"], t["q_idx"], step_k_idx, t["cu_seqlens_q"],
-                        t["cu_seqlens_k"], bufs, fp8=fp8)
+        if kl_out is None:
+            msa.msa_forward(dims, t["q"], t["k"], t["v"], t["q_idx"], step_k_idx, t["cu_seqlens_q"],
+                            t["cu_seqlens_k"], bufs, fp8=fp8)
+            return
+        # the forward with the KL-alignment target (bf16 index branch)
+        msa.index_select(dims, t["q_idx"], t["k_idx"], t["cu_seqlens_q"], t["cu_seqlens_k"],
+                         bufs.sel, bufs.sel_score, bufs.workspace)
+        msa.build_block_query_lists(dims, bufs.sel, t["cu_seqlens_q"], t["cu_seqlens_k"], bufs.offsets,
+                                    bufs.entries, bufs.workspace)
+        msa.attend_with_mass(dims, t["q"], t["k"], t["v"], t["cu_seqlens_q"], t["cu_seqlens_k"],
+                             bufs.sel, bufs.offsets, bufs.entries, bufs.out, kl_out["mass"], bufs.lse,
+                             bufs.workspace)
+        msa.index_kl(dims, t["q_idx"], t["k_idx"], t["cu_seqlens_q"], t["cu_seqlens_k"], bufs.sel,
+                     bufs.sel_score, kl_out["mass"], kl_out["kl"])
 
     for i in range(args.warmup):
         step()
@@ -605,7 +627,7 @@ def main():
                    "num_kv_heads": w.num_kv_heads, "head_dim": w.head_dim,
                    "index_dim": w.index_dim, "block": BLOCK, "top_k": w.top_k,
                    "q_chunk": args.q_chunk, "index_branch": args.index,
-                   "index_projection_dim": args.project_dim or None,
+                   "index_projection_dim": args.project_dim or None, "kl_target": bool(args.kl),
                    "parallelism": "single GPU"},
         "roofline": roof(dominant) if dominant else None,
         "dominant_kernel": dominant,

@@ -18,7 +18,7 @@ __all__ = [
     "MSAError", "Dims", "OP_INDEX_SELECT", "OP_BUILD_LISTS", "OP_ATTEND", "load_library",
     "make_dims", "workspace_size", "index_select", "build_block_query_lists", "attend",
     "msa_forward", "exported_symbols", "LIB_PATH", "HEADER_PATH", "index_quantize_fp8",
-    "index_select_fp8", "Fp8Index", "index_project",
+    "index_select_fp8", "Fp8Index", "index_project", "attend_with_mass", "index_kl",
 ]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -68,6 +68,10 @@ def load_library(path: str = LIB_PATH):
     lib.msa_workspace_size.argtypes = [DP, I32, ctypes.POINTER(SZ)]
     lib.msa_index_select.restype = I32
     lib.msa_index_select.argtypes = [DP, P, P, P, P, P, P, P, SZ, P]
+    lib.msa_attend_with_mass.restype = I32
+    lib.msa_attend_with_mass.argtypes = [DP, P, P, P, P, P, P, P, P, P, P, P, P, SZ, P]
+    lib.msa_index_kl.restype = I32
+    lib.msa_index_kl.argtypes = [DP, P, P, P, P, P, P, P, P, P, P]
     lib.msa_index_project.restype = I32
     lib.msa_index_project.argtypes = [DP, I32, P, P, P, P, P, P, P, P]
     lib.msa_index_quantize_fp8.restype = I32
@@ -285,6 +289,53 @@ def attend(dims, q, k, v, cu_seqlens_q, cu_seqlens_k, sel, block_offsets, block_
     return out
 
 
+def attend_with_mass(dims, q, k, v, cu_seqlens_q, cu_seqlens_k, sel, block_offsets, block_entries,
+                     out, block_mass, lse=None, workspace=None, stream=None):
+    """msa_attend plus the Main Branch's attention mass per selected block
+    (averaged over the group's heads) into block_mass [T, G, top_k] fp32."""
+    T, Hq, D, G = dims.total_q, dims.num_q_heads, dims.head_dim, dims.num_kv_heads
+    _shape(q, (T, Hq, D), "q")
+    _shape(k, (dims.total_k, G, D), "k")
+    _shape(v, (dims.total_k, G, D), "v")
+    _shape(out, (T, Hq, D), "out")
+    _shape(block_mass, (T, G, dims.top_k), "block_mass")
+    if lse is not None:
+        _shape(lse, (T, Hq), "lse")
+    ws = _workspace(dims, OP_ATTEND, workspace, q.device)
+    st = load_library().msa_attend_with_mass(
+        ctypes.byref(dims), _ptr(q, "q", torch.bfloat16), _ptr(k, "k", torch.bfloat16),
+        _ptr(v, "v", torch.bfloat16), _ptr(cu_seqlens_q, "cu_seqlens_q", torch.int32),
+        _ptr(cu_seqlens_k, "cu_seqlens_k", torch.int32), _ptr(sel, "sel", torch.int32),
+        _ptr(block_offsets, "block_offsets", torch.int32), _ptr(block_entries, "block_entries", torch.int32),
+        _ptr(out, "out", torch.bfloat16), _ptr(lse, "lse", torch.float32),
+        _ptr(block_mass, "block_mass", torch.float32), _ptr(ws, "workspace"),
+        ctypes.c_size_t(ws.numel() * ws.element_size()), _stream(stream))
+    _check(st, "msa_attend_with_mass")
+    return out, block_mass
+
+
+def index_kl(dims, q_idx, k_idx, cu_seqlens_q, cu_seqlens_k, sel, sel_score, block_mass, kl,
+             log_q=None, stream=None):
+    """KL(P || Q) per (query, group) of the Main-Branch masses P and the index
+    distribution Q over the selection; log Q optionally."""
+    T, G, k = dims.total_q, dims.num_kv_heads, dims.top_k
+    _shape(q_idx, (T, G, dims.index_dim), "q_idx")
+    _shape(k_idx, (dims.total_k, dims.index_dim), "k_idx")
+    for t_, n_ in ((sel, "sel"), (sel_score, "sel_score"), (block_mass, "block_mass")):
+        _shape(t_, (T, G, k), n_)
+    _shape(kl, (T, G), "kl")
+    if log_q is not None:
+        _shape(log_q, (T, G, k), "log_q")
+    st = load_library().msa_index_kl(
+        ctypes.byref(dims), _ptr(q_idx, "q_idx", torch.bfloat16), _ptr(k_idx, "k_idx", torch.bfloat16),
+        _ptr(cu_seqlens_q, "cu_seqlens_q", torch.int32), _ptr(cu_seqlens_k, "cu_seqlens_k", torch.int32),
+        _ptr(sel, "sel", torch.int32), _ptr(sel_score, "sel_score", torch.float32),
+        _ptr(block_mass, "block_mass", torch.float32), _ptr(log_q, "log_q", torch.float32),
+        _ptr(kl, "kl", torch.float32), _stream(stream))
+    _check(st, "msa_index_kl")
+    return kl
+
+
 class Buffers:
     """Output and workspace buffers of one MSA forward for fixed dims."""
 
@@ -326,7 +377,7 @@ def msa_forward(dims: Dims, q, k, v, q_idx, k_idx, cu_seqlens_q, cu_seqlens_k, b
     return bufs
 
 
-PROFILE_KERNELS = 10
+PROFILE_KERNELS = 12
 
 
 def profile_enable(on: bool = True):

@@ -33,6 +33,11 @@ hipError_t launch_attend_decode(int, int, const void*, const void*, const void*,
 hipError_t launch_merge(int, const float*, const float2*, const int32_t*, int, int, int, int, int,
                         void*, float*, hipStream_t);
 int fp8_max_blocks_per_sequence();
+hipError_t launch_block_mass(int, const float2*, const int32_t*, int, int, int, int, float*,
+                             hipStream_t);
+hipError_t launch_index_kl(int, const void*, const void*, const int32_t*, const int32_t*, int, int,
+                           int, int, const int32_t*, const float*, const float*, float*, float*,
+                           hipStream_t);
 hipError_t launch_index_project(const void*, const void*, const void*, int, int, int, int,
                                 const int32_t*, const int32_t*, int, void*, void*, hipStream_t);
 hipError_t launch_quantize_index_fp8(int, const void*, const void*, const int32_t*, int, int,
@@ -160,12 +165,13 @@ bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 // --- opt-in per-launch timing: each launcher call is bracketed by two hipEvents
 // recorded on the launch stream; msa_profile_collect() waits for them.
 enum KernelId { K_INDEX_PREFILL, K_INDEX_DECODE, K_TOPK, K_LISTS, K_ATTEND, K_MERGE,
-                K_QUANT_FP8, K_INDEX_PREFILL_FP8, K_INDEX_DECODE_FP8, K_PROJECT };
+                K_QUANT_FP8, K_INDEX_PREFILL_FP8, K_INDEX_DECODE_FP8, K_PROJECT, K_MASS,
+                K_INDEX_KL };
 const char* const kKernelNames[MSA_PROFILE_KERNELS] = {
     "index_select_prefill", "index_score_decode", "topk_select",
     "build_lists", "attend_blocks", "merge_partials",
     "quantize_index_fp8", "index_select_prefill_fp8", "index_score_decode_fp8",
-    "index_project"};
+    "index_project", "block_mass", "index_kl"};
 
 std::atomic<bool> g_prof_on{false};
 std::mutex g_prof_mu;
@@ -401,11 +407,12 @@ msa_status_t msa_build_block_query_lists(const msa_dims_t* dims, const int32_t* 
   return e == hipSuccess ? MSA_OK : hip_fail(e);
 }
 
-msa_status_t msa_attend(const msa_dims_t* dims, const void* q, const void* k, const void* v,
-                        const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
-                        const int32_t* sel, const int32_t* block_offsets,
-                        const int32_t* block_entries, void* out, float* lse, void* workspace,
-                        size_t workspace_bytes, void* stream) {
+static msa_status_t attend_impl(const msa_dims_t* dims, const void* q, const void* k,
+                                const void* v, const int32_t* cu_seqlens_q,
+                                const int32_t* cu_seqlens_k, const int32_t* sel,
+                                const int32_t* block_offsets, const int32_t* block_entries,
+                                void* out, float* lse, float* block_mass, void* workspace,
+                                size_t workspace_bytes, void* stream) {
   Derived x;
   msa_status_t s = check_dims(dims, &x);
   if (s != MSA_OK) return s;
@@ -443,11 +450,62 @@ msa_status_t msa_attend(const msa_dims_t* dims, const void* q, const void* k, co
                                       part_ml, st);
     }
     if (e != hipSuccess) return hip_fail(e);
-    ProfScope ps(K_MERGE, st);
-    e = msa::launch_merge(x.D, part_acc, part_ml, sel, a, z, x.Hq, x.G, x.top_k, out, lse, st);
+    {
+      ProfScope ps(K_MERGE, st);
+      e = msa::launch_merge(x.D, part_acc, part_ml, sel, a, z, x.Hq, x.G, x.top_k, out, lse, st);
+    }
     if (e != hipSuccess) return hip_fail(e);
+    if (block_mass) {
+      ProfScope ps(K_MASS, st);
+      e = msa::launch_block_mass(x.hpg, part_ml, sel, a, z, x.G, x.top_k, block_mass, st);
+      if (e != hipSuccess) return hip_fail(e);
+    }
   }
   return MSA_OK;
+}
+
+msa_status_t msa_attend(const msa_dims_t* dims, const void* q, const void* k, const void* v,
+                        const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                        const int32_t* sel, const int32_t* block_offsets,
+                        const int32_t* block_entries, void* out, float* lse, void* workspace,
+                        size_t workspace_bytes, void* stream) {
+  return attend_impl(dims, q, k, v, cu_seqlens_q, cu_seqlens_k, sel, block_offsets, block_entries,
+                     out, lse, nullptr, workspace, workspace_bytes, stream);
+}
+
+msa_status_t msa_attend_with_mass(const msa_dims_t* dims, const void* q, const void* k,
+                                  const void* v, const int32_t* cu_seqlens_q,
+                                  const int32_t* cu_seqlens_k, const int32_t* sel,
+                                  const int32_t* block_offsets, const int32_t* block_entries,
+                                  void* out, float* lse, float* block_mass, void* workspace,
+                                  size_t workspace_bytes, void* stream) {
+  if (dims && dims->total_q > 0 && !block_mass)
+    return fail(MSA_ERR_NULL_ARG, "block_mass is NULL");
+  if (block_mass && !aligned16(block_mass))
+    return fail(MSA_ERR_ALIGNMENT, "tensor pointers must be 16-byte aligned");
+  return attend_impl(dims, q, k, v, cu_seqlens_q, cu_seqlens_k, sel, block_offsets, block_entries,
+                     out, lse, block_mass, workspace, workspace_bytes, stream);
+}
+
+msa_status_t msa_index_kl(const msa_dims_t* dims, const void* q_idx, const void* k_idx,
+                          const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                          const int32_t* sel, const float* sel_score, const float* block_mass,
+                          float* log_q, float* kl, void* stream) {
+  Derived x;
+  msa_status_t s = check_dims(dims, &x);
+  if (s != MSA_OK) return s;
+  if (x.total_q == 0) return MSA_OK;
+  if (!q_idx || !k_idx || !cu_seqlens_q || !cu_seqlens_k || !sel || !sel_score || !block_mass || !kl)
+    return fail(MSA_ERR_NULL_ARG, "a required pointer is NULL");
+  if (!aligned16(q_idx) || !aligned16(k_idx) || !aligned16(sel) || !aligned16(sel_score) ||
+      !aligned16(block_mass) || !aligned16(kl) || (log_q && !aligned16(log_q)))
+    return fail(MSA_ERR_ALIGNMENT, "tensor pointers must be 16-byte aligned");
+  hipStream_t st = (hipStream_t)stream;
+  ProfScope ps(K_INDEX_KL, st);
+  hipError_t e = msa::launch_index_kl(x.DI, q_idx, k_idx, cu_seqlens_q, cu_seqlens_k, dims->batch,
+                                      x.G, x.top_k, dims->max_q_len, sel, sel_score, block_mass,
+                                      log_q, kl, st);
+  return e == hipSuccess ? MSA_OK : hip_fail(e);
 }
 
 msa_status_t msa_profile_enable(int32_t enable) {

@@ -244,6 +244,38 @@ msa_status_t msa_index_select_fp8(const msa_dims_t* dims, const void* q_idx8, co
                                   int32_t* sel, float* sel_score, void* workspace,
                                   size_t workspace_bytes, void* stream);
 
+/*
+ * KL-alignment target of the Index Branch, forward only.  The pages train the
+ * non-differentiable top-k by pulling the distribution of the Index Branch's
+ * block scores towards the distribution of blocks the Main Branch's exact
+ * attention relied on, through a KL divergence (MSA guide, sections
+ * "非微分的な選択をどう学習させるか（KLダイバージェンス）" and "選択を学習可能にするKL損失").
+ * This library's reading, per (query, group), over the selected blocks:
+ *   P(s) = Main-Branch attention mass on selected slot s, averaged over the
+ *          group's query heads (sums to 1 over the selection);
+ *   Q(s) = softmax of the selected blocks' index scores, the local block
+ *          scored on its visible tokens (no temperature);
+ *   KL   = sum_s P(s) (log P(s) - log Q(s)).
+ *
+ * msa_attend_with_mass: msa_attend plus
+ *   block_mass fp32 [total_q, num_kv_heads, top_k]  out: P, aligned with sel; 0 for padding.
+ * msa_index_kl: from the Index Branch inputs, the selection and its scores
+ *   (msa_index_select with sel_score, bf16 path) and block_mass:
+ *   log_q fp32 [total_q, num_kv_heads, top_k]  out, optional (NULL): log Q, NaN for padding
+ *   kl    fp32 [total_q, num_kv_heads]         out
+ *   No workspace.  total_q == 0 enqueues nothing.
+ */
+msa_status_t msa_attend_with_mass(const msa_dims_t* dims, const void* q, const void* k,
+                                  const void* v, const int32_t* cu_seqlens_q,
+                                  const int32_t* cu_seqlens_k, const int32_t* sel,
+                                  const int32_t* block_offsets, const int32_t* block_entries,
+                                  void* out, float* lse, float* block_mass, void* workspace,
+                                  size_t workspace_bytes, void* stream);
+msa_status_t msa_index_kl(const msa_dims_t* dims, const void* q_idx, const void* k_idx,
+                          const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                          const int32_t* sel, const float* sel_score, const float* block_mass,
+                          float* log_q, float* kl, void* stream);
+
 /* Static description of a status code. */
 const char* msa_status_string(msa_status_t status);
 
@@ -259,13 +291,14 @@ int32_t msa_abi_version(void);
  * recorded on the call's stream.  Stage ids: 0 index_select_prefill (scores + top-k),
  * 1 index_score_decode, 2 topk_select, 3 build_lists (all list kernels),
  * 4 attend_blocks, 5 merge_partials, 6 quantize_index_fp8,
- * 7 index_select_prefill_fp8, 8 index_score_decode_fp8, 9 index_project.  msa_profile_collect() waits for every
+ * 7 index_select_prefill_fp8, 8 index_score_decode_fp8, 9 index_project, 10 block_mass,
+ * 11 index_kl.  msa_profile_collect() waits for every
  * recorded event (it blocks the host), writes the summed milliseconds and the
  * launch count per stage into caller arrays of MSA_PROFILE_KERNELS entries,
  * and forgets the records.  Events are host-side HIP objects kept in a pool
  * for the life of the process; no device memory is allocated.
  */
-#define MSA_PROFILE_KERNELS 10
+#define MSA_PROFILE_KERNELS 12
 msa_status_t msa_profile_enable(int32_t enable);
 msa_status_t msa_profile_collect(float* total_ms, int32_t* launches);
 const char* msa_profile_kernel_name(int32_t id);

@@ -178,3 +178,20 @@ def test_projection_entry_point_validates_on_host():
     assert pj(ctypes.byref(d), 8192, ok, ok, odd, ok, ok, ok, ok, None) == 4
     empty = _dims(total_q=0, max_q_len=0)
     assert pj(ctypes.byref(empty), 8192, None, None, None, None, None, None, None, None) == 0
+
+
+def test_kl_entry_points_validate_on_host():
+    d = _dims()
+    P = ctypes.c_void_p
+    ok = P(0x10000)
+    odd = P(0x10004)
+    big = ctypes.c_size_t(1 << 40)
+    aw = lib.msa_attend_with_mass
+    assert aw(ctypes.byref(d), ok, ok, ok, ok, ok, ok, ok, ok, ok, None, None, ok, big, None) == 1
+    assert aw(ctypes.byref(d), ok, ok, ok, ok, ok, ok, ok, ok, ok, None, odd, ok, big, None) == 4
+    assert aw(ctypes.byref(d), ok, ok, ok, ok, ok, ok, ok, ok, ok, None, ok, ok, ctypes.c_size_t(8), None) == 5
+    kl = lib.msa_index_kl
+    assert kl(ctypes.byref(d), ok, ok, ok, ok, ok, None, ok, None, ok, None) == 1
+    assert kl(ctypes.byref(d), ok, ok, ok, ok, ok, ok, ok, None, odd, None) == 4
+    empty = _dims(total_q=0, max_q_len=0)
+    assert kl(ctypes.byref(empty), None, None, None, None, None, None, None, None, None, None) == 0
