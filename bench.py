@@ -37,6 +37,11 @@ PEAK_HBM_BYTES = 8.0e12       # MI355X HBM3E
 BLOCK = 128
 
 
+def _decode_like(w):
+    """Decode and speculative-verification steps: a few new tokens per sequence."""
+    return w.name == "decode" or w.name.startswith("verify")
+
+
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
@@ -73,23 +78,25 @@ def work_model(w) -> dict:
     attend_bytes = q_gather + part_write + kv_once
     merge_bytes = sel_total * hpg * (d * 4 + 8) + T * Hq * (d * 2 + 4)
     topk_bytes = scored_keys * G * 4 / BLOCK + T * G * k * 4
-    # decode: index keys of every sequence's earlier blocks, read once for all groups,
-    # plus the selected K/V blocks, Q, index queries and O
-    decode_bytes = (dec_kidx_tokens * di * 2 + sel_total * BLOCK * d * 2 * 2
+    # decode-shaped steps: index keys of every sequence's earlier blocks, read once for all
+    # groups and new tokens, plus each selected (group, block) of K/V once, Q, index queries, O
+    decode_bytes = (dec_kidx_tokens * di * 2 + kv_once
                     + T * (Hq * d * 2 * 2 + G * di * 2))
     # fp8 index branch: quantisation reads the bf16 projections and writes codes + exponents;
     # the decode scan then reads one byte per index-key element
     nblk = sum((lk + BLOCK - 1) // BLOCK for lk in w.seq_k_lens)
     quant_bytes = (T * G * di + w.total_k * di) * 3 + T * G + nblk
-    if w.name == "decode":      # a decode step quantises only its new index queries
+    if _decode_like(w):         # a decode step quantises only its new index queries
         quant_bytes = T * G * di * 3 + T * G
-    decode_fp8_bytes = (dec_kidx_tokens * di + sel_total * BLOCK * d * 2 * 2
+    decode_fp8_bytes = (dec_kidx_tokens * di + kv_once
                         + T * (Hq * d * 2 * 2 + G * (di + 1)))
     index_decode_fp8_bytes = dec_kidx_tokens * di + T * G * (di + 1)
+    index_decode_bytes = dec_kidx_tokens * di * 2 + T * G * di * 2
     return dict(index_flops=idx_flops, main_flops=main_flops, sel_total=sel_total,
                 attend_bytes=attend_bytes, merge_bytes=merge_bytes, topk_bytes=topk_bytes,
                 decode_bytes=decode_bytes, kv_once_bytes=kv_once, quant_bytes=quant_bytes,
-                decode_fp8_bytes=decode_fp8_bytes, index_decode_fp8_bytes=index_decode_fp8_bytes)
+                decode_fp8_bytes=decode_fp8_bytes, index_decode_fp8_bytes=index_decode_fp8_bytes,
+                index_decode_bytes=index_decode_bytes)
 
 
 # ---------------------------------------------------------------------------
@@ -389,7 +396,7 @@ def main():
     # fp8 decode: the index-key cache is stored quantised (quantised once, outside the step);
     # each step quantises only its new index queries.  Prefill quantises both in the step.
     step_k_idx = t["k_idx"]
-    if fp8 is not None and w.name == "decode":
+    if fp8 is not None and _decode_like(w):
         msa.index_quantize_fp8(dims, None, t["k_idx"], t["cu_seqlens_k"], fp8)
         torch.cuda.synchronize()
         step_k_idx = None
@@ -426,7 +433,7 @@ def main():
         torch.cuda.synchronize()
         log(f"[bench] warmup {i + 1}/{args.warmup} done")
 
-    use_graph = args.graph == "on" or (args.graph == "auto" and w.name == "decode")
+    use_graph = args.graph == "on" or (args.graph == "auto" and _decode_like(w))
     run = step
     if use_graph:
         # capture the three calls once (no allocation, no memset, no host sync inside)
@@ -509,7 +516,7 @@ def main():
                         dtype="fp8 e4m3" if name.endswith("fp8") else "bf16")
         bytes_ = {"attend_blocks": wm["attend_bytes"], "merge_partials": wm["merge_bytes"],
                   "topk_select": wm["topk_bytes"],
-                  "index_score_decode": wm["decode_bytes"] - wm["sel_total"] * BLOCK * w.head_dim * 4,
+                  "index_score_decode": wm["index_decode_bytes"],
                   "index_score_decode_fp8": wm["index_decode_fp8_bytes"],
                   "quantize_index_fp8": wm["quant_bytes"]}
         if name in bytes_:
@@ -525,7 +532,7 @@ def main():
     kernels = {k_: dict(stage[k_], roofline=roof(k_)) for k_ in stage}
     t_main = (per_step.get("attend_blocks", 0.0) + per_step.get("merge_partials", 0.0)) / 1e3
     main_mfma_frac = wm["main_flops"] / (t_main * PEAK_BF16_FLOPS) if t_main > 0 else None
-    decode = w.name == "decode"
+    decode = _decode_like(w)
     value = w.total_q / (ms_per_step / 1e3)
     extra = {}
     if decode:

@@ -336,7 +336,7 @@ __global__ __launch_bounds__(NW * 64, 2) void index_select_prefill_fp8_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// Decode scoring on E4M3 codes: at most 32 rows per sequence; grid.x = key-block
+// Decode scoring on E4M3 codes: at most 32 * RT rows per sequence; grid.x = key-block
 // segment, grid.y = sequence; wave w computes keys 32w .. 32w+31 of each block.
 // Writes S[beta * ld + row] = 2^(eq + ek) * max_j (q8 . k8_j) for the wide top-k.
 // ---------------------------------------------------------------------------
@@ -368,7 +368,7 @@ struct KTileStage8 {
   }
 };
 
-template <int DI, int SEG>
+template <int DI, int SEG, int RT>
 __global__ __launch_bounds__(256) void index_score_decode_fp8_kernel(
     const uint8_t* __restrict__ q8, const uint8_t* __restrict__ qe, const uint8_t* __restrict__ k8,
     const uint8_t* __restrict__ ke, const int32_t* __restrict__ cu_q,
@@ -377,8 +377,9 @@ __global__ __launch_bounds__(256) void index_score_decode_fp8_kernel(
   constexpr int NT = 256;
   constexpr int KS = DI >= 64 ? DI / 64 : 1;
   constexpr int LD = KTileStage8<DI, NT>::kLd;
+  constexpr int NR = 32 * RT;
   __shared__ __attribute__((aligned(16))) uint8_t lds[2][kBlock * LD];
-  __shared__ float red[2][4][32];
+  __shared__ float red[2][4][NR];
 
   const int b = blockIdx.y;
   const int qoff = cu_q[b], lq = cu_q[b + 1] - qoff;
@@ -390,7 +391,7 @@ __global__ __launch_bounds__(256) void index_score_decode_fp8_kernel(
   const int b0 = (int)blockIdx.x * SEG;
   const int b1 = min(beta_hi, b0 + SEG);
   if (b0 >= b1) return;
-  const int nrows = min((qz - qa) * G, 32);
+  const int nrows = min((qz - qa) * G, NR);
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
@@ -398,13 +399,15 @@ __global__ __launch_bounds__(256) void index_score_decode_fp8_kernel(
   const int col = lane & 31;
   const int half = lane >> 5;
 
-  i32x8 qf[KS];
-  {
-    const uint8_t* src = q8 + ((size_t)qa * G + col) * DI;
+  i32x8 qf[RT][KS];
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) {
+    const int n = rt * 32 + col;
+    const uint8_t* src = q8 + ((size_t)qa * G + n) * DI;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       uint4 lo = make_uint4(0, 0, 0, 0), hi = make_uint4(0, 0, 0, 0);
-      if (col < nrows) {
+      if (n < nrows) {
         if constexpr (DI == 32) {
           lo = *reinterpret_cast<const uint4*>(src + half * 16);
         } else {
@@ -412,10 +415,9 @@ __global__ __launch_bounds__(256) void index_score_decode_fp8_kernel(
           hi = *reinterpret_cast<const uint4*>(src + ks * 64 + half * 32 + 16);
         }
       }
-      qf[ks] = as_i32x8(lo, hi);
+      qf[rt][ks] = as_i32x8(lo, hi);
     }
   }
-  const int eq_lane = lane < nrows ? (int)qe[(size_t)qa * G + lane] - 127 : 0;
 
   const uint8_t* kbase = k8 + (size_t)koff * DI;
   KTileStage8<DI, NT> stage;
@@ -423,20 +425,31 @@ __global__ __launch_bounds__(256) void index_score_decode_fp8_kernel(
   stage.store(lds[0], tid);
   __syncthreads();
 
-  const size_t srow = (size_t)(qa - r0) * G;
+  // the four waves' partial maxima of block `blk`, scaled by 2^(eq + ek) -> S
+  auto finish = [&](int it, int blk) __attribute__((always_inline)) {
+    if (wave != 0) return;
+    const size_t srow = (size_t)(qa - r0) * G;
+    const int ek = (int)ke[(size_t)b * nb_max + blk] - 127;
+#pragma unroll
+    for (int j = 0; j < (NR + 63) / 64; ++j) {
+      const int n = j * 64 + lane;
+      if (n < nrows) {
+        const float* rr = &red[it & 1][0][0];
+        const float m = fmaxf(fmaxf(rr[n], rr[NR + n]), fmaxf(rr[2 * NR + n], rr[3 * NR + n]));
+        const int eq = (int)qe[(size_t)qa * G + n] - 127;
+        S[(size_t)blk * ld + srow + n] = ldexpf(m, eq + ek);
+      }
+    }
+  };
+
   for (int beta = b0; beta < b1; ++beta) {
     const int it = beta - b0;
     stage.load(kbase + (size_t)min(beta + 1, b1 - 1) * kBlock * DI, tid);
-    // finish the previous block's reduction (its partial maxima are complete)
-    if (it > 0 && wave == 0 && lane < nrows) {
-      const float* rr = &red[(it - 1) & 1][0][0];
-      const float m = fmaxf(fmaxf(rr[lane], rr[32 + lane]), fmaxf(rr[64 + lane], rr[96 + lane]));
-      const int ek = (int)ke[(size_t)b * nb_max + beta - 1] - 127;
-      S[(size_t)(beta - 1) * ld + srow + lane] = ldexpf(m, eq_lane + ek);
-    }
-    const uint8_t* kt_lds = lds[it & 1];
-    const uint8_t* arow = kt_lds + (wave * 32 + col) * LD;
-    f32x16 acc = f32x16{};
+    if (it > 0) finish(it - 1, beta - 1);
+    const uint8_t* arow = lds[it & 1] + (wave * 32 + col) * LD;
+    f32x16 acc[RT];
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) acc[rt] = f32x16{};
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       i32x8 a;
@@ -446,23 +459,21 @@ __global__ __launch_bounds__(256) void index_score_decode_fp8_kernel(
         a = as_i32x8(*reinterpret_cast<const uint4*>(arow + ks * 64 + half * 32),
                      *reinterpret_cast<const uint4*>(arow + ks * 64 + half * 32 + 16));
       }
-      acc = mfma32_fp8(a, qf[ks], acc);
-    }
-    float m = acc[0];
 #pragma unroll
-    for (int i = 1; i < 16; ++i) m = fmaxf(m, acc[i]);
-    m = fmaxf(m, shfl_xor_f(m, 32));
-    if (half == 0) red[it & 1][wave][col] = m;
+      for (int rt = 0; rt < RT; ++rt) acc[rt] = mfma32_fp8(a, qf[rt][ks], acc[rt]);
+    }
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+      float m = acc[rt][0];
+#pragma unroll
+      for (int i = 1; i < 16; ++i) m = fmaxf(m, acc[rt][i]);
+      m = fmaxf(m, shfl_xor_f(m, 32));
+      if (half == 0) red[it & 1][wave][rt * 32 + col] = m;
+    }
     stage.store(lds[(it + 1) & 1], tid);
     __syncthreads();
   }
-  if (wave == 0 && lane < nrows) {
-    const int it = b1 - 1 - b0;
-    const float* rr = &red[it & 1][0][0];
-    const float m = fmaxf(fmaxf(rr[lane], rr[32 + lane]), fmaxf(rr[64 + lane], rr[96 + lane]));
-    const int ek = (int)ke[(size_t)b * nb_max + b1 - 1] - 127;
-    S[(size_t)(b1 - 1) * ld + srow + lane] = ldexpf(m, eq_lane + ek);
-  }
+  finish(b1 - 1 - b0, b1 - 1);
 }
 
 // ---------------------------------------------------------------------------
@@ -550,23 +561,27 @@ hipError_t launch_index_select_prefill_fp8(const void* q8, const uint8_t* qe, co
 template <int DI>
 static hipError_t launch_decode8_di(const void* q8, const uint8_t* qe, const void* k8,
                                     const uint8_t* ke, const int32_t* cu_q, const int32_t* cu_k,
-                                    int batch, int G, int nb_max, int r0, int r1, float* S,
-                                    long long ld, hipStream_t st) {
+                                    int batch, int G, int nb_max, int rows, int r0, int r1,
+                                    float* S, long long ld, hipStream_t st) {
   dim3 grid((nb_max + kFp8DecodeSeg - 1) / kFp8DecodeSeg, batch);
-  hipLaunchKernelGGL((index_score_decode_fp8_kernel<DI, kFp8DecodeSeg>), grid, dim3(256), 0, st,
-                     (const uint8_t*)q8, qe, (const uint8_t*)k8, ke, cu_q, cu_k, G, nb_max, r0, r1,
-                     S, ld);
+#define MSA_DEC8(RT) hipLaunchKernelGGL((index_score_decode_fp8_kernel<DI, kFp8DecodeSeg, RT>), grid, dim3(256), 0, st, (const uint8_t*)q8, qe, (const uint8_t*)k8, ke, cu_q, cu_k, G, nb_max, r0, r1, S, ld)
+  if (rows <= 32) MSA_DEC8(1);
+  else if (rows <= 64) MSA_DEC8(2);
+  else if (rows <= 128) MSA_DEC8(4);
+  else return hipErrorInvalidValue;
+#undef MSA_DEC8
   return hipGetLastError();
 }
 
 hipError_t launch_index_score_decode_fp8(const void* q8, const uint8_t* qe, const void* k8,
                                          const uint8_t* ke, const int32_t* cu_q,
                                          const int32_t* cu_k, int batch, int G, int DI, int nb_max,
-                                         int r0, int r1, float* S, long long ld, hipStream_t st) {
+                                         int rows, int r0, int r1, float* S, long long ld,
+                                         hipStream_t st) {
   switch (DI) {
-    case 32: return launch_decode8_di<32>(q8, qe, k8, ke, cu_q, cu_k, batch, G, nb_max, r0, r1, S, ld, st);
-    case 64: return launch_decode8_di<64>(q8, qe, k8, ke, cu_q, cu_k, batch, G, nb_max, r0, r1, S, ld, st);
-    case 128: return launch_decode8_di<128>(q8, qe, k8, ke, cu_q, cu_k, batch, G, nb_max, r0, r1, S, ld, st);
+    case 32: return launch_decode8_di<32>(q8, qe, k8, ke, cu_q, cu_k, batch, G, nb_max, rows, r0, r1, S, ld, st);
+    case 64: return launch_decode8_di<64>(q8, qe, k8, ke, cu_q, cu_k, batch, G, nb_max, rows, r0, r1, S, ld, st);
+    case 128: return launch_decode8_di<128>(q8, qe, k8, ke, cu_q, cu_k, batch, G, nb_max, rows, r0, r1, S, ld, st);
   }
   return hipErrorInvalidValue;
 }

@@ -223,10 +223,11 @@ __global__ __launch_bounds__(NW * 64) void index_select_prefill_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// Decode: at most 32 rows per sequence; grid.x = key-block segment, grid.y = sequence.
-// Wave w computes keys 32w .. 32w+31 of every block in the segment.
+// Decode-shaped steps: at most 32 * RT (query, group) rows per sequence (RT = 1,
+// 2, 4 row tiles); grid.x = key-block segment, grid.y = sequence.  Wave w
+// computes keys 32w .. 32w+31 of every block in the segment for all rows.
 // ---------------------------------------------------------------------------
-template <int DI, int SEG>
+template <int DI, int SEG, int RT>
 __global__ __launch_bounds__(256) void index_score_decode_kernel(
     const uint16_t* __restrict__ q_idx, const uint16_t* __restrict__ k_idx,
     const int32_t* __restrict__ cu_q, const int32_t* __restrict__ cu_k, int G, int r0, int r1,
@@ -234,8 +235,9 @@ __global__ __launch_bounds__(256) void index_score_decode_kernel(
   constexpr int NT = 256;
   constexpr int KS = DI / 16;
   constexpr int LD = DI + 8;
+  constexpr int NR = 32 * RT;              // (query, group) rows of one sequence, at most
   __shared__ __attribute__((aligned(16))) uint16_t lds[2][kBlock * LD];
-  __shared__ float red[2][4][32];
+  __shared__ float red[2][4][NR];
 
   const int b = blockIdx.y;
   const int qoff = cu_q[b], lq = cu_q[b + 1] - qoff;
@@ -247,7 +249,7 @@ __global__ __launch_bounds__(256) void index_score_decode_kernel(
   const int b0 = (int)blockIdx.x * SEG;
   const int b1 = min(beta_hi, b0 + SEG);
   if (b0 >= b1) return;
-  const int nrows = min((qz - qa) * G, 32);
+  const int nrows = min((qz - qa) * G, NR);
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
@@ -255,14 +257,17 @@ __global__ __launch_bounds__(256) void index_score_decode_kernel(
   const int col = lane & 31;
   const int half = lane >> 5;
 
-  bf16x8 qf[KS];
-  {
-    const uint16_t* src = q_idx + ((size_t)qa * G + col) * DI;
+  // row tile rt holds rows 32 rt .. 32 rt + 31 as the MFMA B operand (lane <-> row)
+  bf16x8 qf[RT][KS];
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) {
+    const int n = rt * 32 + col;
+    const uint16_t* src = q_idx + ((size_t)qa * G + n) * DI;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       uint4 v = make_uint4(0, 0, 0, 0);
-      if (col < nrows) v = *reinterpret_cast<const uint4*>(src + ks * 16 + half * 8);
-      qf[ks] = as_bf16x8(v);
+      if (n < nrows) v = *reinterpret_cast<const uint4*>(src + ks * 16 + half * 8);
+      qf[rt][ks] = as_bf16x8(v);
     }
   }
 
@@ -272,37 +277,48 @@ __global__ __launch_bounds__(256) void index_score_decode_kernel(
   stage.store(lds[0], tid);
   __syncthreads();
 
-  const size_t srow = (size_t)(qa - r0) * G;
+  // the four waves' partial maxima of block `blk` (kept in red[it & 1]) -> S
+  auto finish = [&](int it, int blk) __attribute__((always_inline)) {
+    if (wave != 0) return;
+    const size_t srow = (size_t)(qa - r0) * G;
+#pragma unroll
+    for (int j = 0; j < (NR + 63) / 64; ++j) {
+      const int n = j * 64 + lane;
+      if (n < nrows) {
+        const float* rr = &red[it & 1][0][0];
+        const float m = fmaxf(fmaxf(rr[n], rr[NR + n]), fmaxf(rr[2 * NR + n], rr[3 * NR + n]));
+        S[(size_t)blk * ld + srow + n] = m;
+      }
+    }
+  };
+
   for (int beta = b0; beta < b1; ++beta) {
     const int it = beta - b0;
     stage.load(kbase + (size_t)min(beta + 1, b1 - 1) * kBlock * DI, tid);
     // finish the previous block's reduction (its partial maxima are complete)
-    if (it > 0 && wave == 0 && lane < nrows) {
-      const float* rr = &red[(it - 1) & 1][0][0];
-      float m = fmaxf(fmaxf(rr[lane], rr[32 + lane]), fmaxf(rr[64 + lane], rr[96 + lane]));
-      S[(size_t)(beta - 1) * ld + srow + lane] = m;
-    }
+    if (it > 0) finish(it - 1, beta - 1);
     const uint16_t* kt_lds = lds[it & 1];
-    f32x16 acc = f32x16{};
+    f32x16 acc[RT];
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) acc[rt] = f32x16{};
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       bf16x8 a = as_bf16x8(*reinterpret_cast<const uint4*>(kt_lds + (wave * 32 + col) * LD + ks * 16 + half * 8));
-      acc = mfma32(a, qf[ks], acc);
-    }
-    float m = acc[0];
 #pragma unroll
-    for (int i = 1; i < 16; ++i) m = fmaxf(m, acc[i]);
-    m = fmaxf(m, shfl_xor_f(m, 32));
-    if (half == 0) red[it & 1][wave][col] = m;
+      for (int rt = 0; rt < RT; ++rt) acc[rt] = mfma32(a, qf[rt][ks], acc[rt]);
+    }
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+      float m = acc[rt][0];
+#pragma unroll
+      for (int i = 1; i < 16; ++i) m = fmaxf(m, acc[rt][i]);
+      m = fmaxf(m, shfl_xor_f(m, 32));
+      if (half == 0) red[it & 1][wave][rt * 32 + col] = m;
+    }
     stage.store(lds[(it + 1) & 1], tid);
     __syncthreads();
   }
-  if (wave == 0 && lane < nrows) {
-    const int it = b1 - 1 - b0;
-    const float* rr = &red[it & 1][0][0];
-    float m = fmaxf(fmaxf(rr[lane], rr[32 + lane]), fmaxf(rr[64 + lane], rr[96 + lane]));
-    S[(size_t)(b1 - 1) * ld + srow + lane] = m;
-  }
+  finish(b1 - 1 - b0, b1 - 1);
 }
 
 // ---------------------------------------------------------------------------
@@ -356,21 +372,26 @@ hipError_t launch_index_select_prefill(const void* q_idx, const void* k_idx, con
 
 template <int DI>
 static hipError_t launch_decode_di(const void* q_idx, const void* k_idx, const int32_t* cu_q,
-                                   const int32_t* cu_k, int batch, int G, int nb_max, int r0, int r1,
-                                   float* S, long long ld, hipStream_t st) {
+                                   const int32_t* cu_k, int batch, int G, int nb_max, int rows,
+                                   int r0, int r1, float* S, long long ld, hipStream_t st) {
   dim3 grid((nb_max + kDecodeSeg - 1) / kDecodeSeg, batch);
-  hipLaunchKernelGGL((index_score_decode_kernel<DI, kDecodeSeg>), grid, dim3(256), 0, st,
-                     (const uint16_t*)q_idx, (const uint16_t*)k_idx, cu_q, cu_k, G, r0, r1, S, ld);
+#define MSA_DEC(RT) hipLaunchKernelGGL((index_score_decode_kernel<DI, kDecodeSeg, RT>), grid, dim3(256), 0, st, (const uint16_t*)q_idx, (const uint16_t*)k_idx, cu_q, cu_k, G, r0, r1, S, ld)
+  if (rows <= 32) MSA_DEC(1);
+  else if (rows <= 64) MSA_DEC(2);
+  else if (rows <= 128) MSA_DEC(4);
+  else return hipErrorInvalidValue;
+#undef MSA_DEC
   return hipGetLastError();
 }
 
 hipError_t launch_index_score_decode(const void* q_idx, const void* k_idx, const int32_t* cu_q,
                                      const int32_t* cu_k, int batch, int G, int DI, int nb_max,
-                                     int r0, int r1, float* S, long long ld, hipStream_t st) {
+                                     int rows, int r0, int r1, float* S, long long ld,
+                                     hipStream_t st) {
   switch (DI) {
-    case 32: return launch_decode_di<32>(q_idx, k_idx, cu_q, cu_k, batch, G, nb_max, r0, r1, S, ld, st);
-    case 64: return launch_decode_di<64>(q_idx, k_idx, cu_q, cu_k, batch, G, nb_max, r0, r1, S, ld, st);
-    case 128: return launch_decode_di<128>(q_idx, k_idx, cu_q, cu_k, batch, G, nb_max, r0, r1, S, ld, st);
+    case 32: return launch_decode_di<32>(q_idx, k_idx, cu_q, cu_k, batch, G, nb_max, rows, r0, r1, S, ld, st);
+    case 64: return launch_decode_di<64>(q_idx, k_idx, cu_q, cu_k, batch, G, nb_max, rows, r0, r1, S, ld, st);
+    case 128: return launch_decode_di<128>(q_idx, k_idx, cu_q, cu_k, batch, G, nb_max, rows, r0, r1, S, ld, st);
   }
   return hipErrorInvalidValue;
 }

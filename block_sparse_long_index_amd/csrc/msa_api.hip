@@ -17,7 +17,7 @@ namespace msa {
 hipError_t launch_index_select_prefill(const void*, const void*, const int32_t*, const int32_t*, int,
                                        int, int, int, int, int32_t*, float*, hipStream_t);
 hipError_t launch_index_score_decode(const void*, const void*, const int32_t*, const int32_t*, int,
-                                     int, int, int, int, int, float*, long long, hipStream_t);
+                                     int, int, int, int, int, int, float*, long long, hipStream_t);
 hipError_t launch_topk_select(const float*, long long, int, int, const int32_t*, const int32_t*, int,
                               int, int, bool, int32_t*, float*, hipStream_t);
 size_t lists_workspace_bytes(int batch, int G, int nqt_max, int nb_max);
@@ -47,7 +47,7 @@ hipError_t launch_index_select_prefill_fp8(const void*, const uint8_t*, const vo
                                            int, int32_t*, float*, hipStream_t);
 hipError_t launch_index_score_decode_fp8(const void*, const uint8_t*, const void*, const uint8_t*,
                                          const int32_t*, const int32_t*, int, int, int, int, int,
-                                         int, float*, long long, hipStream_t);
+                                         int, int, float*, long long, hipStream_t);
 }  // namespace msa
 
 namespace {
@@ -56,6 +56,8 @@ thread_local std::string g_last_error;
 
 constexpr size_t kDefaultChunkBytes = (size_t)48 << 30;   // workspace cap when q_chunk == 0
 constexpr int kMaxNbLds = 12288;                          // per-sequence blocks the LDS lists hold
+constexpr int kDecodeRowsMax = 128;                       // (query, group) rows per sequence, decode path
+constexpr int kDecodeAttendMaxQ = 8;                      // queries per sequence, per-(query, slot) attend
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
@@ -107,7 +109,8 @@ msa_status_t check_dims(const msa_dims_t* d, Derived* out) {
     return fail(MSA_ERR_UNSUPPORTED, "max_k_len too long for the on-chip list builder");
   if ((long long)d->batch * out->G * out->nb_max >= ((long long)1 << 30))
     return fail(MSA_ERR_UNSUPPORTED, "batch * num_kv_heads * blocks too large");
-  out->decode_path = (long long)d->max_q_len * out->G <= 32;
+  // decode-shaped steps (a few new tokens per sequence): split-scan index kernels
+  out->decode_path = (long long)d->max_q_len * out->G <= kDecodeRowsMax;
   out->scale = d->softmax_scale > 0.f ? d->softmax_scale : 1.f / sqrtf((float)d->head_dim);
   out->total_q = d->total_q;
   return MSA_OK;
@@ -280,7 +283,7 @@ msa_status_t msa_index_select(const msa_dims_t* dims, const void* q_idx, const v
     {
       ProfScope ps(K_INDEX_DECODE, st);
       e = msa::launch_index_score_decode(q_idx, k_idx, cu_seqlens_q, cu_seqlens_k, dims->batch, x.G,
-                                         x.DI, x.nb_max, a, z, S, ld, st);
+                                         x.DI, x.nb_max, dims->max_q_len * x.G, a, z, S, ld, st);
     }
     if (e != hipSuccess) return hip_fail(e);
     ProfScope ps(K_TOPK, st);
@@ -372,8 +375,8 @@ msa_status_t msa_index_select_fp8(const msa_dims_t* dims, const void* q_idx8, co
     {
       ProfScope ps(K_INDEX_DECODE_FP8, st);
       e = msa::launch_index_score_decode_fp8(q_idx8, q_exp, k_idx8, k_exp, cu_seqlens_q,
-                                             cu_seqlens_k, dims->batch, x.G, x.DI, x.nb_max, a, z,
-                                             S, ld, st);
+                                             cu_seqlens_k, dims->batch, x.G, x.DI, x.nb_max,
+                                             dims->max_q_len * x.G, a, z, S, ld, st);
     }
     if (e != hipSuccess) return hip_fail(e);
     ProfScope ps(K_TOPK, st);
@@ -437,9 +440,9 @@ static msa_status_t attend_impl(const msa_dims_t* dims, const void* q, const voi
     hipError_t e;
     {
       ProfScope ps(K_ATTEND, st);
-      if (dims->max_q_len == 1)
-        // one query per sequence: each selected block is hit by that query only;
-        // one wave per (query, slot) reads it once, straight from the selection
+      if (dims->max_q_len <= kDecodeAttendMaxQ)
+        // a few queries per sequence: each selected block is hit by few queries;
+        // one wave per (query, slot) reads it straight from the selection
         e = msa::launch_attend_decode(x.D, x.hpg, q, k, v, cu_seqlens_q, cu_seqlens_k, dims->batch,
                                       x.G, x.Hq, x.top_k, sel, a, z, scale_log2, part_acc, part_ml,
                                       st);

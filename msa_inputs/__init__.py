@@ -97,6 +97,12 @@ def workload(name: str, **overrides) -> Workload:
         lens = _decode_lengths(1004, 32, 512, 2048)
         w = Workload("decode", lens, [1] * len(lens), seed=1004, **big,
                      note="32 seqs x 1 new token, contexts 128*U{512..2048}")
+    elif name in ("verify2", "verify4", "verify8"):
+        # speculative-decoding verification: the decode contexts, n new tokens each
+        n = int(name[-1])
+        lens = _decode_lengths(1004, 32, 512, 2048)
+        w = Workload(name, lens, [n] * len(lens), seed=1006, **big,
+                     note=f"32 seqs x {n} new tokens, contexts 128*U{{512..2048}}")
     else:
         raise KeyError(name)
     for k_, v_ in overrides.items():

@@ -331,3 +331,9 @@ def test_fp8_p128k_sampled():
 def test_fp8_decode_sampled():
     # eight of the 32 sequences (each quantised whole by the oracle)
     _sampled_fp8("decode", lambda w: list(range(0, w.total_q, 4)))
+
+
+def test_fp8_verification_shape():
+    w = custom([7000, 4100, 300, 2049], [8, 8, 5, 8], num_q_heads=32, num_kv_heads=8,
+               head_dim=128, index_dim=128, top_k=8, seed=50, qkv_std=1.0)
+    _full_check(w, "fp8-verify8")

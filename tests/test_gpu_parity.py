@@ -195,3 +195,14 @@ def test_empty_query_set():
     bufs = msa.msa_forward(dims, q, kv, kv, qi, ki, cuq, cuk)
     torch.cuda.synchronize()
     assert int(bufs.offsets[-1]) == 0
+
+
+def test_verification_shapes_two_and_four_row_tiles():
+    # speculative-decoding verification: 8 and 16 new tokens x 8 groups = 64 / 128 rows per
+    # sequence (two / four row tiles of the split-scan index kernel), ragged contexts, tokens
+    # that straddle a block boundary; attention through the per-(query, slot) kernel (<= 8
+    # queries) and the list-based kernel (16 queries)
+    for lq, seed in ((8, 36), (16, 37)):
+        w = custom([7000, 4100, 300, 2049], [lq, lq, 5, lq], num_q_heads=32, num_kv_heads=8,
+                   head_dim=128, index_dim=128, top_k=8, seed=seed, qkv_std=1.0)
+        _full_check(w, tag=f"verify{lq}")
