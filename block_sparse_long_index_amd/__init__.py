@@ -43,7 +43,9 @@ class Dims(ctypes.Structure):
         ("top_k", ctypes.c_int32), ("softmax_scale", ctypes.c_float),
         ("total_q", ctypes.c_int64), ("total_k", ctypes.c_int64),
         ("max_q_len", ctypes.c_int32), ("max_k_len", ctypes.c_int32),
-        ("q_chunk", ctypes.c_int32), ("reserved", ctypes.c_int32),
+        ("q_chunk", ctypes.c_int32), ("kv_pages", ctypes.c_int32),
+        ("block_table", ctypes.c_void_p), ("max_blocks_per_seq", ctypes.c_int32),
+        ("reserved", ctypes.c_int32),
     ]
 
 
@@ -111,10 +113,23 @@ def exported_symbols(header: str = HEADER_PATH) -> list:
 
 
 def make_dims(*, batch, num_q_heads, num_kv_heads, head_dim, index_dim, top_k, total_q, total_k,
-              max_q_len, max_k_len, softmax_scale=0.0, q_chunk=0, block_size=BLOCK) -> Dims:
-    return Dims(int(batch), int(num_q_heads), int(num_kv_heads), int(head_dim), int(index_dim),
-                int(block_size), int(top_k), float(softmax_scale), int(total_q), int(total_k),
-                int(max_q_len), int(max_k_len), int(q_chunk), 0)
+              max_q_len, max_k_len, softmax_scale=0.0, q_chunk=0, block_size=BLOCK,
+              block_table=None) -> Dims:
+    """Problem sizes.  ``block_table`` (device int32 [batch, max_blocks_per_seq]) selects a
+    paged key cache: ``total_k`` is then the cache's row count, 128 per page.  The
+    returned dims keep a reference to the table (they hold its device address)."""
+    pages, table, mbs = 0, None, 0
+    if block_table is not None:
+        _ptr(block_table, "block_table", torch.int32)
+        if block_table.dim() != 2 or block_table.shape[0] != int(batch):
+            raise ValueError("block_table must be [batch, max_blocks_per_seq]")
+        pages, table, mbs = int(total_k) // BLOCK, block_table.data_ptr(), int(block_table.shape[1])
+    d = Dims(int(batch), int(num_q_heads), int(num_kv_heads), int(head_dim), int(index_dim),
+             int(block_size), int(top_k), float(softmax_scale), int(total_q), int(total_k),
+             int(max_q_len), int(max_k_len), int(q_chunk), pages, table, mbs, 0)
+    # the struct holds the table's device address: keep the tensor alive with it
+    d._block_table = block_table
+    return d
 
 
 def workspace_size(dims: Dims, op: int) -> int:
@@ -195,6 +210,11 @@ def index_project(dims, x, w_q, w_k, cu_seqlens_q, cu_seqlens_k, q_idx, k_idx, s
     return q_idx, k_idx
 
 
+def _k_exp_shape(dims):
+    """Per-block exponents of the quantised index keys: [batch, nb_max], or one per page."""
+    return (dims.kv_pages,) if dims.kv_pages else (dims.batch, nb_max(dims))
+
+
 class Fp8Index:
     """E4M3 codes and E8M0 exponents of the index projections for fixed dims."""
 
@@ -204,7 +224,7 @@ class Fp8Index:
         self.q_idx8 = torch.empty((T, G, DI), dtype=torch.uint8, device=dev)
         self.q_exp = torch.empty((T, G), dtype=torch.uint8, device=dev)
         self.k_idx8 = torch.empty((dims.total_k, DI), dtype=torch.uint8, device=dev)
-        self.k_exp = torch.empty((dims.batch, nb_max(dims)), dtype=torch.uint8, device=dev)
+        self.k_exp = torch.empty(_k_exp_shape(dims), dtype=torch.uint8, device=dev)
 
 
 def index_quantize_fp8(dims, q_idx, k_idx, cu_seqlens_k, fp8: Fp8Index, stream=None):
@@ -220,7 +240,7 @@ def index_quantize_fp8(dims, q_idx, k_idx, cu_seqlens_k, fp8: Fp8Index, stream=N
     _shape(fp8.q_idx8, (T, G, DI), "q_idx8")
     _shape(fp8.q_exp, (T, G), "q_exp")
     _shape(fp8.k_idx8, (dims.total_k, DI), "k_idx8")
-    _shape(fp8.k_exp, (dims.batch, nb_max(dims)), "k_exp")
+    _shape(fp8.k_exp, _k_exp_shape(dims), "k_exp")
     st = load_library().msa_index_quantize_fp8(
         ctypes.byref(dims), _ptr(q_idx, "q_idx", torch.bfloat16), _ptr(k_idx, "k_idx", torch.bfloat16),
         _ptr(cu_seqlens_k, "cu_seqlens_k", torch.int32), _ptr(fp8.q_idx8, "q_idx8", torch.uint8),
@@ -237,7 +257,7 @@ def index_select_fp8(dims, fp8: Fp8Index, cu_seqlens_q, cu_seqlens_k, sel, sel_s
     _shape(fp8.q_idx8, (T, G, dims.index_dim), "q_idx8")
     _shape(fp8.k_idx8, (dims.total_k, dims.index_dim), "k_idx8")
     _shape(fp8.q_exp, (T, G), "q_exp")
-    _shape(fp8.k_exp, (dims.batch, nb_max(dims)), "k_exp")
+    _shape(fp8.k_exp, _k_exp_shape(dims), "k_exp")
     _shape(sel, (T, G, dims.top_k), "sel")
     if sel_score is not None:
         _shape(sel_score, (T, G, dims.top_k), "sel_score")

@@ -92,7 +92,7 @@ template <int D, int HPG>
 __device__ __forceinline__ void attend_item(
     long long item, const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, const int32_t* __restrict__ cu_q,
-    const int32_t* __restrict__ cu_k, int batch, int G, int Hq, int top_k, int nb_max,
+    const int32_t* __restrict__ cu_k, KvMap kv, int batch, int G, int Hq, int top_k, int nb_max,
     const int32_t* __restrict__ offsets, const int32_t* __restrict__ entries, int r0, int r1,
     int total_q, float scale_log2, float* __restrict__ part_acc, float2* __restrict__ part_ml,
     int spare_row, uint16_t* Ks, uint16_t* Vt, int* range) {
@@ -145,16 +145,17 @@ __device__ __forceinline__ void attend_item(
   // V: consecutive threads take consecutive keys, so the transposed 2-byte LDS
   //    writes of a wave land on consecutive addresses.
   const int kb = beta * kBlock;
+  const size_t row0 = kv.block_row(b, koff, beta);   // first cache row of the block
   for (int c = tid; c < kBlock * D / 8; c += 256) {
     const int key = c / (D / 8), dc = c % (D / 8);
-    uint4 kv = make_uint4(0, 0, 0, 0);
-    if (kb + key < lk) kv = *reinterpret_cast<const uint4*>(k + ((size_t)(koff + kb + key) * G + g) * D + dc * 8);
-    *reinterpret_cast<uint4*>(Ks + key * LDK + dc * 8) = kv;
+    uint4 kk = make_uint4(0, 0, 0, 0);
+    if (kb + key < lk) kk = *reinterpret_cast<const uint4*>(k + ((row0 + key) * G + g) * D + dc * 8);
+    *reinterpret_cast<uint4*>(Ks + key * LDK + dc * 8) = kk;
   }
   for (int c = tid; c < kBlock * D / 8; c += 256) {
     const int key = c % kBlock, dc = c / kBlock;
     uint4 vv = make_uint4(0, 0, 0, 0);
-    if (kb + key < lk) vv = *reinterpret_cast<const uint4*>(v + ((size_t)(koff + kb + key) * G + g) * D + dc * 8);
+    if (kb + key < lk) vv = *reinterpret_cast<const uint4*>(v + ((row0 + key) * G + g) * D + dc * 8);
     const uint32_t vw[4] = {vv.x, vv.y, vv.z, vv.w};
 #pragma unroll
     for (int i = 0; i < 8; ++i)
@@ -280,10 +281,10 @@ __device__ __forceinline__ void attend_item(
 template <int D, int HPG>
 __global__ __launch_bounds__(256, 2) void attend_blocks_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
-    const int32_t* __restrict__ cu_q, const int32_t* __restrict__ cu_k, int batch, int G, int Hq,
-    int top_k, int nb_max, const int32_t* __restrict__ offsets, const int32_t* __restrict__ entries,
-    int r0, int r1, int total_q, float scale_log2, float* __restrict__ part_acc,
-    float2* __restrict__ part_ml, int spare_row, int items_per_wg) {
+    const int32_t* __restrict__ cu_q, const int32_t* __restrict__ cu_k, KvMap kv, int batch, int G,
+    int Hq, int top_k, int nb_max, const int32_t* __restrict__ offsets,
+    const int32_t* __restrict__ entries, int r0, int r1, int total_q, float scale_log2,
+    float* __restrict__ part_acc, float2* __restrict__ part_ml, int spare_row, int items_per_wg) {
   constexpr int LDK = D + 8;
   constexpr int LDV = kBlock + 4;
   __shared__ __attribute__((aligned(16))) uint16_t Ks[kBlock * LDK];
@@ -294,8 +295,9 @@ __global__ __launch_bounds__(256, 2) void attend_blocks_kernel(
   const long long n_items = (long long)nb_max * BG;
   const long long first = (long long)blockIdx.x * items_per_wg;
   if (items_per_wg == 1) {
-    attend_item<D, HPG>(first, q, k, v, cu_q, cu_k, batch, G, Hq, top_k, nb_max, offsets, entries,
-                        r0, r1, total_q, scale_log2, part_acc, part_ml, spare_row, Ks, Vt, range);
+    attend_item<D, HPG>(first, q, k, v, cu_q, cu_k, kv, batch, G, Hq, top_k, nb_max, offsets,
+                        entries, r0, r1, total_q, scale_log2, part_acc, part_ml, spare_row, Ks, Vt,
+                        range);
     return;
   }
   const int tid = threadIdx.x;
@@ -314,7 +316,7 @@ __global__ __launch_bounds__(256, 2) void attend_blocks_kernel(
   while (m) {
     const int i = __ffsll((long long)m) - 1;
     m &= m - 1;
-    attend_item<D, HPG>(first + i, q, k, v, cu_q, cu_k, batch, G, Hq, top_k, nb_max, offsets,
+    attend_item<D, HPG>(first + i, q, k, v, cu_q, cu_k, kv, batch, G, Hq, top_k, nb_max, offsets,
                         entries, r0, r1, total_q, scale_log2, part_acc, part_ml, spare_row, Ks, Vt,
                         range);
     __syncthreads();   // LDS and range are reused by the next item
@@ -395,7 +397,8 @@ __global__ __launch_bounds__(kMergeWaves * 64) void merge_partials_kernel(
 // ---------------------------------------------------------------------------
 template <int D, int HPG>
 static void launch_attend_t(const void* q, const void* k, const void* v, const int32_t* cu_q,
-                            const int32_t* cu_k, int batch, int G, int Hq, int top_k, int nb_max,
+                            const int32_t* cu_k, KvMap kv, int batch, int G, int Hq, int top_k,
+                            int nb_max,
                             const int32_t* offsets, const int32_t* entries, int r0, int r1,
                             int total_q, float scale_log2, float* part_acc, float2* part_ml,
                             hipStream_t st) {
@@ -405,19 +408,20 @@ static void launch_attend_t(const void* q, const void* k, const void* v, const i
   const int ipw = per_item >= 4.0 ? 1 : 64;
   dim3 grid((unsigned)((n_items + ipw - 1) / ipw));
   hipLaunchKernelGGL((attend_blocks_kernel<D, HPG>), grid, dim3(256), 0, st, (const uint16_t*)q,
-                     (const uint16_t*)k, (const uint16_t*)v, cu_q, cu_k, batch, G, Hq, top_k,
+                     (const uint16_t*)k, (const uint16_t*)v, cu_q, cu_k, kv, batch, G, Hq, top_k,
                      nb_max, offsets, entries, r0, r1, total_q, scale_log2, part_acc, part_ml,
                      (r1 - r0) * Hq * top_k, ipw);
 }
 
 template <int D>
 static hipError_t launch_attend_d(int hpg, const void* q, const void* k, const void* v,
-                                  const int32_t* cu_q, const int32_t* cu_k, int batch, int G, int Hq,
+                                  const int32_t* cu_q, const int32_t* cu_k, KvMap kv, int batch,
+                                  int G, int Hq,
                                   int top_k, int nb_max, const int32_t* offsets,
                                   const int32_t* entries, int r0, int r1, int total_q,
                                   float scale_log2, float* part_acc, float2* part_ml,
                                   hipStream_t st) {
-#define MSA_ATT(H) launch_attend_t<D, H>(q, k, v, cu_q, cu_k, batch, G, Hq, top_k, nb_max, offsets, entries, r0, r1, total_q, scale_log2, part_acc, part_ml, st)
+#define MSA_ATT(H) launch_attend_t<D, H>(q, k, v, cu_q, cu_k, kv, batch, G, Hq, top_k, nb_max, offsets, entries, r0, r1, total_q, scale_log2, part_acc, part_ml, st)
   switch (hpg) {
     case 1: MSA_ATT(1); break;
     case 2: MSA_ATT(2); break;
@@ -432,15 +436,15 @@ static hipError_t launch_attend_d(int hpg, const void* q, const void* k, const v
 }
 
 hipError_t launch_attend_blocks(int D, int hpg, const void* q, const void* k, const void* v,
-                                const int32_t* cu_q, const int32_t* cu_k, int batch, int G, int Hq,
-                                int top_k, int nb_max, const int32_t* offsets,
+                                const int32_t* cu_q, const int32_t* cu_k, KvMap kv, int batch,
+                                int G, int Hq, int top_k, int nb_max, const int32_t* offsets,
                                 const int32_t* entries, int r0, int r1, int total_q,
                                 float scale_log2, float* part_acc, float2* part_ml, hipStream_t st) {
   if (D == 64)
-    return launch_attend_d<64>(hpg, q, k, v, cu_q, cu_k, batch, G, Hq, top_k, nb_max, offsets,
+    return launch_attend_d<64>(hpg, q, k, v, cu_q, cu_k, kv, batch, G, Hq, top_k, nb_max, offsets,
                                entries, r0, r1, total_q, scale_log2, part_acc, part_ml, st);
   if (D == 128)
-    return launch_attend_d<128>(hpg, q, k, v, cu_q, cu_k, batch, G, Hq, top_k, nb_max, offsets,
+    return launch_attend_d<128>(hpg, q, k, v, cu_q, cu_k, kv, batch, G, Hq, top_k, nb_max, offsets,
                                 entries, r0, r1, total_q, scale_log2, part_acc, part_ml, st);
   return hipErrorInvalidValue;
 }

@@ -19,8 +19,8 @@ constexpr int kDecodeWaves = 4;
 template <int D, int HPG>
 __global__ __launch_bounds__(kDecodeWaves * 64) void attend_decode_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
-    const int32_t* __restrict__ cu_q, const int32_t* __restrict__ cu_k, int batch, int G, int Hq,
-    int top_k, const int32_t* __restrict__ sel, int r0, float scale_log2,
+    const int32_t* __restrict__ cu_q, const int32_t* __restrict__ cu_k, KvMap kv, int batch, int G,
+    int Hq, int top_k, const int32_t* __restrict__ sel, int r0, float scale_log2,
     float* __restrict__ part_acc, float2* __restrict__ part_ml) {
   constexpr int KS = D / 16;      // k-steps of Q.K over the head dim
   constexpr int DT = D / 32;      // 32-row tiles of O^T
@@ -41,12 +41,13 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void attend_decode_kernel(
   const int kb = beta * kBlock;
   const bool active = beta >= 0 && kb < rp.lk;
   const int kb_safe = active ? kb : 0;
+  const size_t row0 = kv.block_row(rp.b, rp.koff, kb_safe >> 7);   // first cache row of the block
 
   // V^T of the block into this wave's LDS tile (keys past the sequence are zero)
   for (int c = lane; c < kBlock * D / 8; c += 64) {
     const int key = c % kBlock, dc = c / kBlock;
     const bool in = active && kb_safe + key < rp.lk;
-    const size_t row = (size_t)(rp.koff + (in ? kb_safe + key : 0)) * G + g;
+    const size_t row = (row0 + (in ? key : 0)) * G + g;
     uint4 vv = *reinterpret_cast<const uint4*>(v + row * D + dc * 8);
     vv = in ? vv : make_uint4(0, 0, 0, 0);
     const uint32_t vw[4] = {vv.x, vv.y, vv.z, vv.w};
@@ -73,7 +74,7 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void attend_decode_kernel(
   for (int kt = 0; kt < 4; ++kt) {
     const int key = kb_safe + kt * 32 + col;
     const bool in = active && key < rp.lk;
-    const uint16_t* ks_ptr = k + ((size_t)(rp.koff + (in ? key : 0)) * G + g) * D + half * 8;
+    const uint16_t* ks_ptr = k + ((row0 + (in ? key - kb_safe : 0)) * G + g) * D + half * 8;
     bf16x8 a[KS];
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
@@ -153,21 +154,22 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void attend_decode_kernel(
 
 template <int D, int HPG>
 static void launch_decode_t(const void* q, const void* k, const void* v, const int32_t* cu_q,
-                            const int32_t* cu_k, int batch, int G, int Hq, int top_k,
+                            const int32_t* cu_k, KvMap kv, int batch, int G, int Hq, int top_k,
                             const int32_t* sel, int r0, int r1, float scale_log2, float* part_acc,
                             float2* part_ml, hipStream_t st) {
   dim3 grid(r1 - r0, (top_k + kDecodeWaves - 1) / kDecodeWaves, G);
   hipLaunchKernelGGL((attend_decode_kernel<D, HPG>), grid, dim3(kDecodeWaves * 64), 0, st,
-                     (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, cu_q, cu_k, batch,
+                     (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, cu_q, cu_k, kv, batch,
                      G, Hq, top_k, sel, r0, scale_log2, part_acc, part_ml);
 }
 
 template <int D>
 static hipError_t launch_decode_d(int hpg, const void* q, const void* k, const void* v,
-                                  const int32_t* cu_q, const int32_t* cu_k, int batch, int G, int Hq,
+                                  const int32_t* cu_q, const int32_t* cu_k, KvMap kv, int batch,
+                                  int G, int Hq,
                                   int top_k, const int32_t* sel, int r0, int r1, float scale_log2,
                                   float* part_acc, float2* part_ml, hipStream_t st) {
-#define MSA_DEC(H) launch_decode_t<D, H>(q, k, v, cu_q, cu_k, batch, G, Hq, top_k, sel, r0, r1, scale_log2, part_acc, part_ml, st)
+#define MSA_DEC(H) launch_decode_t<D, H>(q, k, v, cu_q, cu_k, kv, batch, G, Hq, top_k, sel, r0, r1, scale_log2, part_acc, part_ml, st)
   switch (hpg) {
     case 1: MSA_DEC(1); break;
     case 2: MSA_DEC(2); break;
@@ -182,14 +184,15 @@ static hipError_t launch_decode_d(int hpg, const void* q, const void* k, const v
 }
 
 hipError_t launch_attend_decode(int D, int hpg, const void* q, const void* k, const void* v,
-                                const int32_t* cu_q, const int32_t* cu_k, int batch, int G, int Hq,
-                                int top_k, const int32_t* sel, int r0, int r1, float scale_log2,
-                                float* part_acc, float2* part_ml, hipStream_t st) {
+                                const int32_t* cu_q, const int32_t* cu_k, KvMap kv, int batch,
+                                int G, int Hq, int top_k, const int32_t* sel, int r0, int r1,
+                                float scale_log2, float* part_acc, float2* part_ml,
+                                hipStream_t st) {
   if (D == 64)
-    return launch_decode_d<64>(hpg, q, k, v, cu_q, cu_k, batch, G, Hq, top_k, sel, r0, r1,
+    return launch_decode_d<64>(hpg, q, k, v, cu_q, cu_k, kv, batch, G, Hq, top_k, sel, r0, r1,
                                scale_log2, part_acc, part_ml, st);
   if (D == 128)
-    return launch_decode_d<128>(hpg, q, k, v, cu_q, cu_k, batch, G, Hq, top_k, sel, r0, r1,
+    return launch_decode_d<128>(hpg, q, k, v, cu_q, cu_k, kv, batch, G, Hq, top_k, sel, r0, r1,
                                 scale_log2, part_acc, part_ml, st);
   return hipErrorInvalidValue;
 }

@@ -106,7 +106,7 @@ __global__ __launch_bounds__(256) void quantize_q_kernel(const uint16_t* __restr
 // block's keys that belong to the sequence; blocks past its end get 127.
 template <int DI>
 __global__ __launch_bounds__(256) void quantize_k_kernel(const uint16_t* __restrict__ k,
-                                                         const int32_t* __restrict__ cu_k,
+                                                         const int32_t* __restrict__ cu_k, KvMap kv,
                                                          int nb_max, uint8_t* __restrict__ k8,
                                                          uint8_t* __restrict__ ke) {
   constexpr int LPR = DI / 8;                      // 16-byte bf16 chunks per key row
@@ -116,11 +116,12 @@ __global__ __launch_bounds__(256) void quantize_k_kernel(const uint16_t* __restr
   const int koff = cu_k[b], lk = cu_k[b + 1] - koff;
   const int n = min(kBlock, lk - beta * kBlock);   // keys of this block in the sequence
   const int tid = threadIdx.x;
-  if (n <= 0) {
-    if (tid == 0) ke[(size_t)b * nb_max + beta] = 127;
+  if (n <= 0) {   // past the sequence: a contiguous cache keeps the neutral exponent
+    if (tid == 0 && !kv.table) ke[(size_t)b * nb_max + beta] = 127;
     return;
   }
-  const uint16_t* src = k + ((size_t)koff + (size_t)beta * kBlock) * DI;
+  const size_t row0 = kv.block_row(b, koff, beta);
+  const uint16_t* src = k + row0 * DI;
   float x[PER][8];
   float a = 0.f;
 #pragma unroll
@@ -138,14 +139,14 @@ __global__ __launch_bounds__(256) void quantize_k_kernel(const uint16_t* __restr
   __syncthreads();
   a = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
   const int e = fp8_scale_exponent(a);
-  uint8_t* dst = k8 + ((size_t)koff + (size_t)beta * kBlock) * DI;
+  uint8_t* dst = k8 + row0 * DI;
 #pragma unroll
   for (int i = 0; i < PER; ++i) {
     const int c = tid + i * 256, row = c / LPR, col = c % LPR;
     const uint2 w = quantize8(x[i], e);
     if (row < n) *reinterpret_cast<uint2*>(dst + (size_t)row * DI + col * 8) = w;
   }
-  if (tid == 0) ke[(size_t)b * nb_max + beta] = (uint8_t)(e + 127);
+  if (tid == 0) ke[kv.block_index(b, beta, nb_max)] = (uint8_t)(e + 127);
 }
 
 // ---------------------------------------------------------------------------
@@ -171,7 +172,8 @@ struct KRing8 {
   static constexpr int LOADERS = INSTR >= NW ? NW : INSTR;       // waves that load
   static_assert(INSTR < NW || INSTR % NW == 0, "block must split evenly over the waves");
 
-  __device__ static inline void load(const uint8_t* __restrict__ kbase, int blk, uint8_t* buf,
+  // issue this wave's loads of the key block whose first row is `blk_base` into `buf`
+  __device__ static inline void load(const uint8_t* __restrict__ blk_base, uint8_t* buf,
                                      int wave, int lane) {
     if (wave >= LOADERS) return;
 #pragma unroll
@@ -179,7 +181,7 @@ struct KRing8 {
       const int piece = wave * PER_WAVE + i;
       const int m = piece * ROWS_PER_INSTR + lane / CPR;
       const int lc = (lane % CPR) ^ swz(m);
-      const uint8_t* src = kbase + ((size_t)blk * kBlock + m) * DI + lc * 16;
+      const uint8_t* src = blk_base + (size_t)m * DI + lc * 16;
       __builtin_amdgcn_global_load_lds(src, buf + piece * 1024, 16, 0, 0);
     }
   }
@@ -204,7 +206,7 @@ template <int DI, int RT, int NW, int KCAP>
 __global__ __launch_bounds__(NW * 64, 2) void index_select_prefill_fp8_kernel(
     const uint8_t* __restrict__ q8, const uint8_t* __restrict__ qe, const uint8_t* __restrict__ k8,
     const uint8_t* __restrict__ ke, const int32_t* __restrict__ cu_q,
-    const int32_t* __restrict__ cu_k, int G, int nb_max, int qt, int top_k,
+    const int32_t* __restrict__ cu_k, KvMap kv, int G, int nb_max, int qt, int top_k,
     int32_t* __restrict__ sel, float* __restrict__ sel_score) {
   static_assert(RT == 1 || RT == 2, "a lane owns at most one row");
   using Ring = KRing8<DI, NW>;
@@ -242,7 +244,7 @@ __global__ __launch_bounds__(NW * 64, 2) void index_select_prefill_fp8_kernel(
 
   if (beta_hi > 0) {
     // the sequence's key-block exponents, staged once
-    for (int i = tid; i < beta_hi; i += NW * 64) kexp[i] = ke[(size_t)b * nb_max + i];
+    for (int i = tid; i < beta_hi; i += NW * 64) kexp[i] = ke[kv.block_index(b, i, nb_max)];
 
     i32x8 qf[RT][KS];
 #pragma unroll
@@ -264,11 +266,13 @@ __global__ __launch_bounds__(NW * 64, 2) void index_select_prefill_fp8_kernel(
     }
     __syncthreads();   // exponents visible; every earlier load has landed
 
-    const uint8_t* kbase = k8 + (size_t)koff * DI;
+    auto blk = [&](int beta) __attribute__((always_inline)) {
+      return k8 + kv.block_row(b, koff, beta) * DI;
+    };
     uint32_t pending = 0;   // previous block's score key, inserted during the next block's MFMAs
     int pending_beta = 0;
-    Ring::load(kbase, 0, ring0, wave, lane);
-    if (beta_hi > 1) Ring::load(kbase, 1, ring1, wave, lane);
+    Ring::load(blk(0), ring0, wave, lane);
+    if (beta_hi > 1) Ring::load(blk(1), ring1, wave, lane);
 
     auto step = [&](int beta, const uint8_t* rbuf, uint8_t* lbuf) __attribute__((always_inline)) {
       // this wave's pieces of block beta have landed (only beta+1 may be
@@ -279,7 +283,7 @@ __global__ __launch_bounds__(NW * 64, 2) void index_select_prefill_fp8_kernel(
       asm volatile("" ::: "memory");
       __builtin_amdgcn_s_barrier();
       asm volatile("" ::: "memory");
-      if (beta + 2 < beta_hi) Ring::load(kbase, beta + 2, lbuf, wave, lane);
+      if (beta + 2 < beta_hi) Ring::load(blk(beta + 2), lbuf, wave, lane);
 
       // software pipeline: the MFMAs of key tile kt+1 are issued before the
       // row maxima of tile kt are taken, and the previous block's top-k
@@ -372,8 +376,8 @@ template <int DI, int SEG, int RT>
 __global__ __launch_bounds__(256) void index_score_decode_fp8_kernel(
     const uint8_t* __restrict__ q8, const uint8_t* __restrict__ qe, const uint8_t* __restrict__ k8,
     const uint8_t* __restrict__ ke, const int32_t* __restrict__ cu_q,
-    const int32_t* __restrict__ cu_k, int G, int nb_max, int r0, int r1, float* __restrict__ S,
-    long long ld) {
+    const int32_t* __restrict__ cu_k, KvMap kv, int G, int nb_max, int r0, int r1,
+    float* __restrict__ S, long long ld) {
   constexpr int NT = 256;
   constexpr int KS = DI >= 64 ? DI / 64 : 1;
   constexpr int LD = KTileStage8<DI, NT>::kLd;
@@ -419,9 +423,8 @@ __global__ __launch_bounds__(256) void index_score_decode_fp8_kernel(
     }
   }
 
-  const uint8_t* kbase = k8 + (size_t)koff * DI;
   KTileStage8<DI, NT> stage;
-  stage.load(kbase + (size_t)b0 * kBlock * DI, tid);
+  stage.load(k8 + kv.block_row(b, koff, b0) * DI, tid);
   stage.store(lds[0], tid);
   __syncthreads();
 
@@ -429,7 +432,7 @@ __global__ __launch_bounds__(256) void index_score_decode_fp8_kernel(
   auto finish = [&](int it, int blk) __attribute__((always_inline)) {
     if (wave != 0) return;
     const size_t srow = (size_t)(qa - r0) * G;
-    const int ek = (int)ke[(size_t)b * nb_max + blk] - 127;
+    const int ek = (int)ke[kv.block_index(b, blk, nb_max)] - 127;
 #pragma unroll
     for (int j = 0; j < (NR + 63) / 64; ++j) {
       const int n = j * 64 + lane;
@@ -444,7 +447,7 @@ __global__ __launch_bounds__(256) void index_score_decode_fp8_kernel(
 
   for (int beta = b0; beta < b1; ++beta) {
     const int it = beta - b0;
-    stage.load(kbase + (size_t)min(beta + 1, b1 - 1) * kBlock * DI, tid);
+    stage.load(k8 + kv.block_row(b, koff, min(beta + 1, b1 - 1)) * DI, tid);
     if (it > 0) finish(it - 1, beta - 1);
     const uint8_t* arow = lds[it & 1] + (wave * 32 + col) * LD;
     f32x16 acc[RT];
@@ -490,9 +493,9 @@ constexpr int kFp8DecodeSeg = 8;
 int fp8_max_blocks_per_sequence() { return kFp8ExpLds; }
 
 template <int DI>
-static hipError_t launch_quantize_di(const void* q, const void* k, const int32_t* cu_k, int batch,
-                                     int nb_max, long long q_rows, void* q8, uint8_t* qe, void* k8,
-                                     uint8_t* ke, hipStream_t st) {
+static hipError_t launch_quantize_di(const void* q, const void* k, const int32_t* cu_k, KvMap kv,
+                                     int batch, int nb_max, long long q_rows, void* q8, uint8_t* qe,
+                                     void* k8, uint8_t* ke, hipStream_t st) {
   if (q_rows > 0) {
     const long long threads = q_rows * (DI / 8);
     hipLaunchKernelGGL((quantize_q_kernel<DI>), dim3((unsigned)((threads + 255) / 256)), dim3(256),
@@ -500,17 +503,17 @@ static hipError_t launch_quantize_di(const void* q, const void* k, const int32_t
   }
   if (nb_max > 0)
     hipLaunchKernelGGL((quantize_k_kernel<DI>), dim3(nb_max, batch), dim3(256), 0, st,
-                       (const uint16_t*)k, cu_k, nb_max, (uint8_t*)k8, ke);
+                       (const uint16_t*)k, cu_k, kv, nb_max, (uint8_t*)k8, ke);
   return hipGetLastError();
 }
 
 hipError_t launch_quantize_index_fp8(int DI, const void* q, const void* k, const int32_t* cu_k,
-                                     int batch, int nb_max, long long q_rows, void* q8, uint8_t* qe,
-                                     void* k8, uint8_t* ke, hipStream_t st) {
+                                     KvMap kv, int batch, int nb_max, long long q_rows, void* q8,
+                                     uint8_t* qe, void* k8, uint8_t* ke, hipStream_t st) {
   switch (DI) {
-    case 32: return launch_quantize_di<32>(q, k, cu_k, batch, nb_max, q_rows, q8, qe, k8, ke, st);
-    case 64: return launch_quantize_di<64>(q, k, cu_k, batch, nb_max, q_rows, q8, qe, k8, ke, st);
-    case 128: return launch_quantize_di<128>(q, k, cu_k, batch, nb_max, q_rows, q8, qe, k8, ke, st);
+    case 32: return launch_quantize_di<32>(q, k, cu_k, kv, batch, nb_max, q_rows, q8, qe, k8, ke, st);
+    case 64: return launch_quantize_di<64>(q, k, cu_k, kv, batch, nb_max, q_rows, q8, qe, k8, ke, st);
+    case 128: return launch_quantize_di<128>(q, k, cu_k, kv, batch, nb_max, q_rows, q8, qe, k8, ke, st);
   }
   return hipErrorInvalidValue;
 }
@@ -518,24 +521,24 @@ hipError_t launch_quantize_index_fp8(int DI, const void* q, const void* k, const
 template <int DI, int KCAP>
 static hipError_t launch_prefill8_t(const void* q8, const uint8_t* qe, const void* k8,
                                     const uint8_t* ke, const int32_t* cu_q, const int32_t* cu_k,
-                                    int batch, int G, int nb_max, int max_q_len, int top_k,
+                                    KvMap kv, int batch, int G, int nb_max, int max_q_len, int top_k,
                                     int32_t* sel, float* sel_score, hipStream_t st) {
   const int qt = kFp8Rows / G;
   if (qt < 1) return hipErrorInvalidValue;
   dim3 grid((max_q_len + qt - 1) / qt, batch);
   hipLaunchKernelGGL((index_select_prefill_fp8_kernel<DI, kFp8RT, kFp8NW, KCAP>), grid,
                      dim3(kFp8NW * 64), 0, st, (const uint8_t*)q8, qe, (const uint8_t*)k8, ke, cu_q,
-                     cu_k, G, nb_max, qt, top_k, sel, sel_score);
+                     cu_k, kv, G, nb_max, qt, top_k, sel, sel_score);
   return hipGetLastError();
 }
 
 template <int DI>
 static hipError_t launch_prefill8_di(const void* q8, const uint8_t* qe, const void* k8,
                                      const uint8_t* ke, const int32_t* cu_q, const int32_t* cu_k,
-                                     int batch, int G, int nb_max, int max_q_len, int top_k,
-                                     int32_t* sel, float* sel_score, hipStream_t st) {
+                                     KvMap kv, int batch, int G, int nb_max, int max_q_len,
+                                     int top_k, int32_t* sel, float* sel_score, hipStream_t st) {
   const int km = top_k - 1;
-#define MSA_PF8(K) launch_prefill8_t<DI, K>(q8, qe, k8, ke, cu_q, cu_k, batch, G, nb_max, max_q_len, top_k, sel, sel_score, st)
+#define MSA_PF8(K) launch_prefill8_t<DI, K>(q8, qe, k8, ke, cu_q, cu_k, kv, batch, G, nb_max, max_q_len, top_k, sel, sel_score, st)
   if (km <= 1) return MSA_PF8(1);
   if (km <= 2) return MSA_PF8(2);
   if (km <= 4) return MSA_PF8(4);
@@ -547,13 +550,13 @@ static hipError_t launch_prefill8_di(const void* q8, const uint8_t* qe, const vo
 
 hipError_t launch_index_select_prefill_fp8(const void* q8, const uint8_t* qe, const void* k8,
                                            const uint8_t* ke, const int32_t* cu_q,
-                                           const int32_t* cu_k, int batch, int G, int DI,
+                                           const int32_t* cu_k, KvMap kv, int batch, int G, int DI,
                                            int nb_max, int max_q_len, int top_k, int32_t* sel,
                                            float* sel_score, hipStream_t st) {
   switch (DI) {
-    case 32: return launch_prefill8_di<32>(q8, qe, k8, ke, cu_q, cu_k, batch, G, nb_max, max_q_len, top_k, sel, sel_score, st);
-    case 64: return launch_prefill8_di<64>(q8, qe, k8, ke, cu_q, cu_k, batch, G, nb_max, max_q_len, top_k, sel, sel_score, st);
-    case 128: return launch_prefill8_di<128>(q8, qe, k8, ke, cu_q, cu_k, batch, G, nb_max, max_q_len, top_k, sel, sel_score, st);
+    case 32: return launch_prefill8_di<32>(q8, qe, k8, ke, cu_q, cu_k, kv, batch, G, nb_max, max_q_len, top_k, sel, sel_score, st);
+    case 64: return launch_prefill8_di<64>(q8, qe, k8, ke, cu_q, cu_k, kv, batch, G, nb_max, max_q_len, top_k, sel, sel_score, st);
+    case 128: return launch_prefill8_di<128>(q8, qe, k8, ke, cu_q, cu_k, kv, batch, G, nb_max, max_q_len, top_k, sel, sel_score, st);
   }
   return hipErrorInvalidValue;
 }
@@ -561,10 +564,10 @@ hipError_t launch_index_select_prefill_fp8(const void* q8, const uint8_t* qe, co
 template <int DI>
 static hipError_t launch_decode8_di(const void* q8, const uint8_t* qe, const void* k8,
                                     const uint8_t* ke, const int32_t* cu_q, const int32_t* cu_k,
-                                    int batch, int G, int nb_max, int rows, int r0, int r1,
+                                    KvMap kv, int batch, int G, int nb_max, int rows, int r0, int r1,
                                     float* S, long long ld, hipStream_t st) {
   dim3 grid((nb_max + kFp8DecodeSeg - 1) / kFp8DecodeSeg, batch);
-#define MSA_DEC8(RT) hipLaunchKernelGGL((index_score_decode_fp8_kernel<DI, kFp8DecodeSeg, RT>), grid, dim3(256), 0, st, (const uint8_t*)q8, qe, (const uint8_t*)k8, ke, cu_q, cu_k, G, nb_max, r0, r1, S, ld)
+#define MSA_DEC8(RT) hipLaunchKernelGGL((index_score_decode_fp8_kernel<DI, kFp8DecodeSeg, RT>), grid, dim3(256), 0, st, (const uint8_t*)q8, qe, (const uint8_t*)k8, ke, cu_q, cu_k, kv, G, nb_max, r0, r1, S, ld)
   if (rows <= 32) MSA_DEC8(1);
   else if (rows <= 64) MSA_DEC8(2);
   else if (rows <= 128) MSA_DEC8(4);
@@ -575,13 +578,13 @@ static hipError_t launch_decode8_di(const void* q8, const uint8_t* qe, const voi
 
 hipError_t launch_index_score_decode_fp8(const void* q8, const uint8_t* qe, const void* k8,
                                          const uint8_t* ke, const int32_t* cu_q,
-                                         const int32_t* cu_k, int batch, int G, int DI, int nb_max,
-                                         int rows, int r0, int r1, float* S, long long ld,
-                                         hipStream_t st) {
+                                         const int32_t* cu_k, KvMap kv, int batch, int G, int DI,
+                                         int nb_max, int rows, int r0, int r1, float* S,
+                                         long long ld, hipStream_t st) {
   switch (DI) {
-    case 32: return launch_decode8_di<32>(q8, qe, k8, ke, cu_q, cu_k, batch, G, nb_max, rows, r0, r1, S, ld, st);
-    case 64: return launch_decode8_di<64>(q8, qe, k8, ke, cu_q, cu_k, batch, G, nb_max, rows, r0, r1, S, ld, st);
-    case 128: return launch_decode8_di<128>(q8, qe, k8, ke, cu_q, cu_k, batch, G, nb_max, rows, r0, r1, S, ld, st);
+    case 32: return launch_decode8_di<32>(q8, qe, k8, ke, cu_q, cu_k, kv, batch, G, nb_max, rows, r0, r1, S, ld, st);
+    case 64: return launch_decode8_di<64>(q8, qe, k8, ke, cu_q, cu_k, kv, batch, G, nb_max, rows, r0, r1, S, ld, st);
+    case 128: return launch_decode8_di<128>(q8, qe, k8, ke, cu_q, cu_k, kv, batch, G, nb_max, rows, r0, r1, S, ld, st);
   }
   return hipErrorInvalidValue;
 }

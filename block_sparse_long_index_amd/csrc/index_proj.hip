@@ -30,7 +30,7 @@ __device__ inline int proj_swz(int m) { return (m >> 2) & 3; }
 __global__ __launch_bounds__(kProjNW * 64, 2) void index_project_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ wq,
     const uint16_t* __restrict__ wk, int D, int GD, int F, int T, int n_ft, int n_tiles,
-    const int32_t* __restrict__ cu_q, const int32_t* __restrict__ cu_k, int batch, int DI,
+    const int32_t* __restrict__ cu_q, const int32_t* __restrict__ cu_k, KvMap kv, int batch, int DI,
     uint16_t* __restrict__ q_idx, uint16_t* __restrict__ k_idx) {
   __shared__ __attribute__((aligned(1024))) uint16_t a0[kProjBF * kProjBK];
   __shared__ __attribute__((aligned(1024))) uint16_t a1[kProjBF * kProjBK];
@@ -134,7 +134,7 @@ __global__ __launch_bounds__(kProjNW * 64, 2) void index_project_kernel(
     const int t = t0 + wave * 64 + j2 * 32 + col;
     if (t >= T) continue;
     const RowPos rp = locate_row(t, cu_q, cu_k, batch);
-    const size_t krow = (size_t)rp.koff + rp.p;
+    const size_t krow = kv.key_row(rp.b, rp.koff, rp.p);
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -161,7 +161,7 @@ constexpr int kProjSmallMaxT = 512;   // token counts up to this use the small k
 __global__ __launch_bounds__(kProjSmallWaves * 64) void index_project_small_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ wq,
     const uint16_t* __restrict__ wk, int D, int GD, int F, int T, int n_ft,
-    const int32_t* __restrict__ cu_q, const int32_t* __restrict__ cu_k, int batch, int DI,
+    const int32_t* __restrict__ cu_q, const int32_t* __restrict__ cu_k, KvMap kv, int batch, int DI,
     uint16_t* __restrict__ q_idx, uint16_t* __restrict__ k_idx) {
   __shared__ float part[kProjSmallWaves][16][64];
   const int ft = blockIdx.x % n_ft, tt = blockIdx.x / n_ft;
@@ -197,7 +197,7 @@ __global__ __launch_bounds__(kProjSmallWaves * 64) void index_project_small_kern
   const int tok = t0 + col;
   if (tok >= T) return;
   const RowPos rp = locate_row(tok, cu_q, cu_k, batch);
-  const size_t krow = (size_t)rp.koff + rp.p;
+  const size_t krow = kv.key_row(rp.b, rp.koff, rp.p);
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int ff = f0 + 8 * j + 4 * half;
@@ -210,15 +210,15 @@ __global__ __launch_bounds__(kProjSmallWaves * 64) void index_project_small_kern
 }
 
 hipError_t launch_index_project(const void* x, const void* wq, const void* wk, int D, int G, int DI,
-                                int T, const int32_t* cu_q, const int32_t* cu_k, int batch,
-                                void* q_idx, void* k_idx, hipStream_t st) {
+                                int T, const int32_t* cu_q, const int32_t* cu_k, KvMap kv,
+                                int batch, void* q_idx, void* k_idx, hipStream_t st) {
   const int GD = G * DI, F = GD + DI;
   if (T <= kProjSmallMaxT) {
     const int n_ft = (F + 31) / 32, n_tt = (T + 31) / 32;
     if (T <= 0) return hipSuccess;
     hipLaunchKernelGGL(index_project_small_kernel, dim3(n_ft * n_tt), dim3(kProjSmallWaves * 64), 0,
                        st, (const uint16_t*)x, (const uint16_t*)wq, (const uint16_t*)wk, D, GD, F, T,
-                       n_ft, cu_q, cu_k, batch, DI, (uint16_t*)q_idx, (uint16_t*)k_idx);
+                       n_ft, cu_q, cu_k, kv, batch, DI, (uint16_t*)q_idx, (uint16_t*)k_idx);
     return hipGetLastError();
   }
   const int n_ft = (F + kProjBF - 1) / kProjBF;
@@ -228,7 +228,8 @@ hipError_t launch_index_project(const void* x, const void* wq, const void* wk, i
   if (n_tiles >= (1ll << 31)) return hipErrorInvalidValue;
   hipLaunchKernelGGL(index_project_kernel, dim3((unsigned)n_tiles), dim3(kProjNW * 64), 0, st,
                      (const uint16_t*)x, (const uint16_t*)wq, (const uint16_t*)wk, D, GD, F, T,
-                     n_ft, (int)n_tiles, cu_q, cu_k, batch, DI, (uint16_t*)q_idx, (uint16_t*)k_idx);
+                     n_ft, (int)n_tiles, cu_q, cu_k, kv, batch, DI, (uint16_t*)q_idx,
+                     (uint16_t*)k_idx);
   return hipGetLastError();
 }
 

@@ -83,15 +83,15 @@ struct KRing {
   static constexpr int PER_WAVE = INSTR / NW;          // loads per wave per block
   static_assert(INSTR % NW == 0, "block must split evenly over the waves");
 
-  // issue this wave's loads of key block `blk` (rows of `kbase`) into `buf`
-  __device__ static inline void load(const uint16_t* __restrict__ kbase, int blk, uint16_t* buf,
+  // issue this wave's loads of the key block whose first row is `blk_base` into `buf`
+  __device__ static inline void load(const uint16_t* __restrict__ blk_base, uint16_t* buf,
                                      int wave, int lane) {
 #pragma unroll
     for (int i = 0; i < PER_WAVE; ++i) {
       const int piece = wave * PER_WAVE + i;
       const int m = piece * ROWS_PER_INSTR + lane / CPR;
       const int lc = (lane % CPR) ^ swz(m);
-      const uint16_t* src = kbase + ((size_t)blk * kBlock + m) * DI + lc * 8;
+      const uint16_t* src = blk_base + (size_t)m * DI + lc * 8;
       __builtin_amdgcn_global_load_lds(src, buf + piece * 512, 16, 0, 0);
     }
   }
@@ -105,8 +105,8 @@ struct KRing {
 template <int DI, int RT, int NW, int KCAP>
 __global__ __launch_bounds__(NW * 64) void index_select_prefill_kernel(
     const uint16_t* __restrict__ q_idx, const uint16_t* __restrict__ k_idx,
-    const int32_t* __restrict__ cu_q, const int32_t* __restrict__ cu_k, int G, int qt, int top_k,
-    int32_t* __restrict__ sel, float* __restrict__ sel_score) {
+    const int32_t* __restrict__ cu_q, const int32_t* __restrict__ cu_k, KvMap kv, int G, int qt,
+    int top_k, int32_t* __restrict__ sel, float* __restrict__ sel_score) {
   static_assert(RT == 1 || RT == 2, "a lane owns at most one row");
   using Ring = KRing<DI, NW>;
   constexpr int KS = DI / 16;          // MFMA k-steps over the index dim
@@ -159,11 +159,13 @@ __global__ __launch_bounds__(NW * 64) void index_select_prefill_kernel(
       }
     }
 
-    const uint16_t* kbase = k_idx + (size_t)koff * DI;
+    auto blk = [&](int beta) __attribute__((always_inline)) {
+      return k_idx + kv.block_row(b, koff, beta) * DI;
+    };
     uint32_t pending = 0;   // previous block's score key, inserted during the next block's MFMAs
     int pending_beta = 0;
-    Ring::load(kbase, 0, ring0, wave, lane);
-    if (beta_hi > 1) Ring::load(kbase, 1, ring1, wave, lane);
+    Ring::load(blk(0), ring0, wave, lane);
+    if (beta_hi > 1) Ring::load(blk(1), ring1, wave, lane);
 
     // score block beta from `rbuf`; first start loading block beta+2 into `lbuf`
     auto step = [&](int beta, const uint16_t* rbuf, uint16_t* lbuf) __attribute__((always_inline)) {
@@ -176,7 +178,7 @@ __global__ __launch_bounds__(NW * 64) void index_select_prefill_kernel(
       asm volatile("" ::: "memory");
       __builtin_amdgcn_s_barrier();
       asm volatile("" ::: "memory");
-      if (beta + 2 < beta_hi) Ring::load(kbase, beta + 2, lbuf, wave, lane);
+      if (beta + 2 < beta_hi) Ring::load(blk(beta + 2), lbuf, wave, lane);
 
       // the previous block's top-k insert runs while this block's first
       // fragments load
@@ -230,8 +232,8 @@ __global__ __launch_bounds__(NW * 64) void index_select_prefill_kernel(
 template <int DI, int SEG, int RT>
 __global__ __launch_bounds__(256) void index_score_decode_kernel(
     const uint16_t* __restrict__ q_idx, const uint16_t* __restrict__ k_idx,
-    const int32_t* __restrict__ cu_q, const int32_t* __restrict__ cu_k, int G, int r0, int r1,
-    float* __restrict__ S, long long ld) {
+    const int32_t* __restrict__ cu_q, const int32_t* __restrict__ cu_k, KvMap kv, int G, int r0,
+    int r1, float* __restrict__ S, long long ld) {
   constexpr int NT = 256;
   constexpr int KS = DI / 16;
   constexpr int LD = DI + 8;
@@ -271,9 +273,8 @@ __global__ __launch_bounds__(256) void index_score_decode_kernel(
     }
   }
 
-  const uint16_t* kbase = k_idx + (size_t)koff * DI;
   KTileStage<DI, NT> stage;
-  stage.load(kbase + (size_t)b0 * kBlock * DI, tid);
+  stage.load(k_idx + kv.block_row(b, koff, b0) * DI, tid);
   stage.store(lds[0], tid);
   __syncthreads();
 
@@ -294,7 +295,7 @@ __global__ __launch_bounds__(256) void index_score_decode_kernel(
 
   for (int beta = b0; beta < b1; ++beta) {
     const int it = beta - b0;
-    stage.load(kbase + (size_t)min(beta + 1, b1 - 1) * kBlock * DI, tid);
+    stage.load(k_idx + kv.block_row(b, koff, min(beta + 1, b1 - 1)) * DI, tid);
     // finish the previous block's reduction (its partial maxima are complete)
     if (it > 0) finish(it - 1, beta - 1);
     const uint16_t* kt_lds = lds[it & 1];
@@ -333,23 +334,23 @@ int prefill_rows_per_wg() { return kPrefillRows; }
 
 template <int DI, int KCAP>
 static hipError_t launch_prefill_t(const void* q_idx, const void* k_idx, const int32_t* cu_q,
-                                   const int32_t* cu_k, int batch, int G, int max_q_len, int top_k,
-                                   int32_t* sel, float* sel_score, hipStream_t st) {
+                                   const int32_t* cu_k, KvMap kv, int batch, int G, int max_q_len,
+                                   int top_k, int32_t* sel, float* sel_score, hipStream_t st) {
   const int qt = kPrefillRows / G;
   if (qt < 1) return hipErrorInvalidValue;
   dim3 grid((max_q_len + qt - 1) / qt, batch);
   hipLaunchKernelGGL((index_select_prefill_kernel<DI, kPrefillRT, kPrefillNW, KCAP>), grid,
                      dim3(kPrefillNW * 64), 0, st, (const uint16_t*)q_idx, (const uint16_t*)k_idx,
-                     cu_q, cu_k, G, qt, top_k, sel, sel_score);
+                     cu_q, cu_k, kv, G, qt, top_k, sel, sel_score);
   return hipGetLastError();
 }
 
 template <int DI>
 static hipError_t launch_prefill_di(const void* q_idx, const void* k_idx, const int32_t* cu_q,
-                                    const int32_t* cu_k, int batch, int G, int max_q_len, int top_k,
-                                    int32_t* sel, float* sel_score, hipStream_t st) {
+                                    const int32_t* cu_k, KvMap kv, int batch, int G, int max_q_len,
+                                    int top_k, int32_t* sel, float* sel_score, hipStream_t st) {
   const int km = top_k - 1;
-#define MSA_PF(K) launch_prefill_t<DI, K>(q_idx, k_idx, cu_q, cu_k, batch, G, max_q_len, top_k, sel, sel_score, st)
+#define MSA_PF(K) launch_prefill_t<DI, K>(q_idx, k_idx, cu_q, cu_k, kv, batch, G, max_q_len, top_k, sel, sel_score, st)
   if (km <= 1) return MSA_PF(1);
   if (km <= 2) return MSA_PF(2);
   if (km <= 4) return MSA_PF(4);
@@ -360,22 +361,23 @@ static hipError_t launch_prefill_di(const void* q_idx, const void* k_idx, const 
 }
 
 hipError_t launch_index_select_prefill(const void* q_idx, const void* k_idx, const int32_t* cu_q,
-                                       const int32_t* cu_k, int batch, int G, int DI, int max_q_len,
-                                       int top_k, int32_t* sel, float* sel_score, hipStream_t st) {
+                                       const int32_t* cu_k, KvMap kv, int batch, int G, int DI,
+                                       int max_q_len, int top_k, int32_t* sel, float* sel_score,
+                                       hipStream_t st) {
   switch (DI) {
-    case 32: return launch_prefill_di<32>(q_idx, k_idx, cu_q, cu_k, batch, G, max_q_len, top_k, sel, sel_score, st);
-    case 64: return launch_prefill_di<64>(q_idx, k_idx, cu_q, cu_k, batch, G, max_q_len, top_k, sel, sel_score, st);
-    case 128: return launch_prefill_di<128>(q_idx, k_idx, cu_q, cu_k, batch, G, max_q_len, top_k, sel, sel_score, st);
+    case 32: return launch_prefill_di<32>(q_idx, k_idx, cu_q, cu_k, kv, batch, G, max_q_len, top_k, sel, sel_score, st);
+    case 64: return launch_prefill_di<64>(q_idx, k_idx, cu_q, cu_k, kv, batch, G, max_q_len, top_k, sel, sel_score, st);
+    case 128: return launch_prefill_di<128>(q_idx, k_idx, cu_q, cu_k, kv, batch, G, max_q_len, top_k, sel, sel_score, st);
   }
   return hipErrorInvalidValue;
 }
 
 template <int DI>
 static hipError_t launch_decode_di(const void* q_idx, const void* k_idx, const int32_t* cu_q,
-                                   const int32_t* cu_k, int batch, int G, int nb_max, int rows,
-                                   int r0, int r1, float* S, long long ld, hipStream_t st) {
+                                   const int32_t* cu_k, KvMap kv, int batch, int G, int nb_max,
+                                   int rows, int r0, int r1, float* S, long long ld, hipStream_t st) {
   dim3 grid((nb_max + kDecodeSeg - 1) / kDecodeSeg, batch);
-#define MSA_DEC(RT) hipLaunchKernelGGL((index_score_decode_kernel<DI, kDecodeSeg, RT>), grid, dim3(256), 0, st, (const uint16_t*)q_idx, (const uint16_t*)k_idx, cu_q, cu_k, G, r0, r1, S, ld)
+#define MSA_DEC(RT) hipLaunchKernelGGL((index_score_decode_kernel<DI, kDecodeSeg, RT>), grid, dim3(256), 0, st, (const uint16_t*)q_idx, (const uint16_t*)k_idx, cu_q, cu_k, kv, G, r0, r1, S, ld)
   if (rows <= 32) MSA_DEC(1);
   else if (rows <= 64) MSA_DEC(2);
   else if (rows <= 128) MSA_DEC(4);
@@ -385,13 +387,13 @@ static hipError_t launch_decode_di(const void* q_idx, const void* k_idx, const i
 }
 
 hipError_t launch_index_score_decode(const void* q_idx, const void* k_idx, const int32_t* cu_q,
-                                     const int32_t* cu_k, int batch, int G, int DI, int nb_max,
-                                     int rows, int r0, int r1, float* S, long long ld,
+                                     const int32_t* cu_k, KvMap kv, int batch, int G, int DI,
+                                     int nb_max, int rows, int r0, int r1, float* S, long long ld,
                                      hipStream_t st) {
   switch (DI) {
-    case 32: return launch_decode_di<32>(q_idx, k_idx, cu_q, cu_k, batch, G, nb_max, rows, r0, r1, S, ld, st);
-    case 64: return launch_decode_di<64>(q_idx, k_idx, cu_q, cu_k, batch, G, nb_max, rows, r0, r1, S, ld, st);
-    case 128: return launch_decode_di<128>(q_idx, k_idx, cu_q, cu_k, batch, G, nb_max, rows, r0, r1, S, ld, st);
+    case 32: return launch_decode_di<32>(q_idx, k_idx, cu_q, cu_k, kv, batch, G, nb_max, rows, r0, r1, S, ld, st);
+    case 64: return launch_decode_di<64>(q_idx, k_idx, cu_q, cu_k, kv, batch, G, nb_max, rows, r0, r1, S, ld, st);
+    case 128: return launch_decode_di<128>(q_idx, k_idx, cu_q, cu_k, kv, batch, G, nb_max, rows, r0, r1, S, ld, st);
   }
   return hipErrorInvalidValue;
 }

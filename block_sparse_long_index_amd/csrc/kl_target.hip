@@ -105,7 +105,7 @@ hipError_t launch_block_mass(int hpg, const float2* part_ml, const int32_t* sel,
 template <int DI, int KMAX>
 __global__ __launch_bounds__(256) void index_kl_kernel(
     const uint16_t* __restrict__ q_idx, const uint16_t* __restrict__ k_idx,
-    const int32_t* __restrict__ cu_q, const int32_t* __restrict__ cu_k, int G, int top_k,
+    const int32_t* __restrict__ cu_q, const int32_t* __restrict__ cu_k, KvMap kv, int G, int top_k,
     const int32_t* __restrict__ sel, const float* __restrict__ sel_score,
     const float* __restrict__ mass, float* __restrict__ log_q, float* __restrict__ kl) {
   constexpr int KS = DI / 16;
@@ -124,11 +124,12 @@ __global__ __launch_bounds__(256) void index_kl_kernel(
   const int tid = threadIdx.x;
 
   // the block's keys (rows past the sequence are zero and masked below)
+  const size_t row0 = kv.block_row(b, koff, beta);
   for (int c = tid; c < kBlock * DI / 8; c += 256) {
     const int row = c / (DI / 8), cc = c % (DI / 8);
     const int key = beta * kBlock + row;
     uint4 v = make_uint4(0, 0, 0, 0);
-    if (key < lk) v = *reinterpret_cast<const uint4*>(k_idx + ((size_t)koff + key) * DI + cc * 8);
+    if (key < lk) v = *reinterpret_cast<const uint4*>(k_idx + (row0 + row) * DI + cc * 8);
     *reinterpret_cast<uint4*>(kt + row * LD + cc * 8) = v;
   }
   __syncthreads();
@@ -203,12 +204,13 @@ __global__ __launch_bounds__(256) void index_kl_kernel(
 
 template <int DI>
 static hipError_t launch_kl_di(const void* q_idx, const void* k_idx, const int32_t* cu_q,
-                               const int32_t* cu_k, int batch, int G, int top_k, int max_q_len,
+                               const int32_t* cu_k, KvMap kv, int batch, int G, int top_k,
+                               int max_q_len,
                                const int32_t* sel, const float* sel_score, const float* mass,
                                float* log_q, float* kl, hipStream_t st) {
   // a sequence's queries span at most ceil(Lq / 128) + 1 blocks
   dim3 grid((max_q_len + kBlock - 1) / kBlock + 1, batch);
-#define MSA_KL(K) hipLaunchKernelGGL((index_kl_kernel<DI, K>), grid, dim3(256), 0, st, (const uint16_t*)q_idx, (const uint16_t*)k_idx, cu_q, cu_k, G, top_k, sel, sel_score, mass, log_q, kl)
+#define MSA_KL(K) hipLaunchKernelGGL((index_kl_kernel<DI, K>), grid, dim3(256), 0, st, (const uint16_t*)q_idx, (const uint16_t*)k_idx, cu_q, cu_k, kv, G, top_k, sel, sel_score, mass, log_q, kl)
   if (top_k <= 4) MSA_KL(4);
   else if (top_k <= 8) MSA_KL(8);
   else if (top_k <= 16) MSA_KL(16);
@@ -218,13 +220,13 @@ static hipError_t launch_kl_di(const void* q_idx, const void* k_idx, const int32
 }
 
 hipError_t launch_index_kl(int DI, const void* q_idx, const void* k_idx, const int32_t* cu_q,
-                           const int32_t* cu_k, int batch, int G, int top_k, int max_q_len,
-                           const int32_t* sel, const float* sel_score, const float* mass,
-                           float* log_q, float* kl, hipStream_t st) {
+                           const int32_t* cu_k, KvMap kv, int batch, int G, int top_k,
+                           int max_q_len, const int32_t* sel, const float* sel_score,
+                           const float* mass, float* log_q, float* kl, hipStream_t st) {
   switch (DI) {
-    case 32: return launch_kl_di<32>(q_idx, k_idx, cu_q, cu_k, batch, G, top_k, max_q_len, sel, sel_score, mass, log_q, kl, st);
-    case 64: return launch_kl_di<64>(q_idx, k_idx, cu_q, cu_k, batch, G, top_k, max_q_len, sel, sel_score, mass, log_q, kl, st);
-    case 128: return launch_kl_di<128>(q_idx, k_idx, cu_q, cu_k, batch, G, top_k, max_q_len, sel, sel_score, mass, log_q, kl, st);
+    case 32: return launch_kl_di<32>(q_idx, k_idx, cu_q, cu_k, kv, batch, G, top_k, max_q_len, sel, sel_score, mass, log_q, kl, st);
+    case 64: return launch_kl_di<64>(q_idx, k_idx, cu_q, cu_k, kv, batch, G, top_k, max_q_len, sel, sel_score, mass, log_q, kl, st);
+    case 128: return launch_kl_di<128>(q_idx, k_idx, cu_q, cu_k, kv, batch, G, top_k, max_q_len, sel, sel_score, mass, log_q, kl, st);
   }
   return hipErrorInvalidValue;
 }

@@ -14,10 +14,11 @@
 #include "msa_common.h"
 
 namespace msa {
-hipError_t launch_index_select_prefill(const void*, const void*, const int32_t*, const int32_t*, int,
-                                       int, int, int, int, int32_t*, float*, hipStream_t);
-hipError_t launch_index_score_decode(const void*, const void*, const int32_t*, const int32_t*, int,
-                                     int, int, int, int, int, int, float*, long long, hipStream_t);
+hipError_t launch_index_select_prefill(const void*, const void*, const int32_t*, const int32_t*,
+                                       KvMap, int, int, int, int, int, int32_t*, float*, hipStream_t);
+hipError_t launch_index_score_decode(const void*, const void*, const int32_t*, const int32_t*, KvMap,
+                                     int, int, int, int, int, int, int, float*, long long,
+                                     hipStream_t);
 hipError_t launch_topk_select(const float*, long long, int, int, const int32_t*, const int32_t*, int,
                               int, int, bool, int32_t*, float*, hipStream_t);
 size_t lists_workspace_bytes(int batch, int G, int nqt_max, int nb_max);
@@ -25,29 +26,30 @@ int list_tile_rows();
 hipError_t launch_build_lists(const int32_t*, const int32_t*, const int32_t*, int, int, int, int,
                               int, int32_t*, int32_t*, void*, hipStream_t);
 hipError_t launch_attend_blocks(int, int, const void*, const void*, const void*, const int32_t*,
-                                const int32_t*, int, int, int, int, int, const int32_t*,
+                                const int32_t*, KvMap, int, int, int, int, int, const int32_t*,
                                 const int32_t*, int, int, int, float, float*, float2*, hipStream_t);
 hipError_t launch_attend_decode(int, int, const void*, const void*, const void*, const int32_t*,
-                                const int32_t*, int, int, int, int, const int32_t*, int, int, float,
-                                float*, float2*, hipStream_t);
+                                const int32_t*, KvMap, int, int, int, int, const int32_t*, int, int,
+                                float, float*, float2*, hipStream_t);
 hipError_t launch_merge(int, const float*, const float2*, const int32_t*, int, int, int, int, int,
                         void*, float*, hipStream_t);
 int fp8_max_blocks_per_sequence();
 hipError_t launch_block_mass(int, const float2*, const int32_t*, int, int, int, int, float*,
                              hipStream_t);
-hipError_t launch_index_kl(int, const void*, const void*, const int32_t*, const int32_t*, int, int,
-                           int, int, const int32_t*, const float*, const float*, float*, float*,
-                           hipStream_t);
+hipError_t launch_index_kl(int, const void*, const void*, const int32_t*, const int32_t*, KvMap, int,
+                           int, int, int, const int32_t*, const float*, const float*, float*,
+                           float*, hipStream_t);
 hipError_t launch_index_project(const void*, const void*, const void*, int, int, int, int,
-                                const int32_t*, const int32_t*, int, void*, void*, hipStream_t);
-hipError_t launch_quantize_index_fp8(int, const void*, const void*, const int32_t*, int, int,
+                                const int32_t*, const int32_t*, KvMap, int, void*, void*,
+                                hipStream_t);
+hipError_t launch_quantize_index_fp8(int, const void*, const void*, const int32_t*, KvMap, int, int,
                                      long long, void*, uint8_t*, void*, uint8_t*, hipStream_t);
 hipError_t launch_index_select_prefill_fp8(const void*, const uint8_t*, const void*, const uint8_t*,
-                                           const int32_t*, const int32_t*, int, int, int, int, int,
-                                           int, int32_t*, float*, hipStream_t);
+                                           const int32_t*, const int32_t*, KvMap, int, int, int,
+                                           int, int, int, int32_t*, float*, hipStream_t);
 hipError_t launch_index_score_decode_fp8(const void*, const uint8_t*, const void*, const uint8_t*,
-                                         const int32_t*, const int32_t*, int, int, int, int, int,
-                                         int, int, float*, long long, hipStream_t);
+                                         const int32_t*, const int32_t*, KvMap, int, int, int, int,
+                                         int, int, int, float*, long long, hipStream_t);
 }  // namespace msa
 
 namespace {
@@ -72,6 +74,7 @@ struct Derived {
   bool decode_path;
   float scale;
   long long total_q;
+  msa::KvMap kv;   // where key rows live (contiguous or paged)
 };
 
 msa_status_t check_dims(const msa_dims_t* d, Derived* out) {
@@ -97,6 +100,18 @@ msa_status_t check_dims(const msa_dims_t* d, Derived* out) {
     return fail(MSA_ERR_BAD_DIMS, "max lengths exceed totals");
   if (d->q_chunk < 0) return fail(MSA_ERR_BAD_DIMS, "q_chunk must be >= 0");
   if (d->reserved != 0) return fail(MSA_ERR_BAD_DIMS, "reserved must be 0");
+  if (d->kv_pages < 0) return fail(MSA_ERR_BAD_DIMS, "kv_pages must be >= 0");
+  if (d->kv_pages > 0) {
+    if (!d->block_table) return fail(MSA_ERR_NULL_ARG, "block_table is NULL (paged key cache)");
+    if ((long long)d->max_blocks_per_seq * MSA_BLOCK_SIZE < d->max_k_len)
+      return fail(MSA_ERR_BAD_DIMS, "max_blocks_per_seq below ceil(max_k_len / 128)");
+    if ((long long)d->kv_pages * MSA_BLOCK_SIZE != d->total_k)
+      return fail(MSA_ERR_BAD_DIMS, "paged key cache: total_k must equal 128 * kv_pages");
+    if ((long long)d->batch * d->max_blocks_per_seq >= ((long long)1 << 31))
+      return fail(MSA_ERR_UNSUPPORTED, "block table too large");
+  } else if (d->block_table || d->max_blocks_per_seq) {
+    return fail(MSA_ERR_BAD_DIMS, "block_table / max_blocks_per_seq are for a paged cache (kv_pages > 0)");
+  }
   out->G = d->num_kv_heads;
   out->Hq = d->num_q_heads;
   out->D = d->head_dim;
@@ -113,6 +128,9 @@ msa_status_t check_dims(const msa_dims_t* d, Derived* out) {
   out->decode_path = (long long)d->max_q_len * out->G <= kDecodeRowsMax;
   out->scale = d->softmax_scale > 0.f ? d->softmax_scale : 1.f / sqrtf((float)d->head_dim);
   out->total_q = d->total_q;
+  out->kv.table = d->kv_pages > 0 ? d->block_table : nullptr;
+  out->kv.max_blocks = d->kv_pages > 0 ? d->max_blocks_per_seq : 0;
+  out->kv.pages = d->kv_pages;
   return MSA_OK;
 }
 
@@ -269,7 +287,7 @@ msa_status_t msa_index_select(const msa_dims_t* dims, const void* q_idx, const v
   hipStream_t st = (hipStream_t)stream;
   if (!x.decode_path) {
     ProfScope ps(K_INDEX_PREFILL, st);
-    hipError_t e = msa::launch_index_select_prefill(q_idx, k_idx, cu_seqlens_q, cu_seqlens_k,
+    hipError_t e = msa::launch_index_select_prefill(q_idx, k_idx, cu_seqlens_q, cu_seqlens_k, x.kv,
                                                     dims->batch, x.G, x.DI, dims->max_q_len,
                                                     x.top_k, sel, sel_score, st);
     return e == hipSuccess ? MSA_OK : hip_fail(e);
@@ -282,7 +300,7 @@ msa_status_t msa_index_select(const msa_dims_t* dims, const void* q_idx, const v
     hipError_t e;
     {
       ProfScope ps(K_INDEX_DECODE, st);
-      e = msa::launch_index_score_decode(q_idx, k_idx, cu_seqlens_q, cu_seqlens_k, dims->batch, x.G,
+      e = msa::launch_index_score_decode(q_idx, k_idx, cu_seqlens_q, cu_seqlens_k, x.kv, dims->batch, x.G,
                                          x.DI, x.nb_max, dims->max_q_len * x.G, a, z, S, ld, st);
     }
     if (e != hipSuccess) return hip_fail(e);
@@ -311,7 +329,8 @@ msa_status_t msa_index_project(const msa_dims_t* dims, int32_t model_dim, const 
   hipStream_t st = (hipStream_t)stream;
   ProfScope ps(K_PROJECT, st);
   hipError_t e = msa::launch_index_project(x, w_q, w_k, model_dim, x_.G, x_.DI, (int)x_.total_q,
-                                           cu_seqlens_q, cu_seqlens_k, dims->batch, q_idx, k_idx, st);
+                                           cu_seqlens_q, cu_seqlens_k, x_.kv, dims->batch, q_idx,
+                                           k_idx, st);
   return e == hipSuccess ? MSA_OK : hip_fail(e);
 }
 
@@ -332,7 +351,7 @@ msa_status_t msa_index_quantize_fp8(const msa_dims_t* dims, const void* q_idx, c
   if (!has_q && !has_k) return MSA_OK;
   hipStream_t st = (hipStream_t)stream;
   ProfScope ps(K_QUANT_FP8, st);
-  hipError_t e = msa::launch_quantize_index_fp8(x.DI, q_idx, k_idx, cu_seqlens_k, dims->batch,
+  hipError_t e = msa::launch_quantize_index_fp8(x.DI, q_idx, k_idx, cu_seqlens_k, x.kv, dims->batch,
                                                 has_k ? x.nb_max : 0,
                                                 has_q ? x.total_q * x.G : 0, q_idx8, q_exp, k_idx8,
                                                 k_exp, st);
@@ -361,7 +380,7 @@ msa_status_t msa_index_select_fp8(const msa_dims_t* dims, const void* q_idx8, co
   if (!x.decode_path) {
     ProfScope ps(K_INDEX_PREFILL_FP8, st);
     hipError_t e = msa::launch_index_select_prefill_fp8(q_idx8, q_exp, k_idx8, k_exp, cu_seqlens_q,
-                                                        cu_seqlens_k, dims->batch, x.G, x.DI,
+                                                        cu_seqlens_k, x.kv, dims->batch, x.G, x.DI,
                                                         x.nb_max, dims->max_q_len, x.top_k, sel,
                                                         sel_score, st);
     return e == hipSuccess ? MSA_OK : hip_fail(e);
@@ -375,7 +394,7 @@ msa_status_t msa_index_select_fp8(const msa_dims_t* dims, const void* q_idx8, co
     {
       ProfScope ps(K_INDEX_DECODE_FP8, st);
       e = msa::launch_index_score_decode_fp8(q_idx8, q_exp, k_idx8, k_exp, cu_seqlens_q,
-                                             cu_seqlens_k, dims->batch, x.G, x.DI, x.nb_max,
+                                             cu_seqlens_k, x.kv, dims->batch, x.G, x.DI, x.nb_max,
                                              dims->max_q_len * x.G, a, z, S, ld, st);
     }
     if (e != hipSuccess) return hip_fail(e);
@@ -443,11 +462,11 @@ static msa_status_t attend_impl(const msa_dims_t* dims, const void* q, const voi
       if (dims->max_q_len <= kDecodeAttendMaxQ)
         // a few queries per sequence: each selected block is hit by few queries;
         // one wave per (query, slot) reads it straight from the selection
-        e = msa::launch_attend_decode(x.D, x.hpg, q, k, v, cu_seqlens_q, cu_seqlens_k, dims->batch,
+        e = msa::launch_attend_decode(x.D, x.hpg, q, k, v, cu_seqlens_q, cu_seqlens_k, x.kv, dims->batch,
                                       x.G, x.Hq, x.top_k, sel, a, z, scale_log2, part_acc, part_ml,
                                       st);
       else
-        e = msa::launch_attend_blocks(x.D, x.hpg, q, k, v, cu_seqlens_q, cu_seqlens_k,
+        e = msa::launch_attend_blocks(x.D, x.hpg, q, k, v, cu_seqlens_q, cu_seqlens_k, x.kv,
                                       dims->batch, x.G, x.Hq, x.top_k, x.nb_max, block_offsets,
                                       block_entries, a, z, (int)x.total_q, scale_log2, part_acc,
                                       part_ml, st);
@@ -505,7 +524,7 @@ msa_status_t msa_index_kl(const msa_dims_t* dims, const void* q_idx, const void*
     return fail(MSA_ERR_ALIGNMENT, "tensor pointers must be 16-byte aligned");
   hipStream_t st = (hipStream_t)stream;
   ProfScope ps(K_INDEX_KL, st);
-  hipError_t e = msa::launch_index_kl(x.DI, q_idx, k_idx, cu_seqlens_q, cu_seqlens_k, dims->batch,
+  hipError_t e = msa::launch_index_kl(x.DI, q_idx, k_idx, cu_seqlens_q, cu_seqlens_k, x.kv, dims->batch,
                                       x.G, x.top_k, dims->max_q_len, sel, sel_score, block_mass,
                                       log_q, kl, st);
   return e == hipSuccess ? MSA_OK : hip_fail(e);

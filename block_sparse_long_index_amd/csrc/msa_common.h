@@ -24,6 +24,36 @@ struct RowPos {
   int qoff;    // first query row of the sequence
 };
 
+// Where the key rows of a sequence live (K, V and the index keys alike).
+// Contiguous: sequence b owns rows cu_k[b] .. cu_k[b+1]-1.  Paged: block beta
+// of sequence b is page table[b * max_blocks + beta], i.e. rows
+// 128 * page .. 128 * page + 127 of the cache.
+struct KvMap {
+  const int32_t* table;   // nullptr: contiguous rows
+  int max_blocks;         // row stride of the page table
+  int pages;              // pages in the cache (paged only)
+
+  // page of block beta of sequence b, clamped into the cache so that a
+  // malformed table cannot make a kernel address outside it
+  __device__ inline size_t page(int b, int beta) const {
+    const int pg = table[(size_t)b * max_blocks + beta];
+    return (size_t)min(max(pg, 0), pages - 1);
+  }
+  // first row of block beta of sequence b (koff = cu_k[b])
+  __device__ inline size_t block_row(int b, int koff, int beta) const {
+    return table ? page(b, beta) * 128u : (size_t)koff + (size_t)beta * 128u;
+  }
+  // row of key position j of sequence b
+  __device__ inline size_t key_row(int b, int koff, int j) const {
+    return block_row(b, koff, j >> 7) + (size_t)(j & 127);
+  }
+  // index of block beta's per-block exponent (fp8 index keys): per page when
+  // paged, else [batch][nb_max]
+  __device__ inline size_t block_index(int b, int beta, int nb_max) const {
+    return table ? page(b, beta) : (size_t)b * nb_max + beta;
+  }
+};
+
 // Sequence that owns global query row r (binary search over cu_seqlens_q).
 __device__ inline RowPos locate_row(int r, const int32_t* __restrict__ cu_q,
                                     const int32_t* __restrict__ cu_k, int batch) {

@@ -50,7 +50,7 @@
 extern "C" {
 #endif
 
-#define MSA_ABI_VERSION 1
+#define MSA_ABI_VERSION 2
 #define MSA_BLOCK_SIZE 128  /* B_k, MSA guide table in section "ブロック単位選択の数値設計" */
 #define MSA_MAX_TOP_K 32
 
@@ -86,8 +86,28 @@ typedef struct msa_dims {
   int32_t max_k_len;      /* max_b Lk_b (host-known upper bound; sizes launch grids) */
   int32_t q_chunk;        /* query rows processed per internal pass; 0 -> library default.
                              Bounds the workspace; results do not depend on it. */
+  int32_t kv_pages;       /* 0: contiguous key rows (sequence b owns rows cu_seqlens_k[b] ..);
+                             > 0: paged key cache of this many 128-row pages (see below) */
+  const int32_t* block_table;   /* paged only: device int32 [batch, max_blocks_per_seq]; block
+                                   beta of sequence b is page block_table[b][beta] */
+  int32_t max_blocks_per_seq;   /* paged only: row stride of block_table, >= ceil(max_k_len/128) */
   int32_t reserved;       /* must be 0 */
 } msa_dims_t;
+
+/*
+ * Paged key cache (kv_pages > 0).  A page holds one 128-token KV block, the
+ * unit the selection works in, so block beta of sequence b lives in page
+ * block_table[b][beta]: key position j of sequence b is row
+ * 128 * block_table[b][j / 128] + j % 128 of k, v and k_idx (and of k_idx8;
+ * the fp8 key exponents k_exp are then one per page, [kv_pages]).  total_k
+ * must equal 128 * kv_pages (the caches' row count); cu_seqlens_k still gives
+ * each sequence's length (its differences), its offsets are not used.  Every
+ * call that reads or writes key rows follows the table; block_table entries
+ * of a sequence's blocks must be distinct valid pages.  The table is read on
+ * the device, so it is not validated: an entry outside [0, kv_pages) is
+ * clamped into that range (the results are then wrong, but no access leaves
+ * the caches).  The table must stay allocated until the call's work ends.
+ */
 
 /* Bytes of workspace the call `op` needs for `dims` (same dims as the call).
  * Returns MSA_ERR_* on invalid dims, else MSA_OK and *bytes. */
@@ -220,7 +240,8 @@ msa_status_t msa_index_project(const msa_dims_t* dims, int32_t model_dim, const 
  *   k_idx8  uint8 E4M3 [total_k, index_dim]                 out
  *   k_exp   uint8 E8M0 [batch, nb_max], nb_max = ceil(max_k_len / 128)   out;
  *           k_exp[b, beta] scales keys cu_k[b] + 128 beta .. of sequence b;
- *           blocks past a sequence's end get 127.
+ *           blocks past a sequence's end get 127.  Paged cache: [kv_pages],
+ *           one per page; only the pages of the sequences' blocks are written.
  *   No workspace.  With total_q == 0 only the keys are quantised.  Keys are
  *   quantised per whole block, so a key cache quantised this way is
  *   re-quantised block by block as blocks fill (the selection never scores a

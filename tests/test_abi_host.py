@@ -35,8 +35,9 @@ def test_exports_every_declared_symbol():
 
 
 def test_abi_version_and_struct_layout():
-    assert lib.msa_abi_version() == 1
-    assert ctypes.sizeof(msa.Dims) == 64
+    assert lib.msa_abi_version() == 2
+    assert ctypes.sizeof(msa.Dims) == 80
+    assert msa.Dims.block_table.offset == 64 and msa.Dims.reserved.offset == 76
 
 
 def test_status_strings():
@@ -195,3 +196,24 @@ def test_kl_entry_points_validate_on_host():
     assert kl(ctypes.byref(d), ok, ok, ok, ok, ok, ok, ok, None, odd, None) == 4
     empty = _dims(total_q=0, max_q_len=0)
     assert kl(ctypes.byref(empty), None, None, None, None, None, None, None, None, None, None) == 0
+
+
+def test_paged_cache_fields_validated():
+    n = ctypes.c_size_t(0)
+    ws = lib.msa_workspace_size
+    d = _dims(total_k=32768)
+    d.kv_pages = 256
+    assert ws(ctypes.byref(d), 0, ctypes.byref(n)) == 1          # no block table
+    d.block_table = 0x10000
+    d.max_blocks_per_seq = 255                                   # below ceil(32768 / 128)
+    assert ws(ctypes.byref(d), 0, ctypes.byref(n)) == 2
+    d.max_blocks_per_seq = 256
+    assert ws(ctypes.byref(d), 0, ctypes.byref(n)) == 0
+    d.kv_pages = 300                                             # total_k != 128 * pages
+    assert ws(ctypes.byref(d), 0, ctypes.byref(n)) == 2
+    d.kv_pages = -1
+    assert ws(ctypes.byref(d), 0, ctypes.byref(n)) == 2
+    c = _dims()
+    c.max_blocks_per_seq = 4                                     # table fields without pages
+    assert ws(ctypes.byref(c), 0, ctypes.byref(n)) == 2
+
