@@ -238,11 +238,12 @@ def _fp8_top_set_valid(P, r, g, S, sel):
     return min(S[x] + B[x] for x in chosen) >= max((S[z] - B[z] for z in others), default=-np.inf)
 
 
-def projection_parity(proj, t, w, D, dev, n_rows=64):
+def projection_parity(proj, t, w, D, dev, k_store, key_rows=None, n_rows=64):
     """Index projections on sampled rows against the oracle's: each bf16 output
     equals the rounding of the exact sum, or (where the fp32-accumulated sum
     may cross a rounding boundary) lies within the accumulation bound plus one
-    unit in the last place of it."""
+    unit in the last place of it.  ``k_store`` is the index-key cache the step
+    writes (``key_rows`` maps contiguous key rows to its rows when paged)."""
     import torch
     from oracle import projections as PR
     rng = np.random.Generator(np.random.PCG64(4321))
@@ -255,7 +256,10 @@ def projection_parity(proj, t, w, D, dev, n_rows=64):
     b = np.searchsorted(cuq, rows, side="right") - 1
     krows = cuk[b] + (cuk[b + 1] - cuk[b]) - (cuq[b + 1] - cuq[b]) + (rows - cuq[b])
     got_q = t["q_idx"].index_select(0, ridx).double().cpu().numpy().reshape(len(rows), -1)
-    got_k = t["k_idx"].index_select(0, torch.as_tensor(krows, device=dev)).double().cpu().numpy()
+    kr = torch.as_tensor(krows, device=dev)
+    if key_rows is not None:
+        kr = key_rows.index_select(0, kr)
+    got_k = k_store.index_select(0, kr).double().cpu().numpy()
     bad = n_diff = 0
     for got, W in ((got_q, wq), (got_k, wk)):
         y, sa = x @ W.T, np.abs(x) @ np.abs(W).T
@@ -343,6 +347,9 @@ def main():
     ap.add_argument("--kl", action="store_true",
                     help="also compute the Index Branch's KL-alignment target in the step "
                          "(Main-Branch block masses + index log-probabilities + KL per query and group)")
+    ap.add_argument("--paged", action="store_true",
+                    help="hold K, V and the index keys in a paged cache (128-row pages in a "
+                         "scrambled order, found through a block table) instead of contiguous rows")
     ap.add_argument("--graph", choices=["auto", "on", "off"], default="auto",
                     help="replay the step as a captured HIP graph (auto: on for decode, whose "
                          "kernels are short enough for launch gaps to matter)")
@@ -386,6 +393,20 @@ def main():
     torch.cuda.synchronize()
     log(f"[bench] inputs ready in {time.perf_counter() - t0:.1f}s")
     dims = msa.dims_for(w, q_chunk=args.q_chunk)
+    # the step's key caches: the contiguous inputs, or the same rows scattered into pages
+    kc, vc, kic, key_rows = t["k"], t["v"], t["k_idx"], None
+    if args.paged:
+        from msa_inputs import paged_layout, to_pages
+        table, rows_h, pages = paged_layout(w, seed=w.seed)
+        key_rows = rows_h.to(dev)
+        table_d = table.to(dev)
+        kc, vc, kic = (to_pages(t[n], key_rows, pages) for n in ("k", "v", "k_idx"))
+        dims = msa.make_dims(batch=w.batch, num_q_heads=w.num_q_heads, num_kv_heads=w.num_kv_heads,
+                             head_dim=w.head_dim, index_dim=w.index_dim, top_k=w.top_k,
+                             total_q=w.total_q, total_k=pages * BLOCK, max_q_len=max(w.seq_q_lens),
+                             max_k_len=max(w.seq_k_lens), q_chunk=args.q_chunk, block_table=table_d)
+        torch.cuda.synchronize()
+        log(f"[bench] paged key cache: {pages} pages of {BLOCK} rows, scrambled order")
     bufs = msa.Buffers(dims, dev, want_scores=args.kl, want_lse=True)
     kl_out = None
     if args.kl:
@@ -395,9 +416,9 @@ def main():
     log(f"[bench] workspace {bufs.workspace.numel() / 2**30:.2f} GiB; index branch {args.index}")
     # fp8 decode: the index-key cache is stored quantised (quantised once, outside the step);
     # each step quantises only its new index queries.  Prefill quantises both in the step.
-    step_k_idx = t["k_idx"]
+    step_k_idx = kic
     if fp8 is not None and _decode_like(w):
-        msa.index_quantize_fp8(dims, None, t["k_idx"], t["cu_seqlens_k"], fp8)
+        msa.index_quantize_fp8(dims, None, kic, t["cu_seqlens_k"], fp8)
         torch.cuda.synchronize()
         step_k_idx = None
 
@@ -412,20 +433,20 @@ def main():
         if proj is not None:
             # q_idx and the new tokens' index keys come from the layer input
             msa.index_project(dims, proj["x"], proj["w_q"], proj["w_k"], t["cu_seqlens_q"],
-                              t["cu_seqlens_k"], t["q_idx"], t["k_idx"])
+                              t["cu_seqlens_k"], t["q_idx"], kic)
         if kl_out is None:
-            msa.msa_forward(dims, t["q"], t["k"], t["v"], t["q_idx"], step_k_idx, t["cu_seqlens_q"],
+            msa.msa_forward(dims, t["q"], kc, vc, t["q_idx"], step_k_idx, t["cu_seqlens_q"],
                             t["cu_seqlens_k"], bufs, fp8=fp8)
             return
         # the forward with the KL-alignment target (bf16 index branch)
-        msa.index_select(dims, t["q_idx"], t["k_idx"], t["cu_seqlens_q"], t["cu_seqlens_k"],
+        msa.index_select(dims, t["q_idx"], kic, t["cu_seqlens_q"], t["cu_seqlens_k"],
                          bufs.sel, bufs.sel_score, bufs.workspace)
         msa.build_block_query_lists(dims, bufs.sel, t["cu_seqlens_q"], t["cu_seqlens_k"], bufs.offsets,
                                     bufs.entries, bufs.workspace)
-        msa.attend_with_mass(dims, t["q"], t["k"], t["v"], t["cu_seqlens_q"], t["cu_seqlens_k"],
+        msa.attend_with_mass(dims, t["q"], kc, vc, t["cu_seqlens_q"], t["cu_seqlens_k"],
                              bufs.sel, bufs.offsets, bufs.entries, bufs.out, kl_out["mass"], bufs.lse,
                              bufs.workspace)
-        msa.index_kl(dims, t["q_idx"], t["k_idx"], t["cu_seqlens_q"], t["cu_seqlens_k"], bufs.sel,
+        msa.index_kl(dims, t["q_idx"], kic, t["cu_seqlens_q"], t["cu_seqlens_k"], bufs.sel,
                      bufs.sel_score, kl_out["mass"], kl_out["kl"])
 
     for i in range(args.warmup):
@@ -544,7 +565,7 @@ def main():
     cpu = None
     parity = None
     if proj is not None:
-        parity = projection_parity(proj, t, w, args.project_dim, dev)
+        parity = projection_parity(proj, t, w, args.project_dim, dev, kic, key_rows)
         log(f"[bench] projection parity on sampled rows: {parity}")
     elif not args.no_cpu_baseline:
         from oracle import msa_oracle as O
@@ -635,6 +656,7 @@ def main():
                    "index_dim": w.index_dim, "block": BLOCK, "top_k": w.top_k,
                    "q_chunk": args.q_chunk, "index_branch": args.index,
                    "index_projection_dim": args.project_dim or None, "kl_target": bool(args.kl),
+                   "kv_cache": "paged (128-row pages, scrambled)" if args.paged else "contiguous",
                    "parallelism": "single GPU"},
         "roofline": roof(dominant) if dominant else None,
         "dominant_kernel": dominant,

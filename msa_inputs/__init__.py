@@ -236,3 +236,35 @@ def generate_projection(w: Workload, model_dim: int, device="cpu", seed_offset: 
         r1 = min(w.total_q, r0 + _ROW_CHUNK)
         x[r0:r1] = _randn(gen, (r1 - r0, D), device).to(bf)
     return dict(x=x.contiguous(), w_q=w_q.contiguous(), w_k=w_k.contiguous())
+
+
+def paged_layout(w: Workload, seed: int = 0, spare_pages: int = 7):
+    """A scrambled paged placement of the workload's key rows (serving-style
+    key cache): every sequence's 128-token blocks get distinct pages drawn as
+    a random permutation (numpy PCG64(seed)) of ``sum(blocks) + spare_pages``
+    pages.  Returns (block_table int32 [batch, max_blocks + 2], -1 past each
+    sequence's blocks; cache row of every contiguous key row int64
+    [total_k]; page count)."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    nblk = [(int(n) + BLOCK - 1) // BLOCK for n in w.seq_k_lens]
+    pages = sum(nblk) + int(spare_pages)
+    perm = rng.permutation(pages).astype(np.int32)
+    table = np.full((w.batch, max(nblk) + 2), -1, dtype=np.int32)
+    rows = np.empty(w.total_k, dtype=np.int64)
+    i = off = 0
+    for b, n in enumerate(w.seq_k_lens):
+        table[b, :nblk[b]] = perm[i:i + nblk[b]]
+        i += nblk[b]
+        j = np.arange(int(n))
+        rows[off:off + int(n)] = table[b, j // BLOCK].astype(np.int64) * BLOCK + j % BLOCK
+        off += int(n)
+    return torch.from_numpy(table), torch.from_numpy(rows), pages
+
+
+def to_pages(src: torch.Tensor, rows: torch.Tensor, pages: int, fill=0.0) -> torch.Tensor:
+    """Copy contiguous key rows ``src`` [total_k, ...] into a paged cache of
+    ``pages * 128`` rows at ``rows``; every other row holds ``fill``."""
+    cache = torch.full((pages * BLOCK,) + tuple(src.shape[1:]), fill, dtype=src.dtype,
+                       device=src.device)
+    cache[rows.to(src.device)] = src
+    return cache
