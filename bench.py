@@ -433,7 +433,7 @@ def main():
         if proj is not None:
             # q_idx and the new tokens' index keys come from the layer input
             msa.index_project(dims, proj["x"], proj["w_q"], proj["w_k"], t["cu_seqlens_q"],
-                              t["cu_seqlens_k"], t["q_idx"], kic)
+                              t["cu_seqlens_k"], t["q_idx"], kic, bufs.workspace)
         if kl_out is None:
             msa.msa_forward(dims, t["q"], kc, vc, t["q_idx"], step_k_idx, t["cu_seqlens_q"],
                             t["cu_seqlens_k"], bufs, fp8=fp8)

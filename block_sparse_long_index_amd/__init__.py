@@ -15,17 +15,19 @@ import re
 import torch
 
 __all__ = [
-    "MSAError", "Dims", "OP_INDEX_SELECT", "OP_BUILD_LISTS", "OP_ATTEND", "load_library",
+    "MSAError", "Dims", "OP_INDEX_SELECT", "OP_BUILD_LISTS", "OP_ATTEND", "OP_INDEX_PROJECT",
+    "load_library",
     "make_dims", "workspace_size", "index_select", "build_block_query_lists", "attend",
     "msa_forward", "exported_symbols", "LIB_PATH", "HEADER_PATH", "index_quantize_fp8",
     "index_select_fp8", "Fp8Index", "index_project", "attend_with_mass", "index_kl",
+    "attend_reads_lists",
 ]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libmsa.so")
 HEADER_PATH = os.path.join(os.path.dirname(_PKG), "include", "msa.h")
 
-OP_INDEX_SELECT, OP_BUILD_LISTS, OP_ATTEND = 0, 1, 2
+OP_INDEX_SELECT, OP_BUILD_LISTS, OP_ATTEND, OP_INDEX_PROJECT = 0, 1, 2, 3
 BLOCK = 128
 
 
@@ -75,7 +77,7 @@ def load_library(path: str = LIB_PATH):
     lib.msa_index_kl.restype = I32
     lib.msa_index_kl.argtypes = [DP, P, P, P, P, P, P, P, P, P, P]
     lib.msa_index_project.restype = I32
-    lib.msa_index_project.argtypes = [DP, I32, P, P, P, P, P, P, P, P]
+    lib.msa_index_project.argtypes = [DP, I32, P, P, P, P, P, P, P, P, SZ, P]
     lib.msa_index_quantize_fp8.restype = I32
     lib.msa_index_quantize_fp8.argtypes = [DP, P, P, P, P, P, P, P, P]
     lib.msa_index_select_fp8.restype = I32
@@ -84,6 +86,8 @@ def load_library(path: str = LIB_PATH):
     lib.msa_build_block_query_lists.argtypes = [DP, P, P, P, P, P, P, SZ, P]
     lib.msa_attend.restype = I32
     lib.msa_attend.argtypes = [DP, P, P, P, P, P, P, P, P, P, P, P, SZ, P]
+    lib.msa_attend_reads_lists.restype = I32
+    lib.msa_attend_reads_lists.argtypes = [DP]
     lib.msa_profile_enable.restype = I32
     lib.msa_profile_enable.argtypes = [I32]
     lib.msa_profile_collect.restype = I32
@@ -192,7 +196,8 @@ def index_select(dims, q_idx, k_idx, cu_seqlens_q, cu_seqlens_k, sel, sel_score=
     return sel
 
 
-def index_project(dims, x, w_q, w_k, cu_seqlens_q, cu_seqlens_k, q_idx, k_idx, stream=None):
+def index_project(dims, x, w_q, w_k, cu_seqlens_q, cu_seqlens_k, q_idx, k_idx, workspace=None,
+                  stream=None):
     """q_idx = x W_q^T, and the new tokens' rows of k_idx = x W_k^T (bf16)."""
     G, T, DI = dims.num_kv_heads, dims.total_q, dims.index_dim
     D = int(x.shape[1]) if x.dim() == 2 else -1
@@ -201,11 +206,12 @@ def index_project(dims, x, w_q, w_k, cu_seqlens_q, cu_seqlens_k, q_idx, k_idx, s
     _shape(w_k, (DI, D), "w_k")
     _shape(q_idx, (T, G, DI), "q_idx")
     _shape(k_idx, (dims.total_k, DI), "k_idx")
+    ws = _workspace(dims, OP_INDEX_PROJECT, workspace, q_idx.device)
     st = load_library().msa_index_project(
         ctypes.byref(dims), D, _ptr(x, "x", torch.bfloat16), _ptr(w_q, "w_q", torch.bfloat16),
         _ptr(w_k, "w_k", torch.bfloat16), _ptr(cu_seqlens_q, "cu_seqlens_q", torch.int32),
         _ptr(cu_seqlens_k, "cu_seqlens_k", torch.int32), _ptr(q_idx, "q_idx", torch.bfloat16),
-        _ptr(k_idx, "k_idx", torch.bfloat16), _stream(stream))
+        _ptr(k_idx, "k_idx", torch.bfloat16), _ptr(ws, "workspace"), ws.numel(), _stream(stream))
     _check(st, "msa_index_project")
     return q_idx, k_idx
 
@@ -369,8 +375,18 @@ class Buffers:
         self.entries = torch.empty((max(1, T * G * k),), dtype=torch.int32, device=dev)
         self.out = torch.empty((T, dims.num_q_heads, dims.head_dim), dtype=torch.bfloat16, device=dev)
         self.lse = torch.empty((T, dims.num_q_heads), dtype=torch.float32, device=dev) if want_lse else None
-        need = max(workspace_size(dims, op) for op in (OP_INDEX_SELECT, OP_BUILD_LISTS, OP_ATTEND))
+        need = max(workspace_size(dims, op)
+                   for op in (OP_INDEX_SELECT, OP_BUILD_LISTS, OP_ATTEND, OP_INDEX_PROJECT))
         self.workspace = torch.empty((need,), dtype=torch.uint8, device=dev)
+
+
+def attend_reads_lists(dims: Dims) -> bool:
+    """Whether attend reads the per-block query lists for these dims (False for
+    decode-shaped steps, which attend per (query, slot) from the selection)."""
+    r = int(load_library().msa_attend_reads_lists(ctypes.byref(dims)))
+    if r < 0:
+        _check(-r, "msa_attend_reads_lists")
+    return r == 1
 
 
 def msa_forward(dims: Dims, q, k, v, q_idx, k_idx, cu_seqlens_q, cu_seqlens_k, bufs: Buffers = None,
@@ -378,6 +394,7 @@ def msa_forward(dims: Dims, q, k, v, q_idx, k_idx, cu_seqlens_q, cu_seqlens_k, b
     """The whole hot path: index_select -> build_block_query_lists -> attend.
 
     One workspace serves the three calls (they run in order on one stream).
+    Decode-shaped steps skip the lists, which their attend does not read.
     With `fp8` given, the Index Branch quantises q_idx and k_idx into it and
     selects on the codes (index_quantize_fp8 -> index_select_fp8); k_idx=None
     keeps the key codes already in `fp8` (a quantised index-key cache).
@@ -390,8 +407,9 @@ def msa_forward(dims: Dims, q, k, v, q_idx, k_idx, cu_seqlens_q, cu_seqlens_k, b
         index_quantize_fp8(dims, q_idx, k_idx, cu_seqlens_k, fp8, stream)
         index_select_fp8(dims, fp8, cu_seqlens_q, cu_seqlens_k, bufs.sel, bufs.sel_score,
                          bufs.workspace, stream)
-    build_block_query_lists(dims, bufs.sel, cu_seqlens_q, cu_seqlens_k, bufs.offsets, bufs.entries,
-                            bufs.workspace, stream)
+    if attend_reads_lists(dims):
+        build_block_query_lists(dims, bufs.sel, cu_seqlens_q, cu_seqlens_k, bufs.offsets,
+                                bufs.entries, bufs.workspace, stream)
     attend(dims, q, k, v, cu_seqlens_q, cu_seqlens_k, bufs.sel, bufs.offsets, bufs.entries,
            bufs.out, bufs.lse, bufs.workspace, stream)
     return bufs

@@ -13,6 +13,8 @@
 // of 32 through a three-stage LDS ring filled by direct global->LDS loads two
 // steps ahead.  Tile order is XCD-aware: the feature tiles of one token tile
 // run on one XCD, so each x tile is fetched into one L2 and reused there.
+#include <algorithm>
+
 #include "msa_common.h"
 
 namespace msa {
@@ -149,22 +151,51 @@ __global__ __launch_bounds__(kProjNW * 64, 2) void index_project_kernel(
   }
 }
 
-// Few tokens (decode steps): the work is reading the weights once, so the
-// grid spreads over features instead of tokens.  A workgroup computes a
-// 32-feature x 32-token tile over all of K: its 8 waves take interleaved
-// 64-element slices of K, loading fragments straight from global memory
-// (each lane's 4 x 16-byte loads cover 128 contiguous bytes of a row per
-// slice), and the 8 partial tiles are summed in a fixed order through LDS.
-constexpr int kProjSmallWaves = 8;
-constexpr int kProjSmallMaxT = 512;   // token counts up to this use the small kernel
+// Few tokens (decode and verification steps): the work is reading the
+// weights once, and 32 x 32 output tiles alone would give a few dozen
+// workgroups, each walking all of K through a long chain of dependent loads.
+// So K is split across workgroups as well: workgroup (feature tile, token
+// tile, slice) multiplies its tile over one slice of K (a run of 64-element
+// chunks; its 4 waves take every 4th chunk and load up to 4 chunks'
+// fragments at once, straight from global memory), the waves' tiles are
+// summed through LDS in a fixed order, and the fp32 tile goes to the
+// workspace.  A second kernel sums the slices in order, rounds to bf16 and
+// stores the outputs.  Nothing is accumulated with atomics, so results are
+// deterministic.
+constexpr int kProjSmallMaxT = 512;     // token counts up to this take the split path
+constexpr int kProjSplitWaves = 4;
+constexpr int kProjSplitChunks = 4;     // chunks a wave has in flight
+constexpr int kProjSplitMax = 32;       // slices of K at most (sizes the workspace)
+constexpr int kProjSplitTarget = 512;   // workgroups the split aims for at least
 
-__global__ __launch_bounds__(kProjSmallWaves * 64) void index_project_small_kernel(
+// slices of K for T tokens, F features and C chunks of 64: enough workgroups
+// to fill the GPU, and few enough chunks per wave to load them in one go
+static int project_split(int T, int F, int C) {
+  const long long tiles = (long long)((F + 31) / 32) * ((T + 31) / 32);
+  const long long want = std::max((kProjSplitTarget + tiles - 1) / tiles,
+                                  (long long)(C + kProjSplitWaves * kProjSplitChunks - 1) /
+                                      (kProjSplitWaves * kProjSplitChunks));
+  // every wave keeps at least one chunk
+  const long long cap = std::min<long long>(kProjSplitMax, std::max(1, C / kProjSplitWaves));
+  return (int)std::max(1ll, std::min(want, cap));
+}
+
+size_t project_workspace_bytes(int T, int F) {
+  if (T <= 0 || T > kProjSmallMaxT) return 0;
+  return (size_t)kProjSplitMax * (size_t)((T + 31) / 32 * 32) * (size_t)((F + 31) / 32 * 32) *
+         sizeof(float);
+}
+
+// part: fp32 [KS][Tp][Fp], Tp / Fp = T / F rounded up to 32 (padding rows and
+// columns get values from clamped operands and are never read back)
+__global__ __launch_bounds__(kProjSplitWaves * 64) void index_project_split_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ wq,
-    const uint16_t* __restrict__ wk, int D, int GD, int F, int T, int n_ft,
-    const int32_t* __restrict__ cu_q, const int32_t* __restrict__ cu_k, KvMap kv, int batch, int DI,
-    uint16_t* __restrict__ q_idx, uint16_t* __restrict__ k_idx) {
-  __shared__ float part[kProjSmallWaves][16][64];
-  const int ft = blockIdx.x % n_ft, tt = blockIdx.x / n_ft;
+    const uint16_t* __restrict__ wk, int D, int GD, int F, int T, int n_ft, int n_tt, int KS,
+    int Tp, int Fp, float* __restrict__ part) {
+  __shared__ float red[kProjSplitWaves - 1][16][64];
+  const int ft = blockIdx.x % n_ft;
+  const int rest = blockIdx.x / n_ft;
+  const int tt = rest % n_tt, ks = rest / n_tt;
   const int f0 = ft * 32, t0 = tt * 32;
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63, col = lane & 31, half = lane >> 5;
@@ -172,53 +203,111 @@ __global__ __launch_bounds__(kProjSmallWaves * 64) void index_project_small_kern
   const int t = min(t0 + col, T - 1);
   const uint16_t* arow = (f < GD ? wq + (size_t)f * D : wk + (size_t)(f - GD) * D) + 8 * half;
   const uint16_t* brow = x + (size_t)t * D + 8 * half;
+  const int C = D / 64;                                   // 64-element chunks of K
+  const int c0 = (int)((long long)ks * C / KS), c1 = (int)((long long)(ks + 1) * C / KS);
   f32x16 acc = f32x16{};
-  for (int k0 = wave * 64; k0 < D; k0 += kProjSmallWaves * 64) {
-    uint4 a[4], b[4];
+  constexpr int NC = kProjSplitChunks;
+  for (int cb = c0 + wave; cb < c1; cb += NC * kProjSplitWaves) {
+    uint4 a[NC][4], bb[NC][4];
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      a[s] = *reinterpret_cast<const uint4*>(arow + k0 + 16 * s);
-      b[s] = *reinterpret_cast<const uint4*>(brow + k0 + 16 * s);
+    for (int u = 0; u < NC; ++u) {
+      const int c = cb + u * kProjSplitWaves;
+      if (c < c1) {
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          a[u][s] = *reinterpret_cast<const uint4*>(arow + (size_t)c * 64 + 16 * s);
+          bb[u][s] = *reinterpret_cast<const uint4*>(brow + (size_t)c * 64 + 16 * s);
+        }
+      }
     }
 #pragma unroll
-    for (int s = 0; s < 4; ++s) acc = mfma32(as_bf16x8(a[s]), as_bf16x8(b[s]), acc);
-  }
+    for (int u = 0; u < NC; ++u) {
+      if (cb + u * kProjSplitWaves < c1) {
 #pragma unroll
-  for (int i = 0; i < 16; ++i) part[wave][i][lane] = acc[i];
+        for (int s = 0; s < 4; ++s) acc = mfma32(as_bf16x8(a[u][s]), as_bf16x8(bb[u][s]), acc);
+      }
+    }
+  }
+  if (wave != 0) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) red[wave - 1][i][lane] = acc[i];
+  }
   __syncthreads();
   if (wave != 0) return;
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
-    float v = part[0][i][lane];
+    float v = acc[i];
 #pragma unroll
-    for (int w = 1; w < kProjSmallWaves; ++w) v += part[w][i][lane];
+    for (int w = 0; w < kProjSplitWaves - 1; ++w) v += red[w][i][lane];
     acc[i] = v;
   }
-  const int tok = t0 + col;
-  if (tok >= T) return;
-  const RowPos rp = locate_row(tok, cu_q, cu_k, batch);
-  const size_t krow = kv.key_row(rp.b, rp.koff, rp.p);
+  // lane holds token t0 + col, features f0 + 8j + 4 half + (0..3)
+  float* dst = part + ((size_t)ks * Tp + t0 + col) * Fp + f0 + 4 * half;
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int ff = f0 + 8 * j + 4 * half;
-    if (ff >= F) continue;
-    const uint2 v = make_uint2(pack2_bf16(acc[4 * j], acc[4 * j + 1]),
-                               pack2_bf16(acc[4 * j + 2], acc[4 * j + 3]));
-    uint16_t* dst = ff < GD ? q_idx + (size_t)tok * GD + ff : k_idx + krow * DI + (ff - GD);
-    *reinterpret_cast<uint2*>(dst) = v;
+  for (int j = 0; j < 4; ++j)
+    *reinterpret_cast<float4*>(dst + 8 * j) =
+        make_float4(acc[4 * j], acc[4 * j + 1], acc[4 * j + 2], acc[4 * j + 3]);
+}
+
+// One thread per (token, run of 4 features): the slices summed in order,
+// rounded to bf16 and stored to the token's q_idx row or its key row.
+__global__ __launch_bounds__(256) void index_project_reduce_kernel(
+    const float* __restrict__ part, int KS, int Tp, int Fp, int T, int F, int GD, int DI,
+    const int32_t* __restrict__ cu_q, const int32_t* __restrict__ cu_k, KvMap kv, int batch,
+    uint16_t* __restrict__ q_idx, uint16_t* __restrict__ k_idx) {
+  const int F4 = F / 4;
+  const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (i >= (long long)T * F4) return;
+  const int tok = (int)(i / F4), ff = (int)(i % F4) * 4;
+  const float* src = part + (size_t)tok * Fp + ff;
+  const size_t slice = (size_t)Tp * Fp;
+  float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+  // eight slices' loads in flight at a time, added in slice order
+  for (int k0 = 0; k0 < KS; k0 += 8) {
+    float4 u[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      if (k0 + j < KS) u[j] = *reinterpret_cast<const float4*>(src + (size_t)(k0 + j) * slice);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      if (k0 + j < KS) {
+        v.x += u[j].x;
+        v.y += u[j].y;
+        v.z += u[j].z;
+        v.w += u[j].w;
+      }
+    }
+  }
+  const uint2 o = make_uint2(pack2_bf16(v.x, v.y), pack2_bf16(v.z, v.w));
+  if (ff < GD) {
+    *reinterpret_cast<uint2*>(q_idx + (size_t)tok * GD + ff) = o;
+  } else {
+    const RowPos rp = locate_row(tok, cu_q, cu_k, batch);
+    *reinterpret_cast<uint2*>(k_idx + kv.key_row(rp.b, rp.koff, rp.p) * DI + (ff - GD)) = o;
   }
 }
 
 hipError_t launch_index_project(const void* x, const void* wq, const void* wk, int D, int G, int DI,
                                 int T, const int32_t* cu_q, const int32_t* cu_k, KvMap kv,
-                                int batch, void* q_idx, void* k_idx, hipStream_t st) {
+                                int batch, void* q_idx, void* k_idx, void* workspace,
+                                hipStream_t st) {
   const int GD = G * DI, F = GD + DI;
+  if (T <= 0) return hipSuccess;
   if (T <= kProjSmallMaxT) {
     const int n_ft = (F + 31) / 32, n_tt = (T + 31) / 32;
-    if (T <= 0) return hipSuccess;
-    hipLaunchKernelGGL(index_project_small_kernel, dim3(n_ft * n_tt), dim3(kProjSmallWaves * 64), 0,
-                       st, (const uint16_t*)x, (const uint16_t*)wq, (const uint16_t*)wk, D, GD, F, T,
-                       n_ft, cu_q, cu_k, kv, batch, DI, (uint16_t*)q_idx, (uint16_t*)k_idx);
+    const int Tp = n_tt * 32, Fp = n_ft * 32;
+    // at least 4 chunks of 64 per slice, so that every wave has work
+    const int KS = project_split(T, F, D / 64);
+    float* part = reinterpret_cast<float*>(workspace);
+    hipLaunchKernelGGL(index_project_split_kernel, dim3(n_ft * n_tt * KS), dim3(kProjSplitWaves * 64),
+                       0, st, (const uint16_t*)x, (const uint16_t*)wq, (const uint16_t*)wk, D, GD, F,
+                       T, n_ft, n_tt, KS, Tp, Fp, part);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const long long n = (long long)T * (F / 4);
+    hipLaunchKernelGGL(index_project_reduce_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0,
+                       st, (const float*)part, KS, Tp, Fp, T, F, GD, DI, cu_q, cu_k, kv, batch,
+                       (uint16_t*)q_idx, (uint16_t*)k_idx);
     return hipGetLastError();
   }
   const int n_ft = (F + kProjBF - 1) / kProjBF;

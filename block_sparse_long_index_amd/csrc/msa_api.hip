@@ -40,8 +40,9 @@ hipError_t launch_index_kl(int, const void*, const void*, const int32_t*, const 
                            int, int, int, const int32_t*, const float*, const float*, float*,
                            float*, hipStream_t);
 hipError_t launch_index_project(const void*, const void*, const void*, int, int, int, int,
-                                const int32_t*, const int32_t*, KvMap, int, void*, void*,
+                                const int32_t*, const int32_t*, KvMap, int, void*, void*, void*,
                                 hipStream_t);
+size_t project_workspace_bytes(int, int);
 hipError_t launch_quantize_index_fp8(int, const void*, const void*, const int32_t*, KvMap, int, int,
                                      long long, void*, uint8_t*, void*, uint8_t*, hipStream_t);
 hipError_t launch_index_select_prefill_fp8(const void*, const uint8_t*, const void*, const uint8_t*,
@@ -181,6 +182,12 @@ size_t ws_attend(const msa_dims_t* d, const Derived& x) {
   return align256(rows * x.D * 4) + align256(rows * 8) + 256;
 }
 
+size_t ws_project(const Derived& x) {
+  // split-K partial tiles of the few-token path (0 for larger steps)
+  if (x.total_q > (1ll << 30)) return 0;
+  return msa::project_workspace_bytes((int)x.total_q, (x.G + 1) * x.DI);
+}
+
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
 // --- opt-in per-launch timing: each launcher call is bracketed by two hipEvents
@@ -265,6 +272,7 @@ msa_status_t msa_workspace_size(const msa_dims_t* dims, msa_op_t op, size_t* byt
     case MSA_OP_INDEX_SELECT: *bytes = ws_select(dims, x); return MSA_OK;
     case MSA_OP_BUILD_LISTS: *bytes = ws_lists(dims, x); return MSA_OK;
     case MSA_OP_ATTEND: *bytes = ws_attend(dims, x); return MSA_OK;
+    case MSA_OP_INDEX_PROJECT: *bytes = ws_project(x); return MSA_OK;
   }
   return fail(MSA_ERR_BAD_DIMS, "unknown op");
 }
@@ -315,7 +323,7 @@ msa_status_t msa_index_select(const msa_dims_t* dims, const void* q_idx, const v
 msa_status_t msa_index_project(const msa_dims_t* dims, int32_t model_dim, const void* x,
                                const void* w_q, const void* w_k, const int32_t* cu_seqlens_q,
                                const int32_t* cu_seqlens_k, void* q_idx, void* k_idx,
-                               void* stream) {
+                               void* workspace, size_t workspace_bytes, void* stream) {
   Derived x_;
   msa_status_t s = check_dims(dims, &x_);
   if (s != MSA_OK) return s;
@@ -324,13 +332,18 @@ msa_status_t msa_index_project(const msa_dims_t* dims, int32_t model_dim, const 
   if (x_.total_q == 0) return MSA_OK;   // no new tokens
   if (!x || !w_q || !w_k || !cu_seqlens_q || !cu_seqlens_k || !q_idx || !k_idx)
     return fail(MSA_ERR_NULL_ARG, "a required pointer is NULL");
-  if (!aligned16(x) || !aligned16(w_q) || !aligned16(w_k) || !aligned16(q_idx) || !aligned16(k_idx))
+  const size_t need = ws_project(x_);
+  if (need && !workspace) return fail(MSA_ERR_NULL_ARG, "a required pointer is NULL");
+  if (!aligned16(x) || !aligned16(w_q) || !aligned16(w_k) || !aligned16(q_idx) ||
+      !aligned16(k_idx) || (need && !aligned16(workspace)))
     return fail(MSA_ERR_ALIGNMENT, "tensor pointers must be 16-byte aligned");
+  if (workspace_bytes < need)
+    return fail(MSA_ERR_WORKSPACE_TOO_SMALL, "index_project workspace too small");
   hipStream_t st = (hipStream_t)stream;
   ProfScope ps(K_PROJECT, st);
   hipError_t e = msa::launch_index_project(x, w_q, w_k, model_dim, x_.G, x_.DI, (int)x_.total_q,
                                            cu_seqlens_q, cu_seqlens_k, x_.kv, dims->batch, q_idx,
-                                           k_idx, st);
+                                           k_idx, workspace, st);
   return e == hipSuccess ? MSA_OK : hip_fail(e);
 }
 
@@ -429,6 +442,16 @@ msa_status_t msa_build_block_query_lists(const msa_dims_t* dims, const int32_t* 
   return e == hipSuccess ? MSA_OK : hip_fail(e);
 }
 
+// decode-shaped steps attend per (query, slot) from the selection alone
+static bool reads_lists(const msa_dims_t* d) { return d->max_q_len > kDecodeAttendMaxQ; }
+
+int32_t msa_attend_reads_lists(const msa_dims_t* dims) {
+  Derived x;
+  msa_status_t s = check_dims(dims, &x);
+  if (s != MSA_OK) return -(int32_t)s;
+  return reads_lists(dims) ? 1 : 0;
+}
+
 static msa_status_t attend_impl(const msa_dims_t* dims, const void* q, const void* k,
                                 const void* v, const int32_t* cu_seqlens_q,
                                 const int32_t* cu_seqlens_k, const int32_t* sel,
@@ -439,11 +462,12 @@ static msa_status_t attend_impl(const msa_dims_t* dims, const void* q, const voi
   msa_status_t s = check_dims(dims, &x);
   if (s != MSA_OK) return s;
   if (x.total_q == 0) return MSA_OK;   // no queries: no output
-  if (!q || !k || !v || !cu_seqlens_q || !cu_seqlens_k || !sel || !block_offsets || !block_entries ||
-      !out || !workspace)
+  const bool lists = reads_lists(dims);
+  if (!q || !k || !v || !cu_seqlens_q || !cu_seqlens_k || !sel || !out || !workspace ||
+      (lists && (!block_offsets || !block_entries)))
     return fail(MSA_ERR_NULL_ARG, "a required pointer is NULL");
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(sel) || !aligned16(out) ||
-      !aligned16(workspace) || !aligned16(block_offsets) || !aligned16(block_entries) ||
+      !aligned16(workspace) || (lists && (!aligned16(block_offsets) || !aligned16(block_entries))) ||
       (lse && !aligned16(lse)))
     return fail(MSA_ERR_ALIGNMENT, "tensor pointers must be 16-byte aligned");
   if (workspace_bytes < ws_attend(dims, x))
@@ -459,7 +483,7 @@ static msa_status_t attend_impl(const msa_dims_t* dims, const void* q, const voi
     hipError_t e;
     {
       ProfScope ps(K_ATTEND, st);
-      if (dims->max_q_len <= kDecodeAttendMaxQ)
+      if (!lists)
         // a few queries per sequence: each selected block is hit by few queries;
         // one wave per (query, slot) reads it straight from the selection
         e = msa::launch_attend_decode(x.D, x.hpg, q, k, v, cu_seqlens_q, cu_seqlens_k, x.kv, dims->batch,

@@ -67,7 +67,8 @@ typedef enum msa_status {
 typedef enum msa_op {
   MSA_OP_INDEX_SELECT = 0,
   MSA_OP_BUILD_LISTS = 1,
-  MSA_OP_ATTEND = 2
+  MSA_OP_ATTEND = 2,
+  MSA_OP_INDEX_PROJECT = 3
 } msa_op_t;
 
 /* Problem sizes; passed by pointer to every call.  All fields are host values. */
@@ -172,6 +173,12 @@ msa_status_t msa_build_block_query_lists(const msa_dims_t* dims, const int32_t* 
  * K/V is staged on chip once per pass and serves every gathered query; the
  * per-(query, head, block) softmax partials are merged by log-sum-exp.
  *
+ * Decode-shaped steps (max_q_len <= 8 new tokens per sequence): a selected
+ * block is hit by at most a few queries, so the call works per (query, slot)
+ * straight from sel and does not read the lists; msa_attend_reads_lists()
+ * tells which case dims fall in, and where it returns 0 the lists may be NULL
+ * and msa_build_block_query_lists need not run.
+ *
  * q        bf16 [total_q, num_q_heads, head_dim]
  * k, v     bf16 [total_k, num_kv_heads, head_dim]
  * sel, block_offsets, block_entries: as from the two calls above (same dims)
@@ -206,12 +213,16 @@ msa_status_t msa_attend(const msa_dims_t* dims, const void* q, const void* k, co
  * w_k    bf16 [index_dim, D]
  * q_idx  bf16 [total_q, num_kv_heads, index_dim]  out
  * k_idx  bf16 [total_k, index_dim]                out (the new tokens' rows)
- * No workspace.  total_q == 0 enqueues nothing.
+ * workspace >= msa_workspace_size(dims, MSA_OP_INDEX_PROJECT) bytes, 16-byte
+ *   aligned (a few MiB for steps of up to 512 tokens, which split the sum
+ *   over model_dim across workgroups; 0 above, where NULL is accepted).
+ *   Partial sums are added in a fixed order: results are deterministic.
+ * total_q == 0 enqueues nothing.
  */
 msa_status_t msa_index_project(const msa_dims_t* dims, int32_t model_dim, const void* x,
                                const void* w_q, const void* w_k, const int32_t* cu_seqlens_q,
                                const int32_t* cu_seqlens_k, void* q_idx, void* k_idx,
-                               void* stream);
+                               void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * Quantised Index Branch (optional; the bf16 calls above are the reference
@@ -296,6 +307,11 @@ msa_status_t msa_index_kl(const msa_dims_t* dims, const void* q_idx, const void*
                           const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
                           const int32_t* sel, const float* sel_score, const float* block_mass,
                           float* log_q, float* kl, void* stream);
+
+/* 1 if msa_attend / msa_attend_with_mass read block_offsets and
+ * block_entries for these dims, 0 if they work from sel alone (decode-shaped
+ * steps), a negative msa_status_t for invalid dims. */
+int32_t msa_attend_reads_lists(const msa_dims_t* dims);
 
 /* Static description of a status code. */
 const char* msa_status_string(msa_status_t status);

@@ -173,12 +173,22 @@ def test_projection_entry_point_validates_on_host():
     ok = P(0x10000)
     odd = P(0x10004)
     pj = lib.msa_index_project
-    assert pj(ctypes.byref(d), 96, ok, ok, ok, ok, ok, ok, ok, None) == 3      # not a multiple of 64
-    assert pj(ctypes.byref(d), 0, ok, ok, ok, ok, ok, ok, ok, None) == 3
-    assert pj(ctypes.byref(d), 8192, None, ok, ok, ok, ok, ok, ok, None) == 1
-    assert pj(ctypes.byref(d), 8192, ok, ok, odd, ok, ok, ok, ok, None) == 4
+    assert pj(ctypes.byref(d), 96, ok, ok, ok, ok, ok, ok, ok, None, 0, None) == 3   # not a multiple of 64
+    assert pj(ctypes.byref(d), 0, ok, ok, ok, ok, ok, ok, ok, None, 0, None) == 3
+    assert pj(ctypes.byref(d), 8192, None, ok, ok, ok, ok, ok, ok, None, 0, None) == 1
+    assert pj(ctypes.byref(d), 8192, ok, ok, odd, ok, ok, ok, ok, None, 0, None) == 4
     empty = _dims(total_q=0, max_q_len=0)
-    assert pj(ctypes.byref(empty), 8192, None, None, None, None, None, None, None, None) == 0
+    assert pj(ctypes.byref(empty), 8192, None, None, None, None, None, None, None, None, 0, None) == 0
+    # steps of up to 512 tokens split the sum over model_dim: they need a workspace
+    assert msa.workspace_size(d, msa.OP_INDEX_PROJECT) == 0
+    for T in (1, 32, 100, 512):
+        dd = _dims(batch=T, total_q=T, max_q_len=1, max_k_len=1024, total_k=T * 1024)
+        need = msa.workspace_size(dd, msa.OP_INDEX_PROJECT)
+        assert need == 32 * ((T + 31) // 32 * 32) * (9 * 128) * 4    # up to 32 fp32 slices
+        assert pj(ctypes.byref(dd), 8192, ok, ok, ok, ok, ok, ok, ok, None, need, None) == 1
+        assert pj(ctypes.byref(dd), 8192, ok, ok, ok, ok, ok, ok, ok, odd, need, None) == 4
+        assert pj(ctypes.byref(dd), 8192, ok, ok, ok, ok, ok, ok, ok, ok, need - 1, None) == 5
+    assert msa.workspace_size(_dims(total_q=513, max_q_len=513), msa.OP_INDEX_PROJECT) == 0
 
 
 def test_kl_entry_points_validate_on_host():
@@ -217,3 +227,21 @@ def test_paged_cache_fields_validated():
     c.max_blocks_per_seq = 4                                     # table fields without pages
     assert ws(ctypes.byref(c), 0, ctypes.byref(n)) == 2
 
+
+
+def test_attend_reads_lists_only_beyond_decode_shapes():
+    P = ctypes.c_void_p
+    ok = P(0x10000)
+    big = ctypes.c_size_t(1 << 40)
+    at = lib.msa_attend
+    assert lib.msa_attend_reads_lists(ctypes.byref(_dims())) == 1
+    assert not msa.attend_reads_lists(_dims(batch=32, total_q=32 * 8, max_q_len=8,
+                                            total_k=32 * 4096, max_k_len=4096))
+    assert msa.attend_reads_lists(_dims(batch=32, total_q=32 * 9, max_q_len=9,
+                                        total_k=32 * 4096, max_k_len=4096))
+    assert lib.msa_attend_reads_lists(ctypes.byref(_dims(top_k=0))) < 0
+    # lists required where they are read, optional where they are not
+    d = _dims()
+    assert at(ctypes.byref(d), ok, ok, ok, ok, ok, ok, None, ok, ok, None, ok, big, None) == 1
+    dd = _dims(batch=32, total_q=32, max_q_len=1, total_k=32 * 4096, max_k_len=4096)
+    assert at(ctypes.byref(dd), ok, ok, ok, ok, ok, ok, None, None, P(0x10004), None, ok, big, None) == 4

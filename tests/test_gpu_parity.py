@@ -193,6 +193,10 @@ def test_empty_query_set():
     cuq = torch.tensor([0, 0], dtype=torch.int32, device=dev)
     cuk = torch.tensor([0, 256], dtype=torch.int32, device=dev)
     bufs = msa.msa_forward(dims, q, kv, kv, qi, ki, cuq, cuk)
+    # a decode-shaped step: the forward does not build the lists; built on their own
+    # for no queries they are all empty
+    assert not msa.attend_reads_lists(dims)
+    msa.build_block_query_lists(dims, bufs.sel, cuq, cuk, bufs.offsets, bufs.entries, bufs.workspace)
     torch.cuda.synchronize()
     assert int(bufs.offsets[-1]) == 0
 

@@ -97,6 +97,9 @@ def _key_rows(t, w):
     dict(k=[2000, 300, 129], q=[200, 300, 12], G=4, di=64, D=448),  # few-token kernel, 16 tiles
     dict(k=[512], q=[512], G=2, di=32, D=192),            # largest few-token case
     dict(k=[513], q=[513], G=2, di=32, D=192),            # smallest large-tile case
+    dict(k=[4000] * 32, q=[1] * 32, G=8, di=128, D=8192),  # decode at full width: 15 K slices
+    dict(k=[300, 200], q=[3, 2], G=2, di=32, D=64),       # one K chunk: three waves idle
+    dict(k=[900, 400], q=[100, 160], G=4, di=64, D=320),  # 5 K chunks over 4 waves
 ])
 def test_projection_elementwise(case):
     w = custom(case["k"], case["q"], num_q_heads=case["G"] * 4, num_kv_heads=case["G"],
@@ -114,6 +117,34 @@ def test_projection_elementwise(case):
     untouched = np.ones(w.total_k, dtype=bool)
     untouched[kr] = False
     assert np.all(kg[untouched] == -7.0)
+
+
+def test_split_path_is_deterministic_and_ignores_workspace_contents():
+    # the few-token path sums K slices through the workspace in a fixed order
+    w = custom([3000] * 16, [4] * 16, num_q_heads=32, num_kv_heads=8, head_dim=64, index_dim=128,
+               top_k=4, seed=53, qkv_std=1.0)
+    D = 4096
+    t = generate(w, "cpu")
+    p = generate_projection(w, D, "cpu")
+    dev = torch.device("cuda:0")
+    g = {k: v.to(dev) for k, v in t.items()}
+    gp = {k: v.to(dev) for k, v in p.items()}
+    dims = msa.dims_for(w)
+    need = msa.workspace_size(dims, msa.OP_INDEX_PROJECT)
+    assert need > 0
+    outs = []
+    for fill in (float("nan"), 1e30, 0.0):
+        ws = torch.full((need // 4,), fill, dtype=torch.float32, device=dev).view(torch.uint8)
+        q_idx = torch.empty((w.total_q, w.num_kv_heads, w.index_dim), dtype=torch.bfloat16, device=dev)
+        k_idx = torch.zeros((w.total_k, w.index_dim), dtype=torch.bfloat16, device=dev)
+        msa.index_project(dims, gp["x"], gp["w_q"], gp["w_k"], g["cu_seqlens_q"], g["cu_seqlens_k"],
+                          q_idx, k_idx, workspace=ws)
+        torch.cuda.synchronize()
+        outs.append((q_idx, k_idx))
+    for q_idx, k_idx in outs[1:]:
+        assert torch.equal(q_idx, outs[0][0]) and torch.equal(k_idx, outs[0][1])
+    q, rows, (yq, sq), (yk, sk) = _oracle(w, t, p, D)
+    _check_elementwise(outs[0][0].double().cpu().numpy().reshape(w.total_q, -1), yq, sq, D, "q_idx")
 
 
 def test_projection_model_width_8192_sampled():
