@@ -20,7 +20,7 @@ hipError_t launch_index_score_decode(const void*, const void*, const int32_t*, c
                                      int, int, int, int, int, int, int, float*, long long,
                                      hipStream_t);
 hipError_t launch_topk_select(const float*, long long, int, int, const int32_t*, const int32_t*, int,
-                              int, int, bool, int32_t*, float*, hipStream_t);
+                              int, int, int32_t*, float*, hipStream_t);
 size_t lists_workspace_bytes(int batch, int G, int nqt_max, int nb_max);
 int list_tile_rows();
 hipError_t launch_build_lists(const int32_t*, const int32_t*, const int32_t*, int, int, int, int,
@@ -314,7 +314,7 @@ msa_status_t msa_index_select(const msa_dims_t* dims, const void* q_idx, const v
     if (e != hipSuccess) return hip_fail(e);
     ProfScope ps(K_TOPK, st);
     e = msa::launch_topk_select(S, ld, a, z, cu_seqlens_q, cu_seqlens_k, dims->batch, x.G, x.top_k,
-                                true, sel, sel_score, st);
+                                sel, sel_score, st);
     if (e != hipSuccess) return hip_fail(e);
   }
   return MSA_OK;
@@ -413,7 +413,7 @@ msa_status_t msa_index_select_fp8(const msa_dims_t* dims, const void* q_idx8, co
     if (e != hipSuccess) return hip_fail(e);
     ProfScope ps(K_TOPK, st);
     e = msa::launch_topk_select(S, ld, a, z, cu_seqlens_q, cu_seqlens_k, dims->batch, x.G, x.top_k,
-                                true, sel, sel_score, st);
+                                sel, sel_score, st);
     if (e != hipSuccess) return hip_fail(e);
   }
   return MSA_OK;

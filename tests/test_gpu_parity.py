@@ -210,3 +210,38 @@ def test_verification_shapes_two_and_four_row_tiles():
         w = custom([7000, 4100, 300, 2049], [lq, lq, 5, lq], num_q_heads=32, num_kv_heads=8,
                    head_dim=128, index_dim=128, top_k=8, seed=seed, qkv_std=1.0)
         _full_check(w, tag=f"verify{lq}")
+
+
+def test_decode_topk_long_rows_and_many_survivors():
+    # decode selection from the block-score buffer: a row with exactly 2048 earlier blocks
+    # whose scores make more candidates reach the selection threshold than LDS gathers
+    # (blocks of lanes 0..13 tie at 2048, lane 14's at 1024, the rest 1: the list-merge
+    # fallback), and a row with 3000 earlier blocks (candidates beyond the 32 per lane
+    # held in registers)
+    lk = [2048 * 128 + 100, 3000 * 128 + 5, 777]
+    w = custom(lk, [1, 1, 1], num_q_heads=2, num_kv_heads=1, head_dim=64, index_dim=32,
+               top_k=16, seed=38, qkv_std=1.0)
+    t = generate(w, "cpu")
+    n0 = lk[0]
+    beta = np.arange(n0) // 128
+    lane = beta % 64
+    c = np.where(lane < 14, 2048.0, np.where(lane == 14, 1024.0, 1.0))
+    ki = torch.zeros((n0, 32), dtype=torch.float32)
+    ki[:, 0] = torch.from_numpy(c)
+    t["k_idx"][:n0] = ki.to(torch.bfloat16)
+    qi = torch.zeros((1, 1, 32), dtype=torch.bfloat16)
+    qi[0, 0, 0] = 1.0
+    t["q_idx"][0:1] = qi
+    dims, bufs, _ = run_gpu(w, t)
+    P = problem_from(t, w)
+    rows = [0, 1, 2]
+    ref = P.run(rows, want_scores=True)
+    sel = bufs.sel.cpu().numpy()
+    # ties broken by the lower block id: blocks 0..13 and 64, then the local block 2048
+    assert list(ref["sel"][0][0]) == list(range(14)) + [64, 2048]
+    bad, ties = check_selection(P, rows, sel, bufs.sel_score.cpu().numpy(), ref, w.index_dim)
+    log(f"[long-rows] selection mismatches {len(bad)} near-ties {ties}")
+    assert np.array_equal(sel[0], ref["sel"][0])
+    assert not bad, bad[:3]
+    check_out(bufs.out.float().cpu().numpy(), ref["out"], bufs.lse.cpu().numpy(), ref["lse"],
+              "long-rows")
