@@ -186,22 +186,36 @@ __global__ __launch_bounds__(NW * 64) void index_select_prefill_kernel(
       float rmax[RT];
 #pragma unroll
       for (int rt = 0; rt < RT; ++rt) rmax[rt] = -INFINITY;
+      // the block's 4 * KS fragments (key tile f / KS, k-step f % KS) flow through a
+      // window of DEPTH registers: a slot is refilled right after its MFMAs issue,
+      // so DEPTH fragments are in flight; key tiles alternate between two
+      // accumulator sets so a tile's row max does not hold up the next tile
+      constexpr int NF = 4 * KS, DEPTH = 4;
+      bf16x8 win[DEPTH];
 #pragma unroll
-      for (int kt = 0; kt < 4; ++kt) {
-        bf16x8 a[KS];
+      for (int f = 0; f < DEPTH; ++f) win[f] = Ring::frag(rbuf, (f / KS) * 32 + col, 2 * (f % KS) + half);
+      f32x16 acc[2][RT];
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) a[ks] = Ring::frag(rbuf, kt * 32 + col, 2 * ks + half);
-        f32x16 acc[RT];
+      for (int f = 0; f < NF; ++f) {
+        const int kt = f / KS, ks = f % KS, set = kt & 1;
+        if (ks == 0) {
 #pragma unroll
-        for (int rt = 0; rt < RT; ++rt) acc[rt] = f32x16{};
+          for (int rt = 0; rt < RT; ++rt) acc[set][rt] = f32x16{};
+        }
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks)
+        for (int rt = 0; rt < RT; ++rt) acc[set][rt] = mfma32(win[f % DEPTH], qf[rt][ks], acc[set][rt]);
+        if (f + DEPTH < NF)
+          win[f % DEPTH] = Ring::frag(rbuf, ((f + DEPTH) / KS) * 32 + col, 2 * ((f + DEPTH) % KS) + half);
+        if (ks == KS - 1) {
 #pragma unroll
-          for (int rt = 0; rt < RT; ++rt) acc[rt] = mfma32(a[ks], qf[rt][ks], acc[rt]);
+          for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
-        for (int rt = 0; rt < RT; ++rt)
+            for (int i = 0; i < 16; ++i) rmax[rt] = fmaxf(rmax[rt], acc[set][rt][i]);
+          // the tile's max is taken here, so its accumulators die here
 #pragma unroll
-          for (int i = 0; i < 16; ++i) rmax[rt] = fmaxf(rmax[rt], acc[rt][i]);
+          for (int rt = 0; rt < RT; ++rt) asm volatile("" : "+v"(rmax[rt]));
+        }
+        __builtin_amdgcn_sched_barrier(0);   // keep this order: the window is the schedule
       }
       const float mine = row_tile_max<RT>(rmax, half);
       // key 0 is never inserted
