@@ -58,6 +58,34 @@ struct KTileStage {
   }
 };
 
+
+// A key block staged in registers as clang vectors (plain values that stay in
+// registers even when two stages are live; HIP's uint4 struct does not).
+template <int DI, int NT>
+struct KTileRegs {
+  typedef unsigned v4u __attribute__((ext_vector_type(4)));
+  static constexpr int kChunks = kBlock * DI / 8;
+  static constexpr int kPer = (kChunks + NT - 1) / NT;
+  static constexpr int kLd = DI + 8;
+  v4u r[kPer];
+  __device__ inline void load(const uint16_t* __restrict__ src, int tid) {
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const int c = tid + i * NT;
+      if (kChunks % NT == 0 || c < kChunks)
+        r[i] = *reinterpret_cast<const v4u*>(src + (size_t)(c / (DI / 8)) * DI + (c % (DI / 8)) * 8);
+    }
+  }
+  __device__ inline void store(uint16_t* lds, int tid) const {
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const int c = tid + i * NT;
+      if (kChunks % NT == 0 || c < kChunks)
+        *reinterpret_cast<v4u*>(lds + (c / (DI / 8)) * kLd + (c % (DI / 8)) * 8) = r[i];
+    }
+  }
+};
+
 // ---------------------------------------------------------------------------
 // Prefill: scoring fused with the selection.  RT (1 or 2) row tiles of 32 rows
 // per wave, NW waves per workgroup; grid.x = query tiles (latest first),
@@ -287,9 +315,14 @@ __global__ __launch_bounds__(256) void index_score_decode_kernel(
     }
   }
 
-  KTileStage<DI, NT> stage;
-  stage.load(k_idx + kv.block_row(b, koff, b0) * DI, tid);
-  stage.store(lds[0], tid);
+  // two key blocks in flight: while block beta is scored from LDS, block beta+1
+  // (issued one step earlier) and block beta+2 (issued now) are loading.  The
+  // block loop is unrolled over the segment so that every stage index is a
+  // compile-time constant (the stage registers then never touch scratch).
+  KTileRegs<DI, NT> st[2];
+  st[0].load(k_idx + kv.block_row(b, koff, b0) * DI, tid);
+  st[0].store(lds[0], tid);
+  st[1].load(k_idx + kv.block_row(b, koff, min(b0 + 1, b1 - 1)) * DI, tid);
   __syncthreads();
 
   // the four waves' partial maxima of block `blk` (kept in red[it & 1]) -> S
@@ -307,31 +340,36 @@ __global__ __launch_bounds__(256) void index_score_decode_kernel(
     }
   };
 
-  for (int beta = b0; beta < b1; ++beta) {
-    const int it = beta - b0;
-    stage.load(k_idx + kv.block_row(b, koff, min(beta + 1, b1 - 1)) * DI, tid);
-    // finish the previous block's reduction (its partial maxima are complete)
-    if (it > 0) finish(it - 1, beta - 1);
-    const uint16_t* kt_lds = lds[it & 1];
-    f32x16 acc[RT];
 #pragma unroll
-    for (int rt = 0; rt < RT; ++rt) acc[rt] = f32x16{};
+  for (int it = 0; it < SEG; ++it) {
+    const int beta = b0 + it;
+    if (beta < b1) {
+      // stage it&1 held block beta (now in LDS): it takes block beta+2
+      st[it & 1].load(k_idx + kv.block_row(b, koff, min(beta + 2, b1 - 1)) * DI, tid);
+      if (it > 0) finish(it - 1, beta - 1);
+      const uint16_t* kt_lds = lds[it & 1];
+      f32x16 acc[RT];
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      bf16x8 a = as_bf16x8(*reinterpret_cast<const uint4*>(kt_lds + (wave * 32 + col) * LD + ks * 16 + half * 8));
+      for (int rt = 0; rt < RT; ++rt) acc[rt] = f32x16{};
 #pragma unroll
-      for (int rt = 0; rt < RT; ++rt) acc[rt] = mfma32(a, qf[rt][ks], acc[rt]);
+      for (int ks = 0; ks < KS; ++ks) {
+        bf16x8 a = as_bf16x8(
+            *reinterpret_cast<const uint4*>(kt_lds + (wave * 32 + col) * LD + ks * 16 + half * 8));
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) acc[rt] = mfma32(a, qf[rt][ks], acc[rt]);
+      }
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt) {
+        float m = acc[rt][0];
+#pragma unroll
+        for (int i = 1; i < 16; ++i) m = fmaxf(m, acc[rt][i]);
+        m = fmaxf(m, shfl_xor_f(m, 32));
+        if (half == 0) red[it & 1][wave][rt * 32 + col] = m;
+      }
+      // stage (it+1)&1 holds block beta+1
+      if (beta + 1 < b1) st[(it + 1) & 1].store(lds[(it + 1) & 1], tid);
+      __syncthreads();
     }
-#pragma unroll
-    for (int rt = 0; rt < RT; ++rt) {
-      float m = acc[rt][0];
-#pragma unroll
-      for (int i = 1; i < 16; ++i) m = fmaxf(m, acc[rt][i]);
-      m = fmaxf(m, shfl_xor_f(m, 32));
-      if (half == 0) red[it & 1][wave][rt * 32 + col] = m;
-    }
-    stage.store(lds[(it + 1) & 1], tid);
-    __syncthreads();
   }
   finish(b1 - 1 - b0, b1 - 1);
 }
