@@ -20,7 +20,7 @@ __all__ = [
     "make_dims", "workspace_size", "index_select", "build_block_query_lists", "attend",
     "msa_forward", "exported_symbols", "LIB_PATH", "HEADER_PATH", "index_quantize_fp8",
     "index_select_fp8", "Fp8Index", "index_project", "attend_with_mass", "index_kl",
-    "attend_reads_lists",
+    "attend_reads_lists", "Fp8Main", "main_quantize_fp8", "attend_fp8",
 ]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -86,6 +86,10 @@ def load_library(path: str = LIB_PATH):
     lib.msa_build_block_query_lists.argtypes = [DP, P, P, P, P, P, P, SZ, P]
     lib.msa_attend.restype = I32
     lib.msa_attend.argtypes = [DP, P, P, P, P, P, P, P, P, P, P, P, SZ, P]
+    lib.msa_main_quantize_fp8.restype = I32
+    lib.msa_main_quantize_fp8.argtypes = [DP, P, P, P, P, P, P, P, P, P, P, P]
+    lib.msa_attend_fp8.restype = I32
+    lib.msa_attend_fp8.argtypes = [DP, P, P, P, P, P, P, P, P, P, P, P, P, P, P, SZ, P]
     lib.msa_attend_reads_lists.restype = I32
     lib.msa_attend_reads_lists.argtypes = [DP]
     lib.msa_profile_enable.restype = I32
@@ -256,6 +260,80 @@ def index_quantize_fp8(dims, q_idx, k_idx, cu_seqlens_k, fp8: Fp8Index, stream=N
     return fp8
 
 
+def _kv_exp_shape(dims):
+    """Per-block exponents of quantised keys/values: [batch, nb_max, G], or [pages, G]."""
+    G = dims.num_kv_heads
+    return (dims.kv_pages, G) if dims.kv_pages else (dims.batch, nb_max(dims), G)
+
+
+class Fp8Main:
+    """E4M3 codes and E8M0 exponents of the Main Branch's q, k and v for fixed dims."""
+
+    def __init__(self, dims: Dims, device):
+        T, Hq, G, D = dims.total_q, dims.num_q_heads, dims.num_kv_heads, dims.head_dim
+        dev = torch.device(device)
+        self.q8 = torch.empty((T, Hq, D), dtype=torch.uint8, device=dev)
+        self.q_exp = torch.empty((T, Hq), dtype=torch.uint8, device=dev)
+        self.k8 = torch.empty((dims.total_k, G, D), dtype=torch.uint8, device=dev)
+        self.v8 = torch.empty((dims.total_k, G, D), dtype=torch.uint8, device=dev)
+        self.k_exp = torch.empty(_kv_exp_shape(dims), dtype=torch.uint8, device=dev)
+        self.v_exp = torch.empty(_kv_exp_shape(dims), dtype=torch.uint8, device=dev)
+
+
+def _check_fp8_main(dims, f8):
+    T, Hq, G, D = dims.total_q, dims.num_q_heads, dims.num_kv_heads, dims.head_dim
+    _shape(f8.q8, (T, Hq, D), "q8")
+    _shape(f8.q_exp, (T, Hq), "q_exp")
+    _shape(f8.k8, (dims.total_k, G, D), "k8")
+    _shape(f8.v8, (dims.total_k, G, D), "v8")
+    _shape(f8.k_exp, _kv_exp_shape(dims), "k_exp")
+    _shape(f8.v_exp, _kv_exp_shape(dims), "v_exp")
+
+
+def main_quantize_fp8(dims, q, k, v, cu_seqlens_k, f8: Fp8Main, stream=None):
+    """bf16 q / k / v -> E4M3 codes with power-of-two scales (into `f8`).
+
+    Any of q, k, v may be None: that part of `f8` is left as it is.
+    """
+    T, Hq, G, D = dims.total_q, dims.num_q_heads, dims.num_kv_heads, dims.head_dim
+    if q is not None:
+        _shape(q, (T, Hq, D), "q")
+    for name, x in (("k", k), ("v", v)):
+        if x is not None:
+            _shape(x, (dims.total_k, G, D), name)
+    _check_fp8_main(dims, f8)
+    st = load_library().msa_main_quantize_fp8(
+        ctypes.byref(dims), _ptr(q, "q", torch.bfloat16), _ptr(k, "k", torch.bfloat16),
+        _ptr(v, "v", torch.bfloat16), _ptr(cu_seqlens_k, "cu_seqlens_k", torch.int32),
+        _ptr(f8.q8, "q8", torch.uint8), _ptr(f8.q_exp, "q_exp", torch.uint8),
+        _ptr(f8.k8, "k8", torch.uint8), _ptr(f8.k_exp, "k_exp", torch.uint8),
+        _ptr(f8.v8, "v8", torch.uint8), _ptr(f8.v_exp, "v_exp", torch.uint8), _stream(stream))
+    _check(st, "msa_main_quantize_fp8")
+    return f8
+
+
+def attend_fp8(dims, f8: Fp8Main, cu_seqlens_q, cu_seqlens_k, sel, block_offsets, block_entries, out,
+               lse=None, workspace=None, stream=None):
+    """The Main Branch on quantised q, k, v (msa_attend_fp8)."""
+    T, Hq, D = dims.total_q, dims.num_q_heads, dims.head_dim
+    _check_fp8_main(dims, f8)
+    _shape(out, (T, Hq, D), "out")
+    if lse is not None:
+        _shape(lse, (T, Hq), "lse")
+    ws = _workspace(dims, OP_ATTEND, workspace, out.device)
+    st = load_library().msa_attend_fp8(
+        ctypes.byref(dims), _ptr(f8.q8, "q8", torch.uint8), _ptr(f8.q_exp, "q_exp", torch.uint8),
+        _ptr(f8.k8, "k8", torch.uint8), _ptr(f8.k_exp, "k_exp", torch.uint8),
+        _ptr(f8.v8, "v8", torch.uint8), _ptr(f8.v_exp, "v_exp", torch.uint8),
+        _ptr(cu_seqlens_q, "cu_seqlens_q", torch.int32), _ptr(cu_seqlens_k, "cu_seqlens_k", torch.int32),
+        _ptr(sel, "sel", torch.int32), _ptr(block_offsets, "block_offsets", torch.int32),
+        _ptr(block_entries, "block_entries", torch.int32), _ptr(out, "out", torch.bfloat16),
+        _ptr(lse, "lse", torch.float32), _ptr(ws, "workspace"),
+        ctypes.c_size_t(ws.numel() * ws.element_size()), _stream(stream))
+    _check(st, "msa_attend_fp8")
+    return out
+
+
 def index_select_fp8(dims, fp8: Fp8Index, cu_seqlens_q, cu_seqlens_k, sel, sel_score=None,
                      workspace=None, stream=None):
     """Index Branch on the quantised projections (see msa_index_select_fp8)."""
@@ -390,7 +468,7 @@ def attend_reads_lists(dims: Dims) -> bool:
 
 
 def msa_forward(dims: Dims, q, k, v, q_idx, k_idx, cu_seqlens_q, cu_seqlens_k, bufs: Buffers = None,
-                stream=None, fp8: Fp8Index = None) -> Buffers:
+                stream=None, fp8: Fp8Index = None, fp8_main: Fp8Main = None) -> Buffers:
     """The whole hot path: index_select -> build_block_query_lists -> attend.
 
     One workspace serves the three calls (they run in order on one stream).
@@ -398,6 +476,9 @@ def msa_forward(dims: Dims, q, k, v, q_idx, k_idx, cu_seqlens_q, cu_seqlens_k, b
     With `fp8` given, the Index Branch quantises q_idx and k_idx into it and
     selects on the codes (index_quantize_fp8 -> index_select_fp8); k_idx=None
     keeps the key codes already in `fp8` (a quantised index-key cache).
+    With `fp8_main` given, the Main Branch quantises q (and k, v unless they are
+    None: a quantised key/value cache already in `fp8_main`) and attends on the
+    codes (main_quantize_fp8 -> attend_fp8).
     """
     bufs = bufs or Buffers(dims, q.device)
     if fp8 is None:
@@ -410,12 +491,17 @@ def msa_forward(dims: Dims, q, k, v, q_idx, k_idx, cu_seqlens_q, cu_seqlens_k, b
     if attend_reads_lists(dims):
         build_block_query_lists(dims, bufs.sel, cu_seqlens_q, cu_seqlens_k, bufs.offsets,
                                 bufs.entries, bufs.workspace, stream)
-    attend(dims, q, k, v, cu_seqlens_q, cu_seqlens_k, bufs.sel, bufs.offsets, bufs.entries,
-           bufs.out, bufs.lse, bufs.workspace, stream)
+    if fp8_main is None:
+        attend(dims, q, k, v, cu_seqlens_q, cu_seqlens_k, bufs.sel, bufs.offsets, bufs.entries,
+               bufs.out, bufs.lse, bufs.workspace, stream)
+    else:
+        main_quantize_fp8(dims, q, k, v, cu_seqlens_k, fp8_main, stream)
+        attend_fp8(dims, fp8_main, cu_seqlens_q, cu_seqlens_k, bufs.sel, bufs.offsets, bufs.entries,
+                   bufs.out, bufs.lse, bufs.workspace, stream)
     return bufs
 
 
-PROFILE_KERNELS = 12
+PROFILE_KERNELS = 13
 
 
 def profile_enable(on: bool = True):

@@ -21,17 +21,23 @@
 // Partials are laid out [query][group][slot][head-in-group][d], so the
 // heads of one (query, slot) form one contiguous run of HPG * D floats.
 //
+// Q8: the Main Branch's inputs are E4M3 codes with power-of-two scales (one per
+// (query row, head) of q, one per (block, KV head) of k and v); Q fragments
+// and the staged K/V are dequantised on load, exactly, into the same bf16
+// operands, so everything after the loads is the bf16 path.
+//
 // merge_partials_kernel: per (query, head) the log-sum-exp merge of its
 // partials -- M = max m_s, L = sum l_s 2^(m_s - M),
 // out = sum O_s 2^(m_s - M) / L -- which equals one softmax over the union of
 // the selected keys; lse = (M + log2 L) * ln 2.
+#include "fp8_common.h"
 #include "msa_common.h"
 
 namespace msa {
 
 // One 32-row tile's queries: the Q fragments (MFMA B operand, lane <-> query
 // row), the destination partial row (-1 for padding) and the query position.
-template <int D, int HPG>
+template <int D, int HPG, bool Q8>
 struct TileQ {
   static constexpr int KS = D / 16;
   bf16x8 qf[KS];
@@ -42,18 +48,31 @@ struct TileQ {
   // `ent` is the tile's list entry for this lane's query (-1: none).  Every
   // load is issued unconditionally (padding lanes read row 0 and zero it),
   // so the compiler can count outstanding memory operations exactly.
-  __device__ inline void load(const uint16_t* __restrict__ q, int ent, int r0, int r1, int top_k,
-                              int Hq, int G, int g, int hl, int half, int pshift, int spare_row) {
+  __device__ inline void load(const void* __restrict__ q, const uint8_t* __restrict__ qe, int ent,
+                              int r0, int r1, int top_k, int Hq, int G, int g, int hl, int half,
+                              int pshift, int spare_row) {
     const int r = ent >> kEntrySlotBits, slot = ent & ((1 << kEntrySlotBits) - 1);
     ok = ent >= 0 && r >= r0 && r < r1 && slot < top_k;
     drow = ok ? ((((r - r0) * G + g) * top_k + slot) * HPG + hl) : spare_row;
     p = ok ? r + pshift : 0x7fffffff;
-    const uint16_t* qs = q + ((size_t)(ok ? r : 0) * Hq + g * HPG + hl) * D + half * 8;
+    const size_t qrow = (size_t)(ok ? r : 0) * Hq + g * HPG + hl;
+    if constexpr (Q8) {
+      const uint8_t* qs = static_cast<const uint8_t*>(q) + qrow * D + half * 8;
+      const int e = (int)qe[qrow] - 127;
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      uint4 x = *reinterpret_cast<const uint4*>(qs + ks * 16);
-      x = ok ? x : make_uint4(0, 0, 0, 0);
-      qf[ks] = as_bf16x8(x);
+      for (int ks = 0; ks < KS; ++ks) {
+        uint2 x = *reinterpret_cast<const uint2*>(qs + ks * 16);
+        x = ok ? x : make_uint2(0, 0);
+        qf[ks] = as_bf16x8(dequant8_bf16(x, e));
+      }
+    } else {
+      const uint16_t* qs = static_cast<const uint16_t*>(q) + qrow * D + half * 8;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        uint4 x = *reinterpret_cast<const uint4*>(qs + ks * 16);
+        x = ok ? x : make_uint4(0, 0, 0, 0);
+        qf[ks] = as_bf16x8(x);
+      }
     }
   }
 };
@@ -88,10 +107,11 @@ __device__ inline int wave_lower_bound(const int32_t* __restrict__ a, int lo, in
 // One (block, sequence, group) item: stage its K/V block, then attend every
 // gathered query of this pass.  Called by the whole workgroup; every exit is
 // workgroup-uniform.
-template <int D, int HPG>
+template <int D, int HPG, bool Q8>
 __device__ __forceinline__ void attend_item(
-    long long item, const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
-    const uint16_t* __restrict__ v, const int32_t* __restrict__ cu_q,
+    long long item, const void* __restrict__ q, const void* __restrict__ k,
+    const void* __restrict__ v, const uint8_t* __restrict__ qe, const uint8_t* __restrict__ ke,
+    const uint8_t* __restrict__ ve, const int32_t* __restrict__ cu_q,
     const int32_t* __restrict__ cu_k, KvMap kv, int batch, int G, int Hq, int top_k, int nb_max,
     const int32_t* __restrict__ offsets, const int32_t* __restrict__ entries, int r0, int r1,
     int total_q, float scale_log2, float* __restrict__ part_acc, float2* __restrict__ part_ml,
@@ -135,8 +155,8 @@ __device__ __forceinline__ void attend_item(
   // buffers; every load is issued before the current tile's stores (stores
   // share the memory counter on this GPU, so a load issued after them could
   // not be waited for on its own).
-  TileQ<D, HPG> A, B;
-  A.load(q, tile_entry(entries, e0 + wave * QPT + qi, e1), r0, r1, top_k, Hq, G, g, hl, half,
+  TileQ<D, HPG, Q8> A, B;
+  A.load(q, qe, tile_entry(entries, e0 + wave * QPT + qi, e1), r0, r1, top_k, Hq, G, g, hl, half,
          pshift, spare_row);
   int ent_next = tile_entry(entries, e0 + (wave + 4) * QPT + qi, e1);
 
@@ -146,25 +166,53 @@ __device__ __forceinline__ void attend_item(
   //    writes of a wave land on consecutive addresses.
   const int kb = beta * kBlock;
   const size_t row0 = kv.block_row(b, koff, beta);   // first cache row of the block
-  for (int c = tid; c < kBlock * D / 8; c += 256) {
-    const int key = c / (D / 8), dc = c % (D / 8);
-    uint4 kk = make_uint4(0, 0, 0, 0);
-    if (kb + key < lk) kk = *reinterpret_cast<const uint4*>(k + ((row0 + key) * G + g) * D + dc * 8);
-    *reinterpret_cast<uint4*>(Ks + key * LDK + dc * 8) = kk;
-  }
-  for (int c = tid; c < kBlock * D / 8; c += 256) {
-    const int key = c % kBlock, dc = c / kBlock;
-    uint4 vv = make_uint4(0, 0, 0, 0);
-    if (kb + key < lk) vv = *reinterpret_cast<const uint4*>(v + ((row0 + key) * G + g) * D + dc * 8);
-    const uint32_t vw[4] = {vv.x, vv.y, vv.z, vv.w};
+  if constexpr (Q8) {
+    // 16 codes per 16-byte chunk, dequantised with the block's exponents
+    const size_t xi = kv.block_index(b, beta, nb_max) * G + g;
+    const int kexp = (int)ke[xi] - 127, vexp = (int)ve[xi] - 127;
+    const uint8_t* k8 = static_cast<const uint8_t*>(k);
+    const uint8_t* v8 = static_cast<const uint8_t*>(v);
+    for (int c = tid; c < kBlock * D / 16; c += 256) {
+      const int key = c / (D / 16), dc = c % (D / 16);
+      uint4 kk = make_uint4(0, 0, 0, 0);
+      if (kb + key < lk) kk = *reinterpret_cast<const uint4*>(k8 + ((row0 + key) * G + g) * D + dc * 16);
+      *reinterpret_cast<uint4*>(Ks + key * LDK + dc * 16) = dequant8_bf16(make_uint2(kk.x, kk.y), kexp);
+      *reinterpret_cast<uint4*>(Ks + key * LDK + dc * 16 + 8) = dequant8_bf16(make_uint2(kk.z, kk.w), kexp);
+    }
+    for (int c = tid; c < kBlock * D / 16; c += 256) {
+      const int key = c % kBlock, dc = c / kBlock;
+      uint4 vv = make_uint4(0, 0, 0, 0);
+      if (kb + key < lk) vv = *reinterpret_cast<const uint4*>(v8 + ((row0 + key) * G + g) * D + dc * 16);
+      const uint4 lo = dequant8_bf16(make_uint2(vv.x, vv.y), vexp);
+      const uint4 hi = dequant8_bf16(make_uint2(vv.z, vv.w), vexp);
+      const uint32_t vw[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
-      Vt[(dc * 8 + i) * LDV + key] = (uint16_t)(vw[i >> 1] >> (16 * (i & 1)));
+      for (int i = 0; i < 16; ++i)
+        Vt[(dc * 16 + i) * LDV + key] = (uint16_t)(vw[i >> 1] >> (16 * (i & 1)));
+    }
+  } else {
+    const uint16_t* k16 = static_cast<const uint16_t*>(k);
+    const uint16_t* v16 = static_cast<const uint16_t*>(v);
+    for (int c = tid; c < kBlock * D / 8; c += 256) {
+      const int key = c / (D / 8), dc = c % (D / 8);
+      uint4 kk = make_uint4(0, 0, 0, 0);
+      if (kb + key < lk) kk = *reinterpret_cast<const uint4*>(k16 + ((row0 + key) * G + g) * D + dc * 8);
+      *reinterpret_cast<uint4*>(Ks + key * LDK + dc * 8) = kk;
+    }
+    for (int c = tid; c < kBlock * D / 8; c += 256) {
+      const int key = c % kBlock, dc = c / kBlock;
+      uint4 vv = make_uint4(0, 0, 0, 0);
+      if (kb + key < lk) vv = *reinterpret_cast<const uint4*>(v16 + ((row0 + key) * G + g) * D + dc * 8);
+      const uint32_t vw[4] = {vv.x, vv.y, vv.z, vv.w};
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        Vt[(dc * 8 + i) * LDV + key] = (uint16_t)(vw[i >> 1] >> (16 * (i & 1)));
+    }
   }
   __syncthreads();
 
 
-  auto tile = [&](const TileQ<D, HPG>& T) __attribute__((always_inline)) {
+  auto tile = [&](const TileQ<D, HPG, Q8>& T) __attribute__((always_inline)) {
     // The block's K/V fragments do not change across tiles; an opaque zero
     // offset keeps their LDS reads inside the loop instead of letting the
     // compiler hoist all of them into (spilled) registers.
@@ -260,14 +308,14 @@ __device__ __forceinline__ void attend_item(
   for (int t = wave; t < ntiles; t += 8) {
     {
       const int ea = tile_entry(entries, e0 + (t + 8) * QPT + qi, e1);
-      B.load(q, ent_next, r0, r1, top_k, Hq, G, g, hl, half, pshift, spare_row);
+      B.load(q, qe, ent_next, r0, r1, top_k, Hq, G, g, hl, half, pshift, spare_row);
       ent_next = ea;
       tile(A);
     }
     if (t + 4 >= ntiles) break;
     {
       const int ea = tile_entry(entries, e0 + (t + 12) * QPT + qi, e1);
-      A.load(q, ent_next, r0, r1, top_k, Hq, G, g, hl, half, pshift, spare_row);
+      A.load(q, qe, ent_next, r0, r1, top_k, Hq, G, g, hl, half, pshift, spare_row);
       ent_next = ea;
       tile(B);
     }
@@ -278,9 +326,10 @@ __device__ __forceinline__ void attend_item(
 // items_per_wg == 1: one item per workgroup.  items_per_wg in 2..64 (sparse
 // selections, e.g. decode): the workgroup finds which of its items have any
 // query with one coalesced load and processes only those.
-template <int D, int HPG>
+template <int D, int HPG, bool Q8>
 __global__ __launch_bounds__(256, 2) void attend_blocks_kernel(
-    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+    const void* __restrict__ q, const void* __restrict__ k, const void* __restrict__ v,
+    const uint8_t* __restrict__ qe, const uint8_t* __restrict__ ke, const uint8_t* __restrict__ ve,
     const int32_t* __restrict__ cu_q, const int32_t* __restrict__ cu_k, KvMap kv, int batch, int G,
     int Hq, int top_k, int nb_max, const int32_t* __restrict__ offsets,
     const int32_t* __restrict__ entries, int r0, int r1, int total_q, float scale_log2,
@@ -295,7 +344,7 @@ __global__ __launch_bounds__(256, 2) void attend_blocks_kernel(
   const long long n_items = (long long)nb_max * BG;
   const long long first = (long long)blockIdx.x * items_per_wg;
   if (items_per_wg == 1) {
-    attend_item<D, HPG>(first, q, k, v, cu_q, cu_k, kv, batch, G, Hq, top_k, nb_max, offsets,
+    attend_item<D, HPG, Q8>(first, q, k, v, qe, ke, ve, cu_q, cu_k, kv, batch, G, Hq, top_k, nb_max, offsets,
                         entries, r0, r1, total_q, scale_log2, part_acc, part_ml, spare_row, Ks, Vt,
                         range);
     return;
@@ -316,7 +365,7 @@ __global__ __launch_bounds__(256, 2) void attend_blocks_kernel(
   while (m) {
     const int i = __ffsll((long long)m) - 1;
     m &= m - 1;
-    attend_item<D, HPG>(first + i, q, k, v, cu_q, cu_k, kv, batch, G, Hq, top_k, nb_max, offsets,
+    attend_item<D, HPG, Q8>(first + i, q, k, v, qe, ke, ve, cu_q, cu_k, kv, batch, G, Hq, top_k, nb_max, offsets,
                         entries, r0, r1, total_q, scale_log2, part_acc, part_ml, spare_row, Ks, Vt,
                         range);
     __syncthreads();   // LDS and range are reused by the next item
@@ -396,7 +445,8 @@ __global__ __launch_bounds__(kMergeWaves * 64) void merge_partials_kernel(
 
 // ---------------------------------------------------------------------------
 template <int D, int HPG>
-static void launch_attend_t(const void* q, const void* k, const void* v, const int32_t* cu_q,
+static void launch_attend_t(const void* q, const void* k, const void* v, MainFp8 f8,
+                            const int32_t* cu_q,
                             const int32_t* cu_k, KvMap kv, int batch, int G, int Hq, int top_k,
                             int nb_max,
                             const int32_t* offsets, const int32_t* entries, int r0, int r1,
@@ -407,21 +457,26 @@ static void launch_attend_t(const void* q, const void* k, const void* v, const i
   const double per_item = (double)(r1 - r0) * G * top_k / (double)n_items;
   const int ipw = per_item >= 4.0 ? 1 : 64;
   dim3 grid((unsigned)((n_items + ipw - 1) / ipw));
-  hipLaunchKernelGGL((attend_blocks_kernel<D, HPG>), grid, dim3(256), 0, st, (const uint16_t*)q,
-                     (const uint16_t*)k, (const uint16_t*)v, cu_q, cu_k, kv, batch, G, Hq, top_k,
-                     nb_max, offsets, entries, r0, r1, total_q, scale_log2, part_acc, part_ml,
-                     (r1 - r0) * Hq * top_k, ipw);
+  if (f8.qe)
+    hipLaunchKernelGGL((attend_blocks_kernel<D, HPG, true>), grid, dim3(256), 0, st, q, k, v, f8.qe,
+                       f8.ke, f8.ve, cu_q, cu_k, kv, batch, G, Hq, top_k, nb_max, offsets, entries,
+                       r0, r1, total_q, scale_log2, part_acc, part_ml, (r1 - r0) * Hq * top_k, ipw);
+  else
+    hipLaunchKernelGGL((attend_blocks_kernel<D, HPG, false>), grid, dim3(256), 0, st, q, k, v,
+                       (const uint8_t*)nullptr, (const uint8_t*)nullptr, (const uint8_t*)nullptr,
+                       cu_q, cu_k, kv, batch, G, Hq, top_k, nb_max, offsets, entries, r0, r1,
+                       total_q, scale_log2, part_acc, part_ml, (r1 - r0) * Hq * top_k, ipw);
 }
 
 template <int D>
-static hipError_t launch_attend_d(int hpg, const void* q, const void* k, const void* v,
+static hipError_t launch_attend_d(int hpg, const void* q, const void* k, const void* v, MainFp8 f8,
                                   const int32_t* cu_q, const int32_t* cu_k, KvMap kv, int batch,
                                   int G, int Hq,
                                   int top_k, int nb_max, const int32_t* offsets,
                                   const int32_t* entries, int r0, int r1, int total_q,
                                   float scale_log2, float* part_acc, float2* part_ml,
                                   hipStream_t st) {
-#define MSA_ATT(H) launch_attend_t<D, H>(q, k, v, cu_q, cu_k, kv, batch, G, Hq, top_k, nb_max, offsets, entries, r0, r1, total_q, scale_log2, part_acc, part_ml, st)
+#define MSA_ATT(H) launch_attend_t<D, H>(q, k, v, f8, cu_q, cu_k, kv, batch, G, Hq, top_k, nb_max, offsets, entries, r0, r1, total_q, scale_log2, part_acc, part_ml, st)
   switch (hpg) {
     case 1: MSA_ATT(1); break;
     case 2: MSA_ATT(2); break;
@@ -436,15 +491,15 @@ static hipError_t launch_attend_d(int hpg, const void* q, const void* k, const v
 }
 
 hipError_t launch_attend_blocks(int D, int hpg, const void* q, const void* k, const void* v,
-                                const int32_t* cu_q, const int32_t* cu_k, KvMap kv, int batch,
+                                MainFp8 f8, const int32_t* cu_q, const int32_t* cu_k, KvMap kv, int batch,
                                 int G, int Hq, int top_k, int nb_max, const int32_t* offsets,
                                 const int32_t* entries, int r0, int r1, int total_q,
                                 float scale_log2, float* part_acc, float2* part_ml, hipStream_t st) {
   if (D == 64)
-    return launch_attend_d<64>(hpg, q, k, v, cu_q, cu_k, kv, batch, G, Hq, top_k, nb_max, offsets,
+    return launch_attend_d<64>(hpg, q, k, v, f8, cu_q, cu_k, kv, batch, G, Hq, top_k, nb_max, offsets,
                                entries, r0, r1, total_q, scale_log2, part_acc, part_ml, st);
   if (D == 128)
-    return launch_attend_d<128>(hpg, q, k, v, cu_q, cu_k, kv, batch, G, Hq, top_k, nb_max, offsets,
+    return launch_attend_d<128>(hpg, q, k, v, f8, cu_q, cu_k, kv, batch, G, Hq, top_k, nb_max, offsets,
                                 entries, r0, r1, total_q, scale_log2, part_acc, part_ml, st);
   return hipErrorInvalidValue;
 }

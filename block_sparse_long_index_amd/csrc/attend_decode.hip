@@ -9,18 +9,22 @@
 // wave takes one (query, selected slot) straight from the selection and reads
 // that block once.  K goes from global memory straight into MFMA A
 // fragments; V is transposed through a per-wave LDS tile for O^T = V^T * P^T.
-// The tile holds the query's HPG heads as MFMA rows (HPG <= 32).
+// The tile holds the query's HPG heads as MFMA rows (HPG <= 32).  Q8: 8-bit
+// inputs (E4M3 codes with power-of-two scales), dequantised exactly into the
+// same bf16 operands while loading.
+#include "fp8_common.h"
 #include "msa_common.h"
 
 namespace msa {
 
 constexpr int kDecodeWaves = 4;
 
-template <int D, int HPG>
+template <int D, int HPG, bool Q8>
 __global__ __launch_bounds__(kDecodeWaves * 64) void attend_decode_kernel(
-    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+    const void* __restrict__ q, const void* __restrict__ k, const void* __restrict__ v,
+    const uint8_t* __restrict__ qe, const uint8_t* __restrict__ ke, const uint8_t* __restrict__ ve,
     const int32_t* __restrict__ cu_q, const int32_t* __restrict__ cu_k, KvMap kv, int batch, int G,
-    int Hq, int top_k, const int32_t* __restrict__ sel, int r0, float scale_log2,
+    int Hq, int top_k, int nb_max, const int32_t* __restrict__ sel, int r0, float scale_log2,
     float* __restrict__ part_acc, float2* __restrict__ part_ml) {
   constexpr int KS = D / 16;      // k-steps of Q.K over the head dim
   constexpr int DT = D / 32;      // 32-row tiles of O^T
@@ -43,28 +47,63 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void attend_decode_kernel(
   const int kb_safe = active ? kb : 0;
   const size_t row0 = kv.block_row(rp.b, rp.koff, kb_safe >> 7);   // first cache row of the block
 
+  // exponents of the block (8-bit inputs)
+  int kexp = 0, vexp = 0;
+  if constexpr (Q8) {
+    const size_t xi = kv.block_index(rp.b, kb_safe >> 7, nb_max) * G + g;
+    kexp = (int)ke[xi] - 127;
+    vexp = (int)ve[xi] - 127;
+  }
+
   // V^T of the block into this wave's LDS tile (keys past the sequence are zero)
-  for (int c = lane; c < kBlock * D / 8; c += 64) {
-    const int key = c % kBlock, dc = c / kBlock;
-    const bool in = active && kb_safe + key < rp.lk;
-    const size_t row = (row0 + (in ? key : 0)) * G + g;
-    uint4 vv = *reinterpret_cast<const uint4*>(v + row * D + dc * 8);
-    vv = in ? vv : make_uint4(0, 0, 0, 0);
-    const uint32_t vw[4] = {vv.x, vv.y, vv.z, vv.w};
+  if constexpr (Q8) {
+    for (int c = lane; c < kBlock * D / 16; c += 64) {
+      const int key = c % kBlock, dc = c / kBlock;
+      const bool in = active && kb_safe + key < rp.lk;
+      const size_t row = (row0 + (in ? key : 0)) * G + g;
+      uint4 vv = *reinterpret_cast<const uint4*>(static_cast<const uint8_t*>(v) + row * D + dc * 16);
+      vv = in ? vv : make_uint4(0, 0, 0, 0);
+      const uint4 lo = dequant8_bf16(make_uint2(vv.x, vv.y), vexp);
+      const uint4 hi = dequant8_bf16(make_uint2(vv.z, vv.w), vexp);
+      const uint32_t vw[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
-      Vt[(dc * 8 + i) * LDV + key] = (uint16_t)(vw[i >> 1] >> (16 * (i & 1)));
+      for (int i = 0; i < 16; ++i)
+        Vt[(dc * 16 + i) * LDV + key] = (uint16_t)(vw[i >> 1] >> (16 * (i & 1)));
+    }
+  } else {
+    for (int c = lane; c < kBlock * D / 8; c += 64) {
+      const int key = c % kBlock, dc = c / kBlock;
+      const bool in = active && kb_safe + key < rp.lk;
+      const size_t row = (row0 + (in ? key : 0)) * G + g;
+      uint4 vv = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(v) + row * D + dc * 8);
+      vv = in ? vv : make_uint4(0, 0, 0, 0);
+      const uint32_t vw[4] = {vv.x, vv.y, vv.z, vv.w};
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        Vt[(dc * 8 + i) * LDV + key] = (uint16_t)(vw[i >> 1] >> (16 * (i & 1)));
+    }
   }
 
   // Q^T fragments: MFMA column n = head (col) of query r; columns >= HPG are zero
   bf16x8 qf[KS];
   {
     const int hl = col < HPG ? col : 0;
-    const uint16_t* qs = q + ((size_t)r * Hq + g * HPG + hl) * D + half * 8;
+    const size_t qrow = (size_t)r * Hq + g * HPG + hl;
+    if constexpr (Q8) {
+      const uint8_t* qs = static_cast<const uint8_t*>(q) + qrow * D + half * 8;
+      const int e = (int)qe[qrow] - 127;
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      uint4 x = *reinterpret_cast<const uint4*>(qs + ks * 16);
-      qf[ks] = as_bf16x8(col < HPG ? x : make_uint4(0, 0, 0, 0));
+      for (int ks = 0; ks < KS; ++ks) {
+        uint2 x = *reinterpret_cast<const uint2*>(qs + ks * 16);
+        qf[ks] = as_bf16x8(dequant8_bf16(col < HPG ? x : make_uint2(0, 0), e));
+      }
+    } else {
+      const uint16_t* qs = static_cast<const uint16_t*>(q) + qrow * D + half * 8;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        uint4 x = *reinterpret_cast<const uint4*>(qs + ks * 16);
+        qf[ks] = as_bf16x8(col < HPG ? x : make_uint4(0, 0, 0, 0));
+      }
     }
   }
 
@@ -74,12 +113,22 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void attend_decode_kernel(
   for (int kt = 0; kt < 4; ++kt) {
     const int key = kb_safe + kt * 32 + col;
     const bool in = active && key < rp.lk;
-    const uint16_t* ks_ptr = k + ((row0 + (in ? key - kb_safe : 0)) * G + g) * D + half * 8;
+    const size_t krow = (row0 + (in ? key - kb_safe : 0)) * G + g;
     bf16x8 a[KS];
+    if constexpr (Q8) {
+      const uint8_t* ks_ptr = static_cast<const uint8_t*>(k) + krow * D + half * 8;
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      uint4 x = *reinterpret_cast<const uint4*>(ks_ptr + ks * 16);
-      a[ks] = as_bf16x8(in ? x : make_uint4(0, 0, 0, 0));
+      for (int ks = 0; ks < KS; ++ks) {
+        uint2 x = *reinterpret_cast<const uint2*>(ks_ptr + ks * 16);
+        a[ks] = as_bf16x8(dequant8_bf16(in ? x : make_uint2(0, 0), kexp));
+      }
+    } else {
+      const uint16_t* ks_ptr = static_cast<const uint16_t*>(k) + krow * D + half * 8;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        uint4 x = *reinterpret_cast<const uint4*>(ks_ptr + ks * 16);
+        a[ks] = as_bf16x8(in ? x : make_uint4(0, 0, 0, 0));
+      }
     }
     sacc[kt] = f32x16{};
 #pragma unroll
@@ -153,23 +202,29 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void attend_decode_kernel(
 }
 
 template <int D, int HPG>
-static void launch_decode_t(const void* q, const void* k, const void* v, const int32_t* cu_q,
-                            const int32_t* cu_k, KvMap kv, int batch, int G, int Hq, int top_k,
-                            const int32_t* sel, int r0, int r1, float scale_log2, float* part_acc,
-                            float2* part_ml, hipStream_t st) {
+static void launch_decode_t(const void* q, const void* k, const void* v, MainFp8 f8,
+                            const int32_t* cu_q, const int32_t* cu_k, KvMap kv, int batch, int G,
+                            int Hq, int top_k, int nb_max, const int32_t* sel, int r0, int r1,
+                            float scale_log2, float* part_acc, float2* part_ml, hipStream_t st) {
   dim3 grid(r1 - r0, (top_k + kDecodeWaves - 1) / kDecodeWaves, G);
-  hipLaunchKernelGGL((attend_decode_kernel<D, HPG>), grid, dim3(kDecodeWaves * 64), 0, st,
-                     (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, cu_q, cu_k, kv, batch,
-                     G, Hq, top_k, sel, r0, scale_log2, part_acc, part_ml);
+  if (f8.qe)
+    hipLaunchKernelGGL((attend_decode_kernel<D, HPG, true>), grid, dim3(kDecodeWaves * 64), 0, st, q,
+                       k, v, f8.qe, f8.ke, f8.ve, cu_q, cu_k, kv, batch, G, Hq, top_k, nb_max, sel,
+                       r0, scale_log2, part_acc, part_ml);
+  else
+    hipLaunchKernelGGL((attend_decode_kernel<D, HPG, false>), grid, dim3(kDecodeWaves * 64), 0, st,
+                       q, k, v, (const uint8_t*)nullptr, (const uint8_t*)nullptr,
+                       (const uint8_t*)nullptr, cu_q, cu_k, kv, batch, G, Hq, top_k, nb_max, sel, r0,
+                       scale_log2, part_acc, part_ml);
 }
 
 template <int D>
-static hipError_t launch_decode_d(int hpg, const void* q, const void* k, const void* v,
+static hipError_t launch_decode_d(int hpg, const void* q, const void* k, const void* v, MainFp8 f8,
                                   const int32_t* cu_q, const int32_t* cu_k, KvMap kv, int batch,
-                                  int G, int Hq,
-                                  int top_k, const int32_t* sel, int r0, int r1, float scale_log2,
-                                  float* part_acc, float2* part_ml, hipStream_t st) {
-#define MSA_DEC(H) launch_decode_t<D, H>(q, k, v, cu_q, cu_k, kv, batch, G, Hq, top_k, sel, r0, r1, scale_log2, part_acc, part_ml, st)
+                                  int G, int Hq, int top_k, int nb_max, const int32_t* sel, int r0,
+                                  int r1, float scale_log2, float* part_acc, float2* part_ml,
+                                  hipStream_t st) {
+#define MSA_DEC(H) launch_decode_t<D, H>(q, k, v, f8, cu_q, cu_k, kv, batch, G, Hq, top_k, nb_max, sel, r0, r1, scale_log2, part_acc, part_ml, st)
   switch (hpg) {
     case 1: MSA_DEC(1); break;
     case 2: MSA_DEC(2); break;
@@ -184,16 +239,16 @@ static hipError_t launch_decode_d(int hpg, const void* q, const void* k, const v
 }
 
 hipError_t launch_attend_decode(int D, int hpg, const void* q, const void* k, const void* v,
-                                const int32_t* cu_q, const int32_t* cu_k, KvMap kv, int batch,
-                                int G, int Hq, int top_k, const int32_t* sel, int r0, int r1,
-                                float scale_log2, float* part_acc, float2* part_ml,
+                                MainFp8 f8, const int32_t* cu_q, const int32_t* cu_k, KvMap kv,
+                                int batch, int G, int Hq, int top_k, int nb_max, const int32_t* sel,
+                                int r0, int r1, float scale_log2, float* part_acc, float2* part_ml,
                                 hipStream_t st) {
   if (D == 64)
-    return launch_decode_d<64>(hpg, q, k, v, cu_q, cu_k, kv, batch, G, Hq, top_k, sel, r0, r1,
-                               scale_log2, part_acc, part_ml, st);
+    return launch_decode_d<64>(hpg, q, k, v, f8, cu_q, cu_k, kv, batch, G, Hq, top_k, nb_max, sel,
+                               r0, r1, scale_log2, part_acc, part_ml, st);
   if (D == 128)
-    return launch_decode_d<128>(hpg, q, k, v, cu_q, cu_k, kv, batch, G, Hq, top_k, sel, r0, r1,
-                                scale_log2, part_acc, part_ml, st);
+    return launch_decode_d<128>(hpg, q, k, v, f8, cu_q, cu_k, kv, batch, G, Hq, top_k, nb_max, sel,
+                                r0, r1, scale_log2, part_acc, part_ml, st);
   return hipErrorInvalidValue;
 }
 

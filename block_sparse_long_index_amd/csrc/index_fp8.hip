@@ -16,6 +16,7 @@
 // max_j (2^eq q8 . 2^ek k8_j) = 2^(eq + ek) max_j (q8 . k8_j): the kernels
 // contract raw codes on the fp8 MFMA and apply the two exponents once per
 // (row, block), exactly (ldexp).
+#include "fp8_common.h"
 #include "msa_common.h"
 #include "topk_common.h"
 
@@ -36,70 +37,6 @@ __device__ inline i32x8 as_i32x8(uint4 lo, uint4 hi) {
   r[0] = (int)lo.x; r[1] = (int)lo.y; r[2] = (int)lo.z; r[3] = (int)lo.w;
   r[4] = (int)hi.x; r[5] = (int)hi.y; r[6] = (int)hi.z; r[7] = (int)hi.w;
   return r;
-}
-
-// Smallest e with amax * 2^-e <= 448 (the largest E4M3 value), clamped to
-// [-127, 127]; 0 for amax == 0.  amax = f * 2^E with f in [0.5, 1):
-// f * 2^9 <= 448 exactly when f <= 0.875.
-__device__ inline int fp8_scale_exponent(float amax) {
-  if (amax == 0.f) return 0;
-  int E;
-  const float f = frexpf(amax, &E);
-  const int e = f <= 0.875f ? E - 9 : E - 8;
-  return min(127, max(-127, e));
-}
-
-// Eight bf16 values -> eight E4M3 codes of x * 2^-e (exact scaling, then one
-// round-to-nearest-even conversion), little-endian in two dwords.
-__device__ inline uint2 quantize8(const float (&x)[8], int e) {
-  float y[8];
-#pragma unroll
-  for (int i = 0; i < 8; ++i) y[i] = fminf(448.f, fmaxf(-448.f, ldexpf(x[i], -e)));
-  int w0 = __builtin_amdgcn_cvt_pk_fp8_f32(y[0], y[1], 0, false);
-  w0 = __builtin_amdgcn_cvt_pk_fp8_f32(y[2], y[3], w0, true);
-  int w1 = __builtin_amdgcn_cvt_pk_fp8_f32(y[4], y[5], 0, false);
-  w1 = __builtin_amdgcn_cvt_pk_fp8_f32(y[6], y[7], w1, true);
-  return make_uint2((uint32_t)w0, (uint32_t)w1);
-}
-
-__device__ inline void unpack8_bf16(uint4 v, float (&x)[8]) {
-  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    x[2 * i] = __uint_as_float(w[i] << 16);
-    x[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
-  }
-}
-
-// ---------------------------------------------------------------------------
-// Quantisation.  q rows: DI / 8 lanes per (query, group) row, each converting
-// 8 elements; the row maximum is a shuffle reduction inside the row's lanes.
-// ---------------------------------------------------------------------------
-template <int DI>
-__global__ __launch_bounds__(256) void quantize_q_kernel(const uint16_t* __restrict__ q,
-                                                         long long rows,
-                                                         uint8_t* __restrict__ q8,
-                                                         uint8_t* __restrict__ qe) {
-  constexpr int LPR = DI / 8;
-  const long long t = (long long)blockIdx.x * 256 + threadIdx.x;
-  const long long row = t / LPR;
-  const int c = (int)(t % LPR);
-  const bool ok = row < rows;
-  uint4 v = make_uint4(0, 0, 0, 0);
-  if (ok) v = *reinterpret_cast<const uint4*>(q + row * DI + c * 8);
-  float x[8];
-  unpack8_bf16(v, x);
-  float a = 0.f;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) a = fmaxf(a, fabsf(x[i]));
-#pragma unroll
-  for (int off = LPR / 2; off >= 1; off >>= 1) a = fmaxf(a, shfl_xor_f(a, off));
-  const int e = fp8_scale_exponent(a);
-  const uint2 w = quantize8(x, e);
-  if (ok) {
-    *reinterpret_cast<uint2*>(q8 + row * DI + c * 8) = w;
-    if (c == 0) qe[row] = (uint8_t)(e + 127);
-  }
 }
 
 // k blocks: one workgroup per (block beta, sequence b); block maximum over the

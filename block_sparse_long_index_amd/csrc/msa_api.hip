@@ -25,12 +25,16 @@ size_t lists_workspace_bytes(int batch, int G, int nqt_max, int nb_max);
 int list_tile_rows();
 hipError_t launch_build_lists(const int32_t*, const int32_t*, const int32_t*, int, int, int, int,
                               int, int32_t*, int32_t*, void*, hipStream_t);
-hipError_t launch_attend_blocks(int, int, const void*, const void*, const void*, const int32_t*,
-                                const int32_t*, KvMap, int, int, int, int, int, const int32_t*,
-                                const int32_t*, int, int, int, float, float*, float2*, hipStream_t);
-hipError_t launch_attend_decode(int, int, const void*, const void*, const void*, const int32_t*,
-                                const int32_t*, KvMap, int, int, int, int, const int32_t*, int, int,
-                                float, float*, float2*, hipStream_t);
+hipError_t launch_attend_blocks(int, int, const void*, const void*, const void*, MainFp8,
+                                const int32_t*, const int32_t*, KvMap, int, int, int, int, int,
+                                const int32_t*, const int32_t*, int, int, int, float, float*, float2*,
+                                hipStream_t);
+hipError_t launch_attend_decode(int, int, const void*, const void*, const void*, MainFp8,
+                                const int32_t*, const int32_t*, KvMap, int, int, int, int, int,
+                                const int32_t*, int, int, float, float*, float2*, hipStream_t);
+hipError_t launch_main_quantize_fp8(int, const void*, const void*, const void*, const int32_t*, KvMap,
+                                    int, int, int, long long, void*, uint8_t*, void*, uint8_t*,
+                                    void*, uint8_t*, hipStream_t);
 hipError_t launch_merge(int, const float*, const float2*, const int32_t*, int, int, int, int, int,
                         void*, float*, hipStream_t);
 int fp8_max_blocks_per_sequence();
@@ -194,12 +198,12 @@ bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 // recorded on the launch stream; msa_profile_collect() waits for them.
 enum KernelId { K_INDEX_PREFILL, K_INDEX_DECODE, K_TOPK, K_LISTS, K_ATTEND, K_MERGE,
                 K_QUANT_FP8, K_INDEX_PREFILL_FP8, K_INDEX_DECODE_FP8, K_PROJECT, K_MASS,
-                K_INDEX_KL };
+                K_INDEX_KL, K_QUANT_MAIN_FP8 };
 const char* const kKernelNames[MSA_PROFILE_KERNELS] = {
     "index_select_prefill", "index_score_decode", "topk_select",
     "build_lists", "attend_blocks", "merge_partials",
     "quantize_index_fp8", "index_select_prefill_fp8", "index_score_decode_fp8",
-    "index_project", "block_mass", "index_kl"};
+    "index_project", "block_mass", "index_kl", "quantize_main_fp8"};
 
 std::atomic<bool> g_prof_on{false};
 std::mutex g_prof_mu;
@@ -453,7 +457,7 @@ int32_t msa_attend_reads_lists(const msa_dims_t* dims) {
 }
 
 static msa_status_t attend_impl(const msa_dims_t* dims, const void* q, const void* k,
-                                const void* v, const int32_t* cu_seqlens_q,
+                                const void* v, msa::MainFp8 f8, const int32_t* cu_seqlens_q,
                                 const int32_t* cu_seqlens_k, const int32_t* sel,
                                 const int32_t* block_offsets, const int32_t* block_entries,
                                 void* out, float* lse, float* block_mass, void* workspace,
@@ -464,7 +468,8 @@ static msa_status_t attend_impl(const msa_dims_t* dims, const void* q, const voi
   if (x.total_q == 0) return MSA_OK;   // no queries: no output
   const bool lists = reads_lists(dims);
   if (!q || !k || !v || !cu_seqlens_q || !cu_seqlens_k || !sel || !out || !workspace ||
-      (lists && (!block_offsets || !block_entries)))
+      (lists && (!block_offsets || !block_entries)) ||
+      (f8.qe != nullptr) != (f8.ke != nullptr) || (f8.qe != nullptr) != (f8.ve != nullptr))
     return fail(MSA_ERR_NULL_ARG, "a required pointer is NULL");
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(sel) || !aligned16(out) ||
       !aligned16(workspace) || (lists && (!aligned16(block_offsets) || !aligned16(block_entries))) ||
@@ -486,11 +491,11 @@ static msa_status_t attend_impl(const msa_dims_t* dims, const void* q, const voi
       if (!lists)
         // a few queries per sequence: each selected block is hit by few queries;
         // one wave per (query, slot) reads it straight from the selection
-        e = msa::launch_attend_decode(x.D, x.hpg, q, k, v, cu_seqlens_q, cu_seqlens_k, x.kv, dims->batch,
-                                      x.G, x.Hq, x.top_k, sel, a, z, scale_log2, part_acc, part_ml,
-                                      st);
+        e = msa::launch_attend_decode(x.D, x.hpg, q, k, v, f8, cu_seqlens_q, cu_seqlens_k, x.kv,
+                                      dims->batch, x.G, x.Hq, x.top_k, x.nb_max, sel, a, z,
+                                      scale_log2, part_acc, part_ml, st);
       else
-        e = msa::launch_attend_blocks(x.D, x.hpg, q, k, v, cu_seqlens_q, cu_seqlens_k, x.kv,
+        e = msa::launch_attend_blocks(x.D, x.hpg, q, k, v, f8, cu_seqlens_q, cu_seqlens_k, x.kv,
                                       dims->batch, x.G, x.Hq, x.top_k, x.nb_max, block_offsets,
                                       block_entries, a, z, (int)x.total_q, scale_log2, part_acc,
                                       part_ml, st);
@@ -515,8 +520,48 @@ msa_status_t msa_attend(const msa_dims_t* dims, const void* q, const void* k, co
                         const int32_t* sel, const int32_t* block_offsets,
                         const int32_t* block_entries, void* out, float* lse, void* workspace,
                         size_t workspace_bytes, void* stream) {
-  return attend_impl(dims, q, k, v, cu_seqlens_q, cu_seqlens_k, sel, block_offsets, block_entries,
-                     out, lse, nullptr, workspace, workspace_bytes, stream);
+  return attend_impl(dims, q, k, v, msa::MainFp8{nullptr, nullptr, nullptr}, cu_seqlens_q,
+                     cu_seqlens_k, sel, block_offsets, block_entries, out, lse, nullptr, workspace,
+                     workspace_bytes, stream);
+}
+
+msa_status_t msa_attend_fp8(const msa_dims_t* dims, const void* q8, const uint8_t* q_exp,
+                            const void* k8, const uint8_t* k_exp, const void* v8,
+                            const uint8_t* v_exp, const int32_t* cu_seqlens_q,
+                            const int32_t* cu_seqlens_k, const int32_t* sel,
+                            const int32_t* block_offsets, const int32_t* block_entries, void* out,
+                            float* lse, void* workspace, size_t workspace_bytes, void* stream) {
+  if (dims && dims->total_q > 0 && (!q_exp || !k_exp || !v_exp))
+    return fail(MSA_ERR_NULL_ARG, "a required pointer is NULL");
+  return attend_impl(dims, q8, k8, v8, msa::MainFp8{q_exp, k_exp, v_exp}, cu_seqlens_q,
+                     cu_seqlens_k, sel, block_offsets, block_entries, out, lse, nullptr, workspace,
+                     workspace_bytes, stream);
+}
+
+msa_status_t msa_main_quantize_fp8(const msa_dims_t* dims, const void* q, const void* k,
+                                   const void* v, const int32_t* cu_seqlens_k, void* q8,
+                                   uint8_t* q_exp, void* k8, uint8_t* k_exp, void* v8,
+                                   uint8_t* v_exp, void* stream) {
+  Derived x;
+  msa_status_t s = check_dims(dims, &x);
+  if (s != MSA_OK) return s;
+  // any of q, k, v may be left out (NULL input): a decode step quantises its new
+  // queries against a key/value cache quantised when it was written
+  const bool has_q = x.total_q > 0 && q, has_kv = dims->total_k > 0;
+  const bool has_k = has_kv && k, has_v = has_kv && v;
+  if ((has_q && (!q8 || !q_exp)) || ((has_k || has_v) && !cu_seqlens_k) ||
+      (has_k && (!k8 || !k_exp)) || (has_v && (!v8 || !v_exp)))
+    return fail(MSA_ERR_NULL_ARG, "a required pointer is NULL");
+  if ((has_q && (!aligned16(q) || !aligned16(q8))) || (has_k && (!aligned16(k) || !aligned16(k8))) ||
+      (has_v && (!aligned16(v) || !aligned16(v8))))
+    return fail(MSA_ERR_ALIGNMENT, "tensor pointers must be 16-byte aligned");
+  if (!has_q && !has_k && !has_v) return MSA_OK;
+  hipStream_t st = (hipStream_t)stream;
+  ProfScope ps(K_QUANT_MAIN_FP8, st);
+  hipError_t e = msa::launch_main_quantize_fp8(
+      x.D, has_q ? q : nullptr, has_k ? k : nullptr, has_v ? v : nullptr, cu_seqlens_k, x.kv,
+      dims->batch, x.G, x.nb_max, has_q ? x.total_q * x.Hq : 0, q8, q_exp, k8, k_exp, v8, v_exp, st);
+  return e == hipSuccess ? MSA_OK : hip_fail(e);
 }
 
 msa_status_t msa_attend_with_mass(const msa_dims_t* dims, const void* q, const void* k,
@@ -529,8 +574,9 @@ msa_status_t msa_attend_with_mass(const msa_dims_t* dims, const void* q, const v
     return fail(MSA_ERR_NULL_ARG, "block_mass is NULL");
   if (block_mass && !aligned16(block_mass))
     return fail(MSA_ERR_ALIGNMENT, "tensor pointers must be 16-byte aligned");
-  return attend_impl(dims, q, k, v, cu_seqlens_q, cu_seqlens_k, sel, block_offsets, block_entries,
-                     out, lse, block_mass, workspace, workspace_bytes, stream);
+  return attend_impl(dims, q, k, v, msa::MainFp8{nullptr, nullptr, nullptr}, cu_seqlens_q,
+                     cu_seqlens_k, sel, block_offsets, block_entries, out, lse, block_mass,
+                     workspace, workspace_bytes, stream);
 }
 
 msa_status_t msa_index_kl(const msa_dims_t* dims, const void* q_idx, const void* k_idx,

@@ -28,6 +28,14 @@ struct RowPos {
 // Contiguous: sequence b owns rows cu_k[b] .. cu_k[b+1]-1.  Paged: block beta
 // of sequence b is page table[b * max_blocks + beta], i.e. rows
 // 128 * page .. 128 * page + 127 of the cache.
+// E8M0 exponents of a quantised Main Branch's inputs (q per (row, head); k and
+// v per (block index, KV head)); all null for bf16 inputs.
+struct MainFp8 {
+  const uint8_t* qe;
+  const uint8_t* ke;
+  const uint8_t* ve;
+};
+
 struct KvMap {
   const int32_t* table;   // nullptr: contiguous rows
   int max_blocks;         // row stride of the page table

@@ -308,7 +308,46 @@ msa_status_t msa_index_kl(const msa_dims_t* dims, const void* q_idx, const void*
                           const int32_t* sel, const float* sel_score, const float* block_mass,
                           float* log_q, float* kl, void* stream);
 
-/* 1 if msa_attend / msa_attend_with_mass read block_offsets and
+/*
+ * Quantised Main Branch (optional; msa_attend is the reference path).  The
+ * pages note that the production model runs the Main Branch, like the
+ * indexer, with 8-bit queries and 8-bit keys/values (dot-ai.myuuu.co.jp
+ * article on MiniMax M3.1 Flash, section "MiniMax M3.1 Flashとは？428Bの
+ * MoEモデルがウェイト公開", on the model card's quantisation notes: "Q8KV8").
+ * Format and scale rule as for msa_index_quantize_fp8 (OCP E4M3 codes,
+ * E8M0 power-of-two scales, smallest exponent e with max|x| * 2^-e <= 448,
+ * round to nearest even); granularity (this library's reading): one scale
+ * per (query row, head) of q, one per (sequence block, KV head) of k and v.
+ *
+ * msa_main_quantize_fp8: bf16 q / k / v -> codes + exponents.  Any of q, k, v
+ *   may be NULL (its outputs are then not touched): a decode step quantises
+ *   its new queries against a key/value cache quantised when written.
+ *   q     bf16 [total_q, num_q_heads, head_dim]   or NULL
+ *   k, v  bf16 [total_k, num_kv_heads, head_dim]  or NULL
+ *   q8    uint8 E4M3 [total_q, num_q_heads, head_dim]  out
+ *   q_exp uint8 E8M0 [total_q, num_q_heads]             out (no alignment needed)
+ *   k8, v8 uint8 E4M3 [total_k, num_kv_heads, head_dim]  out
+ *   k_exp, v_exp uint8 E8M0 [batch, nb_max, num_kv_heads] out, nb_max =
+ *          ceil(max_k_len / 128); blocks past a sequence's end get 127.
+ *          Paged cache: [kv_pages, num_kv_heads], one per (page, head), and
+ *          only the pages of the sequences' blocks are written.
+ * msa_attend_fp8: msa_attend on the dequantised values (the same exact
+ *   softmax over the selected blocks; the codes are dequantised exactly into
+ *   bf16 operands while loading, so the arithmetic is msa_attend's).  Same
+ *   selection, lists, outputs, workspace and routing as msa_attend.
+ */
+msa_status_t msa_main_quantize_fp8(const msa_dims_t* dims, const void* q, const void* k,
+                                   const void* v, const int32_t* cu_seqlens_k, void* q8,
+                                   uint8_t* q_exp, void* k8, uint8_t* k_exp, void* v8,
+                                   uint8_t* v_exp, void* stream);
+msa_status_t msa_attend_fp8(const msa_dims_t* dims, const void* q8, const uint8_t* q_exp,
+                            const void* k8, const uint8_t* k_exp, const void* v8,
+                            const uint8_t* v_exp, const int32_t* cu_seqlens_q,
+                            const int32_t* cu_seqlens_k, const int32_t* sel,
+                            const int32_t* block_offsets, const int32_t* block_entries, void* out,
+                            float* lse, void* workspace, size_t workspace_bytes, void* stream);
+
+/* 1 if msa_attend / msa_attend_with_mass / msa_attend_fp8 read block_offsets and
  * block_entries for these dims, 0 if they work from sel alone (decode-shaped
  * steps), a negative msa_status_t for invalid dims. */
 int32_t msa_attend_reads_lists(const msa_dims_t* dims);
@@ -329,13 +368,13 @@ int32_t msa_abi_version(void);
  * 1 index_score_decode, 2 topk_select, 3 build_lists (all list kernels),
  * 4 attend_blocks, 5 merge_partials, 6 quantize_index_fp8,
  * 7 index_select_prefill_fp8, 8 index_score_decode_fp8, 9 index_project, 10 block_mass,
- * 11 index_kl.  msa_profile_collect() waits for every
+ * 11 index_kl, 12 quantize_main_fp8.  msa_profile_collect() waits for every
  * recorded event (it blocks the host), writes the summed milliseconds and the
  * launch count per stage into caller arrays of MSA_PROFILE_KERNELS entries,
  * and forgets the records.  Events are host-side HIP objects kept in a pool
  * for the life of the process; no device memory is allocated.
  */
-#define MSA_PROFILE_KERNELS 12
+#define MSA_PROFILE_KERNELS 13
 msa_status_t msa_profile_enable(int32_t enable);
 msa_status_t msa_profile_collect(float* total_ms, int32_t* launches);
 const char* msa_profile_kernel_name(int32_t id);

@@ -245,3 +245,27 @@ def test_attend_reads_lists_only_beyond_decode_shapes():
     assert at(ctypes.byref(d), ok, ok, ok, ok, ok, ok, None, ok, ok, None, ok, big, None) == 1
     dd = _dims(batch=32, total_q=32, max_q_len=1, total_k=32 * 4096, max_k_len=4096)
     assert at(ctypes.byref(dd), ok, ok, ok, ok, ok, ok, None, None, P(0x10004), None, ok, big, None) == 4
+
+
+def test_fp8_main_entry_points_validate_on_host():
+    d = _dims()
+    P = ctypes.c_void_p
+    ok = P(0x10000)
+    odd = P(0x10004)
+    big = ctypes.c_size_t(1 << 40)
+    qz = lib.msa_main_quantize_fp8
+    # q given without its outputs; k without cu_seqlens_k
+    assert qz(ctypes.byref(d), ok, None, None, None, None, None, None, None, None, None, None) == 1
+    assert qz(ctypes.byref(d), None, ok, None, None, None, None, ok, ok, None, None, None) == 1
+    assert qz(ctypes.byref(d), None, None, ok, ok, None, None, None, None, odd, ok, None) == 4
+    assert qz(ctypes.byref(d), None, None, None, None, None, None, None, None, None, None, None) == 0
+    at = lib.msa_attend_fp8
+    # exponents are required; lists as for msa_attend
+    assert at(ctypes.byref(d), ok, None, ok, ok, ok, ok, ok, ok, ok, ok, ok, ok, None, ok, big, None) == 1
+    assert at(ctypes.byref(d), ok, ok, ok, ok, ok, ok, ok, ok, ok, None, ok, ok, None, ok, big, None) == 1
+    assert at(ctypes.byref(d), odd, ok, ok, ok, ok, ok, ok, ok, ok, ok, ok, ok, None, ok, big, None) == 4
+    assert at(ctypes.byref(d), ok, ok, ok, ok, ok, ok, ok, ok, ok, ok, ok, ok, None, ok,
+              ctypes.c_size_t(1), None) == 5
+    empty = _dims(total_q=0, max_q_len=0)
+    assert at(ctypes.byref(empty), None, None, None, None, None, None, None, None, None, None, None,
+              None, None, None, 0, None) == 0
