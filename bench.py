@@ -92,7 +92,17 @@ def work_model(w) -> dict:
                         + T * (Hq * d * 2 * 2 + G * (di + 1)))
     index_decode_fp8_bytes = dec_kidx_tokens * di + T * G * (di + 1)
     index_decode_bytes = dec_kidx_tokens * di * 2 + T * G * di * 2
+    # 8-bit Main Branch: one byte per q / k / v element (+ one exponent per (row, head) and
+    # per (block, KV head)); the fp32 partials are unchanged
+    kv_once_fp8 = kv_blocks * (BLOCK * d + 1) * 2
+    attend_bytes_fp8 = sel_total * hpg * (d + 1) + part_write + kv_once_fp8
+    main_quant_bytes = (T * Hq * d + 2 * w.total_k * G * d) * 3 + T * Hq + 2 * nblk * G
+    if _decode_like(w):         # a decode step quantises only its new queries
+        main_quant_bytes = T * Hq * d * 3 + T * Hq
+    decode_kv_fp8_delta = kv_once_fp8 - kv_once + T * Hq * (d + 1 - 2 * d)
     return dict(index_flops=idx_flops, main_flops=main_flops, sel_total=sel_total,
+                attend_bytes_fp8=attend_bytes_fp8, main_quant_bytes=main_quant_bytes,
+                decode_kv_fp8_delta=decode_kv_fp8_delta,
                 attend_bytes=attend_bytes, merge_bytes=merge_bytes, topk_bytes=topk_bytes,
                 decode_bytes=decode_bytes, kv_once_bytes=kv_once, quant_bytes=quant_bytes,
                 decode_fp8_bytes=decode_fp8_bytes, index_decode_fp8_bytes=index_decode_fp8_bytes,
@@ -340,6 +350,10 @@ def main():
     ap.add_argument("--index", choices=["bf16", "fp8"], default="bf16",
                     help="Index Branch precision: bf16 projections, or quantised in the step to "
                          "FP8 E4M3 with power-of-two scales and scored on the fp8 matrix cores")
+    ap.add_argument("--main", choices=["bf16", "fp8"], default="bf16",
+                    help="Main Branch inputs: bf16 q/k/v, or FP8 E4M3 codes with power-of-two "
+                         "scales (quantised in the step; a decode step's key/value cache is "
+                         "stored quantised and only its new queries are quantised)")
     ap.add_argument("--project-dim", type=int, default=0,
                     help="also run the index projections in the step: q_idx and the new tokens' "
                          "k_idx from a layer input of this width (0: off; the index projections "
@@ -355,8 +369,8 @@ def main():
                          "kernels are short enough for launch gaps to matter)")
     args = ap.parse_args()
 
-    if args.kl and args.index != "bf16":
-        print("--kl uses the bf16 index branch", file=sys.stderr)
+    if args.kl and (args.index != "bf16" or args.main != "bf16"):
+        print("--kl uses the bf16 index and Main branches", file=sys.stderr)
         sys.exit(2)
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); this build has no "
@@ -422,6 +436,15 @@ def main():
         torch.cuda.synchronize()
         step_k_idx = None
 
+    # fp8 Main Branch: prefill quantises q, k, v in the step; decode keeps a quantised K/V
+    # cache (quantised once, outside the step) and quantises its new queries
+    f8m = msa.Fp8Main(dims, dev) if args.main == "fp8" else None
+    step_k, step_v = kc, vc
+    if f8m is not None and _decode_like(w):
+        msa.main_quantize_fp8(dims, None, kc, vc, t["cu_seqlens_k"], f8m)
+        torch.cuda.synchronize()
+        step_k = step_v = None
+
     proj = None
     if args.project_dim:
         from msa_inputs import generate_projection
@@ -435,8 +458,8 @@ def main():
             msa.index_project(dims, proj["x"], proj["w_q"], proj["w_k"], t["cu_seqlens_q"],
                               t["cu_seqlens_k"], t["q_idx"], kic, bufs.workspace)
         if kl_out is None:
-            msa.msa_forward(dims, t["q"], kc, vc, t["q_idx"], step_k_idx, t["cu_seqlens_q"],
-                            t["cu_seqlens_k"], bufs, fp8=fp8)
+            msa.msa_forward(dims, t["q"], step_k, step_v, t["q_idx"], step_k_idx, t["cu_seqlens_q"],
+                            t["cu_seqlens_k"], bufs, fp8=fp8, fp8_main=f8m)
             return
         # the forward with the KL-alignment target (bf16 index branch)
         msa.index_select(dims, t["q_idx"], kic, t["cu_seqlens_q"], t["cu_seqlens_k"],
@@ -514,7 +537,8 @@ def main():
             return None
         rec = json.load(open(path))
         src = open(os.path.join(ROOT, rec["source"]), "rb").read()
-        if hashlib.sha256(src).hexdigest() != rec["source_sha256"] or args.q_chunk:
+        if hashlib.sha256(src).hexdigest() != rec["source_sha256"] or args.q_chunk or \
+                args.main != "bf16" or args.paged:
             return None
         return rec["per_dispatch"]["total_bytes"] / 1e9
 
@@ -535,7 +559,9 @@ def main():
             return dict(bound="mfma", achieved=a / 1e12, peak=peak / 1e12, unit="TFLOP/s",
                         frac=a / peak, traffic=traffic_record(name),
                         dtype="fp8 e4m3" if name.endswith("fp8") else "bf16")
-        bytes_ = {"attend_blocks": wm["attend_bytes"], "merge_partials": wm["merge_bytes"],
+        bytes_ = {"attend_blocks": wm["attend_bytes" if f8m is None else "attend_bytes_fp8"],
+                  "merge_partials": wm["merge_bytes"],
+                  "quantize_main_fp8": wm["main_quant_bytes"],
                   "topk_select": wm["topk_bytes"],
                   "index_score_decode": wm["index_decode_bytes"],
                   "index_score_decode_fp8": wm["index_decode_fp8_bytes"],
@@ -557,7 +583,10 @@ def main():
     value = w.total_q / (ms_per_step / 1e3)
     extra = {}
     if decode:
-        gbs = wm["decode_fp8_bytes" if fp8 is not None else "decode_bytes"] / (ms_per_step / 1e3) / 1e9
+        dec_bytes = wm["decode_fp8_bytes" if fp8 is not None else "decode_bytes"]
+        if f8m is not None:
+            dec_bytes += wm["decode_kv_fp8_delta"]
+        gbs = dec_bytes / (ms_per_step / 1e3) / 1e9
         extra["decode_hbm_GBps"] = gbs
         extra["decode_hbm_frac"] = gbs * 1e9 / PEAK_HBM_BYTES
 
@@ -584,16 +613,31 @@ def main():
             # the oracle scores the dequantised codes it computes itself from the bf16 inputs
             from oracle import fp8_index as F
             nbk = int((np.diff(cuk).max() + BLOCK - 1) // BLOCK)
-            kc, ke = F.quantize_k_idx(kidx, cuk, nbk)
-            kidx = F.dequantize_k_idx(kc, ke, cuk)
-            del kc
+            kcodes, kexp = F.quantize_k_idx(kidx, cuk, nbk)
+            kidx = F.dequantize_k_idx(kcodes, kexp, cuk)
+            del kcodes
+        if f8m is not None:
+            # the oracle attends on the dequantised q, k, v it computes itself from the bf16 inputs
+            from oracle import fp8_main as FM
+            if pooled:
+                nbk = int((np.diff(cuk).max() + BLOCK - 1) // BLOCK)
+                kk = FM.dequantize_kv(*FM.quantize_kv(kk, cuk, nbk), cuk)
+                vv = FM.dequantize_kv(*FM.quantize_kv(vv, cuk, nbk), cuk)
+            else:
+                def fetch(x):
+                    return lambda lo, hi: x[lo:hi].double().cpu().numpy()
+                kk = FM.DequantizedRows(fetch(t["k"]), w.total_k, t["k"].shape[1:], cuk)
+                vv = FM.DequantizedRows(fetch(t["v"]), w.total_k, t["v"].shape[1:], cuk)
 
         def host_rows(rows):
             ridx = torch.as_tensor(rows, device=dev, dtype=torch.long)
             qi = t["q_idx"].index_select(0, ridx).float().cpu().numpy()
             if fp8 is not None:
                 qi = F.dequantize_q_idx(*F.quantize_q_idx(qi))
-            return t["q"].index_select(0, ridx).float().cpu().numpy(), qi
+            qh = t["q"].index_select(0, ridx).float().cpu().numpy()
+            if f8m is not None:
+                qh = FM.dequantize_q(*FM.quantize_q(qh))
+            return qh, qi
 
         # per-row cost on one core, then a sample sized to the time target
         pilot = sorted(set(int(x) for x in rng.integers(0, w.total_q, size=min(6, w.total_q))))
@@ -630,7 +674,8 @@ def main():
         cpu = dict(value=len(rows) / dt, unit="tokens/s", cores=used, kind="oracle",
                    sample=f"{len(rows)} uniformly random query rows of {w.name}, each through the "
                           f"full Index and Main Branch in fp64 numpy"
-                          f"{' (on the dequantised fp8 index projections)' if fp8 is not None else ''}; "
+                          f"{' (on the dequantised fp8 index projections)' if fp8 is not None else ''}"
+                          f"{' (on the dequantised fp8 q, k, v)' if f8m is not None else ''}; "
                           f"{used} worker process(es), 1 BLAS thread each; {dt:.1f} s")
     elif pool:
         pool.close()
@@ -646,7 +691,9 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16" if fp8 is None else "bf16 (Main Branch), fp8 e4m3 (Index Branch)",
+        "dtype": ("bf16" if fp8 is None and f8m is None else
+                  (("bf16" if f8m is None else "fp8 e4m3 storage, bf16 MFMA") + " (Main Branch), "
+                   + ("bf16" if fp8 is None else "fp8 e4m3") + " (Index Branch)")),
         "data": "synthetic",
         "graph": use_graph,
         "config": {"workload": w.name, "seq_k_lens": (w.seq_k_lens if len(w.seq_k_lens) <= 4 else
@@ -654,7 +701,7 @@ def main():
                    "total_q": w.total_q, "num_q_heads": w.num_q_heads,
                    "num_kv_heads": w.num_kv_heads, "head_dim": w.head_dim,
                    "index_dim": w.index_dim, "block": BLOCK, "top_k": w.top_k,
-                   "q_chunk": args.q_chunk, "index_branch": args.index,
+                   "q_chunk": args.q_chunk, "index_branch": args.index, "main_branch": args.main,
                    "index_projection_dim": args.project_dim or None, "kl_target": bool(args.kl),
                    "kv_cache": "paged (128-row pages, scrambled)" if args.paged else "contiguous",
                    "parallelism": "single GPU"},

@@ -80,3 +80,50 @@ def dequantize_kv(codes, ex, cu_seqlens_k, block=BLOCK):
         beta = np.arange(hi - lo) // block
         out[lo:hi] = np.ldexp(vals[lo:hi], (ex[b, beta, :] - F.E8M0_BIAS)[:, :, None])
     return out
+
+
+class DequantizedRows:
+    """Rows of a packed k or v cache [total_k, G, d] as they are after 8-bit
+    quantisation, computed one (sequence block) at a time on first use: a
+    (block, head) unit's codes and scale depend on that block alone (M1), so
+    this equals quantize_kv + dequantize_kv on the whole cache.
+
+    ``fetch(lo, hi)`` returns float64 rows lo .. hi-1 of the unquantised
+    cache.  Supports the access patterns of the oracle: slices of rows
+    (views sharing the cache), and x[rows, g] with an array of rows.
+    """
+
+    def __init__(self, fetch, n_rows, row_shape, cu_seqlens_k, lo=0, hi=None, cache=None):
+        self.fetch, self.n = fetch, int(n_rows)
+        self.row_shape = tuple(row_shape)
+        self.cu = np.asarray(cu_seqlens_k, dtype=np.int64)
+        self.lo, self.hi = lo, self.n if hi is None else hi
+        self.shape = (self.hi - self.lo,) + self.row_shape
+        self.cache = {} if cache is None else cache
+
+    def __len__(self):
+        return self.hi - self.lo
+
+    def _block(self, b, beta):
+        key = (b, beta)
+        if key not in self.cache:
+            lo = int(self.cu[b]) + BLOCK * beta
+            hi = min(lo + BLOCK, int(self.cu[b + 1]))
+            cu = np.array([0, hi - lo])
+            self.cache[key] = dequantize_kv(*quantize_kv(self.fetch(lo, hi), cu, 1), cu)
+        return self.cache[key]
+
+    def __getitem__(self, idx):
+        if isinstance(idx, slice):
+            a, z, st = idx.indices(len(self))
+            assert st == 1
+            return DequantizedRows(self.fetch, self.n, self.row_shape, self.cu, self.lo + a,
+                                   self.lo + z, self.cache)
+        rows, col = idx
+        rows = np.asarray(rows, dtype=np.int64) + self.lo
+        out = np.empty((len(rows),) + self.row_shape[1:])
+        for i, r in enumerate(rows):
+            b = int(np.searchsorted(self.cu, r, side="right") - 1)
+            j = int(r - self.cu[b])
+            out[i] = self._block(b, j // BLOCK)[j % BLOCK, int(col)]
+        return out

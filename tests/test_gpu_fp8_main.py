@@ -161,51 +161,6 @@ def test_fp8_main_paged_equals_contiguous():
             assert torch.equal(fa.v_exp[bb, :nb].cpu(), fb.v_exp.cpu()[pg])
 
 
-class _LazyQuantKV:
-    """Dequantised k or v rows of a device tensor for the oracle, computed block by block
-    with the oracle's own quantiser (a (block, head) unit depends on that block alone)."""
-
-    def __init__(self, x, cu_k, lo=0, hi=None):
-        self.x, self.cu = x, np.asarray(cu_k, dtype=np.int64)
-        self.lo, self.hi = lo, x.shape[0] if hi is None else hi
-        self.shape = (self.hi - self.lo,) + tuple(x.shape[1:])
-        self.cache = {}
-
-    def __len__(self):
-        return self.hi - self.lo
-
-    def _block(self, b, beta):
-        key = (b, beta)
-        if key not in self.cache:
-            lo = int(self.cu[b]) + 128 * beta
-            hi = min(lo + 128, int(self.cu[b + 1]))
-            xb = _f64(self.x[lo:hi])
-            c, e = M.quantize_kv(xb, np.array([0, hi - lo]), 1)
-            self.cache[key] = M.dequantize_kv(c, e, np.array([0, hi - lo]))
-        return self.cache[key]
-
-    def __getitem__(self, idx):
-        if isinstance(idx, slice):
-            a, z, st = idx.indices(len(self))
-            assert st == 1
-            return self._view(self.lo + a, self.lo + z)
-        rows, col = idx
-        rows = np.asarray(rows, dtype=np.int64) + self.lo
-        out = np.empty((len(rows),) + tuple(self.x.shape[2:]))
-        for i, r in enumerate(rows):
-            b = int(np.searchsorted(self.cu, r, side="right") - 1)
-            j = int(r - self.cu[b])
-            out[i] = self._block(b, j // 128)[j % 128, int(col)]
-        return out
-
-    def _view(self, lo, hi):
-        v = _LazyQuantKV.__new__(_LazyQuantKV)
-        v.x, v.cu, v.lo, v.hi = self.x, self.cu, lo, hi
-        v.shape = (hi - lo,) + tuple(self.x.shape[1:])
-        v.cache = self.cache
-        return v
-
-
 class _LazyQuantQ(LazyRows):
     """Dequantised query rows (one scale per (row, head)) of a device tensor."""
 
@@ -223,7 +178,11 @@ def _sampled_full(name, n_random):
     dims, bufs, f8 = _run(w, t)
     rows = sample_rows(w, n_random)
     cu_k = t["cu_seqlens_k"].cpu().numpy()
-    P = O.Problem(_LazyQuantQ(t["q"]), _LazyQuantKV(t["k"], cu_k), _LazyQuantKV(t["v"], cu_k),
+    def rows_of(x):
+        return lambda lo, hi: _f64(x[lo:hi])
+    kq = M.DequantizedRows(rows_of(t["k"]), t["k"].shape[0], t["k"].shape[1:], cu_k)
+    vq = M.DequantizedRows(rows_of(t["v"]), t["v"].shape[0], t["v"].shape[1:], cu_k)
+    P = O.Problem(_LazyQuantQ(t["q"]), kq, vq,
                   LazyRows(t["q_idx"]), t["k_idx"].float().cpu().numpy(), t["cu_seqlens_q"].cpu().numpy(),
                   cu_k, w.top_k)
     log(f"[{name}-fp8-main] forward done; oracle on {len(rows)} rows")

@@ -128,3 +128,13 @@ def test_main_branch_on_dequantised_values_is_dense_attention():
             V = torch.from_numpy(vd[:r + 1, g])[None, None]
             want = torch.nn.functional.scaled_dot_product_attention(Q, K, V, scale=d ** -0.5)[0, 0, 0]
             assert np.allclose(res["out"][i, h], want.numpy(), atol=1e-12, rtol=0)
+
+
+def test_lazy_dequantized_rows_equal_the_whole_cache():
+    k, cu = _kv(8, lens=(700, 300, 5), G=2, d=8)
+    whole = M.dequantize_kv(*M.quantize_kv(k, cu, 6), cu)
+    lazy = M.DequantizedRows(lambda lo, hi: k[lo:hi], k.shape[0], k.shape[1:], cu)
+    J = np.array([0, 5, 130, 699, 700, 850, 999, 1004])
+    assert np.array_equal(lazy[J, 1], whole[J, 1])
+    view = lazy[700:1000]
+    assert np.array_equal(view[np.array([0, 150, 299]), 0], whole[[700, 850, 999], 0])
