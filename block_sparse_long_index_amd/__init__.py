@@ -20,7 +20,8 @@ __all__ = [
     "make_dims", "workspace_size", "index_select", "build_block_query_lists", "attend",
     "msa_forward", "exported_symbols", "LIB_PATH", "HEADER_PATH", "index_quantize_fp8",
     "index_select_fp8", "Fp8Index", "index_project", "attend_with_mass", "index_kl",
-    "attend_reads_lists", "Fp8Main", "main_quantize_fp8", "attend_fp8",
+    "attend_reads_lists", "Fp8Main", "main_quantize_fp8", "attend_fp8", "Q8K4Index",
+    "index_quantize_q8k4", "index_select_q8k4",
 ]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -82,6 +83,10 @@ def load_library(path: str = LIB_PATH):
     lib.msa_index_quantize_fp8.argtypes = [DP, P, P, P, P, P, P, P, P]
     lib.msa_index_select_fp8.restype = I32
     lib.msa_index_select_fp8.argtypes = [DP, P, P, P, P, P, P, P, P, P, SZ, P]
+    lib.msa_index_quantize_q8k4.restype = I32
+    lib.msa_index_quantize_q8k4.argtypes = [DP, P, P, P, P, P, P, P, P]
+    lib.msa_index_select_q8k4.restype = I32
+    lib.msa_index_select_q8k4.argtypes = [DP, P, P, P, P, P, P, P, P, P, SZ, P]
     lib.msa_build_block_query_lists.restype = I32
     lib.msa_build_block_query_lists.argtypes = [DP, P, P, P, P, P, P, SZ, P]
     lib.msa_attend.restype = I32
@@ -334,6 +339,67 @@ def attend_fp8(dims, f8: Fp8Main, cu_seqlens_q, cu_seqlens_k, sel, block_offsets
     return out
 
 
+class Q8K4Index:
+    """8-bit index-query codes and 4-bit index-key codes for fixed dims: E4M3
+    queries with one E8M0 exponent per (row, group); E2M1 keys packed two per
+    byte with one E8M0 exponent per 32 elements of a key row."""
+
+    def __init__(self, dims: Dims, device):
+        T, G, DI = dims.total_q, dims.num_kv_heads, dims.index_dim
+        dev = torch.device(device)
+        self.q_idx8 = torch.empty((T, G, DI), dtype=torch.uint8, device=dev)
+        self.q_exp = torch.empty((T, G), dtype=torch.uint8, device=dev)
+        self.k_idx4 = torch.empty((dims.total_k, DI // 2), dtype=torch.uint8, device=dev)
+        self.k_exp4 = torch.empty((dims.total_k, DI // 32), dtype=torch.uint8, device=dev)
+
+
+def _check_q8k4(dims, qk: Q8K4Index):
+    G, T, DI = dims.num_kv_heads, dims.total_q, dims.index_dim
+    _shape(qk.q_idx8, (T, G, DI), "q_idx8")
+    _shape(qk.q_exp, (T, G), "q_exp")
+    _shape(qk.k_idx4, (dims.total_k, DI // 2), "k_idx4")
+    _shape(qk.k_exp4, (dims.total_k, DI // 32), "k_exp4")
+
+
+def index_quantize_q8k4(dims, q_idx, k_idx, cu_seqlens_k, qk: Q8K4Index, stream=None):
+    """bf16 index projections -> 8-bit query codes and 4-bit key codes (into `qk`).
+
+    Either q_idx or k_idx may be None: that side is left as it is in `qk`.
+    """
+    G, T, DI = dims.num_kv_heads, dims.total_q, dims.index_dim
+    if q_idx is not None:
+        _shape(q_idx, (T, G, DI), "q_idx")
+    if k_idx is not None:
+        _shape(k_idx, (dims.total_k, DI), "k_idx")
+    _check_q8k4(dims, qk)
+    st = load_library().msa_index_quantize_q8k4(
+        ctypes.byref(dims), _ptr(q_idx, "q_idx", torch.bfloat16), _ptr(k_idx, "k_idx", torch.bfloat16),
+        _ptr(cu_seqlens_k, "cu_seqlens_k", torch.int32), _ptr(qk.q_idx8, "q_idx8", torch.uint8),
+        _ptr(qk.q_exp, "q_exp", torch.uint8), _ptr(qk.k_idx4, "k_idx4", torch.uint8),
+        _ptr(qk.k_exp4, "k_exp4", torch.uint8), _stream(stream))
+    _check(st, "msa_index_quantize_q8k4")
+    return qk
+
+
+def index_select_q8k4(dims, qk: Q8K4Index, cu_seqlens_q, cu_seqlens_k, sel, sel_score=None,
+                      workspace=None, stream=None):
+    """Index Branch on 8-bit queries and 4-bit keys (see msa_index_select_q8k4)."""
+    G, T = dims.num_kv_heads, dims.total_q
+    _check_q8k4(dims, qk)
+    _shape(sel, (T, G, dims.top_k), "sel")
+    if sel_score is not None:
+        _shape(sel_score, (T, G, dims.top_k), "sel_score")
+    ws = _workspace(dims, OP_INDEX_SELECT, workspace, sel.device)
+    st = load_library().msa_index_select_q8k4(
+        ctypes.byref(dims), _ptr(qk.q_idx8, "q_idx8", torch.uint8), _ptr(qk.q_exp, "q_exp", torch.uint8),
+        _ptr(qk.k_idx4, "k_idx4", torch.uint8), _ptr(qk.k_exp4, "k_exp4", torch.uint8),
+        _ptr(cu_seqlens_q, "cu_seqlens_q", torch.int32), _ptr(cu_seqlens_k, "cu_seqlens_k", torch.int32),
+        _ptr(sel, "sel", torch.int32), _ptr(sel_score, "sel_score", torch.float32),
+        _ptr(ws, "workspace"), ctypes.c_size_t(ws.numel() * ws.element_size()), _stream(stream))
+    _check(st, "msa_index_select_q8k4")
+    return sel
+
+
 def index_select_fp8(dims, fp8: Fp8Index, cu_seqlens_q, cu_seqlens_k, sel, sel_score=None,
                      workspace=None, stream=None):
     """Index Branch on the quantised projections (see msa_index_select_fp8)."""
@@ -468,7 +534,8 @@ def attend_reads_lists(dims: Dims) -> bool:
 
 
 def msa_forward(dims: Dims, q, k, v, q_idx, k_idx, cu_seqlens_q, cu_seqlens_k, bufs: Buffers = None,
-                stream=None, fp8: Fp8Index = None, fp8_main: Fp8Main = None) -> Buffers:
+                stream=None, fp8: Fp8Index = None, fp8_main: Fp8Main = None,
+                q8k4: Q8K4Index = None) -> Buffers:
     """The whole hot path: index_select -> build_block_query_lists -> attend.
 
     One workspace serves the three calls (they run in order on one stream).
@@ -476,12 +543,20 @@ def msa_forward(dims: Dims, q, k, v, q_idx, k_idx, cu_seqlens_q, cu_seqlens_k, b
     With `fp8` given, the Index Branch quantises q_idx and k_idx into it and
     selects on the codes (index_quantize_fp8 -> index_select_fp8); k_idx=None
     keeps the key codes already in `fp8` (a quantised index-key cache).
+    With `q8k4` given instead, the same with 4-bit index keys
+    (index_quantize_q8k4 -> index_select_q8k4).
     With `fp8_main` given, the Main Branch quantises q (and k, v unless they are
     None: a quantised key/value cache already in `fp8_main`) and attends on the
     codes (main_quantize_fp8 -> attend_fp8).
     """
     bufs = bufs or Buffers(dims, q.device)
-    if fp8 is None:
+    if fp8 is not None and q8k4 is not None:
+        raise ValueError("pass at most one of fp8 and q8k4")
+    if q8k4 is not None:
+        index_quantize_q8k4(dims, q_idx, k_idx, cu_seqlens_k, q8k4, stream)
+        index_select_q8k4(dims, q8k4, cu_seqlens_q, cu_seqlens_k, bufs.sel, bufs.sel_score,
+                          bufs.workspace, stream)
+    elif fp8 is None:
         index_select(dims, q_idx, k_idx, cu_seqlens_q, cu_seqlens_k, bufs.sel, bufs.sel_score,
                      bufs.workspace, stream)
     else:
@@ -501,7 +576,7 @@ def msa_forward(dims: Dims, q, k, v, q_idx, k_idx, cu_seqlens_q, cu_seqlens_k, b
     return bufs
 
 
-PROFILE_KERNELS = 13
+PROFILE_KERNELS = 16
 
 
 def profile_enable(on: bool = True):

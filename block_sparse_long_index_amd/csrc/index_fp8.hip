@@ -16,6 +16,15 @@
 // max_j (2^eq q8 . 2^ek k8_j) = 2^(eq + ek) max_j (q8 . k8_j): the kernels
 // contract raw codes on the fp8 MFMA and apply the two exponents once per
 // (row, block), exactly (ldexp).
+//
+// The same kernels, instantiated with K4, read 4-bit index keys (the pages'
+// move to 4-bit keys): OCP E2M1 codes, two per byte (element 2i in the low
+// nibble), with one E8M0 exponent per 32 elements of a key row, the
+// microscaling layout that gfx950's scaled MFMA consumes directly.  The keys'
+// exponents go to the MFMA as per-lane scales; the query's exponent is applied
+// to the block maximum as before.
+#include <type_traits>
+
 #include "fp8_common.h"
 #include "msa_common.h"
 #include "topk_common.h"
@@ -30,6 +39,17 @@ typedef int i32x8 __attribute__((ext_vector_type(8)));
 // assignment in A and B.
 __device__ inline f32x16 mfma32_fp8(i32x8 a, i32x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+}
+
+// 32x32x64 MFMA of E2M1 keys (A, format code 4) against E4M3 queries (B,
+// format 0) with per-lane E8M0 scales (2^(s - 127)).  Measured lane layout:
+// A lane half h holds contraction elements 32h .. 32h+31 in its first 16 bytes
+// (low nibble first); B lane half h holds elements 16h .. 16h+15 in bytes 0-15
+// and 32+16h .. 32+16h+15 in bytes 16-31; lane half h's scale covers elements
+// 32h .. 32h+31 of its row (A) or column (B).  Products are summed as for the
+// fp8 MFMA (groups of 8 aligned to their largest product).
+__device__ inline f32x16 mfma32_k4(i32x8 a, i32x8 b, f32x16 c, int scale_a) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 4, 0, 0, scale_a, 0, 127);
 }
 
 __device__ inline i32x8 as_i32x8(uint4 lo, uint4 hi) {
@@ -87,6 +107,72 @@ __global__ __launch_bounds__(256) void quantize_k_kernel(const uint16_t* __restr
 }
 
 // ---------------------------------------------------------------------------
+// 4-bit index keys.  A group's exponent e is the smallest integer with
+// amax * 2^-e <= 6 (the largest E2M1 value), clamped to [-127, 127], 0 for an
+// all-zero group; codes are the nearest E2M1 value of x * 2^-e, ties to the
+// even code, with x's sign bit.
+// ---------------------------------------------------------------------------
+__device__ inline int fp4_scale_exponent(float amax) {
+  if (amax == 0.f) return 0;
+  int E;
+  const float f = frexpf(amax, &E);
+  const int e = f <= 0.75f ? E - 3 : E - 2;   // f * 2^3 <= 6 exactly when f <= 0.75
+  return min(127, max(-127, e));
+}
+
+// E2M1 code of one value already scaled into [-6, 6].  The thresholds are the
+// midpoints of the grid 0, .5, 1, 1.5, 2, 3, 4, 6; at a midpoint the even code
+// (mantissa bit 0: 0, 1, 2, 4) wins, hence > below even codes and >= below odd.
+__device__ inline uint32_t e2m1_code(float y) {
+  const float a = fabsf(y);
+  const uint32_t c = (uint32_t)(a > 0.25f) + (uint32_t)(a >= 0.75f) + (uint32_t)(a > 1.25f) +
+                     (uint32_t)(a >= 1.75f) + (uint32_t)(a > 2.5f) + (uint32_t)(a >= 3.5f) +
+                     (uint32_t)(a > 5.f);
+  return c | ((__float_as_uint(y) >> 31) << 3);
+}
+
+// Key rows of one (block beta, sequence b) per workgroup, 8 elements per lane:
+// the four lanes of a 32-element group share its maximum through shuffles.
+// Codes: [rows][DI / 2] bytes; exponents: [rows][DI / 32], row as for k_idx.
+// Rows past the sequence's end are not written.
+template <int DI>
+__global__ __launch_bounds__(256) void quantize_k4_kernel(const uint16_t* __restrict__ k,
+                                                          const int32_t* __restrict__ cu_k, KvMap kv,
+                                                          uint8_t* __restrict__ k4,
+                                                          uint8_t* __restrict__ ke4) {
+  constexpr int LPR = DI / 8;                      // 8-element chunks per key row
+  constexpr int PER = kBlock * LPR / 256;          // chunks per thread
+  static_assert(LPR % 4 == 0 && PER >= 1, "whole 32-element groups per row");
+  const int beta = blockIdx.x, b = blockIdx.y;
+  const int koff = cu_k[b], lk = cu_k[b + 1] - koff;
+  const int n = min(kBlock, lk - beta * kBlock);
+  if (n <= 0) return;
+  const size_t row0 = kv.block_row(b, koff, beta);
+  const int tid = threadIdx.x;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int c = tid + i * 256, row = c / LPR, col = c % LPR;
+    uint4 v = make_uint4(0, 0, 0, 0);
+    if (row < n) v = *reinterpret_cast<const uint4*>(k + (row0 + row) * DI + col * 8);
+    float x[8];
+    unpack8_bf16(v, x);
+    float a = 0.f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) a = fmaxf(a, fabsf(x[j]));
+    a = fmaxf(a, shfl_xor_f(a, 1));
+    a = fmaxf(a, shfl_xor_f(a, 2));
+    const int e = fp4_scale_exponent(a);
+    uint32_t w = 0;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) w |= e2m1_code(ldexpf(x[j], -e)) << (4 * j);
+    if (row < n) {
+      *reinterpret_cast<uint32_t*>(k4 + (row0 + row) * (DI / 2) + col * 4) = w;
+      if ((col & 3) == 0) ke4[(row0 + row) * (DI / 32) + col / 4] = (uint8_t)(e + 127);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Prefill scoring + selection on E4M3 codes.  Same organisation as the bf16
 // prefill kernel: a workgroup owns RT * NW * 32 (query, group) rows of one
 // sequence, waves hold their rows' index queries as MFMA B operands, key
@@ -137,21 +223,120 @@ struct KRing8 {
   }
 };
 
+// Ring of 4-bit key blocks: the block's codes (128 x DI/2 bytes, swizzled as in
+// KRing8) followed by its exponents (128 x DI/32 bytes, in row order).  Every
+// wave issues PER_WAVE code pieces and one exponent piece per block, so all
+// waves count the same LOADS loads in flight.
+template <int DI, int NW>
+struct KRing4 {
+  static constexpr int RB = DI / 2;                               // code bytes per key row
+  static constexpr int CPR = RB / 16;                             // 16-byte chunks per row
+  static constexpr int R = 16 / CPR;                              // rows per 256-byte bank line
+  static constexpr int CODE_BYTES = kBlock * RB;
+  static constexpr int PIECE = CODE_BYTES / NW < 1024 ? CODE_BYTES / NW : 1024;
+  static constexpr int PER_WAVE = CODE_BYTES / PIECE / NW;
+  static constexpr int ROWS_PER_PIECE = PIECE / RB;
+  static constexpr int XB = DI / 32;                              // exponent bytes per key row
+  static constexpr int EXP_PER_WAVE = kBlock * XB / NW;
+  static constexpr int BYTES = CODE_BYTES + kBlock * XB;
+  static constexpr int LOADS = PER_WAVE + 1;
+  static_assert(CODE_BYTES % (PIECE * NW) == 0 && EXP_PER_WAVE % 16 == 0 && PIECE % RB == 0,
+                "block must split evenly over the waves");
+
+  __device__ static inline void load(const uint8_t* __restrict__ codes,
+                                     const uint8_t* __restrict__ exps, uint8_t* buf, int wave,
+                                     int lane) {
+#pragma unroll
+    for (int i = 0; i < PER_WAVE; ++i) {
+      const int piece = wave * PER_WAVE + i;
+      if (PIECE == 1024 || lane < PIECE / 16) {
+        const int m = piece * ROWS_PER_PIECE + lane / CPR;
+        const int lc = (lane % CPR) ^ swz(m);
+        __builtin_amdgcn_global_load_lds(codes + (size_t)m * RB + lc * 16, buf + piece * PIECE, 16,
+                                         0, 0);
+      }
+    }
+    if (lane < EXP_PER_WAVE / 16)
+      __builtin_amdgcn_global_load_lds(exps + wave * EXP_PER_WAVE + lane * 16,
+                                       buf + CODE_BYTES + wave * EXP_PER_WAVE, 16, 0, 0);
+  }
+  __device__ static inline int swz(int m) { return (m / R) % CPR; }
+  // A fragment of k-step ks for lane half h: elements 64ks + 32h .. +31 of row
+  // m, logical chunk 2ks + h (DI = 32: chunk 0 for half 0, zeros for half 1)
+  __device__ static inline i32x8 frag(const uint8_t* buf, int m, int ks, int h) {
+    uint4 v = make_uint4(0, 0, 0, 0);
+    if (DI > 32 || h == 0) {
+      const int lc = DI > 32 ? 2 * ks + h : 0;
+      v = *reinterpret_cast<const uint4*>(buf + m * RB + ((lc ^ swz(m)) * 16));
+    }
+    return as_i32x8(v, make_uint4(0, 0, 0, 0));
+  }
+  // the XB exponent bytes of row m, byte j = elements 32j .. 32j+31
+  __device__ static inline uint32_t exps(const uint8_t* buf, int m) {
+    const uint8_t* p = buf + CODE_BYTES + m * XB;
+    if constexpr (XB == 4) return *reinterpret_cast<const uint32_t*>(p);
+    else if constexpr (XB == 2) return *reinterpret_cast<const uint16_t*>(p);
+    else return *p;
+  }
+};
+
+// E8M0 scale for the A fragment of k-step ks, lane half h, from a row's
+// exponent bytes (0, a factor 2^-127, for the zero half when DI = 32)
+__device__ inline int k4_scale(uint32_t x, int ks, int h) { return (int)((x >> (8 * (2 * ks + h))) & 255u); }
+
+// B fragment of k-step ks for lane half h from a query's E4M3 codes, in the
+// order the MFMA pairs with the A layouts: fp8 keys take 32 contiguous bytes
+// per half (both operands use the same assignment); fp4 keys need elements
+// 16h .. 16h+15 and 32+16h .. 32+16h+15 of the k-step.
+template <int DI, bool K4>
+__device__ inline i32x8 q_frag(const uint8_t* src, int ks, int h) {
+  uint4 lo, hi = make_uint4(0, 0, 0, 0);
+  if constexpr (DI == 32) {
+    lo = *reinterpret_cast<const uint4*>(src + h * 16);
+  } else if constexpr (K4) {
+    lo = *reinterpret_cast<const uint4*>(src + ks * 64 + h * 16);
+    hi = *reinterpret_cast<const uint4*>(src + ks * 64 + 32 + h * 16);
+  } else {
+    lo = *reinterpret_cast<const uint4*>(src + ks * 64 + h * 32);
+    hi = *reinterpret_cast<const uint4*>(src + ks * 64 + h * 32 + 16);
+  }
+  return as_i32x8(lo, hi);
+}
+
 constexpr int kFp8ExpLds = 16384;   // key blocks per sequence whose exponents fit on chip
 
-template <int DI, int RT, int NW, int KCAP>
+// K4: 4-bit keys (codes k8 = [rows][DI/2], exponents ke = [rows][DI/32]);
+// else E4M3 keys (k8 = [rows][DI], ke = one exponent per block index).
+template <int DI, bool K4>
+struct PrefillKeys {
+  using Ring = KRing8<DI, 4>;
+  static constexpr int BYTES = kBlock * DI;
+  static constexpr int LOADS = Ring::PER_WAVE;
+  static constexpr int EXP_LDS = kFp8ExpLds;
+};
+template <int DI>
+struct PrefillKeys<DI, true> {
+  using Ring = KRing4<DI, 4>;
+  static constexpr int BYTES = Ring::BYTES;
+  static constexpr int LOADS = Ring::LOADS;
+  static constexpr int EXP_LDS = 1;
+};
+
+template <int DI, int RT, int NW, int KCAP, bool K4>
 __global__ __launch_bounds__(NW * 64, 2) void index_select_prefill_fp8_kernel(
     const uint8_t* __restrict__ q8, const uint8_t* __restrict__ qe, const uint8_t* __restrict__ k8,
     const uint8_t* __restrict__ ke, const int32_t* __restrict__ cu_q,
     const int32_t* __restrict__ cu_k, KvMap kv, int G, int nb_max, int qt, int top_k,
     int32_t* __restrict__ sel, float* __restrict__ sel_score) {
   static_assert(RT == 1 || RT == 2, "a lane owns at most one row");
-  using Ring = KRing8<DI, NW>;
+  static_assert(NW == 4, "rings are laid out for four waves");
+  using Keys = PrefillKeys<DI, K4>;
+  using Ring = typename Keys::Ring;
   constexpr int KS = DI >= 64 ? DI / 64 : 1;   // MFMA k-steps over the index dim
-  __shared__ __attribute__((aligned(1024))) uint8_t ring0[kBlock * DI];
-  __shared__ __attribute__((aligned(1024))) uint8_t ring1[kBlock * DI];
-  __shared__ __attribute__((aligned(1024))) uint8_t ring2[kBlock * DI];
-  __shared__ uint8_t kexp[kFp8ExpLds];
+  __shared__ __attribute__((aligned(1024))) uint8_t ring0[Keys::BYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t ring1[Keys::BYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t ring2[Keys::BYTES];
+  __shared__ uint8_t kexp[Keys::EXP_LDS];
 
   const int b = blockIdx.y;
   const int qoff = cu_q[b], lq = cu_q[b + 1] - qoff;
@@ -161,7 +346,7 @@ __global__ __launch_bounds__(NW * 64, 2) void index_select_prefill_fp8_kernel(
   const int qz = min(qoff + lq, qa + qt);
   if (qa >= qz) return;
   const int p_last = lk - lq + (qz - 1 - qoff);
-  const int beta_hi = min(p_last / kBlock, kFp8ExpLds);
+  const int beta_hi = K4 ? p_last / kBlock : min(p_last / kBlock, kFp8ExpLds);
   const int nrows = (qz - qa) * G;
 
   const int tid = threadIdx.x;
@@ -180,8 +365,9 @@ __global__ __launch_bounds__(NW * 64, 2) void index_select_prefill_fp8_kernel(
   list.clear();
 
   if (beta_hi > 0) {
-    // the sequence's key-block exponents, staged once
-    for (int i = tid; i < beta_hi; i += NW * 64) kexp[i] = ke[kv.block_index(b, i, nb_max)];
+    // the sequence's key-block exponents (E4M3 keys), staged once
+    if constexpr (!K4)
+      for (int i = tid; i < beta_hi; i += NW * 64) kexp[i] = ke[kv.block_index(b, i, nb_max)];
 
     i32x8 qf[RT][KS];
 #pragma unroll
@@ -190,37 +376,33 @@ __global__ __launch_bounds__(NW * 64, 2) void index_select_prefill_fp8_kernel(
       const uint8_t* src = q8 + ((size_t)qa * G + min(n, nrows - 1)) * DI;
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        uint4 lo, hi = make_uint4(0, 0, 0, 0);
-        if constexpr (DI == 32) {
-          lo = *reinterpret_cast<const uint4*>(src + half * 16);
-        } else {
-          lo = *reinterpret_cast<const uint4*>(src + ks * 64 + half * 32);
-          hi = *reinterpret_cast<const uint4*>(src + ks * 64 + half * 32 + 16);
-        }
-        if (n >= nrows) lo = hi = make_uint4(0, 0, 0, 0);
-        qf[rt][ks] = as_i32x8(lo, hi);
+        qf[rt][ks] = q_frag<DI, K4>(src, ks, half);
+        if (n >= nrows) qf[rt][ks] = i32x8{};
       }
     }
     __syncthreads();   // exponents visible; every earlier load has landed
 
-    auto blk = [&](int beta) __attribute__((always_inline)) {
-      return k8 + kv.block_row(b, koff, beta) * DI;
+    // issue this wave's loads of key block beta into buf
+    auto issue = [&](int beta, uint8_t* buf) __attribute__((always_inline)) {
+      const size_t row0 = kv.block_row(b, koff, beta);
+      if constexpr (K4) Ring::load(k8 + row0 * (DI / 2), ke + row0 * (DI / 32), buf, wave, lane);
+      else Ring::load(k8 + row0 * DI, buf, wave, lane);
     };
     uint32_t pending = 0;   // previous block's score key, inserted during the next block's MFMAs
     int pending_beta = 0;
-    Ring::load(blk(0), ring0, wave, lane);
-    if (beta_hi > 1) Ring::load(blk(1), ring1, wave, lane);
+    issue(0, ring0);
+    if (beta_hi > 1) issue(1, ring1);
 
     auto step = [&](int beta, const uint8_t* rbuf, uint8_t* lbuf) __attribute__((always_inline)) {
       // this wave's pieces of block beta have landed (only beta+1 may be
       // younger); the barrier publishes every wave's pieces and retires the
       // reads of the buffer about to be refilled
-      if (beta + 1 < beta_hi) wait_vmcnt<Ring::PER_WAVE>(); else wait_vmcnt<0>();
+      if (beta + 1 < beta_hi) wait_vmcnt<Keys::LOADS>(); else wait_vmcnt<0>();
       __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0)
       asm volatile("" ::: "memory");
       __builtin_amdgcn_s_barrier();
       asm volatile("" ::: "memory");
-      if (beta + 2 < beta_hi) Ring::load(blk(beta + 2), lbuf, wave, lane);
+      if (beta + 2 < beta_hi) issue(beta + 2, lbuf);
 
       // software pipeline: the MFMAs of key tile kt+1 are issued before the
       // row maxima of tile kt are taken, and the previous block's top-k
@@ -234,13 +416,19 @@ __global__ __launch_bounds__(NW * 64, 2) void index_select_prefill_fp8_kernel(
         i32x8 a[KS];
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) a[ks] = Ring::frag(rbuf, kt * 32 + col, ks, half);
+        uint32_t kx = 0;
+        if constexpr (K4) kx = Ring::exps(rbuf, kt * 32 + col);
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt) acc[kt & 1][rt] = f32x16{};
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
-          for (int rt = 0; rt < RT; ++rt)
-            acc[kt & 1][rt] = mfma32_fp8(a[ks], qf[rt][ks], acc[kt & 1][rt]);
+          for (int rt = 0; rt < RT; ++rt) {
+            if constexpr (K4)
+              acc[kt & 1][rt] = mfma32_k4(a[ks], qf[rt][ks], acc[kt & 1][rt], k4_scale(kx, ks, half));
+            else
+              acc[kt & 1][rt] = mfma32_fp8(a[ks], qf[rt][ks], acc[kt & 1][rt]);
+          }
         if (kt == 0) {
           list.insert(pending, pending_beta);
         } else {
@@ -255,7 +443,7 @@ __global__ __launch_bounds__(NW * 64, 2) void index_select_prefill_fp8_kernel(
 #pragma unroll
         for (int i = 0; i < 16; ++i) rmax[rt] = fmaxf(rmax[rt], acc[1][rt][i]);
       const float mine = row_tile_max<RT>(rmax, half);
-      const float score = ldexpf(mine, eq_own + (int)kexp[beta] - 127);
+      const float score = ldexpf(mine, eq_own + (K4 ? 0 : (int)kexp[beta] - 127));
       // key 0 is never inserted
       pending = (beta < beta_own && score == score) ? float_order_key(score) : 0u;
       pending_beta = beta;
@@ -309,7 +497,60 @@ struct KTileStage8 {
   }
 };
 
-template <int DI, int SEG, int RT>
+// One 4-bit key block through registers into LDS: codes in rows of
+// DI/2 + 16 bytes, then the block's 128 x DI/32 exponent bytes in row order.
+template <int DI, int NT>
+struct KTileStage4 {
+  static constexpr int kRb = DI / 2;
+  static constexpr int kCpr = kRb / 16;
+  static constexpr int kCodeChunks = kBlock * kCpr;
+  static constexpr int kXb = DI / 32;
+  static constexpr int kExpChunks = kBlock * kXb / 16;
+  static constexpr int kLd = kRb + 16;
+  static constexpr int kExpOff = kBlock * kLd;
+  static constexpr int kBytes = kExpOff + kBlock * kXb;
+  // code chunks per thread (a partial pass when the block has fewer chunks
+  // than threads), then one exponent chunk for threads below kExpChunks
+  static constexpr int kCodePer = (kCodeChunks + NT - 1) / NT;
+  static_assert(kExpChunks <= NT, "one exponent chunk per thread");
+  typedef unsigned v4u __attribute__((ext_vector_type(4)));
+  v4u rc[kCodePer];
+  v4u rx;
+
+  __device__ inline void load(const uint8_t* __restrict__ codes, const uint8_t* __restrict__ exps,
+                              int tid) {
+#pragma unroll
+    for (int i = 0; i < kCodePer; ++i) {
+      const int c = tid + i * NT;
+      if (kCodeChunks % NT == 0 || c < kCodeChunks)
+        rc[i] = *reinterpret_cast<const v4u*>(codes + (size_t)(c / kCpr) * kRb + (c % kCpr) * 16);
+    }
+    if (tid < kExpChunks) rx = *reinterpret_cast<const v4u*>(exps + tid * 16);
+  }
+  __device__ inline void store(uint8_t* lds, int tid) const {
+#pragma unroll
+    for (int i = 0; i < kCodePer; ++i) {
+      const int c = tid + i * NT;
+      if (kCodeChunks % NT == 0 || c < kCodeChunks)
+        *reinterpret_cast<v4u*>(lds + (c / kCpr) * kLd + (c % kCpr) * 16) = rc[i];
+    }
+    if (tid < kExpChunks) *reinterpret_cast<v4u*>(lds + kExpOff + tid * 16) = rx;
+  }
+  // A fragment of k-step ks for lane half h of the row at `arow` (see KRing4)
+  __device__ static inline i32x8 frag(const uint8_t* arow, int ks, int h) {
+    uint4 v = make_uint4(0, 0, 0, 0);
+    if (DI > 32 || h == 0) v = *reinterpret_cast<const uint4*>(arow + (DI > 32 ? (2 * ks + h) * 16 : 0));
+    return as_i32x8(v, make_uint4(0, 0, 0, 0));
+  }
+  __device__ static inline uint32_t exps(const uint8_t* lds, int m) {
+    const uint8_t* p = lds + kExpOff + m * kXb;
+    if constexpr (kXb == 4) return *reinterpret_cast<const uint32_t*>(p);
+    else if constexpr (kXb == 2) return *reinterpret_cast<const uint16_t*>(p);
+    else return *p;
+  }
+};
+
+template <int DI, int SEG, int RT, bool K4>
 __global__ __launch_bounds__(256) void index_score_decode_fp8_kernel(
     const uint8_t* __restrict__ q8, const uint8_t* __restrict__ qe, const uint8_t* __restrict__ k8,
     const uint8_t* __restrict__ ke, const int32_t* __restrict__ cu_q,
@@ -317,9 +558,11 @@ __global__ __launch_bounds__(256) void index_score_decode_fp8_kernel(
     float* __restrict__ S, long long ld) {
   constexpr int NT = 256;
   constexpr int KS = DI >= 64 ? DI / 64 : 1;
-  constexpr int LD = KTileStage8<DI, NT>::kLd;
+  using Stage = typename std::conditional<K4, KTileStage4<DI, NT>, KTileStage8<DI, NT>>::type;
+  constexpr int LD = Stage::kLd;
   constexpr int NR = 32 * RT;
-  __shared__ __attribute__((aligned(16))) uint8_t lds[2][kBlock * LD];
+  constexpr int TILE = K4 ? KTileStage4<DI, NT>::kBytes : kBlock * LD;
+  __shared__ __attribute__((aligned(16))) uint8_t lds[2][TILE];
   __shared__ float red[2][4][NR];
 
   const int b = blockIdx.y;
@@ -346,30 +589,26 @@ __global__ __launch_bounds__(256) void index_score_decode_fp8_kernel(
     const int n = rt * 32 + col;
     const uint8_t* src = q8 + ((size_t)qa * G + n) * DI;
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      uint4 lo = make_uint4(0, 0, 0, 0), hi = make_uint4(0, 0, 0, 0);
-      if (n < nrows) {
-        if constexpr (DI == 32) {
-          lo = *reinterpret_cast<const uint4*>(src + half * 16);
-        } else {
-          lo = *reinterpret_cast<const uint4*>(src + ks * 64 + half * 32);
-          hi = *reinterpret_cast<const uint4*>(src + ks * 64 + half * 32 + 16);
-        }
-      }
-      qf[rt][ks] = as_i32x8(lo, hi);
-    }
+    for (int ks = 0; ks < KS; ++ks)
+      qf[rt][ks] = n < nrows ? q_frag<DI, K4>(src, ks, half) : i32x8{};
   }
 
-  KTileStage8<DI, NT> stage;
-  stage.load(k8 + kv.block_row(b, koff, b0) * DI, tid);
+  // stage key block b0 (codes, and the exponents of 4-bit keys)
+  Stage stage;
+  {
+    const size_t row0 = kv.block_row(b, koff, b0);
+    if constexpr (K4) stage.load(k8 + row0 * (DI / 2), ke + row0 * (DI / 32), tid);
+    else stage.load(k8 + row0 * DI, tid);
+  }
   stage.store(lds[0], tid);
   __syncthreads();
 
   // the four waves' partial maxima of block `blk`, scaled by 2^(eq + ek) -> S
+  // (4-bit keys: their exponents are already inside the MFMA results)
   auto finish = [&](int it, int blk) __attribute__((always_inline)) {
     if (wave != 0) return;
     const size_t srow = (size_t)(qa - r0) * G;
-    const int ek = (int)ke[kv.block_index(b, blk, nb_max)] - 127;
+    const int ek = K4 ? 0 : (int)ke[kv.block_index(b, blk, nb_max)] - 127;
 #pragma unroll
     for (int j = 0; j < (NR + 63) / 64; ++j) {
       const int n = j * 64 + lane;
@@ -384,23 +623,34 @@ __global__ __launch_bounds__(256) void index_score_decode_fp8_kernel(
 
   for (int beta = b0; beta < b1; ++beta) {
     const int it = beta - b0;
-    stage.load(k8 + kv.block_row(b, koff, min(beta + 1, b1 - 1)) * DI, tid);
+    {
+      const size_t row1 = kv.block_row(b, koff, min(beta + 1, b1 - 1));
+      if constexpr (K4) stage.load(k8 + row1 * (DI / 2), ke + row1 * (DI / 32), tid);
+      else stage.load(k8 + row1 * DI, tid);
+    }
     if (it > 0) finish(it - 1, beta - 1);
     const uint8_t* arow = lds[it & 1] + (wave * 32 + col) * LD;
     f32x16 acc[RT];
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) acc[rt] = f32x16{};
+    uint32_t kx = 0;
+    if constexpr (K4) kx = KTileStage4<DI, NT>::exps(lds[it & 1], wave * 32 + col);
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       i32x8 a;
-      if constexpr (DI == 32) {
+      if constexpr (K4) {
+        a = KTileStage4<DI, NT>::frag(arow, ks, half);
+      } else if constexpr (DI == 32) {
         a = as_i32x8(*reinterpret_cast<const uint4*>(arow + half * 16), make_uint4(0, 0, 0, 0));
       } else {
         a = as_i32x8(*reinterpret_cast<const uint4*>(arow + ks * 64 + half * 32),
                      *reinterpret_cast<const uint4*>(arow + ks * 64 + half * 32 + 16));
       }
 #pragma unroll
-      for (int rt = 0; rt < RT; ++rt) acc[rt] = mfma32_fp8(a, qf[rt][ks], acc[rt]);
+      for (int rt = 0; rt < RT; ++rt) {
+        if constexpr (K4) acc[rt] = mfma32_k4(a, qf[rt][ks], acc[rt], k4_scale(kx, ks, half));
+        else acc[rt] = mfma32_fp8(a, qf[rt][ks], acc[rt]);
+      }
     }
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) {
@@ -455,7 +705,7 @@ hipError_t launch_quantize_index_fp8(int DI, const void* q, const void* k, const
   return hipErrorInvalidValue;
 }
 
-template <int DI, int KCAP>
+template <int DI, int KCAP, bool K4>
 static hipError_t launch_prefill8_t(const void* q8, const uint8_t* qe, const void* k8,
                                     const uint8_t* ke, const int32_t* cu_q, const int32_t* cu_k,
                                     KvMap kv, int batch, int G, int nb_max, int max_q_len, int top_k,
@@ -463,19 +713,19 @@ static hipError_t launch_prefill8_t(const void* q8, const uint8_t* qe, const voi
   const int qt = kFp8Rows / G;
   if (qt < 1) return hipErrorInvalidValue;
   dim3 grid((max_q_len + qt - 1) / qt, batch);
-  hipLaunchKernelGGL((index_select_prefill_fp8_kernel<DI, kFp8RT, kFp8NW, KCAP>), grid,
+  hipLaunchKernelGGL((index_select_prefill_fp8_kernel<DI, kFp8RT, kFp8NW, KCAP, K4>), grid,
                      dim3(kFp8NW * 64), 0, st, (const uint8_t*)q8, qe, (const uint8_t*)k8, ke, cu_q,
                      cu_k, kv, G, nb_max, qt, top_k, sel, sel_score);
   return hipGetLastError();
 }
 
-template <int DI>
+template <int DI, bool K4>
 static hipError_t launch_prefill8_di(const void* q8, const uint8_t* qe, const void* k8,
                                      const uint8_t* ke, const int32_t* cu_q, const int32_t* cu_k,
                                      KvMap kv, int batch, int G, int nb_max, int max_q_len,
                                      int top_k, int32_t* sel, float* sel_score, hipStream_t st) {
   const int km = top_k - 1;
-#define MSA_PF8(K) launch_prefill8_t<DI, K>(q8, qe, k8, ke, cu_q, cu_k, kv, batch, G, nb_max, max_q_len, top_k, sel, sel_score, st)
+#define MSA_PF8(K) launch_prefill8_t<DI, K, K4>(q8, qe, k8, ke, cu_q, cu_k, kv, batch, G, nb_max, max_q_len, top_k, sel, sel_score, st)
   if (km <= 1) return MSA_PF8(1);
   if (km <= 2) return MSA_PF8(2);
   if (km <= 4) return MSA_PF8(4);
@@ -486,25 +736,27 @@ static hipError_t launch_prefill8_di(const void* q8, const uint8_t* qe, const vo
 }
 
 hipError_t launch_index_select_prefill_fp8(const void* q8, const uint8_t* qe, const void* k8,
-                                           const uint8_t* ke, const int32_t* cu_q,
+                                           const uint8_t* ke, bool k4, const int32_t* cu_q,
                                            const int32_t* cu_k, KvMap kv, int batch, int G, int DI,
                                            int nb_max, int max_q_len, int top_k, int32_t* sel,
                                            float* sel_score, hipStream_t st) {
+#define MSA_PF8DI(D, K) launch_prefill8_di<D, K>(q8, qe, k8, ke, cu_q, cu_k, kv, batch, G, nb_max, max_q_len, top_k, sel, sel_score, st)
   switch (DI) {
-    case 32: return launch_prefill8_di<32>(q8, qe, k8, ke, cu_q, cu_k, kv, batch, G, nb_max, max_q_len, top_k, sel, sel_score, st);
-    case 64: return launch_prefill8_di<64>(q8, qe, k8, ke, cu_q, cu_k, kv, batch, G, nb_max, max_q_len, top_k, sel, sel_score, st);
-    case 128: return launch_prefill8_di<128>(q8, qe, k8, ke, cu_q, cu_k, kv, batch, G, nb_max, max_q_len, top_k, sel, sel_score, st);
+    case 32: return k4 ? MSA_PF8DI(32, true) : MSA_PF8DI(32, false);
+    case 64: return k4 ? MSA_PF8DI(64, true) : MSA_PF8DI(64, false);
+    case 128: return k4 ? MSA_PF8DI(128, true) : MSA_PF8DI(128, false);
   }
+#undef MSA_PF8DI
   return hipErrorInvalidValue;
 }
 
-template <int DI>
+template <int DI, bool K4>
 static hipError_t launch_decode8_di(const void* q8, const uint8_t* qe, const void* k8,
                                     const uint8_t* ke, const int32_t* cu_q, const int32_t* cu_k,
                                     KvMap kv, int batch, int G, int nb_max, int rows, int r0, int r1,
                                     float* S, long long ld, hipStream_t st) {
   dim3 grid((nb_max + kFp8DecodeSeg - 1) / kFp8DecodeSeg, batch);
-#define MSA_DEC8(RT) hipLaunchKernelGGL((index_score_decode_fp8_kernel<DI, kFp8DecodeSeg, RT>), grid, dim3(256), 0, st, (const uint8_t*)q8, qe, (const uint8_t*)k8, ke, cu_q, cu_k, kv, G, nb_max, r0, r1, S, ld)
+#define MSA_DEC8(RT) hipLaunchKernelGGL((index_score_decode_fp8_kernel<DI, kFp8DecodeSeg, RT, K4>), grid, dim3(256), 0, st, (const uint8_t*)q8, qe, (const uint8_t*)k8, ke, cu_q, cu_k, kv, G, nb_max, r0, r1, S, ld)
   if (rows <= 32) MSA_DEC8(1);
   else if (rows <= 64) MSA_DEC8(2);
   else if (rows <= 128) MSA_DEC8(4);
@@ -514,14 +766,44 @@ static hipError_t launch_decode8_di(const void* q8, const uint8_t* qe, const voi
 }
 
 hipError_t launch_index_score_decode_fp8(const void* q8, const uint8_t* qe, const void* k8,
-                                         const uint8_t* ke, const int32_t* cu_q,
+                                         const uint8_t* ke, bool k4, const int32_t* cu_q,
                                          const int32_t* cu_k, KvMap kv, int batch, int G, int DI,
                                          int nb_max, int rows, int r0, int r1, float* S,
                                          long long ld, hipStream_t st) {
+#define MSA_D8DI(D, K) launch_decode8_di<D, K>(q8, qe, k8, ke, cu_q, cu_k, kv, batch, G, nb_max, rows, r0, r1, S, ld, st)
   switch (DI) {
-    case 32: return launch_decode8_di<32>(q8, qe, k8, ke, cu_q, cu_k, kv, batch, G, nb_max, rows, r0, r1, S, ld, st);
-    case 64: return launch_decode8_di<64>(q8, qe, k8, ke, cu_q, cu_k, kv, batch, G, nb_max, rows, r0, r1, S, ld, st);
-    case 128: return launch_decode8_di<128>(q8, qe, k8, ke, cu_q, cu_k, kv, batch, G, nb_max, rows, r0, r1, S, ld, st);
+    case 32: return k4 ? MSA_D8DI(32, true) : MSA_D8DI(32, false);
+    case 64: return k4 ? MSA_D8DI(64, true) : MSA_D8DI(64, false);
+    case 128: return k4 ? MSA_D8DI(128, true) : MSA_D8DI(128, false);
+  }
+#undef MSA_D8DI
+  return hipErrorInvalidValue;
+}
+
+// 4-bit index keys: queries as for the 8-bit path, keys per 32-element group
+template <int DI>
+static hipError_t launch_quantize_q8k4_di(const void* q, const void* k, const int32_t* cu_k,
+                                          KvMap kv, int batch, int nb_max, long long q_rows,
+                                          void* q8, uint8_t* qe, void* k4, uint8_t* ke4,
+                                          hipStream_t st) {
+  if (q_rows > 0) {
+    const long long threads = q_rows * (DI / 8);
+    hipLaunchKernelGGL((quantize_q_kernel<DI>), dim3((unsigned)((threads + 255) / 256)), dim3(256),
+                       0, st, (const uint16_t*)q, q_rows, (uint8_t*)q8, qe);
+  }
+  if (nb_max > 0)
+    hipLaunchKernelGGL((quantize_k4_kernel<DI>), dim3(nb_max, batch), dim3(256), 0, st,
+                       (const uint16_t*)k, cu_k, kv, (uint8_t*)k4, ke4);
+  return hipGetLastError();
+}
+
+hipError_t launch_quantize_index_q8k4(int DI, const void* q, const void* k, const int32_t* cu_k,
+                                      KvMap kv, int batch, int nb_max, long long q_rows, void* q8,
+                                      uint8_t* qe, void* k4, uint8_t* ke4, hipStream_t st) {
+  switch (DI) {
+    case 32: return launch_quantize_q8k4_di<32>(q, k, cu_k, kv, batch, nb_max, q_rows, q8, qe, k4, ke4, st);
+    case 64: return launch_quantize_q8k4_di<64>(q, k, cu_k, kv, batch, nb_max, q_rows, q8, qe, k4, ke4, st);
+    case 128: return launch_quantize_q8k4_di<128>(q, k, cu_k, kv, batch, nb_max, q_rows, q8, qe, k4, ke4, st);
   }
   return hipErrorInvalidValue;
 }

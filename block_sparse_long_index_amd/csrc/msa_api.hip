@@ -50,11 +50,13 @@ size_t project_workspace_bytes(int, int);
 hipError_t launch_quantize_index_fp8(int, const void*, const void*, const int32_t*, KvMap, int, int,
                                      long long, void*, uint8_t*, void*, uint8_t*, hipStream_t);
 hipError_t launch_index_select_prefill_fp8(const void*, const uint8_t*, const void*, const uint8_t*,
-                                           const int32_t*, const int32_t*, KvMap, int, int, int,
-                                           int, int, int, int32_t*, float*, hipStream_t);
+                                           bool, const int32_t*, const int32_t*, KvMap, int, int,
+                                           int, int, int, int, int32_t*, float*, hipStream_t);
 hipError_t launch_index_score_decode_fp8(const void*, const uint8_t*, const void*, const uint8_t*,
-                                         const int32_t*, const int32_t*, KvMap, int, int, int, int,
-                                         int, int, int, float*, long long, hipStream_t);
+                                         bool, const int32_t*, const int32_t*, KvMap, int, int, int,
+                                         int, int, int, int, float*, long long, hipStream_t);
+hipError_t launch_quantize_index_q8k4(int, const void*, const void*, const int32_t*, KvMap, int, int,
+                                      long long, void*, uint8_t*, void*, uint8_t*, hipStream_t);
 }  // namespace msa
 
 namespace {
@@ -198,12 +200,14 @@ bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 // recorded on the launch stream; msa_profile_collect() waits for them.
 enum KernelId { K_INDEX_PREFILL, K_INDEX_DECODE, K_TOPK, K_LISTS, K_ATTEND, K_MERGE,
                 K_QUANT_FP8, K_INDEX_PREFILL_FP8, K_INDEX_DECODE_FP8, K_PROJECT, K_MASS,
-                K_INDEX_KL, K_QUANT_MAIN_FP8 };
+                K_INDEX_KL, K_QUANT_MAIN_FP8, K_QUANT_Q8K4, K_INDEX_PREFILL_Q8K4,
+                K_INDEX_DECODE_Q8K4 };
 const char* const kKernelNames[MSA_PROFILE_KERNELS] = {
     "index_select_prefill", "index_score_decode", "topk_select",
     "build_lists", "attend_blocks", "merge_partials",
     "quantize_index_fp8", "index_select_prefill_fp8", "index_score_decode_fp8",
-    "index_project", "block_mass", "index_kl", "quantize_main_fp8"};
+    "index_project", "block_mass", "index_kl", "quantize_main_fp8", "quantize_index_q8k4",
+    "index_select_prefill_q8k4", "index_score_decode_q8k4"};
 
 std::atomic<bool> g_prof_on{false};
 std::mutex g_prof_mu;
@@ -375,31 +379,34 @@ msa_status_t msa_index_quantize_fp8(const msa_dims_t* dims, const void* q_idx, c
   return e == hipSuccess ? MSA_OK : hip_fail(e);
 }
 
-msa_status_t msa_index_select_fp8(const msa_dims_t* dims, const void* q_idx8, const uint8_t* q_exp,
-                                  const void* k_idx8, const uint8_t* k_exp,
-                                  const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
-                                  int32_t* sel, float* sel_score, void* workspace,
-                                  size_t workspace_bytes, void* stream) {
+namespace {
+
+// The Index Branch on 8-bit query codes against 8-bit (k4 = false) or 4-bit
+// (k4 = true) key codes; both share the selection kernels' organisation.
+msa_status_t select_q8(const msa_dims_t* dims, const void* q_idx8, const uint8_t* q_exp,
+                       const void* k_codes, const uint8_t* k_exp, bool k4,
+                       const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, int32_t* sel,
+                       float* sel_score, void* workspace, size_t workspace_bytes, void* stream) {
   Derived x;
   msa_status_t s = check_dims(dims, &x);
   if (s != MSA_OK) return s;
-  if (x.nb_max > msa::fp8_max_blocks_per_sequence())
+  if (!k4 && x.nb_max > msa::fp8_max_blocks_per_sequence())
     return fail(MSA_ERR_UNSUPPORTED, "max_k_len too long for the fp8 index kernels (16384 blocks)");
   if (x.total_q == 0) return MSA_OK;
-  if (!q_idx8 || !q_exp || !k_idx8 || !k_exp || !cu_seqlens_q || !cu_seqlens_k || !sel || !workspace)
+  if (!q_idx8 || !q_exp || !k_codes || !k_exp || !cu_seqlens_q || !cu_seqlens_k || !sel || !workspace)
     return fail(MSA_ERR_NULL_ARG, "a required pointer is NULL");
-  if (!aligned16(q_idx8) || !aligned16(k_idx8) || !aligned16(sel) || !aligned16(workspace) ||
-      (sel_score && !aligned16(sel_score)))
+  if (!aligned16(q_idx8) || !aligned16(k_codes) || !aligned16(sel) || !aligned16(workspace) ||
+      (sel_score && !aligned16(sel_score)) || (k4 && !aligned16(k_exp)))
     return fail(MSA_ERR_ALIGNMENT, "tensor pointers must be 16-byte aligned");
   if (workspace_bytes < ws_select(dims, x))
     return fail(MSA_ERR_WORKSPACE_TOO_SMALL, "index_select workspace too small");
   hipStream_t st = (hipStream_t)stream;
   if (!x.decode_path) {
-    ProfScope ps(K_INDEX_PREFILL_FP8, st);
-    hipError_t e = msa::launch_index_select_prefill_fp8(q_idx8, q_exp, k_idx8, k_exp, cu_seqlens_q,
-                                                        cu_seqlens_k, x.kv, dims->batch, x.G, x.DI,
-                                                        x.nb_max, dims->max_q_len, x.top_k, sel,
-                                                        sel_score, st);
+    ProfScope ps(k4 ? K_INDEX_PREFILL_Q8K4 : K_INDEX_PREFILL_FP8, st);
+    hipError_t e = msa::launch_index_select_prefill_fp8(q_idx8, q_exp, k_codes, k_exp, k4,
+                                                        cu_seqlens_q, cu_seqlens_k, x.kv,
+                                                        dims->batch, x.G, x.DI, x.nb_max,
+                                                        dims->max_q_len, x.top_k, sel, sel_score, st);
     return e == hipSuccess ? MSA_OK : hip_fail(e);
   }
   float* S = (float*)(((uintptr_t)workspace + 255) & ~(uintptr_t)255);
@@ -409,8 +416,8 @@ msa_status_t msa_index_select_fp8(const msa_dims_t* dims, const void* q_idx8, co
     const long long ld = (long long)(z - a) * x.G;
     hipError_t e;
     {
-      ProfScope ps(K_INDEX_DECODE_FP8, st);
-      e = msa::launch_index_score_decode_fp8(q_idx8, q_exp, k_idx8, k_exp, cu_seqlens_q,
+      ProfScope ps(k4 ? K_INDEX_DECODE_Q8K4 : K_INDEX_DECODE_FP8, st);
+      e = msa::launch_index_score_decode_fp8(q_idx8, q_exp, k_codes, k_exp, k4, cu_seqlens_q,
                                              cu_seqlens_k, x.kv, dims->batch, x.G, x.DI, x.nb_max,
                                              dims->max_q_len * x.G, a, z, S, ld, st);
     }
@@ -421,6 +428,48 @@ msa_status_t msa_index_select_fp8(const msa_dims_t* dims, const void* q_idx8, co
     if (e != hipSuccess) return hip_fail(e);
   }
   return MSA_OK;
+}
+
+}  // namespace
+
+msa_status_t msa_index_select_fp8(const msa_dims_t* dims, const void* q_idx8, const uint8_t* q_exp,
+                                  const void* k_idx8, const uint8_t* k_exp,
+                                  const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                                  int32_t* sel, float* sel_score, void* workspace,
+                                  size_t workspace_bytes, void* stream) {
+  return select_q8(dims, q_idx8, q_exp, k_idx8, k_exp, false, cu_seqlens_q, cu_seqlens_k, sel,
+                   sel_score, workspace, workspace_bytes, stream);
+}
+
+msa_status_t msa_index_quantize_q8k4(const msa_dims_t* dims, const void* q_idx, const void* k_idx,
+                                     const int32_t* cu_seqlens_k, void* q_idx8, uint8_t* q_exp,
+                                     void* k_idx4, uint8_t* k_exp4, void* stream) {
+  Derived x;
+  msa_status_t s = check_dims(dims, &x);
+  if (s != MSA_OK) return s;
+  const bool has_q = x.total_q > 0 && q_idx, has_k = dims->total_k > 0 && k_idx;
+  if ((has_q && (!q_idx8 || !q_exp)) || (has_k && (!k_idx4 || !k_exp4 || !cu_seqlens_k)))
+    return fail(MSA_ERR_NULL_ARG, "a required pointer is NULL");
+  if ((has_q && (!aligned16(q_idx) || !aligned16(q_idx8))) ||
+      (has_k && (!aligned16(k_idx) || !aligned16(k_idx4) || !aligned16(k_exp4))))
+    return fail(MSA_ERR_ALIGNMENT, "tensor pointers must be 16-byte aligned");
+  if (!has_q && !has_k) return MSA_OK;
+  hipStream_t st = (hipStream_t)stream;
+  ProfScope ps(K_QUANT_Q8K4, st);
+  hipError_t e = msa::launch_quantize_index_q8k4(x.DI, q_idx, k_idx, cu_seqlens_k, x.kv, dims->batch,
+                                                 has_k ? x.nb_max : 0,
+                                                 has_q ? x.total_q * x.G : 0, q_idx8, q_exp, k_idx4,
+                                                 k_exp4, st);
+  return e == hipSuccess ? MSA_OK : hip_fail(e);
+}
+
+msa_status_t msa_index_select_q8k4(const msa_dims_t* dims, const void* q_idx8, const uint8_t* q_exp,
+                                   const void* k_idx4, const uint8_t* k_exp4,
+                                   const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                                   int32_t* sel, float* sel_score, void* workspace,
+                                   size_t workspace_bytes, void* stream) {
+  return select_q8(dims, q_idx8, q_exp, k_idx4, k_exp4, true, cu_seqlens_q, cu_seqlens_k, sel,
+                   sel_score, workspace, workspace_bytes, stream);
 }
 
 msa_status_t msa_build_block_query_lists(const msa_dims_t* dims, const int32_t* sel,

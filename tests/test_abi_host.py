@@ -167,6 +167,34 @@ def test_fp8_entry_points_validate_on_host():
     assert s8(ctypes.byref(empty), None, None, None, None, None, None, None, None, None, big, None) == 0
 
 
+def test_q8k4_entry_points_validate_on_host():
+    d = _dims()
+    P = ctypes.c_void_p
+    ok = P(0x10000)
+    odd = P(0x10004)
+    big = ctypes.c_size_t(1 << 40)
+    qz = lib.msa_index_quantize_q8k4
+    # a side with an input needs its outputs
+    assert qz(ctypes.byref(d), ok, None, None, None, ok, None, None, None) == 1
+    assert qz(ctypes.byref(d), None, ok, ok, None, None, ok, None, None) == 1
+    assert qz(ctypes.byref(d), None, ok, None, None, None, ok, ok, None) == 1
+    assert qz(ctypes.byref(d), ok, ok, ok, odd, ok, ok, None, None) == 1     # k_exp4 NULL
+    assert qz(ctypes.byref(d), ok, ok, ok, odd, ok, ok, ok, None) == 4
+    # key codes and their exponents are read in 16-byte pieces
+    assert qz(ctypes.byref(d), None, odd, ok, None, None, ok, ok, None) == 4
+    assert qz(ctypes.byref(d), None, ok, ok, None, None, odd, ok, None) == 4
+    assert qz(ctypes.byref(d), None, ok, ok, None, None, ok, odd, None) == 4
+    s4 = lib.msa_index_select_q8k4
+    assert s4(ctypes.byref(d), ok, None, ok, ok, ok, ok, ok, None, ok, big, None) == 1
+    assert s4(ctypes.byref(d), ok, ok, odd, ok, ok, ok, ok, None, ok, big, None) == 4
+    assert s4(ctypes.byref(d), ok, ok, ok, odd, ok, ok, ok, None, ok, big, None) == 4
+    assert s4(ctypes.byref(d), ok, ok, ok, ok, ok, ok, ok, None, ok, ctypes.c_size_t(8), None) == 5
+    empty = _dims(total_q=0, total_k=0, max_q_len=0, max_k_len=0)
+    assert qz(ctypes.byref(empty), None, None, None, None, None, None, None, None) == 0
+    assert qz(ctypes.byref(d), None, None, None, None, None, None, None, None) == 0
+    assert s4(ctypes.byref(empty), None, None, None, None, None, None, None, None, None, big, None) == 0
+
+
 def test_projection_entry_point_validates_on_host():
     d = _dims()
     P = ctypes.c_void_p
