@@ -6,7 +6,7 @@ msa_index_select -> msa_build_block_query_lists -> msa_attend, through the C
 ABI on one stream.  Prints ONE JSON line on stdout; progress goes to stderr.
 
     python bench.py [--steps K] [--warmup W] [--workload p128k|p1m|p32k|decode|tiny]
-                    [--index bf16|fp8]
+                    [--index bf16|fp8|q8k4]
 
 The default workload is the 128K-token single-layer prefill (64 query heads /
 8 KV heads, head dim 128, index dim 128, top-k 16 incl. the local block).
@@ -92,6 +92,14 @@ def work_model(w) -> dict:
                         + T * (Hq * d * 2 * 2 + G * (di + 1)))
     index_decode_fp8_bytes = dec_kidx_tokens * di + T * G * (di + 1)
     index_decode_bytes = dec_kidx_tokens * di * 2 + T * G * di * 2
+    # 4-bit index keys: di / 2 code bytes + di / 32 exponent bytes per key
+    k4_row = di / 2 + di / 32
+    quant_q8k4_bytes = T * G * (di * 3 + 1) + w.total_k * (di * 2 + k4_row)
+    if _decode_like(w):
+        quant_q8k4_bytes = T * G * (di * 3 + 1)
+    index_decode_q8k4_bytes = dec_kidx_tokens * k4_row + T * G * (di + 1)
+    decode_q8k4_bytes = (dec_kidx_tokens * k4_row + kv_once
+                         + T * (Hq * d * 2 * 2 + G * (di + 1)))
     # 8-bit Main Branch: one byte per q / k / v element (+ one exponent per (row, head) and
     # per (block, KV head)); the fp32 partials are unchanged
     kv_once_fp8 = kv_blocks * (BLOCK * d + 1) * 2
@@ -106,7 +114,8 @@ def work_model(w) -> dict:
                 attend_bytes=attend_bytes, merge_bytes=merge_bytes, topk_bytes=topk_bytes,
                 decode_bytes=decode_bytes, kv_once_bytes=kv_once, quant_bytes=quant_bytes,
                 decode_fp8_bytes=decode_fp8_bytes, index_decode_fp8_bytes=index_decode_fp8_bytes,
-                index_decode_bytes=index_decode_bytes)
+                index_decode_bytes=index_decode_bytes, quant_q8k4_bytes=quant_q8k4_bytes,
+                index_decode_q8k4_bytes=index_decode_q8k4_bytes, decode_q8k4_bytes=decode_q8k4_bytes)
 
 
 # ---------------------------------------------------------------------------
@@ -146,6 +155,30 @@ class _LazyDevRows:
             x = self.t.index_select(0, r)
             x = x[:, int(rest[0])] if rest else x
         return x.double().cpu().numpy()
+
+
+class _SliceDequant4:
+    """Index keys as the oracle sees them after 4-bit quantisation, one
+    sequence slice at a time (keys scale per 32 elements of a row, so a slice
+    quantises as the whole cache does).  prefetch() quantises the sequences of
+    the given query rows before the oracle is timed: a decode step's key cache
+    is stored quantised, outside the step."""
+
+    def __init__(self, kidx, f4):
+        self.kidx, self.f4, self.cache = kidx, f4, {}
+        self.shape = kidx.shape
+
+    def __getitem__(self, sl):
+        assert isinstance(sl, slice) and (sl.step in (None, 1))
+        key = (sl.start, sl.stop)
+        if key not in self.cache:
+            self.cache[key] = self.f4.dequantize_k_idx4(*self.f4.quantize_k_idx4(self.kidx[sl]))
+        return self.cache[key]
+
+    def prefetch(self, rows, cuq, cuk):
+        for r in rows:
+            b = int(np.searchsorted(cuq, r, side="right") - 1)
+            self[int(cuk[b]):int(cuk[b + 1])]
 
 
 _W = {}   # per-worker cache: attached shared arrays and the oracle problem
@@ -347,9 +380,12 @@ def main():
     ap.add_argument("--copy-gib", type=float, default=0.0,
                     help="before the workload, run three device copies of this many GiB (fp32): a "
                          "kernel of known traffic for scaling the FETCH_SIZE/WRITE_SIZE counters")
-    ap.add_argument("--index", choices=["bf16", "fp8"], default="bf16",
-                    help="Index Branch precision: bf16 projections, or quantised in the step to "
-                         "FP8 E4M3 with power-of-two scales and scored on the fp8 matrix cores")
+    ap.add_argument("--index", choices=["bf16", "fp8", "q8k4"], default="bf16",
+                    help="Index Branch precision: bf16 projections; quantised in the step to "
+                         "FP8 E4M3 with power-of-two scales and scored on the fp8 matrix cores "
+                         "(fp8); or 8-bit queries with 4-bit E2M1 keys scaled per 32 elements, "
+                         "scored on the microscaled matrix cores (q8k4).  A decode step's "
+                         "index-key cache is stored quantised; only its new queries are quantised")
     ap.add_argument("--main", choices=["bf16", "fp8"], default="bf16",
                     help="Main Branch inputs: bf16 q/k/v, or FP8 E4M3 codes with power-of-two "
                          "scales (quantised in the step; a decode step's key/value cache is "
@@ -427,12 +463,17 @@ def main():
         kl_out = dict(mass=torch.empty((w.total_q, w.num_kv_heads, w.top_k), dtype=torch.float32, device=dev),
                       kl=torch.empty((w.total_q, w.num_kv_heads), dtype=torch.float32, device=dev))
     fp8 = msa.Fp8Index(dims, dev) if args.index == "fp8" else None
+    qk = msa.Q8K4Index(dims, dev) if args.index == "q8k4" else None
     log(f"[bench] workspace {bufs.workspace.numel() / 2**30:.2f} GiB; index branch {args.index}")
     # fp8 decode: the index-key cache is stored quantised (quantised once, outside the step);
     # each step quantises only its new index queries.  Prefill quantises both in the step.
     step_k_idx = kic
     if fp8 is not None and _decode_like(w):
         msa.index_quantize_fp8(dims, None, kic, t["cu_seqlens_k"], fp8)
+        torch.cuda.synchronize()
+        step_k_idx = None
+    if qk is not None and _decode_like(w):
+        msa.index_quantize_q8k4(dims, None, kic, t["cu_seqlens_k"], qk)
         torch.cuda.synchronize()
         step_k_idx = None
 
@@ -459,7 +500,7 @@ def main():
                               t["cu_seqlens_k"], t["q_idx"], kic, bufs.workspace)
         if kl_out is None:
             msa.msa_forward(dims, t["q"], step_k, step_v, t["q_idx"], step_k_idx, t["cu_seqlens_q"],
-                            t["cu_seqlens_k"], bufs, fp8=fp8, fp8_main=f8m)
+                            t["cu_seqlens_k"], bufs, fp8=fp8, fp8_main=f8m, q8k4=qk)
             return
         # the forward with the KL-alignment target (bf16 index branch)
         msa.index_select(dims, t["q_idx"], kic, t["cu_seqlens_q"], t["cu_seqlens_k"],
@@ -553,18 +594,22 @@ def main():
             a = wm["project_flops"] / n_launch / sec
             return dict(bound="mfma", achieved=a / 1e12, peak=PEAK_BF16_FLOPS / 1e12, unit="TFLOP/s",
                         frac=a / PEAK_BF16_FLOPS, traffic=traffic_record(name), dtype="bf16")
-        if name in ("index_select_prefill", "index_select_prefill_fp8"):
-            peak = PEAK_FP8_FLOPS if name.endswith("fp8") else PEAK_BF16_FLOPS
+        if name in ("index_select_prefill", "index_select_prefill_fp8", "index_select_prefill_q8k4"):
+            # E2M1 x E4M3 runs at the fp8 rate (an 8-bit operand sets the MFMA's cycle count)
+            peak = PEAK_BF16_FLOPS if name == "index_select_prefill" else PEAK_FP8_FLOPS
             a = wm["index_flops"] / n_launch / sec
             return dict(bound="mfma", achieved=a / 1e12, peak=peak / 1e12, unit="TFLOP/s",
                         frac=a / peak, traffic=traffic_record(name),
-                        dtype="fp8 e4m3" if name.endswith("fp8") else "bf16")
+                        dtype={"index_select_prefill": "bf16", "index_select_prefill_fp8": "fp8 e4m3",
+                               "index_select_prefill_q8k4": "e2m1 keys x e4m3 queries"}[name])
         bytes_ = {"attend_blocks": wm["attend_bytes" if f8m is None else "attend_bytes_fp8"],
                   "merge_partials": wm["merge_bytes"],
                   "quantize_main_fp8": wm["main_quant_bytes"],
                   "topk_select": wm["topk_bytes"],
                   "index_score_decode": wm["index_decode_bytes"],
                   "index_score_decode_fp8": wm["index_decode_fp8_bytes"],
+                  "index_score_decode_q8k4": wm["index_decode_q8k4_bytes"],
+                  "quantize_index_q8k4": wm["quant_q8k4_bytes"],
                   "quantize_index_fp8": wm["quant_bytes"]}
         if name in bytes_:
             per_launch = bytes_[name] / n_launch
@@ -583,7 +628,8 @@ def main():
     value = w.total_q / (ms_per_step / 1e3)
     extra = {}
     if decode:
-        dec_bytes = wm["decode_fp8_bytes" if fp8 is not None else "decode_bytes"]
+        dec_bytes = wm["decode_fp8_bytes" if fp8 is not None else
+                       "decode_q8k4_bytes" if qk is not None else "decode_bytes"]
         if f8m is not None:
             dec_bytes += wm["decode_kv_fp8_delta"]
         gbs = dec_bytes / (ms_per_step / 1e3) / 1e9
@@ -616,6 +662,12 @@ def main():
             kcodes, kexp = F.quantize_k_idx(kidx, cuk, nbk)
             kidx = F.dequantize_k_idx(kcodes, kexp, cuk)
             del kcodes
+        if qk is not None:
+            # 4-bit keys scale per 32 elements of a row: any slice of rows quantises alone
+            from oracle import fp8_index as F
+            from oracle import fp4_index as F4
+            kidx = (F4.dequantize_k_idx4(*F4.quantize_k_idx4(kidx)) if pooled
+                    else _SliceDequant4(kidx, F4))
         if f8m is not None:
             # the oracle attends on the dequantised q, k, v it computes itself from the bf16 inputs
             from oracle import fp8_main as FM
@@ -632,7 +684,7 @@ def main():
         def host_rows(rows):
             ridx = torch.as_tensor(rows, device=dev, dtype=torch.long)
             qi = t["q_idx"].index_select(0, ridx).float().cpu().numpy()
-            if fp8 is not None:
+            if fp8 is not None or qk is not None:
                 qi = F.dequantize_q_idx(*F.quantize_q_idx(qi))
             qh = t["q"].index_select(0, ridx).float().cpu().numpy()
             if f8m is not None:
@@ -642,6 +694,8 @@ def main():
         # per-row cost on one core, then a sample sized to the time target
         pilot = sorted(set(int(x) for x in rng.integers(0, w.total_q, size=min(6, w.total_q))))
         qh, qih = host_rows(pilot)
+        if isinstance(kidx, _SliceDequant4):     # a decode step's key cache is stored quantised
+            kidx.prefetch(pilot, cuq, cuk)
         Pp = O.Problem(_RowSubset(pilot, qh), kk, vv, _RowSubset(pilot, qih), kidx, cuq, cuk, w.top_k)
         tp0 = time.perf_counter()
         for r in pilot:
@@ -653,6 +707,8 @@ def main():
         log(f"[bench] oracle: {per_row * 1e3:.1f} ms/row on one core; sampling {len(rows)} rows "
             f"on {used} worker(s)")
         qh, qih = host_rows(rows)
+        if isinstance(kidx, _SliceDequant4):
+            kidx.prefetch(rows, cuq, cuk)
         P = O.Problem(_RowSubset(rows, qh), kk, vv, _RowSubset(rows, qih), kidx, cuq, cuk, w.top_k)
         if pooled:
             spec = dict(id=1, rows=rows, top_k=w.top_k,
@@ -669,12 +725,14 @@ def main():
         sel_g = bufs.sel.index_select(0, ridx).cpu().numpy()
         out_g = bufs.out.index_select(0, ridx).float().cpu().numpy()
         lse_g = bufs.lse.index_select(0, ridx).cpu().numpy()
-        parity = parity_on_rows(P, rows, ref, sel_g, out_g, lse_g, w.top_k, fp8=fp8 is not None)
+        parity = parity_on_rows(P, rows, ref, sel_g, out_g, lse_g, w.top_k,
+                                fp8=fp8 is not None or qk is not None)
         log(f"[bench] parity on sampled rows: {parity}")
         cpu = dict(value=len(rows) / dt, unit="tokens/s", cores=used, kind="oracle",
                    sample=f"{len(rows)} uniformly random query rows of {w.name}, each through the "
                           f"full Index and Main Branch in fp64 numpy"
                           f"{' (on the dequantised fp8 index projections)' if fp8 is not None else ''}"
+                          f"{' (on the dequantised 8-bit index queries and 4-bit index keys)' if qk is not None else ''}"
                           f"{' (on the dequantised fp8 q, k, v)' if f8m is not None else ''}; "
                           f"{used} worker process(es), 1 BLAS thread each; {dt:.1f} s")
     elif pool:
@@ -691,9 +749,10 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": ("bf16" if fp8 is None and f8m is None else
+        "dtype": ("bf16" if fp8 is None and f8m is None and qk is None else
                   (("bf16" if f8m is None else "fp8 e4m3 storage, bf16 MFMA") + " (Main Branch), "
-                   + ("bf16" if fp8 is None else "fp8 e4m3") + " (Index Branch)")),
+                   + ("fp8 e4m3" if fp8 is not None else
+                      "e4m3 queries, e2m1 keys" if qk is not None else "bf16") + " (Index Branch)")),
         "data": "synthetic",
         "graph": use_graph,
         "config": {"workload": w.name, "seq_k_lens": (w.seq_k_lens if len(w.seq_k_lens) <= 4 else

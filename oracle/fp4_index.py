@@ -26,8 +26,6 @@ F5  the selection is the bf16 path's rule on the dequantised values.
 """
 from __future__ import annotations
 
-import math
-
 import numpy as np
 
 E2M1_MAX = 6.0
@@ -61,42 +59,45 @@ def e2m1_encode(x):
     if not np.all(np.isfinite(x)) or np.any(np.abs(x) > E2M1_MAX):
         raise ValueError("e2m1_encode: finite values with |x| <= 6 only")
     a = np.abs(x)
-    i = np.clip(np.searchsorted(_POS, a, side="right") - 1, 0, 7)     # _POS[i] <= a
-    j = np.minimum(i + 1, 7)
+    i = np.zeros(a.shape, dtype=np.uint8)       # index of the largest grid value <= a
+    for v in _POS[1:]:
+        i += a >= v
+    j = np.minimum(i + 1, 7).astype(np.uint8)   # the next grid value up (i itself at 6)
     d_lo, d_hi = a - _POS[i], _POS[j] - a
     pick_hi = (d_hi < d_lo) | ((d_hi == d_lo) & (j != i) & (j % 2 == 0))
-    code = np.where(pick_hi, j, i).astype(np.uint8)
-    return np.where(np.signbit(x), code | 0x8, code).astype(np.uint8)
+    code = np.where(pick_hi, j, i)
+    return code | (np.signbit(x).astype(np.uint8) << 3)
 
 
-def scale_exponent4(amax):
-    """Smallest integer e with amax * 2^-e <= 6, clamped to [-127, 127] (F2).
+def scale_exponents4(amax):
+    """Elementwise: the smallest integer e with amax * 2^-e <= 6, clamped to
+    [-127, 127] (F2).
 
     amax = f * 2^E with f in [0.5, 1): f * 2^3 <= 6 exactly when f <= 0.75,
     so e = E - 3 then, else E - 2 (f * 2^2 < 4).  amax = 0 gives 0.
     """
-    amax = float(amax)
-    if amax == 0.0:
-        return 0
-    f, E = math.frexp(amax)
-    e = E - 3 if f <= 0.75 else E - 2
-    return max(-127, min(127, e))
+    a = np.asarray(amax, dtype=np.float64)
+    f, E = np.frexp(a)
+    e = np.where(f <= 0.75, E - 3, E - 2)
+    e = np.where(a == 0.0, 0, e)
+    return np.clip(e, -127, 127).astype(np.int64)
+
+
+def scale_exponent4(amax):
+    """scale_exponents4 of one value."""
+    return int(scale_exponents4(np.array([float(amax)]))[0])
 
 
 def quantize_k_idx4(k_idx, group=GROUP):
     """k_idx [total_k, d_idx] -> (codes uint8 [total_k, d_idx] in 0..15,
-    E8M0 bytes uint8 [total_k, d_idx / group]); one scale per `group` elements."""
+    E8M0 bytes uint8 [total_k, d_idx / group]); one scale per `group`
+    consecutive elements of a key row (F2, F3)."""
     k = np.asarray(k_idx, dtype=np.float64)
     T, D = k.shape
-    codes = np.zeros((T, D), dtype=np.uint8)
-    ex = np.zeros((T, D // group), dtype=np.uint8)
-    for t in range(T):
-        for c in range(D // group):
-            seg = k[t, c * group:(c + 1) * group]
-            e = scale_exponent4(np.abs(seg).max())
-            codes[t, c * group:(c + 1) * group] = e2m1_encode(np.ldexp(seg, -e))
-            ex[t, c] = e + E8M0_BIAS
-    return codes, ex
+    g = k.reshape(T, D // group, group)
+    e = scale_exponents4(np.abs(g).max(axis=2))                  # [T, D / group]
+    codes = e2m1_encode(np.ldexp(g, -e[:, :, None])).reshape(T, D)
+    return codes, (e + E8M0_BIAS).astype(np.uint8)
 
 
 def dequantize_k_idx4(codes, ex, group=GROUP):

@@ -76,6 +76,12 @@ def _scale_off_by_one(amax):
     return max(-127, min(127, (E - 3 if f < 0.75 else E - 2)))
 
 
+def _scales_floor_log2(amax):
+    a = np.asarray(amax, dtype=np.float64)
+    _, E = np.frexp(a)
+    return np.clip(np.where(a == 0, 0, E - 3), -127, 127).astype(np.int64)
+
+
 def _quantize_per_row(k_idx, group=F4.GROUP):
     k = np.asarray(k_idx, dtype=np.float64)
     T, D = k.shape
@@ -100,6 +106,7 @@ MUTATIONS = {
     "scale_floor_log2": [("scale_exponent4", _scale_floor_log2)],
     "scale_off_by_one": [("scale_exponent4", _scale_off_by_one)],
     "scale_per_row": [("quantize_k_idx4", _quantize_per_row)],
+    "vector_scale_floor_log2": [("scale_exponents4", _scales_floor_log2)],
     "pack_high_first": [("pack", _pack_high_first)],
 }
 
