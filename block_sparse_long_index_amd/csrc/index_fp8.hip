@@ -17,14 +17,13 @@
 // contract raw codes on the fp8 MFMA and apply the two exponents once per
 // (row, block), exactly (ldexp).
 //
-// The same kernels, instantiated with K4, read 4-bit index keys (the pages'
-// move to 4-bit keys): OCP E2M1 codes, two per byte (element 2i in the low
-// nibble), with one E8M0 exponent per 32 elements of a key row, the
-// microscaling layout that gfx950's scaled MFMA consumes directly.  The keys'
-// exponents go to the MFMA as per-lane scales; the query's exponent is applied
-// to the block maximum as before.
-#include <type_traits>
-
+// 4-bit index keys (the pages' move to 4-bit keys) are OCP E2M1 codes, two
+// per byte (element 2i in the low nibble), with one E8M0 exponent per 32
+// elements of a key row, the microscaling layout that gfx950's scaled MFMA
+// consumes directly: the keys' exponents go to the MFMA as per-lane scales and
+// the query's exponent is applied to the block maximum as before.  The prefill
+// kernel reads them when instantiated with K4; decode steps have a kernel of
+// their own (index_score_decode_k4_kernel).
 #include "fp8_common.h"
 #include "msa_common.h"
 #include "topk_common.h"
@@ -497,60 +496,7 @@ struct KTileStage8 {
   }
 };
 
-// One 4-bit key block through registers into LDS: codes in rows of
-// DI/2 + 16 bytes, then the block's 128 x DI/32 exponent bytes in row order.
-template <int DI, int NT>
-struct KTileStage4 {
-  static constexpr int kRb = DI / 2;
-  static constexpr int kCpr = kRb / 16;
-  static constexpr int kCodeChunks = kBlock * kCpr;
-  static constexpr int kXb = DI / 32;
-  static constexpr int kExpChunks = kBlock * kXb / 16;
-  static constexpr int kLd = kRb + 16;
-  static constexpr int kExpOff = kBlock * kLd;
-  static constexpr int kBytes = kExpOff + kBlock * kXb;
-  // code chunks per thread (a partial pass when the block has fewer chunks
-  // than threads), then one exponent chunk for threads below kExpChunks
-  static constexpr int kCodePer = (kCodeChunks + NT - 1) / NT;
-  static_assert(kExpChunks <= NT, "one exponent chunk per thread");
-  typedef unsigned v4u __attribute__((ext_vector_type(4)));
-  v4u rc[kCodePer];
-  v4u rx;
-
-  __device__ inline void load(const uint8_t* __restrict__ codes, const uint8_t* __restrict__ exps,
-                              int tid) {
-#pragma unroll
-    for (int i = 0; i < kCodePer; ++i) {
-      const int c = tid + i * NT;
-      if (kCodeChunks % NT == 0 || c < kCodeChunks)
-        rc[i] = *reinterpret_cast<const v4u*>(codes + (size_t)(c / kCpr) * kRb + (c % kCpr) * 16);
-    }
-    if (tid < kExpChunks) rx = *reinterpret_cast<const v4u*>(exps + tid * 16);
-  }
-  __device__ inline void store(uint8_t* lds, int tid) const {
-#pragma unroll
-    for (int i = 0; i < kCodePer; ++i) {
-      const int c = tid + i * NT;
-      if (kCodeChunks % NT == 0 || c < kCodeChunks)
-        *reinterpret_cast<v4u*>(lds + (c / kCpr) * kLd + (c % kCpr) * 16) = rc[i];
-    }
-    if (tid < kExpChunks) *reinterpret_cast<v4u*>(lds + kExpOff + tid * 16) = rx;
-  }
-  // A fragment of k-step ks for lane half h of the row at `arow` (see KRing4)
-  __device__ static inline i32x8 frag(const uint8_t* arow, int ks, int h) {
-    uint4 v = make_uint4(0, 0, 0, 0);
-    if (DI > 32 || h == 0) v = *reinterpret_cast<const uint4*>(arow + (DI > 32 ? (2 * ks + h) * 16 : 0));
-    return as_i32x8(v, make_uint4(0, 0, 0, 0));
-  }
-  __device__ static inline uint32_t exps(const uint8_t* lds, int m) {
-    const uint8_t* p = lds + kExpOff + m * kXb;
-    if constexpr (kXb == 4) return *reinterpret_cast<const uint32_t*>(p);
-    else if constexpr (kXb == 2) return *reinterpret_cast<const uint16_t*>(p);
-    else return *p;
-  }
-};
-
-template <int DI, int SEG, int RT, bool K4>
+template <int DI, int SEG, int RT>
 __global__ __launch_bounds__(256) void index_score_decode_fp8_kernel(
     const uint8_t* __restrict__ q8, const uint8_t* __restrict__ qe, const uint8_t* __restrict__ k8,
     const uint8_t* __restrict__ ke, const int32_t* __restrict__ cu_q,
@@ -558,11 +504,9 @@ __global__ __launch_bounds__(256) void index_score_decode_fp8_kernel(
     float* __restrict__ S, long long ld) {
   constexpr int NT = 256;
   constexpr int KS = DI >= 64 ? DI / 64 : 1;
-  using Stage = typename std::conditional<K4, KTileStage4<DI, NT>, KTileStage8<DI, NT>>::type;
-  constexpr int LD = Stage::kLd;
+  constexpr int LD = KTileStage8<DI, NT>::kLd;
   constexpr int NR = 32 * RT;
-  constexpr int TILE = K4 ? KTileStage4<DI, NT>::kBytes : kBlock * LD;
-  __shared__ __attribute__((aligned(16))) uint8_t lds[2][TILE];
+  __shared__ __attribute__((aligned(16))) uint8_t lds[2][kBlock * LD];
   __shared__ float red[2][4][NR];
 
   const int b = blockIdx.y;
@@ -590,25 +534,19 @@ __global__ __launch_bounds__(256) void index_score_decode_fp8_kernel(
     const uint8_t* src = q8 + ((size_t)qa * G + n) * DI;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
-      qf[rt][ks] = n < nrows ? q_frag<DI, K4>(src, ks, half) : i32x8{};
+      qf[rt][ks] = n < nrows ? q_frag<DI, false>(src, ks, half) : i32x8{};
   }
 
-  // stage key block b0 (codes, and the exponents of 4-bit keys)
-  Stage stage;
-  {
-    const size_t row0 = kv.block_row(b, koff, b0);
-    if constexpr (K4) stage.load(k8 + row0 * (DI / 2), ke + row0 * (DI / 32), tid);
-    else stage.load(k8 + row0 * DI, tid);
-  }
+  KTileStage8<DI, NT> stage;
+  stage.load(k8 + kv.block_row(b, koff, b0) * DI, tid);
   stage.store(lds[0], tid);
   __syncthreads();
 
   // the four waves' partial maxima of block `blk`, scaled by 2^(eq + ek) -> S
-  // (4-bit keys: their exponents are already inside the MFMA results)
   auto finish = [&](int it, int blk) __attribute__((always_inline)) {
     if (wave != 0) return;
     const size_t srow = (size_t)(qa - r0) * G;
-    const int ek = K4 ? 0 : (int)ke[kv.block_index(b, blk, nb_max)] - 127;
+    const int ek = (int)ke[kv.block_index(b, blk, nb_max)] - 127;
 #pragma unroll
     for (int j = 0; j < (NR + 63) / 64; ++j) {
       const int n = j * 64 + lane;
@@ -623,34 +561,23 @@ __global__ __launch_bounds__(256) void index_score_decode_fp8_kernel(
 
   for (int beta = b0; beta < b1; ++beta) {
     const int it = beta - b0;
-    {
-      const size_t row1 = kv.block_row(b, koff, min(beta + 1, b1 - 1));
-      if constexpr (K4) stage.load(k8 + row1 * (DI / 2), ke + row1 * (DI / 32), tid);
-      else stage.load(k8 + row1 * DI, tid);
-    }
+    stage.load(k8 + kv.block_row(b, koff, min(beta + 1, b1 - 1)) * DI, tid);
     if (it > 0) finish(it - 1, beta - 1);
     const uint8_t* arow = lds[it & 1] + (wave * 32 + col) * LD;
     f32x16 acc[RT];
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) acc[rt] = f32x16{};
-    uint32_t kx = 0;
-    if constexpr (K4) kx = KTileStage4<DI, NT>::exps(lds[it & 1], wave * 32 + col);
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       i32x8 a;
-      if constexpr (K4) {
-        a = KTileStage4<DI, NT>::frag(arow, ks, half);
-      } else if constexpr (DI == 32) {
+      if constexpr (DI == 32) {
         a = as_i32x8(*reinterpret_cast<const uint4*>(arow + half * 16), make_uint4(0, 0, 0, 0));
       } else {
         a = as_i32x8(*reinterpret_cast<const uint4*>(arow + ks * 64 + half * 32),
                      *reinterpret_cast<const uint4*>(arow + ks * 64 + half * 32 + 16));
       }
 #pragma unroll
-      for (int rt = 0; rt < RT; ++rt) {
-        if constexpr (K4) acc[rt] = mfma32_k4(a, qf[rt][ks], acc[rt], k4_scale(kx, ks, half));
-        else acc[rt] = mfma32_fp8(a, qf[rt][ks], acc[rt]);
-      }
+      for (int rt = 0; rt < RT; ++rt) acc[rt] = mfma32_fp8(a, qf[rt][ks], acc[rt]);
     }
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) {
@@ -664,6 +591,123 @@ __global__ __launch_bounds__(256) void index_score_decode_fp8_kernel(
     __syncthreads();
   }
   finish(b1 - 1 - b0, b1 - 1);
+}
+
+// ---------------------------------------------------------------------------
+// Decode scoring on 4-bit keys without LDS.  A 4-bit key block is 128 x
+// (DI/2 + DI/32) bytes, so per-block costs of a shared staging tile (the LDS
+// round trip, a barrier, a cross-wave maximum) weigh twice as much as for 8-bit
+// keys.  Here each wave scores whole blocks on its own: it loads its MFMA
+// fragments straight from global memory, two of its blocks ahead, takes the
+// block maximum in registers and writes S[beta * ld + row] = 2^eq * max_j
+// (q8 . k_j).  Wave w of a workgroup owns blocks b0 + w, b0 + w + 4, ... of
+// the workgroup's SEG, so the four waves stream adjacent blocks together.
+// ---------------------------------------------------------------------------
+template <int DI>
+struct K4BlockFrags {
+  typedef unsigned v4u __attribute__((ext_vector_type(4)));
+  static constexpr int KS = DI >= 64 ? DI / 64 : 1;
+  v4u a[4][KS];     // tile kt, k-step ks: elements 64ks + 32h .. +31 of row 32kt + col
+  uint32_t x[4];    // the row's exponent bytes, per tile
+
+  __device__ inline void load(const uint8_t* __restrict__ k4, const uint8_t* __restrict__ ke4,
+                              size_t row0, int col, int h) {
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt) {
+      const size_t row = row0 + kt * 32 + col;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        if (DI > 32 || h == 0)
+          a[kt][ks] = *reinterpret_cast<const v4u*>(k4 + row * (DI / 2) + (DI > 32 ? (2 * ks + h) * 16 : 0));
+        else
+          a[kt][ks] = v4u{0, 0, 0, 0};
+      }
+      const uint8_t* xp = ke4 + row * (DI / 32);
+      if constexpr (DI == 128) x[kt] = *reinterpret_cast<const uint32_t*>(xp);
+      else if constexpr (DI == 64) x[kt] = *reinterpret_cast<const uint16_t*>(xp);
+      else x[kt] = *xp;
+    }
+  }
+};
+
+template <int DI, int SEG, int RT>
+__global__ __launch_bounds__(256) void index_score_decode_k4_kernel(
+    const uint8_t* __restrict__ q8, const uint8_t* __restrict__ qe, const uint8_t* __restrict__ k4,
+    const uint8_t* __restrict__ ke4, const int32_t* __restrict__ cu_q,
+    const int32_t* __restrict__ cu_k, KvMap kv, int G, int r0, int r1, float* __restrict__ S,
+    long long ld) {
+  static_assert(SEG % 4 == 0, "whole rounds of four waves");
+  constexpr int KS = K4BlockFrags<DI>::KS;
+  constexpr int NR = 32 * RT;
+  const int b = blockIdx.y;
+  const int qoff = cu_q[b], lq = cu_q[b + 1] - qoff;
+  const int koff = cu_k[b], lk = cu_k[b + 1] - koff;
+  const int qa = max(qoff, r0), qz = min(qoff + lq, r1);
+  if (qa >= qz) return;
+  const int beta_hi = (lk - lq + (qz - 1 - qoff)) / kBlock;
+  const int b0 = (int)blockIdx.x * SEG;
+  const int b1 = min(beta_hi, b0 + SEG);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  if (b0 + wave >= b1) return;
+  const int nrows = min((qz - qa) * G, NR);
+  const int lane = threadIdx.x & 63;
+  const int col = lane & 31;
+  const int half = lane >> 5;
+
+  i32x8 qf[RT][KS];
+  int eq[RT];
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) {
+    const int n = rt * 32 + col;
+    const uint8_t* src = q8 + ((size_t)qa * G + n) * DI;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) qf[rt][ks] = n < nrows ? q_frag<DI, true>(src, ks, half) : i32x8{};
+    eq[rt] = n < nrows ? (int)qe[(size_t)qa * G + n] - 127 : 0;
+  }
+  const size_t srow = (size_t)(qa - r0) * G;
+
+  auto score = [&](const K4BlockFrags<DI>& f, int beta) __attribute__((always_inline)) {
+    float m[RT];
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) m[rt] = -INFINITY;
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt) {
+      f32x16 acc[RT];
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt) acc[rt] = f32x16{};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const i32x8 a = as_i32x8(make_uint4(f.a[kt][ks].x, f.a[kt][ks].y, f.a[kt][ks].z, f.a[kt][ks].w),
+                                 make_uint4(0, 0, 0, 0));
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) acc[rt] = mfma32_k4(a, qf[rt][ks], acc[rt], k4_scale(f.x[kt], ks, half));
+      }
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) m[rt] = fmaxf(m[rt], acc[rt][i]);
+    }
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+      const float mm = fmaxf(m[rt], shfl_xor_f(m[rt], 32));
+      const int n = rt * 32 + col;
+      if (half == 0 && n < nrows) S[(size_t)beta * ld + srow + n] = ldexpf(mm, eq[rt]);
+    }
+  };
+
+  // two fragment sets in flight: this wave's blocks beta and beta + 4
+  K4BlockFrags<DI> f0, f1;
+  int beta = b0 + wave;
+  f0.load(k4, ke4, kv.block_row(b, koff, beta), col, half);
+  if (beta + 4 < b1) f1.load(k4, ke4, kv.block_row(b, koff, beta + 4), col, half);
+  for (; beta < b1; beta += 8) {
+    score(f0, beta);
+    if (beta + 8 < b1) f0.load(k4, ke4, kv.block_row(b, koff, beta + 8), col, half);
+    if (beta + 4 < b1) {
+      score(f1, beta + 4);
+      if (beta + 12 < b1) f1.load(k4, ke4, kv.block_row(b, koff, beta + 12), col, half);
+    }
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -750,18 +794,32 @@ hipError_t launch_index_select_prefill_fp8(const void* q8, const uint8_t* qe, co
   return hipErrorInvalidValue;
 }
 
+// blocks per workgroup: one query row tile leaves each wave little work per
+// block, so more, smaller workgroups; several tiles favour longer runs
+constexpr int kK4DecodeSeg1 = 8;
+constexpr int kK4DecodeSeg = 16;
+
 template <int DI, bool K4>
 static hipError_t launch_decode8_di(const void* q8, const uint8_t* qe, const void* k8,
                                     const uint8_t* ke, const int32_t* cu_q, const int32_t* cu_k,
                                     KvMap kv, int batch, int G, int nb_max, int rows, int r0, int r1,
                                     float* S, long long ld, hipStream_t st) {
-  dim3 grid((nb_max + kFp8DecodeSeg - 1) / kFp8DecodeSeg, batch);
-#define MSA_DEC8(RT) hipLaunchKernelGGL((index_score_decode_fp8_kernel<DI, kFp8DecodeSeg, RT, K4>), grid, dim3(256), 0, st, (const uint8_t*)q8, qe, (const uint8_t*)k8, ke, cu_q, cu_k, kv, G, nb_max, r0, r1, S, ld)
-  if (rows <= 32) MSA_DEC8(1);
-  else if (rows <= 64) MSA_DEC8(2);
-  else if (rows <= 128) MSA_DEC8(4);
-  else return hipErrorInvalidValue;
+  if constexpr (K4) {
+#define MSA_DEC4(RT, SEG) hipLaunchKernelGGL((index_score_decode_k4_kernel<DI, SEG, RT>), dim3((nb_max + SEG - 1) / SEG, batch), dim3(256), 0, st, (const uint8_t*)q8, qe, (const uint8_t*)k8, ke, cu_q, cu_k, kv, G, r0, r1, S, ld)
+    if (rows <= 32) MSA_DEC4(1, kK4DecodeSeg1);
+    else if (rows <= 64) MSA_DEC4(2, kK4DecodeSeg);
+    else if (rows <= 128) MSA_DEC4(4, kK4DecodeSeg);
+    else return hipErrorInvalidValue;
+#undef MSA_DEC4
+  } else {
+    dim3 grid((nb_max + kFp8DecodeSeg - 1) / kFp8DecodeSeg, batch);
+#define MSA_DEC8(RT) hipLaunchKernelGGL((index_score_decode_fp8_kernel<DI, kFp8DecodeSeg, RT>), grid, dim3(256), 0, st, (const uint8_t*)q8, qe, (const uint8_t*)k8, ke, cu_q, cu_k, kv, G, nb_max, r0, r1, S, ld)
+    if (rows <= 32) MSA_DEC8(1);
+    else if (rows <= 64) MSA_DEC8(2);
+    else if (rows <= 128) MSA_DEC8(4);
+    else return hipErrorInvalidValue;
 #undef MSA_DEC8
+  }
   return hipGetLastError();
 }
 
