@@ -7,11 +7,13 @@
 // by that query alone, so "KV block outer, gather the queries that hit it"
 // (tnkblog.net MiniMax M3 MSA post, section "MSA の実装") needs no list: each
 // wave takes one (query, selected slot) straight from the selection and reads
-// that block once.  K goes from global memory straight into MFMA A
-// fragments; V is transposed through a per-wave LDS tile for O^T = V^T * P^T.
-// The tile holds the query's HPG heads as MFMA rows (HPG <= 32).  Q8: 8-bit
-// inputs (E4M3 codes with power-of-two scales), dequantised exactly into the
-// same bf16 operands while loading.
+// that block once.  Two kernels: bf16 inputs stage the block in LDS with
+// whole-row loads (attend_decode_lds_kernel, one workgroup per item); 8-bit
+// inputs (E4M3 codes with power-of-two scales), dequantised exactly into bf16
+// operands while loading, take attend_decode_kernel, one wave per item: K from
+// global memory straight into MFMA A fragments, V transposed through a
+// per-wave LDS tile for O^T = V^T * P^T.  The query's HPG heads are MFMA
+// columns (HPG <= 32).
 #include "fp8_common.h"
 #include "msa_common.h"
 
@@ -102,7 +104,7 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void attend_decode_kernel(
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
         uint4 x = *reinterpret_cast<const uint4*>(qs + ks * 16);
-        qf[ks] = as_bf16x8(col < HPG ? x : make_uint4(0, 0, 0, 0));
+        qf[ks] = as_bf16x8(x);   // columns >= HPG repeat head 0: never stored
       }
     }
   }
@@ -201,11 +203,205 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void attend_decode_kernel(
   }
 }
 
+// ---------------------------------------------------------------------------
+// bf16 inputs: the selected block staged in LDS.  One workgroup (4 waves) per
+// (group, slot, query), groups fastest.  Fragment loads straight from global
+// memory touch 32 key rows per instruction; here every load instruction reads
+// whole rows (1 KiB of consecutive row bytes per wave).  K reaches LDS by
+// direct global->LDS 16-byte loads; V is loaded into registers at the same
+// time and written over K once the scores are done, so waiting for K never
+// waits for V (the compiler cannot tell two direct-to-LDS streams apart), and
+// the block needs 32 KiB of LDS.  Chunk positions are XOR-swizzled: K so that
+// an A-fragment read (16 consecutive rows, one 16-byte chunk each) hits 16
+// bank groups; V so that the transposed reads (ds_read_b64_tr_b16: within 16
+// lanes, lane 4a + c receives element c of the 8-byte pieces addressed by
+// lanes a, a + 4, a + 8, a + 12) of 4 rows x 4 chunks hit 16 bank groups.
+// Those transposed reads give each lane four consecutive keys of one column:
+// the V^T A fragment without a transposing store.  Wave w scores key tile w;
+// the softmax maximum and sum combine through LDS; every key tile's bf16 P goes
+// through LDS, and wave w then forms output columns 32w .. 32w + 31 (D = 64:
+// waves 0 and 1).  Barriers are bare (s_barrier after lgkmcnt(0)): a
+// workgroup fence would also wait for the loads still in flight.
+// ---------------------------------------------------------------------------
+typedef short lds_tr_v4s __attribute__((ext_vector_type(4)));
+
+// ds_read_b64_tr_b16 at an LDS byte address: the four 16-bit values this lane
+// receives, as two dwords
+__device__ inline uint2 lds_read_tr16(const uint8_t* p) {
+  typedef __attribute__((address_space(3))) lds_tr_v4s lds_v4s;
+  return __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)p));
+}
+
+// one 16-byte direct global->LDS load per lane; lane L writes lds_base + 16 L
+__device__ inline void lds_load16(const uint16_t* src, uint8_t* lds_base) {
+  __builtin_amdgcn_global_load_lds(src, lds_base, 16, 0, 0);
+}
+
+template <int D, int HPG>
+__global__ __launch_bounds__(256) void attend_decode_lds_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+    const int32_t* __restrict__ cu_q, const int32_t* __restrict__ cu_k, KvMap kv, int batch, int G,
+    int Hq, int top_k, const int32_t* __restrict__ sel, int r0, float scale_log2,
+    float* __restrict__ part_acc, float2* __restrict__ part_ml) {
+  constexpr int RB = D * 2;                     // bytes per key row
+  constexpr int CPR = RB / 16;                  // 16-byte chunks per row
+  constexpr int R = 256 / RB;                   // rows per 256-byte bank line
+  constexpr int ROWS_PER_PIECE = 1024 / RB;     // rows per wave load instruction
+  constexpr int PER_WAVE = kBlock / ROWS_PER_PIECE / 4;
+  constexpr int KS = D / 16;
+  constexpr int DT = D / 32;
+  __shared__ __attribute__((aligned(1024))) uint8_t Ks[kBlock * RB];   // K, then V
+  uint8_t* const Vs = Ks;
+  __shared__ __attribute__((aligned(16))) uint4 Pl[4][2][64];
+  __shared__ float red_m[4][32], red_l[4][32];
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63, col = lane & 31, half = lane >> 5;
+  const int r = r0 + (int)blockIdx.z, slot = (int)blockIdx.y, g = (int)blockIdx.x;
+  const RowPos rp = locate_row(r, cu_q, cu_k, batch);
+  const int beta = sel[((size_t)r * G + g) * top_k + slot];
+  if (beta < 0 || beta * kBlock >= rp.lk) return;   // the same for the whole workgroup
+  const int kb = beta * kBlock;
+  const int nvalid = min(kBlock, rp.lk - kb);       // rows of the block in the sequence
+  const size_t row0 = kv.block_row(rp.b, rp.koff, beta);
+
+  // Q^T fragments: MFMA column n = head n of the query's group; columns >= HPG are zero
+  bf16x8 qf[KS];
+  {
+    const int hl = col < HPG ? col : 0;
+    const uint16_t* qs = q + ((size_t)r * Hq + g * HPG + hl) * D + half * 8;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const uint4 x = *reinterpret_cast<const uint4*>(qs + ks * 16);
+      qf[ks] = as_bf16x8(x);   // columns >= HPG repeat head 0: never stored
+    }
+  }
+  auto swz_k = [](int m) { return (m / R) % CPR; };
+  auto swz_v = [](int m) { return 4 * ((m / R) % (CPR / 4)); };
+  // this wave's pieces of K and V; rows past the sequence read its last row
+  // (masked below, so they only need to be finite)
+#pragma unroll
+  for (int i = 0; i < PER_WAVE; ++i) {
+    const int piece = wave * PER_WAVE + i;
+    const int m = piece * ROWS_PER_PIECE + lane / CPR;
+    const size_t src = ((row0 + min(m, nvalid - 1)) * G + g) * D;
+    lds_load16(k + src + ((lane % CPR) ^ swz_k(m)) * 8, Ks + piece * 1024);
+  }
+  // V into registers (the same coalesced pieces), written to LDS over K once
+  // the scores are done
+  typedef unsigned v4u __attribute__((ext_vector_type(4)));
+  v4u vreg[PER_WAVE];
+#pragma unroll
+  for (int i = 0; i < PER_WAVE; ++i) {
+    const int piece = wave * PER_WAVE + i;
+    const int m = piece * ROWS_PER_PIECE + lane / CPR;
+    const size_t src = ((row0 + min(m, nvalid - 1)) * G + g) * D;
+    vreg[i] = *reinterpret_cast<const v4u*>(v + src + (lane % CPR) * 8);
+  }
+
+  wait_vmcnt<PER_WAVE>();   // this wave's K pieces (its V pieces may still be in flight)
+  __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0): this wave's LDS accesses are done
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+
+  // S^T = K * Q^T for keys 32 wave .. 32 wave + 31
+  f32x16 sacc = f32x16{};
+  {
+    const int m = wave * 32 + col;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const uint4 a = *reinterpret_cast<const uint4*>(Ks + m * RB + (((2 * ks + half) ^ swz_k(m)) * 16));
+      sacc = mfma32(as_bf16x8(a), qf[ks], sacc);
+    }
+  }
+  // mask keys after the query, then the block maximum over the four waves
+  const int pr = rp.p - kb - wave * 32 - 4 * half;
+#pragma unroll
+  for (int i = 0; i < 16; ++i)
+    if (8 * (i >> 2) + (i & 3) > pr) sacc[i] = -INFINITY;
+  float mr = sacc[0];
+#pragma unroll
+  for (int i = 1; i < 16; ++i) mr = fmaxf(mr, sacc[i]);
+  mr = fmaxf(mr, shfl_xor_f(mr, 32));
+  if (half == 0) red_m[wave][col] = mr;
+  __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0): this wave's LDS accesses are done
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+  mr = fmaxf(fmaxf(red_m[0][col], red_m[1][col]), fmaxf(red_m[2][col], red_m[3][col]));
+  const float m = mr * scale_log2;
+  const float nm = (mr == -INFINITY) ? 0.f : -m;
+  float l = 0.f;
+#pragma unroll
+  for (int s2 = 0; s2 < 2; ++s2) {
+    float x[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      x[e] = __builtin_amdgcn_exp2f(fmaf(sacc[8 * s2 + e], scale_log2, nm));
+      l += x[e];
+    }
+    Pl[wave][s2][lane] = make_uint4(pack2_bf16(x[0], x[1]), pack2_bf16(x[2], x[3]),
+                                    pack2_bf16(x[4], x[5]), pack2_bf16(x[6], x[7]));
+  }
+  l += shfl_xor_f(l, 32);
+  if (half == 0) red_l[wave][col] = l;
+  // every wave's K reads ended at the barrier above: V replaces K
+#pragma unroll
+  for (int i = 0; i < PER_WAVE; ++i) {
+    const int piece = wave * PER_WAVE + i;
+    const int m = piece * ROWS_PER_PIECE + lane / CPR;
+    *reinterpret_cast<v4u*>(Vs + m * RB + (((lane % CPR) ^ swz_v(m)) * 16)) = vreg[i];
+  }
+  __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0): this wave's LDS accesses are done
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+  if (wave >= DT) return;
+
+  // O^T = V^T * P^T for output columns 32 wave .. 32 wave + 31: lane <-> head,
+  // register i <-> column 32 wave + 8(i/4) + 4 half + i%4
+  f32x16 oacc = f32x16{};
+  {
+    const int grp = lane >> 4, mm = lane & 15;
+    const int d0 = wave * 32 + 16 * (grp & 1);              // this 16-lane group's columns
+    const int cb = (2 * d0 + 8 * (mm & 3)) >> 4;             // logical chunk of lane mm's piece
+    const int cofs = 8 * (mm & 1);                           // byte offset inside the chunk
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2) {
+        const int kb1 = kt * 32 + 16 * s2 + 4 * (grp >> 1) + (mm >> 2);   // row this lane addresses
+        const int kb2 = kb1 + 8;
+        const uint2 lw = lds_read_tr16(Vs + kb1 * RB + ((cb ^ swz_v(kb1)) * 16) + cofs);
+        const uint2 hw = lds_read_tr16(Vs + kb2 * RB + ((cb ^ swz_v(kb2)) * 16) + cofs);
+        oacc = mfma32(as_bf16x8(make_uint4(lw.x, lw.y, hw.x, hw.y)), as_bf16x8(Pl[kt][s2][lane]), oacc);
+      }
+  }
+  if (col < HPG) {
+    const int drow = (((r - r0) * G + g) * top_k + slot) * HPG + col;
+    if (wave == 0 && half == 0)
+      part_ml[drow] = make_float2(m, red_l[0][col] + red_l[1][col] + red_l[2][col] + red_l[3][col]);
+    float* dst = part_acc + (size_t)drow * D + wave * 32 + 4 * half;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      *reinterpret_cast<float4*>(dst + 8 * j) =
+          make_float4(oacc[4 * j], oacc[4 * j + 1], oacc[4 * j + 2], oacc[4 * j + 3]);
+  }
+}
+
 template <int D, int HPG>
 static void launch_decode_t(const void* q, const void* k, const void* v, MainFp8 f8,
                             const int32_t* cu_q, const int32_t* cu_k, KvMap kv, int batch, int G,
                             int Hq, int top_k, int nb_max, const int32_t* sel, int r0, int r1,
                             float scale_log2, float* part_acc, float2* part_ml, hipStream_t st) {
+  if (!f8.qe && HPG <= 32) {
+    hipLaunchKernelGGL((attend_decode_lds_kernel<D, HPG>), dim3(G, top_k, r1 - r0), dim3(256), 0, st,
+                       (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, cu_q, cu_k, kv,
+                       batch, G, Hq, top_k, sel, r0, scale_log2, part_acc, part_ml);
+    return;
+  }
   dim3 grid(r1 - r0, (top_k + kDecodeWaves - 1) / kDecodeWaves, G);
   if (f8.qe)
     hipLaunchKernelGGL((attend_decode_kernel<D, HPG, true>), grid, dim3(kDecodeWaves * 64), 0, st, q,
