@@ -57,6 +57,18 @@ def test_decode_path_small():
     _full_check(w)
 
 
+@pytest.mark.parametrize("d,hq,g", [(64, 8, 8), (64, 64, 8), (128, 16, 1), (128, 64, 4),
+                                     (128, 128, 4), (64, 32, 1)],
+                         ids=["d64-hpg1", "d64-hpg8", "d128-hpg16", "d128-hpg16-g4",
+                              "d128-hpg32", "d64-hpg32"])
+def test_decode_attend_head_layouts(d, hq, g):
+    """The decode Main Branch across head dims and heads per group: contexts
+    shorter than a block, exactly one block, a ragged last block, and long."""
+    w = custom([100, 128, 1300, 9000, 257], [1, 1, 1, 1, 1], num_q_heads=hq, num_kv_heads=g,
+               head_dim=d, index_dim=64, top_k=8, seed=27 + d + hq + g, qkv_std=1.0)
+    _full_check(w, tag=f"decode-d{d}-hpg{hq // g}")
+
+
 def test_multi_token_decode_path():
     # 4 new tokens x 8 groups = 32 rows: still the split-scan index path
     w = custom([9000, 4100], [4, 3], num_q_heads=32, num_kv_heads=8, head_dim=64, index_dim=32,
