@@ -380,7 +380,7 @@ __global__ __launch_bounds__(256) void index_score_decode_kernel(
 constexpr int kPrefillRT = 2;
 constexpr int kPrefillNW = 8;
 constexpr int kPrefillRows = kPrefillRT * kPrefillNW * 32;   // rows per workgroup
-constexpr int kDecodeSeg = 8;
+constexpr int kDecodeSeg = 4;
 
 int prefill_rows_per_wg() { return kPrefillRows; }
 
