@@ -34,20 +34,6 @@
 
 namespace msa {
 
-typedef short lds_tr_v4s __attribute__((ext_vector_type(4)));
-
-// ds_read_b64_tr_b16 at an LDS byte address: the four 16-bit values this lane
-// receives, as two dwords
-__device__ inline uint2 lds_read_tr16(const uint8_t* p) {
-  typedef __attribute__((address_space(3))) lds_tr_v4s lds_v4s;
-  return __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)p));
-}
-
-// one 16-byte direct global->LDS load per lane; lane L writes lds_base + 16 L
-__device__ inline void lds_load16(const uint8_t* src, uint8_t* lds_base) {
-  __builtin_amdgcn_global_load_lds(src, lds_base, 16, 0, 0);
-}
-
 template <int D, int HPG, bool Q8>
 __global__ __launch_bounds__(256) void attend_decode_lds_kernel(
     const void* __restrict__ q, const void* __restrict__ k, const void* __restrict__ v,

@@ -143,6 +143,23 @@ __device__ inline float row_tile_max(const float (&rmax)[RT], int half) {
   }
 }
 
+// ds_read_b64_tr_b16 at an LDS byte address: the four 16-bit values this lane
+// receives, as two dwords.  Within each 16 lanes, lane 4a + c receives element
+// c of the 8-byte pieces addressed by lanes a, a + 4, a + 8, a + 12 (measured):
+// if lane m addresses row k0 + m/4 at column d0 + 4 (m%4) of a row-major bf16
+// tile, lane n receives rows k0 .. k0+3 of column d0 + n.
+typedef short lds_tr_v4s __attribute__((ext_vector_type(4)));
+__device__ inline uint2 lds_read_tr16(const uint8_t* p) {
+  typedef __attribute__((address_space(3))) lds_tr_v4s lds_v4s;
+  return __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)p));
+}
+
+// one 16-byte direct global->LDS load per lane; lane L writes lds_base + 16 L
+// (lds_base wave-uniform)
+__device__ inline void lds_load16(const uint8_t* src, uint8_t* lds_base) {
+  __builtin_amdgcn_global_load_lds(src, lds_base, 16, 0, 0);
+}
+
 // vmcnt(n) with the other counters left alone (gfx9 s_waitcnt encoding)
 template <int N>
 __device__ inline void wait_vmcnt() {
