@@ -21,7 +21,7 @@ __all__ = [
     "msa_forward", "exported_symbols", "LIB_PATH", "HEADER_PATH", "index_quantize_fp8",
     "index_select_fp8", "Fp8Index", "index_project", "attend_with_mass", "index_kl",
     "attend_reads_lists", "Fp8Main", "main_quantize_fp8", "attend_fp8", "Q8K4Index",
-    "index_quantize_q8k4", "index_select_q8k4",
+    "index_quantize_q8k4", "index_select_q8k4", "Q8KV4Main", "main_quantize_q8kv4", "attend_q8kv4",
 ]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -95,6 +95,10 @@ def load_library(path: str = LIB_PATH):
     lib.msa_main_quantize_fp8.argtypes = [DP, P, P, P, P, P, P, P, P, P, P, P]
     lib.msa_attend_fp8.restype = I32
     lib.msa_attend_fp8.argtypes = [DP, P, P, P, P, P, P, P, P, P, P, P, P, P, P, SZ, P]
+    lib.msa_main_quantize_q8kv4.restype = I32
+    lib.msa_main_quantize_q8kv4.argtypes = [DP, P, P, P, P, P, P, P, P, P, P, P]
+    lib.msa_attend_q8kv4.restype = I32
+    lib.msa_attend_q8kv4.argtypes = [DP, P, P, P, P, P, P, P, P, P, P, P, P, P, P, SZ, P]
     lib.msa_attend_reads_lists.restype = I32
     lib.msa_attend_reads_lists.argtypes = [DP]
     lib.msa_profile_enable.restype = I32
@@ -339,6 +343,76 @@ def attend_fp8(dims, f8: Fp8Main, cu_seqlens_q, cu_seqlens_k, sel, block_offsets
     return out
 
 
+class Q8KV4Main:
+    """The Main Branch's 8-bit q codes and 4-bit k, v codes for fixed dims:
+    E4M3 q with one E8M0 exponent per (row, head); E2M1 k and v packed two per
+    byte with one E8M0 exponent per 32 elements of every (key, KV head) row."""
+
+    def __init__(self, dims: Dims, device):
+        T, Hq, G, D = dims.total_q, dims.num_q_heads, dims.num_kv_heads, dims.head_dim
+        dev = torch.device(device)
+        self.q8 = torch.empty((T, Hq, D), dtype=torch.uint8, device=dev)
+        self.q_exp = torch.empty((T, Hq), dtype=torch.uint8, device=dev)
+        self.k4 = torch.empty((dims.total_k, G, D // 2), dtype=torch.uint8, device=dev)
+        self.v4 = torch.empty((dims.total_k, G, D // 2), dtype=torch.uint8, device=dev)
+        self.k_exp4 = torch.empty((dims.total_k, G, D // 32), dtype=torch.uint8, device=dev)
+        self.v_exp4 = torch.empty((dims.total_k, G, D // 32), dtype=torch.uint8, device=dev)
+
+
+def _check_q8kv4(dims, m: Q8KV4Main):
+    T, Hq, G, D = dims.total_q, dims.num_q_heads, dims.num_kv_heads, dims.head_dim
+    _shape(m.q8, (T, Hq, D), "q8")
+    _shape(m.q_exp, (T, Hq), "q_exp")
+    for name in ("k4", "v4"):
+        _shape(getattr(m, name), (dims.total_k, G, D // 2), name)
+    for name in ("k_exp4", "v_exp4"):
+        _shape(getattr(m, name), (dims.total_k, G, D // 32), name)
+
+
+def main_quantize_q8kv4(dims, q, k, v, cu_seqlens_k, m: Q8KV4Main, stream=None):
+    """bf16 q / k / v -> 8-bit q codes and 4-bit k, v codes (into `m`).
+
+    Any of q, k, v may be None: that part of `m` is left as it is.
+    """
+    T, Hq, G, D = dims.total_q, dims.num_q_heads, dims.num_kv_heads, dims.head_dim
+    if q is not None:
+        _shape(q, (T, Hq, D), "q")
+    for name, x in (("k", k), ("v", v)):
+        if x is not None:
+            _shape(x, (dims.total_k, G, D), name)
+    _check_q8kv4(dims, m)
+    st = load_library().msa_main_quantize_q8kv4(
+        ctypes.byref(dims), _ptr(q, "q", torch.bfloat16), _ptr(k, "k", torch.bfloat16),
+        _ptr(v, "v", torch.bfloat16), _ptr(cu_seqlens_k, "cu_seqlens_k", torch.int32),
+        _ptr(m.q8, "q8", torch.uint8), _ptr(m.q_exp, "q_exp", torch.uint8),
+        _ptr(m.k4, "k4", torch.uint8), _ptr(m.k_exp4, "k_exp4", torch.uint8),
+        _ptr(m.v4, "v4", torch.uint8), _ptr(m.v_exp4, "v_exp4", torch.uint8), _stream(stream))
+    _check(st, "msa_main_quantize_q8kv4")
+    return m
+
+
+def attend_q8kv4(dims, m: Q8KV4Main, cu_seqlens_q, cu_seqlens_k, sel, block_offsets, block_entries,
+                 out, lse=None, workspace=None, stream=None):
+    """The Main Branch on 8-bit q and 4-bit k, v (msa_attend_q8kv4)."""
+    T, Hq, D = dims.total_q, dims.num_q_heads, dims.head_dim
+    _check_q8kv4(dims, m)
+    _shape(out, (T, Hq, D), "out")
+    if lse is not None:
+        _shape(lse, (T, Hq), "lse")
+    ws = _workspace(dims, OP_ATTEND, workspace, out.device)
+    st = load_library().msa_attend_q8kv4(
+        ctypes.byref(dims), _ptr(m.q8, "q8", torch.uint8), _ptr(m.q_exp, "q_exp", torch.uint8),
+        _ptr(m.k4, "k4", torch.uint8), _ptr(m.k_exp4, "k_exp4", torch.uint8),
+        _ptr(m.v4, "v4", torch.uint8), _ptr(m.v_exp4, "v_exp4", torch.uint8),
+        _ptr(cu_seqlens_q, "cu_seqlens_q", torch.int32), _ptr(cu_seqlens_k, "cu_seqlens_k", torch.int32),
+        _ptr(sel, "sel", torch.int32), _ptr(block_offsets, "block_offsets", torch.int32),
+        _ptr(block_entries, "block_entries", torch.int32), _ptr(out, "out", torch.bfloat16),
+        _ptr(lse, "lse", torch.float32), _ptr(ws, "workspace"),
+        ctypes.c_size_t(ws.numel() * ws.element_size()), _stream(stream))
+    _check(st, "msa_attend_q8kv4")
+    return out
+
+
 class Q8K4Index:
     """8-bit index-query codes and 4-bit index-key codes for fixed dims: E4M3
     queries with one E8M0 exponent per (row, group); E2M1 keys packed two per
@@ -545,7 +619,8 @@ def msa_forward(dims: Dims, q, k, v, q_idx, k_idx, cu_seqlens_q, cu_seqlens_k, b
     keeps the key codes already in `fp8` (a quantised index-key cache).
     With `q8k4` given instead, the same with 4-bit index keys
     (index_quantize_q8k4 -> index_select_q8k4).
-    With `fp8_main` given, the Main Branch quantises q (and k, v unless they are
+    With `fp8_main` given (Fp8Main: 8-bit q, k, v; Q8KV4Main: 8-bit q, 4-bit
+    k, v), the Main Branch quantises q (and k, v unless they are
     None: a quantised key/value cache already in `fp8_main`) and attends on the
     codes (main_quantize_fp8 -> attend_fp8).
     """
@@ -569,6 +644,10 @@ def msa_forward(dims: Dims, q, k, v, q_idx, k_idx, cu_seqlens_q, cu_seqlens_k, b
     if fp8_main is None:
         attend(dims, q, k, v, cu_seqlens_q, cu_seqlens_k, bufs.sel, bufs.offsets, bufs.entries,
                bufs.out, bufs.lse, bufs.workspace, stream)
+    elif isinstance(fp8_main, Q8KV4Main):
+        main_quantize_q8kv4(dims, q, k, v, cu_seqlens_k, fp8_main, stream)
+        attend_q8kv4(dims, fp8_main, cu_seqlens_q, cu_seqlens_k, bufs.sel, bufs.offsets, bufs.entries,
+                     bufs.out, bufs.lse, bufs.workspace, stream)
     else:
         main_quantize_fp8(dims, q, k, v, cu_seqlens_k, fp8_main, stream)
         attend_fp8(dims, fp8_main, cu_seqlens_q, cu_seqlens_k, bufs.sel, bufs.offsets, bufs.entries,
@@ -576,7 +655,7 @@ def msa_forward(dims: Dims, q, k, v, q_idx, k_idx, cu_seqlens_q, cu_seqlens_k, b
     return bufs
 
 
-PROFILE_KERNELS = 16
+PROFILE_KERNELS = 17
 
 
 def profile_enable(on: bool = True):

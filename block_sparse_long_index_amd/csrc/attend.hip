@@ -22,9 +22,11 @@
 // heads of one (query, slot) form one contiguous run of HPG * D floats.
 //
 // Q8: the Main Branch's inputs are E4M3 codes with power-of-two scales (one per
-// (query row, head) of q, one per (block, KV head) of k and v); Q fragments
-// and the staged K/V are dequantised on load, exactly, into the same bf16
-// operands, so everything after the loads is the bf16 path.
+// (query row, head) of q, one per (block, KV head) of k and v); KV4 (with Q8):
+// k and v are E2M1 codes with one power-of-two scale per 32 elements of every
+// (key, KV head) row.  Q fragments and the staged K/V are dequantised on
+// load, exactly, into the same bf16 operands, so everything after the loads
+// is the bf16 path.
 //
 // merge_partials_kernel: per (query, head) the log-sum-exp merge of its
 // partials -- M = max m_s, L = sum l_s 2^(m_s - M),
@@ -107,7 +109,7 @@ __device__ inline int wave_lower_bound(const int32_t* __restrict__ a, int lo, in
 // One (block, sequence, group) item: stage its K/V block, then attend every
 // gathered query of this pass.  Called by the whole workgroup; every exit is
 // workgroup-uniform.
-template <int D, int HPG, bool Q8>
+template <int D, int HPG, bool Q8, bool KV4>
 __device__ __forceinline__ void attend_item(
     long long item, const void* __restrict__ q, const void* __restrict__ k,
     const void* __restrict__ v, const uint8_t* __restrict__ qe, const uint8_t* __restrict__ ke,
@@ -166,7 +168,44 @@ __device__ __forceinline__ void attend_item(
   //    writes of a wave land on consecutive addresses.
   const int kb = beta * kBlock;
   const size_t row0 = kv.block_row(b, koff, beta);   // first cache row of the block
-  if constexpr (Q8) {
+  if constexpr (KV4) {
+    // 32 codes (16 bytes) and their exponent per chunk: chunk gc of key row
+    // `key` holds elements 32 gc .. 32 gc + 31
+    const uint8_t* k4 = static_cast<const uint8_t*>(k);
+    const uint8_t* v4 = static_cast<const uint8_t*>(v);
+    for (int c = tid; c < kBlock * D / 32; c += 256) {
+      const int key = c / (D / 32), gc = c % (D / 32);
+      const size_t rr = (row0 + key) * G + g;
+      uint4 kk = make_uint4(0, 0, 0, 0);
+      int e = 0;
+      if (kb + key < lk) {
+        kk = *reinterpret_cast<const uint4*>(k4 + rr * (D / 2) + gc * 16);
+        e = (int)ke[rr * (D / 32) + gc] - 127;
+      }
+      uint16_t* dst = Ks + key * LDK + gc * 32;
+      *reinterpret_cast<uint4*>(dst) = dequant4_bf16(kk.x, e);
+      *reinterpret_cast<uint4*>(dst + 8) = dequant4_bf16(kk.y, e);
+      *reinterpret_cast<uint4*>(dst + 16) = dequant4_bf16(kk.z, e);
+      *reinterpret_cast<uint4*>(dst + 24) = dequant4_bf16(kk.w, e);
+    }
+    for (int c = tid; c < kBlock * D / 32; c += 256) {
+      const int key = c % kBlock, gc = c / kBlock;
+      const size_t rr = (row0 + key) * G + g;
+      uint4 vv = make_uint4(0, 0, 0, 0);
+      int e = 0;
+      if (kb + key < lk) {
+        vv = *reinterpret_cast<const uint4*>(v4 + rr * (D / 2) + gc * 16);
+        e = (int)ve[rr * (D / 32) + gc] - 127;
+      }
+      const uint4 d0 = dequant4_bf16(vv.x, e), d1 = dequant4_bf16(vv.y, e);
+      const uint4 d2 = dequant4_bf16(vv.z, e), d3 = dequant4_bf16(vv.w, e);
+      const uint32_t vw[16] = {d0.x, d0.y, d0.z, d0.w, d1.x, d1.y, d1.z, d1.w,
+                               d2.x, d2.y, d2.z, d2.w, d3.x, d3.y, d3.z, d3.w};
+#pragma unroll
+      for (int i = 0; i < 32; ++i)
+        Vt[(gc * 32 + i) * LDV + key] = (uint16_t)(vw[i >> 1] >> (16 * (i & 1)));
+    }
+  } else if constexpr (Q8) {
     // 16 codes per 16-byte chunk, dequantised with the block's exponents
     const size_t xi = kv.block_index(b, beta, nb_max) * G + g;
     const int kexp = (int)ke[xi] - 127, vexp = (int)ve[xi] - 127;
@@ -326,7 +365,7 @@ __device__ __forceinline__ void attend_item(
 // items_per_wg == 1: one item per workgroup.  items_per_wg in 2..64 (sparse
 // selections, e.g. decode): the workgroup finds which of its items have any
 // query with one coalesced load and processes only those.
-template <int D, int HPG, bool Q8>
+template <int D, int HPG, bool Q8, bool KV4>
 __global__ __launch_bounds__(256, 2) void attend_blocks_kernel(
     const void* __restrict__ q, const void* __restrict__ k, const void* __restrict__ v,
     const uint8_t* __restrict__ qe, const uint8_t* __restrict__ ke, const uint8_t* __restrict__ ve,
@@ -344,7 +383,7 @@ __global__ __launch_bounds__(256, 2) void attend_blocks_kernel(
   const long long n_items = (long long)nb_max * BG;
   const long long first = (long long)blockIdx.x * items_per_wg;
   if (items_per_wg == 1) {
-    attend_item<D, HPG, Q8>(first, q, k, v, qe, ke, ve, cu_q, cu_k, kv, batch, G, Hq, top_k, nb_max, offsets,
+    attend_item<D, HPG, Q8, KV4>(first, q, k, v, qe, ke, ve, cu_q, cu_k, kv, batch, G, Hq, top_k, nb_max, offsets,
                         entries, r0, r1, total_q, scale_log2, part_acc, part_ml, spare_row, Ks, Vt,
                         range);
     return;
@@ -365,7 +404,7 @@ __global__ __launch_bounds__(256, 2) void attend_blocks_kernel(
   while (m) {
     const int i = __ffsll((long long)m) - 1;
     m &= m - 1;
-    attend_item<D, HPG, Q8>(first + i, q, k, v, qe, ke, ve, cu_q, cu_k, kv, batch, G, Hq, top_k, nb_max, offsets,
+    attend_item<D, HPG, Q8, KV4>(first + i, q, k, v, qe, ke, ve, cu_q, cu_k, kv, batch, G, Hq, top_k, nb_max, offsets,
                         entries, r0, r1, total_q, scale_log2, part_acc, part_ml, spare_row, Ks, Vt,
                         range);
     __syncthreads();   // LDS and range are reused by the next item
@@ -457,12 +496,17 @@ static void launch_attend_t(const void* q, const void* k, const void* v, MainFp8
   const double per_item = (double)(r1 - r0) * G * top_k / (double)n_items;
   const int ipw = per_item >= 4.0 ? 1 : 64;
   dim3 grid((unsigned)((n_items + ipw - 1) / ipw));
-  if (f8.qe)
-    hipLaunchKernelGGL((attend_blocks_kernel<D, HPG, true>), grid, dim3(256), 0, st, q, k, v, f8.qe,
+  if (f8.qe && f8.kv4)
+    hipLaunchKernelGGL((attend_blocks_kernel<D, HPG, true, true>), grid, dim3(256), 0, st, q, k, v,
+                       f8.qe, f8.ke, f8.ve, cu_q, cu_k, kv, batch, G, Hq, top_k, nb_max, offsets,
+                       entries, r0, r1, total_q, scale_log2, part_acc, part_ml,
+                       (r1 - r0) * Hq * top_k, ipw);
+  else if (f8.qe)
+    hipLaunchKernelGGL((attend_blocks_kernel<D, HPG, true, false>), grid, dim3(256), 0, st, q, k, v, f8.qe,
                        f8.ke, f8.ve, cu_q, cu_k, kv, batch, G, Hq, top_k, nb_max, offsets, entries,
                        r0, r1, total_q, scale_log2, part_acc, part_ml, (r1 - r0) * Hq * top_k, ipw);
   else
-    hipLaunchKernelGGL((attend_blocks_kernel<D, HPG, false>), grid, dim3(256), 0, st, q, k, v,
+    hipLaunchKernelGGL((attend_blocks_kernel<D, HPG, false, false>), grid, dim3(256), 0, st, q, k, v,
                        (const uint8_t*)nullptr, (const uint8_t*)nullptr, (const uint8_t*)nullptr,
                        cu_q, cu_k, kv, batch, G, Hq, top_k, nb_max, offsets, entries, r0, r1,
                        total_q, scale_log2, part_acc, part_ml, (r1 - r0) * Hq * top_k, ipw);

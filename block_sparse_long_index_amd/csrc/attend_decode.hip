@@ -34,7 +34,7 @@
 
 namespace msa {
 
-template <int D, int HPG, bool Q8>
+template <int D, int HPG, bool Q8, bool KV4>
 __global__ __launch_bounds__(256) void attend_decode_lds_kernel(
     const void* __restrict__ q, const void* __restrict__ k, const void* __restrict__ v,
     const uint8_t* __restrict__ qe, const uint8_t* __restrict__ ke, const uint8_t* __restrict__ ve,
@@ -44,14 +44,20 @@ __global__ __launch_bounds__(256) void attend_decode_lds_kernel(
   constexpr int RB = D * 2;                     // bytes per bf16 row (the V tile)
   constexpr int CPR = RB / 16;                  // 16-byte chunks per bf16 row
   constexpr int R = 256 / RB;                   // bf16 rows per 256-byte bank line
-  constexpr int RBS = Q8 ? D : 2 * D;           // bytes per stored row (codes or bf16)
+  constexpr int RBS = KV4 ? D / 2 : Q8 ? D : 2 * D;   // bytes per stored row (codes or bf16)
   constexpr int CPRS = RBS / 16;
   constexpr int RS = 256 / RBS;
   constexpr int ROWS_PER_PIECE = 1024 / RBS;    // rows per wave load instruction
   constexpr int PER_WAVE = kBlock / ROWS_PER_PIECE / 4;
+  constexpr int XB = D / 32;                    // 4-bit rows: exponent bytes per (key, head)
+  constexpr int XS = 4;                         // LDS bytes per key of a direct exponent load
+  constexpr int EXP_OFF = kBlock * RBS;         // 4-bit K: the block's exponents after its codes
+  constexpr int VC_OFF = kBlock * RB;           // 4-bit V: codes after the bf16 V tile, then exponents
+  constexpr int VX_OFF = VC_OFF + kBlock * RBS;
   constexpr int KS = D / 16;
   constexpr int DT = D / 32;
-  __shared__ __attribute__((aligned(1024))) uint8_t Ks[kBlock * RB];   // K (as stored), then V (bf16)
+  // K (as stored), then the bf16 V tile; 4-bit V's codes and exponents follow the tile
+  __shared__ __attribute__((aligned(1024))) uint8_t Ks[kBlock * RB + (KV4 ? kBlock * (RBS + XS) : 0)];
   uint8_t* const Vs = Ks;
   __shared__ __attribute__((aligned(16))) uint4 Pl[4][2][64];
   __shared__ float red_m[4][32], red_l[4][32];
@@ -71,14 +77,30 @@ __global__ __launch_bounds__(256) void attend_decode_lds_kernel(
 
   // Q^T: MFMA column n = head n of the query's group (columns >= HPG repeat
   // head 0 and are never stored).  bf16: k-step ks of lane half h covers
-  // elements 16ks + 8h .. +7.  8-bit: k-step 2j + e covers 32j + 16h + 8e .. +7,
-  // so that a lane's two k-steps read one 16-byte chunk of K codes; the raw
-  // codes are loaded before the block and dequantised once K has landed.
+  // elements 16ks + 8h .. +7.  8-bit K: k-step 2j + e covers 32j + 16h + 8e ..
+  // +7, so that a lane's two k-steps read one 16-byte chunk of K codes; 4-bit
+  // K: k-step 4j + e covers 64j + 32h + 8e .. +7 (one 16-byte chunk of codes
+  // = one 32-element scale group per four k-steps).  Raw query codes are
+  // loaded before the block and dequantised once K has landed.
   const int hl = col < HPG ? col : 0;
   const size_t qrow = (size_t)r * Hq + g * HPG + hl;
   bf16x8 qf[KS];
   uint2 qraw[Q8 ? KS : 1];
-  if constexpr (Q8) {
+  // exponent bytes are loaded before the block and used raw (subtracting the
+  // bias at once would make the first block load wait for them)
+  uint32_t qexp_b = Q8 ? (uint32_t)qe[qrow] : 127u;
+  uint32_t kexp_b = 127u, vexp_b = 127u;
+  if constexpr (Q8 && !KV4) {
+    const size_t xi = kv.block_index(rp.b, beta, nb_max) * G + g;
+    kexp_b = ke[xi];
+    vexp_b = ve[xi];
+  }
+  if constexpr (KV4) {
+    const uint8_t* qs = static_cast<const uint8_t*>(q) + qrow * D + half * 32;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+      qraw[ks] = *reinterpret_cast<const uint2*>(qs + (ks >> 2) * 64 + (ks & 3) * 8);
+  } else if constexpr (Q8) {
     const uint8_t* qs = static_cast<const uint8_t*>(q) + qrow * D + half * 16;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
@@ -102,19 +124,33 @@ __global__ __launch_bounds__(256) void attend_decode_lds_kernel(
     lds_load16(kbytes + src + ((lane % CPRS) ^ swz_k(m)) * 16, Ks + piece * 1024);
   }
   typedef unsigned v4u __attribute__((ext_vector_type(4)));
-  v4u vreg[PER_WAVE];
+  v4u vreg[KV4 ? 1 : PER_WAVE];
+  if constexpr (KV4) {
+    // 4-bit rows are small: K's and V's codes and exponents all go straight to
+    // LDS, waited for at once; V is dequantised from its LDS copy into the
+    // bf16 tile after the scores.  Exponents: XB bytes per key, one key per
+    // lane; loads of up to 4 bytes put lane L's bytes at 4 L (XS).
+    const int key = (wave & 1) * 64 + lane;
+    const size_t rk = ((row0 + min(key, nvalid - 1)) * G + g) * XB;
+    if (wave < 2) lds_load_n<XB>(ke + rk, Ks + EXP_OFF + wave * 64 * XS);
+    else lds_load_n<XB>(ve + rk, Ks + VX_OFF + (wave - 2) * 64 * XS);
 #pragma unroll
-  for (int i = 0; i < PER_WAVE; ++i) {
-    const int piece = wave * PER_WAVE + i;
-    const int m = piece * ROWS_PER_PIECE + lane / CPRS;
-    const size_t src = ((row0 + min(m, nvalid - 1)) * G + g) * RBS;
-    vreg[i] = *reinterpret_cast<const v4u*>(vbytes + src + (lane % CPRS) * 16);
-  }
-  int kexp = 0, vexp = 0;
-  if constexpr (Q8) {
-    const size_t xi = kv.block_index(rp.b, beta, nb_max) * G + g;
-    kexp = (int)ke[xi] - 127;
-    vexp = (int)ve[xi] - 127;
+    for (int i = 0; i < PER_WAVE; ++i) {
+      const int piece = wave * PER_WAVE + i;
+      const int m = piece * ROWS_PER_PIECE + lane / CPRS;
+      const size_t src = ((row0 + min(m, nvalid - 1)) * G + g) * RBS;
+      lds_load16(vbytes + src + (lane % CPRS) * 16, Ks + VC_OFF + piece * 1024);
+    }
+  } else {
+    // V into registers (the same coalesced pieces), written to LDS over K once
+    // the scores are done
+#pragma unroll
+    for (int i = 0; i < PER_WAVE; ++i) {
+      const int piece = wave * PER_WAVE + i;
+      const int m = piece * ROWS_PER_PIECE + lane / CPRS;
+      const size_t src = ((row0 + min(m, nvalid - 1)) * G + g) * RBS;
+      vreg[i] = *reinterpret_cast<const v4u*>(vbytes + src + (lane % CPRS) * 16);
+    }
   }
 
   auto barrier = []() __attribute__((always_inline)) {
@@ -123,19 +159,36 @@ __global__ __launch_bounds__(256) void attend_decode_lds_kernel(
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
   };
-  wait_vmcnt<PER_WAVE>();   // the query and this wave's K pieces (V may still be in flight)
+  if constexpr (KV4) wait_vmcnt<0>();
+  else wait_vmcnt<PER_WAVE>();   // the query and this wave's K pieces (V may still be in flight)
   barrier();
   if constexpr (Q8) {
-    const int e = (int)qe[qrow] - 127;
+    // opaque after the barrier: the compiler would otherwise dequantise the
+    // query before it and wait for every load, V's included, to do so
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) qf[ks] = as_bf16x8(dequant8_bf16(qraw[ks], e));
+    for (int ks = 0; ks < KS; ++ks) asm volatile("" : "+v"(qraw[ks].x), "+v"(qraw[ks].y));
+    asm volatile("" : "+v"(qexp_b), "+v"(kexp_b), "+v"(vexp_b));
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) qf[ks] = as_bf16x8(dequant8_bf16(qraw[ks], (int)qexp_b - 127));
   }
+  const int kexp = (int)kexp_b - 127, vexp = (int)vexp_b - 127;
 
   // S^T = K * Q^T for keys 32 wave .. 32 wave + 31
   f32x16 sacc = f32x16{};
   {
     const int m = wave * 32 + col;
-    if constexpr (Q8) {
+    if constexpr (KV4) {
+#pragma unroll
+      for (int j = 0; j < KS / 4; ++j) {
+        const int ch = 2 * j + half;   // elements 64j + 32 half .. +31: one scale group
+        const uint4 c = *reinterpret_cast<const uint4*>(Ks + m * RBS + ((ch ^ swz_k(m)) * 16));
+        const int e = (int)Ks[EXP_OFF + m * XS + ch] - 127;
+        sacc = mfma32(as_bf16x8(dequant4_bf16(c.x, e)), qf[4 * j], sacc);
+        sacc = mfma32(as_bf16x8(dequant4_bf16(c.y, e)), qf[4 * j + 1], sacc);
+        sacc = mfma32(as_bf16x8(dequant4_bf16(c.z, e)), qf[4 * j + 2], sacc);
+        sacc = mfma32(as_bf16x8(dequant4_bf16(c.w, e)), qf[4 * j + 3], sacc);
+      }
+    } else if constexpr (Q8) {
 #pragma unroll
       for (int j = 0; j < KS / 2; ++j) {
         const uint4 c = *reinterpret_cast<const uint4*>(Ks + m * RBS + (((2 * j + half) ^ swz_k(m)) * 16));
@@ -184,7 +237,16 @@ __global__ __launch_bounds__(256) void attend_decode_lds_kernel(
     const int piece = wave * PER_WAVE + i;
     const int mv = piece * ROWS_PER_PIECE + lane / CPRS;
     const int c = lane % CPRS;   // chunk of the stored row
-    if constexpr (Q8) {
+    if constexpr (KV4) {
+      // this lane's own piece of V codes (32 codes: one scale group) -> bf16
+      // chunks 4c .. 4c + 3 of the row
+      const uint4 cv = *reinterpret_cast<const uint4*>(Ks + VC_OFF + piece * 1024 + lane * 16);
+      const int e = (int)Ks[VX_OFF + mv * XS + c] - 127;
+      *reinterpret_cast<uint4*>(Vs + mv * RB + (((4 * c) ^ swz_v(mv)) * 16)) = dequant4_bf16(cv.x, e);
+      *reinterpret_cast<uint4*>(Vs + mv * RB + (((4 * c + 1) ^ swz_v(mv)) * 16)) = dequant4_bf16(cv.y, e);
+      *reinterpret_cast<uint4*>(Vs + mv * RB + (((4 * c + 2) ^ swz_v(mv)) * 16)) = dequant4_bf16(cv.z, e);
+      *reinterpret_cast<uint4*>(Vs + mv * RB + (((4 * c + 3) ^ swz_v(mv)) * 16)) = dequant4_bf16(cv.w, e);
+    } else if constexpr (Q8) {
       // 16 codes -> bf16 chunks 2c and 2c + 1 of the row
       *reinterpret_cast<uint4*>(Vs + mv * RB + (((2 * c) ^ swz_v(mv)) * 16)) =
           dequant8_bf16(make_uint2(vreg[i].x, vreg[i].y), vexp);
@@ -233,12 +295,16 @@ static void launch_decode_t(const void* q, const void* k, const void* v, MainFp8
                             const int32_t* cu_q, const int32_t* cu_k, KvMap kv, int batch, int G,
                             int Hq, int top_k, int nb_max, const int32_t* sel, int r0, int r1,
                             float scale_log2, float* part_acc, float2* part_ml, hipStream_t st) {
-  if (f8.qe)
-    hipLaunchKernelGGL((attend_decode_lds_kernel<D, HPG, true>), dim3(G, top_k, r1 - r0), dim3(256), 0,
+  if (f8.qe && f8.kv4)
+    hipLaunchKernelGGL((attend_decode_lds_kernel<D, HPG, true, true>), dim3(G, top_k, r1 - r0), dim3(256),
+                       0, st, q, k, v, f8.qe, f8.ke, f8.ve, cu_q, cu_k, kv, batch, G, Hq, top_k, nb_max,
+                       sel, r0, scale_log2, part_acc, part_ml);
+  else if (f8.qe)
+    hipLaunchKernelGGL((attend_decode_lds_kernel<D, HPG, true, false>), dim3(G, top_k, r1 - r0), dim3(256), 0,
                        st, q, k, v, f8.qe, f8.ke, f8.ve, cu_q, cu_k, kv, batch, G, Hq, top_k, nb_max,
                        sel, r0, scale_log2, part_acc, part_ml);
   else
-    hipLaunchKernelGGL((attend_decode_lds_kernel<D, HPG, false>), dim3(G, top_k, r1 - r0), dim3(256), 0,
+    hipLaunchKernelGGL((attend_decode_lds_kernel<D, HPG, false, false>), dim3(G, top_k, r1 - r0), dim3(256), 0,
                        st, q, k, v, (const uint8_t*)nullptr, (const uint8_t*)nullptr,
                        (const uint8_t*)nullptr, cu_q, cu_k, kv, batch, G, Hq, top_k, nb_max, sel, r0,
                        scale_log2, part_acc, part_ml);

@@ -86,4 +86,48 @@ __device__ inline uint4 dequant8_bf16(uint2 w, int e) {
                     pack2_bf16(ldexpf(c.x, e), ldexpf(c.y, e)), pack2_bf16(ldexpf(d.x, e), ldexpf(d.y, e)));
 }
 
+// ---------------------------------------------------------------------------
+// 4-bit codes (index keys; Main-Branch keys and values).  A 32-element
+// group's exponent e is the smallest integer with amax * 2^-e <= 6 (the
+// largest E2M1 value), clamped to [-127, 127], 0 for an all-zero group; codes
+// are the nearest E2M1 value of x * 2^-e, ties to the even code, with x's
+// sign bit.
+// ---------------------------------------------------------------------------
+__device__ inline int fp4_scale_exponent(float amax) {
+  if (amax == 0.f) return 0;
+  int E;
+  const float f = frexpf(amax, &E);
+  const int e = f <= 0.75f ? E - 3 : E - 2;   // f * 2^3 <= 6 exactly when f <= 0.75
+  return min(127, max(-127, e));
+}
+
+// E2M1 code of one value already scaled into [-6, 6].  The thresholds are the
+// midpoints of the grid 0, .5, 1, 1.5, 2, 3, 4, 6; at a midpoint the even code
+// (mantissa bit 0: 0, 1, 2, 4) wins, hence > below even codes and >= below odd.
+__device__ inline uint32_t e2m1_code(float y) {
+  const float a = fabsf(y);
+  const uint32_t c = (uint32_t)(a > 0.25f) + (uint32_t)(a >= 0.75f) + (uint32_t)(a > 1.25f) +
+                     (uint32_t)(a >= 1.75f) + (uint32_t)(a > 2.5f) + (uint32_t)(a >= 3.5f) +
+                     (uint32_t)(a > 5.f);
+  return c | ((__float_as_uint(y) >> 31) << 3);
+}
+
+// Eight E2M1 codes (element i in nibble i of w, low nibble first) at
+// exponent e -> eight bf16 values.  Magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6 are
+// m * 2^s with m in {0, 1, 2, 3}; a value has at most 2 significant bits, so
+// the ldexp and the bf16 rounding are exact (within bf16's range).
+__device__ inline uint4 dequant4_bf16(uint32_t w, int e) {
+  float x[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const uint32_t c = (w >> (4 * i)) & 15u, mag = c & 7u;
+    const float m = mag < 2 ? (float)mag : (float)(2u + (mag & 1u));
+    const int s = mag < 2 ? -1 : (int)(mag >> 1) - 2;
+    const float v = ldexpf(m, s + e);
+    x[i] = (c & 8u) ? -v : v;
+  }
+  return make_uint4(pack2_bf16(x[0], x[1]), pack2_bf16(x[2], x[3]), pack2_bf16(x[4], x[5]),
+                    pack2_bf16(x[6], x[7]));
+}
+
 }  // namespace msa

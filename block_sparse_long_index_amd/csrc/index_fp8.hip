@@ -106,30 +106,8 @@ __global__ __launch_bounds__(256) void quantize_k_kernel(const uint16_t* __restr
 }
 
 // ---------------------------------------------------------------------------
-// 4-bit index keys.  A group's exponent e is the smallest integer with
-// amax * 2^-e <= 6 (the largest E2M1 value), clamped to [-127, 127], 0 for an
-// all-zero group; codes are the nearest E2M1 value of x * 2^-e, ties to the
-// even code, with x's sign bit.
+// 4-bit index keys (fp4_scale_exponent, e2m1_code: fp8_common.h)
 // ---------------------------------------------------------------------------
-__device__ inline int fp4_scale_exponent(float amax) {
-  if (amax == 0.f) return 0;
-  int E;
-  const float f = frexpf(amax, &E);
-  const int e = f <= 0.75f ? E - 3 : E - 2;   // f * 2^3 <= 6 exactly when f <= 0.75
-  return min(127, max(-127, e));
-}
-
-// E2M1 code of one value already scaled into [-6, 6].  The thresholds are the
-// midpoints of the grid 0, .5, 1, 1.5, 2, 3, 4, 6; at a midpoint the even code
-// (mantissa bit 0: 0, 1, 2, 4) wins, hence > below even codes and >= below odd.
-__device__ inline uint32_t e2m1_code(float y) {
-  const float a = fabsf(y);
-  const uint32_t c = (uint32_t)(a > 0.25f) + (uint32_t)(a >= 0.75f) + (uint32_t)(a > 1.25f) +
-                     (uint32_t)(a >= 1.75f) + (uint32_t)(a > 2.5f) + (uint32_t)(a >= 3.5f) +
-                     (uint32_t)(a > 5.f);
-  return c | ((__float_as_uint(y) >> 31) << 3);
-}
-
 // Key rows of one (block beta, sequence b) per workgroup, 8 elements per lane:
 // the four lanes of a 32-element group share its maximum through shuffles.
 // Codes: [rows][DI / 2] bytes; exponents: [rows][DI / 32], row as for k_idx.

@@ -63,6 +63,83 @@ __global__ __launch_bounds__(256) void quantize_kv_kernel(const uint16_t* __rest
   if (tid == 0) xe[kv.block_index(b, beta, nb_max) * G + g] = (uint8_t)(e + 127);
 }
 
+// 4-bit keys or values: E2M1 codes with one E8M0 exponent per 32 elements of
+// every (key, KV head) row (the same rule as the 4-bit index keys: e is the
+// smallest integer with amax * 2^-e <= 6, clamped to [-127, 127]; nearest
+// E2M1 value of x * 2^-e, ties to the even code, with x's sign bit).  One
+// workgroup per (block beta, sequence b): the block's keys are n * G rows of D
+// elements, 8 per lane; the four lanes of a 32-element group share its
+// maximum through two shuffles.  Codes [rows][G][D/2] (element 2i in the low
+// nibble), exponents [rows][G][D/32]; rows past the sequence are not written.
+template <int D>
+__global__ __launch_bounds__(256) void quantize_kv4_kernel(const uint16_t* __restrict__ x,
+                                                           const int32_t* __restrict__ cu_k, KvMap kv,
+                                                           int G, uint8_t* __restrict__ x4,
+                                                           uint8_t* __restrict__ xe) {
+  constexpr int LPR = D / 8;    // 8-element chunks per (key, head) row
+  const int beta = blockIdx.x, b = blockIdx.y;
+  const int koff = cu_k[b], lk = cu_k[b + 1] - koff;
+  const int n = min(kBlock, lk - beta * kBlock);
+  if (n <= 0) return;
+  const size_t r0 = kv.block_row(b, koff, beta) * G;      // first (key, head) row of the block
+  const int chunks = n * G * LPR;                          // a multiple of 4: whole groups
+  const int iters = (kBlock * G * LPR + 255) / 256;        // the same count for every lane
+  for (int it = 0; it < iters; ++it) {
+    const int c = (int)threadIdx.x + it * 256;
+    const bool ok = c < chunks;
+    const int row = c / LPR, col = c % LPR;
+    uint4 v = make_uint4(0, 0, 0, 0);
+    if (ok) v = *reinterpret_cast<const uint4*>(x + (r0 + row) * D + col * 8);
+    float f[8];
+    unpack8_bf16(v, f);
+    float a = 0.f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) a = fmaxf(a, fabsf(f[j]));
+    a = fmaxf(a, shfl_xor_f(a, 1));
+    a = fmaxf(a, shfl_xor_f(a, 2));
+    const int e = fp4_scale_exponent(a);
+    uint32_t w = 0;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) w |= e2m1_code(ldexpf(f[j], -e)) << (4 * j);
+    if (ok) {
+      *reinterpret_cast<uint32_t*>(x4 + (r0 + row) * (D / 2) + col * 4) = w;
+      if ((col & 3) == 0) xe[(r0 + row) * (D / 32) + col / 4] = (uint8_t)(e + 127);
+    }
+  }
+}
+
+template <int D>
+static hipError_t launch_main_quantize_kv4_d(const void* q, const void* k, const void* v,
+                                             const int32_t* cu_k, KvMap kv, int batch, int G,
+                                             int nb_max, long long q_rows, void* q8, uint8_t* qe,
+                                             void* k4, uint8_t* ke, void* v4, uint8_t* ve,
+                                             hipStream_t st) {
+  if (q && q_rows > 0) {
+    const long long threads = q_rows * (D / 8);
+    hipLaunchKernelGGL(quantize_q_kernel<D>, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0,
+                       st, (const uint16_t*)q, q_rows, (uint8_t*)q8, qe);
+  }
+  const dim3 grid(nb_max, batch);
+  if (k && nb_max > 0)
+    hipLaunchKernelGGL(quantize_kv4_kernel<D>, grid, dim3(256), 0, st, (const uint16_t*)k, cu_k, kv,
+                       G, (uint8_t*)k4, ke);
+  if (v && nb_max > 0)
+    hipLaunchKernelGGL(quantize_kv4_kernel<D>, grid, dim3(256), 0, st, (const uint16_t*)v, cu_k, kv,
+                       G, (uint8_t*)v4, ve);
+  return hipGetLastError();
+}
+
+hipError_t launch_main_quantize_q8kv4(int D, const void* q, const void* k, const void* v,
+                                      const int32_t* cu_k, KvMap kv, int batch, int G, int nb_max,
+                                      long long q_rows, void* q8, uint8_t* qe, void* k4,
+                                      uint8_t* ke, void* v4, uint8_t* ve, hipStream_t st) {
+  switch (D) {
+    case 64: return launch_main_quantize_kv4_d<64>(q, k, v, cu_k, kv, batch, G, nb_max, q_rows, q8, qe, k4, ke, v4, ve, st);
+    case 128: return launch_main_quantize_kv4_d<128>(q, k, v, cu_k, kv, batch, G, nb_max, q_rows, q8, qe, k4, ke, v4, ve, st);
+  }
+  return hipErrorInvalidValue;
+}
+
 template <int D>
 static hipError_t launch_main_quantize_d(const void* q, const void* k, const void* v,
                                          const int32_t* cu_k, KvMap kv, int batch, int G,

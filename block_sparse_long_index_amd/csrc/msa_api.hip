@@ -35,6 +35,9 @@ hipError_t launch_attend_decode(int, int, const void*, const void*, const void*,
 hipError_t launch_main_quantize_fp8(int, const void*, const void*, const void*, const int32_t*, KvMap,
                                     int, int, int, long long, void*, uint8_t*, void*, uint8_t*,
                                     void*, uint8_t*, hipStream_t);
+hipError_t launch_main_quantize_q8kv4(int, const void*, const void*, const void*, const int32_t*,
+                                      KvMap, int, int, int, long long, void*, uint8_t*, void*,
+                                      uint8_t*, void*, uint8_t*, hipStream_t);
 hipError_t launch_merge(int, const float*, const float2*, const int32_t*, int, int, int, int, int,
                         void*, float*, hipStream_t);
 int fp8_max_blocks_per_sequence();
@@ -201,13 +204,13 @@ bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 enum KernelId { K_INDEX_PREFILL, K_INDEX_DECODE, K_TOPK, K_LISTS, K_ATTEND, K_MERGE,
                 K_QUANT_FP8, K_INDEX_PREFILL_FP8, K_INDEX_DECODE_FP8, K_PROJECT, K_MASS,
                 K_INDEX_KL, K_QUANT_MAIN_FP8, K_QUANT_Q8K4, K_INDEX_PREFILL_Q8K4,
-                K_INDEX_DECODE_Q8K4 };
+                K_INDEX_DECODE_Q8K4, K_QUANT_MAIN_Q8KV4 };
 const char* const kKernelNames[MSA_PROFILE_KERNELS] = {
     "index_select_prefill", "index_score_decode", "topk_select",
     "build_lists", "attend_blocks", "merge_partials",
     "quantize_index_fp8", "index_select_prefill_fp8", "index_score_decode_fp8",
     "index_project", "block_mass", "index_kl", "quantize_main_fp8", "quantize_index_q8k4",
-    "index_select_prefill_q8k4", "index_score_decode_q8k4"};
+    "index_select_prefill_q8k4", "index_score_decode_q8k4", "quantize_main_q8kv4"};
 
 std::atomic<bool> g_prof_on{false};
 std::mutex g_prof_mu;
@@ -522,7 +525,7 @@ static msa_status_t attend_impl(const msa_dims_t* dims, const void* q, const voi
     return fail(MSA_ERR_NULL_ARG, "a required pointer is NULL");
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(sel) || !aligned16(out) ||
       !aligned16(workspace) || (lists && (!aligned16(block_offsets) || !aligned16(block_entries))) ||
-      (lse && !aligned16(lse)))
+      (lse && !aligned16(lse)) || (f8.kv4 && (!aligned16(f8.ke) || !aligned16(f8.ve))))
     return fail(MSA_ERR_ALIGNMENT, "tensor pointers must be 16-byte aligned");
   if (workspace_bytes < ws_attend(dims, x))
     return fail(MSA_ERR_WORKSPACE_TOO_SMALL, "attend workspace too small");
@@ -539,7 +542,7 @@ static msa_status_t attend_impl(const msa_dims_t* dims, const void* q, const voi
       ProfScope ps(K_ATTEND, st);
       if (!lists)
         // a few queries per sequence: each selected block is hit by few queries;
-        // one wave per (query, slot) reads it straight from the selection
+        // one workgroup per (group, slot, query) reads it straight from the selection
         e = msa::launch_attend_decode(x.D, x.hpg, q, k, v, f8, cu_seqlens_q, cu_seqlens_k, x.kv,
                                       dims->batch, x.G, x.Hq, x.top_k, x.nb_max, sel, a, z,
                                       scale_log2, part_acc, part_ml, st);
@@ -587,6 +590,19 @@ msa_status_t msa_attend_fp8(const msa_dims_t* dims, const void* q8, const uint8_
                      workspace_bytes, stream);
 }
 
+msa_status_t msa_attend_q8kv4(const msa_dims_t* dims, const void* q8, const uint8_t* q_exp,
+                              const void* k4, const uint8_t* k_exp4, const void* v4,
+                              const uint8_t* v_exp4, const int32_t* cu_seqlens_q,
+                              const int32_t* cu_seqlens_k, const int32_t* sel,
+                              const int32_t* block_offsets, const int32_t* block_entries, void* out,
+                              float* lse, void* workspace, size_t workspace_bytes, void* stream) {
+  if (dims && dims->total_q > 0 && (!q_exp || !k_exp4 || !v_exp4))
+    return fail(MSA_ERR_NULL_ARG, "a required pointer is NULL");
+  return attend_impl(dims, q8, k4, v4, msa::MainFp8{q_exp, k_exp4, v_exp4, 1}, cu_seqlens_q,
+                     cu_seqlens_k, sel, block_offsets, block_entries, out, lse, nullptr, workspace,
+                     workspace_bytes, stream);
+}
+
 msa_status_t msa_main_quantize_fp8(const msa_dims_t* dims, const void* q, const void* k,
                                    const void* v, const int32_t* cu_seqlens_k, void* q8,
                                    uint8_t* q_exp, void* k8, uint8_t* k_exp, void* v8,
@@ -610,6 +626,32 @@ msa_status_t msa_main_quantize_fp8(const msa_dims_t* dims, const void* q, const 
   hipError_t e = msa::launch_main_quantize_fp8(
       x.D, has_q ? q : nullptr, has_k ? k : nullptr, has_v ? v : nullptr, cu_seqlens_k, x.kv,
       dims->batch, x.G, x.nb_max, has_q ? x.total_q * x.Hq : 0, q8, q_exp, k8, k_exp, v8, v_exp, st);
+  return e == hipSuccess ? MSA_OK : hip_fail(e);
+}
+
+msa_status_t msa_main_quantize_q8kv4(const msa_dims_t* dims, const void* q, const void* k,
+                                     const void* v, const int32_t* cu_seqlens_k, void* q8,
+                                     uint8_t* q_exp, void* k4, uint8_t* k_exp4, void* v4,
+                                     uint8_t* v_exp4, void* stream) {
+  Derived x;
+  msa_status_t s = check_dims(dims, &x);
+  if (s != MSA_OK) return s;
+  const bool has_q = x.total_q > 0 && q, has_kv = dims->total_k > 0;
+  const bool has_k = has_kv && k, has_v = has_kv && v;
+  if ((has_q && (!q8 || !q_exp)) || ((has_k || has_v) && !cu_seqlens_k) ||
+      (has_k && (!k4 || !k_exp4)) || (has_v && (!v4 || !v_exp4)))
+    return fail(MSA_ERR_NULL_ARG, "a required pointer is NULL");
+  if ((has_q && (!aligned16(q) || !aligned16(q8))) ||
+      (has_k && (!aligned16(k) || !aligned16(k4) || !aligned16(k_exp4))) ||
+      (has_v && (!aligned16(v) || !aligned16(v4) || !aligned16(v_exp4))))
+    return fail(MSA_ERR_ALIGNMENT, "tensor pointers must be 16-byte aligned");
+  if (!has_q && !has_k && !has_v) return MSA_OK;
+  hipStream_t st = (hipStream_t)stream;
+  ProfScope ps(K_QUANT_MAIN_Q8KV4, st);
+  hipError_t e = msa::launch_main_quantize_q8kv4(
+      x.D, has_q ? q : nullptr, has_k ? k : nullptr, has_v ? v : nullptr, cu_seqlens_k, x.kv,
+      dims->batch, x.G, x.nb_max, has_q ? x.total_q * x.Hq : 0, q8, q_exp, k4, k_exp4, v4, v_exp4,
+      st);
   return e == hipSuccess ? MSA_OK : hip_fail(e);
 }
 

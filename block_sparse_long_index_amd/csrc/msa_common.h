@@ -28,12 +28,15 @@ struct RowPos {
 // Contiguous: sequence b owns rows cu_k[b] .. cu_k[b+1]-1.  Paged: block beta
 // of sequence b is page table[b * max_blocks + beta], i.e. rows
 // 128 * page .. 128 * page + 127 of the cache.
-// E8M0 exponents of a quantised Main Branch's inputs (q per (row, head); k and
-// v per (block index, KV head)); all null for bf16 inputs.
+// E8M0 exponents of a quantised Main Branch's inputs: q per (row, head) of
+// E4M3 codes; k and v per (block index, KV head) of E4M3 codes, or (kv4 != 0)
+// per 32 elements of every (key, KV head) row of E2M1 codes.  All null for
+// bf16 inputs.
 struct MainFp8 {
   const uint8_t* qe;
   const uint8_t* ke;
   const uint8_t* ve;
+  int kv4;
 };
 
 struct KvMap {
@@ -158,6 +161,15 @@ __device__ inline uint2 lds_read_tr16(const uint8_t* p) {
 // (lds_base wave-uniform)
 __device__ inline void lds_load16(const uint8_t* src, uint8_t* lds_base) {
   __builtin_amdgcn_global_load_lds(src, lds_base, 16, 0, 0);
+}
+// the same with N = 1, 2 or 4 bytes per lane: lane L's N bytes land at
+// lds_base + 4 L whatever N is
+template <int N>
+__device__ inline void lds_load_n(const uint8_t* src, uint8_t* lds_base) {
+  static_assert(N == 1 || N == 2 || N == 4, "1, 2 or 4 bytes per lane");
+  if constexpr (N == 4) __builtin_amdgcn_global_load_lds(src, lds_base, 4, 0, 0);
+  else if constexpr (N == 2) __builtin_amdgcn_global_load_lds(src, lds_base, 2, 0, 0);
+  else __builtin_amdgcn_global_load_lds(src, lds_base, 1, 0, 0);
 }
 
 // vmcnt(n) with the other counters left alone (gfx9 s_waitcnt encoding)

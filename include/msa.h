@@ -405,6 +405,45 @@ msa_status_t msa_attend_fp8(const msa_dims_t* dims, const void* q8, const uint8_
  * steps), a negative msa_status_t for invalid dims. */
 int32_t msa_attend_reads_lists(const msa_dims_t* dims);
 
+/*
+ * Main Branch with 4-bit keys and values ("Q8KV4").  The pages state that
+ * the production indexer and Main Branch move from 8-bit queries and
+ * keys/values to 8-bit queries and 4-bit keys/values (dot-ai.myuuu.co.jp
+ * article on MiniMax M3.1 Flash, section "MiniMax M3.1 Flashとは？428Bの
+ * MoEモデルがウェイト公開", on the model card's quantisation notes).  This
+ * library's reading: queries as msa_main_quantize_fp8 (E4M3, one E8M0
+ * exponent per (query row, head)); keys and values in the 4-bit index keys'
+ * format (see msa_index_quantize_q8k4): OCP E2M1 codes, two per byte
+ * (element 2i in the low nibble), one E8M0 exponent per 32 consecutive
+ * elements of every (key, KV head) row, e = smallest integer with
+ * max|x| * 2^-e <= 6 clamped to [-127, 127], nearest E2M1 value of x * 2^-e
+ * with ties to the even code.
+ *
+ * msa_main_quantize_q8kv4: bf16 q / k / v -> codes + exponents; any of q, k,
+ *   v may be NULL (its outputs are then not touched): a decode step
+ *   quantises its new queries against a cache quantised when written.
+ *   q8      uint8 E4M3 [total_q, num_q_heads, head_dim]        out
+ *   q_exp   uint8 E8M0 [total_q, num_q_heads]                   out
+ *   k4, v4  uint8 [total_k, num_kv_heads, head_dim / 2]         out
+ *   k_exp4, v_exp4  uint8 E8M0 [total_k, num_kv_heads, head_dim / 32]  out
+ *   Rows as in k (page rows when paged); only the sequences' keys are
+ *   written.  q, k, v, q8, k4, v4, k_exp4, v_exp4 16-byte aligned.
+ * msa_attend_q8kv4: msa_attend on the dequantised q, k, v.  The kernels
+ *   dequantise exactly into bf16 operands (an E2M1 value times a power of
+ *   two is a bf16 value) and then compute what msa_attend computes; lists,
+ *   outputs, workspace and errors as msa_attend.
+ */
+msa_status_t msa_main_quantize_q8kv4(const msa_dims_t* dims, const void* q, const void* k,
+                                     const void* v, const int32_t* cu_seqlens_k, void* q8,
+                                     uint8_t* q_exp, void* k4, uint8_t* k_exp4, void* v4,
+                                     uint8_t* v_exp4, void* stream);
+msa_status_t msa_attend_q8kv4(const msa_dims_t* dims, const void* q8, const uint8_t* q_exp,
+                              const void* k4, const uint8_t* k_exp4, const void* v4,
+                              const uint8_t* v_exp4, const int32_t* cu_seqlens_q,
+                              const int32_t* cu_seqlens_k, const int32_t* sel,
+                              const int32_t* block_offsets, const int32_t* block_entries, void* out,
+                              float* lse, void* workspace, size_t workspace_bytes, void* stream);
+
 /* Static description of a status code. */
 const char* msa_status_string(msa_status_t status);
 
@@ -422,13 +461,14 @@ int32_t msa_abi_version(void);
  * 4 attend_blocks, 5 merge_partials, 6 quantize_index_fp8,
  * 7 index_select_prefill_fp8, 8 index_score_decode_fp8, 9 index_project, 10 block_mass,
  * 11 index_kl, 12 quantize_main_fp8, 13 quantize_index_q8k4,
- * 14 index_select_prefill_q8k4, 15 index_score_decode_q8k4.  msa_profile_collect() waits for every
+ * 14 index_select_prefill_q8k4, 15 index_score_decode_q8k4, 16 quantize_main_q8kv4.
+ * msa_profile_collect() waits for every
  * recorded event (it blocks the host), writes the summed milliseconds and the
  * launch count per stage into caller arrays of MSA_PROFILE_KERNELS entries,
  * and forgets the records.  Events are host-side HIP objects kept in a pool
  * for the life of the process; no device memory is allocated.
  */
-#define MSA_PROFILE_KERNELS 16
+#define MSA_PROFILE_KERNELS 17
 msa_status_t msa_profile_enable(int32_t enable);
 msa_status_t msa_profile_collect(float* total_ms, int32_t* launches);
 const char* msa_profile_kernel_name(int32_t id);

@@ -61,7 +61,7 @@ class DequantizedRows4:
     def __len__(self):
         return self.hi - self.lo
 
-    _CHUNK = 4096
+    _CHUNK = 128   # rows quantised together (any split gives the same values)
 
     def _chunk(self, c):
         if c not in self.cache:
@@ -79,6 +79,8 @@ class DequantizedRows4:
         rows, col = idx
         rows = np.asarray(rows, dtype=np.int64) + self.lo
         out = np.empty((len(rows),) + self.row_shape[1:])
-        for i, r in enumerate(rows):
-            out[i] = self._chunk(int(r) // self._CHUNK)[int(r) % self._CHUNK, int(col)]
+        chunk = rows // self._CHUNK
+        for c in np.unique(chunk):
+            sel = chunk == c
+            out[sel] = self._chunk(int(c))[rows[sel] % self._CHUNK, int(col)]
         return out

@@ -195,6 +195,28 @@ def test_q8k4_entry_points_validate_on_host():
     assert s4(ctypes.byref(empty), None, None, None, None, None, None, None, None, None, big, None) == 0
 
 
+def test_q8kv4_main_entry_points_validate_on_host():
+    d = _dims()
+    P = ctypes.c_void_p
+    ok = P(0x10000)
+    odd = P(0x10004)
+    big = ctypes.c_size_t(1 << 40)
+    qz = lib.msa_main_quantize_q8kv4
+    # (dims, q, k, v, cu_k, q8, q_exp, k4, k_exp4, v4, v_exp4, stream)
+    assert qz(ctypes.byref(d), ok, None, None, None, None, ok, None, None, None, None, None) == 1
+    assert qz(ctypes.byref(d), None, ok, None, ok, None, None, ok, None, None, None, None) == 1
+    assert qz(ctypes.byref(d), None, ok, None, None, None, None, ok, ok, None, None, None) == 1
+    assert qz(ctypes.byref(d), None, ok, None, ok, None, None, ok, odd, None, None, None) == 4
+    assert qz(ctypes.byref(d), None, None, ok, ok, None, None, None, None, odd, ok, None) == 4
+    assert qz(ctypes.byref(d), None, None, None, None, None, None, None, None, None, None, None) == 0
+    at = lib.msa_attend_q8kv4
+    # (dims, q8, q_exp, k4, k_exp4, v4, v_exp4, cu_q, cu_k, sel, offs, ents, out, lse, ws, bytes, stream)
+    assert at(ctypes.byref(d), ok, ok, ok, None, ok, ok, ok, ok, ok, ok, ok, ok, None, ok, big, None) == 1
+    assert at(ctypes.byref(d), ok, ok, ok, odd, ok, ok, ok, ok, ok, ok, ok, ok, None, ok, big, None) == 4
+    assert at(ctypes.byref(d), ok, ok, ok, ok, ok, ok, ok, ok, ok, ok, ok, ok, None, ok,
+              ctypes.c_size_t(8), None) == 5
+
+
 def test_projection_entry_point_validates_on_host():
     d = _dims()
     P = ctypes.c_void_p
