@@ -108,9 +108,18 @@ def work_model(w) -> dict:
     if _decode_like(w):         # a decode step quantises only its new queries
         main_quant_bytes = T * Hq * d * 3 + T * Hq
     decode_kv_fp8_delta = kv_once_fp8 - kv_once + T * Hq * (d + 1 - 2 * d)
+    # 8-bit q with 4-bit k and v: d / 2 code bytes + d / 32 exponent bytes per (key, head) row
+    kv4_row = d / 2 + d / 32
+    kv_once_kv4 = kv_blocks * BLOCK * kv4_row * 2
+    attend_bytes_kv4 = sel_total * hpg * (d + 1) + part_write + kv_once_kv4
+    main_quant_kv4_bytes = T * Hq * (d * 3 + 1) + 2 * w.total_k * G * (d * 2 + kv4_row)
+    if _decode_like(w):
+        main_quant_kv4_bytes = T * Hq * (d * 3 + 1)
+    decode_kv4_delta = kv_once_kv4 - kv_once + T * Hq * (d + 1 - 2 * d)
     return dict(index_flops=idx_flops, main_flops=main_flops, sel_total=sel_total,
                 attend_bytes_fp8=attend_bytes_fp8, main_quant_bytes=main_quant_bytes,
-                decode_kv_fp8_delta=decode_kv_fp8_delta,
+                decode_kv_fp8_delta=decode_kv_fp8_delta, attend_bytes_kv4=attend_bytes_kv4,
+                main_quant_kv4_bytes=main_quant_kv4_bytes, decode_kv4_delta=decode_kv4_delta,
                 attend_bytes=attend_bytes, merge_bytes=merge_bytes, topk_bytes=topk_bytes,
                 decode_bytes=decode_bytes, kv_once_bytes=kv_once, quant_bytes=quant_bytes,
                 decode_fp8_bytes=decode_fp8_bytes, index_decode_fp8_bytes=index_decode_fp8_bytes,
@@ -386,10 +395,12 @@ def main():
                          "(fp8); or 8-bit queries with 4-bit E2M1 keys scaled per 32 elements, "
                          "scored on the microscaled matrix cores (q8k4).  A decode step's "
                          "index-key cache is stored quantised; only its new queries are quantised")
-    ap.add_argument("--main", choices=["bf16", "fp8"], default="bf16",
-                    help="Main Branch inputs: bf16 q/k/v, or FP8 E4M3 codes with power-of-two "
-                         "scales (quantised in the step; a decode step's key/value cache is "
-                         "stored quantised and only its new queries are quantised)")
+    ap.add_argument("--main", choices=["bf16", "fp8", "q8kv4"], default="bf16",
+                    help="Main Branch inputs: bf16 q/k/v; FP8 E4M3 codes with power-of-two "
+                         "scales (fp8); or E4M3 queries with 4-bit E2M1 keys and values scaled "
+                         "per 32 elements (q8kv4).  Prefill quantises in the step; a decode "
+                         "step's key/value cache is stored quantised and only its new queries "
+                         "are quantised")
     ap.add_argument("--project-dim", type=int, default=0,
                     help="also run the index projections in the step: q_idx and the new tokens' "
                          "k_idx from a layer input of this width (0: off; the index projections "
@@ -479,10 +490,12 @@ def main():
 
     # fp8 Main Branch: prefill quantises q, k, v in the step; decode keeps a quantised K/V
     # cache (quantised once, outside the step) and quantises its new queries
-    f8m = msa.Fp8Main(dims, dev) if args.main == "fp8" else None
+    f8m = (msa.Fp8Main(dims, dev) if args.main == "fp8" else
+           msa.Q8KV4Main(dims, dev) if args.main == "q8kv4" else None)
     step_k, step_v = kc, vc
     if f8m is not None and _decode_like(w):
-        msa.main_quantize_fp8(dims, None, kc, vc, t["cu_seqlens_k"], f8m)
+        (msa.main_quantize_fp8 if args.main == "fp8" else msa.main_quantize_q8kv4)(
+            dims, None, kc, vc, t["cu_seqlens_k"], f8m)
         torch.cuda.synchronize()
         step_k = step_v = None
 
@@ -602,9 +615,11 @@ def main():
                         frac=a / peak, traffic=traffic_record(name),
                         dtype={"index_select_prefill": "bf16", "index_select_prefill_fp8": "fp8 e4m3",
                                "index_select_prefill_q8k4": "e2m1 keys x e4m3 queries"}[name])
-        bytes_ = {"attend_blocks": wm["attend_bytes" if f8m is None else "attend_bytes_fp8"],
+        bytes_ = {"attend_blocks": wm[{"bf16": "attend_bytes", "fp8": "attend_bytes_fp8",
+                                       "q8kv4": "attend_bytes_kv4"}[args.main]],
                   "merge_partials": wm["merge_bytes"],
                   "quantize_main_fp8": wm["main_quant_bytes"],
+                  "quantize_main_q8kv4": wm["main_quant_kv4_bytes"],
                   "topk_select": wm["topk_bytes"],
                   "index_score_decode": wm["index_decode_bytes"],
                   "index_score_decode_fp8": wm["index_decode_fp8_bytes"],
@@ -631,7 +646,7 @@ def main():
         dec_bytes = wm["decode_fp8_bytes" if fp8 is not None else
                        "decode_q8k4_bytes" if qk is not None else "decode_bytes"]
         if f8m is not None:
-            dec_bytes += wm["decode_kv_fp8_delta"]
+            dec_bytes += wm["decode_kv_fp8_delta" if args.main == "fp8" else "decode_kv4_delta"]
         gbs = dec_bytes / (ms_per_step / 1e3) / 1e9
         extra["decode_hbm_GBps"] = gbs
         extra["decode_hbm_frac"] = gbs * 1e9 / PEAK_HBM_BYTES
@@ -668,7 +683,20 @@ def main():
             from oracle import fp4_index as F4
             kidx = (F4.dequantize_k_idx4(*F4.quantize_k_idx4(kidx)) if pooled
                     else _SliceDequant4(kidx, F4))
-        if f8m is not None:
+        if f8m is not None and args.main == "q8kv4":
+            # 8-bit q as in the fp8 Main Branch; k and v scale per 32 elements of a
+            # (key, head) row, so any slice of rows quantises alone
+            from oracle import fp4_main as M4
+            from oracle import fp8_main as FM
+            if pooled:
+                kk = M4.dequantize_kv4(*M4.quantize_kv4(kk))
+                vv = M4.dequantize_kv4(*M4.quantize_kv4(vv))
+            else:
+                def fetch(x):
+                    return lambda lo, hi: x[lo:hi].double().cpu().numpy()
+                kk = M4.DequantizedRows4(fetch(t["k"]), w.total_k, t["k"].shape[1:])
+                vv = M4.DequantizedRows4(fetch(t["v"]), w.total_k, t["v"].shape[1:])
+        elif f8m is not None:
             # the oracle attends on the dequantised q, k, v it computes itself from the bf16 inputs
             from oracle import fp8_main as FM
             if pooled:
@@ -733,7 +761,8 @@ def main():
                           f"full Index and Main Branch in fp64 numpy"
                           f"{' (on the dequantised fp8 index projections)' if fp8 is not None else ''}"
                           f"{' (on the dequantised 8-bit index queries and 4-bit index keys)' if qk is not None else ''}"
-                          f"{' (on the dequantised fp8 q, k, v)' if f8m is not None else ''}; "
+                          f"{' (on the dequantised fp8 q, k, v)' if args.main == 'fp8' else ''}"
+                          f"{' (on the dequantised 8-bit q and 4-bit k, v)' if args.main == 'q8kv4' else ''}; "
                           f"{used} worker process(es), 1 BLAS thread each; {dt:.1f} s")
     elif pool:
         pool.close()
@@ -750,7 +779,8 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": ("bf16" if fp8 is None and f8m is None and qk is None else
-                  (("bf16" if f8m is None else "fp8 e4m3 storage, bf16 MFMA") + " (Main Branch), "
+                  ({"bf16": "bf16", "fp8": "fp8 e4m3 storage, bf16 MFMA",
+                    "q8kv4": "e4m3 q, e2m1 k/v storage, bf16 MFMA"}[args.main] + " (Main Branch), "
                    + ("fp8 e4m3" if fp8 is not None else
                       "e4m3 queries, e2m1 keys" if qk is not None else "bf16") + " (Index Branch)")),
         "data": "synthetic",

@@ -16,8 +16,12 @@
 // loads; V is loaded into registers at the same time and written over K, as
 // bf16, once the scores are done, so waiting for K never waits for V (the
 // compiler cannot tell two direct-to-LDS streams apart) and the block needs
-// 32 KiB of LDS.  8-bit inputs (E4M3 codes with power-of-two scales) are
-// dequantised exactly into bf16: K fragments as they leave LDS, V as it enters.
+// one bf16 tile of LDS (32 KiB at D = 128).  8-bit inputs (E4M3 codes with
+// power-of-two scales) are dequantised exactly into bf16: K fragments as they
+// leave LDS, V as it enters.  4-bit K and V (E2M1 codes, one exponent per 32
+// elements) are small enough to come in together: codes and exponents of
+// both land inside the tile's bytes, V's codes move to registers before the
+// barrier that ends the score phase, and V enters the tile as bf16 after it.
 // Chunk positions are XOR-swizzled: K so that an A-fragment read (16
 // consecutive rows, one 16-byte chunk each) hits 16 bank groups; V so that the
 // transposed reads (ds_read_b64_tr_b16: within 16 lanes, lane 4a + c receives
@@ -25,8 +29,10 @@
 // of 4 rows x 4 chunks hit 16 bank groups.  Those transposed reads give each
 // lane four consecutive keys of one column: the V^T A fragment without a
 // transposing store.  Wave w scores key tile w; the softmax maximum and sum
-// combine through LDS; every key tile's bf16 P goes through LDS, and wave w
-// then forms output columns 32w .. 32w + 31 (D = 64: waves 0 and 1).  Barriers
+// combine through LDS; every key tile's bf16 P goes through LDS (the group's
+// head columns only: with 8 heads a workgroup needs 35 KiB of LDS at D = 128,
+// so 4 fit on a CU), and wave w then forms output columns 32w .. 32w + 31
+// (D = 64: waves 0 and 1).  Barriers
 // are bare (s_barrier after lgkmcnt(0)): a workgroup fence would also wait for
 // the loads still in flight.
 #include "fp8_common.h"
@@ -51,15 +57,19 @@ __global__ __launch_bounds__(256) void attend_decode_lds_kernel(
   constexpr int PER_WAVE = kBlock / ROWS_PER_PIECE / 4;
   constexpr int XB = D / 32;                    // 4-bit rows: exponent bytes per (key, head)
   constexpr int XS = 4;                         // LDS bytes per key of a direct exponent load
-  constexpr int EXP_OFF = kBlock * RBS;         // 4-bit K: the block's exponents after its codes
-  constexpr int VC_OFF = kBlock * RB;           // 4-bit V: codes after the bf16 V tile, then exponents
+  // 4-bit K and V: codes, then exponents, of K and then of V, all inside the
+  // bf16 V tile's bytes (read out before the tile is written)
+  constexpr int EXP_OFF = kBlock * RBS;
+  constexpr int VC_OFF = (EXP_OFF + kBlock * XS + 1023) / 1024 * 1024;
   constexpr int VX_OFF = VC_OFF + kBlock * RBS;
+  static_assert(!KV4 || VX_OFF + kBlock * XS <= kBlock * RB, "4-bit K and V fit the V tile");
   constexpr int KS = D / 16;
   constexpr int DT = D / 32;
-  // K (as stored), then the bf16 V tile; 4-bit V's codes and exponents follow the tile
-  __shared__ __attribute__((aligned(1024))) uint8_t Ks[kBlock * RB + (KV4 ? kBlock * (RBS + XS) : 0)];
+  constexpr int PC = HPG;                       // P columns kept: the group's heads
+  // K as stored (and 4-bit V as stored), then the bf16 V tile over it
+  __shared__ __attribute__((aligned(1024))) uint8_t Ks[kBlock * RB];
   uint8_t* const Vs = Ks;
-  __shared__ __attribute__((aligned(16))) uint4 Pl[4][2][64];
+  __shared__ __attribute__((aligned(16))) uint4 Pl[4][2][2][PC];
   __shared__ float red_m[4][32], red_l[4][32];
 
   const int tid = threadIdx.x;
@@ -213,6 +223,20 @@ __global__ __launch_bounds__(256) void attend_decode_lds_kernel(
   for (int i = 1; i < 16; ++i) mr = fmaxf(mr, sacc[i]);
   mr = fmaxf(mr, shfl_xor_f(mr, 32));
   if (half == 0) red_m[wave][col] = mr;
+  // 4-bit V: this lane's codes (32 codes, one scale group, per piece) and
+  // their exponents leave LDS before the barrier, after which the tile is
+  // overwritten
+  uint4 vcode[KV4 ? PER_WAVE : 1];
+  int vex[KV4 ? PER_WAVE : 1];
+  if constexpr (KV4) {
+#pragma unroll
+    for (int i = 0; i < PER_WAVE; ++i) {
+      const int piece = wave * PER_WAVE + i;
+      const int mv = piece * ROWS_PER_PIECE + lane / CPRS;
+      vcode[i] = *reinterpret_cast<const uint4*>(Ks + VC_OFF + piece * 1024 + lane * 16);
+      vex[i] = (int)Ks[VX_OFF + mv * XS + lane % CPRS] - 127;
+    }
+  }
   barrier();
   mr = fmaxf(fmaxf(red_m[0][col], red_m[1][col]), fmaxf(red_m[2][col], red_m[3][col]));
   const float m = mr * scale_log2;
@@ -226,12 +250,14 @@ __global__ __launch_bounds__(256) void attend_decode_lds_kernel(
       x[e] = __builtin_amdgcn_exp2f(fmaf(sacc[8 * s2 + e], scale_log2, nm));
       l += x[e];
     }
-    Pl[wave][s2][lane] = make_uint4(pack2_bf16(x[0], x[1]), pack2_bf16(x[2], x[3]),
-                                    pack2_bf16(x[4], x[5]), pack2_bf16(x[6], x[7]));
+    if (col < PC)
+      Pl[wave][s2][half][col] = make_uint4(pack2_bf16(x[0], x[1]), pack2_bf16(x[2], x[3]),
+                                           pack2_bf16(x[4], x[5]), pack2_bf16(x[6], x[7]));
   }
   l += shfl_xor_f(l, 32);
   if (half == 0) red_l[wave][col] = l;
-  // every wave's K reads ended at the barrier above: V (bf16) replaces K
+  // every wave's K (and 4-bit V) reads ended at the barrier above: V (bf16)
+  // replaces them
 #pragma unroll
   for (int i = 0; i < PER_WAVE; ++i) {
     const int piece = wave * PER_WAVE + i;
@@ -240,8 +266,8 @@ __global__ __launch_bounds__(256) void attend_decode_lds_kernel(
     if constexpr (KV4) {
       // this lane's own piece of V codes (32 codes: one scale group) -> bf16
       // chunks 4c .. 4c + 3 of the row
-      const uint4 cv = *reinterpret_cast<const uint4*>(Ks + VC_OFF + piece * 1024 + lane * 16);
-      const int e = (int)Ks[VX_OFF + mv * XS + c] - 127;
+      const uint4 cv = vcode[i];
+      const int e = vex[i];
       *reinterpret_cast<uint4*>(Vs + mv * RB + (((4 * c) ^ swz_v(mv)) * 16)) = dequant4_bf16(cv.x, e);
       *reinterpret_cast<uint4*>(Vs + mv * RB + (((4 * c + 1) ^ swz_v(mv)) * 16)) = dequant4_bf16(cv.y, e);
       *reinterpret_cast<uint4*>(Vs + mv * RB + (((4 * c + 2) ^ swz_v(mv)) * 16)) = dequant4_bf16(cv.z, e);
@@ -275,7 +301,9 @@ __global__ __launch_bounds__(256) void attend_decode_lds_kernel(
         const int kb2 = kb1 + 8;
         const uint2 lw = lds_read_tr16(Vs + kb1 * RB + ((cb ^ swz_v(kb1)) * 16) + cofs);
         const uint2 hw = lds_read_tr16(Vs + kb2 * RB + ((cb ^ swz_v(kb2)) * 16) + cofs);
-        oacc = mfma32(as_bf16x8(make_uint4(lw.x, lw.y, hw.x, hw.y)), as_bf16x8(Pl[kt][s2][lane]), oacc);
+        // P columns past the group's heads are zero (their outputs are never stored)
+        const uint4 pb = col < PC ? Pl[kt][s2][half][col] : make_uint4(0, 0, 0, 0);
+        oacc = mfma32(as_bf16x8(make_uint4(lw.x, lw.y, hw.x, hw.y)), as_bf16x8(pb), oacc);
       }
   }
   if (col < HPG) {

@@ -112,22 +112,20 @@ __device__ inline uint32_t e2m1_code(float y) {
   return c | ((__float_as_uint(y) >> 31) << 3);
 }
 
-// Eight E2M1 codes (element i in nibble i of w, low nibble first) at
-// exponent e -> eight bf16 values.  Magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6 are
-// m * 2^s with m in {0, 1, 2, 3}; a value has at most 2 significant bits, so
-// the ldexp and the bf16 rounding are exact (within bf16's range).
-__device__ inline uint4 dequant4_bf16(uint32_t w, int e) {
-  float x[8];
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const uint32_t c = (w >> (4 * i)) & 15u, mag = c & 7u;
-    const float m = mag < 2 ? (float)mag : (float)(2u + (mag & 1u));
-    const int s = mag < 2 ? -1 : (int)(mag >> 1) - 2;
-    const float v = ldexpf(m, s + e);
-    x[i] = (c & 8u) ? -v : v;
-  }
-  return make_uint4(pack2_bf16(x[0], x[1]), pack2_bf16(x[2], x[3]), pack2_bf16(x[4], x[5]),
-                    pack2_bf16(x[6], x[7]));
+// Eight E2M1 codes (element i in nibble i of w, low nibble first) times the
+// group scale s = 2^e -> eight bf16 values.  A code's value has at most 2
+// significant bits, so the product and its bf16 rounding are exact within
+// bf16's range.  One scaled conversion (v_cvt_scalef32_pk_bf16_fp4) turns the
+// two codes of one byte into two bf16 values, low nibble first; over every
+// code, byte position and exponent -127 .. 127 it gives exactly these values.
+__device__ inline uint4 dequant4_bf16_scaled(uint32_t w, float s) {
+  typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
+  return make_uint4(__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, s, 0)),
+                    __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, s, 1)),
+                    __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, s, 2)),
+                    __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, s, 3)));
 }
+
+__device__ inline uint4 dequant4_bf16(uint32_t w, int e) { return dequant4_bf16_scaled(w, ldexpf(1.f, e)); }
 
 }  // namespace msa
