@@ -450,6 +450,8 @@ __global__ __launch_bounds__(NW * 64, 2) void index_select_prefill_fp8_kernel(
 // (row stride DI + 16 bytes).
 template <int DI, int NT>
 struct KTileStage8 {
+  // a decode scan reads each key once: non-temporal loads
+  typedef unsigned v4u_t __attribute__((ext_vector_type(4)));
   static constexpr int kCpr = DI / 16;
   static constexpr int kChunks = kBlock * kCpr;
   static constexpr int kPer = (kChunks + NT - 1) / NT;
@@ -461,7 +463,8 @@ struct KTileStage8 {
     for (int i = 0; i < kPer; ++i) {
       const int c = tid + i * NT;
       if (kChunks % NT == 0 || c < kChunks)
-        r[i] = *reinterpret_cast<const uint4*>(src + (size_t)(c / kCpr) * DI + (c % kCpr) * 16);
+        r[i] = __builtin_bit_cast(uint4, __builtin_nontemporal_load(reinterpret_cast<const v4u_t*>(
+                   src + (size_t)(c / kCpr) * DI + (c % kCpr) * 16)));
     }
   }
   __device__ inline void store(uint8_t* lds, int tid) const {
@@ -583,6 +586,7 @@ __global__ __launch_bounds__(256) void index_score_decode_fp8_kernel(
 // ---------------------------------------------------------------------------
 template <int DI>
 struct K4BlockFrags {
+  // a decode scan reads each key once: non-temporal loads
   typedef unsigned v4u __attribute__((ext_vector_type(4)));
   static constexpr int KS = DI >= 64 ? DI / 64 : 1;
   v4u a[4][KS];     // tile kt, k-step ks: elements 64ks + 32h .. +31 of row 32kt + col
@@ -596,14 +600,15 @@ struct K4BlockFrags {
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
         if (DI > 32 || h == 0)
-          a[kt][ks] = *reinterpret_cast<const v4u*>(k4 + row * (DI / 2) + (DI > 32 ? (2 * ks + h) * 16 : 0));
+          a[kt][ks] = __builtin_nontemporal_load(
+              reinterpret_cast<const v4u*>(k4 + row * (DI / 2) + (DI > 32 ? (2 * ks + h) * 16 : 0)));
         else
           a[kt][ks] = v4u{0, 0, 0, 0};
       }
       const uint8_t* xp = ke4 + row * (DI / 32);
-      if constexpr (DI == 128) x[kt] = *reinterpret_cast<const uint32_t*>(xp);
-      else if constexpr (DI == 64) x[kt] = *reinterpret_cast<const uint16_t*>(xp);
-      else x[kt] = *xp;
+      if constexpr (DI == 128) x[kt] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(xp));
+      else if constexpr (DI == 64) x[kt] = __builtin_nontemporal_load(reinterpret_cast<const uint16_t*>(xp));
+      else x[kt] = __builtin_nontemporal_load(xp);
     }
   }
 };

@@ -60,7 +60,8 @@ struct KTileStage {
 
 
 // A key block staged in registers as clang vectors (plain values that stay in
-// registers even when two stages are live; HIP's uint4 struct does not).
+// registers even when two stages are live; HIP's uint4 struct does not).  A
+// decode scan reads each key once, so the loads are non-temporal.
 template <int DI, int NT>
 struct KTileRegs {
   typedef unsigned v4u __attribute__((ext_vector_type(4)));
@@ -73,7 +74,8 @@ struct KTileRegs {
     for (int i = 0; i < kPer; ++i) {
       const int c = tid + i * NT;
       if (kChunks % NT == 0 || c < kChunks)
-        r[i] = *reinterpret_cast<const v4u*>(src + (size_t)(c / (DI / 8)) * DI + (c % (DI / 8)) * 8);
+        r[i] = __builtin_nontemporal_load(
+            reinterpret_cast<const v4u*>(src + (size_t)(c / (DI / 8)) * DI + (c % (DI / 8)) * 8));
     }
   }
   __device__ inline void store(uint16_t* lds, int tid) const {
