@@ -5,7 +5,7 @@ One step = the whole hot path on one batch of synthetic input already in HBM:
 msa_index_select -> msa_build_block_query_lists -> msa_attend, through the C
 ABI on one stream.  Prints ONE JSON line on stdout; progress goes to stderr.
 
-    python bench.py [--steps K] [--warmup W] [--workload p128k|p1m|p32k|decode|tiny]
+    python bench.py [--steps K] [--warmup W] [--workload p128k|p1m|p32k|decode|verify8|tiny]
                     [--index bf16|fp8|q8k4]
 
 The default workload is the 128K-token single-layer prefill (64 query heads /
