@@ -96,6 +96,16 @@ def test_fp8_main_decode_and_verify():
     _check(w, "fp8-main-verify8")
 
 
+@pytest.mark.parametrize("d,hq,g", [(64, 8, 8), (64, 128, 8), (128, 8, 8), (128, 256, 8),
+                                    (128, 32, 2)])
+def test_fp8_main_decode_head_layouts(d, hq, g):
+    """Decode across head dims and heads per group (1, 16, 32): the P tile
+    keeps the group's head columns only, so every layout is checked."""
+    w = custom([100, 128, 1300, 9000, 257], [1, 1, 1, 1, 1], num_q_heads=hq, num_kv_heads=g,
+               head_dim=d, index_dim=64, top_k=8, seed=101 + d + hq + g, qkv_std=1.0)
+    _check(w, f"fp8-main-decode-d{d}-hpg{hq // g}")
+
+
 def test_fp8_main_wide_magnitudes():
     # per-head and per-block exponents that differ widely: values scaled by 2^-6 .. 2^6
     w = custom([1100, 600], [1100, 600], num_q_heads=8, num_kv_heads=2, head_dim=64, index_dim=32,

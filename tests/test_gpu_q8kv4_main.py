@@ -106,6 +106,16 @@ def test_q8kv4_main_decode_and_verify():
     _check(w, "q8kv4-verify8")
 
 
+@pytest.mark.parametrize("d,hq,g", [(64, 8, 8), (64, 128, 8), (128, 8, 8), (128, 256, 8),
+                                    (128, 32, 2)])
+def test_q8kv4_main_decode_head_layouts(d, hq, g):
+    """Decode across head dims and heads per group (1, 16, 32): the P tile
+    keeps the group's head columns only, so every layout is checked."""
+    w = custom([100, 128, 1300, 9000, 257], [1, 1, 1, 1, 1], num_q_heads=hq, num_kv_heads=g,
+               head_dim=d, index_dim=64, top_k=8, seed=111 + d + hq + g, qkv_std=1.0)
+    _check(w, f"q8kv4-decode-d{d}-hpg{hq // g}")
+
+
 def test_q8kv4_main_decode_head_dim_64():
     w = custom([100, 128, 1300, 9000, 257], [1, 1, 1, 1, 1], num_q_heads=64, num_kv_heads=8,
                head_dim=64, index_dim=64, top_k=8, seed=95, qkv_std=1.0)
