@@ -35,6 +35,8 @@
 // (D = 64: waves 0 and 1).  Barriers
 // are bare (s_barrier after lgkmcnt(0)): a workgroup fence would also wait for
 // the loads still in flight.
+#include <algorithm>
+
 #include "fp8_common.h"
 #include "msa_common.h"
 
@@ -45,7 +47,7 @@ __global__ __launch_bounds__(256) void attend_decode_lds_kernel(
     const void* __restrict__ q, const void* __restrict__ k, const void* __restrict__ v,
     const uint8_t* __restrict__ qe, const uint8_t* __restrict__ ke, const uint8_t* __restrict__ ve,
     const int32_t* __restrict__ cu_q, const int32_t* __restrict__ cu_k, KvMap kv, int batch, int G,
-    int Hq, int top_k, int nb_max, const int32_t* __restrict__ sel, int r0, float scale_log2,
+    int Hq, int top_k, int nb_max, const int32_t* __restrict__ sel, int r0, int rz, float scale_log2,
     float* __restrict__ part_acc, float2* __restrict__ part_ml) {
   constexpr int RB = D * 2;                     // bytes per bf16 row (the V tile)
   constexpr int CPR = RB / 16;                  // 16-byte chunks per bf16 row
@@ -75,7 +77,8 @@ __global__ __launch_bounds__(256) void attend_decode_lds_kernel(
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63, col = lane & 31, half = lane >> 5;
-  const int r = r0 + (int)blockIdx.z, slot = (int)blockIdx.y, g = (int)blockIdx.x;
+  // r0: the pass's first row (partials are indexed from it); rz: this launch's
+  const int r = rz + (int)blockIdx.z, slot = (int)blockIdx.y, g = (int)blockIdx.x;
   const RowPos rp = locate_row(r, cu_q, cu_k, batch);
   const int beta = sel[((size_t)r * G + g) * top_k + slot];
   if (beta < 0 || beta * kBlock >= rp.lk) return;   // the same for the whole workgroup
@@ -323,19 +326,24 @@ static void launch_decode_t(const void* q, const void* k, const void* v, MainFp8
                             const int32_t* cu_q, const int32_t* cu_k, KvMap kv, int batch, int G,
                             int Hq, int top_k, int nb_max, const int32_t* sel, int r0, int r1,
                             float scale_log2, float* part_acc, float2* part_ml, hipStream_t st) {
-  if (f8.qe && f8.kv4)
-    hipLaunchKernelGGL((attend_decode_lds_kernel<D, HPG, true, true>), dim3(G, top_k, r1 - r0), dim3(256),
-                       0, st, q, k, v, f8.qe, f8.ke, f8.ve, cu_q, cu_k, kv, batch, G, Hq, top_k, nb_max,
-                       sel, r0, scale_log2, part_acc, part_ml);
-  else if (f8.qe)
-    hipLaunchKernelGGL((attend_decode_lds_kernel<D, HPG, true, false>), dim3(G, top_k, r1 - r0), dim3(256), 0,
-                       st, q, k, v, f8.qe, f8.ke, f8.ve, cu_q, cu_k, kv, batch, G, Hq, top_k, nb_max,
-                       sel, r0, scale_log2, part_acc, part_ml);
-  else
-    hipLaunchKernelGGL((attend_decode_lds_kernel<D, HPG, false, false>), dim3(G, top_k, r1 - r0), dim3(256), 0,
-                       st, q, k, v, (const uint8_t*)nullptr, (const uint8_t*)nullptr,
-                       (const uint8_t*)nullptr, cu_q, cu_k, kv, batch, G, Hq, top_k, nb_max, sel, r0,
-                       scale_log2, part_acc, part_ml);
+  // rows go in grid z, whose limit is 65535: larger passes take several launches
+  constexpr int kMaxRowsPerLaunch = 65535;
+  for (int rz = r0; rz < r1; rz += kMaxRowsPerLaunch) {
+    const dim3 grid(G, top_k, std::min(r1 - rz, kMaxRowsPerLaunch));
+    if (f8.qe && f8.kv4)
+      hipLaunchKernelGGL((attend_decode_lds_kernel<D, HPG, true, true>), grid, dim3(256), 0, st, q, k, v,
+                         f8.qe, f8.ke, f8.ve, cu_q, cu_k, kv, batch, G, Hq, top_k, nb_max, sel, r0, rz,
+                         scale_log2, part_acc, part_ml);
+    else if (f8.qe)
+      hipLaunchKernelGGL((attend_decode_lds_kernel<D, HPG, true, false>), grid, dim3(256), 0, st, q, k, v,
+                         f8.qe, f8.ke, f8.ve, cu_q, cu_k, kv, batch, G, Hq, top_k, nb_max, sel, r0, rz,
+                         scale_log2, part_acc, part_ml);
+    else
+      hipLaunchKernelGGL((attend_decode_lds_kernel<D, HPG, false, false>), grid, dim3(256), 0, st, q, k, v,
+                         (const uint8_t*)nullptr, (const uint8_t*)nullptr, (const uint8_t*)nullptr, cu_q,
+                         cu_k, kv, batch, G, Hq, top_k, nb_max, sel, r0, rz, scale_log2, part_acc,
+                         part_ml);
+  }
 }
 
 template <int D>

@@ -68,6 +68,7 @@ thread_local std::string g_last_error;
 
 constexpr size_t kDefaultChunkBytes = (size_t)48 << 30;   // workspace cap when q_chunk == 0
 constexpr int kMaxNbLds = 12288;                          // per-sequence blocks the LDS lists hold
+constexpr int kMaxBatch = 65535;                            // a grid dimension's limit
 constexpr int kDecodeRowsMax = 128;                       // (query, group) rows per sequence, decode path
 constexpr int kDecodeAttendMaxQ = 8;                      // queries per sequence, per-(query, slot) attend
 
@@ -90,6 +91,7 @@ struct Derived {
 msa_status_t check_dims(const msa_dims_t* d, Derived* out) {
   if (!d) return fail(MSA_ERR_NULL_ARG, "dims is NULL");
   if (d->batch < 1) return fail(MSA_ERR_BAD_DIMS, "batch must be >= 1");
+  if (d->batch > kMaxBatch) return fail(MSA_ERR_UNSUPPORTED, "batch must be <= 65535 (sequences index a grid dimension)");
   if (d->num_q_heads < 1 || d->num_kv_heads < 1) return fail(MSA_ERR_BAD_DIMS, "head counts must be >= 1");
   if (d->num_q_heads % d->num_kv_heads) return fail(MSA_ERR_BAD_DIMS, "num_q_heads % num_kv_heads != 0");
   int hpg = d->num_q_heads / d->num_kv_heads;

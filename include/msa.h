@@ -73,7 +73,7 @@ typedef enum msa_op {
 
 /* Problem sizes; passed by pointer to every call.  All fields are host values. */
 typedef struct msa_dims {
-  int32_t batch;          /* number of packed sequences, >= 1 */
+  int32_t batch;          /* number of packed sequences, 1 .. 65535 */
   int32_t num_q_heads;    /* Hq; Hq / Hkv must be a power of two <= 32 */
   int32_t num_kv_heads;   /* Hkv = G = number of GQA groups = number of index-query heads */
   int32_t head_dim;       /* d in {64, 128} */

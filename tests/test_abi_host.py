@@ -75,6 +75,7 @@ def test_1m_context_default_workspace_is_bounded():
     (dict(total_q=40000), 2), (dict(max_q_len=40000), 2), (dict(q_chunk=-1), 2),
     (dict(total_q=1 << 26, total_k=1 << 27, max_q_len=1, max_k_len=1), 3),
     (dict(total_k=1 << 22, max_k_len=1 << 22), 3),
+    (dict(batch=65536, total_q=65536, total_k=1 << 20, max_q_len=1, max_k_len=16), 3),
 ])
 def test_bad_dims_rejected(kw, status):
     d = _dims(**kw)

@@ -9,6 +9,7 @@ import numpy as np
 import pytest
 import torch
 
+import block_sparse_long_index_amd as msa
 from msa_inputs import custom, generate, workload
 from oracle import msa_oracle as O
 
@@ -67,6 +68,31 @@ def test_decode_attend_head_layouts(d, hq, g):
     w = custom([100, 128, 1300, 9000, 257], [1, 1, 1, 1, 1], num_q_heads=hq, num_kv_heads=g,
                head_dim=d, index_dim=64, top_k=8, seed=27 + d + hq + g, qkv_std=1.0)
     _full_check(w, tag=f"decode-d{d}-hpg{hq // g}")
+
+
+def test_decode_attend_more_rows_than_one_launch():
+    """8200 sequences x 8 new tokens = 65600 rows, one pass: the decode
+    attention's rows sit in a grid dimension limited to 65535, so the pass
+    takes two launches; rows on both sides of the split are checked."""
+    rng = np.random.default_rng(36)
+    n = 8200
+    lk = [int(x) for x in rng.integers(129, 260, size=n)]
+    w = custom(lk, [8] * n, num_q_heads=2, num_kv_heads=1, head_dim=64, index_dim=32, top_k=2,
+               seed=36, qkv_std=1.0)
+    t = generate(w, "cpu")
+    dims, bufs, _ = run_gpu(w, t)
+    assert w.total_q > 65535 and not msa.attend_reads_lists(dims)
+    P = problem_from(t, w, lazy=True)
+    rows = sorted(set(list(range(8)) + list(range(65520, 65560)) + list(range(w.total_q - 8, w.total_q))
+                      + [int(x) for x in rng.integers(0, w.total_q, size=32)]))
+    ref = P.run(rows, want_scores=True)
+    idx = torch.as_tensor(rows)
+    bad, ties = check_selection(P, rows, bufs.sel.cpu()[idx].numpy(), bufs.sel_score.cpu()[idx].numpy(),
+                                ref, w.index_dim)
+    log(f"[rows>65535] selection mismatches {len(bad)} near-ties {ties}")
+    assert not bad, bad[:3]
+    check_out(bufs.out.cpu()[idx].float().numpy(), ref["out"], bufs.lse.cpu()[idx].numpy(), ref["lse"],
+              "rows>65535")
 
 
 def test_multi_token_decode_path():
