@@ -75,15 +75,18 @@ __global__ __launch_bounds__(256) void quantize_q_kernel(const uint16_t* __restr
 
 // Eight E4M3 codes (little-endian in two dwords) at exponent e -> their
 // eight values as bf16.  decode(code) * 2^e has at most 4 significant bits,
-// so both the ldexp and the bf16 rounding are exact (within bf16's range).
+// so the product and its bf16 rounding are exact (within bf16's range).  One
+// scaled conversion (v_cvt_scalef32_pk_bf16_fp8) turns the two codes of one
+// 16-bit half and the scale 2^e into two bf16 values, low byte first; over
+// every code that is not NaN (the quantisers never produce one), both byte
+// positions and exponents -127 .. 127 it gives exactly these values.
 __device__ inline uint4 dequant8_bf16(uint2 w, int e) {
-  typedef float f2 __attribute__((ext_vector_type(2)));
-  const f2 a = __builtin_amdgcn_cvt_pk_f32_fp8((int)w.x, false);
-  const f2 b = __builtin_amdgcn_cvt_pk_f32_fp8((int)w.x, true);
-  const f2 c = __builtin_amdgcn_cvt_pk_f32_fp8((int)w.y, false);
-  const f2 d = __builtin_amdgcn_cvt_pk_f32_fp8((int)w.y, true);
-  return make_uint4(pack2_bf16(ldexpf(a.x, e), ldexpf(a.y, e)), pack2_bf16(ldexpf(b.x, e), ldexpf(b.y, e)),
-                    pack2_bf16(ldexpf(c.x, e), ldexpf(c.y, e)), pack2_bf16(ldexpf(d.x, e), ldexpf(d.y, e)));
+  typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
+  const float s = ldexpf(1.f, e);
+  return make_uint4(__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w.x, s, false)),
+                    __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w.x, s, true)),
+                    __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w.y, s, false)),
+                    __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w.y, s, true)));
 }
 
 // ---------------------------------------------------------------------------
