@@ -431,7 +431,8 @@ int32_t msa_attend_reads_lists(const msa_dims_t* dims);
  * msa_attend_q8kv4: msa_attend on the dequantised q, k, v.  The kernels
  *   dequantise exactly into bf16 operands (an E2M1 value times a power of
  *   two is a bf16 value) and then compute what msa_attend computes; lists,
- *   outputs, workspace and errors as msa_attend.
+ *   outputs, workspace and errors as msa_attend.  q8, k4, v4, k_exp4 and
+ *   v_exp4 16-byte aligned (MSA_ERR_ALIGNMENT otherwise).
  */
 msa_status_t msa_main_quantize_q8kv4(const msa_dims_t* dims, const void* q, const void* k,
                                      const void* v, const int32_t* cu_seqlens_k, void* q8,
