@@ -731,7 +731,9 @@ def main():
         per_row = (time.perf_counter() - tp0) / len(pilot)
         used = cores if pooled else 1
         n_rows = int(max(16, min(w.total_q, args.cpu_seconds * used / max(per_row, 1e-6))))
-        rows = sorted(set(int(x) for x in rng.integers(0, w.total_q, size=n_rows)))
+        # a workload with fewer rows than the time budget allows (decode) is taken whole
+        rows = (list(range(w.total_q)) if n_rows >= w.total_q else
+                sorted(set(int(x) for x in rng.integers(0, w.total_q, size=n_rows))))
         log(f"[bench] oracle: {per_row * 1e3:.1f} ms/row on one core; sampling {len(rows)} rows "
             f"on {used} worker(s)")
         qh, qih = host_rows(rows)
@@ -757,7 +759,8 @@ def main():
                                 fp8=fp8 is not None or qk is not None)
         log(f"[bench] parity on sampled rows: {parity}")
         cpu = dict(value=len(rows) / dt, unit="tokens/s", cores=used, kind="oracle",
-                   sample=f"{len(rows)} uniformly random query rows of {w.name}, each through the "
+                   sample=(f"all {len(rows)} query rows" if len(rows) == w.total_q else
+                           f"{len(rows)} uniformly random query rows") + f" of {w.name}, each through the "
                           f"full Index and Main Branch in fp64 numpy"
                           f"{' (on the dequantised fp8 index projections)' if fp8 is not None else ''}"
                           f"{' (on the dequantised 8-bit index queries and 4-bit index keys)' if qk is not None else ''}"
