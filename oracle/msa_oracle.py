@@ -310,20 +310,38 @@ def build_block_query_lists(sel, seq_of_row, batch, G, nb_max):
 # ----------------------------------------------------------------------------
 # near-tie classification (for comparing a float32 selection to this one)
 # ----------------------------------------------------------------------------
+def _tie_tolerance(S_g, beta_p, top_k, rel):
+    """(S_(k-1), S_(k), rel * max(|S_(k-1)|, |S_(k)|, 1e-30)) over the
+    non-local blocks 0 .. beta_p - 1, sorted by score descending (1-based
+    order statistics).  Only defined when more than k-1 such blocks exist."""
+    v = np.sort(np.asarray(S_g[:beta_p], dtype=np.float64))[::-1]
+    a, b = float(v[top_k - 2]), float(v[top_k - 1])
+    return a, b, rel * max(abs(a), abs(b), 1e-30)
+
+
 def near_tie(S_g, beta_p, top_k, rel=1e-4):
     """True when the (k-1)-th and k-th best non-local block scores are within
-    `rel` (relative): then more than one selection is correct."""
+    `rel` (relative): then more than one selection is correct.
+
+    Rows with at most k-1 non-local blocks take every block, and k = 1 takes
+    only the local block: neither has a choice to tie over.
+    """
     if beta_p <= top_k - 1 or top_k < 2:
         return False
-    v = np.sort(np.asarray(S_g[:beta_p], dtype=np.float64))[::-1]
-    a, b = v[top_k - 2], v[top_k - 1]
-    return (a - b) <= rel * max(abs(a), abs(b), 1e-30)
+    a, b, tol = _tie_tolerance(S_g, beta_p, top_k, rel)
+    return (a - b) <= tol
 
 
 def valid_selection(S_g, beta_p, top_k, chosen, rel=1e-4):
-    """A selection (ascending, incl. local) is valid if it has the local block,
-    the right size, and every chosen non-local block scores at least the
-    k-th best non-local score minus the relative tolerance."""
+    """Whether `chosen` (block ids, -1 padding ignored) is a correct selection
+    of one (query, group) up to the near-tie tolerance.
+
+    It must hold the local block beta_p, min(top_k, beta_p + 1) distinct ids,
+    none after beta_p, and no unchosen earlier block may score more than
+    tol = rel * max(|S_(k-1)|, |S_(k)|) above a chosen earlier block.  Away
+    from a near-tie only the exact top-(k-1) passes; on a near-tie the blocks
+    inside the tie band may be exchanged, and nothing else.
+    """
     chosen = [int(x) for x in chosen if x >= 0]
     if beta_p not in chosen or len(chosen) != min(top_k, beta_p + 1):
         return False
@@ -331,8 +349,9 @@ def valid_selection(S_g, beta_p, top_k, chosen, rel=1e-4):
         return False
     if beta_p <= top_k - 1:
         return True
-    v = np.sort(np.asarray(S_g[:beta_p], dtype=np.float64))[::-1]
-    kth = v[top_k - 2]
-    nxt = v[top_k - 1]
-    floor_ = nxt - rel * max(abs(kth), abs(nxt), 1e-30)
-    return all(S_g[c] >= floor_ for c in chosen if c != beta_p)
+    _, _, tol = _tie_tolerance(S_g, beta_p, top_k, rel)
+    mine = [c for c in chosen if c != beta_p]
+    rest = [u for u in range(beta_p) if u not in set(mine)]
+    if not mine or not rest:
+        return True
+    return max(float(S_g[u]) for u in rest) - min(float(S_g[c]) for c in mine) <= tol
