@@ -180,10 +180,16 @@ def _stream(stream):
     return ctypes.c_void_p(s.cuda_stream)
 
 
-def _workspace(dims, op, workspace, device):
+def _workspace(dims, op, workspace, device, stream=None):
+    """The caller's workspace, or a temporary one from torch's caching
+    allocator.  A temporary is tied to the launch stream (record_stream), so
+    the allocator does not hand it to other work before the library's
+    kernels on that stream are done with it."""
     need = workspace_size(dims, op)
     if workspace is None:
         workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=device)
+        if stream is not None:
+            workspace.record_stream(stream)
     return workspace
 
 
@@ -199,7 +205,7 @@ def index_select(dims, q_idx, k_idx, cu_seqlens_q, cu_seqlens_k, sel, sel_score=
     _shape(sel, (T, G, dims.top_k), "sel")
     if sel_score is not None:
         _shape(sel_score, (T, G, dims.top_k), "sel_score")
-    ws = _workspace(dims, OP_INDEX_SELECT, workspace, q_idx.device)
+    ws = _workspace(dims, OP_INDEX_SELECT, workspace, q_idx.device, stream)
     st = load_library().msa_index_select(
         ctypes.byref(dims), _ptr(q_idx, "q_idx", torch.bfloat16), _ptr(k_idx, "k_idx", torch.bfloat16),
         _ptr(cu_seqlens_q, "cu_seqlens_q", torch.int32), _ptr(cu_seqlens_k, "cu_seqlens_k", torch.int32),
@@ -219,7 +225,7 @@ def index_project(dims, x, w_q, w_k, cu_seqlens_q, cu_seqlens_k, q_idx, k_idx, w
     _shape(w_k, (DI, D), "w_k")
     _shape(q_idx, (T, G, DI), "q_idx")
     _shape(k_idx, (dims.total_k, DI), "k_idx")
-    ws = _workspace(dims, OP_INDEX_PROJECT, workspace, q_idx.device)
+    ws = _workspace(dims, OP_INDEX_PROJECT, workspace, q_idx.device, stream)
     st = load_library().msa_index_project(
         ctypes.byref(dims), D, _ptr(x, "x", torch.bfloat16), _ptr(w_q, "w_q", torch.bfloat16),
         _ptr(w_k, "w_k", torch.bfloat16), _ptr(cu_seqlens_q, "cu_seqlens_q", torch.int32),
@@ -329,7 +335,7 @@ def attend_fp8(dims, f8: Fp8Main, cu_seqlens_q, cu_seqlens_k, sel, block_offsets
     _shape(out, (T, Hq, D), "out")
     if lse is not None:
         _shape(lse, (T, Hq), "lse")
-    ws = _workspace(dims, OP_ATTEND, workspace, out.device)
+    ws = _workspace(dims, OP_ATTEND, workspace, out.device, stream)
     st = load_library().msa_attend_fp8(
         ctypes.byref(dims), _ptr(f8.q8, "q8", torch.uint8), _ptr(f8.q_exp, "q_exp", torch.uint8),
         _ptr(f8.k8, "k8", torch.uint8), _ptr(f8.k_exp, "k_exp", torch.uint8),
@@ -399,7 +405,7 @@ def attend_q8kv4(dims, m: Q8KV4Main, cu_seqlens_q, cu_seqlens_k, sel, block_offs
     _shape(out, (T, Hq, D), "out")
     if lse is not None:
         _shape(lse, (T, Hq), "lse")
-    ws = _workspace(dims, OP_ATTEND, workspace, out.device)
+    ws = _workspace(dims, OP_ATTEND, workspace, out.device, stream)
     st = load_library().msa_attend_q8kv4(
         ctypes.byref(dims), _ptr(m.q8, "q8", torch.uint8), _ptr(m.q_exp, "q_exp", torch.uint8),
         _ptr(m.k4, "k4", torch.uint8), _ptr(m.k_exp4, "k_exp4", torch.uint8),
@@ -463,7 +469,7 @@ def index_select_q8k4(dims, qk: Q8K4Index, cu_seqlens_q, cu_seqlens_k, sel, sel_
     _shape(sel, (T, G, dims.top_k), "sel")
     if sel_score is not None:
         _shape(sel_score, (T, G, dims.top_k), "sel_score")
-    ws = _workspace(dims, OP_INDEX_SELECT, workspace, sel.device)
+    ws = _workspace(dims, OP_INDEX_SELECT, workspace, sel.device, stream)
     st = load_library().msa_index_select_q8k4(
         ctypes.byref(dims), _ptr(qk.q_idx8, "q_idx8", torch.uint8), _ptr(qk.q_exp, "q_exp", torch.uint8),
         _ptr(qk.k_idx4, "k_idx4", torch.uint8), _ptr(qk.k_exp4, "k_exp4", torch.uint8),
@@ -485,7 +491,7 @@ def index_select_fp8(dims, fp8: Fp8Index, cu_seqlens_q, cu_seqlens_k, sel, sel_s
     _shape(sel, (T, G, dims.top_k), "sel")
     if sel_score is not None:
         _shape(sel_score, (T, G, dims.top_k), "sel_score")
-    ws = _workspace(dims, OP_INDEX_SELECT, workspace, sel.device)
+    ws = _workspace(dims, OP_INDEX_SELECT, workspace, sel.device, stream)
     st = load_library().msa_index_select_fp8(
         ctypes.byref(dims), _ptr(fp8.q_idx8, "q_idx8", torch.uint8), _ptr(fp8.q_exp, "q_exp", torch.uint8),
         _ptr(fp8.k_idx8, "k_idx8", torch.uint8), _ptr(fp8.k_exp, "k_exp", torch.uint8),
@@ -502,7 +508,7 @@ def build_block_query_lists(dims, sel, cu_seqlens_q, cu_seqlens_k, block_offsets
     _shape(block_offsets, (U + 1,), "block_offsets")
     if block_entries.numel() < dims.total_q * dims.num_kv_heads * dims.top_k:
         raise ValueError("block_entries too small")
-    ws = _workspace(dims, OP_BUILD_LISTS, workspace, sel.device)
+    ws = _workspace(dims, OP_BUILD_LISTS, workspace, sel.device, stream)
     st = load_library().msa_build_block_query_lists(
         ctypes.byref(dims), _ptr(sel, "sel", torch.int32),
         _ptr(cu_seqlens_q, "cu_seqlens_q", torch.int32), _ptr(cu_seqlens_k, "cu_seqlens_k", torch.int32),
@@ -521,7 +527,7 @@ def attend(dims, q, k, v, cu_seqlens_q, cu_seqlens_k, sel, block_offsets, block_
     _shape(out, (T, Hq, D), "out")
     if lse is not None:
         _shape(lse, (T, Hq), "lse")
-    ws = _workspace(dims, OP_ATTEND, workspace, q.device)
+    ws = _workspace(dims, OP_ATTEND, workspace, q.device, stream)
     st = load_library().msa_attend(
         ctypes.byref(dims), _ptr(q, "q", torch.bfloat16), _ptr(k, "k", torch.bfloat16),
         _ptr(v, "v", torch.bfloat16), _ptr(cu_seqlens_q, "cu_seqlens_q", torch.int32),
@@ -545,7 +551,7 @@ def attend_with_mass(dims, q, k, v, cu_seqlens_q, cu_seqlens_k, sel, block_offse
     _shape(block_mass, (T, G, dims.top_k), "block_mass")
     if lse is not None:
         _shape(lse, (T, Hq), "lse")
-    ws = _workspace(dims, OP_ATTEND, workspace, q.device)
+    ws = _workspace(dims, OP_ATTEND, workspace, q.device, stream)
     st = load_library().msa_attend_with_mass(
         ctypes.byref(dims), _ptr(q, "q", torch.bfloat16), _ptr(k, "k", torch.bfloat16),
         _ptr(v, "v", torch.bfloat16), _ptr(cu_seqlens_q, "cu_seqlens_q", torch.int32),

@@ -23,13 +23,14 @@ namespace msa {
 
 constexpr int kListTile = 128;   // query rows per counting tile
 
+// grid: x = (sequence, group), y = 128-query tile
 __global__ __launch_bounds__(256) void lists_count_kernel(
     const int32_t* __restrict__ sel, const int32_t* __restrict__ cu_q, int G, int top_k,
     int nqt_max, int nb_max, int32_t* __restrict__ cnt) {
   extern __shared__ int hist[];
-  const int t = blockIdx.x;
-  const int b = blockIdx.y / G;
-  const int g = blockIdx.y % G;
+  const int t = blockIdx.y;
+  const int b = blockIdx.x / G;
+  const int g = blockIdx.x % G;
   for (int i = threadIdx.x; i < nb_max; i += 256) hist[i] = 0;
   __syncthreads();
   const int qoff = cu_q[b], lq = cu_q[b + 1] - qoff;
@@ -145,7 +146,7 @@ __global__ __launch_bounds__(256) void scan_add_kernel(const int32_t* __restrict
   }
 }
 
-// one wave per (sequence, tile, group)
+// one wave per (sequence, tile, group); grid as lists_count_kernel
 __global__ __launch_bounds__(64) void lists_scatter_kernel(
     const int32_t* __restrict__ sel, const int32_t* __restrict__ cu_q,
     const int32_t* __restrict__ cu_k, int G, int top_k, int nqt_max, int nb_max,
@@ -154,9 +155,9 @@ __global__ __launch_bounds__(64) void lists_scatter_kernel(
   extern __shared__ int smem[];
   int* run = smem;                    // nb_max
   int* sl = smem + nb_max;            // kListTile * top_k
-  const int t = blockIdx.x;
-  const int b = blockIdx.y / G;
-  const int g = blockIdx.y % G;
+  const int t = blockIdx.y;
+  const int b = blockIdx.x / G;
+  const int g = blockIdx.x % G;
   const int lane = threadIdx.x;
   const int qoff = cu_q[b], lq = cu_q[b + 1] - qoff;
   const int lk = cu_k[b + 1] - cu_k[b];
@@ -211,8 +212,10 @@ hipError_t launch_build_lists(const int32_t* sel, const int32_t* cu_q, const int
   int32_t* part = (int32_t*)p;
   size_t nparts = (U + kScanItems - 1) / kScanItems;
 
-  // zero-size grids are skipped (no queries, or no blocks)
-  dim3 g1(nqt_max, batch * G);
+  // zero-size grids are skipped (no queries, or no blocks).  (sequence, group)
+  // pairs run along x, which holds any count the host accepts; query tiles
+  // along y (at most the per-sequence block limit of the LDS lists)
+  dim3 g1((unsigned)(batch * G), nqt_max);
   if (nqt_max > 0 && U > 0)
     hipLaunchKernelGGL(lists_count_kernel, g1, dim3(256), nb_max * sizeof(int), st, sel, cu_q, G,
                        top_k, nqt_max, nb_max, cnt);

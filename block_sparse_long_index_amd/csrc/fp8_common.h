@@ -74,12 +74,16 @@ __global__ __launch_bounds__(256) void quantize_q_kernel(const uint16_t* __restr
 }
 
 // Eight E4M3 codes (little-endian in two dwords) at exponent e -> their
-// eight values as bf16.  decode(code) * 2^e has at most 4 significant bits,
-// so the product and its bf16 rounding are exact (within bf16's range).  One
-// scaled conversion (v_cvt_scalef32_pk_bf16_fp8) turns the two codes of one
-// 16-bit half and the scale 2^e into two bf16 values, low byte first; over
-// every code that is not NaN (the quantisers never produce one), both byte
-// positions and exponents -127 .. 127 it gives exactly these values.
+// eight values as bf16.  decode(code) * 2^e has at most 4 significant bits
+// and its lowest set bit is at least 2^(e-9), so it is a bf16 number -- and
+// the conversion exact -- whenever e >= -124 (bf16's finest subnormal step is
+// 2^-133); for e in -127 .. -125 the smallest codes' values lie below that
+// step and are rounded to nearest even, like any value rounded to bf16 (an
+// absolute change below 2^-133).  One scaled conversion
+// (v_cvt_scalef32_pk_bf16_fp8) turns the two codes of one 16-bit half and the
+// scale 2^e into two bf16 values, low byte first; over every code that is not
+// NaN (the quantisers never produce one), both byte positions and exponents
+// -127 .. 127 it gives the round-to-nearest-even bf16 of the exact product.
 __device__ inline uint4 dequant8_bf16(uint2 w, int e) {
   typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
   const float s = ldexpf(1.f, e);
@@ -117,10 +121,10 @@ __device__ inline uint32_t e2m1_code(float y) {
 
 // Eight E2M1 codes (element i in nibble i of w, low nibble first) times the
 // group scale s = 2^e -> eight bf16 values.  A code's value has at most 2
-// significant bits, so the product and its bf16 rounding are exact within
-// bf16's range.  One scaled conversion (v_cvt_scalef32_pk_bf16_fp4) turns the
-// two codes of one byte into two bf16 values, low nibble first; over every
-// code, byte position and exponent -127 .. 127 it gives exactly these values.
+// significant bits and its lowest set bit is at least 2^(e-1), so the product
+// is a bf16 number for every e in -127 .. 127 and the conversion is exact.
+// One scaled conversion (v_cvt_scalef32_pk_bf16_fp4) turns the two codes of
+// one byte into two bf16 values, low nibble first.
 __device__ inline uint4 dequant4_bf16_scaled(uint32_t w, float s) {
   typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
   return make_uint4(__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, s, 0)),

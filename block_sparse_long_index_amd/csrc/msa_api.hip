@@ -94,6 +94,12 @@ msa_status_t check_dims(const msa_dims_t* d, Derived* out) {
   if (d->batch > kMaxBatch) return fail(MSA_ERR_UNSUPPORTED, "batch must be <= 65535 (sequences index a grid dimension)");
   if (d->num_q_heads < 1 || d->num_kv_heads < 1) return fail(MSA_ERR_BAD_DIMS, "head counts must be >= 1");
   if (d->num_q_heads % d->num_kv_heads) return fail(MSA_ERR_BAD_DIMS, "num_q_heads % num_kv_heads != 0");
+  // grid limits: some kernels put the KV head in a grid dimension of at most
+  // 65535; the list builder runs one 256-lane workgroup per (sequence, group)
+  // along x, whose lane count must stay below 2^32
+  if (d->num_kv_heads > kMaxBatch) return fail(MSA_ERR_UNSUPPORTED, "num_kv_heads must be <= 65535");
+  if ((long long)d->batch * d->num_kv_heads >= (1ll << 24))
+    return fail(MSA_ERR_UNSUPPORTED, "batch * num_kv_heads must be < 2^24");
   int hpg = d->num_q_heads / d->num_kv_heads;
   if (hpg > 32 || (hpg & (hpg - 1))) return fail(MSA_ERR_UNSUPPORTED, "heads per group must be a power of two <= 32");
   if (d->head_dim != 64 && d->head_dim != 128) return fail(MSA_ERR_UNSUPPORTED, "head_dim must be 64 or 128");

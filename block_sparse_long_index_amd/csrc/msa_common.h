@@ -45,9 +45,10 @@ struct KvMap {
   int pages;              // pages in the cache (paged only)
 
   // page of block beta of sequence b, clamped into the cache so that a
-  // malformed table cannot make a kernel address outside it
+  // malformed table cannot make a kernel address outside it; beta is clamped
+  // into the sequence's table row for the same reason
   __device__ inline size_t page(int b, int beta) const {
-    const int pg = table[(size_t)b * max_blocks + beta];
+    const int pg = table[(size_t)b * max_blocks + min(max(beta, 0), max_blocks - 1)];
     return (size_t)min(max(pg, 0), pages - 1);
   }
   // first row of block beta of sequence b (koff = cu_k[b])

@@ -35,10 +35,15 @@
  * - Errors: every argument is validated on the host before anything is
  *   launched; a call that returns an error has enqueued nothing.  A failed
  *   HIP launch returns MSA_ERR_HIP (msa_last_error() gives HIP's message).
- *   Device data that breaks the stated layout (e.g. a hand-written `sel`
- *   with out-of-range ids, or cu_seqlens not matching the dims) gives
- *   undefined results; kernels bound every address they derive from such
- *   data, so it cannot make them read or write outside the buffers.
+ *   Device data that breaks the stated layout gives undefined results.  For
+ *   the two kinds of device data a caller typically writes by hand -- block
+ *   ids in `sel` (out of range, repeated, or after the query's block) and
+ *   block_table entries -- the kernels bound every address they derive from
+ *   them, so such data cannot make a kernel read or write outside its
+ *   buffers.  cu_seqlens_q / cu_seqlens_k are trusted: they must be
+ *   non-decreasing, start at 0, end at total_q / total_k, and agree with
+ *   max_q_len / max_k_len and 0 <= Lq_b <= Lk_b; other values are undefined
+ *   behaviour (kernels may then access memory outside the buffers).
  */
 #ifndef MSA_H_
 #define MSA_H_

@@ -76,6 +76,11 @@ def test_1m_context_default_workspace_is_bounded():
     (dict(total_q=1 << 26, total_k=1 << 27, max_q_len=1, max_k_len=1), 3),
     (dict(total_k=1 << 22, max_k_len=1 << 22), 3),
     (dict(batch=65536, total_q=65536, total_k=1 << 20, max_q_len=1, max_k_len=16), 3),
+    # a KV head count beyond a grid dimension's 65535
+    (dict(num_q_heads=131072, num_kv_heads=65536), 3),
+    # (sequence, group) pairs beyond what the list builder's grid holds
+    (dict(batch=65535, num_q_heads=512, num_kv_heads=512, total_q=65535, total_k=1 << 20,
+          max_q_len=1, max_k_len=16), 3),
 ])
 def test_bad_dims_rejected(kw, status):
     d = _dims(**kw)

@@ -95,6 +95,40 @@ def test_decode_attend_more_rows_than_one_launch():
               "rows>65535")
 
 
+def test_lists_path_more_sequence_groups_than_a_grid_dimension():
+    """4100 sequences x 16 KV heads = 65600 (sequence, group) pairs on the
+    lists path (400 tokens each, so max_q_len > 8): the list builder runs one
+    workgroup per pair, more than a grid's y or z dimension holds.  The lists
+    must be the exact inverse of the selection, and sampled rows match the
+    oracle."""
+    n, L = 4100, 400
+    w = custom([L] * n, [L] * n, num_q_heads=16, num_kv_heads=16, head_dim=64, index_dim=32,
+               top_k=2, seed=37, qkv_std=1.0)
+    dev = torch.device("cuda:0")
+    t = generate(w, dev)
+    dims = msa.dims_for(w)
+    assert msa.attend_reads_lists(dims) and w.batch * w.num_kv_heads > 65535
+    bufs = msa.Buffers(dims, dev, want_scores=True)
+    msa.msa_forward(dims, t["q"], t["k"], t["v"], t["q_idx"], t["k_idx"], t["cu_seqlens_q"],
+                    t["cu_seqlens_k"], bufs)
+    torch.cuda.synchronize()
+    sel = bufs.sel.cpu().numpy()
+    P = problem_from(t, w, lazy=True)
+    off, ent = O.build_block_query_lists(sel, P.seq, w.batch, w.num_kv_heads, msa.nb_max(dims))
+    assert np.array_equal(bufs.offsets.cpu().numpy(), off)
+    assert np.array_equal(bufs.entries.cpu().numpy()[:len(ent)], ent)
+    rng = np.random.default_rng(37)
+    rows = sorted(set([0, 399, 400, w.total_q - 1] + [int(x) for x in rng.integers(0, w.total_q, 40)]
+                      + list(range(65535 // 16 * L, 65535 // 16 * L + 3))))
+    ref = P.run(rows, want_scores=True)
+    idx = torch.as_tensor(rows)
+    bad, ties = check_selection(P, rows, sel[rows], bufs.sel_score.cpu()[idx].numpy(), ref, w.index_dim)
+    log(f"[pairs>65535] selection mismatches {len(bad)} near-ties {ties}")
+    assert not bad, bad[:3]
+    check_out(bufs.out.cpu()[idx].float().numpy(), ref["out"], bufs.lse.cpu()[idx].numpy(), ref["lse"],
+              "pairs>65535")
+
+
 def test_multi_token_decode_path():
     # 4 new tokens x 8 groups = 32 rows: still the split-scan index path
     w = custom([9000, 4100], [4, 3], num_q_heads=32, num_kv_heads=8, head_dim=64, index_dim=32,
