@@ -22,6 +22,7 @@ __all__ = [
     "index_select_fp8", "Fp8Index", "index_project", "attend_with_mass", "index_kl",
     "attend_reads_lists", "Fp8Main", "main_quantize_fp8", "attend_fp8", "Q8K4Index",
     "index_quantize_q8k4", "index_select_q8k4", "Q8KV4Main", "main_quantize_q8kv4", "attend_q8kv4",
+    "attend_noalloc", "NOALLOC_SCRATCH_BYTES",
 ]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -30,6 +31,7 @@ HEADER_PATH = os.path.join(os.path.dirname(_PKG), "include", "msa.h")
 
 OP_INDEX_SELECT, OP_BUILD_LISTS, OP_ATTEND, OP_INDEX_PROJECT = 0, 1, 2, 3
 BLOCK = 128
+NOALLOC_SCRATCH_BYTES = 64 << 20   # MSA_NOALLOC_SCRATCH_BYTES
 
 
 class MSAError(RuntimeError):
@@ -99,6 +101,8 @@ def load_library(path: str = LIB_PATH):
     lib.msa_main_quantize_q8kv4.argtypes = [DP, P, P, P, P, P, P, P, P, P, P, P]
     lib.msa_attend_q8kv4.restype = I32
     lib.msa_attend_q8kv4.argtypes = [DP, P, P, P, P, P, P, P, P, P, P, P, P, P, P, SZ, P]
+    lib.msa_attend_noalloc.restype = I32
+    lib.msa_attend_noalloc.argtypes = [DP, P, P, P, P, P, P, P, P, P, P, P]
     lib.msa_attend_reads_lists.restype = I32
     lib.msa_attend_reads_lists.argtypes = [DP]
     lib.msa_profile_enable.restype = I32
@@ -536,6 +540,27 @@ def attend(dims, q, k, v, cu_seqlens_q, cu_seqlens_k, sel, block_offsets, block_
         _ptr(out, "out", torch.bfloat16), _ptr(lse, "lse", torch.float32), _ptr(ws, "workspace"),
         ctypes.c_size_t(ws.numel() * ws.element_size()), _stream(stream))
     _check(st, "msa_attend")
+    return out
+
+
+def attend_noalloc(dims, q, k, v, cu_seqlens_q, cu_seqlens_k, sel, block_offsets, block_entries, out,
+                   lse=None, stream=None):
+    """msa_attend_noalloc: msa_attend with its partials in the library's own
+    per-GPU scratch; no workspace is allocated or passed."""
+    T, Hq, D, G = dims.total_q, dims.num_q_heads, dims.head_dim, dims.num_kv_heads
+    _shape(q, (T, Hq, D), "q")
+    _shape(k, (dims.total_k, G, D), "k")
+    _shape(v, (dims.total_k, G, D), "v")
+    _shape(out, (T, Hq, D), "out")
+    if lse is not None:
+        _shape(lse, (T, Hq), "lse")
+    st = load_library().msa_attend_noalloc(
+        ctypes.byref(dims), _ptr(q, "q", torch.bfloat16), _ptr(k, "k", torch.bfloat16),
+        _ptr(v, "v", torch.bfloat16), _ptr(cu_seqlens_q, "cu_seqlens_q", torch.int32),
+        _ptr(cu_seqlens_k, "cu_seqlens_k", torch.int32), _ptr(sel, "sel", torch.int32),
+        _ptr(block_offsets, "block_offsets", torch.int32), _ptr(block_entries, "block_entries", torch.int32),
+        _ptr(out, "out", torch.bfloat16), _ptr(lse, "lse", torch.float32), _stream(stream))
+    _check(st, "msa_attend_noalloc")
     return out
 
 

@@ -263,6 +263,49 @@ msa_status_t hip_fail(hipError_t e) {
 
 }  // namespace
 
+// Scratch of msa_attend_noalloc (the Main Branch's partials), for callers that
+// cannot allocate.  Each GPU the library runs on holds its own copy for the
+// life of the process.  Host code never passes `scratch` itself to a kernel
+// (on the host it names a stand-in, not device memory): it uses the device
+// address resolved by scratch_address() for the device of the call's stream.
+static __device__ __align__(256) uint8_t scratch[MSA_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of `scratch` on the device `stream` belongs to (the current
+// device for the NULL stream), looked up once per device with that device
+// current and kept.
+msa_status_t scratch_address(hipStream_t stream, void** out) {
+  int cur = -1, dev = -1;
+  hipError_t e = hipGetDevice(&cur);
+  if (e != hipSuccess) return hip_fail(e);
+  dev = cur;
+  if (stream) {
+    e = hipStreamGetDevice(stream, &dev);
+    if (e != hipSuccess) return hip_fail(e);
+  }
+  if (dev < 0 || dev >= kMaxDevices) return fail(MSA_ERR_UNSUPPORTED, "device ordinal above 63");
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    if (dev != cur && (e = hipSetDevice(dev)) != hipSuccess) return hip_fail(e);
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    hipError_t e2 = dev != cur ? hipSetDevice(cur) : hipSuccess;
+    if (e != hipSuccess) return hip_fail(e);
+    if (e2 != hipSuccess) return hip_fail(e2);
+    if (!p || ((uintptr_t)p & 255u)) return fail(MSA_ERR_HIP, "scratch address missing or misaligned");
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return MSA_OK;
+}
+
+}  // namespace
+
 extern "C" {
 
 int32_t msa_abi_version(void) { return MSA_ABI_VERSION; }
@@ -583,6 +626,28 @@ msa_status_t msa_attend(const msa_dims_t* dims, const void* q, const void* k, co
   return attend_impl(dims, q, k, v, msa::MainFp8{nullptr, nullptr, nullptr}, cu_seqlens_q,
                      cu_seqlens_k, sel, block_offsets, block_entries, out, lse, nullptr, workspace,
                      workspace_bytes, stream);
+}
+
+msa_status_t msa_attend_noalloc(const msa_dims_t* dims, const void* q, const void* k,
+                                const void* v, const int32_t* cu_seqlens_q,
+                                const int32_t* cu_seqlens_k, const int32_t* sel,
+                                const int32_t* block_offsets, const int32_t* block_entries,
+                                void* out, float* lse, void* stream) {
+  Derived x;
+  msa_status_t s = check_dims(dims, &x);
+  if (s != MSA_OK) return s;
+  if (ws_attend(dims, x) > (size_t)MSA_NOALLOC_SCRATCH_BYTES)
+    return fail(MSA_ERR_WORKSPACE_TOO_SMALL,
+                "msa_attend_noalloc: the partials of one pass exceed the library's "
+                "MSA_NOALLOC_SCRATCH_BYTES scratch; set dims->q_chunk so that "
+                "msa_workspace_size(dims, MSA_OP_ATTEND) <= MSA_NOALLOC_SCRATCH_BYTES");
+  if (x.total_q == 0) return MSA_OK;
+  void* ws = nullptr;
+  s = scratch_address((hipStream_t)stream, &ws);
+  if (s != MSA_OK) return s;
+  return attend_impl(dims, q, k, v, msa::MainFp8{nullptr, nullptr, nullptr}, cu_seqlens_q,
+                     cu_seqlens_k, sel, block_offsets, block_entries, out, lse, nullptr, ws,
+                     (size_t)MSA_NOALLOC_SCRATCH_BYTES, stream);
 }
 
 msa_status_t msa_attend_fp8(const msa_dims_t* dims, const void* q8, const uint8_t* q_exp,

@@ -405,6 +405,33 @@ msa_status_t msa_attend_fp8(const msa_dims_t* dims, const void* q8, const uint8_
                             const int32_t* block_offsets, const int32_t* block_entries, void* out,
                             float* lse, void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * msa_attend without a workspace argument, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc).  It computes exactly what msa_attend computes, with
+ * the same kernels, and allocates nothing: the per-(query, head, block)
+ * partials live in a scratch array the library holds in device memory, one
+ * copy of MSA_NOALLOC_SCRATCH_BYTES per GPU for the life of the process,
+ * located on its first call on a device (the device of `stream`).
+ * - Sizes: the call needs msa_workspace_size(dims, MSA_OP_ATTEND) <=
+ *   MSA_NOALLOC_SCRATCH_BYTES, else it returns MSA_ERR_WORKSPACE_TOO_SMALL
+ *   and enqueues nothing; dims->q_chunk lowers that size (results do not
+ *   depend on it).  A decode step of 32 sequences with 64 query heads and
+ *   top_k 16 needs about 17 MiB.
+ * - Every call on one GPU shares that GPU's scratch, which keeps the last
+ *   call's contents; nothing in it needs to start at zero (every partial
+ *   the call reads, it has written).  Calls that overlap on one GPU (on
+ *   different streams, or from different host threads without ordering)
+ *   race on the scratch and give undefined results.
+ * Other arguments, errors and stream semantics as msa_attend.
+ */
+#define MSA_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+msa_status_t msa_attend_noalloc(const msa_dims_t* dims, const void* q, const void* k,
+                                const void* v, const int32_t* cu_seqlens_q,
+                                const int32_t* cu_seqlens_k, const int32_t* sel,
+                                const int32_t* block_offsets, const int32_t* block_entries,
+                                void* out, float* lse, void* stream);
+
 /* 1 if msa_attend / msa_attend_with_mass / msa_attend_fp8 read block_offsets and
  * block_entries for these dims, 0 if they work from sel alone (decode-shaped
  * steps), a negative msa_status_t for invalid dims. */
