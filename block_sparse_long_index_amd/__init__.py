@@ -22,7 +22,8 @@ __all__ = [
     "index_select_fp8", "Fp8Index", "index_project", "attend_with_mass", "index_kl",
     "attend_reads_lists", "Fp8Main", "main_quantize_fp8", "attend_fp8", "Q8K4Index",
     "index_quantize_q8k4", "index_select_q8k4", "Q8KV4Main", "main_quantize_q8kv4", "attend_q8kv4",
-    "attend_noalloc", "NOALLOC_SCRATCH_BYTES",
+    "attend_noalloc", "NOALLOC_SCRATCH_BYTES", "attend_pass_rows", "FLAG_COMPACT_PARTIALS",
+    "hbm_stream",
 ]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -31,6 +32,7 @@ HEADER_PATH = os.path.join(os.path.dirname(_PKG), "include", "msa.h")
 
 OP_INDEX_SELECT, OP_BUILD_LISTS, OP_ATTEND, OP_INDEX_PROJECT = 0, 1, 2, 3
 BLOCK = 128
+FLAG_COMPACT_PARTIALS = 1          # MSA_FLAG_COMPACT_PARTIALS
 NOALLOC_SCRATCH_BYTES = 64 << 20   # MSA_NOALLOC_SCRATCH_BYTES
 
 
@@ -50,7 +52,7 @@ class Dims(ctypes.Structure):
         ("max_q_len", ctypes.c_int32), ("max_k_len", ctypes.c_int32),
         ("q_chunk", ctypes.c_int32), ("kv_pages", ctypes.c_int32),
         ("block_table", ctypes.c_void_p), ("max_blocks_per_seq", ctypes.c_int32),
-        ("reserved", ctypes.c_int32),
+        ("flags", ctypes.c_int32),
     ]
 
 
@@ -103,6 +105,10 @@ def load_library(path: str = LIB_PATH):
     lib.msa_attend_q8kv4.argtypes = [DP, P, P, P, P, P, P, P, P, P, P, P, P, P, P, SZ, P]
     lib.msa_attend_noalloc.restype = I32
     lib.msa_attend_noalloc.argtypes = [DP, P, P, P, P, P, P, P, P, P, P, P]
+    lib.msa_hbm_stream.restype = I32
+    lib.msa_hbm_stream.argtypes = [P, SZ, I32, P, P, P]
+    lib.msa_attend_pass_rows.restype = ctypes.c_int64
+    lib.msa_attend_pass_rows.argtypes = [DP]
     lib.msa_attend_reads_lists.restype = I32
     lib.msa_attend_reads_lists.argtypes = [DP]
     lib.msa_profile_enable.restype = I32
@@ -135,10 +141,12 @@ def exported_symbols(header: str = HEADER_PATH) -> list:
 
 def make_dims(*, batch, num_q_heads, num_kv_heads, head_dim, index_dim, top_k, total_q, total_k,
               max_q_len, max_k_len, softmax_scale=0.0, q_chunk=0, block_size=BLOCK,
-              block_table=None) -> Dims:
+              block_table=None, flags=0) -> Dims:
     """Problem sizes.  ``block_table`` (device int32 [batch, max_blocks_per_seq]) selects a
     paged key cache: ``total_k`` is then the cache's row count, 128 per page.  The
-    returned dims keep a reference to the table (they hold its device address)."""
+    returned dims keep a reference to the table (they hold its device address).
+    ``flags``: 0 or FLAG_COMPACT_PARTIALS (the Main Branch's partials in 2 * head_dim + 8
+    bytes instead of 4 * head_dim + 8 on prefill-shaped steps)."""
     pages, table, mbs = 0, None, 0
     if block_table is not None:
         _ptr(block_table, "block_table", torch.int32)
@@ -147,7 +155,7 @@ def make_dims(*, batch, num_q_heads, num_kv_heads, head_dim, index_dim, top_k, t
         pages, table, mbs = int(total_k) // BLOCK, block_table.data_ptr(), int(block_table.shape[1])
     d = Dims(int(batch), int(num_q_heads), int(num_kv_heads), int(head_dim), int(index_dim),
              int(block_size), int(top_k), float(softmax_scale), int(total_q), int(total_k),
-             int(max_q_len), int(max_k_len), int(q_chunk), pages, table, mbs, 0)
+             int(max_q_len), int(max_k_len), int(q_chunk), pages, table, mbs, int(flags))
     # the struct holds the table's device address: keep the tensor alive with it
     d._block_table = block_table
     return d
@@ -629,6 +637,14 @@ class Buffers:
         self.workspace = torch.empty((need,), dtype=torch.uint8, device=dev)
 
 
+def attend_pass_rows(dims: Dims) -> int:
+    """Query rows per internal pass of msa_attend for these dims."""
+    n = int(load_library().msa_attend_pass_rows(ctypes.byref(dims)))
+    if n < 0:
+        _check(-n, "msa_attend_pass_rows")
+    return n
+
+
 def attend_reads_lists(dims: Dims) -> bool:
     """Whether attend reads the per-block query lists for these dims (False for
     decode-shaped steps, which attend per (query, slot) from the selection)."""
@@ -686,6 +702,19 @@ def msa_forward(dims: Dims, q, k, v, q_idx, k_idx, cu_seqlens_q, cu_seqlens_k, b
     return bufs
 
 
+def hbm_stream(src, ratio, dst, sink, stream=None):
+    """Measuring aid (msa_hbm_stream): stream all of `src` (uint8, a multiple of 16
+    bytes) and write ratio * its size into `dst`; `sink`: >= 8 KiB scratch."""
+    nbytes = src.numel() * src.element_size()
+    if ratio > 0 and dst.numel() * dst.element_size() < ratio * nbytes:
+        raise ValueError("dst too small")
+    if sink.numel() * sink.element_size() < 4 * 2048:
+        raise ValueError("sink too small")
+    _check(load_library().msa_hbm_stream(_ptr(src, "src"), ctypes.c_size_t(nbytes), int(ratio),
+                                         _ptr(dst, "dst") if ratio > 0 else None, _ptr(sink, "sink"),
+                                         _stream(stream)), "msa_hbm_stream")
+
+
 PROFILE_KERNELS = 17
 
 
@@ -705,11 +734,11 @@ def profile_collect() -> dict:
             for i in range(PROFILE_KERNELS)}
 
 
-def dims_for(workload_like, q_chunk=0, softmax_scale=0.0) -> Dims:
+def dims_for(workload_like, q_chunk=0, softmax_scale=0.0, flags=0) -> Dims:
     """Dims of a problem described by per-sequence lengths and head sizes."""
     w = workload_like
     return make_dims(batch=len(w.seq_k_lens), num_q_heads=w.num_q_heads,
                      num_kv_heads=w.num_kv_heads, head_dim=w.head_dim, index_dim=w.index_dim,
                      top_k=w.top_k, total_q=sum(w.seq_q_lens), total_k=sum(w.seq_k_lens),
                      max_q_len=max(w.seq_q_lens), max_k_len=max(w.seq_k_lens),
-                     softmax_scale=softmax_scale, q_chunk=q_chunk)
+                     softmax_scale=softmax_scale, q_chunk=q_chunk, flags=flags)

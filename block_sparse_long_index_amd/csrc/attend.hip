@@ -32,6 +32,13 @@
 // partials -- M = max m_s, L = sum l_s 2^(m_s - M),
 // out = sum O_s 2^(m_s - M) / L -- which equals one softmax over the union of
 // the selected keys; lse = (M + log2 L) * ln 2.
+//
+// Compact partials (an option of the lists path; fp32 is the default): the
+// same partial as (w, E, o) with w = m + log2 l (the block's log-sum-exp in
+// log2 units), E the exponent with max_d |O_d| / l in [2^(E-1), 2^E), and
+// o = O / l * 2^-E in fp16 (|o| < 1, 11 significant bits): 2 * D + 8 bytes
+// per row instead of 4 * D + 8.  The merge is then M = max w_s,
+// L = sum 2^(w_s - M), out = 2^Emax * sum o_s 2^(w_s - M + E_s - Emax) / L.
 #include "fp8_common.h"
 #include "msa_common.h"
 
@@ -109,14 +116,14 @@ __device__ inline int wave_lower_bound(const int32_t* __restrict__ a, int lo, in
 // One (block, sequence, group) item: stage its K/V block, then attend every
 // gathered query of this pass.  Called by the whole workgroup; every exit is
 // workgroup-uniform.
-template <int D, int HPG, bool Q8, bool KV4>
+template <int D, int HPG, bool Q8, bool KV4, bool COMPACT>
 __device__ __forceinline__ void attend_item(
     long long item, const void* __restrict__ q, const void* __restrict__ k,
     const void* __restrict__ v, const uint8_t* __restrict__ qe, const uint8_t* __restrict__ ke,
     const uint8_t* __restrict__ ve, const int32_t* __restrict__ cu_q,
     const int32_t* __restrict__ cu_k, KvMap kv, int batch, int G, int Hq, int top_k, int nb_max,
     const int32_t* __restrict__ offsets, const int32_t* __restrict__ entries, int r0, int r1,
-    int total_q, float scale_log2, float* __restrict__ part_acc, float2* __restrict__ part_ml,
+    int total_q, float scale_log2, void* __restrict__ part_acc, float2* __restrict__ part_ml,
     int spare_row, uint16_t* Ks, uint16_t* Vt, int* range) {
   constexpr int QPT = 32 / HPG;   // queries per 32-row tile
   constexpr int KS = D / 16;      // k-steps of Q.K over the head dim
@@ -328,13 +335,37 @@ __device__ __forceinline__ void attend_item(
       }
     }
 
-    // write the partial (m, l, O) of the lane's row: 16-byte stores of 4 consecutive d
+    // write the partial (m, l, O) of the lane's row: stores of 4 consecutive d
     // (padding lanes write the spare row; stores are unconditional for the
     // same exact-counting reason as the loads; both lane halves hold the
     // row's m and l and write the same value)
-    {
+    if constexpr (COMPACT) {
+      // the row's largest |O_d| (this lane holds half of the row's d, its
+      // partner lane ^ 32 the other half), then (w, E) and fp16 O / l * 2^-E
+      float a = 0.f;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) a = fmaxf(a, fabsf(oacc[dt][i]));
+      a = fmaxf(a, shfl_xor_f(a, 32));
+      const float inv_l = l > 0.f ? 1.f / l : 0.f;
+      int E = 0;
+      (void)frexpf(a * inv_l, &E);
+      part_ml[drow] = make_float2(m + log2f(l), (float)E);
+      // O / l first (no larger than the largest |v|), then the exact power-of-two
+      // scaling into (-1, 1]: no intermediate overflows whatever E is
+      auto sc = [&](float x) __attribute__((always_inline)) { return ldexpf(x * inv_l, -E); };
+      uint16_t* dst = static_cast<uint16_t*>(part_acc) + (size_t)drow * D + 4 * half;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          *reinterpret_cast<uint2*>(dst + dt * 32 + 8 * j) =
+              make_uint2(pack2_f16(sc(oacc[dt][4 * j]), sc(oacc[dt][4 * j + 1])),
+                         pack2_f16(sc(oacc[dt][4 * j + 2]), sc(oacc[dt][4 * j + 3])));
+    } else {
       part_ml[drow] = make_float2(m, l);
-      float* dst = part_acc + (size_t)drow * D + 4 * half;
+      float* dst = static_cast<float*>(part_acc) + (size_t)drow * D + 4 * half;
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
@@ -365,14 +396,14 @@ __device__ __forceinline__ void attend_item(
 // items_per_wg == 1: one item per workgroup.  items_per_wg in 2..64 (sparse
 // selections, e.g. decode): the workgroup finds which of its items have any
 // query with one coalesced load and processes only those.
-template <int D, int HPG, bool Q8, bool KV4>
+template <int D, int HPG, bool Q8, bool KV4, bool COMPACT>
 __global__ __launch_bounds__(256, 2) void attend_blocks_kernel(
     const void* __restrict__ q, const void* __restrict__ k, const void* __restrict__ v,
     const uint8_t* __restrict__ qe, const uint8_t* __restrict__ ke, const uint8_t* __restrict__ ve,
     const int32_t* __restrict__ cu_q, const int32_t* __restrict__ cu_k, KvMap kv, int batch, int G,
     int Hq, int top_k, int nb_max, const int32_t* __restrict__ offsets,
     const int32_t* __restrict__ entries, int r0, int r1, int total_q, float scale_log2,
-    float* __restrict__ part_acc, float2* __restrict__ part_ml, int spare_row, int items_per_wg) {
+    void* __restrict__ part_acc, float2* __restrict__ part_ml, int spare_row, int items_per_wg) {
   constexpr int LDK = D + 8;
   constexpr int LDV = kBlock + 4;
   __shared__ __attribute__((aligned(16))) uint16_t Ks[kBlock * LDK];
@@ -383,7 +414,7 @@ __global__ __launch_bounds__(256, 2) void attend_blocks_kernel(
   const long long n_items = (long long)nb_max * BG;
   const long long first = (long long)blockIdx.x * items_per_wg;
   if (items_per_wg == 1) {
-    attend_item<D, HPG, Q8, KV4>(first, q, k, v, qe, ke, ve, cu_q, cu_k, kv, batch, G, Hq, top_k, nb_max, offsets,
+    attend_item<D, HPG, Q8, KV4, COMPACT>(first, q, k, v, qe, ke, ve, cu_q, cu_k, kv, batch, G, Hq, top_k, nb_max, offsets,
                         entries, r0, r1, total_q, scale_log2, part_acc, part_ml, spare_row, Ks, Vt,
                         range);
     return;
@@ -404,7 +435,7 @@ __global__ __launch_bounds__(256, 2) void attend_blocks_kernel(
   while (m) {
     const int i = __ffsll((long long)m) - 1;
     m &= m - 1;
-    attend_item<D, HPG, Q8, KV4>(first + i, q, k, v, qe, ke, ve, cu_q, cu_k, kv, batch, G, Hq, top_k, nb_max, offsets,
+    attend_item<D, HPG, Q8, KV4, COMPACT>(first + i, q, k, v, qe, ke, ve, cu_q, cu_k, kv, batch, G, Hq, top_k, nb_max, offsets,
                         entries, r0, r1, total_q, scale_log2, part_acc, part_ml, spare_row, Ks, Vt,
                         range);
     __syncthreads();   // LDS and range are reused by the next item
@@ -415,9 +446,9 @@ __global__ __launch_bounds__(256, 2) void attend_blocks_kernel(
 // up front.  Eight waves per workgroup take eight consecutive heads, so a
 // workgroup reads whole (row, group) partial runs contiguously.
 constexpr int kMergeWaves = 8;
-template <int D, int KMAX>
+template <int D, int KMAX, bool COMPACT>
 __global__ __launch_bounds__(kMergeWaves * 64) void merge_partials_kernel(
-    const float* __restrict__ part_acc, const float2* __restrict__ part_ml,
+    const void* __restrict__ part_acc, const float2* __restrict__ part_ml,
     const int32_t* __restrict__ sel, int r0, int r1, int Hq, int G, int top_k,
     uint16_t* __restrict__ out, float* __restrict__ lse) {
   constexpr int PER = D / 64;
@@ -446,15 +477,59 @@ __global__ __launch_bounds__(kMergeWaves * 64) void merge_partials_kernel(
     for (int j = 0; j < PER; ++j) a[s][j] = 0.f;
     if (s < ns) {
       ml[s] = part_ml[base + (size_t)s * hpg];
-      const float* src = part_acc + (base + (size_t)s * hpg) * D + lane * PER;
-      if constexpr (PER == 2) {
-        float2 x = *reinterpret_cast<const float2*>(src);
-        a[s][0] = x.x;
-        a[s][1] = x.y;
+      if constexpr (COMPACT) {
+        const uint16_t* src = static_cast<const uint16_t*>(part_acc) + (base + (size_t)s * hpg) * D + lane * PER;
+        if constexpr (PER == 2) {
+          const float2 x = unpack2_f16(*reinterpret_cast<const uint32_t*>(src));
+          a[s][0] = x.x;
+          a[s][1] = x.y;
+        } else {
+          a[s][0] = f16_bits_to_f32(src[0]);
+        }
       } else {
-        a[s][0] = src[0];
+        const float* src = static_cast<const float*>(part_acc) + (base + (size_t)s * hpg) * D + lane * PER;
+        if constexpr (PER == 2) {
+          float2 x = *reinterpret_cast<const float2*>(src);
+          a[s][0] = x.x;
+          a[s][1] = x.y;
+        } else {
+          a[s][0] = src[0];
+        }
       }
     }
+  }
+  if constexpr (COMPACT) {
+    // ml[s] = (w_s, E_s): weights 2^(w_s - M), values o_s 2^E_s
+    float M = -INFINITY, Em = -INFINITY;
+#pragma unroll
+    for (int s = 0; s < KMAX; ++s)
+      if (s < ns) {
+        M = fmaxf(M, ml[s].x);
+        Em = fmaxf(Em, ml[s].y);
+      }
+    float L = 0.f;
+    float acc[PER];
+#pragma unroll
+    for (int j = 0; j < PER; ++j) acc[j] = 0.f;
+#pragma unroll
+    for (int s = 0; s < KMAX; ++s) {
+      if (s < ns) {
+        L += exp2f(ml[s].x - M);
+        const float wgt = exp2f(ml[s].x - M + (ml[s].y - Em));
+#pragma unroll
+        for (int j = 0; j < PER; ++j) acc[j] += wgt * a[s][j];
+      }
+    }
+    const float inv = 1.f / L;
+    const int e = (int)Em;
+    uint16_t* o = out + ((size_t)r * Hq + h) * D + lane * PER;
+    if constexpr (PER == 2) {
+      *reinterpret_cast<uint32_t*>(o) = pack2_bf16(ldexpf(acc[0] * inv, e), ldexpf(acc[1] * inv, e));
+    } else {
+      o[0] = __builtin_bit_cast(uint16_t, (__bf16)ldexpf(acc[0] * inv, e));
+    }
+    if (lse && lane == 0) lse[(size_t)r * Hq + h] = (M + log2f(L)) * 0.69314718055994530942f;
+    return;
   }
   float M = -INFINITY;
 #pragma unroll
@@ -483,13 +558,13 @@ __global__ __launch_bounds__(kMergeWaves * 64) void merge_partials_kernel(
 }
 
 // ---------------------------------------------------------------------------
-template <int D, int HPG>
+template <int D, int HPG, bool COMPACT>
 static void launch_attend_t(const void* q, const void* k, const void* v, MainFp8 f8,
                             const int32_t* cu_q,
                             const int32_t* cu_k, KvMap kv, int batch, int G, int Hq, int top_k,
                             int nb_max,
                             const int32_t* offsets, const int32_t* entries, int r0, int r1,
-                            int total_q, float scale_log2, float* part_acc, float2* part_ml,
+                            int total_q, float scale_log2, void* part_acc, float2* part_ml,
                             hipStream_t st) {
   // sparse selections (few queries per item on average): scan items in runs of 64
   const long long n_items = (long long)nb_max * batch * G;
@@ -497,30 +572,30 @@ static void launch_attend_t(const void* q, const void* k, const void* v, MainFp8
   const int ipw = per_item >= 4.0 ? 1 : 64;
   dim3 grid((unsigned)((n_items + ipw - 1) / ipw));
   if (f8.qe && f8.kv4)
-    hipLaunchKernelGGL((attend_blocks_kernel<D, HPG, true, true>), grid, dim3(256), 0, st, q, k, v,
+    hipLaunchKernelGGL((attend_blocks_kernel<D, HPG, true, true, COMPACT>), grid, dim3(256), 0, st, q, k, v,
                        f8.qe, f8.ke, f8.ve, cu_q, cu_k, kv, batch, G, Hq, top_k, nb_max, offsets,
                        entries, r0, r1, total_q, scale_log2, part_acc, part_ml,
                        (r1 - r0) * Hq * top_k, ipw);
   else if (f8.qe)
-    hipLaunchKernelGGL((attend_blocks_kernel<D, HPG, true, false>), grid, dim3(256), 0, st, q, k, v, f8.qe,
+    hipLaunchKernelGGL((attend_blocks_kernel<D, HPG, true, false, COMPACT>), grid, dim3(256), 0, st, q, k, v, f8.qe,
                        f8.ke, f8.ve, cu_q, cu_k, kv, batch, G, Hq, top_k, nb_max, offsets, entries,
                        r0, r1, total_q, scale_log2, part_acc, part_ml, (r1 - r0) * Hq * top_k, ipw);
   else
-    hipLaunchKernelGGL((attend_blocks_kernel<D, HPG, false, false>), grid, dim3(256), 0, st, q, k, v,
+    hipLaunchKernelGGL((attend_blocks_kernel<D, HPG, false, false, COMPACT>), grid, dim3(256), 0, st, q, k, v,
                        (const uint8_t*)nullptr, (const uint8_t*)nullptr, (const uint8_t*)nullptr,
                        cu_q, cu_k, kv, batch, G, Hq, top_k, nb_max, offsets, entries, r0, r1,
                        total_q, scale_log2, part_acc, part_ml, (r1 - r0) * Hq * top_k, ipw);
 }
 
-template <int D>
+template <int D, bool COMPACT>
 static hipError_t launch_attend_d(int hpg, const void* q, const void* k, const void* v, MainFp8 f8,
                                   const int32_t* cu_q, const int32_t* cu_k, KvMap kv, int batch,
                                   int G, int Hq,
                                   int top_k, int nb_max, const int32_t* offsets,
                                   const int32_t* entries, int r0, int r1, int total_q,
-                                  float scale_log2, float* part_acc, float2* part_ml,
+                                  float scale_log2, void* part_acc, float2* part_ml,
                                   hipStream_t st) {
-#define MSA_ATT(H) launch_attend_t<D, H>(q, k, v, f8, cu_q, cu_k, kv, batch, G, Hq, top_k, nb_max, offsets, entries, r0, r1, total_q, scale_log2, part_acc, part_ml, st)
+#define MSA_ATT(H) launch_attend_t<D, H, COMPACT>(q, k, v, f8, cu_q, cu_k, kv, batch, G, Hq, top_k, nb_max, offsets, entries, r0, r1, total_q, scale_log2, part_acc, part_ml, st)
   switch (hpg) {
     case 1: MSA_ATT(1); break;
     case 2: MSA_ATT(2); break;
@@ -534,33 +609,32 @@ static hipError_t launch_attend_d(int hpg, const void* q, const void* k, const v
   return hipGetLastError();
 }
 
-hipError_t launch_attend_blocks(int D, int hpg, const void* q, const void* k, const void* v,
-                                MainFp8 f8, const int32_t* cu_q, const int32_t* cu_k, KvMap kv, int batch,
-                                int G, int Hq, int top_k, int nb_max, const int32_t* offsets,
-                                const int32_t* entries, int r0, int r1, int total_q,
-                                float scale_log2, float* part_acc, float2* part_ml, hipStream_t st) {
-  if (D == 64)
-    return launch_attend_d<64>(hpg, q, k, v, f8, cu_q, cu_k, kv, batch, G, Hq, top_k, nb_max, offsets,
-                               entries, r0, r1, total_q, scale_log2, part_acc, part_ml, st);
-  if (D == 128)
-    return launch_attend_d<128>(hpg, q, k, v, f8, cu_q, cu_k, kv, batch, G, Hq, top_k, nb_max, offsets,
-                                entries, r0, r1, total_q, scale_log2, part_acc, part_ml, st);
+hipError_t launch_attend_blocks(int D, int hpg, bool compact, const void* q, const void* k,
+                                const void* v, MainFp8 f8, const int32_t* cu_q, const int32_t* cu_k,
+                                KvMap kv, int batch, int G, int Hq, int top_k, int nb_max,
+                                const int32_t* offsets, const int32_t* entries, int r0, int r1,
+                                int total_q, float scale_log2, void* part_acc, float2* part_ml,
+                                hipStream_t st) {
+#define MSA_ATD(DD, C) launch_attend_d<DD, C>(hpg, q, k, v, f8, cu_q, cu_k, kv, batch, G, Hq, top_k, nb_max, offsets, entries, r0, r1, total_q, scale_log2, part_acc, part_ml, st)
+  if (D == 64) return compact ? MSA_ATD(64, true) : MSA_ATD(64, false);
+  if (D == 128) return compact ? MSA_ATD(128, true) : MSA_ATD(128, false);
+#undef MSA_ATD
   return hipErrorInvalidValue;
 }
 
-template <int D, int KMAX>
-static void launch_merge_t(dim3 grid, const float* part_acc, const float2* part_ml, const int32_t* sel,
+template <int D, int KMAX, bool COMPACT>
+static void launch_merge_t(dim3 grid, const void* part_acc, const float2* part_ml, const int32_t* sel,
                            int r0, int r1, int Hq, int G, int top_k, void* out, float* lse,
                            hipStream_t st) {
-  hipLaunchKernelGGL((merge_partials_kernel<D, KMAX>), grid, dim3(kMergeWaves * 64), 0, st, part_acc, part_ml, sel,
-                     r0, r1, Hq, G, top_k, (uint16_t*)out, lse);
+  hipLaunchKernelGGL((merge_partials_kernel<D, KMAX, COMPACT>), grid, dim3(kMergeWaves * 64), 0, st,
+                     part_acc, part_ml, sel, r0, r1, Hq, G, top_k, (uint16_t*)out, lse);
 }
 
-template <int D>
-static void launch_merge_d(dim3 grid, const float* part_acc, const float2* part_ml, const int32_t* sel,
+template <int D, bool COMPACT>
+static void launch_merge_d(dim3 grid, const void* part_acc, const float2* part_ml, const int32_t* sel,
                            int r0, int r1, int Hq, int G, int top_k, void* out, float* lse,
                            hipStream_t st) {
-#define MSA_MRG(K) launch_merge_t<D, K>(grid, part_acc, part_ml, sel, r0, r1, Hq, G, top_k, out, lse, st)
+#define MSA_MRG(K) launch_merge_t<D, K, COMPACT>(grid, part_acc, part_ml, sel, r0, r1, Hq, G, top_k, out, lse, st)
   if (top_k <= 4) MSA_MRG(4);
   else if (top_k <= 8) MSA_MRG(8);
   else if (top_k <= 16) MSA_MRG(16);
@@ -568,17 +642,20 @@ static void launch_merge_d(dim3 grid, const float* part_acc, const float2* part_
 #undef MSA_MRG
 }
 
-hipError_t launch_merge(int D, const float* part_acc, const float2* part_ml, const int32_t* sel,
-                        int r0, int r1, int Hq, int G, int top_k, void* out, float* lse,
-                        hipStream_t st) {
+hipError_t launch_merge(int D, bool compact, const void* part_acc, const float2* part_ml,
+                        const int32_t* sel, int r0, int r1, int Hq, int G, int top_k, void* out,
+                        float* lse, hipStream_t st) {
   long long n = (long long)(r1 - r0) * Hq;
   dim3 grid((unsigned)((n + kMergeWaves - 1) / kMergeWaves));
-  if (D == 64)
-    launch_merge_d<64>(grid, part_acc, part_ml, sel, r0, r1, Hq, G, top_k, out, lse, st);
-  else if (D == 128)
-    launch_merge_d<128>(grid, part_acc, part_ml, sel, r0, r1, Hq, G, top_k, out, lse, st);
-  else
+#define MSA_MRD(DD, C) launch_merge_d<DD, C>(grid, part_acc, part_ml, sel, r0, r1, Hq, G, top_k, out, lse, st)
+  if (D == 64) {
+    if (compact) MSA_MRD(64, true); else MSA_MRD(64, false);
+  } else if (D == 128) {
+    if (compact) MSA_MRD(128, true); else MSA_MRD(128, false);
+  } else {
     return hipErrorInvalidValue;
+  }
+#undef MSA_MRD
   return hipGetLastError();
 }
 

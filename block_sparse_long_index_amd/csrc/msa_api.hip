@@ -25,9 +25,9 @@ size_t lists_workspace_bytes(int batch, int G, int nqt_max, int nb_max);
 int list_tile_rows();
 hipError_t launch_build_lists(const int32_t*, const int32_t*, const int32_t*, int, int, int, int,
                               int, int32_t*, int32_t*, void*, hipStream_t);
-hipError_t launch_attend_blocks(int, int, const void*, const void*, const void*, MainFp8,
+hipError_t launch_attend_blocks(int, int, bool, const void*, const void*, const void*, MainFp8,
                                 const int32_t*, const int32_t*, KvMap, int, int, int, int, int,
-                                const int32_t*, const int32_t*, int, int, int, float, float*, float2*,
+                                const int32_t*, const int32_t*, int, int, int, float, void*, float2*,
                                 hipStream_t);
 hipError_t launch_attend_decode(int, int, const void*, const void*, const void*, MainFp8,
                                 const int32_t*, const int32_t*, KvMap, int, int, int, int, int,
@@ -38,8 +38,8 @@ hipError_t launch_main_quantize_fp8(int, const void*, const void*, const void*, 
 hipError_t launch_main_quantize_q8kv4(int, const void*, const void*, const void*, const int32_t*,
                                       KvMap, int, int, int, long long, void*, uint8_t*, void*,
                                       uint8_t*, void*, uint8_t*, hipStream_t);
-hipError_t launch_merge(int, const float*, const float2*, const int32_t*, int, int, int, int, int,
-                        void*, float*, hipStream_t);
+hipError_t launch_merge(int, bool, const void*, const float2*, const int32_t*, int, int, int, int,
+                        int, void*, float*, hipStream_t);
 int fp8_max_blocks_per_sequence();
 hipError_t launch_block_mass(int, const float2*, const int32_t*, int, int, int, int, float*,
                              hipStream_t);
@@ -50,6 +50,7 @@ hipError_t launch_index_project(const void*, const void*, const void*, int, int,
                                 const int32_t*, const int32_t*, KvMap, int, void*, void*, void*,
                                 hipStream_t);
 size_t project_workspace_bytes(int, int);
+hipError_t launch_hbm_stream(const void*, long long, int, void*, void*, int, hipStream_t);
 hipError_t launch_quantize_index_fp8(int, const void*, const void*, const int32_t*, KvMap, int, int,
                                      long long, void*, uint8_t*, void*, uint8_t*, hipStream_t);
 hipError_t launch_index_select_prefill_fp8(const void*, const uint8_t*, const void*, const uint8_t*,
@@ -83,6 +84,7 @@ struct Derived {
   int G, Hq, D, DI, hpg, top_k;
   int nb_max, nqt_max;
   bool decode_path;
+  bool compact;     // compact Main-Branch partials (lists path only)
   float scale;
   long long total_q;
   msa::KvMap kv;   // where key rows live (contiguous or paged)
@@ -117,7 +119,7 @@ msa_status_t check_dims(const msa_dims_t* d, Derived* out) {
   if (d->max_q_len > d->total_q || d->max_k_len > d->total_k)
     return fail(MSA_ERR_BAD_DIMS, "max lengths exceed totals");
   if (d->q_chunk < 0) return fail(MSA_ERR_BAD_DIMS, "q_chunk must be >= 0");
-  if (d->reserved != 0) return fail(MSA_ERR_BAD_DIMS, "reserved must be 0");
+  if (d->flags & ~MSA_FLAG_COMPACT_PARTIALS) return fail(MSA_ERR_BAD_DIMS, "unknown bits in flags");
   if (d->kv_pages < 0) return fail(MSA_ERR_BAD_DIMS, "kv_pages must be >= 0");
   if (d->kv_pages > 0) {
     if (!d->block_table) return fail(MSA_ERR_NULL_ARG, "block_table is NULL (paged key cache)");
@@ -144,6 +146,7 @@ msa_status_t check_dims(const msa_dims_t* d, Derived* out) {
     return fail(MSA_ERR_UNSUPPORTED, "batch * num_kv_heads * blocks too large");
   // decode-shaped steps (a few new tokens per sequence): split-scan index kernels
   out->decode_path = (long long)d->max_q_len * out->G <= kDecodeRowsMax;
+  out->compact = (d->flags & MSA_FLAG_COMPACT_PARTIALS) && d->max_q_len > kDecodeAttendMaxQ;
   out->scale = d->softmax_scale > 0.f ? d->softmax_scale : 1.f / sqrtf((float)d->head_dim);
   out->total_q = d->total_q;
   out->kv.table = d->kv_pages > 0 ? d->block_table : nullptr;
@@ -171,8 +174,11 @@ long long select_chunk(const msa_dims_t* d, const Derived& x) {
   return round_chunk(rows, x.total_q, d->q_chunk > 0);
 }
 
+// bytes of one partial row's acc values: fp32, or fp16 when compact
+long long acc_bytes(const Derived& x) { return (long long)x.D * (x.compact ? 2 : 4); }
+
 long long attend_chunk(const msa_dims_t* d, const Derived& x) {
-  long long per_row = (long long)x.Hq * x.top_k * ((long long)x.D * 4 + 8);
+  long long per_row = (long long)x.Hq * x.top_k * (acc_bytes(x) + 8);
   long long rows = d->q_chunk > 0 ? d->q_chunk : (long long)(kDefaultChunkBytes / per_row);
   // partial rows are indexed with int32
   long long cap = (((long long)1 << 31) - 1) / ((long long)x.Hq * x.top_k);
@@ -196,7 +202,7 @@ size_t attend_rows(const msa_dims_t* d, const Derived& x) {
 }
 size_t ws_attend(const msa_dims_t* d, const Derived& x) {
   size_t rows = attend_rows(d, x);
-  return align256(rows * x.D * 4) + align256(rows * 8) + 256;
+  return align256(rows * acc_bytes(x)) + align256(rows * 8) + 256;
 }
 
 size_t ws_project(const Derived& x) {
@@ -559,6 +565,13 @@ int32_t msa_attend_reads_lists(const msa_dims_t* dims) {
   return reads_lists(dims) ? 1 : 0;
 }
 
+int64_t msa_attend_pass_rows(const msa_dims_t* dims) {
+  Derived x;
+  msa_status_t s = check_dims(dims, &x);
+  if (s != MSA_OK) return -(int64_t)s;
+  return attend_chunk(dims, x);
+}
+
 static msa_status_t attend_impl(const msa_dims_t* dims, const void* q, const void* k,
                                 const void* v, msa::MainFp8 f8, const int32_t* cu_seqlens_q,
                                 const int32_t* cu_seqlens_k, const int32_t* sel,
@@ -583,8 +596,8 @@ static msa_status_t attend_impl(const msa_dims_t* dims, const void* q, const voi
   hipStream_t st = (hipStream_t)stream;
   const long long chunk = attend_chunk(dims, x);
   char* base = (char*)(((uintptr_t)workspace + 255) & ~(uintptr_t)255);
-  float* part_acc = (float*)base;
-  float2* part_ml = (float2*)(base + align256(attend_rows(dims, x) * x.D * 4));
+  void* part_acc = base;
+  float2* part_ml = (float2*)(base + align256(attend_rows(dims, x) * acc_bytes(x)));
   const float scale_log2 = x.scale * 1.44269504088896340736f;
   for (long long r0 = 0; r0 < x.total_q; r0 += chunk) {
     const int a = (int)r0, z = (int)std::min<long long>(x.total_q, r0 + chunk);
@@ -596,9 +609,9 @@ static msa_status_t attend_impl(const msa_dims_t* dims, const void* q, const voi
         // one workgroup per (group, slot, query) reads it straight from the selection
         e = msa::launch_attend_decode(x.D, x.hpg, q, k, v, f8, cu_seqlens_q, cu_seqlens_k, x.kv,
                                       dims->batch, x.G, x.Hq, x.top_k, x.nb_max, sel, a, z,
-                                      scale_log2, part_acc, part_ml, st);
+                                      scale_log2, (float*)part_acc, part_ml, st);
       else
-        e = msa::launch_attend_blocks(x.D, x.hpg, q, k, v, f8, cu_seqlens_q, cu_seqlens_k, x.kv,
+        e = msa::launch_attend_blocks(x.D, x.hpg, x.compact, q, k, v, f8, cu_seqlens_q, cu_seqlens_k, x.kv,
                                       dims->batch, x.G, x.Hq, x.top_k, x.nb_max, block_offsets,
                                       block_entries, a, z, (int)x.total_q, scale_log2, part_acc,
                                       part_ml, st);
@@ -606,7 +619,8 @@ static msa_status_t attend_impl(const msa_dims_t* dims, const void* q, const voi
     if (e != hipSuccess) return hip_fail(e);
     {
       ProfScope ps(K_MERGE, st);
-      e = msa::launch_merge(x.D, part_acc, part_ml, sel, a, z, x.Hq, x.G, x.top_k, out, lse, st);
+      e = msa::launch_merge(x.D, x.compact, part_acc, part_ml, sel, a, z, x.Hq, x.G, x.top_k, out,
+                            lse, st);
     }
     if (e != hipSuccess) return hip_fail(e);
     if (block_mass) {
@@ -734,6 +748,8 @@ msa_status_t msa_attend_with_mass(const msa_dims_t* dims, const void* q, const v
                                   const int32_t* block_offsets, const int32_t* block_entries,
                                   void* out, float* lse, float* block_mass, void* workspace,
                                   size_t workspace_bytes, void* stream) {
+  if (dims && (dims->flags & MSA_FLAG_COMPACT_PARTIALS))
+    return fail(MSA_ERR_UNSUPPORTED, "block masses need fp32 partials (MSA_FLAG_COMPACT_PARTIALS)");
   if (dims && dims->total_q > 0 && !block_mass)
     return fail(MSA_ERR_NULL_ARG, "block_mass is NULL");
   if (block_mass && !aligned16(block_mass))
@@ -761,6 +777,20 @@ msa_status_t msa_index_kl(const msa_dims_t* dims, const void* q_idx, const void*
   hipError_t e = msa::launch_index_kl(x.DI, q_idx, k_idx, cu_seqlens_q, cu_seqlens_k, x.kv, dims->batch,
                                       x.G, x.top_k, dims->max_q_len, sel, sel_score, block_mass,
                                       log_q, kl, st);
+  return e == hipSuccess ? MSA_OK : hip_fail(e);
+}
+
+msa_status_t msa_hbm_stream(const void* src, size_t read_bytes, int32_t ratio, void* dst,
+                            void* sink, void* stream) {
+  if (!src || !sink || (ratio > 0 && !dst)) return fail(MSA_ERR_NULL_ARG, "a required pointer is NULL");
+  if (ratio < 0 || ratio > 4) return fail(MSA_ERR_BAD_DIMS, "ratio must be in 0..4");
+  if (read_bytes == 0 || read_bytes % 16) return fail(MSA_ERR_BAD_DIMS, "read_bytes must be a positive multiple of 16");
+  if (!aligned16(src) || !aligned16(sink) || (ratio > 0 && !aligned16(dst)))
+    return fail(MSA_ERR_ALIGNMENT, "tensor pointers must be 16-byte aligned");
+  const long long units = (long long)(read_bytes / 16);
+  const long long wgs = (units + 255) / 256;
+  const int grid = (int)std::min<long long>(wgs, MSA_HBM_STREAM_MAX_WORKGROUPS);
+  hipError_t e = msa::launch_hbm_stream(src, units, ratio, dst, sink, grid, (hipStream_t)stream);
   return e == hipSuccess ? MSA_OK : hip_fail(e);
 }
 

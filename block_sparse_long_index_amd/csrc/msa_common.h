@@ -117,6 +117,18 @@ __device__ inline uint32_t pack2_bf16(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, v);
 }
 
+// Pack two floats as two fp16 (round to nearest even) in one dword: lo in bits 0..15.
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+__device__ inline uint32_t pack2_f16(float lo, float hi) {
+  f16x2_t v = {(_Float16)lo, (_Float16)hi};
+  return __builtin_bit_cast(uint32_t, v);
+}
+__device__ inline float2 unpack2_f16(uint32_t w) {
+  const f16x2_t v = __builtin_bit_cast(f16x2_t, w);
+  return make_float2((float)v[0], (float)v[1]);
+}
+__device__ inline float f16_bits_to_f32(uint16_t h) { return (float)__builtin_bit_cast(_Float16, h); }
+
 // Order-preserving map of fp32 to uint32 (larger float -> larger key).
 __device__ inline uint32_t float_order_key(float f) {
   uint32_t u = __float_as_uint(f);

@@ -55,7 +55,7 @@
 extern "C" {
 #endif
 
-#define MSA_ABI_VERSION 2
+#define MSA_ABI_VERSION 3
 #define MSA_BLOCK_SIZE 128  /* B_k, MSA guide table in section "ブロック単位選択の数値設計" */
 #define MSA_MAX_TOP_K 32
 
@@ -97,8 +97,27 @@ typedef struct msa_dims {
   const int32_t* block_table;   /* paged only: device int32 [batch, max_blocks_per_seq]; block
                                    beta of sequence b is page block_table[b][beta] */
   int32_t max_blocks_per_seq;   /* paged only: row stride of block_table, >= ceil(max_k_len/128) */
-  int32_t reserved;       /* must be 0 */
+  int32_t flags;          /* 0, or MSA_FLAG_COMPACT_PARTIALS; other bits must be 0 */
 } msa_dims_t;
+
+/*
+ * MSA_FLAG_COMPACT_PARTIALS: the Main Branch's per-(query, head, block)
+ * softmax partials, which it writes and merges inside msa_attend (and
+ * msa_attend_fp8 / _q8kv4 / _noalloc), are kept as 2 * head_dim + 8 bytes
+ * instead of 4 * head_dim + 8: the block's log-sum-exp w = m + log2 l and a
+ * power-of-two exponent E in fp32, and O / l * 2^-E in fp16 (magnitudes below
+ * 1, 11 significant bits; E is chosen per row from its largest |O|).  This
+ * roughly halves the Main Branch's memory traffic on prefill-shaped steps.
+ * Each stored value is off by at most 2^-11 of its row's largest |O / l|
+ * (fp16 rounding), so the merged output moves by at most 2^-11 of the
+ * largest |v| the query attends to, on the order of the bf16 rounding of the
+ * output itself.  It applies where msa_attend_reads_lists()
+ * is 1 (decode-shaped steps keep fp32 partials, a small part of their
+ * bytes), lowers msa_workspace_size(MSA_OP_ATTEND) accordingly, and is not
+ * supported by msa_attend_with_mass (MSA_ERR_UNSUPPORTED), whose block
+ * masses read the fp32 (m, l).  Without the flag the partials are fp32.
+ */
+#define MSA_FLAG_COMPACT_PARTIALS 1
 
 /*
  * Paged key cache (kv_pages > 0).  A page holds one 128-token KV block, the
@@ -432,6 +451,13 @@ msa_status_t msa_attend_noalloc(const msa_dims_t* dims, const void* q, const voi
                                 const int32_t* block_offsets, const int32_t* block_entries,
                                 void* out, float* lse, void* stream);
 
+/* Query rows that msa_attend and its variants process per internal pass for
+ * these dims (dims->q_chunk when set, else the library's choice, which keeps
+ * the workspace under 48 GiB): a call makes ceil(total_q / rows) passes, and
+ * a KV block whose query list spans several passes is staged once per pass.
+ * A negative msa_status_t for invalid dims. */
+int64_t msa_attend_pass_rows(const msa_dims_t* dims);
+
 /* 1 if msa_attend / msa_attend_with_mass / msa_attend_fp8 read block_offsets and
  * block_entries for these dims, 0 if they work from sel alone (decode-shaped
  * steps), a negative msa_status_t for invalid dims. */
@@ -501,6 +527,21 @@ int32_t msa_abi_version(void);
  * and forgets the records.  Events are host-side HIP objects kept in a pool
  * for the life of the process; no device memory is allocated.
  */
+/*
+ * A second measuring aid: a plain streaming kernel that reads read_bytes from
+ * src and writes ratio * read_bytes to dst (ratio 0..4; 0 reads only), each
+ * byte once, with every instruction covering 1 KiB of consecutive bytes.  Its
+ * rate is the ceiling a kernel with the same read:write mix can reach on the
+ * GPU at hand (the Main Branch's attend pass writes about two bytes per byte
+ * read; its merge pass reads almost only).  read_bytes: a positive multiple
+ * of 16; dst: ratio * read_bytes bytes (NULL allowed for ratio 0); sink: at
+ * least 4 * MSA_HBM_STREAM_MAX_WORKGROUPS bytes (practically never written).
+ * All pointers device memory, 16-byte aligned.  Enqueued on `stream`.
+ */
+#define MSA_HBM_STREAM_MAX_WORKGROUPS 2048
+msa_status_t msa_hbm_stream(const void* src, size_t read_bytes, int32_t ratio, void* dst,
+                            void* sink, void* stream);
+
 #define MSA_PROFILE_KERNELS 17
 msa_status_t msa_profile_enable(int32_t enable);
 msa_status_t msa_profile_collect(float* total_ms, int32_t* launches);

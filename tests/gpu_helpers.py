@@ -65,10 +65,10 @@ def problem_from(t, w, lazy=False):
                      t["cu_seqlens_k"].cpu().numpy(), w.top_k)
 
 
-def run_gpu(w, t, q_chunk=0, want_scores=True, workspace_fill=None):
+def run_gpu(w, t, q_chunk=0, want_scores=True, workspace_fill=None, flags=0):
     dev = torch.device("cuda:0")
     g = {k: v.to(dev) for k, v in t.items()}
-    dims = msa.dims_for(w, q_chunk=q_chunk)
+    dims = msa.dims_for(w, q_chunk=q_chunk, flags=flags)
     bufs = msa.Buffers(dims, dev, want_scores=want_scores)
     if workspace_fill is not None:
         bufs.workspace.fill_(workspace_fill)
@@ -118,9 +118,9 @@ def check_out(gpu_out, ref_out, gpu_lse=None, ref_lse=None, what=""):
         assert dl <= LSE_ABS
 
 
-def run_gpu_inputs(w, t, q_chunk=0, want_scores=True):
+def run_gpu_inputs(w, t, q_chunk=0, want_scores=True, flags=0):
     """Forward on inputs already on the GPU (full-size workloads)."""
-    dims = msa.dims_for(w, q_chunk=q_chunk)
+    dims = msa.dims_for(w, q_chunk=q_chunk, flags=flags)
     bufs = msa.Buffers(dims, t["q"].device, want_scores=want_scores)
     msa.msa_forward(dims, t["q"], t["k"], t["v"], t["q_idx"], t["k_idx"], t["cu_seqlens_q"],
                     t["cu_seqlens_k"], bufs)

@@ -35,9 +35,9 @@ def test_exports_every_declared_symbol():
 
 
 def test_abi_version_and_struct_layout():
-    assert lib.msa_abi_version() == 2
+    assert lib.msa_abi_version() == 3
     assert ctypes.sizeof(msa.Dims) == 80
-    assert msa.Dims.block_table.offset == 64 and msa.Dims.reserved.offset == 76
+    assert msa.Dims.block_table.offset == 64 and msa.Dims.flags.offset == 76
 
 
 def test_status_strings():
@@ -88,11 +88,34 @@ def test_bad_dims_rejected(kw, status):
     assert lib.msa_workspace_size(ctypes.byref(d), 0, ctypes.byref(n)) == status
 
 
-def test_reserved_must_be_zero():
-    d = _dims()
-    d.reserved = 1
+def test_unknown_flag_bits_rejected():
     n = ctypes.c_size_t(0)
-    assert lib.msa_workspace_size(ctypes.byref(d), 0, ctypes.byref(n)) == 2
+    for bits in (2, 4, 1 << 30, -1):
+        d = _dims()
+        d.flags = bits
+        assert lib.msa_workspace_size(ctypes.byref(d), 0, ctypes.byref(n)) == 2
+
+
+def test_compact_partials_workspace_and_scope():
+    """Compact partials take 2 * head_dim + 8 bytes per row on the lists path;
+    decode-shaped steps keep fp32 partials; the block-mass call refuses them."""
+    full = msa.workspace_size(_dims(q_chunk=256), msa.OP_ATTEND)
+    comp = msa.workspace_size(_dims(q_chunk=256, flags=msa.FLAG_COMPACT_PARTIALS), msa.OP_ATTEND)
+    rows = 256 * 64 * 16
+    assert full >= rows * (128 * 4 + 8) and comp >= rows * (128 * 2 + 8)
+    assert comp < full and comp <= rows * (128 * 2 + 8) + 4096
+    # 48 GiB default cap: a compact pass holds nearly twice the rows
+    p_full = msa.attend_pass_rows(_dims(total_q=1 << 20, total_k=1 << 20, max_q_len=1 << 20,
+                                        max_k_len=1 << 20))
+    p_comp = msa.attend_pass_rows(_dims(total_q=1 << 20, total_k=1 << 20, max_q_len=1 << 20,
+                                        max_k_len=1 << 20, flags=msa.FLAG_COMPACT_PARTIALS))
+    assert p_comp > 1.7 * p_full          # passes are rounded to equal sizes
+    dec = dict(batch=32, total_q=32, total_k=32 * 65536, max_q_len=1, max_k_len=65536)
+    assert msa.workspace_size(_dims(**dec), msa.OP_ATTEND) == \
+        msa.workspace_size(_dims(**dec, flags=msa.FLAG_COMPACT_PARTIALS), msa.OP_ATTEND)
+    d = _dims(flags=msa.FLAG_COMPACT_PARTIALS)
+    st = lib.msa_attend_with_mass(ctypes.byref(d), *([None] * 12), ctypes.c_size_t(0), None)
+    assert st == 3
 
 
 def test_null_and_alignment_and_workspace_checks_launch_nothing():

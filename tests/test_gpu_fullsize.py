@@ -6,6 +6,7 @@ import numpy as np
 import pytest
 import torch
 
+import block_sparse_long_index_amd as msa
 from msa_inputs import generate, sample_rows, workload
 
 pytestmark = pytest.mark.gpu
@@ -13,14 +14,20 @@ pytestmark = pytest.mark.gpu
 from gpu_helpers import check_out, check_selection, log, problem_from, run_gpu_inputs  # noqa: E402
 
 
-def _sampled(name, n_random, max_rows=None):
+def _sampled(name, n_random, max_rows=None, flags=0, pass_edges=False):
     w = workload(name)
     log(f"[{name}] generating {w.note}")
     t = generate(w, "cuda:0")
-    dims, bufs = run_gpu_inputs(w, t)
+    dims, bufs = run_gpu_inputs(w, t, flags=flags)
     rows = sample_rows(w, n_random)
     if max_rows:
         rows = rows[:max_rows]
+    if pass_edges:
+        # the first and last rows of every attend pass
+        step = msa.attend_pass_rows(dims)
+        edges = [r for a in range(step, w.total_q, step) for r in (a - 1, a)]
+        log(f"[{name}] attend passes of {step} rows; edge rows {edges}")
+        rows = sorted(set(rows) | set(edges))
     log(f"[{name}] forward done; oracle on {len(rows)} rows")
     P = problem_from(t, w, lazy=True)
     ref = P.run(rows, want_scores=True)
@@ -54,4 +61,14 @@ def test_decode_batch_all_rows():
 
 
 def test_p1m_sampled():
-    _sampled("p1m", 4, max_rows=10)
+    # 64 random rows (top-k over up to 8191 earlier blocks), the first two
+    # blocks' ends, the last block, and both sides of every attend pass boundary
+    _sampled("p1m", 64, pass_edges=True)
+
+
+def test_p128k_compact_partials_sampled():
+    _sampled("p128k", 24, flags=msa.FLAG_COMPACT_PARTIALS, pass_edges=True)
+
+
+def test_p32k_peaky_compact_partials_sampled():
+    _sampled("p32k_peaky", 24, flags=msa.FLAG_COMPACT_PARTIALS)

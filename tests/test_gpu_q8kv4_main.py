@@ -238,3 +238,49 @@ def test_q8kv4_main_p128k_sampled():
 
 def test_q8kv4_main_decode_all_rows():
     _sampled_full("decode", 0)
+
+
+def test_q8k4_index_q8kv4_main_p1m_sampled():
+    """Both branches quantised as in production (8-bit queries, 4-bit keys
+    and values; the pages' "Q8KV4") at 1M tokens, in the launch configuration
+    bench.py times: index codes checked on the sampled rows and on the first
+    key blocks, the selection against the oracle on the dequantised index
+    projections within the fp8 matrix cores' bound, the Main Branch against
+    the oracle on the dequantised q, k, v."""
+    from test_gpu_fp8 import _DeqQ, check_rows_fp8
+    from test_gpu_q8k4 import _DeqK4
+    from oracle import fp8_index as F8
+    w = workload("p1m")
+    log(f"[p1m-q8k4-q8kv4] generating {w.note}")
+    t = generate(w, "cuda:0")
+    dims = msa.dims_for(w)
+    dev = t["q"].device
+    bufs = msa.Buffers(dims, dev, want_scores=True)
+    qk = msa.Q8K4Index(dims, dev)
+    m = msa.Q8KV4Main(dims, dev)
+    msa.msa_forward(dims, t["q"], t["k"], t["v"], t["q_idx"], t["k_idx"], t["cu_seqlens_q"],
+                    t["cu_seqlens_k"], bufs, q8k4=qk, fp8_main=m)
+    torch.cuda.synchronize()
+    rows = sample_rows(w, 48)
+    log(f"[p1m-q8k4-q8kv4] forward done; oracle on {len(rows)} rows")
+    ridx = torch.as_tensor(rows, device=dev, dtype=torch.long)
+    qc, qe = F8.quantize_q_idx(t["q_idx"].index_select(0, ridx).double().cpu().numpy())
+    assert np.array_equal(qk.q_idx8.index_select(0, ridx).cpu().numpy(), qc)
+    assert np.array_equal(qk.q_exp.index_select(0, ridx).cpu().numpy(), qe)
+    n0 = 128 * 64
+    kc, ke = F4.quantize_k_idx4(t["k_idx"][:n0].double().cpu().numpy())
+    assert np.array_equal(qk.k_idx4[:n0].cpu().numpy(), F4.pack(kc))
+    assert np.array_equal(qk.k_exp4[:n0].cpu().numpy(), ke)
+
+    def rows_of(x):
+        return lambda lo, hi: _f64(x[lo:hi])
+    kq = M4.DequantizedRows4(rows_of(t["k"]), t["k"].shape[0], t["k"].shape[1:])
+    vq = M4.DequantizedRows4(rows_of(t["v"]), t["v"].shape[0], t["v"].shape[1:])
+    P = O.Problem(_LazyQuantQ(t["q"]), kq, vq, _DeqQ(t["q_idx"]), _DeqK4(t["k_idx"]),
+                  t["cu_seqlens_q"].cpu().numpy(), t["cu_seqlens_k"].cpu().numpy(), w.top_k)
+    ref = P.run(rows, want_scores=True)
+    sel = bufs.sel.index_select(0, ridx).cpu().numpy()
+    score = bufs.sel_score.index_select(0, ridx).cpu().numpy()
+    out = bufs.out.index_select(0, ridx).float().cpu().numpy()
+    lse = bufs.lse.index_select(0, ridx).cpu().numpy()
+    check_rows_fp8(P, rows, sel, score, ref, out, lse, "p1m-q8k4-q8kv4")
