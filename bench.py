@@ -582,6 +582,15 @@ def run_leg(args):
         torch.cuda.synchronize()
         log(f"[bench] paged key cache: {pages} pages of {BLOCK} rows, scrambled order")
     bufs = msa.Buffers(dims, dev, want_scores=args.kl, want_lse=True)
+    # the compact-partial pass (measured after the headline) may hold more rows per pass,
+    # i.e. need more workspace: one buffer serves both
+    if (args.partials == "both" or (args.partials is None and not _decode_like(w) and args.main == "bf16"
+                                    and not args.kl and not args.project_dim)):
+        dims_probe = msa.Dims.from_buffer_copy(dims)
+        dims_probe.flags = msa.FLAG_COMPACT_PARTIALS
+        need_c = msa.workspace_size(dims_probe, msa.OP_ATTEND)
+        if need_c > bufs.workspace.numel():
+            bufs.workspace = torch.empty((need_c,), dtype=torch.uint8, device=dev)
     kl_out = None
     if args.kl:
         kl_out = dict(mass=torch.empty((w.total_q, w.num_kv_heads, w.top_k), dtype=torch.float32, device=dev),

@@ -355,14 +355,28 @@ __device__ __forceinline__ void attend_item(
       // O / l first (no larger than the largest |v|), then the exact power-of-two
       // scaling into (-1, 1]: no intermediate overflows whatever E is
       auto sc = [&](float x) __attribute__((always_inline)) { return ldexpf(x * inv_l, -E); };
-      uint16_t* dst = static_cast<uint16_t*>(part_acc) + (size_t)drow * D + 4 * half;
+      // A lane holds its row's d = 32 dt + 8 j + 4 half + (0..3), j = 0..3.  For each
+      // 16-value run 32 dt + 16 m the two lane halves trade one 4-value group, so that
+      // half 0 holds d 0..7 and half 1 holds d 8..15 of the run: every store is then
+      // 16 contiguous bytes per lane (32 per row), as for fp32 partials.
+      uint16_t* dst = static_cast<uint16_t*>(part_acc) + (size_t)drow * D + 8 * half;
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-          *reinterpret_cast<uint2*>(dst + dt * 32 + 8 * j) =
-              make_uint2(pack2_f16(sc(oacc[dt][4 * j]), sc(oacc[dt][4 * j + 1])),
-                         pack2_f16(sc(oacc[dt][4 * j + 2]), sc(oacc[dt][4 * j + 3])));
+        for (int m = 0; m < 2; ++m) {
+          const int i = 8 * m;
+          // group j = 2m: d 16m + 4 half + 0..3; group j = 2m + 1: d 16m + 8 + 4 half + 0..3
+          const uint32_t a0 = pack2_f16(sc(oacc[dt][i]), sc(oacc[dt][i + 1]));
+          const uint32_t a1 = pack2_f16(sc(oacc[dt][i + 2]), sc(oacc[dt][i + 3]));
+          const uint32_t b0 = pack2_f16(sc(oacc[dt][i + 4]), sc(oacc[dt][i + 5]));
+          const uint32_t b1 = pack2_f16(sc(oacc[dt][i + 6]), sc(oacc[dt][i + 7]));
+          // half 0 receives half 1's group 2m (d 16m + 4..7), half 1 receives half 0's
+          // group 2m + 1 (d 16m + 8..11)
+          const uint2 s0 = permlane32_swap_u32(a0, b0);
+          const uint2 s1 = permlane32_swap_u32(a1, b1);
+          const uint4 v = half == 0 ? make_uint4(a0, a1, s0.y, s1.y) : make_uint4(s0.x, s1.x, b0, b1);
+          *reinterpret_cast<uint4*>(dst + dt * 32 + 16 * m) = v;
+        }
     } else {
       part_ml[drow] = make_float2(m, l);
       float* dst = static_cast<float*>(part_acc) + (size_t)drow * D + 4 * half;
@@ -442,119 +456,114 @@ __global__ __launch_bounds__(256, 2) void attend_blocks_kernel(
   }
 }
 
-// One wave per (query row, head); KMAX >= top_k, so every slot load is issued
-// up front.  Eight waves per workgroup take eight consecutive heads, so a
-// workgroup reads whole (row, group) partial runs contiguously.
-constexpr int kMergeWaves = 8;
+// Merge: each lane owns one 16-byte chunk of one (query row, head)'s partial
+// rows -- 4 fp32 values, or 8 fp16 values with compact partials -- so a wave
+// covers 64 * 16 bytes of one slot per load instruction (2 heads at D = 128 with
+// fp32 partials, 4 with compact ones; heads of one (row, group) are contiguous
+// in every slot).  KMAX >= top_k, so every slot load is issued up front.
+constexpr int kMergeWaves = 4;
 template <int D, int KMAX, bool COMPACT>
 __global__ __launch_bounds__(kMergeWaves * 64) void merge_partials_kernel(
     const void* __restrict__ part_acc, const float2* __restrict__ part_ml,
     const int32_t* __restrict__ sel, int r0, int r1, int Hq, int G, int top_k,
     uint16_t* __restrict__ out, float* __restrict__ lse) {
-  constexpr int PER = D / 64;
+  constexpr int VPL = COMPACT ? 8 : 4;   // values per lane: 16 bytes
+  constexpr int LPH = D / VPL;           // lanes per head
+  constexpr int HPW = 64 / LPH;          // heads per wave
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const long long w = (long long)blockIdx.x * kMergeWaves + wv;
-  const long long n = (long long)(r1 - r0) * Hq;
-  if (w >= n) return;
   const int lane = threadIdx.x & 63;
-  const int rr = (int)(w / Hq), h = (int)(w % Hq);
+  const long long n = (long long)(r1 - r0) * Hq;
+  const long long hh = ((long long)blockIdx.x * kMergeWaves + wv) * HPW + lane / LPH;
+  if (hh >= n) return;
+  const int c = lane % LPH;              // this lane's chunk of the row
+  const int rr = (int)(hh / Hq), h = (int)(hh % Hq);
   const int r = r0 + rr;
-  const int g = h / (Hq / G);
+  const int hpg = Hq / G;
+  const int g = h / hpg;
   const int32_t* srow = sel + ((size_t)r * G + g) * top_k;
   int ns = 0;
 #pragma unroll
   for (int s = 0; s < KMAX; ++s)
     if (s < top_k) ns += srow[s] >= 0 ? 1 : 0;
   // partial rows of (row, group, slot) hold the group's heads contiguously
-  const int hpg = Hq / G;
   const size_t base = ((size_t)rr * G + g) * top_k * hpg + (h - g * hpg);
   float2 ml[KMAX];
-  float a[KMAX][PER];
+  uint4 a[KMAX];
 #pragma unroll
   for (int s = 0; s < KMAX; ++s) {
     ml[s] = make_float2(-INFINITY, 0.f);
-#pragma unroll
-    for (int j = 0; j < PER; ++j) a[s][j] = 0.f;
+    a[s] = make_uint4(0, 0, 0, 0);
     if (s < ns) {
-      ml[s] = part_ml[base + (size_t)s * hpg];
-      if constexpr (COMPACT) {
-        const uint16_t* src = static_cast<const uint16_t*>(part_acc) + (base + (size_t)s * hpg) * D + lane * PER;
-        if constexpr (PER == 2) {
-          const float2 x = unpack2_f16(*reinterpret_cast<const uint32_t*>(src));
-          a[s][0] = x.x;
-          a[s][1] = x.y;
-        } else {
-          a[s][0] = f16_bits_to_f32(src[0]);
-        }
-      } else {
-        const float* src = static_cast<const float*>(part_acc) + (base + (size_t)s * hpg) * D + lane * PER;
-        if constexpr (PER == 2) {
-          float2 x = *reinterpret_cast<const float2*>(src);
-          a[s][0] = x.x;
-          a[s][1] = x.y;
-        } else {
-          a[s][0] = src[0];
-        }
-      }
+      const size_t row = base + (size_t)s * hpg;
+      ml[s] = part_ml[row];
+      if constexpr (COMPACT)
+        a[s] = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(part_acc) + row * D + c * VPL);
+      else
+        a[s] = *reinterpret_cast<const uint4*>(static_cast<const float*>(part_acc) + row * D + c * VPL);
     }
   }
+  float acc[VPL];
+#pragma unroll
+  for (int j = 0; j < VPL; ++j) acc[j] = 0.f;
+  float M = -INFINITY, L = 0.f;
+  int e_out = 0;
   if constexpr (COMPACT) {
     // ml[s] = (w_s, E_s): weights 2^(w_s - M), values o_s 2^E_s
-    float M = -INFINITY, Em = -INFINITY;
+    float Em = -INFINITY;
 #pragma unroll
     for (int s = 0; s < KMAX; ++s)
       if (s < ns) {
         M = fmaxf(M, ml[s].x);
         Em = fmaxf(Em, ml[s].y);
       }
-    float L = 0.f;
-    float acc[PER];
-#pragma unroll
-    for (int j = 0; j < PER; ++j) acc[j] = 0.f;
 #pragma unroll
     for (int s = 0; s < KMAX; ++s) {
       if (s < ns) {
         L += exp2f(ml[s].x - M);
         const float wgt = exp2f(ml[s].x - M + (ml[s].y - Em));
+        // the packed words pass through an empty asm so that each slot is
+        // unpacked only here: converting every slot's fp16 values up front
+        // would hold 8 * KMAX floats (175 registers at KMAX 16 instead of 111)
+        // and halve the waves that keep loads in flight
+        uint4 av = a[s];
+        asm volatile("" : "+v"(av.x), "+v"(av.y), "+v"(av.z), "+v"(av.w));
+        const uint32_t w4[4] = {av.x, av.y, av.z, av.w};
 #pragma unroll
-        for (int j = 0; j < PER; ++j) acc[j] += wgt * a[s][j];
+        for (int q = 0; q < 4; ++q) {
+          const float2 v = unpack2_f16(w4[q]);
+          acc[2 * q] += wgt * v.x;
+          acc[2 * q + 1] += wgt * v.y;
+        }
       }
     }
-    const float inv = 1.f / L;
-    const int e = (int)Em;
-    uint16_t* o = out + ((size_t)r * Hq + h) * D + lane * PER;
-    if constexpr (PER == 2) {
-      *reinterpret_cast<uint32_t*>(o) = pack2_bf16(ldexpf(acc[0] * inv, e), ldexpf(acc[1] * inv, e));
-    } else {
-      o[0] = __builtin_bit_cast(uint16_t, (__bf16)ldexpf(acc[0] * inv, e));
-    }
-    if (lse && lane == 0) lse[(size_t)r * Hq + h] = (M + log2f(L)) * 0.69314718055994530942f;
-    return;
-  }
-  float M = -INFINITY;
+    e_out = (int)Em;
+  } else {
 #pragma unroll
-  for (int s = 0; s < KMAX; ++s) M = fmaxf(M, ml[s].x);
-  float L = 0.f;
-  float acc[PER];
+    for (int s = 0; s < KMAX; ++s)
+      if (s < ns) M = fmaxf(M, ml[s].x);
 #pragma unroll
-  for (int j = 0; j < PER; ++j) acc[j] = 0.f;
-#pragma unroll
-  for (int s = 0; s < KMAX; ++s) {
-    if (s < ns) {
-      const float wgt = exp2f(ml[s].x - M);
-      L += ml[s].y * wgt;
-#pragma unroll
-      for (int j = 0; j < PER; ++j) acc[j] += wgt * a[s][j];
+    for (int s = 0; s < KMAX; ++s) {
+      if (s < ns) {
+        const float wgt = exp2f(ml[s].x - M);
+        L += ml[s].y * wgt;
+        acc[0] += wgt * __uint_as_float(a[s].x);
+        acc[1] += wgt * __uint_as_float(a[s].y);
+        acc[2] += wgt * __uint_as_float(a[s].z);
+        acc[3] += wgt * __uint_as_float(a[s].w);
+      }
     }
   }
   const float inv = 1.f / L;
-  uint16_t* o = out + ((size_t)r * Hq + h) * D + lane * PER;
-  if constexpr (PER == 2) {
-    *reinterpret_cast<uint32_t*>(o) = pack2_bf16(acc[0] * inv, acc[1] * inv);
-  } else {
-    o[0] = __builtin_bit_cast(uint16_t, (__bf16)(acc[0] * inv));
-  }
-  if (lse && lane == 0) lse[(size_t)r * Hq + h] = (M + log2f(L)) * 0.69314718055994530942f;
+  uint16_t* o = out + ((size_t)r * Hq + h) * D + c * VPL;
+  uint32_t packed[VPL / 2];
+#pragma unroll
+  for (int q = 0; q < VPL / 2; ++q)
+    packed[q] = pack2_bf16(ldexpf(acc[2 * q] * inv, e_out), ldexpf(acc[2 * q + 1] * inv, e_out));
+  if constexpr (VPL == 8)
+    *reinterpret_cast<uint4*>(o) = make_uint4(packed[0], packed[1], packed[2], packed[3]);
+  else
+    *reinterpret_cast<uint2*>(o) = make_uint2(packed[0], packed[1]);
+  if (lse && c == 0) lse[(size_t)r * Hq + h] = (M + log2f(L)) * 0.69314718055994530942f;
 }
 
 // ---------------------------------------------------------------------------
@@ -645,8 +654,11 @@ static void launch_merge_d(dim3 grid, const void* part_acc, const float2* part_m
 hipError_t launch_merge(int D, bool compact, const void* part_acc, const float2* part_ml,
                         const int32_t* sel, int r0, int r1, int Hq, int G, int top_k, void* out,
                         float* lse, hipStream_t st) {
-  long long n = (long long)(r1 - r0) * Hq;
-  dim3 grid((unsigned)((n + kMergeWaves - 1) / kMergeWaves));
+  // heads per wave: 64 lanes of 16 bytes over one head's row of D fp32 or fp16 values
+  const long long hpw = 64 / (D / (compact ? 8 : 4));
+  const long long n = (long long)(r1 - r0) * Hq;
+  const long long waves = (n + hpw - 1) / hpw;
+  dim3 grid((unsigned)((waves + kMergeWaves - 1) / kMergeWaves));
 #define MSA_MRD(DD, C) launch_merge_d<DD, C>(grid, part_acc, part_ml, sel, r0, r1, Hq, G, top_k, out, lse, st)
   if (D == 64) {
     if (compact) MSA_MRD(64, true); else MSA_MRD(64, false);

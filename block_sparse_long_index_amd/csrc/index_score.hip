@@ -216,18 +216,23 @@ __global__ __launch_bounds__(NW * 64) void index_select_prefill_kernel(
       float rmax[RT];
 #pragma unroll
       for (int rt = 0; rt < RT; ++rt) rmax[rt] = -INFINITY;
-      // the block's 4 * KS fragments (key tile f / KS, k-step f % KS) flow through a
-      // window of DEPTH registers: a slot is refilled right after its MFMAs issue,
-      // so DEPTH fragments are in flight; key tiles alternate between two
-      // accumulator sets so a tile's row max does not hold up the next tile
+      // the block's 4 * KS fragments flow through a window of DEPTH registers:
+      // a slot is refilled right after its MFMAs issue, so DEPTH fragments are
+      // in flight.  Key tiles are scored in pairs, k-step by k-step, into two
+      // accumulator sets (fragment f: pair f / (2 KS), k-step (f % (2 KS)) / 2,
+      // tile 2 pair + f % 2), so each accumulator's next MFMA comes 2 * RT
+      // MFMAs after its last one (RT independent chains per tile would leave
+      // dependent MFMAs back to back)
       constexpr int NF = 4 * KS, DEPTH = 4;
+      auto kt_of = [](int f) { return 2 * (f / (2 * KS)) + (f & 1); };
+      auto ks_of = [](int f) { return (f % (2 * KS)) >> 1; };
       bf16x8 win[DEPTH];
 #pragma unroll
-      for (int f = 0; f < DEPTH; ++f) win[f] = Ring::frag(rbuf, (f / KS) * 32 + col, 2 * (f % KS) + half);
+      for (int f = 0; f < DEPTH; ++f) win[f] = Ring::frag(rbuf, kt_of(f) * 32 + col, 2 * ks_of(f) + half);
       f32x16 acc[2][RT];
 #pragma unroll
       for (int f = 0; f < NF; ++f) {
-        const int kt = f / KS, ks = f % KS, set = kt & 1;
+        const int ks = ks_of(f), set = f & 1;
         if (ks == 0) {
 #pragma unroll
           for (int rt = 0; rt < RT; ++rt) acc[set][rt] = f32x16{};
@@ -235,7 +240,7 @@ __global__ __launch_bounds__(NW * 64) void index_select_prefill_kernel(
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt) acc[set][rt] = mfma32(win[f % DEPTH], qf[rt][ks], acc[set][rt]);
         if (f + DEPTH < NF)
-          win[f % DEPTH] = Ring::frag(rbuf, ((f + DEPTH) / KS) * 32 + col, 2 * ((f + DEPTH) % KS) + half);
+          win[f % DEPTH] = Ring::frag(rbuf, kt_of(f + DEPTH) * 32 + col, 2 * ks_of(f + DEPTH) + half);
         if (ks == KS - 1) {
 #pragma unroll
           for (int rt = 0; rt < RT; ++rt)

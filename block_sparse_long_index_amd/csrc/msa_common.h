@@ -159,6 +159,14 @@ __device__ inline float row_tile_max(const float (&rmax)[RT], int half) {
   }
 }
 
+// v_permlane32_swap of x and y: x's lanes 32-63 trade places with y's lanes
+// 0-31.  So lanes 0-31 receive x of lanes 32-63 (in .y) and lanes 32-63
+// receive y of lanes 0-31 (in .x); the other halves keep their own values.
+__device__ inline uint2 permlane32_swap_u32(uint32_t x, uint32_t y) {
+  const auto r = __builtin_amdgcn_permlane32_swap(x, y, false, false);
+  return make_uint2(r[0], r[1]);
+}
+
 // ds_read_b64_tr_b16 at an LDS byte address: the four 16-bit values this lane
 // receives, as two dwords.  Within each 16 lanes, lane 4a + c receives element
 // c of the 8-byte pieces addressed by lanes a, a + 4, a + 8, a + 12 (measured):
