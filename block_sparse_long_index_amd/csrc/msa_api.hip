@@ -3,6 +3,7 @@
 // is allocated here and nothing synchronises the stream.
 #include <math.h>
 #include <stdio.h>
+#include <stdlib.h>
 #include <string.h>
 
 #include <atomic>
@@ -267,6 +268,54 @@ msa_status_t hip_fail(hipError_t e) {
   return MSA_ERR_HIP;
 }
 
+// MSA_DEBUG_SYNC (environment, read at every call; any value but "" or "0"):
+// a debugging aid that blocks the host.  Each call first validates its
+// cu_seqlens on the host, and every kernel stage is followed by a wait on the
+// call's stream and an error check that names the stage.  Not for use under
+// graph capture (it synchronises the stream).
+bool debug_sync_on() {
+  const char* v = getenv("MSA_DEBUG_SYNC");
+  return v && v[0] && strcmp(v, "0") != 0;
+}
+
+// status of a stage whose launch returned e
+msa_status_t launched(hipError_t e, hipStream_t st, int kid) {
+  if (e != hipSuccess) return hip_fail(e);
+  if (!debug_sync_on()) return MSA_OK;
+  e = hipStreamSynchronize(st);
+  if (e == hipSuccess) e = hipGetLastError();
+  if (e != hipSuccess) {
+    g_last_error = std::string("MSA_DEBUG_SYNC: after stage ") + kKernelNames[kid] + ": " +
+                   hipGetErrorString(e);
+    return MSA_ERR_HIP;
+  }
+  return MSA_OK;
+}
+
+// MSA_DEBUG_SYNC: cu_seqlens_q / cu_seqlens_k (either may be NULL) must start
+// at 0, not decrease, end at total_q / total_k (total_k: contiguous caches
+// only) and agree with max_q_len / max_k_len and Lq_b <= Lk_b.
+msa_status_t debug_check_seqlens(const msa_dims_t* d, const int32_t* cu_q, const int32_t* cu_k,
+                                 hipStream_t st) {
+  if (!debug_sync_on()) return MSA_OK;
+  const int n = d->batch + 1;
+  std::vector<int32_t> q(n, 0), k(n, 0);
+  hipError_t e = hipStreamSynchronize(st);
+  if (e == hipSuccess && cu_q) e = hipMemcpy(q.data(), cu_q, n * sizeof(int32_t), hipMemcpyDeviceToHost);
+  if (e == hipSuccess && cu_k) e = hipMemcpy(k.data(), cu_k, n * sizeof(int32_t), hipMemcpyDeviceToHost);
+  if (e != hipSuccess) return hip_fail(e);
+  for (int b = 0; b + 1 < n; ++b) {
+    const long long lq = (long long)q[b + 1] - q[b], lk = (long long)k[b + 1] - k[b];
+    if ((cu_q && (lq < 0 || lq > d->max_q_len)) || (cu_k && (lk < 0 || lk > d->max_k_len)) ||
+        (cu_q && cu_k && lq > lk))
+      return fail(MSA_ERR_BAD_DIMS, "MSA_DEBUG_SYNC: cu_seqlens do not match the dims");
+  }
+  if ((cu_q && (q[0] != 0 || q[n - 1] != d->total_q)) ||
+      (cu_k && (k[0] != 0 || (d->kv_pages == 0 && k[n - 1] != d->total_k))))
+    return fail(MSA_ERR_BAD_DIMS, "MSA_DEBUG_SYNC: cu_seqlens do not start at 0 or end at the totals");
+  return MSA_OK;
+}
+
 }  // namespace
 
 // Scratch of msa_attend_noalloc (the Main Branch's partials), for callers that
@@ -318,7 +367,11 @@ int32_t msa_abi_version(void) { return MSA_ABI_VERSION; }
 
 const char* msa_last_error(void) { return g_last_error.c_str(); }
 
-const char* msa_status_string(msa_status_t s) {
+const char* msa_status_string(msa_status_t s_in) {
+  // a C caller may pass any int: read it as one (loading an out-of-range value
+  // as this C++ enum would be undefined)
+  int s;
+  memcpy(&s, &s_in, sizeof s);
   switch (s) {
     case MSA_OK: return "MSA_OK";
     case MSA_ERR_NULL_ARG: return "MSA_ERR_NULL_ARG: a required pointer is NULL";
@@ -331,11 +384,13 @@ const char* msa_status_string(msa_status_t s) {
   return "MSA_ERR_UNKNOWN";
 }
 
-msa_status_t msa_workspace_size(const msa_dims_t* dims, msa_op_t op, size_t* bytes) {
+msa_status_t msa_workspace_size(const msa_dims_t* dims, msa_op_t op_in, size_t* bytes) {
   Derived x;
   msa_status_t s = check_dims(dims, &x);
   if (s != MSA_OK) return s;
   if (!bytes) return fail(MSA_ERR_NULL_ARG, "bytes is NULL");
+  int op;   // any int from a C caller (see msa_status_string)
+  memcpy(&op, &op_in, sizeof op);
   switch (op) {
     case MSA_OP_INDEX_SELECT: *bytes = ws_select(dims, x); return MSA_OK;
     case MSA_OP_BUILD_LISTS: *bytes = ws_lists(dims, x); return MSA_OK;
@@ -361,12 +416,13 @@ msa_status_t msa_index_select(const msa_dims_t* dims, const void* q_idx, const v
   if (workspace_bytes < ws_select(dims, x))
     return fail(MSA_ERR_WORKSPACE_TOO_SMALL, "index_select workspace too small");
   hipStream_t st = (hipStream_t)stream;
+  if (msa_status_t v = debug_check_seqlens(dims, cu_seqlens_q, cu_seqlens_k, st); v != MSA_OK) return v;
   if (!x.decode_path) {
     ProfScope ps(K_INDEX_PREFILL, st);
     hipError_t e = msa::launch_index_select_prefill(q_idx, k_idx, cu_seqlens_q, cu_seqlens_k, x.kv,
                                                     dims->batch, x.G, x.DI, dims->max_q_len,
                                                     x.top_k, sel, sel_score, st);
-    return e == hipSuccess ? MSA_OK : hip_fail(e);
+    return launched(e, st, K_INDEX_PREFILL);
   }
   float* S = (float*)(((uintptr_t)workspace + 255) & ~(uintptr_t)255);
   const long long chunk = select_chunk(dims, x);
@@ -379,11 +435,11 @@ msa_status_t msa_index_select(const msa_dims_t* dims, const void* q_idx, const v
       e = msa::launch_index_score_decode(q_idx, k_idx, cu_seqlens_q, cu_seqlens_k, x.kv, dims->batch, x.G,
                                          x.DI, x.nb_max, dims->max_q_len * x.G, a, z, S, ld, st);
     }
-    if (e != hipSuccess) return hip_fail(e);
+    if (msa_status_t ls = launched(e, st, K_INDEX_DECODE); ls != MSA_OK) return ls;
     ProfScope ps(K_TOPK, st);
     e = msa::launch_topk_select(S, ld, a, z, cu_seqlens_q, cu_seqlens_k, dims->batch, x.G, x.top_k,
                                 sel, sel_score, st);
-    if (e != hipSuccess) return hip_fail(e);
+    if (msa_status_t ls = launched(e, st, K_TOPK); ls != MSA_OK) return ls;
   }
   return MSA_OK;
 }
@@ -408,11 +464,12 @@ msa_status_t msa_index_project(const msa_dims_t* dims, int32_t model_dim, const 
   if (workspace_bytes < need)
     return fail(MSA_ERR_WORKSPACE_TOO_SMALL, "index_project workspace too small");
   hipStream_t st = (hipStream_t)stream;
+  if (msa_status_t v = debug_check_seqlens(dims, cu_seqlens_q, cu_seqlens_k, st); v != MSA_OK) return v;
   ProfScope ps(K_PROJECT, st);
   hipError_t e = msa::launch_index_project(x, w_q, w_k, model_dim, x_.G, x_.DI, (int)x_.total_q,
                                            cu_seqlens_q, cu_seqlens_k, x_.kv, dims->batch, q_idx,
                                            k_idx, workspace, st);
-  return e == hipSuccess ? MSA_OK : hip_fail(e);
+  return launched(e, st, K_PROJECT);
 }
 
 msa_status_t msa_index_quantize_fp8(const msa_dims_t* dims, const void* q_idx, const void* k_idx,
@@ -436,7 +493,7 @@ msa_status_t msa_index_quantize_fp8(const msa_dims_t* dims, const void* q_idx, c
                                                 has_k ? x.nb_max : 0,
                                                 has_q ? x.total_q * x.G : 0, q_idx8, q_exp, k_idx8,
                                                 k_exp, st);
-  return e == hipSuccess ? MSA_OK : hip_fail(e);
+  return launched(e, st, K_QUANT_FP8);
 }
 
 namespace {
@@ -461,13 +518,14 @@ msa_status_t select_q8(const msa_dims_t* dims, const void* q_idx8, const uint8_t
   if (workspace_bytes < ws_select(dims, x))
     return fail(MSA_ERR_WORKSPACE_TOO_SMALL, "index_select workspace too small");
   hipStream_t st = (hipStream_t)stream;
+  if (msa_status_t v = debug_check_seqlens(dims, cu_seqlens_q, cu_seqlens_k, st); v != MSA_OK) return v;
   if (!x.decode_path) {
     ProfScope ps(k4 ? K_INDEX_PREFILL_Q8K4 : K_INDEX_PREFILL_FP8, st);
     hipError_t e = msa::launch_index_select_prefill_fp8(q_idx8, q_exp, k_codes, k_exp, k4,
                                                         cu_seqlens_q, cu_seqlens_k, x.kv,
                                                         dims->batch, x.G, x.DI, x.nb_max,
                                                         dims->max_q_len, x.top_k, sel, sel_score, st);
-    return e == hipSuccess ? MSA_OK : hip_fail(e);
+    return launched(e, st, k4 ? K_INDEX_PREFILL_Q8K4 : K_INDEX_PREFILL_FP8);
   }
   float* S = (float*)(((uintptr_t)workspace + 255) & ~(uintptr_t)255);
   const long long chunk = select_chunk(dims, x);
@@ -481,11 +539,11 @@ msa_status_t select_q8(const msa_dims_t* dims, const void* q_idx8, const uint8_t
                                              cu_seqlens_k, x.kv, dims->batch, x.G, x.DI, x.nb_max,
                                              dims->max_q_len * x.G, a, z, S, ld, st);
     }
-    if (e != hipSuccess) return hip_fail(e);
+    if (msa_status_t ls = launched(e, st, k4 ? K_INDEX_DECODE_Q8K4 : K_INDEX_DECODE_FP8); ls != MSA_OK) return ls;
     ProfScope ps(K_TOPK, st);
     e = msa::launch_topk_select(S, ld, a, z, cu_seqlens_q, cu_seqlens_k, dims->batch, x.G, x.top_k,
                                 sel, sel_score, st);
-    if (e != hipSuccess) return hip_fail(e);
+    if (msa_status_t ls = launched(e, st, K_TOPK); ls != MSA_OK) return ls;
   }
   return MSA_OK;
 }
@@ -520,7 +578,7 @@ msa_status_t msa_index_quantize_q8k4(const msa_dims_t* dims, const void* q_idx, 
                                                  has_k ? x.nb_max : 0,
                                                  has_q ? x.total_q * x.G : 0, q_idx8, q_exp, k_idx4,
                                                  k_exp4, st);
-  return e == hipSuccess ? MSA_OK : hip_fail(e);
+  return launched(e, st, K_QUANT_Q8K4);
 }
 
 msa_status_t msa_index_select_q8k4(const msa_dims_t* dims, const void* q_idx8, const uint8_t* q_exp,
@@ -547,12 +605,14 @@ msa_status_t msa_build_block_query_lists(const msa_dims_t* dims, const int32_t* 
     return fail(MSA_ERR_ALIGNMENT, "tensor pointers must be 16-byte aligned");
   if (workspace_bytes < ws_lists(dims, x))
     return fail(MSA_ERR_WORKSPACE_TOO_SMALL, "build_lists workspace too small");
+  if (msa_status_t v = debug_check_seqlens(dims, cu_seqlens_q, cu_seqlens_k, (hipStream_t)stream); v != MSA_OK)
+    return v;
   void* ws = (void*)(((uintptr_t)workspace + 255) & ~(uintptr_t)255);
   ProfScope ps(K_LISTS, (hipStream_t)stream);
   hipError_t e = msa::launch_build_lists(sel, cu_seqlens_q, cu_seqlens_k, dims->batch, x.G, x.top_k,
                                          x.nqt_max, x.nb_max, block_offsets, block_entries, ws,
                                          (hipStream_t)stream);
-  return e == hipSuccess ? MSA_OK : hip_fail(e);
+  return launched(e, (hipStream_t)stream, K_LISTS);
 }
 
 // decode-shaped steps attend per (query, slot) from the selection alone
@@ -594,6 +654,7 @@ static msa_status_t attend_impl(const msa_dims_t* dims, const void* q, const voi
   if (workspace_bytes < ws_attend(dims, x))
     return fail(MSA_ERR_WORKSPACE_TOO_SMALL, "attend workspace too small");
   hipStream_t st = (hipStream_t)stream;
+  if (msa_status_t dv = debug_check_seqlens(dims, cu_seqlens_q, cu_seqlens_k, st); dv != MSA_OK) return dv;
   const long long chunk = attend_chunk(dims, x);
   char* base = (char*)(((uintptr_t)workspace + 255) & ~(uintptr_t)255);
   void* part_acc = base;
@@ -616,17 +677,17 @@ static msa_status_t attend_impl(const msa_dims_t* dims, const void* q, const voi
                                       block_entries, a, z, (int)x.total_q, scale_log2, part_acc,
                                       part_ml, st);
     }
-    if (e != hipSuccess) return hip_fail(e);
+    if (msa_status_t ls = launched(e, st, K_ATTEND); ls != MSA_OK) return ls;
     {
       ProfScope ps(K_MERGE, st);
       e = msa::launch_merge(x.D, x.compact, part_acc, part_ml, sel, a, z, x.Hq, x.G, x.top_k, out,
                             lse, st);
     }
-    if (e != hipSuccess) return hip_fail(e);
+    if (msa_status_t ls = launched(e, st, K_MERGE); ls != MSA_OK) return ls;
     if (block_mass) {
       ProfScope ps(K_MASS, st);
       e = msa::launch_block_mass(x.hpg, part_ml, sel, a, z, x.G, x.top_k, block_mass, st);
-      if (e != hipSuccess) return hip_fail(e);
+      if (msa_status_t ls = launched(e, st, K_MASS); ls != MSA_OK) return ls;
     }
   }
   return MSA_OK;
@@ -713,7 +774,7 @@ msa_status_t msa_main_quantize_fp8(const msa_dims_t* dims, const void* q, const 
   hipError_t e = msa::launch_main_quantize_fp8(
       x.D, has_q ? q : nullptr, has_k ? k : nullptr, has_v ? v : nullptr, cu_seqlens_k, x.kv,
       dims->batch, x.G, x.nb_max, has_q ? x.total_q * x.Hq : 0, q8, q_exp, k8, k_exp, v8, v_exp, st);
-  return e == hipSuccess ? MSA_OK : hip_fail(e);
+  return launched(e, st, K_QUANT_MAIN_FP8);
 }
 
 msa_status_t msa_main_quantize_q8kv4(const msa_dims_t* dims, const void* q, const void* k,
@@ -739,7 +800,7 @@ msa_status_t msa_main_quantize_q8kv4(const msa_dims_t* dims, const void* q, cons
       x.D, has_q ? q : nullptr, has_k ? k : nullptr, has_v ? v : nullptr, cu_seqlens_k, x.kv,
       dims->batch, x.G, x.nb_max, has_q ? x.total_q * x.Hq : 0, q8, q_exp, k4, k_exp4, v4, v_exp4,
       st);
-  return e == hipSuccess ? MSA_OK : hip_fail(e);
+  return launched(e, st, K_QUANT_MAIN_Q8KV4);
 }
 
 msa_status_t msa_attend_with_mass(const msa_dims_t* dims, const void* q, const void* k,
@@ -773,11 +834,12 @@ msa_status_t msa_index_kl(const msa_dims_t* dims, const void* q_idx, const void*
       !aligned16(block_mass) || !aligned16(kl) || (log_q && !aligned16(log_q)))
     return fail(MSA_ERR_ALIGNMENT, "tensor pointers must be 16-byte aligned");
   hipStream_t st = (hipStream_t)stream;
+  if (msa_status_t v = debug_check_seqlens(dims, cu_seqlens_q, cu_seqlens_k, st); v != MSA_OK) return v;
   ProfScope ps(K_INDEX_KL, st);
   hipError_t e = msa::launch_index_kl(x.DI, q_idx, k_idx, cu_seqlens_q, cu_seqlens_k, x.kv, dims->batch,
                                       x.G, x.top_k, dims->max_q_len, sel, sel_score, block_mass,
                                       log_q, kl, st);
-  return e == hipSuccess ? MSA_OK : hip_fail(e);
+  return launched(e, st, K_INDEX_KL);
 }
 
 msa_status_t msa_hbm_stream(const void* src, size_t read_bytes, int32_t ratio, void* dst,

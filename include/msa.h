@@ -44,6 +44,12 @@
  *   non-decreasing, start at 0, end at total_q / total_k, and agree with
  *   max_q_len / max_k_len and 0 <= Lq_b <= Lk_b; other values are undefined
  *   behaviour (kernels may then access memory outside the buffers).
+ * - Debugging: with the environment variable MSA_DEBUG_SYNC set (to anything
+ *   but "" or "0"; read at every call), each call first copies its
+ *   cu_seqlens to the host and rejects values that break the rules above
+ *   (MSA_ERR_BAD_DIMS, nothing enqueued), and every kernel stage is followed
+ *   by a wait on the stream and an error check whose message names the
+ *   stage (MSA_ERR_HIP).  It blocks the host; not for use under graph capture.
  */
 #ifndef MSA_H_
 #define MSA_H_
