@@ -711,11 +711,13 @@ def run_leg(args):
     per_step = {k_: v["ms_per_step"] for k_, v in stage.items()}
     log("[bench] stages (ms/step): " + ", ".join(f"{k_} {v:.3f}" for k_, v in per_step.items()))
 
-    def traffic_record(name):
+    def traffic_record(name, compact=False):
         """Measured HBM bytes per launch (FETCH_SIZE/WRITE_SIZE scaled by a copy of known
-        size, profiles/<kernel>_<workload>_traffic.json) if the kernel source is unchanged."""
+        size, profiles/<kernel>_<workload>[_compact]_traffic.json) if the kernel source is
+        unchanged."""
         import hashlib
-        path = os.path.join(ROOT, "profiles", f"{name}_{w.name}_traffic.json")
+        path = os.path.join(ROOT, "profiles",
+                            f"{name}_{w.name}{'_compact' if compact else ''}_traffic.json")
         if not os.path.exists(path):
             return None
         rec = json.load(open(path))
@@ -762,7 +764,7 @@ def run_leg(args):
             per_launch = bytes_[name] / n_launch
             a = per_launch / sec
             return dict(bound="hbm", achieved=a / 1e9, peak=PEAK_HBM_BYTES / 1e9, unit="GB/s",
-                        frac=a / PEAK_HBM_BYTES, traffic=None if compact else traffic_record(name),
+                        frac=a / PEAK_HBM_BYTES, traffic=traffic_record(name, compact),
                         traffic_unit="GB per launch (HBM, counters scaled by a copy of known size)",
                         algorithmic_per_launch=per_launch / 1e9)
         return None
