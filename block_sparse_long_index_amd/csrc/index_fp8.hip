@@ -175,7 +175,11 @@ struct KRing8 {
   // issue this wave's loads of the key block whose first row is `blk_base` into `buf`
   __device__ static inline void load(const uint8_t* __restrict__ blk_base, uint8_t* buf,
                                      int wave, int lane) {
-    if (wave >= LOADERS) return;
+    // (only small blocks leave waves idle: a branch where every wave loads
+    // would rejoin before the fragment reads and cost a wait for all loads)
+    if constexpr (INSTR < NW) {
+      if (wave >= LOADERS) return;
+    }
 #pragma unroll
     for (int i = 0; i < PER_WAVE; ++i) {
       const int piece = wave * PER_WAVE + i;
@@ -215,7 +219,13 @@ struct KRing4 {
   static constexpr int ROWS_PER_PIECE = PIECE / RB;
   static constexpr int XB = DI / 32;                              // exponent bytes per key row
   static constexpr int EXP_PER_WAVE = kBlock * XB / NW;
-  static constexpr int BYTES = CODE_BYTES + kBlock * XB;
+  // every lane of a wave issues the exponent load (a branch on the lane would
+  // rejoin before the next fragment reads, and the compiler would then wait
+  // for all the loads in flight): the wave's EXP_PER_WAVE bytes, repeated, fill
+  // a 1 KiB region per wave; rows 32w .. 32w + 31 read theirs from the first
+  // EXP_PER_WAVE bytes of region w
+  static constexpr int EXP_REGION = 1024;
+  static constexpr int BYTES = CODE_BYTES + NW * EXP_REGION;
   static constexpr int LOADS = PER_WAVE + 1;
   static_assert(CODE_BYTES % (PIECE * NW) == 0 && EXP_PER_WAVE % 16 == 0 && PIECE % RB == 0,
                 "block must split evenly over the waves");
@@ -233,9 +243,8 @@ struct KRing4 {
                                          0, 0);
       }
     }
-    if (lane < EXP_PER_WAVE / 16)
-      __builtin_amdgcn_global_load_lds(exps + wave * EXP_PER_WAVE + lane * 16,
-                                       buf + CODE_BYTES + wave * EXP_PER_WAVE, 16, 0, 0);
+    __builtin_amdgcn_global_load_lds(exps + wave * EXP_PER_WAVE + (lane % (EXP_PER_WAVE / 16)) * 16,
+                                     buf + CODE_BYTES + wave * EXP_REGION, 16, 0, 0);
   }
   __device__ static inline int swz(int m) { return (m / R) % CPR; }
   // A fragment of k-step ks for lane half h: elements 64ks + 32h .. +31 of row
@@ -250,7 +259,8 @@ struct KRing4 {
   }
   // the XB exponent bytes of row m, byte j = elements 32j .. 32j+31
   __device__ static inline uint32_t exps(const uint8_t* buf, int m) {
-    const uint8_t* p = buf + CODE_BYTES + m * XB;
+    constexpr int ROWS_PER_WAVE = EXP_PER_WAVE / XB;
+    const uint8_t* p = buf + CODE_BYTES + (m / ROWS_PER_WAVE) * EXP_REGION + (m % ROWS_PER_WAVE) * XB;
     if constexpr (XB == 4) return *reinterpret_cast<const uint32_t*>(p);
     else if constexpr (XB == 2) return *reinterpret_cast<const uint16_t*>(p);
     else return *p;
@@ -299,7 +309,7 @@ struct PrefillKeys<DI, true> {
   static constexpr int EXP_LDS = 1;
 };
 
-template <int DI, int RT, int NW, int KCAP, bool K4>
+template <int DI, int RT, int NW, int KCAP, bool K4, bool PAGED>
 __global__ __launch_bounds__(NW * 64, 2) void index_select_prefill_fp8_kernel(
     const uint8_t* __restrict__ q8, const uint8_t* __restrict__ qe, const uint8_t* __restrict__ k8,
     const uint8_t* __restrict__ ke, const int32_t* __restrict__ cu_q,
@@ -359,27 +369,36 @@ __global__ __launch_bounds__(NW * 64, 2) void index_select_prefill_fp8_kernel(
     }
     __syncthreads();   // exponents visible; every earlier load has landed
 
-    // issue this wave's loads of key block beta into buf
+    // issue this wave's loads of key block beta into buf.  Blocks past the
+    // last earlier one are clamped to it, and every step issues its loads: a
+    // branch around them (or on the page table: PAGED is a template argument)
+    // would rejoin before the next fragment reads, and at such a join the
+    // compiler loses track of which ring buffer the direct loads in flight
+    // write and waits for all of them.
     auto issue = [&](int beta, uint8_t* buf) __attribute__((always_inline)) {
-      const size_t row0 = kv.block_row(b, koff, beta);
+      const int bc = min(beta, beta_hi - 1);
+      const size_t row0 = PAGED ? kv.page(b, bc) * kBlock : (size_t)koff + (size_t)bc * kBlock;
       if constexpr (K4) Ring::load(k8 + row0 * (DI / 2), ke + row0 * (DI / 32), buf, wave, lane);
       else Ring::load(k8 + row0 * DI, buf, wave, lane);
     };
     uint32_t pending = 0;   // previous block's score key, inserted during the next block's MFMAs
     int pending_beta = 0;
+    // blocks 0 and 1, and block 2 (which step 0 loads again): the loop is
+    // entered with loads into all three buffers, as its back edge has them
     issue(0, ring0);
-    if (beta_hi > 1) issue(1, ring1);
+    issue(1, ring1);
+    issue(2, ring2);
 
     auto step = [&](int beta, const uint8_t* rbuf, uint8_t* lbuf) __attribute__((always_inline)) {
       // this wave's pieces of block beta have landed (only beta+1 may be
       // younger); the barrier publishes every wave's pieces and retires the
       // reads of the buffer about to be refilled
-      if (beta + 1 < beta_hi) wait_vmcnt<Keys::LOADS>(); else wait_vmcnt<0>();
+      wait_vmcnt<Keys::LOADS>();   // (waits for one step more in steps 0 and 1)
       __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0)
       asm volatile("" ::: "memory");
       __builtin_amdgcn_s_barrier();
       asm volatile("" ::: "memory");
-      if (beta + 2 < beta_hi) issue(beta + 2, lbuf);
+      issue(beta + 2, lbuf);
 
       // software pipeline: the MFMAs of key tile kt+1 are issued before the
       // row maxima of tile kt are taken, and the previous block's top-k
@@ -420,17 +439,23 @@ __global__ __launch_bounds__(NW * 64, 2) void index_select_prefill_fp8_kernel(
 #pragma unroll
         for (int i = 0; i < 16; ++i) rmax[rt] = fmaxf(rmax[rt], acc[1][rt][i]);
       const float mine = row_tile_max<RT>(rmax, half);
-      const float score = ldexpf(mine, eq_own + (K4 ? 0 : (int)kexp[beta] - 127));
+      const float score = ldexpf(mine, eq_own + (K4 ? 0 : (int)kexp[min(beta, beta_hi - 1)] - 127));
       // key 0 is never inserted
       pending = (beta < beta_own && score == score) ? float_order_key(score) : 0u;
       pending_beta = beta;
     };
 
+    // Whole trips of three steps, none of them conditional (a conditional step
+    // lets the compiler merge the steps' load code, and it then no longer
+    // knows which buffer the loads write).  Steps past the last earlier block
+    // score a reloaded copy of it and insert nothing: their beta is at or
+    // above every row's own block.
     for (int beta = 0; beta < beta_hi; beta += 3) {
       step(beta, ring0, ring2);
-      if (beta + 1 < beta_hi) step(beta + 1, ring1, ring0);
-      if (beta + 2 < beta_hi) step(beta + 2, ring2, ring1);
+      step(beta + 1, ring1, ring0);
+      step(beta + 2, ring2, ring1);
     }
+    wait_vmcnt<0>();   // no direct load may still write LDS when the workgroup ends
     list.insert(pending, pending_beta);
   }
   if (own_valid) {
@@ -740,9 +765,14 @@ static hipError_t launch_prefill8_t(const void* q8, const uint8_t* qe, const voi
   const int qt = kFp8Rows / G;
   if (qt < 1) return hipErrorInvalidValue;
   dim3 grid((max_q_len + qt - 1) / qt, batch);
-  hipLaunchKernelGGL((index_select_prefill_fp8_kernel<DI, kFp8RT, kFp8NW, KCAP, K4>), grid,
-                     dim3(kFp8NW * 64), 0, st, (const uint8_t*)q8, qe, (const uint8_t*)k8, ke, cu_q,
-                     cu_k, kv, G, nb_max, qt, top_k, sel, sel_score);
+  if (kv.table)
+    hipLaunchKernelGGL((index_select_prefill_fp8_kernel<DI, kFp8RT, kFp8NW, KCAP, K4, true>), grid,
+                       dim3(kFp8NW * 64), 0, st, (const uint8_t*)q8, qe, (const uint8_t*)k8, ke, cu_q,
+                       cu_k, kv, G, nb_max, qt, top_k, sel, sel_score);
+  else
+    hipLaunchKernelGGL((index_select_prefill_fp8_kernel<DI, kFp8RT, kFp8NW, KCAP, K4, false>), grid,
+                       dim3(kFp8NW * 64), 0, st, (const uint8_t*)q8, qe, (const uint8_t*)k8, ke, cu_q,
+                       cu_k, kv, G, nb_max, qt, top_k, sel, sel_score);
   return hipGetLastError();
 }
 

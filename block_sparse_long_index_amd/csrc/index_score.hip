@@ -132,7 +132,7 @@ struct KRing {
   }
 };
 
-template <int DI, int RT, int NW, int KCAP>
+template <int DI, int RT, int NW, int KCAP, bool PAGED>
 __global__ __launch_bounds__(NW * 64) void index_select_prefill_kernel(
     const uint16_t* __restrict__ q_idx, const uint16_t* __restrict__ k_idx,
     const int32_t* __restrict__ cu_q, const int32_t* __restrict__ cu_k, KvMap kv, int G, int qt,
@@ -189,13 +189,24 @@ __global__ __launch_bounds__(NW * 64) void index_select_prefill_kernel(
       }
     }
 
+    // (PAGED is a template argument: a branch on the table here would join
+    // right before the next fragment reads, and at such a join the compiler
+    // loses track of which ring buffer the direct loads in flight write, so
+    // it waits for all of them)
     auto blk = [&](int beta) __attribute__((always_inline)) {
-      return k_idx + kv.block_row(b, koff, beta) * DI;
+      const size_t row0 = PAGED ? kv.page(b, beta) * kBlock : (size_t)koff + (size_t)beta * kBlock;
+      return k_idx + row0 * DI;
     };
     uint32_t pending = 0;   // previous block's score key, inserted during the next block's MFMAs
     int pending_beta = 0;
+    // blocks 0 and 1, and block 2 (which step 0 loads again): every step
+    // issues its loads, clamped to the last block past the end (a branch
+    // around them would rejoin before the next fragment reads, and there the
+    // compiler would wait for every load in flight), and the loop is entered
+    // with loads into all three buffers, as its back edge has them
     Ring::load(blk(0), ring0, wave, lane);
-    if (beta_hi > 1) Ring::load(blk(1), ring1, wave, lane);
+    Ring::load(blk(min(1, beta_hi - 1)), ring1, wave, lane);
+    Ring::load(blk(min(2, beta_hi - 1)), ring2, wave, lane);
 
     // score block beta from `rbuf`; first start loading block beta+2 into `lbuf`
     auto step = [&](int beta, const uint16_t* rbuf, uint16_t* lbuf) __attribute__((always_inline)) {
@@ -203,12 +214,12 @@ __global__ __launch_bounds__(NW * 64) void index_select_prefill_kernel(
       // younger); the barrier makes every wave's pieces visible and retires
       // the buffer read in the previous step (a plain __syncthreads would also
       // drain the younger block's loads)
-      if (beta + 1 < beta_hi) wait_vmcnt<Ring::PER_WAVE>(); else wait_vmcnt<0>();
+      wait_vmcnt<Ring::PER_WAVE>();   // (waits for one step more in steps 0 and 1)
       __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0): this wave's LDS reads are done
       asm volatile("" ::: "memory");
       __builtin_amdgcn_s_barrier();
       asm volatile("" ::: "memory");
-      if (beta + 2 < beta_hi) Ring::load(blk(beta + 2), lbuf, wave, lane);
+      Ring::load(blk(min(beta + 2, beta_hi - 1)), lbuf, wave, lane);
 
       // the previous block's top-k insert runs while this block's first
       // fragments load
@@ -258,11 +269,17 @@ __global__ __launch_bounds__(NW * 64) void index_select_prefill_kernel(
       pending_beta = beta;
     };
 
+    // Whole trips of three steps, none of them conditional (a conditional step
+    // lets the compiler merge the steps' load code, and it then no longer
+    // knows which buffer the loads write).  Steps past the last earlier block
+    // score a reloaded copy of it and insert nothing: their beta is at or
+    // above every row's own block.
     for (int beta = 0; beta < beta_hi; beta += 3) {
       step(beta, ring0, ring2);
-      if (beta + 1 < beta_hi) step(beta + 1, ring1, ring0);
-      if (beta + 2 < beta_hi) step(beta + 2, ring2, ring1);
+      step(beta + 1, ring1, ring0);
+      step(beta + 2, ring2, ring1);
     }
+    wait_vmcnt<0>();   // no direct load may still write LDS when the workgroup ends
     list.insert(pending, pending_beta);
   }
   if (own_valid) {
@@ -398,9 +415,14 @@ static hipError_t launch_prefill_t(const void* q_idx, const void* k_idx, const i
   const int qt = kPrefillRows / G;
   if (qt < 1) return hipErrorInvalidValue;
   dim3 grid((max_q_len + qt - 1) / qt, batch);
-  hipLaunchKernelGGL((index_select_prefill_kernel<DI, kPrefillRT, kPrefillNW, KCAP>), grid,
-                     dim3(kPrefillNW * 64), 0, st, (const uint16_t*)q_idx, (const uint16_t*)k_idx,
-                     cu_q, cu_k, kv, G, qt, top_k, sel, sel_score);
+  if (kv.table)
+    hipLaunchKernelGGL((index_select_prefill_kernel<DI, kPrefillRT, kPrefillNW, KCAP, true>), grid,
+                       dim3(kPrefillNW * 64), 0, st, (const uint16_t*)q_idx, (const uint16_t*)k_idx,
+                       cu_q, cu_k, kv, G, qt, top_k, sel, sel_score);
+  else
+    hipLaunchKernelGGL((index_select_prefill_kernel<DI, kPrefillRT, kPrefillNW, KCAP, false>), grid,
+                       dim3(kPrefillNW * 64), 0, st, (const uint16_t*)q_idx, (const uint16_t*)k_idx,
+                       cu_q, cu_k, kv, G, qt, top_k, sel, sel_score);
   return hipGetLastError();
 }
 
