@@ -375,9 +375,14 @@ __global__ __launch_bounds__(NW * 64, 2) void index_select_prefill_fp8_kernel(
     // would rejoin before the next fragment reads, and at such a join the
     // compiler loses track of which ring buffer the direct loads in flight
     // write and waits for all of them.
-    auto issue = [&](int beta, uint8_t* buf) __attribute__((always_inline)) {
+    // A page is read one step before its block's loads are issued, and
+    // before the loads of the block in between: the wait for it then covers
+    // no younger ring load.
+    auto row_of = [&](int beta) __attribute__((always_inline)) {
       const int bc = min(beta, beta_hi - 1);
-      const size_t row0 = PAGED ? kv.page(b, bc) * kBlock : (size_t)koff + (size_t)bc * kBlock;
+      return PAGED ? kv.page_uniform(b, bc) * kBlock : (size_t)koff + (size_t)bc * kBlock;
+    };
+    auto issue = [&](size_t row0, uint8_t* buf) __attribute__((always_inline)) {
       if constexpr (K4) Ring::load(k8 + row0 * (DI / 2), ke + row0 * (DI / 32), buf, wave, lane);
       else Ring::load(k8 + row0 * DI, buf, wave, lane);
     };
@@ -385,9 +390,10 @@ __global__ __launch_bounds__(NW * 64, 2) void index_select_prefill_fp8_kernel(
     int pending_beta = 0;
     // blocks 0 and 1, and block 2 (which step 0 loads again): the loop is
     // entered with loads into all three buffers, as its back edge has them
-    issue(0, ring0);
-    issue(1, ring1);
-    issue(2, ring2);
+    size_t next_row = row_of(2);   // the block step `beta` loads: beta + 2
+    issue(row_of(0), ring0);
+    issue(row_of(1), ring1);
+    issue(next_row, ring2);
 
     auto step = [&](int beta, const uint8_t* rbuf, uint8_t* lbuf) __attribute__((always_inline)) {
       // this wave's pieces of block beta have landed (only beta+1 may be
@@ -398,7 +404,9 @@ __global__ __launch_bounds__(NW * 64, 2) void index_select_prefill_fp8_kernel(
       asm volatile("" ::: "memory");
       __builtin_amdgcn_s_barrier();
       asm volatile("" ::: "memory");
-      issue(beta + 2, lbuf);
+      const size_t row2 = next_row;
+      next_row = row_of(beta + 3);
+      issue(row2, lbuf);
 
       // software pipeline: the MFMAs of key tile kt+1 are issued before the
       // row maxima of tile kt are taken, and the previous block's top-k

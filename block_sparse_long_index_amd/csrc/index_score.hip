@@ -189,13 +189,16 @@ __global__ __launch_bounds__(NW * 64) void index_select_prefill_kernel(
       }
     }
 
-    // (PAGED is a template argument: a branch on the table here would join
-    // right before the next fragment reads, and at such a join the compiler
-    // loses track of which ring buffer the direct loads in flight write, so
-    // it waits for all of them)
-    auto blk = [&](int beta) __attribute__((always_inline)) {
-      const size_t row0 = PAGED ? kv.page(b, beta) * kBlock : (size_t)koff + (size_t)beta * kBlock;
-      return k_idx + row0 * DI;
+    // First row of key block beta, clamped to the last earlier block.  PAGED
+    // is a template argument: a branch on the table here would join right
+    // before the next fragment reads, and at such a join the compiler loses
+    // track of which ring buffer the direct loads in flight write, so it
+    // waits for all of them.  A page is read one step before its block's
+    // loads are issued, and before the loads of the block in between: the
+    // wait for it then covers no younger ring load.
+    auto row_of = [&](int beta) __attribute__((always_inline)) {
+      const int bc = min(beta, beta_hi - 1);
+      return PAGED ? kv.page_uniform(b, bc) * kBlock : (size_t)koff + (size_t)bc * kBlock;
     };
     uint32_t pending = 0;   // previous block's score key, inserted during the next block's MFMAs
     int pending_beta = 0;
@@ -204,9 +207,10 @@ __global__ __launch_bounds__(NW * 64) void index_select_prefill_kernel(
     // around them would rejoin before the next fragment reads, and there the
     // compiler would wait for every load in flight), and the loop is entered
     // with loads into all three buffers, as its back edge has them
-    Ring::load(blk(0), ring0, wave, lane);
-    Ring::load(blk(min(1, beta_hi - 1)), ring1, wave, lane);
-    Ring::load(blk(min(2, beta_hi - 1)), ring2, wave, lane);
+    size_t next_row = row_of(2);   // the block step `beta` loads: beta + 2
+    Ring::load(k_idx + row_of(0) * DI, ring0, wave, lane);
+    Ring::load(k_idx + row_of(1) * DI, ring1, wave, lane);
+    Ring::load(k_idx + next_row * DI, ring2, wave, lane);
 
     // score block beta from `rbuf`; first start loading block beta+2 into `lbuf`
     auto step = [&](int beta, const uint16_t* rbuf, uint16_t* lbuf) __attribute__((always_inline)) {
@@ -219,7 +223,9 @@ __global__ __launch_bounds__(NW * 64) void index_select_prefill_kernel(
       asm volatile("" ::: "memory");
       __builtin_amdgcn_s_barrier();
       asm volatile("" ::: "memory");
-      Ring::load(blk(min(beta + 2, beta_hi - 1)), lbuf, wave, lane);
+      const size_t row2 = next_row;
+      next_row = row_of(beta + 3);
+      Ring::load(k_idx + row2 * DI, lbuf, wave, lane);
 
       // the previous block's top-k insert runs while this block's first
       // fragments load

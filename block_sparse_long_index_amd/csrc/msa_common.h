@@ -51,6 +51,16 @@ struct KvMap {
     const int pg = table[(size_t)b * max_blocks + min(max(beta, 0), max_blocks - 1)];
     return (size_t)min(max(pg, 0), pages - 1);
   }
+  // the same page through the scalar cache (a read-only view of the table,
+  // which no kernel writes): the load is counted by lgkmcnt, so waiting for
+  // it never waits for vector loads in flight (b and beta wave-uniform)
+  __device__ inline size_t page_uniform(int b, int beta) const {
+    typedef const __attribute__((address_space(4))) int32_t ctable_t;
+    ctable_t* t = (ctable_t*)table;
+    const int j = __builtin_amdgcn_readfirstlane(b * max_blocks + min(max(beta, 0), max_blocks - 1));
+    const int pg = t[j];
+    return (size_t)min(max(pg, 0), pages - 1);
+  }
   // first row of block beta of sequence b (koff = cu_k[b])
   __device__ inline size_t block_row(int b, int koff, int beta) const {
     return table ? page(b, beta) * 128u : (size_t)koff + (size_t)beta * 128u;
