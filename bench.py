@@ -384,6 +384,17 @@ def parity_on_rows(P, rows, ref, sel_gpu, out_gpu, lse_gpu, top_k, fp8=False):
 
 
 # ---------------------------------------------------------------------------
+def source_code_hash(path: str) -> str:
+    """sha256 of a kernel source with its comments and whitespace removed: a
+    traffic record stays valid while the code it was measured on is unchanged."""
+    import hashlib
+    import re
+    text = open(path, encoding="utf-8").read()
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return hashlib.sha256(" ".join(text.split()).encode()).hexdigest()
+
+
 def parse_args(argv=None):
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -713,17 +724,15 @@ def run_leg(args):
 
     def traffic_record(name, compact=False):
         """Measured HBM bytes per launch (FETCH_SIZE/WRITE_SIZE scaled by a copy of known
-        size, profiles/<kernel>_<workload>[_compact]_traffic.json) if the kernel source is
+        size, profiles/<kernel>_<workload>[_compact]_traffic.json) if the kernel code is
         unchanged."""
-        import hashlib
         path = os.path.join(ROOT, "profiles",
                             f"{name}_{w.name}{'_compact' if compact else ''}_traffic.json")
         if not os.path.exists(path):
             return None
         rec = json.load(open(path))
-        src = open(os.path.join(ROOT, rec["source"]), "rb").read()
-        if hashlib.sha256(src).hexdigest() != rec["source_sha256"] or args.q_chunk or \
-                args.main != "bf16" or args.paged:
+        if source_code_hash(os.path.join(ROOT, rec["source"])) != rec.get("source_code_sha256") or \
+                args.q_chunk or args.main != "bf16" or args.paged:
             return None
         return rec["per_dispatch"]["total_bytes"] / 1e9
 
@@ -785,10 +794,8 @@ def run_leg(args):
     rec_name = "attend_blocks"
     rec_path = os.path.join(ROOT, "profiles", f"{rec_name}_{w.name}_traffic.json")
     if os.path.exists(rec_path) and args.main == "bf16" and not args.paged and not args.q_chunk:
-        import hashlib
         rec = json.load(open(rec_path))
-        src = open(os.path.join(ROOT, rec["source"]), "rb").read()
-        if hashlib.sha256(src).hexdigest() == rec["source_sha256"]:
+        if source_code_hash(os.path.join(ROOT, rec["source"])) == rec.get("source_code_sha256"):
             n_disp = stage.get("attend_blocks", {}).get("launches_per_step", 0)
             fetch = rec["per_dispatch"]["read_gb"] * 1e9 * n_disp
             hpg = w.num_q_heads // w.num_kv_heads

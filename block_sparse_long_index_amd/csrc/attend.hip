@@ -496,9 +496,8 @@ __global__ __launch_bounds__(kMergeWaves * 64) void merge_partials_kernel(
     if (s < ns) {
       const size_t row = base + (size_t)s * hpg;
       ml[s] = part_ml[row];
-      // non-temporal: each partial is read once (at 128K this kernel took
-      // 6.0 instead of 6.8-6.9 ms per launch with fp32 partials and 6.15
-      // instead of 6.7 with compact ones; at 1M the same within 3%)
+      // non-temporal: each partial is read once (measured against ordinary
+      // loads on the same buffers: within 1% either way)
       typedef unsigned v4u_nt __attribute__((ext_vector_type(4)));
       const v4u_nt* src = COMPACT
           ? reinterpret_cast<const v4u_nt*>(static_cast<const uint16_t*>(part_acc) + row * D + c * VPL)
