@@ -9,10 +9,18 @@
 // one token: its 4-feature runs go straight to that token's q_idx row or, for
 // the key head, to the key row the token occupies in its sequence.
 //
-// Workgroup tile: 128 features x 256 tokens, 4 waves of 128 x 64; K in steps
-// of 32 through a three-stage LDS ring filled by direct global->LDS loads two
-// steps ahead.  Tile order is XCD-aware: the feature tiles of one token tile
-// run on one XCD, so each x tile is fetched into one L2 and reused there.
+// Workgroup tile: 128 features x 512 tokens, one wave per SIMD, each wave a
+// 128 x 128 register tile (16 MFMA tiles, 256 accumulators), so every
+// fragment read from LDS feeds four MFMAs.  K runs in stages of 32: the
+// weight tile and each wave's own 128 token rows go through a four-stage LDS
+// ring (160 KiB: all of a CU's LDS) filled by direct global->LDS loads.
+// The barrier sits in the middle of a stage, so no fragment read is ever
+// waited for right away: a stage issues its second half's reads, runs its
+// first half's 16 MFMAs, waits for the next stage's loads and passes the
+// barrier, refills its own buffer, issues the next stage's first-half reads
+// and runs its second half's MFMAs.
+// Tile order is XCD-aware: the feature tiles of one token tile run on one
+// XCD, so each x tile is fetched into one L2 and reused there.
 #include <algorithm>
 
 #include "msa_common.h"
@@ -20,8 +28,8 @@
 namespace msa {
 
 constexpr int kProjBF = 128;   // features per workgroup tile
-constexpr int kProjBT = 256;   // tokens per workgroup tile
-constexpr int kProjBK = 32;    // K per step
+constexpr int kProjBT = 512;   // tokens per workgroup tile (128 per wave)
+constexpr int kProjBK = 32;    // K per stage
 constexpr int kProjNW = 4;
 
 // Rows of 32 bf16 (64 bytes, 4 chunks of 16 bytes); 4 rows share a 256-byte
@@ -29,17 +37,31 @@ constexpr int kProjNW = 4;
 // fragment read serves at once land in 16 different 16-byte bank groups.
 __device__ inline int proj_swz(int m) { return (m >> 2) & 3; }
 
-__global__ __launch_bounds__(kProjNW * 64, 2) void index_project_kernel(
+// vmcnt(n) for n < 64 (gfx9 encoding: low four bits and bits 14-15)
+template <int N>
+__device__ inline void wait_vmcnt_wide() {
+  static_assert(N >= 0 && N < 64, "vmcnt is six bits");
+  __builtin_amdgcn_s_waitcnt((N >> 4) << 14 | 0x0F70 | (N & 15));
+}
+
+// the fragments of one half-stage (16 of the stage's 32 K): 4 weight tiles
+// and 4 token tiles of 32 rows
+struct ProjFrags {
+  bf16x8 a[4], b[4];
+};
+
+__global__ __launch_bounds__(kProjNW * 64, 1) void index_project_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ wq,
     const uint16_t* __restrict__ wk, int D, int GD, int F, int T, int n_ft, int n_tiles,
     const int32_t* __restrict__ cu_q, const int32_t* __restrict__ cu_k, KvMap kv, int batch, int DI,
     uint16_t* __restrict__ q_idx, uint16_t* __restrict__ k_idx) {
-  __shared__ __attribute__((aligned(1024))) uint16_t a0[kProjBF * kProjBK];
-  __shared__ __attribute__((aligned(1024))) uint16_t a1[kProjBF * kProjBK];
-  __shared__ __attribute__((aligned(1024))) uint16_t a2[kProjBF * kProjBK];
-  __shared__ __attribute__((aligned(1024))) uint16_t b0[kProjBT * kProjBK];
-  __shared__ __attribute__((aligned(1024))) uint16_t b1[kProjBT * kProjBK];
-  __shared__ __attribute__((aligned(1024))) uint16_t b2[kProjBT * kProjBK];
+  // one array per stage: the weight tile [128 rows][32 elements], then the
+  // token rows [wave][128 rows][32 elements]
+  constexpr int kStageElems = (kProjBF + kProjBT) * kProjBK;
+  __shared__ __attribute__((aligned(1024))) uint16_t s0[kStageElems];
+  __shared__ __attribute__((aligned(1024))) uint16_t s1[kStageElems];
+  __shared__ __attribute__((aligned(1024))) uint16_t s2[kStageElems];
+  __shared__ __attribute__((aligned(1024))) uint16_t s3[kStageElems];
 
   // XCD-aware tile order: workgroups are dealt to the 8 XCDs round-robin, so
   // block b runs on XCD b % 8; give each XCD a contiguous run of logical tiles
@@ -56,12 +78,11 @@ __global__ __launch_bounds__(kProjNW * 64, 2) void index_project_kernel(
   const int col = lane & 31;
   const int half = lane >> 5;
 
-  // this lane's source rows for its 6 pieces per stage (2 of the weight tile,
-  // 4 of the token tile); rows past the end are clamped (never stored)
+  // weight tile: 8 pieces of 16 rows per stage, 2 per wave; rows past F are
+  // clamped (their outputs are never stored)
   const int prow = lane >> 2;                        // row within a 16-row piece
   const uint16_t* asrc[2];
-  const uint16_t* bsrc[4];
-  int apos[2], bpos[4];
+  int apos[2];
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
     const int m = (wave * 2 + i) * 16 + prow;
@@ -70,81 +91,131 @@ __global__ __launch_bounds__(kProjNW * 64, 2) void index_project_kernel(
     asrc[i] = (f < GD ? wq + (size_t)f * D : wk + (size_t)(f - GD) * D) + lc * 8;
     apos[i] = (wave * 2 + i) * 512;                  // bf16 elements: 1 KiB pieces
   }
+  // this wave's token rows: 8 pieces of 16 rows per stage, laid out as the
+  // weight tile; rows past T are clamped (never stored)
+  const uint16_t* bsrc[8];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int m = (wave * 4 + i) * 16 + prow;
-    const int t = min(t0 + m, T - 1);
-    const int lc = (lane & 3) ^ proj_swz(m);
-    bsrc[i] = x + (size_t)t * D + lc * 8;
-    bpos[i] = (wave * 4 + i) * 512;
+  for (int i = 0; i < 8; ++i) {
+    const int m = i * 16 + prow;
+    const int t = min(t0 + wave * 128 + m, T - 1);
+    bsrc[i] = x + (size_t)t * D + ((lane & 3) ^ proj_swz(m)) * 8;
   }
-  auto load = [&](int ks, uint16_t* sa, uint16_t* sb) __attribute__((always_inline)) {
-    const int k0 = ks * kProjBK;
+  const int bbase = kProjBF * kProjBK + wave * 128 * kProjBK;
+  const int nk = D / kProjBK;                        // >= 2 and even (D is a multiple of 64)
+  // stage s of K into buf; a stage past the last is clamped to it (the copy
+  // lands in a buffer no stage reads), so every stage issues the same loads
+  // and the loop has no branch.  After a branch joins, the compiler can no
+  // longer tell which buffer a direct load in flight writes and waits for all
+  // of them before the next LDS read, which would drain the prefetch.
+  auto load = [&](int s, uint16_t* buf) __attribute__((always_inline)) {
+    const int k0 = min(s, nk - 1) * kProjBK;
 #pragma unroll
-    for (int i = 0; i < 2; ++i) __builtin_amdgcn_global_load_lds(asrc[i] + k0, sa + apos[i], 16, 0, 0);
+    for (int i = 0; i < 2; ++i) __builtin_amdgcn_global_load_lds(asrc[i] + k0, buf + apos[i], 16, 0, 0);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) __builtin_amdgcn_global_load_lds(bsrc[i] + k0, sb + bpos[i], 16, 0, 0);
+    for (int i = 0; i < 8; ++i)
+      __builtin_amdgcn_global_load_lds(bsrc[i] + k0, buf + bbase + i * 512, 16, 0, 0);
   };
-  auto frag = [&](const uint16_t* s, int m, int lc) __attribute__((always_inline)) {
-    return as_bf16x8(*reinterpret_cast<const uint4*>(s + m * kProjBK + ((lc ^ proj_swz(m)) * 8)));
+  auto frag = [&](const uint16_t* buf, int m, int c) __attribute__((always_inline)) {
+    return as_bf16x8(*reinterpret_cast<const uint4*>(buf + m * kProjBK + ((c ^ proj_swz(m)) * 8)));
+  };
+  // half u of a stage: K elements 16u .. 16u + 15, lane half h holding 8h .. 8h + 7
+  auto read = [&](const uint16_t* buf, int u, ProjFrags& f) __attribute__((always_inline)) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) f.b[j] = frag(buf + bbase, j * 32 + col, 2 * u + half);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) f.a[i] = frag(buf, i * 32 + col, 2 * u + half);
   };
 
-  f32x16 acc[4][2];
+  f32x16 acc[4][4];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j) acc[i][j] = f32x16{};
-
-  const int nk = D / kProjBK;
-  load(0, a0, b0);
-  if (nk > 1) load(1, a1, b1);
-
-  auto step = [&](int ks, const uint16_t* ra, const uint16_t* rb, uint16_t* la, uint16_t* lb)
-      __attribute__((always_inline)) {
-    // this wave's pieces of step ks have landed (only step ks+1 may be younger);
-    // the barrier publishes every wave's pieces and retires the reads of the
-    // stage about to be refilled
-    if (ks + 1 < nk) wait_vmcnt<6>(); else wait_vmcnt<0>();
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x16{};
+  auto mfmas = [&](const ProjFrags& f) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[i][j] = mfma32(f.a[i], f.b[j], acc[i][j]);
+  };
+  auto sync = [&]() __attribute__((always_inline)) {
     __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0)
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
-    if (ks + 2 < nk) load(ks + 2, la, lb);
-#pragma unroll
-    for (int kk = 0; kk < kProjBK / 16; ++kk) {
-      bf16x8 fa[4], fb[2];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) fa[i] = frag(ra, i * 32 + col, 2 * kk + half);
-#pragma unroll
-      for (int j = 0; j < 2; ++j) fb[j] = frag(rb, wave * 64 + j * 32 + col, 2 * kk + half);
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 2; ++j) acc[i][j] = mfma32(fa[i], fb[j], acc[i][j]);
-    }
   };
-  for (int ks = 0; ks < nk; ks += 3) {
-    step(ks, a0, b0, a2, b2);
-    if (ks + 1 < nk) step(ks + 1, a1, b1, a0, b0);
-    if (ks + 2 < nk) step(ks + 2, a2, b2, a1, b1);
-  }
 
-  // epilogue: lane <-> token; register 4j..4j+3 of tile i <-> features
-  // f0 + 32i + 8j + 4half + 0..3, written as one 8-byte run
+  // prologue: stages 0 .. 3 in flight, stage 0 published, its first half read
+  ProjFrags fa;
+  load(0, s0);
+  load(1, s1);
+  load(2, s2);
+  load(3, s3);
+  wait_vmcnt_wide<30>();
+  sync();
+  read(s0, 0, fa);
+
+  // a half-stage's 16 MFMAs with the 8 fragment reads of the next half
+  // between its first 9, one at a time: a burst of reads fills the LDS
+  // command queue and holds up the MFMAs behind it.  Each half starts with an
+  // MFMA, so the wait the compiler puts before it covers only fragments read
+  // a half-stage earlier.
+  auto interleave = [&]() __attribute__((always_inline)) {
 #pragma unroll
-  for (int j2 = 0; j2 < 2; ++j2) {
-    const int t = t0 + wave * 64 + j2 * 32 + col;
+    for (int r = 0; r < 8; ++r) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // an MFMA
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // a fragment read
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);     // the other 8 MFMAs
+  };
+
+  // stage s: buffer rb holds it, nb the next; fa holds its first half
+  auto stage = [&](int s, uint16_t* rb, const uint16_t* nb) __attribute__((always_inline)) {
+    ProjFrags fb;
+    read(rb, 1, fb);
+    mfmas(fa);
+    interleave();
+    __builtin_amdgcn_sched_barrier(0);   // none of them may sink past the barrier
+    // stage s + 1 has landed (stages s + 2 and s + 3, 10 loads each, may be
+    // younger) and this wave's reads of stage s are done; the barrier
+    // publishes every wave's pieces of stage s + 1 and frees rb for stage s + 4
+    wait_vmcnt_wide<20>();
+    sync();
+    load(s + 4, rb);
+    read(nb, 0, fa);
+    mfmas(fb);
+    interleave();
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  int s = 0;
+  for (; s + 4 <= nk; s += 4) {
+    stage(s, s0, s1);
+    stage(s + 1, s1, s2);
+    stage(s + 2, s2, s3);
+    stage(s + 3, s3, s0);
+  }
+  if (s < nk) {   // nk % 4 == 2
+    stage(s, s0, s1);
+    stage(s + 1, s1, s2);
+  }
+  wait_vmcnt_wide<0>();   // no direct load may still write LDS when the workgroup ends
+
+  // epilogue: lane <-> token; register 4r..4r+3 of tile (i, j) <-> features
+  // f0 + 32i + 8r + 4half + 0..3 of token t0 + 128 wave + 32 j + col, written
+  // as one 8-byte run
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int t = t0 + wave * 128 + j * 32 + col;
     if (t >= T) continue;
     const RowPos rp = locate_row(t, cu_q, cu_k, batch);
     const size_t krow = kv.key_row(rp.b, rp.koff, rp.p);
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int f = f0 + 32 * i + 8 * j + 4 * half;
+      for (int r = 0; r < 4; ++r) {
+        const int f = f0 + 32 * i + 8 * r + 4 * half;
         if (f >= F) continue;
-        const uint2 v = make_uint2(pack2_bf16(acc[i][j2][4 * j], acc[i][j2][4 * j + 1]),
-                                   pack2_bf16(acc[i][j2][4 * j + 2], acc[i][j2][4 * j + 3]));
+        const uint2 v = make_uint2(pack2_bf16(acc[i][j][4 * r], acc[i][j][4 * r + 1]),
+                                   pack2_bf16(acc[i][j][4 * r + 2], acc[i][j][4 * r + 3]));
         uint16_t* dst = f < GD ? q_idx + (size_t)t * GD + f : k_idx + krow * DI + (f - GD);
         *reinterpret_cast<uint2*>(dst) = v;
       }
