@@ -50,11 +50,16 @@ struct ProjFrags {
   bf16x8 a[4], b[4];
 };
 
+// PART: the workgroup sums one slice of K (kps stages; the last slice may be
+// shorter) and stores its fp32 tile to part [slice][T][F], which
+// index_project_reduce_kernel adds up; otherwise it sums all of K and stores
+// the bf16 outputs.
+template <bool PART>
 __global__ __launch_bounds__(kProjNW * 64, 1) void index_project_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ wq,
-    const uint16_t* __restrict__ wk, int D, int GD, int F, int T, int n_ft, int n_tiles,
-    const int32_t* __restrict__ cu_q, const int32_t* __restrict__ cu_k, KvMap kv, int batch, int DI,
-    uint16_t* __restrict__ q_idx, uint16_t* __restrict__ k_idx) {
+    const uint16_t* __restrict__ wk, int D, int GD, int F, int T, int n_ft, int n_tt, int n_tiles,
+    int kps, const int32_t* __restrict__ cu_q, const int32_t* __restrict__ cu_k, KvMap kv, int batch,
+    int DI, uint16_t* __restrict__ q_idx, uint16_t* __restrict__ k_idx, float* __restrict__ part) {
   // one array per stage: the weight tile [128 rows][32 elements], then the
   // token rows [wave][128 rows][32 elements]
   constexpr int kStageElems = (kProjBF + kProjBT) * kProjBK;
@@ -69,7 +74,8 @@ __global__ __launch_bounds__(kProjNW * 64, 1) void index_project_kernel(
   const int xcd = bid & 7, slot = bid >> 3;
   const int per = n_tiles >> 3, rem = n_tiles & 7;
   const int logical = (xcd < rem ? xcd * (per + 1) : rem * (per + 1) + (xcd - rem) * per) + slot;
-  const int ft = logical % n_ft, tt = logical / n_ft;
+  const int ft = logical % n_ft, rest = logical / n_ft;
+  const int tt = rest % n_tt, slice = rest / n_tt;
   const int f0 = ft * kProjBF, t0 = tt * kProjBT;
 
   const int tid = threadIdx.x;
@@ -101,14 +107,17 @@ __global__ __launch_bounds__(kProjNW * 64, 1) void index_project_kernel(
     bsrc[i] = x + (size_t)t * D + ((lane & 3) ^ proj_swz(m)) * 8;
   }
   const int bbase = kProjBF * kProjBK + wave * 128 * kProjBK;
-  const int nk = D / kProjBK;                        // >= 2 and even (D is a multiple of 64)
+  // this workgroup's stages of K: kps per slice, kps and D / kProjBK even, so
+  // every slice has an even count >= 2
+  const int kb = slice * kps;
+  const int nk = min(kps, D / kProjBK - kb);
   // stage s of K into buf; a stage past the last is clamped to it (the copy
   // lands in a buffer no stage reads), so every stage issues the same loads
   // and the loop has no branch.  After a branch joins, the compiler can no
   // longer tell which buffer a direct load in flight writes and waits for all
   // of them before the next LDS read, which would drain the prefetch.
   auto load = [&](int s, uint16_t* buf) __attribute__((always_inline)) {
-    const int k0 = min(s, nk - 1) * kProjBK;
+    const int k0 = (kb + min(s, nk - 1)) * kProjBK;
 #pragma unroll
     for (int i = 0; i < 2; ++i) __builtin_amdgcn_global_load_lds(asrc[i] + k0, buf + apos[i], 16, 0, 0);
 #pragma unroll
@@ -201,11 +210,24 @@ __global__ __launch_bounds__(kProjNW * 64, 1) void index_project_kernel(
 
   // epilogue: lane <-> token; register 4r..4r+3 of tile (i, j) <-> features
   // f0 + 32i + 8r + 4half + 0..3 of token t0 + 128 wave + 32 j + col, written
-  // as one 8-byte run
+  // as one 8-byte bf16 run (or one 16-byte fp32 run of the slice's tile)
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int t = t0 + wave * 128 + j * 32 + col;
     if (t >= T) continue;
+    if constexpr (PART) {
+      float* dst = part + ((size_t)slice * T + t) * F;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int f = f0 + 32 * i + 8 * r + 4 * half;
+          if (f < F)
+            *reinterpret_cast<float4*>(dst + f) =
+                make_float4(acc[i][j][4 * r], acc[i][j][4 * r + 1], acc[i][j][4 * r + 2], acc[i][j][4 * r + 3]);
+        }
+      continue;
+    }
     const RowPos rp = locate_row(t, cu_q, cu_k, batch);
     const size_t krow = kv.key_row(rp.b, rp.koff, rp.p);
 #pragma unroll
@@ -251,10 +273,43 @@ static int project_split(int T, int F, int C) {
   return (int)std::max(1ll, std::min(want, cap));
 }
 
+// Up to a few thousand tokens the large-tile kernel has fewer tiles than the
+// GPU has CUs (one large-tile workgroup fits a CU), and its time is one
+// workgroup's walk over all of K.  Then K is split into slices as well, as
+// many as keep every workgroup in one round, each of at least 16 stages (512
+// of K); the fp32 slice tiles go to the workspace and the reduce kernel adds
+// them in slice order.  With at most 256 / tiles slices of T x F, the
+// workspace stays under 256 x 512 x 128 x 4 B = 64 MiB.
+constexpr int kProjCUs = 256;            // compute units of a gfx950 GPU
+constexpr int kProjBigSplitMax = 16;
+constexpr int kProjBigMinStages = 16;
+
+// slices of K for n_tiles large tiles and nk stages of K (0: not known yet)
+static int project_big_split(long long n_tiles, int nk) {
+  if (n_tiles <= 0 || 2 * n_tiles > kProjCUs) return 1;
+  int S = (int)std::min<long long>(kProjBigSplitMax, kProjCUs / n_tiles);
+  if (nk > 0) S = std::min(S, nk / kProjBigMinStages);
+  return std::max(S, 1);
+}
+
+static long long project_big_tiles(int T, int F) {
+  return (long long)((F + kProjBF - 1) / kProjBF) * (((long long)T + kProjBT - 1) / kProjBT);
+}
+
+// what the fastest launch uses (the split of K, whenever it applies)
 size_t project_workspace_bytes(int T, int F) {
-  if (T <= 0 || T > kProjSmallMaxT) return 0;
-  return (size_t)kProjSplitMax * (size_t)((T + 31) / 32 * 32) * (size_t)((F + 31) / 32 * 32) *
-         sizeof(float);
+  if (T <= 0) return 0;
+  if (T <= kProjSmallMaxT)
+    return (size_t)kProjSplitMax * (size_t)((T + 31) / 32 * 32) * (size_t)((F + 31) / 32 * 32) *
+           sizeof(float);
+  const int S = project_big_split(project_big_tiles(T, F), 0);
+  return S >= 2 ? (size_t)S * (size_t)T * (size_t)F * sizeof(float) : 0;
+}
+
+// what a call must be given: the few-token path always splits K; above it the
+// split is taken only when the workspace holds it
+size_t project_workspace_required(int T, int F) {
+  return T <= kProjSmallMaxT ? project_workspace_bytes(T, F) : 0;
 }
 
 // part: fp32 [KS][Tp][Fp], Tp / Fp = T / F rounded up to 32 (padding rows and
@@ -361,35 +416,54 @@ __global__ __launch_bounds__(256) void index_project_reduce_kernel(
 hipError_t launch_index_project(const void* x, const void* wq, const void* wk, int D, int G, int DI,
                                 int T, const int32_t* cu_q, const int32_t* cu_k, KvMap kv,
                                 int batch, void* q_idx, void* k_idx, void* workspace,
-                                hipStream_t st) {
+                                size_t workspace_bytes, hipStream_t st) {
   const int GD = G * DI, F = GD + DI;
   if (T <= 0) return hipSuccess;
-  if (T <= kProjSmallMaxT) {
-    const int n_ft = (F + 31) / 32, n_tt = (T + 31) / 32;
-    const int Tp = n_tt * 32, Fp = n_ft * 32;
-    // at least 4 chunks of 64 per slice, so that every wave has work
-    const int KS = project_split(T, F, D / 64);
-    float* part = reinterpret_cast<float*>(workspace);
-    hipLaunchKernelGGL(index_project_split_kernel, dim3(n_ft * n_tt * KS), dim3(kProjSplitWaves * 64),
-                       0, st, (const uint16_t*)x, (const uint16_t*)wq, (const uint16_t*)wk, D, GD, F,
-                       T, n_ft, n_tt, KS, Tp, Fp, part);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
+  float* part = reinterpret_cast<float*>(workspace);
+  auto reduce = [&](int KS, int Tp, int Fp) {
     const long long n = (long long)T * (F / 4);
     hipLaunchKernelGGL(index_project_reduce_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0,
                        st, (const float*)part, KS, Tp, Fp, T, F, GD, DI, cu_q, cu_k, kv, batch,
                        (uint16_t*)q_idx, (uint16_t*)k_idx);
     return hipGetLastError();
+  };
+  if (T <= kProjSmallMaxT) {
+    const int n_ft = (F + 31) / 32, n_tt = (T + 31) / 32;
+    const int Tp = n_tt * 32, Fp = n_ft * 32;
+    // at least 4 chunks of 64 per slice, so that every wave has work
+    const int KS = project_split(T, F, D / 64);
+    hipLaunchKernelGGL(index_project_split_kernel, dim3(n_ft * n_tt * KS), dim3(kProjSplitWaves * 64),
+                       0, st, (const uint16_t*)x, (const uint16_t*)wq, (const uint16_t*)wk, D, GD, F,
+                       T, n_ft, n_tt, KS, Tp, Fp, part);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    return reduce(KS, Tp, Fp);
   }
   const int n_ft = (F + kProjBF - 1) / kProjBF;
   const long long n_tt = ((long long)T + kProjBT - 1) / kProjBT;
   const long long n_tiles = n_ft * n_tt;
   if (n_tiles <= 0) return hipSuccess;
   if (n_tiles >= (1ll << 31)) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(index_project_kernel, dim3((unsigned)n_tiles), dim3(kProjNW * 64), 0, st,
+  const int nk = D / kProjBK;                      // even, >= 2
+  int S = project_big_split(n_tiles, nk), kps = nk;
+  if (S >= 2) {
+    kps = (nk + S - 1) / S;
+    kps += kps & 1;                                // even: every slice's stage count is even
+    S = (nk + kps - 1) / kps;
+  }
+  if (S >= 2 && part && workspace_bytes >= (size_t)S * (size_t)T * (size_t)F * sizeof(float)) {
+    hipLaunchKernelGGL(index_project_kernel<true>, dim3((unsigned)(n_tiles * S)), dim3(kProjNW * 64), 0,
+                       st, (const uint16_t*)x, (const uint16_t*)wq, (const uint16_t*)wk, D, GD, F, T,
+                       n_ft, (int)n_tt, (int)(n_tiles * S), kps, cu_q, cu_k, kv, batch, DI,
+                       (uint16_t*)q_idx, (uint16_t*)k_idx, part);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    return reduce(S, T, F);
+  }
+  hipLaunchKernelGGL(index_project_kernel<false>, dim3((unsigned)n_tiles), dim3(kProjNW * 64), 0, st,
                      (const uint16_t*)x, (const uint16_t*)wq, (const uint16_t*)wk, D, GD, F, T,
-                     n_ft, (int)n_tiles, cu_q, cu_k, kv, batch, DI, (uint16_t*)q_idx,
-                     (uint16_t*)k_idx);
+                     n_ft, (int)n_tt, (int)n_tiles, nk, cu_q, cu_k, kv, batch, DI, (uint16_t*)q_idx,
+                     (uint16_t*)k_idx, (float*)nullptr);
   return hipGetLastError();
 }
 

@@ -49,8 +49,9 @@ hipError_t launch_index_kl(int, const void*, const void*, const int32_t*, const 
                            float*, hipStream_t);
 hipError_t launch_index_project(const void*, const void*, const void*, int, int, int, int,
                                 const int32_t*, const int32_t*, KvMap, int, void*, void*, void*,
-                                hipStream_t);
+                                size_t, hipStream_t);
 size_t project_workspace_bytes(int, int);
+size_t project_workspace_required(int, int);
 hipError_t launch_hbm_stream(const void*, long long, int, void*, void*, int, hipStream_t);
 hipError_t launch_quantize_index_fp8(int, const void*, const void*, const int32_t*, KvMap, int, int,
                                      long long, void*, uint8_t*, void*, uint8_t*, hipStream_t);
@@ -207,9 +208,16 @@ size_t ws_attend(const msa_dims_t* d, const Derived& x) {
 }
 
 size_t ws_project(const Derived& x) {
-  // split-K partial tiles of the few-token path (0 for larger steps)
+  // fp32 tiles of the slices of K: always for few-token steps, and up to a few
+  // thousand tokens when the large-tile kernel would not fill the GPU (0 above)
   if (x.total_q > (1ll << 30)) return 0;
   return msa::project_workspace_bytes((int)x.total_q, (x.G + 1) * x.DI);
+}
+
+size_t ws_project_required(const Derived& x) {
+  // the part a call cannot do without (the few-token path's slices)
+  if (x.total_q > (1ll << 30)) return 0;
+  return msa::project_workspace_required((int)x.total_q, (x.G + 1) * x.DI);
 }
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
@@ -456,10 +464,10 @@ msa_status_t msa_index_project(const msa_dims_t* dims, int32_t model_dim, const 
   if (x_.total_q == 0) return MSA_OK;   // no new tokens
   if (!x || !w_q || !w_k || !cu_seqlens_q || !cu_seqlens_k || !q_idx || !k_idx)
     return fail(MSA_ERR_NULL_ARG, "a required pointer is NULL");
-  const size_t need = ws_project(x_);
+  const size_t need = ws_project_required(x_);
   if (need && !workspace) return fail(MSA_ERR_NULL_ARG, "a required pointer is NULL");
   if (!aligned16(x) || !aligned16(w_q) || !aligned16(w_k) || !aligned16(q_idx) ||
-      !aligned16(k_idx) || (need && !aligned16(workspace)))
+      !aligned16(k_idx) || (workspace && !aligned16(workspace)))
     return fail(MSA_ERR_ALIGNMENT, "tensor pointers must be 16-byte aligned");
   if (workspace_bytes < need)
     return fail(MSA_ERR_WORKSPACE_TOO_SMALL, "index_project workspace too small");
@@ -468,7 +476,7 @@ msa_status_t msa_index_project(const msa_dims_t* dims, int32_t model_dim, const 
   ProfScope ps(K_PROJECT, st);
   hipError_t e = msa::launch_index_project(x, w_q, w_k, model_dim, x_.G, x_.DI, (int)x_.total_q,
                                            cu_seqlens_q, cu_seqlens_k, x_.kv, dims->batch, q_idx,
-                                           k_idx, workspace, st);
+                                           k_idx, workspace, workspace ? workspace_bytes : 0, st);
   return launched(e, st, K_PROJECT);
 }
 

@@ -243,10 +243,16 @@ msa_status_t msa_attend(const msa_dims_t* dims, const void* q, const void* k, co
  * w_k    bf16 [index_dim, D]
  * q_idx  bf16 [total_q, num_kv_heads, index_dim]  out
  * k_idx  bf16 [total_k, index_dim]                out (the new tokens' rows)
- * workspace >= msa_workspace_size(dims, MSA_OP_INDEX_PROJECT) bytes, 16-byte
- *   aligned (a few MiB for steps of up to 512 tokens, which split the sum
- *   over model_dim across workgroups; 0 above, where NULL is accepted).
- *   Partial sums are added in a fixed order: results are deterministic.
+ * workspace  16-byte aligned; msa_workspace_size(dims, MSA_OP_INDEX_PROJECT)
+ *   bytes is what the fastest launch uses: fp32 tiles of slices of the sum
+ *   over model_dim, taken by different workgroups.  Steps of up to 512
+ *   tokens always split the sum and must be given at least that much (a
+ *   few MiB; else MSA_ERR_NULL_ARG or MSA_ERR_WORKSPACE_TOO_SMALL).  Larger
+ *   steps split it only while the GPU would otherwise be underfilled (up to
+ *   a few thousand tokens; at most 64 MiB) and only if the workspace holds
+ *   the slices; NULL or a smaller workspace runs them unsplit.  Partial sums
+ *   are added in a fixed order: results are deterministic for a given
+ *   workspace size (a split and an unsplit run differ by fp32 rounding).
  * total_q == 0 enqueues nothing.
  */
 msa_status_t msa_index_project(const msa_dims_t* dims, int32_t model_dim, const void* x,

@@ -267,7 +267,20 @@ def test_projection_entry_point_validates_on_host():
         assert pj(ctypes.byref(dd), 8192, ok, ok, ok, ok, ok, ok, ok, None, need, None) == 1
         assert pj(ctypes.byref(dd), 8192, ok, ok, ok, ok, ok, ok, ok, odd, need, None) == 4
         assert pj(ctypes.byref(dd), 8192, ok, ok, ok, ok, ok, ok, ok, ok, need - 1, None) == 5
-    assert msa.workspace_size(_dims(total_q=513, max_q_len=513), msa.OP_INDEX_PROJECT) == 0
+    # larger steps: the large-tile kernel (512 tokens x 128 features per workgroup, one per CU)
+    # splits K only while its tiles would leave half the 256 CUs idle, into 256 // tiles slices
+    # (at most 16) of fp32 T x F tiles; the workspace is then optional
+    F = 9 * 128
+    for T, slices in ((513, 14), (2048, 7), (7168, 2), (7680, 0), (32768, 0)):
+        tiles = 9 * ((T + 511) // 512)
+        assert slices == (min(16, 256 // tiles) if 2 * tiles <= 256 else 0)
+        dd = _dims(total_q=T, max_q_len=T, total_k=T, max_k_len=T)
+        assert msa.workspace_size(dd, msa.OP_INDEX_PROJECT) == slices * T * F * 4
+        # an optional workspace is still used, so it must be aligned too
+        assert pj(ctypes.byref(dd), 8192, ok, ok, ok, ok, ok, ok, ok, odd, 1 << 30, None) == 4
+    for T in range(513, 20000, 97):
+        dd = _dims(total_q=T, max_q_len=T, total_k=T, max_k_len=T)
+        assert msa.workspace_size(dd, msa.OP_INDEX_PROJECT) <= 64 << 20
 
 
 def test_kl_entry_points_validate_on_host():

@@ -100,6 +100,11 @@ def _key_rows(t, w):
     dict(k=[4000] * 32, q=[1] * 32, G=8, di=128, D=8192),  # decode at full width: 15 K slices
     dict(k=[300, 200], q=[3, 2], G=2, di=32, D=64),       # one K chunk: three waves idle
     dict(k=[900, 400], q=[100, 160], G=4, di=64, D=320),  # 5 K chunks over 4 waves
+    # mid-size steps: the large-tile kernel splits K when its tiles would leave CUs idle
+    dict(k=[1200, 700, 100], q=[1200, 700, 100], G=8, di=128, D=4096),  # 7 slices, the last shorter
+    dict(k=[640], q=[640], G=8, di=128, D=8192),          # 13 slices of 20 stages
+    dict(k=[1100], q=[1100], G=2, di=64, D=1344),         # 2 slices of 22 and 20 stages
+    dict(k=[5000, 3000], q=[400, 300], G=8, di=128, D=2048),  # 4 slices; new keys appended
 ])
 def test_projection_elementwise(case):
     w = custom(case["k"], case["q"], num_q_heads=case["G"] * 4, num_kv_heads=case["G"],
@@ -145,6 +150,49 @@ def test_split_path_is_deterministic_and_ignores_workspace_contents():
         assert torch.equal(q_idx, outs[0][0]) and torch.equal(k_idx, outs[0][1])
     q, rows, (yq, sq), (yk, sk) = _oracle(w, t, p, D)
     _check_elementwise(outs[0][0].double().cpu().numpy().reshape(w.total_q, -1), yq, sq, D, "q_idx")
+
+
+def test_mid_size_split_matches_unsplit_within_rounding():
+    """Up to a few thousand tokens the large-tile kernel sums slices of K through
+    the workspace; with a workspace too small for them it runs unsplit.  Both
+    are checked against the oracle element by element; the split run is
+    deterministic and ignores what the workspace held before."""
+    w = custom([1500, 600], [1500, 600], num_q_heads=32, num_kv_heads=8, head_dim=64,
+               index_dim=128, top_k=4, seed=54, qkv_std=1.0)
+    D = 4096
+    t = generate(w, "cpu")
+    p = generate_projection(w, D, "cpu")
+    dev = torch.device("cuda:0")
+    g = {k: v.to(dev) for k, v in t.items()}
+    gp = {k: v.to(dev) for k, v in p.items()}
+    dims = msa.dims_for(w)
+    F = 9 * 128
+    # 2100 tokens: 5 x 9 tiles of 512 tokens x 128 features -> 256 // 45 = 5 slices of K
+    need = msa.workspace_size(dims, msa.OP_INDEX_PROJECT)
+    assert need == 5 * w.total_q * F * 4
+
+    def run(ws):
+        q_idx = torch.empty((w.total_q, w.num_kv_heads, w.index_dim), dtype=torch.bfloat16, device=dev)
+        k_idx = torch.zeros((w.total_k, w.index_dim), dtype=torch.bfloat16, device=dev)
+        msa.index_project(dims, gp["x"], gp["w_q"], gp["w_k"], g["cu_seqlens_q"], g["cu_seqlens_k"],
+                          q_idx, k_idx, workspace=ws)
+        torch.cuda.synchronize()
+        return q_idx, k_idx
+
+    split = [run(torch.full((need // 4,), fill, dtype=torch.float32, device=dev).view(torch.uint8))
+             for fill in (float("nan"), 1e30)]
+    assert torch.equal(split[0][0], split[1][0]) and torch.equal(split[0][1], split[1][1])
+    unsplit = run(torch.empty(need - 16, dtype=torch.uint8, device=dev))
+    q, rows, (yq, sq), (yk, sk) = _oracle(w, t, p, D)
+    kr = _key_rows(t, w)
+    for what, (q_idx, k_idx) in (("split", split[0]), ("unsplit", unsplit)):
+        _check_elementwise(q_idx.double().cpu().numpy().reshape(w.total_q, -1), yq, sq, D,
+                           f"q_idx {what}")
+        _check_elementwise(k_idx.double().cpu().numpy()[kr], yk, sk, D, f"k_idx {what}")
+    # the two differ by fp32 summation order only, so most outputs agree exactly
+    same = (split[0][0] == unsplit[0]).float().mean().item()
+    log(f"[proj] split vs unsplit: {same:.4f} of q_idx outputs identical")
+    assert same > 0.9
 
 
 def test_projection_model_width_8192_sampled():
