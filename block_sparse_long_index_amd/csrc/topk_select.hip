@@ -13,40 +13,46 @@
 // This kernel selects from a materialised block-score buffer (the decode
 // path); the prefill path fuses the same selection into its scoring kernel.
 //
-// One wave per row.  Candidates are (score, block) 64-bit keys, unique per
-// row, so the km = top_k - 1 best form one well-defined set.  Each lane loads
-// its share of the row's blocks (lane w takes blocks w, w + 64, ...; the first
-// 32 per lane all in flight at once) and keeps its largest key.  The km-th
-// largest of the 64 lane maxima is a threshold t: at least km candidates reach
-// it (one per lane among the km best lanes), so the km best candidates are all
-// >= t, and usually only a few dozen others reach it.  Those survivors are
+// Four waves per row.  Candidates are (score, block) 64-bit keys, unique per
+// row, so the km = top_k - 1 best form one well-defined set.  Each thread
+// loads its share of the row's blocks (thread i takes blocks i, i + 256, ...;
+// the first 8 per thread all in flight at once) and keeps its largest key.
+// In each wave the km-th largest of the 64 lane maxima is a threshold t_w
+// that at least km of that wave's candidates reach; the row's threshold t is
+// the largest t_w, so at least km candidates reach t and the km best are all
+// >= t, while usually only a few dozen others reach it.  Those survivors are
 // gathered in LDS; each one's rank among them (how many survivors are larger)
 // decides whether it is selected, and the selected blocks' rank by id gives
 // their output slot.  If more survivors than LDS holds reach t (many equal
-// scores), the wave falls back to per-lane sorted lists merged by km rounds of
-// wave-wide maxima.
+// scores), the threads fall back to per-thread sorted lists merged by km
+// rounds of workgroup-wide maxima.  (One wave per row left three quarters of
+// the SIMDs idle at decode sizes, where the rows' latency is the kernel's time.)
 #include "msa_common.h"
 #include "topk_common.h"
 
 namespace msa {
 
-constexpr int kTopkPerLane = 32;     // candidates per lane held in registers
+constexpr int kTopkWaves = 4;
+constexpr int kTopkThreads = kTopkWaves * kWave;
+constexpr int kTopkPerThread = 8;    // candidates per thread held in registers
 constexpr int kTopkSurvMax = 256;    // survivors gathered in LDS
 
-// grid.x = rows of the pass (chunk row = (query - r0) * G + g), one wave each.
+// grid.x = rows of the pass (chunk row = (query - r0) * G + g), one workgroup each.
 template <int KCAP>
-__global__ __launch_bounds__(64) void topk_select_kernel(
+__global__ __launch_bounds__(kTopkThreads) void topk_select_kernel(
     const float* __restrict__ S, long long ld, int r0, int r1, const int32_t* __restrict__ cu_q,
     const int32_t* __restrict__ cu_k, int batch, int G, int top_k, int32_t* __restrict__ sel,
     float* __restrict__ sel_score) {
-  __shared__ uint64_t lane_max[kWave];
+  __shared__ uint64_t lane_max[kTopkWaves][kWave];
+  __shared__ uint64_t wave_t[kTopkWaves];
+  __shared__ uint64_t wave_best[kTopkWaves];
   __shared__ uint64_t surv[kTopkSurvMax];
   __shared__ uint64_t chosen[KCAP];
-  __shared__ uint64_t thresh;
   __shared__ int n_surv;
 
   const long long crow = blockIdx.x;
-  const int lane = threadIdx.x;
+  const int tid = threadIdx.x;
+  const int wave = tid / kWave, lane = tid % kWave;
   const int km = top_k - 1;
   const int r = r0 + (int)(crow / G);
   const int g = (int)(crow % G);
@@ -63,50 +69,51 @@ __global__ __launch_bounds__(64) void topk_select_kernel(
     return s == s ? make_key(s, beta) : 0;
   };
 
-  // 1. the first kTopkPerLane candidates of the lane in registers; the lane's max
-  uint64_t first[kTopkPerLane];
+  // 1. the first kTopkPerThread candidates of the thread in registers; its max
+  uint64_t first[kTopkPerThread];
   {
-    float s[kTopkPerLane];
+    float s[kTopkPerThread];
 #pragma unroll
-    for (int i = 0; i < kTopkPerLane; ++i) {
-      const int beta = lane + i * kWave;
+    for (int i = 0; i < kTopkPerThread; ++i) {
+      const int beta = tid + i * kTopkThreads;
       s[i] = col[(size_t)min(beta, max(beta_p - 1, 0)) * ld];
     }
 #pragma unroll
-    for (int i = 0; i < kTopkPerLane; ++i) {
-      const int beta = lane + i * kWave;
+    for (int i = 0; i < kTopkPerThread; ++i) {
+      const int beta = tid + i * kTopkThreads;
       first[i] = (beta < beta_p && s[i] == s[i]) ? make_key(s[i], beta) : 0;
     }
   }
   uint64_t mx = 0;
 #pragma unroll
-  for (int i = 0; i < kTopkPerLane; ++i) mx = first[i] > mx ? first[i] : mx;
-  for (int beta = lane + kTopkPerLane * kWave; beta < beta_p; beta += kWave) {
+  for (int i = 0; i < kTopkPerThread; ++i) mx = first[i] > mx ? first[i] : mx;
+  for (int beta = tid + kTopkPerThread * kTopkThreads; beta < beta_p; beta += kTopkThreads) {
     const uint64_t k = key_of(beta);
     mx = k > mx ? k : mx;
   }
 
-  // 2. threshold: the km-th largest lane maximum (0 if fewer than km lanes hold one)
-  lane_max[lane] = mx;
-  if (lane == 0) {
-    thresh = 0;
-    n_surv = 0;
-  }
+  // 2. threshold: per wave the km-th largest lane maximum (0 if fewer than km
+  // of its lanes hold one), then the largest of the waves'
+  lane_max[wave][lane] = mx;
+  if (lane == 0) wave_t[wave] = 0;
+  if (tid == 0) n_surv = 0;
   __syncthreads();
   if (km > 0 && mx != 0) {
     int rank = 0;
-    for (int j = 0; j < kWave; ++j) rank += lane_max[j] > mx ? 1 : 0;
-    if (rank == km - 1) thresh = mx;
+    for (int j = 0; j < kWave; ++j) rank += lane_max[wave][j] > mx ? 1 : 0;
+    if (rank == km - 1) wave_t[wave] = mx;
   }
   __syncthreads();
-  const uint64_t t = thresh;
+  uint64_t t = wave_t[0];
+#pragma unroll
+  for (int w = 1; w < kTopkWaves; ++w) t = wave_t[w] > t ? wave_t[w] : t;
 
   // 3. gather the survivors (keys >= t)
   int mine = 0;
   if (km > 0) {
 #pragma unroll
-    for (int i = 0; i < kTopkPerLane; ++i) mine += (first[i] != 0 && first[i] >= t) ? 1 : 0;
-    for (int beta = lane + kTopkPerLane * kWave; beta < beta_p; beta += kWave) {
+    for (int i = 0; i < kTopkPerThread; ++i) mine += (first[i] != 0 && first[i] >= t) ? 1 : 0;
+    for (int beta = tid + kTopkPerThread * kTopkThreads; beta < beta_p; beta += kTopkThreads) {
       const uint64_t k = key_of(beta);
       mine += (k != 0 && k >= t) ? 1 : 0;
     }
@@ -117,31 +124,31 @@ __global__ __launch_bounds__(64) void topk_select_kernel(
   if (n <= kTopkSurvMax) {
     if (mine) {
 #pragma unroll
-      for (int i = 0; i < kTopkPerLane; ++i)
+      for (int i = 0; i < kTopkPerThread; ++i)
         if (first[i] != 0 && first[i] >= t) surv[base++] = first[i];
-      for (int beta = lane + kTopkPerLane * kWave; beta < beta_p; beta += kWave) {
+      for (int beta = tid + kTopkPerThread * kTopkThreads; beta < beta_p; beta += kTopkThreads) {
         const uint64_t k = key_of(beta);
         if (k != 0 && k >= t) surv[base++] = k;
       }
     }
     __syncthreads();
     // 4. rank among the survivors: the km largest are selected
-    for (int i = lane; i < n; i += kWave) {
+    for (int i = tid; i < n; i += kTopkThreads) {
       const uint64_t k = surv[i];
       int rank = 0;
       for (int j = 0; j < n; ++j) rank += surv[j] > k ? 1 : 0;
       if (rank < km) chosen[rank] = k;
     }
   } else {
-    // many equal scores: per-lane sorted lists of the keys >= t, merged by
-    // km rounds of wave-wide maxima
+    // many equal scores: per-thread sorted lists of the keys >= t, merged by
+    // km rounds of workgroup-wide maxima
     uint64_t list[KCAP];
 #pragma unroll
     for (int i = 0; i < KCAP; ++i) list[i] = 0;
 #pragma unroll
-    for (int i = 0; i < kTopkPerLane; ++i)
+    for (int i = 0; i < kTopkPerThread; ++i)
       if (first[i] != 0 && first[i] >= t) list_insert(list, first[i]);
-    for (int beta = lane + kTopkPerLane * kWave; beta < beta_p; beta += kWave) {
+    for (int beta = tid + kTopkPerThread * kTopkThreads; beta < beta_p; beta += kTopkThreads) {
       const uint64_t k = key_of(beta);
       if (k != 0 && k >= t) list_insert(list, k);
     }
@@ -153,28 +160,35 @@ __global__ __launch_bounds__(64) void topk_select_kernel(
         const uint64_t o = shfl_xor_u64(best, off);
         best = o > best ? o : best;
       }
+      if (lane == 0) wave_best[wave] = best;
+      __syncthreads();
+      best = wave_best[0];
+#pragma unroll
+      for (int w = 1; w < kTopkWaves; ++w) best = wave_best[w] > best ? wave_best[w] : best;
+      // keys are unique: exactly one thread holds the best at its head
       if (best != 0 && head == best) {
 #pragma unroll
         for (int j = 0; j < KCAP - 1; ++j) list[j] = list[j + 1];
         list[KCAP - 1] = 0;
       }
-      if (lane == 0) chosen[i] = best;
+      if (tid == 0) chosen[i] = best;
+      __syncthreads();   // wave_best is rewritten by the next round
     }
   }
   __syncthreads();
 
   // 5. output: the selected blocks in ascending id, then the local block, then padding
   const int cnt = min(km, n);   // every survivor is a real candidate; the fallback has n > km
-  if (lane < cnt) {
-    const uint64_t k = chosen[lane];
+  if (tid < cnt) {
+    const uint64_t k = chosen[tid];
     const int id = key_block(k);
     int pos = 0;
     for (int j = 0; j < cnt; ++j) pos += key_block(chosen[j]) < id ? 1 : 0;
     so[pos] = id;
     if (sco) sco[pos] = key_score(k);
-  } else if (lane < top_k) {
-    so[lane] = lane == cnt ? beta_p : -1;
-    if (sco) sco[lane] = lane == cnt ? INFINITY : __uint_as_float(0x7fc00000u);
+  } else if (tid < top_k) {
+    so[tid] = tid == cnt ? beta_p : -1;
+    if (sco) sco[tid] = tid == cnt ? INFINITY : __uint_as_float(0x7fc00000u);
   }
 }
 
@@ -184,7 +198,7 @@ static hipError_t launch_topk_kcap(const float* S, long long ld, int r0, int r1,
                                    float* sel_score, hipStream_t st) {
   const long long nrows = (long long)(r1 - r0) * G;
   if (nrows <= 0) return hipSuccess;
-  hipLaunchKernelGGL((topk_select_kernel<KCAP>), dim3((unsigned)nrows), dim3(kWave), 0, st, S, ld, r0,
+  hipLaunchKernelGGL((topk_select_kernel<KCAP>), dim3((unsigned)nrows), dim3(kTopkThreads), 0, st, S, ld, r0,
                      r1, cu_q, cu_k, batch, G, top_k, sel, sel_score);
   return hipGetLastError();
 }

@@ -287,9 +287,10 @@ def test_verification_shapes_two_and_four_row_tiles():
 def test_decode_topk_long_rows_and_many_survivors():
     # decode selection from the block-score buffer: a row with exactly 2048 earlier blocks
     # whose scores make more candidates reach the selection threshold than LDS gathers
-    # (blocks of lanes 0..13 tie at 2048, lane 14's at 1024, the rest 1: the list-merge
-    # fallback), and a row with 3000 earlier blocks (candidates beyond the 32 per lane
-    # held in registers)
+    # (in every wave, the blocks of lanes 0..13 tie at 2048, lane 14's at 1024, the rest 1:
+    # each wave's threshold is a 1024 key, so 449 keys reach the row's: the list-merge
+    # fallback), and a row with 3000 earlier blocks (candidates beyond the 8 per thread, 2048
+    # per row, held in registers)
     lk = [2048 * 128 + 100, 3000 * 128 + 5, 777]
     w = custom(lk, [1, 1, 1], num_q_heads=2, num_kv_heads=1, head_dim=64, index_dim=32,
                top_k=16, seed=38, qkv_std=1.0)
