@@ -155,12 +155,15 @@ def test_paged_kl_target():
     _check_paged(w, "paged-kl", want_kl=True, oracle=False)
 
 
-def test_paged_projection_writes_the_pages():
+# model width 256: the large-tile kernel writes the keys; 2048: K is split over
+# 4 workgroup slices (12 tiles), and the reduce kernel writes them through the table
+@pytest.mark.parametrize("D", [256, 2048])
+def test_paged_projection_writes_the_pages(D):
     w = custom([700, 2000, 130], [1, 2000, 3], num_q_heads=16, num_kv_heads=4, head_dim=64,
                index_dim=64, top_k=5, seed=77, qkv_std=1.0)
     dev = torch.device("cuda:0")
     t = generate(w, "cpu")
-    p = generate_projection(w, 256, "cpu")
+    p = generate_projection(w, D, "cpu")
     cache, table, pages, rows = _paged(w, t)
     g = {k_: v_.to(dev) for k_, v_ in t.items()}
     gp = {k_: v_.to(dev) for k_, v_ in p.items()}
