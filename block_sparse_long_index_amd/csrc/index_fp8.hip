@@ -738,6 +738,7 @@ constexpr int kFp8Rows = kFp8RT * kFp8NW * 32;
 constexpr int kFp8DecodeSeg = 8;
 
 int fp8_max_blocks_per_sequence() { return kFp8ExpLds; }
+int fp8_prefill_rows_per_wg() { return kFp8Rows; }
 
 template <int DI>
 static hipError_t launch_quantize_di(const void* q, const void* k, const int32_t* cu_k, KvMap kv,

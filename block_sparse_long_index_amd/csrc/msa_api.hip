@@ -42,6 +42,8 @@ hipError_t launch_main_quantize_q8kv4(int, const void*, const void*, const void*
 hipError_t launch_merge(int, bool, const void*, const float2*, const int32_t*, int, int, int, int,
                         int, void*, float*, hipStream_t);
 int fp8_max_blocks_per_sequence();
+int fp8_prefill_rows_per_wg();
+int prefill_rows_per_wg();
 hipError_t launch_block_mass(int, const float2*, const int32_t*, int, int, int, int, float*,
                              hipStream_t);
 hipError_t launch_index_kl(int, const void*, const void*, const int32_t*, const int32_t*, KvMap, int,
@@ -416,6 +418,9 @@ msa_status_t msa_index_select(const msa_dims_t* dims, const void* q_idx, const v
   msa_status_t s = check_dims(dims, &x);
   if (s != MSA_OK) return s;
   if (x.total_q == 0) return MSA_OK;   // no queries: nothing to select
+  // a prefill workgroup scores whole queries: all G of their (query, group) rows
+  if (!x.decode_path && x.G > msa::prefill_rows_per_wg())
+    return fail(MSA_ERR_UNSUPPORTED, "num_kv_heads must be <= 512 when max_q_len * num_kv_heads > 128");
   if (!q_idx || !k_idx || !cu_seqlens_q || !cu_seqlens_k || !sel || !workspace)
     return fail(MSA_ERR_NULL_ARG, "a required pointer is NULL");
   if (!aligned16(q_idx) || !aligned16(k_idx) || !aligned16(sel) || !aligned16(workspace) ||
@@ -518,6 +523,8 @@ msa_status_t select_q8(const msa_dims_t* dims, const void* q_idx8, const uint8_t
   if (!k4 && x.nb_max > msa::fp8_max_blocks_per_sequence())
     return fail(MSA_ERR_UNSUPPORTED, "max_k_len too long for the fp8 index kernels (16384 blocks)");
   if (x.total_q == 0) return MSA_OK;
+  if (!x.decode_path && x.G > msa::fp8_prefill_rows_per_wg())
+    return fail(MSA_ERR_UNSUPPORTED, "num_kv_heads must be <= 256 when max_q_len * num_kv_heads > 128");
   if (!q_idx8 || !q_exp || !k_codes || !k_exp || !cu_seqlens_q || !cu_seqlens_k || !sel || !workspace)
     return fail(MSA_ERR_NULL_ARG, "a required pointer is NULL");
   if (!aligned16(q_idx8) || !aligned16(k_codes) || !aligned16(sel) || !aligned16(workspace) ||

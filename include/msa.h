@@ -168,6 +168,9 @@ msa_status_t msa_workspace_size(const msa_dims_t* dims, msa_op_t op, size_t* byt
  * sel_score fp32  [total_q, num_kv_heads, top_k]  out, optional (NULL): S of each
  *           selected block, +inf for the local block, NaN for padding
  * workspace >= msa_workspace_size(dims, MSA_OP_INDEX_SELECT) bytes
+ * When max_q_len * num_kv_heads > 128 (the prefill kernel, which scores all
+ * groups of a query in one workgroup) num_kv_heads must be <= 512, else
+ * MSA_ERR_UNSUPPORTED.
  */
 msa_status_t msa_index_select(const msa_dims_t* dims, const void* q_idx, const void* k_idx,
                               const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
@@ -304,7 +307,8 @@ msa_status_t msa_index_project(const msa_dims_t* dims, int32_t model_dim, const 
  *   block score is 2^(eq + ek) * max_j (q8 . k8_j), applied exactly.  Selection rule, tie
  *   rule, outputs and workspace (msa_workspace_size with MSA_OP_INDEX_SELECT)
  *   are those of msa_index_select; sel_score holds the dequantised block
- *   scores.  Requires ceil(max_k_len / 128) <= 16384 (MSA_ERR_UNSUPPORTED).
+ *   scores.  Requires ceil(max_k_len / 128) <= 16384, and num_kv_heads <= 256
+ *   when max_q_len * num_kv_heads > 128 (else MSA_ERR_UNSUPPORTED).
  */
 msa_status_t msa_index_quantize_fp8(const msa_dims_t* dims, const void* q_idx, const void* k_idx,
                                     const int32_t* cu_seqlens_k, void* q_idx8, uint8_t* q_exp,
@@ -354,7 +358,8 @@ msa_status_t msa_index_select_fp8(const msa_dims_t* dims, const void* q_idx8, co
  *   token score is within 2^-10 * sum_c |q_c k_c| of the exact value; the
  *   query exponent is applied to the block maximum.  Selection rule, tie
  *   rule, outputs and workspace are those of msa_index_select; sel_score
- *   holds the dequantised block scores.
+ *   holds the dequantised block scores.  num_kv_heads <= 256 when
+ *   max_q_len * num_kv_heads > 128 (else MSA_ERR_UNSUPPORTED).
  */
 msa_status_t msa_index_quantize_q8k4(const msa_dims_t* dims, const void* q_idx, const void* k_idx,
                                      const int32_t* cu_seqlens_k, void* q_idx8, uint8_t* q_exp,

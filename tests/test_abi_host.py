@@ -361,3 +361,26 @@ def test_fp8_main_entry_points_validate_on_host():
     empty = _dims(total_q=0, max_q_len=0)
     assert at(ctypes.byref(empty), None, None, None, None, None, None, None, None, None, None, None,
               None, None, None, 0, None) == 0
+
+
+def test_prefill_index_kv_head_limit_rejected_on_host():
+    """The prefill index kernels score all groups of a query in one workgroup
+    (512 (query, group) rows for bf16 keys, 256 for 8-bit and 4-bit keys), so
+    a larger KV head count on that path (max_q_len * num_kv_heads > 128,
+    which every count above 128 is) is refused before any launch."""
+    P = ctypes.c_void_p
+    ok = P(0x10000)
+    big = ctypes.c_size_t(1 << 40)
+    sel, s8, s4 = lib.msa_index_select, lib.msa_index_select_fp8, lib.msa_index_select_q8k4
+
+    def dims(G, q_len):
+        return _dims(num_q_heads=G, num_kv_heads=G, total_q=q_len, max_q_len=q_len)
+
+    for G, bf16_status, q8_status in ((1024, 3, 3), (512, None, 3)):
+        d = dims(G, 256)
+        if bf16_status is not None:
+            assert sel(ctypes.byref(d), ok, ok, ok, ok, ok, None, ok, big, None) == bf16_status
+            assert "512" in lib.msa_last_error().decode()
+        assert s8(ctypes.byref(d), ok, ok, ok, ok, ok, ok, ok, None, ok, big, None) == q8_status
+        assert "256" in lib.msa_last_error().decode()
+        assert s4(ctypes.byref(d), ok, ok, ok, ok, ok, ok, ok, None, ok, big, None) == q8_status
