@@ -188,6 +188,42 @@ def test_chunking_is_bitwise_invisible():
         assert torch.equal(a.lse, x.lse)
 
 
+def test_prefill_split_into_query_chunks_is_bitwise_the_whole():
+    """A prefill cut into query-row sub-problems, each with the keys up to its
+    last query (the queries are the last Lq of Lk; chunked prefill as a serving
+    engine runs it), selects and attends bitwise as the whole prefill does:
+    every row's scores, selection and partials depend only on its own
+    position.  Chunk edges fall inside 128-token blocks; every chunk keeps
+    more than 128 / G rows, so all of them take the prefill kernels."""
+    w = custom([2600], [2600], num_q_heads=16, num_kv_heads=2, head_dim=128, index_dim=64,
+               top_k=6, seed=31, qkv_std=1.0)
+    t = generate(w, "cpu")
+    _, whole, g = run_gpu(w, t)
+    dev = g["q"].device
+    G, K = w.num_kv_heads, w.top_k
+    sel = torch.full_like(whole.sel, -7)
+    out = torch.zeros_like(whole.out)
+    lse = torch.zeros_like(whole.lse)
+    edges = [0, 700, 1301, 2048, 2600]
+    log(f"[split] chunk edges {edges}")
+    for a, z in zip(edges[:-1], edges[1:]):
+        d = msa.make_dims(batch=1, num_q_heads=w.num_q_heads, num_kv_heads=G, head_dim=w.head_dim,
+                          index_dim=w.index_dim, top_k=K, total_q=z - a, total_k=z,
+                          max_q_len=z - a, max_k_len=z)
+        assert (z - a) * G > 128 and msa.attend_reads_lists(d)
+        cq = torch.tensor([0, z - a], dtype=torch.int32, device=dev)
+        ck = torch.tensor([0, z], dtype=torch.int32, device=dev)
+        b = msa.Buffers(d, dev)
+        msa.index_select(d, g["q_idx"][a:z], g["k_idx"][:z], cq, ck, sel[a:z], workspace=b.workspace)
+        msa.build_block_query_lists(d, sel[a:z], cq, ck, b.offsets, b.entries, b.workspace)
+        msa.attend(d, g["q"][a:z], g["k"][:z], g["v"][:z], cq, ck, sel[a:z], b.offsets, b.entries,
+                   out[a:z], lse[a:z], b.workspace)
+    torch.cuda.synchronize()
+    assert torch.equal(sel, whole.sel)
+    assert torch.equal(out, whole.out)
+    assert torch.equal(lse, whole.lse)
+
+
 def test_deterministic_and_workspace_poison_proof():
     w = custom([2500], [2500], num_q_heads=16, num_kv_heads=2, head_dim=128, index_dim=128,
                top_k=8, seed=30, qkv_std=1.0)
