@@ -926,6 +926,10 @@ def run_leg(args):
         oracle_ctx = (P, rows, ref)
         cpu = dict(value=len(rows) / dt, unit="tokens/s", cores=used, kind="oracle",
                    cpu_model=cpu_model(),
+                   # uniformly random rows sample the per-row cost (which grows with the
+                   # row's position) without bias, so the whole workload on the same
+                   # cores would take about total_q / value seconds
+                   full_workload_s_extrapolated=w.total_q * dt / len(rows),
                    sample=(f"all {len(rows)} query rows" if len(rows) == w.total_q else
                            f"{len(rows)} uniformly random query rows") + f" of {w.name}, each through the "
                           f"full Index and Main Branch in fp64 numpy"

@@ -169,11 +169,23 @@ __global__ __launch_bounds__(64) void lists_scatter_kernel(
   const int nbt = min(nb_max, max(0, p_last / kBlock + 1));
   const int32_t* pre = cnt_prefix + (((size_t)b * nqt_max + t) * G + g) * nb_max;
   const int32_t* off = offsets + ((size_t)b * G + g) * nb_max;
-  for (int i = lane; i < nbt; i += 64) run[i] = off[i] + pre[i];
   const int n = (rz - ra) * top_k;
   for (int e = lane; e < n; e += 64) {
     int row = ra + e / top_k, s = e % top_k;
     sl[e] = sel[((size_t)row * G + g) * top_k + s];
+  }
+  // each block's first position: for all blocks the tile can select when they
+  // are fewer than its selections, else only for the selected ones (a long
+  // context's late tiles can select thousands of blocks but hold at most
+  // kListTile * top_k selections); lanes that share a block write the same value
+  if (nbt <= n) {
+    for (int i = lane; i < nbt; i += 64) run[i] = off[i] + pre[i];
+  } else {
+    __syncthreads();
+    for (int e = lane; e < n; e += 64) {
+      const int beta = sl[e];
+      if (beta >= 0 && beta < nbt) run[beta] = off[beta] + pre[beta];
+    }
   }
   __syncthreads();
   for (int i = 0; i < rz - ra; ++i) {

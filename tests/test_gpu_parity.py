@@ -250,6 +250,22 @@ def test_lists_are_exact_inverse():
     assert np.array_equal(bufs.entries[:n].cpu().numpy().astype(np.int64), ent)
 
 
+@pytest.mark.parametrize("top_k", [2, 4])
+def test_lists_when_tiles_reach_more_blocks_than_they_select(top_k):
+    """Late query tiles of a long context can select from more blocks than they
+    hold selections (128 rows x top_k); the list builder then looks up the
+    first position of the selected blocks only.  Lists must still be the exact
+    inverse of the selection, and the outputs those of the oracle."""
+    w = custom([40000, 9000], [300, 70], num_q_heads=4, num_kv_heads=1, head_dim=64, index_dim=32,
+               top_k=top_k, seed=37, qkv_std=1.0)
+    t, dims, bufs, P, ref = _full_check(w, tag=f"lists-long-k{top_k}")
+    sel = bufs.sel.cpu().numpy()
+    off, ent = O.build_block_query_lists(sel, P.seq, P.batch, P.G, P.nb_max)
+    n = int(off[-1])
+    assert np.array_equal(bufs.offsets.cpu().numpy().astype(np.int64), off)
+    assert np.array_equal(bufs.entries[:n].cpu().numpy().astype(np.int64), ent)
+
+
 def test_attend_on_oracle_selection():
     """Main Branch checked on the oracle's own selection (lists built on GPU)."""
     import block_sparse_long_index_amd as msa
