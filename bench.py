@@ -722,7 +722,7 @@ def run_leg(args):
     per_step = {k_: v["ms_per_step"] for k_, v in stage.items()}
     log("[bench] stages (ms/step): " + ", ".join(f"{k_} {v:.3f}" for k_, v in per_step.items()))
 
-    def traffic_record(name, compact=False):
+    def traffic_record(name, compact=False, launches=None):
         """Measured HBM bytes per launch (FETCH_SIZE/WRITE_SIZE scaled by a copy of known
         size, profiles/<kernel>_<workload>[_compact]_traffic.json) if the kernel code is
         unchanged."""
@@ -733,6 +733,10 @@ def run_leg(args):
         rec = json.load(open(path))
         if source_code_hash(os.path.join(ROOT, rec["source"])) != rec.get("source_code_sha256") or \
                 args.q_chunk or args.main != "bf16" or args.paged:
+            return None
+        # a launch's bytes depend on the pass size: the record must come from a run
+        # that launched the kernel as often per step as this one does
+        if "dispatches_per_step" in rec and rec["dispatches_per_step"] != launches:
             return None
         return rec["per_dispatch"]["total_bytes"] / 1e9
 
@@ -746,13 +750,13 @@ def run_leg(args):
         if name == "index_project":
             a = wm["project_flops"] / n_launch / sec
             return dict(bound="mfma", achieved=a / 1e12, peak=PEAK_BF16_FLOPS / 1e12, unit="TFLOP/s",
-                        frac=a / PEAK_BF16_FLOPS, traffic=traffic_record(name), dtype="bf16")
+                        frac=a / PEAK_BF16_FLOPS, traffic=traffic_record(name, launches=n_launch), dtype="bf16")
         if name in ("index_select_prefill", "index_select_prefill_fp8", "index_select_prefill_q8k4"):
             # E2M1 x E4M3 runs at the fp8 rate (an 8-bit operand sets the MFMA's cycle count)
             peak = PEAK_BF16_FLOPS if name == "index_select_prefill" else PEAK_FP8_FLOPS
             a = wm["index_flops"] / n_launch / sec
             return dict(bound="mfma", achieved=a / 1e12, peak=peak / 1e12, unit="TFLOP/s",
-                        frac=a / peak, traffic=traffic_record(name),
+                        frac=a / peak, traffic=traffic_record(name, launches=n_launch),
                         dtype={"index_select_prefill": "bf16", "index_select_prefill_fp8": "fp8 e4m3",
                                "index_select_prefill_q8k4": "e2m1 keys x e4m3 queries"}[name])
         bytes_ = {"attend_blocks": wm[{"bf16": "attend_bytes", "fp8": "attend_bytes_fp8",
@@ -773,7 +777,7 @@ def run_leg(args):
             per_launch = bytes_[name] / n_launch
             a = per_launch / sec
             return dict(bound="hbm", achieved=a / 1e9, peak=PEAK_HBM_BYTES / 1e9, unit="GB/s",
-                        frac=a / PEAK_HBM_BYTES, traffic=traffic_record(name, compact),
+                        frac=a / PEAK_HBM_BYTES, traffic=traffic_record(name, compact, n_launch),
                         traffic_unit="GB per launch (HBM, counters scaled by a copy of known size)",
                         algorithmic_per_launch=per_launch / 1e9)
         return None
@@ -795,15 +799,26 @@ def run_leg(args):
     rec_path = os.path.join(ROOT, "profiles", f"{rec_name}_{w.name}_traffic.json")
     if os.path.exists(rec_path) and args.main == "bf16" and not args.paged and not args.q_chunk:
         rec = json.load(open(rec_path))
-        if source_code_hash(os.path.join(ROOT, rec["source"])) == rec.get("source_code_sha256"):
-            n_disp = stage.get("attend_blocks", {}).get("launches_per_step", 0)
+        n_disp = stage.get("attend_blocks", {}).get("launches_per_step", 0)
+        if source_code_hash(os.path.join(ROOT, rec["source"])) == rec.get("source_code_sha256") and \
+                rec.get("dispatches_per_step", n_disp) == n_disp:
             fetch = rec["per_dispatch"]["read_gb"] * 1e9 * n_disp
             hpg = w.num_q_heads // w.num_kv_heads
             q_bytes = wm["sel_total"] * hpg * w.head_dim * 2
             list_bytes = wm["sel_total"] * 4 if lists_path else 0.0
             kv_read = fetch - q_bytes - list_bytes
             reread["counter_kv_read_bytes"] = kv_read
-            reread["counter_frac"] = kv_read / reread["unique_kv_bytes"] - 1.0
+            # the estimate subtracts the gathered Q, assumed all from HBM (some comes
+            # from the caches); when the unique K/V is a small share of the kernel's
+            # reads that assumption's error exceeds the K/V term, and no fraction is given
+            share = reread["unique_kv_bytes"] / fetch if fetch > 0 else 0.0
+            reread["counter_kv_share_of_reads"] = share
+            if share >= 0.05:
+                reread["counter_frac"] = kv_read / reread["unique_kv_bytes"] - 1.0
+            else:
+                reread["counter_frac"] = None
+                reread["counter_note"] = (f"unique K/V is {100 * share:.1f}% of the attend kernel's HBM "
+                                          "reads, below what subtracting the gathered Q can resolve")
     log(f"[bench] K/V re-read fraction (schedule): {reread['frac']:.4f}")
     extra = {}
     if decode:

@@ -71,7 +71,7 @@ namespace {
 
 thread_local std::string g_last_error;
 
-constexpr size_t kDefaultChunkBytes = (size_t)48 << 30;   // workspace cap when q_chunk == 0
+constexpr size_t kDefaultChunkBytes = (size_t)72 << 30;   // workspace cap when q_chunk == 0
 constexpr int kMaxNbLds = 12288;                          // per-sequence blocks the LDS lists hold
 constexpr int kMaxBatch = 65535;                            // a grid dimension's limit
 constexpr int kDecodeRowsMax = 128;                       // (query, group) rows per sequence, decode path

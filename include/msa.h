@@ -470,7 +470,7 @@ msa_status_t msa_attend_noalloc(const msa_dims_t* dims, const void* q, const voi
 
 /* Query rows that msa_attend and its variants process per internal pass for
  * these dims (dims->q_chunk when set, else the library's choice, which keeps
- * the workspace under 48 GiB): a call makes ceil(total_q / rows) passes, and
+ * the workspace under 72 GiB): a call makes ceil(total_q / rows) passes, and
  * a KV block whose query list spans several passes is staged once per pass.
  * A negative msa_status_t for invalid dims. */
 int64_t msa_attend_pass_rows(const msa_dims_t* dims);
