@@ -20,8 +20,8 @@ hipError_t launch_index_select_prefill(const void*, const void*, const int32_t*,
 hipError_t launch_index_score_decode(const void*, const void*, const int32_t*, const int32_t*, KvMap,
                                      int, int, int, int, int, int, int, float*, long long,
                                      hipStream_t);
-hipError_t launch_topk_select(const float*, long long, int, int, const int32_t*, const int32_t*, int,
-                              int, int, int32_t*, float*, hipStream_t);
+hipError_t launch_topk_select(const float*, long long, int, int, int, const int32_t*, const int32_t*,
+                              int, int, int, int32_t*, float*, hipStream_t);
 size_t lists_workspace_bytes(int batch, int G, int nqt_max, int nb_max);
 int list_tile_rows();
 hipError_t launch_build_lists(const int32_t*, const int32_t*, const int32_t*, int, int, int, int,
@@ -450,7 +450,7 @@ msa_status_t msa_index_select(const msa_dims_t* dims, const void* q_idx, const v
     }
     if (msa_status_t ls = launched(e, st, K_INDEX_DECODE); ls != MSA_OK) return ls;
     ProfScope ps(K_TOPK, st);
-    e = msa::launch_topk_select(S, ld, a, z, cu_seqlens_q, cu_seqlens_k, dims->batch, x.G, x.top_k,
+    e = msa::launch_topk_select(S, ld, x.nb_max, a, z, cu_seqlens_q, cu_seqlens_k, dims->batch, x.G, x.top_k,
                                 sel, sel_score, st);
     if (msa_status_t ls = launched(e, st, K_TOPK); ls != MSA_OK) return ls;
   }
@@ -556,7 +556,7 @@ msa_status_t select_q8(const msa_dims_t* dims, const void* q_idx8, const uint8_t
     }
     if (msa_status_t ls = launched(e, st, k4 ? K_INDEX_DECODE_Q8K4 : K_INDEX_DECODE_FP8); ls != MSA_OK) return ls;
     ProfScope ps(K_TOPK, st);
-    e = msa::launch_topk_select(S, ld, a, z, cu_seqlens_q, cu_seqlens_k, dims->batch, x.G, x.top_k,
+    e = msa::launch_topk_select(S, ld, x.nb_max, a, z, cu_seqlens_q, cu_seqlens_k, dims->batch, x.G, x.top_k,
                                 sel, sel_score, st);
     if (msa_status_t ls = launched(e, st, K_TOPK); ls != MSA_OK) return ls;
   }

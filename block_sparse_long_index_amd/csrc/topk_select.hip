@@ -40,9 +40,9 @@ constexpr int kTopkSurvMax = 256;    // survivors gathered in LDS
 // grid.x = rows of the pass (chunk row = (query - r0) * G + g), one workgroup each.
 template <int KCAP>
 __global__ __launch_bounds__(kTopkThreads) void topk_select_kernel(
-    const float* __restrict__ S, long long ld, int r0, int r1, const int32_t* __restrict__ cu_q,
-    const int32_t* __restrict__ cu_k, int batch, int G, int top_k, int32_t* __restrict__ sel,
-    float* __restrict__ sel_score) {
+    const float* __restrict__ S, long long ld, int nb_rows, int r0, int r1,
+    const int32_t* __restrict__ cu_q, const int32_t* __restrict__ cu_k, int batch, int G, int top_k,
+    int32_t* __restrict__ sel, float* __restrict__ sel_score) {
   __shared__ uint64_t lane_max[kTopkWaves][kWave];
   __shared__ uint64_t wave_t[kTopkWaves];
   __shared__ uint64_t wave_best[kTopkWaves];
@@ -56,9 +56,17 @@ __global__ __launch_bounds__(kTopkThreads) void topk_select_kernel(
   const int km = top_k - 1;
   const int r = r0 + (int)(crow / G);
   const int g = (int)(crow % G);
+  const float* col = S + crow;
+  // the first kTopkPerThread scores of the thread are loaded before the row's
+  // own block is known (clamped to the buffer's nb_rows block rows; scores of
+  // blocks at or after the row's own block are dropped below), so the loads
+  // overlap the row lookup
+  float s_first[kTopkPerThread];
+#pragma unroll
+  for (int i = 0; i < kTopkPerThread; ++i)
+    s_first[i] = col[(size_t)min(tid + i * kTopkThreads, nb_rows - 1) * ld];
   const RowPos rp = locate_row(r, cu_q, cu_k, batch);
   const int beta_p = rp.p / kBlock;
-  const float* col = S + crow;
   int32_t* so = sel + ((size_t)r * G + g) * top_k;
   float* sco = sel_score ? sel_score + ((size_t)r * G + g) * top_k : nullptr;
 
@@ -71,18 +79,10 @@ __global__ __launch_bounds__(kTopkThreads) void topk_select_kernel(
 
   // 1. the first kTopkPerThread candidates of the thread in registers; its max
   uint64_t first[kTopkPerThread];
-  {
-    float s[kTopkPerThread];
 #pragma unroll
-    for (int i = 0; i < kTopkPerThread; ++i) {
-      const int beta = tid + i * kTopkThreads;
-      s[i] = col[(size_t)min(beta, max(beta_p - 1, 0)) * ld];
-    }
-#pragma unroll
-    for (int i = 0; i < kTopkPerThread; ++i) {
-      const int beta = tid + i * kTopkThreads;
-      first[i] = (beta < beta_p && s[i] == s[i]) ? make_key(s[i], beta) : 0;
-    }
+  for (int i = 0; i < kTopkPerThread; ++i) {
+    const int beta = tid + i * kTopkThreads;
+    first[i] = (beta < beta_p && s_first[i] == s_first[i]) ? make_key(s_first[i], beta) : 0;
   }
   uint64_t mx = 0;
 #pragma unroll
@@ -193,26 +193,26 @@ __global__ __launch_bounds__(kTopkThreads) void topk_select_kernel(
 }
 
 template <int KCAP>
-static hipError_t launch_topk_kcap(const float* S, long long ld, int r0, int r1, const int32_t* cu_q,
+static hipError_t launch_topk_kcap(const float* S, long long ld, int nb_rows, int r0, int r1, const int32_t* cu_q,
                                    const int32_t* cu_k, int batch, int G, int top_k, int32_t* sel,
                                    float* sel_score, hipStream_t st) {
   const long long nrows = (long long)(r1 - r0) * G;
   if (nrows <= 0) return hipSuccess;
-  hipLaunchKernelGGL((topk_select_kernel<KCAP>), dim3((unsigned)nrows), dim3(kTopkThreads), 0, st, S, ld, r0,
-                     r1, cu_q, cu_k, batch, G, top_k, sel, sel_score);
+  hipLaunchKernelGGL((topk_select_kernel<KCAP>), dim3((unsigned)nrows), dim3(kTopkThreads), 0, st, S, ld,
+                     nb_rows, r0, r1, cu_q, cu_k, batch, G, top_k, sel, sel_score);
   return hipGetLastError();
 }
 
-hipError_t launch_topk_select(const float* S, long long ld, int r0, int r1, const int32_t* cu_q,
+hipError_t launch_topk_select(const float* S, long long ld, int nb_rows, int r0, int r1, const int32_t* cu_q,
                               const int32_t* cu_k, int batch, int G, int top_k, int32_t* sel,
                               float* sel_score, hipStream_t st) {
   const int km = top_k - 1;
-  if (km <= 1) return launch_topk_kcap<1>(S, ld, r0, r1, cu_q, cu_k, batch, G, top_k, sel, sel_score, st);
-  if (km <= 2) return launch_topk_kcap<2>(S, ld, r0, r1, cu_q, cu_k, batch, G, top_k, sel, sel_score, st);
-  if (km <= 4) return launch_topk_kcap<4>(S, ld, r0, r1, cu_q, cu_k, batch, G, top_k, sel, sel_score, st);
-  if (km <= 8) return launch_topk_kcap<8>(S, ld, r0, r1, cu_q, cu_k, batch, G, top_k, sel, sel_score, st);
-  if (km <= 16) return launch_topk_kcap<16>(S, ld, r0, r1, cu_q, cu_k, batch, G, top_k, sel, sel_score, st);
-  return launch_topk_kcap<32>(S, ld, r0, r1, cu_q, cu_k, batch, G, top_k, sel, sel_score, st);
+  if (km <= 1) return launch_topk_kcap<1>(S, ld, nb_rows, r0, r1, cu_q, cu_k, batch, G, top_k, sel, sel_score, st);
+  if (km <= 2) return launch_topk_kcap<2>(S, ld, nb_rows, r0, r1, cu_q, cu_k, batch, G, top_k, sel, sel_score, st);
+  if (km <= 4) return launch_topk_kcap<4>(S, ld, nb_rows, r0, r1, cu_q, cu_k, batch, G, top_k, sel, sel_score, st);
+  if (km <= 8) return launch_topk_kcap<8>(S, ld, nb_rows, r0, r1, cu_q, cu_k, batch, G, top_k, sel, sel_score, st);
+  if (km <= 16) return launch_topk_kcap<16>(S, ld, nb_rows, r0, r1, cu_q, cu_k, batch, G, top_k, sel, sel_score, st);
+  return launch_topk_kcap<32>(S, ld, nb_rows, r0, r1, cu_q, cu_k, batch, G, top_k, sel, sel_score, st);
 }
 
 }  // namespace msa
