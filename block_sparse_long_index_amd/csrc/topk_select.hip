@@ -64,7 +64,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_select_kernel(
   float s_first[kTopkPerThread];
 #pragma unroll
   for (int i = 0; i < kTopkPerThread; ++i)
-    s_first[i] = col[(size_t)min(tid + i * kTopkThreads, nb_rows - 1) * ld];
+    s_first[i] = col[(size_t)min(tid + i * kTopkThreads, max(nb_rows - 1, 0)) * ld];
   const RowPos rp = locate_row(r, cu_q, cu_k, batch);
   const int beta_p = rp.p / kBlock;
   int32_t* so = sel + ((size_t)r * G + g) * top_k;
