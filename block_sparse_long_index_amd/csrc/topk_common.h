@@ -64,7 +64,9 @@ struct OrderedTopList {
 #pragma unroll
       for (int i = N - 1; i >= 1; --i) {
         id[i] = gt[i - 1] ? id[i - 1] : (gt[i] ? beta : id[i]);
-        key[i] = max(key[i], min(key[i - 1], k));   // median, as key[i-1] >= key[i]
+        // the median of key[i-1] >= key[i] and k, written as the general median
+        // so that it becomes one v_med3_u32
+        key[i] = max(min(key[i - 1], key[i]), min(max(key[i - 1], key[i]), k));
       }
       id[0] = gt[0] ? beta : id[0];
       key[0] = max(key[0], k);
