@@ -385,14 +385,29 @@ def parity_on_rows(P, rows, ref, sel_gpu, out_gpu, lse_gpu, top_k, fp8=False):
 
 # ---------------------------------------------------------------------------
 def source_code_hash(path: str) -> str:
-    """sha256 of a kernel source with its comments and whitespace removed: a
-    traffic record stays valid while the code it was measured on is unchanged."""
+    """sha256 of a kernel source and of the local headers it includes (recursively),
+    with comments and whitespace removed: a traffic record stays valid while the
+    code it was measured on is unchanged."""
     import hashlib
     import re
-    text = open(path, encoding="utf-8").read()
-    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
-    text = re.sub(r"//[^\n]*", " ", text)
-    return hashlib.sha256(" ".join(text.split()).encode()).hexdigest()
+    seen, order = set(), []
+
+    def visit(p):
+        if p in seen or not os.path.exists(p):
+            return
+        seen.add(p)
+        order.append(p)
+        for inc in sorted(re.findall(r'#include\s+"([^"]+)"', open(p, encoding="utf-8").read())):
+            visit(os.path.join(os.path.dirname(p), inc))
+
+    visit(path)
+    h = hashlib.sha256()
+    for p in order:
+        text = open(p, encoding="utf-8").read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        h.update(" ".join(text.split()).encode())
+    return h.hexdigest()
 
 
 def parse_args(argv=None):
